@@ -1,0 +1,14 @@
+"""CPU oracle (test infrastructure only; see logp_oracle's header)."""
+
+from .logp_oracle import (  # noqa: F401
+    InvalidTargetError,
+    linear_logits,
+    linear_logp_fwd,
+    logp_bwd,
+    logp_fwd,
+    merge_partials,
+    num_tiles,
+    shard_tile_ranges,
+    tile_partials,
+    tiled_logp_fwd,
+)

@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test fixes the oracle against a closed form, a brute-force evaluation,
+an independent library routine or an invariant of the mathematics, chosen so
+that a plausible slip in the oracle (a dropped max shift, a wrong sign, a
+wrong column, a transposed operand, a lost padding rule) fails at least one.
+Sources: "Batch-Invariant LogP" (opening definition, Reference Semantics,
+Tensor Parallel, Batch-Invariance) and the fused LM-head operator of
+"[RFC][ROCm] End-to-end optimization of bitwise VIME R/R beyond native P/P"
+(Workstream 3).
+"""
+
+import json
+import math
+import os
+from decimal import Decimal
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _golden_row(spec, v):
+    kind = spec["kind"]
+    if kind == "constant":
+        return np.full(v, spec["value"], dtype=np.float64)
+    if kind == "log_ladder":
+        return np.array([math.log(j + 1) for j in range(v)], dtype=np.float64)
+    if kind == "two_level":
+        x = np.full(v, spec["b"], dtype=np.float64)
+        x[: spec["k"]] = spec["a"]
+        return x
+    if kind == "spike":
+        x = np.zeros(v, dtype=np.float64)
+        x[spec["col"]] = spec["height"]
+        return x
+    raise ValueError(kind)
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_closed_forms(case):
+    """logp, lse and gradient against decimal closed forms (golden file)."""
+    v = case["v"]
+    x = _golden_row(case["row"], v)
+    targets = [e["target"] for e in case["targets"]]
+    rows = np.tile(x, (len(targets), 1))
+    logp, lse = oracle.logp_fwd(rows, targets)
+    want_lse = float(Decimal(case["lse"]))
+    for i, e in enumerate(case["targets"]):
+        want = float(Decimal(e["logp"]))
+        assert abs(logp[i] - want) <= 1e-12 * max(1.0, abs(want)), (i, logp[i], want)
+        assert abs(lse[i] - want_lse) <= 1e-12 * max(1.0, abs(want_lse))
+    d = oracle.logp_bwd(rows, targets, np.ones(len(targets)))
+    for i, e in enumerate(case["targets"]):
+        for j, val in e["grad_g1"].items():
+            assert abs(d[i, int(j)] - float(Decimal(val))) <= 1e-12, (i, j)
+
+
+def _brute(x_row, t):
+    total = math.fsum(math.exp(float(a)) for a in x_row)
+    return math.log(math.exp(float(x_row[t])) / total)
+
+
+def test_brute_force_v8():
+    """Tiny V: direct log(exp(x_t)/sum exp(x)) without any max shift."""
+    c = synth.tiny_v8(n=64)
+    x = c["logits"].numpy()
+    t = c["targets"].numpy()
+    logp, lse = oracle.logp_fwd(x, t)
+    for r in range(x.shape[0]):
+        assert abs(logp[r] - _brute(x[r], t[r])) <= 1e-14
+        lse_b = math.log(math.fsum(math.exp(float(a)) for a in x[r]))
+        assert abs(lse[r] - lse_b) <= 1e-14 * max(1.0, abs(lse_b))
+
+
+def test_library_log_softmax():
+    """The pages' reference semantics evaluated by torch in float64."""
+    c = synth.tiny_fp32()
+    x = c["logits"].double()
+    t = c["targets"]
+    logp, lse = oracle.logp_fwd(c["logits"].numpy(), t.numpy(), c["ignore_index"])
+    active = t != c["ignore_index"]
+    ref = torch.log_softmax(x, dim=-1).gather(
+        -1, t.clamp(min=0).unsqueeze(-1)).squeeze(-1)
+    ref = torch.where(active, ref, torch.zeros_like(ref)).numpy()
+    np.testing.assert_allclose(logp, ref, rtol=1e-13, atol=1e-13)
+    ref_lse = torch.logsumexp(x, dim=-1).numpy()
+    np.testing.assert_allclose(lse[active.numpy()], ref_lse[active.numpy()],
+                               rtol=1e-13, atol=0)
+    assert np.all(logp[~active.numpy()] == 0.0)
+    assert np.all(lse[~active.numpy()] == 0.0)
+
+
+def test_library_log_softmax_large_v():
+    """bf16 Qwen3-vocab rows (widened exactly to float32) vs torch float64."""
+    c = synth.qwen3_fwd(n=24)
+    x32 = c["logits"].float()
+    t = c["targets"]
+    logp, lse = oracle.logp_fwd(x32.numpy(), t.numpy())
+    active = (t != -100)
+    ref = torch.log_softmax(x32.double(), -1).gather(
+        -1, t.clamp(min=0).unsqueeze(-1)).squeeze(-1).numpy()
+    a = active.numpy()
+    np.testing.assert_allclose(logp[a], ref[a], rtol=1e-13, atol=1e-12)
+
+
+def test_shift_invariance():
+    """logp(x + c) = logp(x) and lse(x + c) = lse(x) + c."""
+    c = synth.tiny_fp32()
+    x = c["logits"].numpy().astype(np.float64)
+    t = c["targets"].numpy()
+    logp0, lse0 = oracle.logp_fwd(x, t)
+    for shift in (7.25, -30.0, 1000.0):
+        logp1, lse1 = oracle.logp_fwd(x + shift, t)
+        a = t != -100
+        np.testing.assert_allclose(logp1[a], logp0[a], atol=1e-10, rtol=0)
+        np.testing.assert_allclose(lse1[a], lse0[a] + shift, rtol=1e-13)
+
+
+@pytest.mark.parametrize("v", [8, 300, 4096])
+def test_normalisation(v):
+    """sum over every target of exp(logp) is 1, and logp_j = x_j - lse."""
+    g = np.random.default_rng(v)
+    x = g.normal(0, 2.0, v)
+    rows = np.tile(x, (v, 1))
+    logp, lse = oracle.logp_fwd(rows, np.arange(v))
+    assert abs(math.fsum(np.exp(logp)) - 1.0) <= 1e-13
+    assert np.all(lse == lse[0])
+    np.testing.assert_allclose(logp, x - lse[0], rtol=0, atol=1e-13)
+
+
+def test_spike_bound():
+    """Target on a one-hot spike: logp is within the two bounds set by the
+    gap from the spike to the next-largest logit."""
+    v = 151936
+    g = np.random.default_rng(5)
+    x = g.normal(0, 3.0, v)
+    x[1234] = x.max() + 20.0
+    gap = x[1234] - np.partition(x, -2)[-2]
+    logp, _ = oracle.logp_fwd(x[None, :], [1234])
+    # log(1 + e^-gap) <= -logp = log(1 + sum_{j != t} e^(x_j - x_t)) <= (V-1) e^-gap
+    assert logp[0] <= 0.0
+    assert abs(logp[0]) <= (v - 1) * math.exp(-gap) * (1 + 1e-9)
+    assert abs(logp[0]) >= math.log1p(math.exp(-gap)) * (1 - 1e-9)
+
+
+def test_ignore_and_invalid_targets():
+    x = np.random.default_rng(0).normal(size=(4, 16))
+    logp, lse = oracle.logp_fwd(x, [3, -100, 0, 15])
+    assert logp[1] == 0.0 and lse[1] == 0.0
+    assert logp[0] != 0.0
+    with pytest.raises(oracle.InvalidTargetError):
+        oracle.logp_fwd(x, [3, 16, 0, 0])
+    with pytest.raises(oracle.InvalidTargetError):
+        oracle.logp_fwd(x, [3, -1, 0, 0])
+    # target -1 is an ignored row only when ignore_index is -1
+    logp, _ = oracle.logp_fwd(x, [3, -1, 0, 0], ignore_index=-1)
+    assert logp[1] == 0.0
+    with pytest.raises(oracle.InvalidTargetError):
+        oracle.logp_fwd(x, [3, -100, 0, 0], ignore_index=-1)
+    d = oracle.logp_bwd(x, [3, -100, 0, 15], np.ones(4))
+    assert np.all(d[1] == 0.0)
+
+
+def test_sign_bound():
+    c = synth.tiny_fp32()
+    logp, _ = oracle.logp_fwd(c["logits"].numpy(), c["targets"].numpy())
+    assert np.all(logp <= 0.0)
+
+
+def test_leading_shape_flatten():
+    """[B, T, V] logits are the same rows as the flattened [B*T, V]."""
+    g = np.random.default_rng(1)
+    x = g.normal(size=(2, 4, 300))
+    t = g.integers(0, 300, size=(2, 4))
+    t[0, 0] = -100
+    logp3, _ = oracle.logp_fwd(x, t)
+    logp2, _ = oracle.logp_fwd(x.reshape(8, 300), t.reshape(8))
+    assert np.array_equal(logp3, logp2)
+    assert logp3[0] == 0.0
+
+
+# ----- tiled construction: merge identity and bookkeeping -----------------
+
+def test_shard_tile_ranges_qwen3():
+    v, w = 151936, 4096
+    assert oracle.num_tiles(v, w) == 38
+    assert oracle.shard_tile_ranges(v, w, 1) == [(0, 38)]
+    assert oracle.shard_tile_ranges(v, w, 2) == [(0, 19), (19, 38)]
+    assert oracle.shard_tile_ranges(v, w, 4) == [(0, 10), (10, 19), (19, 28), (28, 38)]
+    with pytest.raises(ValueError):
+        oracle.shard_tile_ranges(v, w, 3)
+
+
+@pytest.mark.parametrize("v,w,s", [(151936, 4096, 4), (4096, 512, 2), (8, 512, 8),
+                                   (300, 7, 3), (1000, 64, 5), (64, 1, 64)])
+def test_shard_ranges_partition(v, w, s):
+    """Every tile has exactly one owner, owners are ascending and contiguous,
+    and each tile's first column lies in its owner's nominal range."""
+    ranges = oracle.shard_tile_ranges(v, w, s)
+    t = oracle.num_tiles(v, w)
+    assert ranges[0][0] == 0 and ranges[-1][1] == t
+    for (a, b), (c, _) in zip(ranges, ranges[1:]):
+        assert b == c and a <= b
+    per = v // s
+    for i, (lo, hi) in enumerate(ranges):
+        for k in range(lo, hi):
+            assert i * per <= k * w < (i + 1) * per
+
+
+def test_tile_partials_brute():
+    """(m_k, s_k) against Python loops, with the -inf padded last tile."""
+    g = np.random.default_rng(2)
+    x = g.normal(0, 3, 37)
+    m, s = oracle.tile_partials(x, 8)
+    assert m.shape == (5,)
+    for k in range(5):
+        cols = [float(a) for a in x[8 * k: 8 * k + 8]]
+        assert m[k] == max(cols)
+        assert abs(s[k] - math.fsum(math.exp(a - max(cols)) for a in cols)) <= 1e-14
+    assert s[4] <= 5.0 + 1e-12  # 5 real columns in the padded tile
+
+
+@pytest.mark.parametrize("w", [1, 7, 512, 4096])
+@pytest.mark.parametrize("s", [1, 2, 4])
+def test_tiled_merge_identity(w, s):
+    """fp64 tile partials merged in the fixed order equal the untiled LSE
+    (associativity of the (max, sumexp) merge in real arithmetic)."""
+    g = np.random.default_rng(w * 10 + s)
+    for v in (8, 300, 4096, 151936):
+        if v % s or (v > 4096 and w < 512):
+            continue
+        x = g.normal(0, 3.0, (3, v))
+        t = g.integers(0, v, 3)
+        logp0, lse0 = oracle.logp_fwd(x, t)
+        logp1, lse1 = oracle.tiled_logp_fwd(x, t, -100, w, s)
+        np.testing.assert_allclose(lse1, lse0, rtol=1e-12)
+        np.testing.assert_allclose(logp1, logp0, rtol=1e-12, atol=1e-12)
+
+
+def test_tiled_fp32_contract_error():
+    """The float32 tiled construction stays well inside 1e-5 abs + 1e-5 rel
+    of the exact value on the Qwen3-vocab distribution (the tolerance the
+    GPU path is held to)."""
+    c = synth.qwen3_fwd(n=16)
+    x = c["logits"].float().numpy()
+    t = c["targets"].numpy()
+    logp0, lse0 = oracle.logp_fwd(x, t)
+    logp1, lse1 = oracle.tiled_logp_fwd(x, t, -100, 4096, 1, dtype=np.float32)
+    err = np.abs(logp1 - logp0)
+    assert np.all(err <= 1e-5 + 1e-5 * np.abs(logp0))
+    assert np.all(np.abs(lse1 - lse0) <= 1e-5 + 1e-5 * np.abs(lse0))
+
+
+# ----- backward ------------------------------------------------------------
+
+def test_bwd_finite_difference():
+    """Central differences of the float64 forward reproduce g*(onehot - p)."""
+    g = np.random.default_rng(3)
+    x = g.normal(0, 2.0, (4, 8))
+    t = np.array([0, 3, 7, 5])
+    gr = np.array([1.0, -0.5, 2.0, 0.25])
+    d = oracle.logp_bwd(x, t, gr)
+    h = 1e-6
+    for r in range(4):
+        for j in range(8):
+            xp = x[r].copy(); xp[j] += h
+            xm = x[r].copy(); xm[j] -= h
+            fp, _ = oracle.logp_fwd(xp[None], [t[r]])
+            fm, _ = oracle.logp_fwd(xm[None], [t[r]])
+            fd = gr[r] * (fp[0] - fm[0]) / (2 * h)
+            assert abs(fd - d[r, j]) <= 1e-8, (r, j, fd, d[r, j])
+
+
+def test_bwd_library_autograd():
+    """torch float64 autograd of log_softmax.gather, scaled by g."""
+    c = synth.tiny_fp32()
+    x = c["logits"].double().requires_grad_(True)
+    t = c["targets"]
+    gr = torch.linspace(-1.5, 2.0, x.shape[0], dtype=torch.float64)
+    active = t != -100
+    sel = torch.log_softmax(x, -1).gather(-1, t.clamp(min=0)[:, None])[:, 0]
+    (torch.where(active, sel, torch.zeros_like(sel)) * gr).sum().backward()
+    d = oracle.logp_bwd(c["logits"].numpy(), t.numpy(), gr.numpy())
+    np.testing.assert_allclose(d, x.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_bwd_row_sum_zero():
+    c = synth.tiny_fp32()
+    gr = np.random.default_rng(4).normal(size=64)
+    d = oracle.logp_bwd(c["logits"].numpy(), c["targets"].numpy(), gr)
+    assert np.all(np.abs(d.sum(axis=1)) <= 1e-12)
+    ign = c["targets"].numpy() == -100
+    assert np.all(d[ign] == 0.0)
+
+
+# ----- fused LM head ---------------------------------------------------------
+
+def test_linear_identity_weight():
+    """W = I: z = h exactly, so the fused result is logp_fwd(h)."""
+    g = np.random.default_rng(6)
+    h = g.normal(size=(16, 64)).astype(np.float32)
+    t = g.integers(0, 64, 16)
+    t[3] = -100
+    a = oracle.linear_logp_fwd(h, np.eye(64, dtype=np.float32), t)
+    b = oracle.logp_fwd(h, t)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_linear_zero_weight():
+    """W = 0: every logit is 0, logp = -log V."""
+    h = np.random.default_rng(7).normal(size=(5, 32))
+    logp, lse = oracle.linear_logp_fwd(h, np.zeros((1000, 32)), [0, 1, 2, 999, 500])
+    np.testing.assert_allclose(logp, -math.log(1000), rtol=1e-15)
+    np.testing.assert_allclose(lse, math.log(1000), rtol=1e-15)
+
+
+def test_linear_brute_force():
+    """Pure-Python dot products and log-sum-exp on a tiny problem; a
+    transposed weight (z = h W instead of h W^T) cannot pass this."""
+    g = np.random.default_rng(8)
+    n, hd, v = 4, 8, 16
+    h = g.normal(size=(n, hd))
+    w = g.normal(size=(v, hd))
+    t = [0, 5, 15, 9]
+    logp, lse = oracle.linear_logp_fwd(h, w, t)
+    for r in range(n):
+        z = [math.fsum(float(h[r, k]) * float(w[j, k]) for k in range(hd))
+             for j in range(v)]
+        assert abs(logp[r] - _brute(z, t[r])) <= 1e-13
+    with pytest.raises(ValueError):
+        oracle.linear_logp_fwd(h, w.T, t)
