@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Throughput of the batch-invariant selected-token logp path on one MI355X.
+
+Default workload (one "step" = the whole hot path over one batch):
+  logits bf16 [8192, 151936] ~ N(0, 3) (Qwen3-8B vocabulary), 10% of rows
+  ignored, upstream gradient g ~ N(0, 1) fp32, tile width 4096;
+  step = logp_fwd (logp + lse) followed by logp_bwd (dlogits bf16 [N, V]).
+
+Inputs are generated on the device before timing (synthetic, seeded).  Prints
+one JSON line.  `value` is rows/s over the timed steps; the roofline object
+prices the dominant kernel's algorithmic bytes against the MI355X HBM peak;
+cpu_baseline times the float64 CPU oracle on a bounded row sample of the same
+workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload fwd_bwd|fwd|linear]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "logp_fwd_fused_kernel": ["invariant_token_log_amd/csrc/logp_kernels.hip",
+                              "invariant_token_log_amd/csrc/logp_device.h"],
+    "logp_bwd_kernel": ["invariant_token_log_amd/csrc/logp_kernels.hip",
+                        "invariant_token_log_amd/csrc/logp_device.h"],
+    "linear_logp_stats_kernel": ["invariant_token_log_amd/csrc/linear_logp.hip",
+                                 "invariant_token_log_amd/csrc/logp_device.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<kernel>_<workload>.txt), or None when absent or when
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_events(torch, fn, steps):
+    """Mean device time of fn() over `steps` calls, with events on the
+    current stream (the stream every library call launches on)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def bench_fwd_bwd(args, torch, itl, synth):
+    n, v, w = 8192, synth.QWEN3_VOCAB, 4096
+    dev = torch.device("cuda", 0)
+    c = synth.qwen3_fwd_bwd(n=n, v=v, device=dev)
+    x, t, g = c["logits"], c["targets"], c["grad"]
+    n_active = int((t != -100).sum().item())
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    dl = torch.empty_like(x)
+
+    def fwd():
+        itl.logp_fwd(x, t, -100, w, logp_out=logp, lse_out=lse)
+
+    def bwd():
+        itl.logp_bwd(x, t, lse, g, -100, w, dlogits_out=dl)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    # per-kernel averages over a second timed pass of the same steps
+    fwd_ms = time_events(torch, fwd, args.steps)
+    bwd_ms = time_events(torch, bwd, args.steps)
+
+    fwd_bytes = n_active * v * 2 + n * (8 + 4 + 4)
+    bwd_bytes = n_active * v * 2 + n * v * 2 + n * (8 + 4 + 4)
+    step_bytes = fwd_bytes + bwd_bytes
+    kernels = {
+        "logp_fwd_fused_kernel": dict(ms=fwd_ms, bytes=fwd_bytes),
+        "logp_bwd_kernel": dict(ms=bwd_ms, bytes=bwd_bytes),
+    }
+    for k in kernels.values():
+        k["gbps"] = k["bytes"] / (k["ms"] * 1e-3) / 1e9
+        k["hbm_frac"] = k["gbps"] / HBM_PEAK_GBS
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    traffic = measured_traffic(dom, "qwen3_8192x151936")
+    roofline = {"bound": "hbm", "achieved": round(kernels[dom]["gbps"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kernels[dom]["gbps"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": dom,
+                "algorithmic_bytes_per_launch": kernels[dom]["bytes"]}
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "rows/s and achieved HBM GB/s (% of peak), N=8192 V=151936 bf16 fwd+bwd",
+        "value": round(n / (ms_step * 1e-3), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_vocab_logp_fwd_bwd", "n": n, "v": v,
+                   "tile_width": w, "ignored_rows": n - n_active, "num_shards": 1},
+        "gb_per_s": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                        for kk, vv in d.items()} for k, d in kernels.items()},
+        "roofline": roofline,
+        "wall_s_timed": round(wall, 4),
+    }
+    sample = None
+    if not args.no_cpu_baseline:
+        sample = dict(x=x, t=t, g=g, n=n, v=v)
+    return out, sample
+
+
+def cpu_baseline_fwd_bwd(sample, rows):
+    """The float64 oracle (forward then backward) on the first `rows` rows
+    of the same workload, single process; D2H copies are excluded."""
+    import numpy as np
+
+    import oracle
+
+    x = sample["x"][:rows].float().cpu().numpy()
+    t = sample["t"][:rows].cpu().numpy()
+    g = sample["g"][:rows].cpu().numpy()
+    t0 = time.perf_counter()
+    for r0 in range(0, rows, 128):
+        xs, ts, gs = x[r0:r0 + 128], t[r0:r0 + 128], g[r0:r0 + 128]
+        _, lse = oracle.logp_fwd(xs, ts)
+        d = oracle.logp_bwd(xs, ts, gs, lse=lse)
+        del d
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": round(rows / dt, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} rows of the same [8192, 151936] bf16 batch, "
+                      f"float64 numpy forward+backward, {dt:.1f} s",
+            "cpu": cpu_model()}
+
+
+def bench_fwd(args, torch, itl, synth):
+    n, v, w = 4096, synth.QWEN3_VOCAB, 4096
+    dev = torch.device("cuda", 0)
+    c = synth.qwen3_fwd(n=n, v=v, device=dev)
+    x, t = c["logits"], c["targets"]
+    n_active = int((t != -100).sum().item())
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+
+    def fwd():
+        itl.logp_fwd(x, t, -100, w, logp_out=logp, lse_out=lse)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    ms = time_events(torch, fwd, args.steps)
+    byts = n_active * v * 2 + n * 16
+    gbps = byts / (ms * 1e-3) / 1e9
+    return {
+        "metric": "rows/s and achieved HBM GB/s (% of peak), N=4096 V=151936 bf16 fwd",
+        "value": round(n / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_vocab_logp_fwd", "n": n, "v": v, "tile_width": w,
+                   "ignored_rows": n - n_active},
+        "gb_per_s": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("logp_fwd_fused_kernel",
+                                                 "qwen3_4096x151936"),
+                     "kernel": "logp_fwd_fused_kernel"},
+    }, None
+
+
+def bench_linear(args, torch, itl, synth):
+    n, h, v = 4096, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB
+    dev = torch.device("cuda", 0)
+    c = synth.qwen3_linear(n=n, h=h, v=v, device=dev)
+    hid, wt, t = c["hidden"], c["weight"], c["targets"]
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = torch.empty(itl.lib().linear_logp_fwd_workspace_bytes(n, v, 256), dtype=torch.uint8,
+                     device=dev)
+
+    def run():
+        itl.linear_logp_fwd(hid, wt, t, -100, 256, logp_out=logp, lse_out=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ms = time_events(torch, run, args.steps)
+    flops = 2.0 * n * h * v
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "rows/s and MFMA TFLOP/s (% of peak), fused LM-head+logp N=4096 H=4096 "
+                  "V=151936 bf16",
+        "value": round(n / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_lm_head_linear_logp", "n": n, "h": h, "v": v,
+                   "tile_width": 256},
+        "tflops": round(tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("linear_logp_stats_kernel",
+                                                 "qwen3_4096x4096x151936"),
+                     "kernel": "linear_logp_stats_kernel"},
+    }
+    sample = None
+    if not args.no_cpu_baseline:
+        sample = dict(h=hid, w=wt, t=t)
+    return out, sample
+
+
+def cpu_baseline_linear(sample, rows):
+    import oracle
+
+    h = sample["h"][:rows].float().cpu().numpy()
+    w = sample["w"].float().cpu().numpy()
+    t = sample["t"][:rows].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.linear_logp_fwd(h, w, t)
+    dt = time.perf_counter() - t0
+    threads = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
+    return {"value": round(rows / dt, 2), "unit": "rows/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {rows} rows, float64 numpy h @ W^T then logp, {dt:.1f} s "
+                      "(BLAS threads = cores)",
+            "cpu": cpu_model()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwd_bwd", choices=["fwd_bwd", "fwd", "linear"])
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows for the CPU oracle baseline (0 = workload default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run three plain 1 GiB device copies (a known byte count "
+                         "for scaling HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows are independent, so data-parallel scaling needs no exchange); "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import invariant_token_log_amd as itl
+    import synth
+
+    if not torch.cuda.is_available():
+        sys.exit("no ROCm GPU visible")
+    itl.lib()  # fail loudly if the HIP library is missing
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    runner = {"fwd_bwd": bench_fwd_bwd, "fwd": bench_fwd, "linear": bench_linear}[args.workload]
+    out, sample = runner(args, torch, itl, synth)
+    if sample is not None:
+        if args.workload == "fwd_bwd":
+            out["cpu_baseline"] = cpu_baseline_fwd_bwd(sample, args.cpu_rows or 1024)
+        elif args.workload == "linear":
+            out["cpu_baseline"] = cpu_baseline_linear(sample, args.cpu_rows or 32)
+    if "cpu_baseline" in out and out["cpu_baseline"]["value"]:
+        out["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
+    out["contract_id"] = itl.contract_id()
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * invariant_logp.h -- C ABI of the batch-invariant selected-token
+ * log-probability library for AMD Instinct MI355X (gfx950).
+ *
+ * Operation ("Batch-Invariant LogP", opening definition and Reference
+ * Semantics): for every row r of a [N, V] logits matrix with target t_r,
+ *     logp[r] = logits[r, t_r] - logsumexp(logits[r, :])
+ * A row whose target equals ignore_index outputs 0 and receives a zero
+ * gradient; any other target outside [0, V) is invalid.
+ *
+ * Arithmetic contract ("Batch-Invariant LogP", Tensor Parallel; the contract
+ * vocabulary of the RFC "[RFC][ROCm] End-to-end optimization of bitwise VIME
+ * R/R beyond native P/P", section Contract boundary):
+ *   - the vocabulary is cut into fixed tiles of tile_width columns over the
+ *     global column index; columns >= V are -inf and never read;
+ *   - every tile gives an fp32 pair (m_k = tile max, s_k = sum exp(x - m_k))
+ *     through one fixed summation tree that depends only on the column
+ *     position inside the tile, the tile width and the dtype;
+ *   - the T = ceil(V / tile_width) pairs are merged in one fixed ascending
+ *     order: M = max m_k, acc = fma(s_k, exp(m_k - M), acc),
+ *     LSE = M + log(acc);
+ *   - the target logit is copied from the tile that holds it, never summed;
+ *     logp = target_logit - LSE in fp32.
+ * Hence a row's output bits depend only on that row's logits, its target,
+ * ignore_index and tile_width: not on N, on the row's position, on its
+ * neighbours, on the launch geometry or on num_shards.
+ *
+ * Conventions for every entry point:
+ *   - pointers are DEVICE pointers owned by the caller unless noted; the
+ *     library allocates nothing, frees nothing and keeps no pointer after it
+ *     returns;
+ *   - work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously; the caller keeps every buffer alive
+ *     until the stream has finished it;
+ *   - all arguments are checked on the host before any HIP call; on an error
+ *     nothing is enqueued and no output is touched;
+ *   - every output element is written, ignored rows included;
+ *   - the return value is a logp_status code; no C++ exception crosses the
+ *     ABI.
+ */
+#ifndef INVARIANT_LOGP_H
+#define INVARIANT_LOGP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum logp_status {
+  LOGP_OK = 0,
+  LOGP_ERR_NULL = 1,      /* a required pointer is NULL */
+  LOGP_ERR_SHAPE = 2,     /* n < 0, v < 1, ld < v, h < 1, or T too large */
+  LOGP_ERR_DTYPE = 3,     /* unknown dtype code */
+  LOGP_ERR_TILE = 4,      /* tile_width not supported for this dtype/op */
+  LOGP_ERR_ALIGN = 5,     /* fused LM-head operand not 16-byte aligned */
+  LOGP_ERR_SHARDS = 6,    /* num_shards < 1 or not a divisor of v */
+  LOGP_ERR_WORKSPACE = 7, /* workspace NULL or smaller than required */
+  LOGP_ERR_TARGET = 8,    /* validate = 1 found an active target outside [0, v) */
+  LOGP_ERR_HIP = 9        /* a HIP launch or copy failed */
+};
+
+/* Logits element types. */
+enum logp_dtype {
+  LOGP_F32 = 0,  /* IEEE binary32 */
+  LOGP_BF16 = 1  /* bfloat16, widened exactly to fp32 before any arithmetic */
+};
+
+/*
+ * Workspace of logp_fwd, in bytes.  It is 0 for num_shards == 1 with
+ * validate == 0 (the fused single-launch path).  Otherwise it holds the
+ * [T, n] tile partials (m and s, fp32), the copied target logits [n] and a
+ * 256-byte status block.  Returns 0 for arguments logp_fwd would reject.
+ */
+size_t logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width,
+                                int32_t num_shards, int32_t validate);
+
+/*
+ * Selected-token log-probability and row LSE ("Batch-Invariant LogP",
+ * Entry Point, Tensor Contract and Tensor Parallel).
+ *
+ *   logits        [n, ld] row-major, first v columns used; dtype LOGP_F32 or
+ *                 LOGP_BF16.  Any alignment is accepted; rows whose start is
+ *                 16-byte aligned stream with 128-bit loads.
+ *   targets       int64 [n].
+ *   ignore_index  rows with this target give logp = +0, lse = +0 and are not
+ *                 read.
+ *   tile_width    vocabulary tile width W: 512, 1024, 2048, 4096 or 8192 for
+ *                 bf16; 256, 512, 1024, 2048 or 4096 for fp32.  T =
+ *                 ceil(v / W) must not exceed 4096.  W is part of the
+ *                 arithmetic contract (it fixes the summation tree).
+ *   num_shards    S >= 1, v % S == 0: the vocabulary is split into S nominal
+ *                 ranges of v/S columns; shard s owns the tiles whose first
+ *                 column lies in its range, computes their partials in its own
+ *                 launch into the shared [T, n] table (the byte-only
+ *                 all-gather of the Tensor Parallel section), the owner of the
+ *                 target's tile copies the target logit, and one merge launch
+ *                 follows.  Results are bitwise equal for every S.
+ *   validate      0: no synchronisation; an active row whose target is
+ *                 outside [0, v) gets logp = NaN and nothing out of bounds is
+ *                 read.  1: the same, then the call waits for the stream and
+ *                 returns LOGP_ERR_TARGET if any such row was seen.
+ *   logp_out      fp32 [n].
+ *   lse_out       fp32 [n], may be NULL.  Saved for logp_bwd.
+ *   workspace     device buffer of at least logp_fwd_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0), 256-byte aligned.
+ */
+int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
+                 int64_t ld, const int64_t* targets, int64_t ignore_index,
+                 int32_t tile_width, int32_t num_shards, int32_t validate,
+                 float* logp_out, float* lse_out, void* workspace,
+                 size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Gradient of logp with respect to the logits ("Batch-Invariant LogP",
+ * Batch-Invariance: the tile-wise backward reusing the forward's per-row
+ * LSE; Reference Semantics: ignored rows get a zero gradient).
+ *
+ *   dlogits[r, j] = RNE_dtype( g[r] * u ),  u = 1 - p if j == t_r, else -p,
+ *   p = exp(x[r, j] - lse[r]) with the same exp primitive as the forward.
+ *
+ *   logits, dtype, n, v, ld, targets, ignore_index: as for logp_fwd.
+ *   tile_width  accepted for symmetry with logp_fwd and checked the same
+ *               way; it does not change any bit (the backward is elementwise).
+ *   lse         fp32 [n] from logp_fwd.
+ *   grad_logp   fp32 [n], the upstream gradient g.
+ *   dlogits_out [n, ld_out] of the logits dtype; ld_out >= v; columns >= v
+ *               are not written.  Ignored rows are written +0 without reading
+ *               the logits.  It may be exactly the logits buffer (same
+ *               pointer and ld_out == ld: in place); partial overlap is
+ *               undefined.  A row with an invalid target gets u = -p.
+ */
+int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
+                 int64_t ld, const int64_t* targets, int64_t ignore_index,
+                 int32_t tile_width, const float* lse, const float* grad_logp,
+                 void* dlogits_out, int64_t ld_out, void* hip_stream);
+
+/*
+ * Workspace of linear_logp_fwd in bytes: the [T, n] partials (m, s) for
+ * T = ceil(v / tile_width) and the copied target logits [n].  Returns 0 for
+ * arguments linear_logp_fwd would reject.
+ */
+size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width);
+
+/*
+ * Fused LM-head + selected-token log-probability ("[RFC][ROCm] End-to-end
+ * optimization of bitwise VIME R/R beyond native P/P", Workstream 3):
+ *   z[r, j] = sum_k hidden[r, k] * weight[j, k]   (fp32, never stored)
+ *   logp[r] = z[r, t_r] - LSE(z[r, :])
+ * The products run on bf16 MFMA with fp32 accumulation, one accumulator per
+ * output, K walked in ascending fixed blocks with no split-K; the tile
+ * statistics of the logp contract are taken on the fp32 z in the GEMM
+ * epilogue, then merged in the fixed ascending order.
+ *
+ *   hidden      bf16 [n, ld_h], first h columns used.
+ *   weight      bf16 [v, ld_w] (vocabulary-major LM-head weight).
+ *   h           hidden size, a multiple of 64.
+ *   tile_width  the statistic tile: must be 256 (the kernel's vocabulary
+ *               block).
+ *   hidden, weight, ld_h and ld_w must give 16-byte aligned rows
+ *   (LOGP_ERR_ALIGN otherwise).
+ *   targets, ignore_index, logp_out, lse_out (may be NULL): as logp_fwd,
+ *   with no validation (invalid active targets give logp = NaN).
+ *   workspace   at least linear_logp_fwd_workspace_bytes(...) bytes,
+ *               256-byte aligned.
+ */
+int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight,
+                        int64_t ld_w, int64_t n, int64_t h, int64_t v,
+                        const int64_t* targets, int64_t ignore_index,
+                        int32_t tile_width, float* logp_out, float* lse_out,
+                        void* workspace, size_t workspace_bytes,
+                        void* hip_stream);
+
+/* Short English text for a status code (static storage, host memory). */
+const char* logp_status_str(int32_t status);
+
+/* Identifier of the arithmetic contracts this build implements (static
+ * storage, host memory): tile tree, merge order, exp/log primitives, MFMA
+ * form and K walk.  Two builds that report the same string produce the same
+ * bits. */
+const char* logp_contract_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INVARIANT_LOGP_H */

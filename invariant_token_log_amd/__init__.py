@@ -1,0 +1,15 @@
+"""Batch-invariant selected-token log-probability for AMD Instinct MI355X.
+
+The computation runs in the HIP library libinvariant_logp.so (C ABI declared
+in include/invariant_logp.h); this package only marshals PyTorch tensors into
+it.  There is no CPU or PyTorch fallback: a missing library raises.
+"""
+
+from ._lib import LogpError, contract_id, lib, status_str  # noqa: F401
+from .ops import (  # noqa: F401
+    LINEAR_TILE,
+    batch_invariant_logp,
+    linear_logp_fwd,
+    logp_bwd,
+    logp_fwd,
+)

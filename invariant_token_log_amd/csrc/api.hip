@@ -1,0 +1,203 @@
+// C ABI of the library: argument checks (all before any HIP call), workspace
+// layout, and the launch sequence of each entry point.
+#include "invariant_logp.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxTiles = 4096;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Chunks per lane for a supported (dtype, tile width), else 0.
+int chunks_for(int32_t dtype, int32_t w) {
+  const int per = dtype == LOGP_BF16 ? 512 : 256;  // one 16-byte chunk per lane
+  if (w < per || w % per) return 0;
+  const int c = w / per;
+  return (c == 1 || c == 2 || c == 4 || c == 8 || c == 16) ? c : 0;
+}
+
+int elt_size(int32_t dtype) { return dtype == LOGP_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p, int64_t ld, int32_t dtype) {
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * elt_size(dtype)) % 16 == 0);
+}
+
+// Common checks of logp_fwd / logp_bwd that involve no pointer.
+int32_t check_stream_args(int32_t dtype, int64_t n, int64_t v, int64_t ld, int32_t w) {
+  if (dtype != LOGP_F32 && dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
+  if (n < 0 || v < 1 || ld < v) return LOGP_ERR_SHAPE;
+  if (chunks_for(dtype, w) == 0) return LOGP_ERR_TILE;
+  if ((v + w - 1) / w > kMaxTiles) return LOGP_ERR_SHAPE;
+  return LOGP_OK;
+}
+
+// Workspace layout of logp_fwd: [status block | pm (T*n) | ps (T*n) | pt (n)].
+struct FwdLayout {
+  size_t pm, ps, pt, total;
+};
+
+FwdLayout fwd_layout(int64_t n, int64_t ntiles, int32_t shards, int32_t validate) {
+  FwdLayout l{0, 0, 0, 0};
+  if (shards == 1) {
+    l.total = validate ? kAlign : 0;
+    return l;
+  }
+  const size_t table = round_up(static_cast<size_t>(ntiles) * static_cast<size_t>(n) * sizeof(float));
+  l.pm = kAlign;
+  l.ps = l.pm + table;
+  l.pt = l.ps + table;
+  l.total = l.pt + round_up(static_cast<size_t>(n) * sizeof(float));
+  return l;
+}
+
+int32_t hip_status() {
+  return hipGetLastError() == hipSuccess ? LOGP_OK : LOGP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width, int32_t num_shards,
+                                int32_t validate) {
+  if (check_stream_args(LOGP_BF16, n, v, v, tile_width) != LOGP_OK &&
+      check_stream_args(LOGP_F32, n, v, v, tile_width) != LOGP_OK)
+    return 0;
+  if (num_shards < 1 || v % num_shards) return 0;
+  return fwd_layout(n, (v + tile_width - 1) / tile_width, num_shards, validate).total;
+}
+
+int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_t ld,
+                 const int64_t* targets, int64_t ignore_index, int32_t tile_width,
+                 int32_t num_shards, int32_t validate, float* logp_out, float* lse_out,
+                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int32_t st = check_stream_args(dtype, n, v, ld, tile_width);
+  if (st != LOGP_OK) return st;
+  if (num_shards < 1 || v % num_shards) return LOGP_ERR_SHARDS;
+  const int ntiles = static_cast<int>((v + tile_width - 1) / tile_width);
+  const FwdLayout lay = fwd_layout(n, ntiles, num_shards, validate);
+  if (n == 0) return LOGP_OK;
+  if (!logits || !targets || !logp_out) return LOGP_ERR_NULL;
+  if (lay.total) {
+    if (!workspace || workspace_bytes < lay.total ||
+        reinterpret_cast<uintptr_t>(workspace) % kAlign)
+      return LOGP_ERR_WORKSPACE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  int* status = validate ? reinterpret_cast<int*>(ws) : nullptr;
+  const int chunks = chunks_for(dtype, tile_width);
+  const bool vec = aligned16(logits, ld, dtype);
+  (void)hipGetLastError();
+  if (status && hipMemsetAsync(status, 0, sizeof(int), s) != hipSuccess) return LOGP_ERR_HIP;
+  if (num_shards == 1) {
+    itl::launch_fwd_fused(dtype, vec, chunks, logits, ld, n, v, targets, ignore_index, ntiles,
+                          logp_out, lse_out, status, s);
+  } else {
+    float* pm = reinterpret_cast<float*>(ws + lay.pm);
+    float* ps = reinterpret_cast<float*>(ws + lay.ps);
+    float* pt = reinterpret_cast<float*>(ws + lay.pt);
+    const int64_t per = v / num_shards;
+    for (int32_t sh = 0; sh < num_shards; ++sh) {
+      // Shard sh owns the tiles whose first column lies in [sh*per, (sh+1)*per).
+      const int kb = static_cast<int>((sh * per + tile_width - 1) / tile_width);
+      const int ke = static_cast<int>(((sh + 1) * per + tile_width - 1) / tile_width);
+      if (ke > kb)
+        itl::launch_fwd_partials(dtype, vec, chunks, logits, ld, n, v, targets, ignore_index, kb,
+                                 ke, pm, ps, pt, s);
+    }
+    itl::launch_fwd_merge(pm, ps, pt, n, ntiles, v, targets, ignore_index, logp_out, lse_out,
+                          status, s);
+  }
+  st = hip_status();
+  if (st != LOGP_OK) return st;
+  if (status) {
+    int flag = 0;
+    if (hipMemcpyAsync(&flag, status, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return LOGP_ERR_HIP;
+    if (flag) return LOGP_ERR_TARGET;
+  }
+  return LOGP_OK;
+}
+
+int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_t ld,
+                 const int64_t* targets, int64_t ignore_index, int32_t tile_width,
+                 const float* lse, const float* grad_logp, void* dlogits_out, int64_t ld_out,
+                 void* hip_stream) {
+  int32_t st = check_stream_args(dtype, n, v, ld, tile_width);
+  if (st != LOGP_OK) return st;
+  if (ld_out < v) return LOGP_ERR_SHAPE;
+  if (n == 0) return LOGP_OK;
+  if (!logits || !targets || !lse || !grad_logp || !dlogits_out) return LOGP_ERR_NULL;
+  const bool vec = aligned16(logits, ld, dtype) && aligned16(dlogits_out, ld_out, dtype);
+  (void)hipGetLastError();
+  itl::launch_bwd(dtype, vec, logits, ld, n, v, targets, ignore_index, lse, grad_logp,
+                  dlogits_out, ld_out, static_cast<hipStream_t>(hip_stream));
+  return hip_status();
+}
+
+size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width) {
+  if (n < 0 || v < 1 || tile_width != itl::kLinearTile) return 0;
+  const int64_t ntiles = (v + tile_width - 1) / tile_width;
+  return fwd_layout(n, ntiles, 2, 0).total;
+}
+
+int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                        int64_t n, int64_t h, int64_t v, const int64_t* targets,
+                        int64_t ignore_index, int32_t tile_width, float* logp_out,
+                        float* lse_out, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
+  if (n < 0 || v < 1 || h < 1 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
+  if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
+  const int64_t ntiles = (v + tile_width - 1) / tile_width;
+  if (ntiles > (int64_t{1} << 24) || (n + 127) / 128 * ntiles > (int64_t{1} << 30))
+    return LOGP_ERR_SHAPE;
+  const FwdLayout lay = fwd_layout(n, ntiles, 2, 0);
+  if (n == 0) return LOGP_OK;
+  if (!hidden || !weight || !targets || !logp_out) return LOGP_ERR_NULL;
+  if (!aligned16(hidden, ld_h, LOGP_BF16) || !aligned16(weight, ld_w, LOGP_BF16))
+    return LOGP_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lay.total ||
+      reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return LOGP_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  float* pm = reinterpret_cast<float*>(ws + lay.pm);
+  float* ps = reinterpret_cast<float*>(ws + lay.ps);
+  float* pt = reinterpret_cast<float*>(ws + lay.pt);
+  (void)hipGetLastError();
+  itl::launch_linear_partials(static_cast<const uint16_t*>(hidden), ld_h,
+                              static_cast<const uint16_t*>(weight), ld_w, n, h, v, targets,
+                              ignore_index, pm, ps, pt, s);
+  itl::launch_fwd_merge(pm, ps, pt, n, static_cast<int>(ntiles), v, targets, ignore_index,
+                        logp_out, lse_out, nullptr, s);
+  return hip_status();
+}
+
+const char* logp_status_str(int32_t status) {
+  switch (status) {
+    case LOGP_OK: return "ok";
+    case LOGP_ERR_NULL: return "a required pointer is NULL";
+    case LOGP_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case LOGP_ERR_DTYPE: return "unknown dtype";
+    case LOGP_ERR_TILE: return "unsupported tile width";
+    case LOGP_ERR_ALIGN: return "operand rows are not 16-byte aligned";
+    case LOGP_ERR_SHARDS: return "num_shards must be >= 1 and divide v";
+    case LOGP_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case LOGP_ERR_TARGET: return "an active target lies outside [0, v)";
+    case LOGP_ERR_HIP: return "HIP launch or copy failed";
+    default: return "unknown status";
+  }
+}
+
+const char* logp_contract_id(void) {
+  return "itl.logp.v1[tile=lane-asc-fold+xor1..32;tilestat=two-pass;merge=asc-fma;"
+         "exp=v_exp_f32((a-b)*log2e);log=v_log_f32*ln2;bwd=rne(g*(onehot-p))]"
+         "+itl.linear_logp.v1[mfma=f32_16x16x32_bf16;k=asc32-nosplit;tile=256;"
+         "tilestat=lane-asc-fold8+xor1..8+half0+half1]/gfx950";
+}
+
+}  // extern "C"

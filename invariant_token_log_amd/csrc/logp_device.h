@@ -1,0 +1,163 @@
+// Device arithmetic shared by every kernel of the logp contract.
+//
+// The tile statistic, the wave reductions, the exp/log primitives and the
+// fixed-order merge live here once, so that the single-launch forward, the
+// shard-partial kernel, the merge kernel, the backward and the fused LM-head
+// epilogue all perform the same floating-point operations in the same order
+// ("Batch-Invariant LogP", Tensor Parallel: every tile is reduced as the same
+// contiguous shape on any rank and every rank merges in the same fixed
+// order).  Built with -ffp-contract=off: every fused multiply-add below is an
+// explicit fmaf, nothing else is contracted or reassociated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace itl {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// e^(a - b) as 2^((a - b) * log2 e) on the hardware base-2 exponential
+// (v_exp_f32).  The subtraction comes first, so the row maximum gives exactly
+// 2^0 = 1: every tile that holds its own maximum has s >= 1, the merged sum is
+// >= 1 and log(sum) >= 0, hence logp <= 0 on every active row.
+__device__ __forceinline__ float exp_sub(float a, float b) {
+  return __builtin_amdgcn_exp2f((a - b) * kLog2e);
+}
+
+// Natural log as log2 (v_log_f32) times ln 2.  Only called on sums >= 1.
+__device__ __forceinline__ float log_nat(float a) {
+  return __builtin_amdgcn_logf(a) * kLn2;
+}
+
+// XOR butterfly over the 64 lanes of a wave, offsets 1, 2, 4, ..., 32.  Every
+// lane ends with the same value: at each level both partners add the same
+// two operands (addition commutes exactly).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) x = x + __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Element access.  bf16 is carried as its raw 16 bits; widening to fp32 is a
+// 16-bit left shift and exact.
+// ---------------------------------------------------------------------------
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static constexpr int kPerChunk = 4;  // 16 bytes
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+};
+template <> struct Elt<uint16_t> {
+  static constexpr int kPerChunk = 8;  // 16 bytes
+  __device__ static float load(const uint16_t* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+  }
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Widen one 16-byte chunk that starts at element c of a row; elements at or
+// beyond v become -inf and are not read.  VEC: the chunk start is 16-byte
+// aligned, so a whole chunk is one 128-bit load.
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_chunk(const T* row, int64_t c, int64_t v,
+                                           float (&x)[Elt<T>::kPerChunk]) {
+  constexpr int E = Elt<T>::kPerChunk;
+  if (VEC && c + E <= v) {
+    const uint4 q = *reinterpret_cast<const uint4*>(row + c);
+    if constexpr (E == 4) {
+      x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
+      x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
+    } else {
+      x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x);
+      x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
+      x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z);
+      x[6] = bf16_lo(q.w); x[7] = bf16_hi(q.w);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      x[e] = (c + e < v) ? Elt<T>::load(row, c + e) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tile statistic ("Batch-Invariant LogP", Tensor Parallel, step 2): one wave
+// reduces the W = C * 64 * E columns [col0, col0 + W) of one row to
+//   m = max x,   s = sum exp(x - m)   (fp32, two passes over registers).
+// Layout: lane l holds chunks j = 0..C-1 covering the tile-local elements
+// [(j * 64 + l) * E, +E), so every chunk load is one coalesced 1 KiB wave
+// access.  Summation tree: each lane folds its C * E terms in ascending
+// tile-local column order (chunk by chunk, element by element) starting from
+// +0, then the xor butterfly adds across lanes.  The tree depends only on the
+// column index inside the tile, on W and on the dtype.  Padding columns
+// (>= v) contribute exp(-inf) = +0, which leaves every partial sum unchanged.
+// ---------------------------------------------------------------------------
+template <typename T, int C, bool VEC>
+__device__ __forceinline__ void tile_stats(const T* row, int64_t col0, int64_t v,
+                                           float& m_out, float& s_out) {
+  constexpr int E = Elt<T>::kPerChunk;
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int W = C * kWave * E;
+  float x[C][E];
+  if (VEC && col0 + W <= v) {
+    // Whole tile inside the row: unguarded 128-bit loads.
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      load_chunk<T, true>(row, col0 + static_cast<int64_t>(j * kWave + lane) * E, INT64_MAX, x[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      load_chunk<T, VEC>(row, col0 + static_cast<int64_t>(j * kWave + lane) * E, v, x[j]);
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < C; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = fmaxf(m, x[j][e]);
+  m = wave_max(m);
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < C; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) s = s + exp_sub(x[j][e], m);
+  m_out = m;
+  s_out = wave_sum(s);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-order merge ("Batch-Invariant LogP", Tensor Parallel, step 4):
+//   M = max_k m_k;  acc = +0;  for k = 0 .. T-1:  acc = fma(s_k, e^(m_k - M), acc)
+//   (tiles with m_k = -inf skipped: they hold no column);  LSE = M + log(acc).
+// Partials are read at m[k * stride], s[k * stride].
+// ---------------------------------------------------------------------------
+template <typename P>
+__device__ __forceinline__ float merge_lse(P m, P s, int ntiles, int64_t stride) {
+  float big_m = -INFINITY;
+  for (int k = 0; k < ntiles; ++k) big_m = fmaxf(big_m, m[k * stride]);
+  float acc = 0.0f;
+  for (int k = 0; k < ntiles; ++k) {
+    const float mk = m[k * stride];
+    if (mk != -INFINITY) acc = fmaf(s[k * stride], exp_sub(mk, big_m), acc);
+  }
+  return big_m + log_nat(acc);
+}
+
+// Final combine (step 6): logp = target_logit - LSE, or NaN for an active row
+// whose target lies outside [0, v).
+__device__ __forceinline__ float combine(float target_logit, float lse, bool valid) {
+  return valid ? target_logit - lse : __uint_as_float(0x7fc00000u);
+}
+
+}  // namespace itl

@@ -1,0 +1,309 @@
+// Streaming kernels of the logp contract on gfx950: the single-launch
+// forward, the shard-partial forward, the fixed-order merge and the
+// tile-wise backward.  Host-side argument checks live in api.hip; the
+// launchers here assume valid arguments.
+#include "launch.h"
+#include "logp_device.h"
+
+namespace itl {
+
+constexpr int kBlock = 256;               // 4 waves
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int64_t kMaxRowBlocks = 1 << 20;  // grid-stride beyond this
+
+// ---------------------------------------------------------------------------
+// Single-launch forward ("Batch-Invariant LogP", Tensor Parallel with one
+// shard).  One workgroup per row (grid-stride over rows); wave w reduces the
+// tiles k = w, w + 4, ... and parks (m_k, s_k) in LDS; thread 0 merges them in
+// ascending order, copies the target logit and writes logp and lse.  Ignored
+// rows are not read.
+// ---------------------------------------------------------------------------
+template <typename T, int C, bool VEC>
+__global__ __launch_bounds__(kBlock) void logp_fwd_fused_kernel(
+    const T* __restrict__ logits, int64_t ld, int64_t n, int64_t v,
+    const int64_t* __restrict__ targets, int64_t ignore_index, int ntiles,
+    float* __restrict__ logp, float* __restrict__ lse, int* __restrict__ status) {
+  extern __shared__ float lds[];
+  float* lm = lds;
+  float* ls = lds + ntiles;
+  constexpr int W = C * kWave * Elt<T>::kPerChunk;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    const int64_t t = targets[r];
+    if (t == ignore_index) {
+      if (threadIdx.x == 0) {
+        logp[r] = 0.0f;
+        if (lse) lse[r] = 0.0f;
+      }
+      continue;
+    }
+    const T* row = logits + r * ld;
+    for (int k = wave; k < ntiles; k += kWavesPerBlock) {
+      float mk, sk;
+      tile_stats<T, C, VEC>(row, static_cast<int64_t>(k) * W, v, mk, sk);
+      if (lane == 0) {
+        lm[k] = mk;
+        ls[k] = sk;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const float L = merge_lse(lm, ls, ntiles, 1);
+      const bool valid = t >= 0 && t < v;
+      const float xt = valid ? Elt<T>::load(row, t) : 0.0f;
+      logp[r] = combine(xt, L, valid);
+      if (lse) lse[r] = L;
+      if (!valid && status) status[0] = 1;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shard partials: the same tile statistic over the tiles [k_begin, k_end) a
+// shard owns, written to the [T, n] tables pm / ps (tile-major, so the merge
+// reads them coalesced).  The owner of the target's tile copies the target
+// logit into pt[r].  Ignored rows are skipped (the merge never reads them).
+// ---------------------------------------------------------------------------
+template <typename T, int C, bool VEC>
+__global__ __launch_bounds__(kBlock) void logp_partials_kernel(
+    const T* __restrict__ logits, int64_t ld, int64_t n, int64_t v,
+    const int64_t* __restrict__ targets, int64_t ignore_index, int k_begin,
+    int k_end, float* __restrict__ pm, float* __restrict__ ps,
+    float* __restrict__ pt) {
+  constexpr int W = C * kWave * Elt<T>::kPerChunk;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    const int64_t t = targets[r];
+    if (t == ignore_index) continue;
+    const T* row = logits + r * ld;
+    for (int k = k_begin + wave; k < k_end; k += kWavesPerBlock) {
+      float mk, sk;
+      tile_stats<T, C, VEC>(row, static_cast<int64_t>(k) * W, v, mk, sk);
+      if (lane == 0) {
+        pm[static_cast<int64_t>(k) * n + r] = mk;
+        ps[static_cast<int64_t>(k) * n + r] = sk;
+      }
+    }
+    if (threadIdx.x == 0 && t >= 0 && t < v &&
+        t >= static_cast<int64_t>(k_begin) * W && t < static_cast<int64_t>(k_end) * W)
+      pt[r] = Elt<T>::load(row, t);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the gathered [T, n] partials: one lane per row, the same
+// merge_lse and combine as the single-launch forward.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void logp_merge_kernel(
+    const float* __restrict__ pm, const float* __restrict__ ps,
+    const float* __restrict__ pt, int64_t n, int ntiles, int64_t v,
+    const int64_t* __restrict__ targets, int64_t ignore_index,
+    float* __restrict__ logp, float* __restrict__ lse, int* __restrict__ status) {
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < n;
+       r += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = targets[r];
+    if (t == ignore_index) {
+      logp[r] = 0.0f;
+      if (lse) lse[r] = 0.0f;
+      continue;
+    }
+    const float L = merge_lse(pm + r, ps + r, ntiles, n);
+    const bool valid = t >= 0 && t < v;
+    logp[r] = combine(valid ? pt[r] : 0.0f, L, valid);
+    if (lse) lse[r] = L;
+    if (!valid && status) status[0] = 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward ("Batch-Invariant LogP", Batch-Invariance: one program per row
+// tile reusing the forward's lse, no cross-row reduction).
+//   p = exp(x - lse);  u = 1 - p on the target column, -p elsewhere;
+//   d = g * u rounded to the logits dtype (RNE).
+// g * (-p) is computed as (-g) * p, which is the same IEEE product.
+// One workgroup per row (grid-stride); each thread moves 16-byte chunks, four
+// in flight.  Ignored rows are written +0 without reading the logits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo);
+  const __bf16 b = static_cast<__bf16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+template <typename T> __device__ __forceinline__ void store_elem(T* p, int64_t i, float d);
+template <> __device__ __forceinline__ void store_elem<float>(float* p, int64_t i, float d) { p[i] = d; }
+template <> __device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, int64_t i, float d) {
+  p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(d));
+}
+
+__device__ __forceinline__ float grad_elem(float x, float L, float g, float ng, bool is_target) {
+  const float p = exp_sub(x, L);
+  return is_target ? g * (1.0f - p) : ng * p;
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 grad_chunk(const uint4 q, float L, float g, float ng,
+                                            int64_t c, int64_t t) {
+  constexpr int E = Elt<T>::kPerChunk;
+  float x[E];
+  if constexpr (E == 4) {
+    x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
+    x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
+  } else {
+    x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x); x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
+    x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z); x[6] = bf16_lo(q.w); x[7] = bf16_hi(q.w);
+  }
+  float d[E];
+  if (t >= c && t < c + E) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) d[e] = grad_elem(x[e], L, g, ng, c + e == t);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) d[e] = ng * exp_sub(x[e], L);
+  }
+  uint4 o;
+  if constexpr (E == 4) {
+    o.x = __float_as_uint(d[0]); o.y = __float_as_uint(d[1]);
+    o.z = __float_as_uint(d[2]); o.w = __float_as_uint(d[3]);
+  } else {
+    o.x = pack_bf16(d[0], d[1]); o.y = pack_bf16(d[2], d[3]);
+    o.z = pack_bf16(d[4], d[5]); o.w = pack_bf16(d[6], d[7]);
+  }
+  return o;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kBlock) void logp_bwd_kernel(
+    const T* logits, int64_t ld, int64_t n, int64_t v,
+    const int64_t* __restrict__ targets, int64_t ignore_index,
+    const float* __restrict__ lse, const float* __restrict__ grad, T* dlogits,
+    int64_t ld_out) {
+  constexpr int E = Elt<T>::kPerChunk;
+  constexpr int U = 4;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    const int64_t t = targets[r];
+    T* orow = dlogits + r * ld_out;
+    const int64_t nchunk = VEC ? v / E : 0;
+    if (t == ignore_index) {
+      for (int64_t c = threadIdx.x; c < nchunk; c += kBlock)
+        *reinterpret_cast<uint4*>(orow + c * E) = make_uint4(0u, 0u, 0u, 0u);
+      for (int64_t j = nchunk * E + threadIdx.x; j < v; j += kBlock) store_elem<T>(orow, j, 0.0f);
+      continue;
+    }
+    const T* row = logits + r * ld;
+    const float L = lse[r];
+    const float g = grad[r];
+    const float ng = -g;
+    for (int64_t c0 = threadIdx.x; c0 < nchunk; c0 += kBlock * U) {
+      uint4 q[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * kBlock;
+        if (c < nchunk) q[u] = *reinterpret_cast<const uint4*>(row + c * E);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * kBlock;
+        if (c < nchunk)
+          *reinterpret_cast<uint4*>(orow + c * E) = grad_chunk<T>(q[u], L, g, ng, c * E, t);
+      }
+    }
+    for (int64_t j = nchunk * E + threadIdx.x; j < v; j += kBlock)
+      store_elem<T>(orow, j, grad_elem(Elt<T>::load(row, j), L, g, ng, j == t));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static unsigned row_grid(int64_t n) {
+  return static_cast<unsigned>(n < kMaxRowBlocks ? n : kMaxRowBlocks);
+}
+
+template <typename T, bool VEC>
+static void fused_dispatch(int chunks, const void* logits, int64_t ld, int64_t n, int64_t v,
+                           const int64_t* targets, int64_t ignore, int ntiles, float* logp,
+                           float* lse, int* status, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(ntiles) * 2 * sizeof(float);
+  const T* x = static_cast<const T*>(logits);
+#define ITL_FUSED(CC)                                                                   \
+  case CC:                                                                              \
+    hipLaunchKernelGGL((logp_fwd_fused_kernel<T, CC, VEC>), dim3(row_grid(n)),          \
+                       dim3(kBlock), lds, s, x, ld, n, v, targets, ignore, ntiles, logp, \
+                       lse, status);                                                    \
+    break;
+  switch (chunks) { ITL_FUSED(1) ITL_FUSED(2) ITL_FUSED(4) ITL_FUSED(8) ITL_FUSED(16) }
+#undef ITL_FUSED
+}
+
+template <typename T, bool VEC>
+static void partials_dispatch(int chunks, const void* logits, int64_t ld, int64_t n,
+                              int64_t v, const int64_t* targets, int64_t ignore, int kb,
+                              int ke, float* pm, float* ps, float* pt, hipStream_t s) {
+  const T* x = static_cast<const T*>(logits);
+#define ITL_PART(CC)                                                                     \
+  case CC:                                                                               \
+    hipLaunchKernelGGL((logp_partials_kernel<T, CC, VEC>), dim3(row_grid(n)),            \
+                       dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, kb, ke, pm, ps, \
+                       pt);                                                              \
+    break;
+  switch (chunks) { ITL_PART(1) ITL_PART(2) ITL_PART(4) ITL_PART(8) ITL_PART(16) }
+#undef ITL_PART
+}
+
+void launch_fwd_fused(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
+                      int64_t n, int64_t v, const int64_t* targets, int64_t ignore,
+                      int ntiles, float* logp, float* lse, int* status, hipStream_t s) {
+  if (dtype == kF32) {
+    if (vec) fused_dispatch<float, true>(chunks, logits, ld, n, v, targets, ignore, ntiles, logp, lse, status, s);
+    else fused_dispatch<float, false>(chunks, logits, ld, n, v, targets, ignore, ntiles, logp, lse, status, s);
+  } else {
+    if (vec) fused_dispatch<uint16_t, true>(chunks, logits, ld, n, v, targets, ignore, ntiles, logp, lse, status, s);
+    else fused_dispatch<uint16_t, false>(chunks, logits, ld, n, v, targets, ignore, ntiles, logp, lse, status, s);
+  }
+}
+
+void launch_fwd_partials(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
+                         int64_t n, int64_t v, const int64_t* targets, int64_t ignore,
+                         int k_begin, int k_end, float* pm, float* ps, float* pt,
+                         hipStream_t s) {
+  if (dtype == kF32) {
+    if (vec) partials_dispatch<float, true>(chunks, logits, ld, n, v, targets, ignore, k_begin, k_end, pm, ps, pt, s);
+    else partials_dispatch<float, false>(chunks, logits, ld, n, v, targets, ignore, k_begin, k_end, pm, ps, pt, s);
+  } else {
+    if (vec) partials_dispatch<uint16_t, true>(chunks, logits, ld, n, v, targets, ignore, k_begin, k_end, pm, ps, pt, s);
+    else partials_dispatch<uint16_t, false>(chunks, logits, ld, n, v, targets, ignore, k_begin, k_end, pm, ps, pt, s);
+  }
+}
+
+void launch_fwd_merge(const float* pm, const float* ps, const float* pt, int64_t n,
+                      int ntiles, int64_t v, const int64_t* targets, int64_t ignore,
+                      float* logp, float* lse, int* status, hipStream_t s) {
+  int64_t blocks = (n + kBlock - 1) / kBlock;
+  if (blocks > kMaxRowBlocks) blocks = kMaxRowBlocks;
+  hipLaunchKernelGGL(logp_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                     s, pm, ps, pt, n, ntiles, v, targets, ignore, logp, lse, status);
+}
+
+void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, int64_t v,
+                const int64_t* targets, int64_t ignore, const float* lse, const float* grad,
+                void* dlogits, int64_t ld_out, hipStream_t s) {
+  const dim3 grid(row_grid(n));
+  if (dtype == kF32) {
+    const float* x = static_cast<const float*>(logits);
+    float* d = static_cast<float*>(dlogits);
+    if (vec) hipLaunchKernelGGL((logp_bwd_kernel<float, true>), grid, dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, lse, grad, d, ld_out);
+    else hipLaunchKernelGGL((logp_bwd_kernel<float, false>), grid, dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, lse, grad, d, ld_out);
+  } else {
+    const uint16_t* x = static_cast<const uint16_t*>(logits);
+    uint16_t* d = static_cast<uint16_t*>(dlogits);
+    if (vec) hipLaunchKernelGGL((logp_bwd_kernel<uint16_t, true>), grid, dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, lse, grad, d, ld_out);
+    else hipLaunchKernelGGL((logp_bwd_kernel<uint16_t, false>), grid, dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, lse, grad, d, ld_out);
+  }
+}
+
+}  // namespace itl

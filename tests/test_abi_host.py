@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/*.h, and rejects bad arguments on the host with the
+documented status before any HIP call (so nothing here touches a device)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import invariant_token_log_amd as itl
+from invariant_token_log_amd import _lib
+from invariant_token_log_amd.build import LIB_PATH, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB_PATH):
+        build()
+    return _lib.lib()
+
+
+def _declared_functions():
+    names = []
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \t\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert {"logp_fwd", "logp_bwd", "linear_logp_fwd"} <= set(names)
+    raw = ctypes.CDLL(LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+    assert set(names) == set(_lib._SIGNATURES)
+
+
+def test_strings(L):
+    assert itl.status_str(0) == "ok"
+    assert "tile" in itl.status_str(_lib.LOGP_ERR_TILE)
+    assert itl.status_str(99) == "unknown status"
+    cid = itl.contract_id()
+    assert cid.startswith("itl.logp.v1[") and "gfx950" in cid
+
+
+FAKE = 0x10000  # a non-NULL address that the checks never dereference
+
+
+def _fwd(L, logits=FAKE, dtype=1, n=4, v=151936, ld=None, targets=FAKE, w=4096, shards=1,
+         validate=0, logp=FAKE, lse=FAKE, ws=None, ws_bytes=0):
+    return L.logp_fwd(logits, dtype, n, v, v if ld is None else ld, targets, -100, w, shards,
+                      validate, logp, lse, ws, ws_bytes, None)
+
+
+def test_fwd_argument_errors(L):
+    assert _fwd(L, dtype=2) == _lib.LOGP_ERR_DTYPE
+    assert _fwd(L, n=-1) == _lib.LOGP_ERR_SHAPE
+    assert _fwd(L, v=0) == _lib.LOGP_ERR_SHAPE
+    assert _fwd(L, ld=100) == _lib.LOGP_ERR_SHAPE
+    for w in (0, 256, 1000, 1536, 3072, 16384):
+        assert _fwd(L, w=w) == _lib.LOGP_ERR_TILE, w
+    assert _fwd(L, dtype=0, w=128, v=4096) == _lib.LOGP_ERR_TILE
+    assert _fwd(L, v=512 * 4097, w=512) == _lib.LOGP_ERR_SHAPE  # T > 4096
+    assert _fwd(L, shards=0) == _lib.LOGP_ERR_SHARDS
+    assert _fwd(L, shards=3) == _lib.LOGP_ERR_SHARDS  # 151936 % 3 != 0
+    assert _fwd(L, logits=None) == _lib.LOGP_ERR_NULL
+    assert _fwd(L, targets=None) == _lib.LOGP_ERR_NULL
+    assert _fwd(L, logp=None) == _lib.LOGP_ERR_NULL
+    assert _fwd(L, shards=2) == _lib.LOGP_ERR_WORKSPACE
+    need = L.logp_fwd_workspace_bytes(4, 151936, 4096, 2, 0)
+    assert _fwd(L, shards=2, ws=FAKE, ws_bytes=need - 1) == _lib.LOGP_ERR_WORKSPACE
+    assert _fwd(L, shards=2, ws=FAKE + 16, ws_bytes=need) == _lib.LOGP_ERR_WORKSPACE
+    assert _fwd(L, validate=1) == _lib.LOGP_ERR_WORKSPACE
+    # n = 0 is a no-op that succeeds without touching any pointer
+    assert _fwd(L, n=0, logits=None, targets=None, logp=None) == _lib.LOGP_OK
+
+
+def test_fwd_workspace_sizes(L):
+    n, v = 8192, 151936
+    assert L.logp_fwd_workspace_bytes(n, v, 4096, 1, 0) == 0
+    assert L.logp_fwd_workspace_bytes(n, v, 4096, 1, 1) == 256
+    table = -(-(38 * n * 4) // 256) * 256
+    rows = -(-(n * 4) // 256) * 256
+    for s in (2, 4):
+        assert L.logp_fwd_workspace_bytes(n, v, 4096, s, 0) == 256 + 2 * table + rows
+    assert L.logp_fwd_workspace_bytes(n, v, 1000, 1, 0) == 0  # rejected tile
+    assert L.logp_fwd_workspace_bytes(n, v, 4096, 3, 0) == 0  # rejected shards
+
+
+def test_bwd_argument_errors(L):
+    def bwd(**kw):
+        a = dict(logits=FAKE, dtype=1, n=4, v=151936, ld=151936, targets=FAKE, w=4096,
+                 lse=FAKE, g=FAKE, d=FAKE, ld_out=151936)
+        a.update(kw)
+        return L.logp_bwd(a["logits"], a["dtype"], a["n"], a["v"], a["ld"], a["targets"],
+                          -100, a["w"], a["lse"], a["g"], a["d"], a["ld_out"], None)
+    assert bwd(dtype=5) == _lib.LOGP_ERR_DTYPE
+    assert bwd(ld_out=10) == _lib.LOGP_ERR_SHAPE
+    assert bwd(w=100) == _lib.LOGP_ERR_TILE
+    for k in ("logits", "targets", "lse", "g", "d"):
+        assert bwd(**{k: None}) == _lib.LOGP_ERR_NULL, k
+    assert bwd(n=0, logits=None, d=None) == _lib.LOGP_OK
+
+
+def test_linear_argument_errors(L):
+    def lin(**kw):
+        a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
+                 targets=FAKE, tile=256, logp=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        return L.linear_logp_fwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
+                                 a["v"], a["targets"], -100, a["tile"], a["logp"], a["lse"],
+                                 a["ws"], a["ws_bytes"], None)
+    assert lin(tile=4096) == _lib.LOGP_ERR_TILE
+    assert lin(h=100, ld_h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
+    assert lin(ld_h=10) == _lib.LOGP_ERR_SHAPE
+    assert lin(h_ptr=None) == _lib.LOGP_ERR_NULL
+    assert lin(h_ptr=FAKE + 2) == _lib.LOGP_ERR_ALIGN
+    assert lin(ld_w=4100) == _lib.LOGP_ERR_ALIGN
+    assert lin(ws_bytes=16) == _lib.LOGP_ERR_WORKSPACE
+    assert lin(n=0, h_ptr=None, w_ptr=None) == _lib.LOGP_OK
+    need = L.linear_logp_fwd_workspace_bytes(8, 151936, 256)
+    assert need == 256 + 2 * 256 * (-(-(594 * 8 * 4) // 256)) + 256
+    assert L.linear_logp_fwd_workspace_bytes(8, 151936, 512) == 0

@@ -1,0 +1,88 @@
+"""GPU parity and invariance of the fused LM-head + logp against the float64
+oracle ("[RFC][ROCm] End-to-end optimization of bitwise VIME R/R beyond
+native P/P", Workstream 3)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_token_log_amd as itl
+import oracle
+import synth
+from gpu_helpers import assert_logp_parity, bits, dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(h, w, t, ignore_index=-100):
+    return oracle.linear_logp_fwd(h.float().cpu().numpy(), w.float().cpu().numpy(),
+                                  t.cpu().numpy(), ignore_index)
+
+
+@pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (200, 128, 1000), (1, 64, 256),
+                                    (129, 512, 2 * 256 + 17), (300, 4096, 4096)])
+def test_tiny_brute(n, hd, v):
+    """Small problems with ragged N (not a multiple of 128) and ragged V."""
+    c = synth.qwen3_linear(seed=n + v, n=n, h=hd, v=v, device=dev(), ignore_frac=0.05)
+    logp, lse = itl.linear_logp_fwd(c["hidden"], c["weight"], c["targets"])
+    ref = _oracle(c["hidden"], c["weight"], c["targets"])
+    assert_logp_parity(logp, lse, *ref, c["targets"], what=f"linear {n} {hd} {v}")
+
+
+def test_identity_weight_matches_logp():
+    """W = I (V = H): z = h exactly in fp32 under any K order, so the fused
+    result matches the oracle's logp of h itself."""
+    n, hd = 96, 256
+    h = synth.normal_matrix(n, hd, 3.0, torch.bfloat16, seed=1).to(dev())
+    w = torch.eye(hd, dtype=torch.bfloat16, device=dev())
+    t = synth.uniform_targets(n, hd, seed=2, ignore_rows=torch.tensor([4])).to(dev())
+    logp, lse = itl.linear_logp_fwd(h, w, t)
+    ref = oracle.logp_fwd(h.float().cpu().numpy(), t.cpu().numpy())
+    assert_logp_parity(logp, lse, *ref, t, what="identity")
+
+
+@pytest.mark.parametrize("v", [256, 1000, synth.QWEN3_VOCAB])
+def test_zero_weight_is_minus_log_v(v):
+    """W = 0: every z is 0, the sums are exact integers, and the result has
+    the same bits as logp_fwd on a zero row."""
+    n, hd = 8, 64
+    h = synth.normal_matrix(n, hd, 1.0, torch.bfloat16, seed=3).to(dev())
+    w = torch.zeros(v, hd, dtype=torch.bfloat16, device=dev())
+    t = torch.arange(n, device=dev()) * (v // n)
+    logp, lse = itl.linear_logp_fwd(h, w, t)
+    want = np.float32(-math.log(v))
+    assert (np.abs(to_np(logp) - float(want)) <= 2 * float(np.spacing(want))).all()
+    zrow = torch.zeros(n, v, dtype=torch.float32, device=dev())
+    lz, sz = itl.logp_fwd(zrow, t, -100, 256)
+    assert torch.equal(bits(logp), bits(lz)) and torch.equal(bits(lse), bits(sz))
+
+
+def test_row_invariance():
+    """A row's z, statistics and logp do not depend on N, its position in the
+    128-row block, or its neighbours."""
+    c = synth.qwen3_linear(seed=44, n=300, h=512, v=5000, device=dev())
+    h, w, t = c["hidden"], c["weight"], c["targets"]
+    base, _ = itl.linear_logp_fwd(h, w, t)
+    b0 = bits(base)
+    for r in [0, 5, 127, 128, 299]:
+        lr, _ = itl.linear_logp_fwd(h[r:r + 1].contiguous(), w, t[r:r + 1].contiguous())
+        assert torch.equal(bits(lr), b0[r:r + 1]), r
+    perm = torch.randperm(300, generator=torch.Generator().manual_seed(0)).to(dev())
+    lp, _ = itl.linear_logp_fwd(h[perm].contiguous(), w, t[perm].contiguous())
+    assert torch.equal(bits(lp), b0[perm.cpu()])
+    again, _ = itl.linear_logp_fwd(h, w, t)
+    assert torch.equal(bits(again), b0)
+
+
+def test_full_size_sampled():
+    """Qwen3-8B LM head (N = 4096, H = 4096, V = 151936) at the benchmarked
+    launch: 48 sampled rows against the float64 oracle."""
+    c = synth.qwen3_linear(device=dev())
+    h, w, t = c["hidden"], c["weight"], c["targets"]
+    logp, lse = itl.linear_logp_fwd(h, w, t)
+    rows = torch.tensor(list(range(0, 4096, 89)) + [4095], device=dev())
+    ref = _oracle(h[rows], w, t[rows])
+    assert_logp_parity(logp[rows], lse[rows], *ref, t[rows], what="linear full")
+    assert torch.isfinite(logp).all()

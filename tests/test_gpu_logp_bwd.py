@@ -1,0 +1,126 @@
+"""GPU parity and invariance of logp_bwd against the float64 oracle.
+
+Sources: "Batch-Invariant LogP" (Batch-Invariance: tile-wise backward from
+the saved per-row lse; Reference Semantics: ignored rows get zero gradient;
+Entry Point: logp.sum().backward())."""
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_token_log_amd as itl
+import oracle
+import synth
+from gpu_helpers import assert_grad_parity, dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+V = synth.QWEN3_VOCAB
+
+
+def _check(x, t, g, w, what):
+    logp, lse = itl.logp_fwd(x, t, -100, w)
+    d = itl.logp_bwd(x, t, lse, g, -100, w)
+    xn = x.detach().float().cpu().numpy().astype(np.float64)
+    tn = t.cpu().numpy()
+    _, lse64 = oracle.logp_fwd(xn, tn)
+    d64 = oracle.logp_bwd(xn, tn, g.cpu().numpy(), lse=lse64)
+    assert_grad_parity(d, d64, xn, lse64, g.cpu().numpy(), t, what=what)
+    return d
+
+
+def test_tiny_fp32():
+    c = synth.tiny_fp32()
+    g = synth.normal_matrix(1, 64, 1.0, torch.float32, seed=21)[0].to(dev())
+    _check(c["logits"].to(dev()), c["targets"].to(dev()), g, 512, "tiny fp32")
+
+
+@pytest.mark.parametrize("v,w", [(8, 512), (300, 512), (4099, 1024), (V, 4096)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ragged(v, w, dtype):
+    n = 24
+    x = synth.normal_matrix(n, v, 3.0, dtype, seed=v).to(dev())
+    t = synth.uniform_targets(n, v, seed=v + 1, ignore_rows=torch.tensor([2, 5])).to(dev())
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=v + 2)[0].to(dev())
+    _check(x, t, g, w, f"ragged {v} {dtype}")
+
+
+def test_qwen_rows_with_spikes():
+    c = synth.qwen3_fwd(n=256, device=dev())
+    g = synth.normal_matrix(1, 256, 1.0, torch.float32, seed=5)[0].to(dev())
+    # put some targets on the spikes: the target column then has 1 - p ~ 0
+    t = c["targets"].clone()
+    sr = c["spike_rows"][c["spike_rows"] < 256]
+    t[sr.to(dev())] = c["spike_cols"][c["spike_rows"] < 256].to(dev())
+    _check(c["logits"], t, g, 4096, "qwen spikes")
+
+
+def test_in_place_and_invariance():
+    """dlogits may overwrite the logits; rows are invariant to batch order."""
+    n = 64
+    x = synth.normal_matrix(n, V, 3.0, torch.bfloat16, seed=8).to(dev())
+    t = synth.uniform_targets(n, V, seed=9, ignore_rows=torch.tensor([1, 60])).to(dev())
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=10)[0].to(dev())
+    _, lse = itl.logp_fwd(x, t, -100, 4096)
+    d = itl.logp_bwd(x, t, lse, g, -100, 4096)
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(1)).to(dev())
+    dp = itl.logp_bwd(x[perm].contiguous(), t[perm].contiguous(), lse[perm].contiguous(),
+                      g[perm].contiguous(), -100, 4096)
+    assert torch.equal(dp.view(torch.int16), d[perm].view(torch.int16))
+    x2 = x.clone()
+    itl.logp_bwd(x2, t, lse, g, -100, 4096, dlogits_out=x2)
+    assert torch.equal(x2.view(torch.int16), d.view(torch.int16))
+    # a row alone, unaligned
+    buf = torch.empty(1, V + 1, dtype=torch.bfloat16, device=dev())
+    xr = buf[:, 1:]
+    xr.copy_(x[7:8])
+    dr = itl.logp_bwd(xr, t[7:8].clone(), lse[7:8].clone(), g[7:8].clone(), -100, 4096)
+    assert torch.equal(dr.view(torch.int16), d[7:8].view(torch.int16))
+
+
+def test_tile_width_is_bit_neutral():
+    n = 8
+    x = synth.normal_matrix(n, 5000, 2.0, torch.bfloat16, seed=3).to(dev())
+    t = synth.uniform_targets(n, 5000, seed=4).to(dev())
+    g = torch.ones(n, device=dev())
+    _, lse = itl.logp_fwd(x, t, -100, 512)
+    a = itl.logp_bwd(x, t, lse, g, -100, 512)
+    b = itl.logp_bwd(x, t, lse, g, -100, 8192)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_autograd_sum_backward():
+    """logp.sum().backward() fills logits.grad with g = 1."""
+    x = synth.normal_matrix(2 * 4, 300, 1.0, torch.bfloat16, seed=0).view(2, 4, 300).to(dev())
+    x.requires_grad_(True)
+    t = synth.uniform_targets(8, 300, seed=1).view(2, 4).to(dev())
+    t[0, 0] = -100
+    out = itl.batch_invariant_logp(x, t, -100, 512)
+    out.sum().backward()
+    assert x.grad.shape == x.shape and x.grad.dtype == torch.bfloat16
+    assert (x.grad[0, 0].view(torch.int16) == 0).all()
+    xn = x.detach().float().cpu().numpy().reshape(8, 300).astype(np.float64)
+    tn = t.reshape(-1).cpu().numpy()
+    _, lse64 = oracle.logp_fwd(xn, tn)
+    d64 = oracle.logp_bwd(xn, tn, np.ones(8), lse=lse64)
+    assert_grad_parity(x.grad.reshape(8, 300), d64, xn, lse64, np.ones(8), t, what="autograd")
+
+
+def test_full_size_sampled():
+    """N = 8192 Qwen3-vocab forward+backward at the benchmarked launch:
+    sampled rows against the oracle, every ignored row exactly zero, and the
+    gradient row sums near zero."""
+    c = synth.qwen3_fwd_bwd(device=dev())
+    x, t, g = c["logits"], c["targets"], c["grad"]
+    logp, lse = itl.logp_fwd(x, t, -100, 4096)
+    d = itl.logp_bwd(x, t, lse, g, -100, 4096)
+    rows = torch.tensor(list(range(0, 8192, 97)) + [8191], device=dev())
+    xn = x[rows].float().cpu().numpy().astype(np.float64)
+    tn = t[rows].cpu().numpy()
+    _, lse64 = oracle.logp_fwd(xn, tn)
+    d64 = oracle.logp_bwd(xn, tn, g[rows].cpu().numpy(), lse=lse64)
+    assert_grad_parity(d[rows], d64, xn, lse64, g[rows].cpu().numpy(), t[rows], what="full")
+    ign = (t == -100)
+    assert (d[ign].view(torch.int16) == 0).all()
+    rs = d[~ign][:512].float().sum(dim=1).abs() / g[~ign][:512].abs()
+    assert (rs < 0.05).all()
