@@ -183,8 +183,8 @@ def cpu_baseline_fwd_bwd(sample, rows):
     dt = time.perf_counter() - t0
     del np
     return {"value": round(rows / dt, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} rows of the same [8192, 151936] bf16 batch, "
-                      f"float64 numpy forward+backward, {dt:.1f} s",
+            "sample": f"{rows} rows of the same [8192, 151936] bf16 batch, "
+                      f"float64 numpy forward+backward in 128-row blocks, {dt:.1f} s",
             "cpu": cpu_model()}
 
 
@@ -323,9 +323,9 @@ def main():
     out, sample = runner(args, torch, itl, synth)
     if sample is not None:
         if args.workload == "fwd_bwd":
-            out["cpu_baseline"] = cpu_baseline_fwd_bwd(sample, args.cpu_rows or 1024)
+            out["cpu_baseline"] = cpu_baseline_fwd_bwd(sample, args.cpu_rows or 8192)
         elif args.workload == "linear":
-            out["cpu_baseline"] = cpu_baseline_linear(sample, args.cpu_rows or 32)
+            out["cpu_baseline"] = cpu_baseline_linear(sample, args.cpu_rows or 512)
     if "cpu_baseline" in out and out["cpu_baseline"]["value"]:
         out["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
     out["contract_id"] = itl.contract_id()
