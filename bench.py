@@ -31,7 +31,7 @@ KERNEL_SOURCES = {
                               "invariant_token_log_amd/csrc/logp_device.h"],
     "logp_bwd_kernel": ["invariant_token_log_amd/csrc/logp_kernels.hip",
                         "invariant_token_log_amd/csrc/logp_device.h"],
-    "linear_logp_stats_kernel": ["invariant_token_log_amd/csrc/linear_logp.hip",
+    "linear_stats_dma": ["invariant_token_log_amd/csrc/linear_logp.hip",
                                  "invariant_token_log_amd/csrc/logp_device.h"],
 }
 
@@ -255,9 +255,9 @@ def bench_linear(args, torch, itl, synth):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("linear_logp_stats_kernel",
+                     "traffic": measured_traffic("linear_stats_dma",
                                                  "qwen3_4096x4096x151936"),
-                     "kernel": "linear_logp_stats_kernel"},
+                     "kernel": "linear_stats_dma"},
     }
     sample = None
     if not args.no_cpu_baseline:

@@ -197,7 +197,7 @@ const char* logp_contract_id(void) {
   return "itl.logp.v1[tile=lane-asc-fold+xor1..32;tilestat=two-pass;merge=asc-fma;"
          "exp=v_exp_f32((a-b)*log2e);log=v_log_f32*ln2;bwd=rne(g*(onehot-p))]"
          "+itl.linear_logp.v1[mfma=f32_16x16x32_bf16;k=asc32-nosplit;tile=256;"
-         "tilestat=lane-asc-fold8+xor1..8+half0+half1]/gfx950";
+         "tilestat=4x64(lane-asc-fold4+xor1..8)+(q0+q1)+(q2+q3)]/gfx950";
 }
 
 }  // extern "C"

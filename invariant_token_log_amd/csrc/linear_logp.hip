@@ -5,13 +5,31 @@
 //
 //   z[r, j] = sum_k hidden[r, k] * weight[j, k]
 //
-// Each workgroup computes a 128 (rows) x 256 (vocabulary) block of z in fp32
-// with v_mfma_f32_16x16x32_bf16, walking K in ascending steps of 32, one
-// accumulator per output and no split-K, so every z[r, j] is the same bits
-// for any N, any row position and any grid.  The epilogue reduces each row's
-// 256 columns to the tile pair (m, s) of the logp contract with the shared
-// exp primitive, copies z at the target column, and writes them to the
-// [T, n] partial tables that the fixed-order merge consumes.
+// Arithmetic (identical in both kernels below, so they give the same bits):
+//   * every z[r, j] is one fp32 accumulator fed by v_mfma_f32_16x16x32_bf16
+//     over K in ascending steps of 32, no split-K;
+//   * the 256-column statistic tile of a row is cut into four quarters of 64
+//     columns; column c of the tile is column group G = c / 16, lane li =
+//     c % 16, quarter Q = G / 4.
+//     max: exact (order-free);
+//     sum: per lane, exp(z - m) folded over the quarter's 4 groups in
+//          ascending order from +0; xor butterfly over the 16 lanes (1, 2, 4,
+//          8) gives the quarter sum q_Q; s = (q0 + q1) + (q2 + q3);
+//     columns >= v are -inf and add +0;
+//   * the target logit is the accumulator itself, copied by the lane that
+//     holds it.
+// A row's z, m, s and target logit therefore depend only on that row of
+// hidden, the weight and K: not on N, the row's position, the block shape or
+// the grid.
+//
+// Two kernels share this contract:
+//   * linear_stats_dma (N > 128): 256 x 256 block, eight waves of 128 x 64 (two
+//     per SIMD, so each hides the other's LDS and barrier latency), operands
+//     streamed global -> LDS by direct 16-byte LDS loads through a four-stage
+//     ring (three K steps in flight), XOR-swizzled LDS rows;
+//   * linear_stats_regstage (N <= 128): 128 x 256 block, four waves of
+//     64 x 128, operands staged through registers into a double-buffered,
+//     padded LDS tile.
 #include "launch.h"
 #include "logp_device.h"
 
@@ -22,20 +40,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;             // rows of hidden per workgroup
-constexpr int BN = kLinearTile;     // vocabulary columns per workgroup (= statistic tile)
-constexpr int BK = 32;              // K per MFMA step
-constexpr int kThreads = 256;       // 4 waves: 2 (rows) x 2 (columns)
-constexpr int kLdsStride = BK + 8;  // bf16 elements per LDS row (80 B: breaks bank aliasing)
-constexpr int kAChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread per step
-constexpr int kBChunks = BN * BK / 8 / kThreads;
-
-struct Smem {
-  uint16_t a[2][BM * kLdsStride];
-  uint16_t b[2][BN * kLdsStride];
-  float red[2][BM];       // per column-half row statistics
-  int64_t target[BM];
-};
+constexpr int BN = kLinearTile;  // vocabulary columns per workgroup (= statistic tile)
+constexpr int BK = 32;           // K per MFMA step
 
 // Blocks are dealt round-robin to the 8 XCDs; give each XCD one contiguous
 // range of logical tiles so that a vocabulary block's weight rows are read
@@ -45,14 +51,216 @@ __device__ __forceinline__ int xcd_logical(int b, int g) {
   return x < rem ? x * (per + 1) + y : rem * (per + 1) + (x - rem) * per + y;
 }
 
-}  // namespace
+template <int BM>
+struct Reduce {
+  float red[4][BM];  // per-quarter row maxima
+  float sum[4][BM];  // per-quarter row sums
+  int64_t target[BM];
+};
 
-__global__ __launch_bounds__(kThreads) void linear_logp_stats_kernel(
+// Statistic epilogue.  The wave holds acc[i][j][q] =
+//   z[m0 + row0 + i*16 + 4g + q][v0 + col0 + j*16 + li],  j < NJ,
+// where its NJ column groups form NJ / 4 whole quarters starting at quarter
+// col0 / 64.  NT = threads of the workgroup.
+template <int MI, int NJ, int BM, int NT>
+__device__ __forceinline__ void stats_epilogue(const f32x4 (&acc)[MI][NJ], Reduce<BM>& rd,
+                                               int row0, int col0, int li, int g, int tid,
+                                               int64_t m0, int64_t v0, int vb, int64_t n,
+                                               int64_t v, int64_t ignore_index, float* pm,
+                                               float* ps, float* pt) {
+  constexpr int NQ = NJ / 4;  // quarters held by this wave
+  const int q0 = col0 / 64;
+  bool col_ok[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) col_ok[j] = v0 + col0 + j * 16 + li < v;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int h = 0; h < NQ; ++h) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 4 * h; j < 4 * h + 4; ++j)
+          m = fmaxf(m, col_ok[j] ? acc[i][j][q] : -INFINITY);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        if (li == 0) rd.red[q0 + h][row0 + i * 16 + 4 * g + q] = m;
+      }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = row0 + i * 16 + 4 * g + q;
+      const float m =
+          fmaxf(fmaxf(rd.red[0][lr], rd.red[1][lr]), fmaxf(rd.red[2][lr], rd.red[3][lr]));
+#pragma unroll
+      for (int h = 0; h < NQ; ++h) {
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 4 * h; j < 4 * h + 4; ++j)
+          s = s + exp_sub(col_ok[j] ? acc[i][j][q] : -INFINITY, m);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) s = s + __shfl_xor(s, o, kWave);
+        if (li == 0) rd.sum[q0 + h][lr] = s;
+      }
+    }
+  __syncthreads();
+  for (int lr = tid; lr < BM; lr += NT) {
+    const int64_t r = m0 + lr;
+    if (r < n && rd.target[lr] != ignore_index) {
+      pm[static_cast<int64_t>(vb) * n + r] =
+          fmaxf(fmaxf(rd.red[0][lr], rd.red[1][lr]), fmaxf(rd.red[2][lr], rd.red[3][lr]));
+      ps[static_cast<int64_t>(vb) * n + r] =
+          (rd.sum[0][lr] + rd.sum[1][lr]) + (rd.sum[2][lr] + rd.sum[3][lr]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = row0 + i * 16 + 4 * g + q;
+      const int64_t r = m0 + lr;
+      const int64_t t = rd.target[lr];
+      if (r < n && t != ignore_index && t >= 0 && t < v && t >= v0 + col0 &&
+          t < v0 + col0 + NJ * 16) {
+        const int off = static_cast<int>(t - v0 - col0);
+        if (off % 16 == li) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            if (off / 16 == j) pt[r] = acc[i][j][q];
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// linear_stats_dma: BM = 256, 8 waves (wm = wave / 4 picks 128 rows, wn =
+// wave % 4 picks 64 columns), four LDS stages filled by direct loads.
+// LDS stage layout: [A | B], each 256 rows x 32 bf16 (64 B per row, 16 KiB);
+// 16-byte chunk kc of row r sits in slot kc ^ swz(r), swz(r) = ((r>>1)^(r>>2))&3,
+// so the 16 rows of a fragment read (one 16-byte chunk per row) spread over
+// all banks.  One direct load instruction fills 1 KiB = 16 rows: lane L
+// writes row L/4, slot L%4, so it fetches chunk (L%4) ^ swz(L/4) of its row.
+// Wave w fills A blocks w, w+8 and B blocks w, w+8 of every stage.
+// ---------------------------------------------------------------------------
+constexpr int kDmaThreads = 512;
+constexpr int kStages = 4;
+constexpr int kStageElems = 256 * BK;  // bf16 per operand per stage
+
+struct SmemDma {
+  uint16_t stage[kStages][2][kStageElems];  // 128 KiB
+  Reduce<256> rd;
+};
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Issue this wave's 4 direct loads of K step `step` into LDS stage `s`.
+__device__ __forceinline__ void issue_step(SmemDma& sm, const uint16_t* a0, const uint16_t* a1,
+                                           const uint16_t* b0, const uint16_t* b1, int wave,
+                                           int s, int step) {
+  const int64_t k0 = static_cast<int64_t>(step) * BK;
+  constexpr int kBlk = 16 * BK;  // elements per 16-row block
+  __builtin_amdgcn_global_load_lds(a0 + k0, sm.stage[s][0] + wave * kBlk, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(b0 + k0, sm.stage[s][1] + wave * kBlk, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(a1 + k0, sm.stage[s][0] + (wave + 8) * kBlk, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(b1 + k0, sm.stage[s][1] + (wave + 8) * kBlk, 16, 0, 0);
+}
+
+__global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
     const int64_t* __restrict__ targets, int64_t ignore_index, float* __restrict__ pm,
     float* __restrict__ ps, float* __restrict__ pt) {
-  __shared__ __align__(16) Smem sm;
+  __shared__ __align__(16) SmemDma sm;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / 4, wn = wave % 4;
+  const int li = lane % 16, g = lane / 16;
+
+  const int logical = xcd_logical(blockIdx.x, mblocks * vblocks);
+  const int mb = logical % mblocks;
+  const int vb = logical / mblocks;
+  const int64_t m0 = static_cast<int64_t>(mb) * 256;
+  const int64_t v0 = static_cast<int64_t>(vb) * BN;
+  if (tid < 256) sm.rd.target[tid] = (m0 + tid < n) ? targets[m0 + tid] : ignore_index;
+
+  // Source rows past n / v are clamped to the last valid row: they only feed
+  // outputs that are masked out, and every load stays in bounds.
+  const int lrow = lane / 4;
+  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
+  const uint16_t* a0 = hidden + min(m0 + wave * 16 + lrow, n - 1) * ld_h + lk;
+  const uint16_t* a1 = hidden + min(m0 + (wave + 8) * 16 + lrow, n - 1) * ld_h + lk;
+  const uint16_t* b0 = weight + min(v0 + wave * 16 + lrow, v - 1) * ld_w + lk;
+  const uint16_t* b1 = weight + min(v0 + (wave + 8) * 16 + lrow, v - 1) * ld_w + lk;
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Fragment offsets (elements) inside a stage: row wm*128 + li (+16 i) of A,
+  // row wn*64 + li (+16 j) of B, chunk g.
+  const int aoff = (wm * 128 + li) * BK + ((g ^ swz(li)) * 8);
+  const int boff = (wn * 64 + li) * BK + ((g ^ swz(li)) * 8);
+  const int ksteps = static_cast<int>(hdim / BK);
+
+  // Every iteration issues exactly 4 loads per wave, so the wait count is
+  // constant: past the end the loads re-fetch the last K step into the stage
+  // that is no longer read.
+  for (int st = 0; st < kStages - 1; ++st)
+    issue_step(sm, a0, a1, b0, b1, wave, st, st < ksteps ? st : ksteps - 1);
+  for (int kt = 0; kt < ksteps; ++kt) {
+    // This wave's loads of step kt have landed (steps kt+1, kt+2 may still be
+    // in flight) and its fragment reads of the previous stage are done; after
+    // the barrier step kt is in LDS for every wave and stage (kt+3) % 4 is
+    // free.  A bare s_barrier: the fence of __syncthreads would also wait
+    // for the later steps' loads.
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    issue_step(sm, a0, a1, b0, b1, wave, (kt + kStages - 1) % kStages,
+               kt + kStages - 1 < ksteps ? kt + kStages - 1 : ksteps - 1);
+    const uint16_t* sa = sm.stage[kt % kStages][0];
+    const uint16_t* sb = sm.stage[kt % kStages][1];
+    bf16x8 a[8], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(sb + boff + j * 16 * BK);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const bf16x8*>(sa + aoff + i * 16 * BK);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  stats_epilogue<8, 4, 256, kDmaThreads>(acc, sm.rd, wm * 128, wn * 64, li, g, tid, m0, v0, vb,
+                                         n, v, ignore_index, pm, ps, pt);
+}
+
+// ---------------------------------------------------------------------------
+// linear_stats_regstage: BM = 128, 4 waves (wm = wave / 2 picks 64 rows, wn =
+// wave % 2 picks 128 columns), register staging, padded double buffer.
+// ---------------------------------------------------------------------------
+constexpr int kRegThreads = 256;
+constexpr int kLdsStride = BK + 8;  // bf16 elements per LDS row (80 B: breaks bank aliasing)
+
+struct SmemReg {
+  uint16_t a[2][128 * kLdsStride];
+  uint16_t b[2][BN * kLdsStride];
+  Reduce<128> rd;
+};
+
+__global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
+    const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
+    int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
+    const int64_t* __restrict__ targets, int64_t ignore_index, float* __restrict__ pm,
+    float* __restrict__ ps, float* __restrict__ pt) {
+  __shared__ __align__(16) SmemReg sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
@@ -62,41 +270,30 @@ __global__ __launch_bounds__(kThreads) void linear_logp_stats_kernel(
   const int logical = xcd_logical(blockIdx.x, mblocks * vblocks);
   const int mb = logical % mblocks;
   const int vb = logical / mblocks;
-  const int64_t m0 = static_cast<int64_t>(mb) * BM;
+  const int64_t m0 = static_cast<int64_t>(mb) * 128;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
+  if (tid < 128) sm.rd.target[tid] = (m0 + tid < n) ? targets[m0 + tid] : ignore_index;
 
-  if (tid < BM) sm.target[tid] = (m0 + tid < n) ? targets[m0 + tid] : ignore_index;
-
-  // Global -> register staging of one K step.
-  uint4 ra[kAChunks], rb[kBChunks];
-  auto fetch = [&](int64_t k0) {
-#pragma unroll
-    for (int p = 0; p < kAChunks; ++p) {
-      const int c = tid + p * kThreads, row = c / 4, kc = c % 4;
-      ra[p] = (m0 + row < n)
-                  ? *reinterpret_cast<const uint4*>(hidden + (m0 + row) * ld_h + k0 + kc * 8)
-                  : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int p = 0; p < kBChunks; ++p) {
-      const int c = tid + p * kThreads, row = c / 4, kc = c % 4;
-      rb[p] = (v0 + row < v)
-                  ? *reinterpret_cast<const uint4*>(weight + (v0 + row) * ld_w + k0 + kc * 8)
-                  : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < kAChunks; ++p) {
-      const int c = tid + p * kThreads, row = c / 4, kc = c % 4;
-      *reinterpret_cast<uint4*>(&sm.a[buf][row * kLdsStride + kc * 8]) = ra[p];
-    }
-#pragma unroll
-    for (int p = 0; p < kBChunks; ++p) {
-      const int c = tid + p * kThreads, row = c / 4, kc = c % 4;
-      *reinterpret_cast<uint4*>(&sm.b[buf][row * kLdsStride + kc * 8]) = rb[p];
-    }
-  };
+  // Each thread moves 2 (A) + 4 (B) 16-byte chunks per K step: chunk p covers
+  // row frow + 64p, columns [fk, fk + 8) of the step.  Rows past n / v are
+  // clamped to the last valid row.  Straight-line code keeps the staging
+  // values in registers.
+  const int frow = tid / 4, fk = (tid % 4) * 8;
+  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
+#define ITL_LD(DST, BASE, LD, R0, LIM, P, K0)                                              \
+  {                                                                                        \
+    const int64_t gr = min((R0) + frow + (P) * 64, (LIM) - 1);                             \
+    DST = *reinterpret_cast<const uint4*>((BASE) + gr * (LD) + (K0) + fk);                 \
+  }
+#define ITL_FETCH(K0)                                                                      \
+  ITL_LD(ra0, hidden, ld_h, m0, n, 0, K0) ITL_LD(ra1, hidden, ld_h, m0, n, 1, K0)         \
+  ITL_LD(rb0, weight, ld_w, v0, v, 0, K0) ITL_LD(rb1, weight, ld_w, v0, v, 1, K0)         \
+  ITL_LD(rb2, weight, ld_w, v0, v, 2, K0) ITL_LD(rb3, weight, ld_w, v0, v, 3, K0)
+#define ITL_ST(ARR, P, SRC) \
+  *reinterpret_cast<uint4*>(&(ARR)[(frow + (P) * 64) * kLdsStride + fk]) = SRC;
+#define ITL_STASH(BUF)                                                                     \
+  ITL_ST(sm.a[BUF], 0, ra0) ITL_ST(sm.a[BUF], 1, ra1) ITL_ST(sm.b[BUF], 0, rb0)           \
+  ITL_ST(sm.b[BUF], 1, rb1) ITL_ST(sm.b[BUF], 2, rb2) ITL_ST(sm.b[BUF], 3, rb3)
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -105,12 +302,14 @@ __global__ __launch_bounds__(kThreads) void linear_logp_stats_kernel(
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int ksteps = static_cast<int>(hdim / BK);
-  fetch(0);
-  stash(0);
+  ITL_FETCH(0)
+  ITL_STASH(0)
   __syncthreads();
   for (int kt = 0; kt < ksteps; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < ksteps) fetch(static_cast<int64_t>(kt + 1) * BK);
+    if (kt + 1 < ksteps) {
+      ITL_FETCH(static_cast<int64_t>(kt + 1) * BK)
+    }
     bf16x8 a[4], b[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -123,110 +322,37 @@ __global__ __launch_bounds__(kThreads) void linear_logp_stats_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    if (kt + 1 < ksteps) stash(buf ^ 1);
+    if (kt + 1 < ksteps) {
+      ITL_STASH(buf ^ 1)
+    }
     __syncthreads();
   }
-
-  // Epilogue.  acc[i][j][q] = z[m0 + wm*64 + i*16 + 4g + q][v0 + wn*128 + j*16 + li].
-  // Tile statistic over the 256 columns of each row, two passes:
-  //   max: lane max over j, xor butterfly over the 16 lanes of a row group
-  //        (offsets 1, 2, 4, 8), then max of the two column halves;
-  //   sum: each lane folds exp(z - m) over j = 0..7 ascending from +0, xor
-  //        butterfly over the 16 lanes, then (half 0) + (half 1).
-  // Columns >= v are -inf (they add +0).
-  float rowmax[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t col = v0 + wn * 128 + j * 16 + li;
-        m = fmaxf(m, col < v ? acc[i][j][q] : -INFINITY);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-      rowmax[i][q] = m;
-    }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (li == 0) sm.red[wn][wm * 64 + i * 16 + 4 * g + q] = rowmax[i][q];
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lr = wm * 64 + i * 16 + 4 * g + q;
-      rowmax[i][q] = fmaxf(sm.red[0][lr], sm.red[1][lr]);
-    }
-  __syncthreads();
-  float rowsum[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float m = rowmax[i][q];
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t col = v0 + wn * 128 + j * 16 + li;
-        s = s + exp_sub(col < v ? acc[i][j][q] : -INFINITY, m);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s = s + __shfl_xor(s, o, kWave);
-      rowsum[i][q] = s;
-    }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (li == 0) sm.red[wn][wm * 64 + i * 16 + 4 * g + q] = rowsum[i][q];
-  __syncthreads();
-  if (wn == 0 && li == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int lr = wm * 64 + i * 16 + 4 * g + q;
-        const int64_t r = m0 + lr;
-        if (r < n && sm.target[lr] != ignore_index) {
-          pm[static_cast<int64_t>(vb) * n + r] = rowmax[i][q];
-          ps[static_cast<int64_t>(vb) * n + r] = sm.red[0][lr] + sm.red[1][lr];
-        }
-      }
-  }
-  // Target copy: the lane holding column t of row r writes z[r, t].
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lr = wm * 64 + i * 16 + 4 * g + q;
-      const int64_t r = m0 + lr;
-      const int64_t t = sm.target[lr];
-      if (r < n && t != ignore_index && t >= 0 && t < v && t >= v0 + wn * 128 &&
-          t < v0 + wn * 128 + 128) {
-        const int off = static_cast<int>(t - v0 - wn * 128);
-        if (off % 16 == li) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (off / 16 == j) pt[r] = acc[i][j][q];
-        }
-      }
-    }
+#undef ITL_LD
+#undef ITL_FETCH
+#undef ITL_ST
+#undef ITL_STASH
+  stats_epilogue<4, 8, 128, kRegThreads>(acc, sm.rd, wm * 64, wn * 128, li, g, tid, m0, v0, vb,
+                                         n, v, ignore_index, pm, ps, pt);
 }
+
+}  // namespace
 
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
                             int64_t ld_w, int64_t n, int64_t h, int64_t v,
                             const int64_t* targets, int64_t ignore, float* pm, float* ps,
                             float* pt, hipStream_t s) {
-  const int mblocks = static_cast<int>((n + BM - 1) / BM);
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
-  hipLaunchKernelGGL(linear_logp_stats_kernel, dim3(mblocks * vblocks), dim3(kThreads), 0, s,
-                     hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets, ignore,
-                     pm, ps, pt);
+  if (n <= 128) {
+    const int mblocks = static_cast<int>((n + 127) / 128);
+    hipLaunchKernelGGL(linear_stats_regstage, dim3(mblocks * vblocks), dim3(kRegThreads), 0, s,
+                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets, ignore,
+                       pm, ps, pt);
+  } else {
+    const int mblocks = static_cast<int>((n + 255) / 256);
+    hipLaunchKernelGGL(linear_stats_dma, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,
+                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets, ignore,
+                       pm, ps, pt);
+  }
 }
 
 }  // namespace itl
