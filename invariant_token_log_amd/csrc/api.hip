@@ -108,8 +108,8 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
         itl::launch_fwd_partials(dtype, vec, chunks, logits, ld, n, v, targets, ignore_index, kb,
                                  ke, pm, ps, pt, s);
     }
-    itl::launch_fwd_merge(pm, ps, pt, n, ntiles, v, targets, ignore_index, logp_out, lse_out,
-                          status, s);
+    itl::launch_fwd_merge(pm, ps, pt, n, ntiles, 1, n, v, targets, ignore_index, logp_out,
+                          lse_out, status, s);
   }
   st = hip_status();
   if (st != LOGP_OK) return st;
@@ -172,8 +172,8 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
   itl::launch_linear_partials(static_cast<const uint16_t*>(hidden), ld_h,
                               static_cast<const uint16_t*>(weight), ld_w, n, h, v, targets,
                               ignore_index, pm, ps, pt, s);
-  itl::launch_fwd_merge(pm, ps, pt, n, static_cast<int>(ntiles), v, targets, ignore_index,
-                        logp_out, lse_out, nullptr, s);
+  itl::launch_fwd_merge(pm, ps, pt, n, static_cast<int>(ntiles), ntiles, 1, v, targets,
+                        ignore_index, logp_out, lse_out, nullptr, s);
   return hip_status();
 }
 

@@ -18,16 +18,18 @@ void launch_fwd_partials(int dtype, bool vec, int chunks, const void* logits, in
                          int k_begin, int k_end, float* pm, float* ps, float* pt,
                          hipStream_t s);
 
+// Partial (r, k) of the [n, T] / [T, n] tables sits at r * row_stride + k * tile_stride.
 void launch_fwd_merge(const float* pm, const float* ps, const float* pt, int64_t n,
-                      int ntiles, int64_t v, const int64_t* targets, int64_t ignore,
-                      float* logp, float* lse, int* status, hipStream_t s);
+                      int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
+                      const int64_t* targets, int64_t ignore, float* logp, float* lse,
+                      int* status, hipStream_t s);
 
 void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, int64_t v,
                 const int64_t* targets, int64_t ignore, const float* lse, const float* grad,
                 void* dlogits, int64_t ld_out, hipStream_t s);
 
-// Fused LM-head statistics: writes the [T, n] partials and the target logits
-// of every active row (T = ceil(v / 256)).
+// Fused LM-head statistics: writes the row-major [n, T] partials and the
+// target logits of every active row (T = ceil(v / 256)).
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
                             int64_t ld_w, int64_t n, int64_t h, int64_t v,
                             const int64_t* targets, int64_t ignore, float* pm, float* ps,

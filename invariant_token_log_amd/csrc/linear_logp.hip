@@ -13,8 +13,8 @@
 //     c % 16, quarter Q = G / 4.
 //     max: exact (order-free);
 //     sum: per lane, exp(z - m) folded over the quarter's 4 groups in
-//          ascending order from +0; xor butterfly over the 16 lanes (1, 2, 4,
-//          8) gives the quarter sum q_Q; s = (q0 + q1) + (q2 + q3);
+//          ascending order from +0; the xor-butterfly association over the 16
+//          lanes (1, 2, 4, 8) gives the quarter sum q_Q; s = (q0 + q1) + (q2 + q3);
 //     columns >= v are -inf and add +0;
 //   * the target logit is the accumulator itself, copied by the lane that
 //     holds it.
@@ -51,6 +51,21 @@ __device__ __forceinline__ int xcd_logical(int b, int g) {
   return x < rem ? x * (per + 1) + y : rem * (per + 1) + (x - rem) * per + y;
 }
 
+// Logical tile -> (row block, vocabulary block).  Tiles are grouped 8 row
+// blocks x 4 vocabulary blocks, so the ~32 workgroups an XCD runs at once
+// share each hidden slice 4 ways and each weight slice 8 ways in its L2.
+__device__ __forceinline__ void tile_coords(int logical, int mblocks, int vblocks, int& mb,
+                                            int& vb) {
+  const int vbg = logical / (mblocks * 4);
+  const int gv = min(4, vblocks - vbg * 4);
+  const int rem = logical - vbg * mblocks * 4;
+  const int mbg = rem / (8 * gv);
+  const int gm = min(8, mblocks - mbg * 8);
+  const int r2 = rem - mbg * 8 * gv;
+  mb = mbg * 8 + r2 % gm;
+  vb = vbg * 4 + r2 / gm;
+}
+
 template <int BM>
 struct Reduce {
   float red[4][BM];  // per-quarter row maxima
@@ -65,8 +80,9 @@ struct Reduce {
 template <int MI, int NJ, int BM, int NT>
 __device__ __forceinline__ void stats_epilogue(const f32x4 (&acc)[MI][NJ], Reduce<BM>& rd,
                                                int row0, int col0, int li, int g, int tid,
-                                               int64_t m0, int64_t v0, int vb, int64_t n,
-                                               int64_t v, int64_t ignore_index, float* pm,
+                                               int64_t m0, int64_t v0, int vb, int vblocks,
+                                               int64_t n, int64_t v, int64_t ignore_index,
+                                               float* pm,
                                                float* ps, float* pt) {
   constexpr int NQ = NJ / 4;  // quarters held by this wave
   const int q0 = col0 / 64;
@@ -83,8 +99,7 @@ __device__ __forceinline__ void stats_epilogue(const f32x4 (&acc)[MI][NJ], Reduc
 #pragma unroll
         for (int j = 4 * h; j < 4 * h + 4; ++j)
           m = fmaxf(m, col_ok[j] ? acc[i][j][q] : -INFINITY);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        m = row16_max_first(m);
         if (li == 0) rd.red[q0 + h][row0 + i * 16 + 4 * g + q] = m;
       }
   __syncthreads();
@@ -101,8 +116,7 @@ __device__ __forceinline__ void stats_epilogue(const f32x4 (&acc)[MI][NJ], Reduc
 #pragma unroll
         for (int j = 4 * h; j < 4 * h + 4; ++j)
           s = s + exp_sub(col_ok[j] ? acc[i][j][q] : -INFINITY, m);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) s = s + __shfl_xor(s, o, kWave);
+        s = row16_sum_first(s);
         if (li == 0) rd.sum[q0 + h][lr] = s;
       }
     }
@@ -110,10 +124,9 @@ __device__ __forceinline__ void stats_epilogue(const f32x4 (&acc)[MI][NJ], Reduc
   for (int lr = tid; lr < BM; lr += NT) {
     const int64_t r = m0 + lr;
     if (r < n && rd.target[lr] != ignore_index) {
-      pm[static_cast<int64_t>(vb) * n + r] =
+      pm[r * vblocks + vb] =
           fmaxf(fmaxf(rd.red[0][lr], rd.red[1][lr]), fmaxf(rd.red[2][lr], rd.red[3][lr]));
-      ps[static_cast<int64_t>(vb) * n + r] =
-          (rd.sum[0][lr] + rd.sum[1][lr]) + (rd.sum[2][lr] + rd.sum[3][lr]);
+      ps[r * vblocks + vb] = (rd.sum[0][lr] + rd.sum[1][lr]) + (rd.sum[2][lr] + rd.sum[3][lr]);
     }
   }
 #pragma unroll
@@ -180,9 +193,8 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   const int wm = wave / 4, wn = wave % 4;
   const int li = lane % 16, g = lane / 16;
 
-  const int logical = xcd_logical(blockIdx.x, mblocks * vblocks);
-  const int mb = logical % mblocks;
-  const int vb = logical / mblocks;
+  int mb, vb;
+  tile_coords(xcd_logical(blockIdx.x, mblocks * vblocks), mblocks, vblocks, mb, vb);
   const int64_t m0 = static_cast<int64_t>(mb) * 256;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
   if (tid < 256) sm.rd.target[tid] = (m0 + tid < n) ? targets[m0 + tid] : ignore_index;
@@ -208,38 +220,63 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   const int boff = (wn * 64 + li) * BK + ((g ^ swz(li)) * 8);
   const int ksteps = static_cast<int>(hdim / BK);
 
-  // Every iteration issues exactly 4 loads per wave, so the wait count is
-  // constant: past the end the loads re-fetch the last K step into the stage
-  // that is no longer read.
-  for (int st = 0; st < kStages - 1; ++st)
+  // Pipeline (ksteps is even: h is a multiple of 64).  Iteration kt runs the
+  // MFMAs of step kt on fragments already in registers while the fragments of
+  // step kt+1 are read from LDS and the direct loads of step kt+4 go out
+  // (steps kt+2, kt+3 are in flight).  Every iteration issues exactly 4 loads
+  // per wave and 12 fragment reads, so the wait counts are constant: past the
+  // end the loads re-fetch the last K step into the stage that is no longer
+  // read, and the extra fragment reads land in registers that are not used.
+  for (int st = 0; st < kStages; ++st)
     issue_step(sm, a0, a1, b0, b1, wave, st, st < ksteps ? st : ksteps - 1);
-  for (int kt = 0; kt < ksteps; ++kt) {
-    // This wave's loads of step kt have landed (steps kt+1, kt+2 may still be
-    // in flight) and its fragment reads of the previous stage are done; after
-    // the barrier step kt is in LDS for every wave and stage (kt+3) % 4 is
-    // free.  A bare s_barrier: the fence of __syncthreads would also wait
-    // for the later steps' loads.
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    issue_step(sm, a0, a1, b0, b1, wave, (kt + kStages - 1) % kStages,
-               kt + kStages - 1 < ksteps ? kt + kStages - 1 : ksteps - 1);
-    const uint16_t* sa = sm.stage[kt % kStages][0];
-    const uint16_t* sb = sm.stage[kt % kStages][1];
-    bf16x8 a[8], b[4];
+  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  bf16x8 xa[8], xb[4], ya[8], yb[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(sb + boff + j * 16 * BK);
+  for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(sm.stage[0][1] + boff + j * 16 * BK);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const bf16x8*>(sa + aoff + i * 16 * BK);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const bf16x8*>(sm.stage[0][0] + aoff + i * 16 * BK);
+  // One step: this wave's reads of stage KT % 4 and its loads of step KT+1
+  // have landed (KT+2, KT+3 may still be in flight); after the barrier step
+  // KT+1 is in LDS for every wave and stage KT % 4 is free.  A bare
+  // s_barrier: the fence of __syncthreads would also wait for KT+2, KT+3.
+#define ITL_STEP(CA, CB, NA, NB, KT)                                                         \
+  {                                                                                          \
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");                              \
+    __builtin_amdgcn_s_barrier();                                                            \
+    issue_step(sm, a0, a1, b0, b1, wave, (KT) % kStages,                                     \
+               (KT) + kStages < ksteps ? (KT) + kStages : ksteps - 1);                       \
+    {                                                                                        \
+      const uint16_t* sa = sm.stage[((KT) + 1) % kStages][0];                                \
+      const uint16_t* sb = sm.stage[((KT) + 1) % kStages][1];                                \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+        NB[j] = *reinterpret_cast<const bf16x8*>(sb + boff + j * 16 * BK);                   \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i)                                          \
+        NA[i] = *reinterpret_cast<const bf16x8*>(sa + aoff + i * 16 * BK);                   \
+    }                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                            \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0); \
+    /* Interleave so that the MFMA stream never waits behind the load issue: */              \
+    /* 4 x (1 direct load, then 3 x (2 MFMAs, 1 fragment read)), then 8 MFMAs. */            \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                          \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
+      _Pragma("unroll") for (int w = 0; w < 3; ++w) {                                        \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                   \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
+      }                                                                                      \
+    }                                                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                       \
   }
+  for (int kt = 0; kt < ksteps; kt += 2) {
+    ITL_STEP(xa, xb, ya, yb, kt)
+    ITL_STEP(ya, yb, xa, xb, kt + 1)
+  }
+#undef ITL_STEP
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   stats_epilogue<8, 4, 256, kDmaThreads>(acc, sm.rd, wm * 128, wn * 64, li, g, tid, m0, v0, vb,
-                                         n, v, ignore_index, pm, ps, pt);
+                                         vblocks, n, v, ignore_index, pm, ps, pt);
 }
 
 // ---------------------------------------------------------------------------
@@ -332,7 +369,7 @@ __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
 #undef ITL_ST
 #undef ITL_STASH
   stats_epilogue<4, 8, 128, kRegThreads>(acc, sm.rd, wm * 64, wn * 128, li, g, tid, m0, v0, vb,
-                                         n, v, ignore_index, pm, ps, pt);
+                                         vblocks, n, v, ignore_index, pm, ps, pt);
 }
 
 }  // namespace

@@ -47,6 +47,39 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Reductions over the 16 lanes of a row (lanes 16r .. 16r+15) whose result is
+// taken from the row's first lane.  That lane sees exactly the xor butterfly
+// (offsets 1, 2, 4, 8): ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7)) ...
+// in the same association as __shfl_xor steps, but the partners come from
+// DPP lane moves instead of LDS-routed permutes: quad permutes for 1 and 2,
+// then row rotations (a rotation right by n hands lane i the value of lane
+// i - n mod 16), by 12 so that lane 0 reads lane 4, and by 8 so that it reads
+// lane 8.  Other lanes of the row end with other, unused associations.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor12 = 0x12C;  // lane i <- lane i + 4 (mod 16)
+constexpr int kDppRowRor8 = 0x128;   // lane i <- lane i + 8 (mod 16)
+
+__device__ __forceinline__ float row16_sum_first(float x) {
+  x = x + dpp_mov<kDppXor1>(x);
+  x = x + dpp_mov<kDppXor2>(x);
+  x = x + dpp_mov<kDppRowRor12>(x);
+  x = x + dpp_mov<kDppRowRor8>(x);
+  return x;
+}
+
+__device__ __forceinline__ float row16_max_first(float x) {
+  x = fmaxf(x, dpp_mov<kDppXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppRowRor12>(x));
+  x = fmaxf(x, dpp_mov<kDppRowRor8>(x));
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // Element access.  bf16 is carried as its raw 16 bits; widening to fp32 is a
 // 16-bit left shift and exact.
@@ -140,16 +173,38 @@ __device__ __forceinline__ void tile_stats(const T* row, int64_t col0, int64_t v
 // Fixed-order merge ("Batch-Invariant LogP", Tensor Parallel, step 4):
 //   M = max_k m_k;  acc = +0;  for k = 0 .. T-1:  acc = fma(s_k, e^(m_k - M), acc)
 //   (tiles with m_k = -inf skipped: they hold no column);  LSE = M + log(acc).
-// Partials are read at m[k * stride], s[k * stride].
+// One wave evaluates one row: the max and the T exponentials are spread over
+// the lanes (the max is exact in any order; each exponential is the same
+// function of the same two values), then the ascending fma chain runs over
+// them in tile order, 64 tiles at a time, with every operand read back
+// exactly from the lane that computed it.  Partial k of the row is read at
+// m[k * stride], s[k * stride].  All 64 lanes must call; all return the LSE.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float lane_value(float x, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+}
+
 template <typename P>
 __device__ __forceinline__ float merge_lse(P m, P s, int ntiles, int64_t stride) {
-  float big_m = -INFINITY;
-  for (int k = 0; k < ntiles; ++k) big_m = fmaxf(big_m, m[k * stride]);
+  const int lane = threadIdx.x & (kWave - 1);
+  float mx = -INFINITY;
+  for (int k = lane; k < ntiles; k += kWave) mx = fmaxf(mx, m[k * stride]);
+  const float big_m = wave_max(mx);
   float acc = 0.0f;
-  for (int k = 0; k < ntiles; ++k) {
-    const float mk = m[k * stride];
-    if (mk != -INFINITY) acc = fmaf(s[k * stride], exp_sub(mk, big_m), acc);
+  for (int c = 0; c < ntiles; c += kWave) {
+    const int k = c + lane;
+    float mk = -INFINITY, sk = 0.0f;
+    if (k < ntiles) {
+      mk = m[k * stride];
+      sk = s[k * stride];
+    }
+    // e_k >= 0 always (or NaN); -1 marks a tile without columns.
+    const float ek = mk != -INFINITY ? exp_sub(mk, big_m) : -1.0f;
+    const int cnt = ntiles - c < kWave ? ntiles - c : kWave;
+    for (int j = 0; j < cnt; ++j) {
+      const float e = lane_value(ek, j);
+      if (e != -1.0f) acc = fmaf(lane_value(sk, j), e, acc);
+    }
   }
   return big_m + log_nat(acc);
 }

@@ -14,7 +14,7 @@ constexpr int64_t kMaxRowBlocks = 1 << 20;  // grid-stride beyond this
 // ---------------------------------------------------------------------------
 // Single-launch forward ("Batch-Invariant LogP", Tensor Parallel with one
 // shard).  One workgroup per row (grid-stride over rows); wave w reduces the
-// tiles k = w, w + 4, ... and parks (m_k, s_k) in LDS; thread 0 merges them in
+// tiles k = w, w + 4, ... and parks (m_k, s_k) in LDS; wave 0 merges them in
 // ascending order, copies the target logit and writes logp and lse.  Ignored
 // rows are not read.
 // ---------------------------------------------------------------------------
@@ -48,13 +48,15 @@ __global__ __launch_bounds__(kBlock) void logp_fwd_fused_kernel(
       }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (wave == 0) {
       const float L = merge_lse(lm, ls, ntiles, 1);
-      const bool valid = t >= 0 && t < v;
-      const float xt = valid ? Elt<T>::load(row, t) : 0.0f;
-      logp[r] = combine(xt, L, valid);
-      if (lse) lse[r] = L;
-      if (!valid && status) status[0] = 1;
+      if (lane == 0) {
+        const bool valid = t >= 0 && t < v;
+        const float xt = valid ? Elt<T>::load(row, t) : 0.0f;
+        logp[r] = combine(xt, L, valid);
+        if (lse) lse[r] = L;
+        if (!valid && status) status[0] = 1;
+      }
     }
     __syncthreads();
   }
@@ -62,8 +64,7 @@ __global__ __launch_bounds__(kBlock) void logp_fwd_fused_kernel(
 
 // ---------------------------------------------------------------------------
 // Shard partials: the same tile statistic over the tiles [k_begin, k_end) a
-// shard owns, written to the [T, n] tables pm / ps (tile-major, so the merge
-// reads them coalesced).  The owner of the target's tile copies the target
+// shard owns, written to the tile-major [T, n] tables pm / ps.  The owner of the target's tile copies the target
 // logit into pt[r].  Ignored rows are skipped (the merge never reads them).
 // ---------------------------------------------------------------------------
 template <typename T, int C, bool VEC>
@@ -94,27 +95,35 @@ __global__ __launch_bounds__(kBlock) void logp_partials_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the gathered [T, n] partials: one lane per row, the same
-// merge_lse and combine as the single-launch forward.
+// Merge of gathered partials: one wave per row, the same merge_lse and
+// combine as the single-launch forward.  Partial (r, k) sits at
+// p[r * row_stride + k * tile_stride] (tile-major [T, n] tables from the
+// shard launches, row-major [n, T] tables from the fused LM head).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void logp_merge_kernel(
-    const float* __restrict__ pm, const float* __restrict__ ps,
-    const float* __restrict__ pt, int64_t n, int ntiles, int64_t v,
-    const int64_t* __restrict__ targets, int64_t ignore_index,
-    float* __restrict__ logp, float* __restrict__ lse, int* __restrict__ status) {
-  for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < n;
-       r += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ pt,
+    int64_t n, int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
+    const int64_t* __restrict__ targets, int64_t ignore_index, float* __restrict__ logp,
+    float* __restrict__ lse, int* __restrict__ status) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; r < n;
+       r += waves) {
     const int64_t t = targets[r];
     if (t == ignore_index) {
-      logp[r] = 0.0f;
-      if (lse) lse[r] = 0.0f;
+      if (lane == 0) {
+        logp[r] = 0.0f;
+        if (lse) lse[r] = 0.0f;
+      }
       continue;
     }
-    const float L = merge_lse(pm + r, ps + r, ntiles, n);
-    const bool valid = t >= 0 && t < v;
-    logp[r] = combine(valid ? pt[r] : 0.0f, L, valid);
-    if (lse) lse[r] = L;
-    if (!valid && status) status[0] = 1;
+    const float L = merge_lse(pm + r * row_stride, ps + r * row_stride, ntiles, tile_stride);
+    if (lane == 0) {
+      const bool valid = t >= 0 && t < v;
+      logp[r] = combine(valid ? pt[r] : 0.0f, L, valid);
+      if (lse) lse[r] = L;
+      if (!valid && status) status[0] = 1;
+    }
   }
 }
 
@@ -281,12 +290,14 @@ void launch_fwd_partials(int dtype, bool vec, int chunks, const void* logits, in
 }
 
 void launch_fwd_merge(const float* pm, const float* ps, const float* pt, int64_t n,
-                      int ntiles, int64_t v, const int64_t* targets, int64_t ignore,
-                      float* logp, float* lse, int* status, hipStream_t s) {
-  int64_t blocks = (n + kBlock - 1) / kBlock;
+                      int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
+                      const int64_t* targets, int64_t ignore, float* logp, float* lse,
+                      int* status, hipStream_t s) {
+  int64_t blocks = (n + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > kMaxRowBlocks) blocks = kMaxRowBlocks;
   hipLaunchKernelGGL(logp_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                     s, pm, ps, pt, n, ntiles, v, targets, ignore, logp, lse, status);
+                     s, pm, ps, pt, n, ntiles, row_stride, tile_stride, v, targets, ignore, logp,
+                     lse, status);
 }
 
 void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, int64_t v,
