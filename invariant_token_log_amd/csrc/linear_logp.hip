@@ -68,84 +68,140 @@ __device__ __forceinline__ void tile_coords(int logical, int mblocks, int vblock
 
 template <int BM>
 struct Reduce {
-  float red[4][BM];  // per-quarter row maxima
-  float sum[4][BM];  // per-quarter row sums
-  int64_t target[BM];
+  float red[BM][4];  // per-row quarter maxima
+  float sum[BM][4];  // per-row quarter sums
+  float tmax[BM];    // per-row tile maximum
+  float tval[BM];    // target logit, when the target column is in this block
+  int code[BM];      // row_code() of each row
 };
+
+// Per-row code for the epilogue: -2 = no statistics (row past n, or its
+// target is ignore_index), -1 = target column outside this vocabulary block,
+// else the target column minus v0.
+__device__ __forceinline__ int row_code(int64_t r, int64_t n, const int64_t* targets,
+                                        int64_t ignore_index, int64_t v0, int64_t v) {
+  if (r >= n) return -2;
+  const int64_t t = targets[r];
+  if (t == ignore_index) return -2;
+  return (t >= v0 && t < v0 + BN && t < v) ? static_cast<int>(t - v0) : -1;
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads or stores.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Statistic epilogue.  The wave holds acc[i][j][q] =
 //   z[m0 + row0 + i*16 + 4g + q][v0 + col0 + j*16 + li],  j < NJ,
 // where its NJ column groups form NJ / 4 whole quarters starting at quarter
-// col0 / 64.  NT = threads of the workgroup.
+// col0 / 64.  NT = threads of the workgroup.  rd.code must be filled, and
+// accumulators of columns >= v must already hold -inf.
 template <int MI, int NJ, int BM, int NT>
-__device__ __forceinline__ void stats_epilogue(const f32x4 (&acc)[MI][NJ], Reduce<BM>& rd,
-                                               int row0, int col0, int li, int g, int tid,
-                                               int64_t m0, int64_t v0, int vb, int vblocks,
-                                               int64_t n, int64_t v, int64_t ignore_index,
-                                               float* pm,
-                                               float* ps, float* pt) {
+__device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], Reduce<BM>& rd,
+                                                    int row0, int col0, int li, int g, int tid,
+                                                    int64_t m0, int64_t v0, int vb, int vblocks,
+                                                    int64_t v, float* pm, float* ps, float* pt) {
   constexpr int NQ = NJ / 4;  // quarters held by this wave
   const int q0 = col0 / 64;
-  bool col_ok[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) col_ok[j] = v0 + col0 + j * 16 + li < v;
+  auto z = [&](int i, int j, int q) { return acc[i][j][q]; };
+
+  // Pass 1: quarter maxima (exact, order-free).
+  float part[MI][4][NQ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int h = 0; h < NQ; ++h) {
-        float m = -INFINITY;
+        float m = z(i, 4 * h, q);
 #pragma unroll
-        for (int j = 4 * h; j < 4 * h + 4; ++j)
-          m = fmaxf(m, col_ok[j] ? acc[i][j][q] : -INFINITY);
-        m = row16_max_first(m);
-        if (li == 0) rd.red[q0 + h][row0 + i * 16 + 4 * g + q] = m;
+        for (int j = 4 * h + 1; j < 4 * h + 4; ++j) m = fmaxf(m, z(i, j, q));
+        part[i][q][h] = row16_max_first(m);
       }
-  __syncthreads();
+  if (li == 0) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) rd.red[row0 + i * 16 + 4 * g + q][q0 + h] = part[i][q][h];
+  }
+  block_sync_lds();
+  for (int lr = tid; lr < BM; lr += NT) {
+    const float4 r4 = *reinterpret_cast<const float4*>(rd.red[lr]);
+    rd.tmax[lr] = fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w));
+  }
+  block_sync_lds();
+
+  // Pass 2: quarter sums against the tile maximum; the one lane holding the
+  // target column of a row parks z[r, t] in LDS.  The empty asm keeps the
+  // LDS reads of row group i from being hoisted above group i - 1, which
+  // would hold every row's operands in registers at once.
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int lr = row0 + i * 16 + 4 * g + q;
-      const float m =
-          fmaxf(fmaxf(rd.red[0][lr], rd.red[1][lr]), fmaxf(rd.red[2][lr], rd.red[3][lr]));
+      const float m = rd.tmax[lr];
 #pragma unroll
       for (int h = 0; h < NQ; ++h) {
-        float s = 0.0f;
+        float s = exp_sub(z(i, 4 * h, q), m);
 #pragma unroll
-        for (int j = 4 * h; j < 4 * h + 4; ++j)
-          s = s + exp_sub(col_ok[j] ? acc[i][j][q] : -INFINITY, m);
-        s = row16_sum_first(s);
-        if (li == 0) rd.sum[q0 + h][lr] = s;
+        for (int j = 4 * h + 1; j < 4 * h + 4; ++j) s = s + exp_sub(z(i, j, q), m);
+        part[i][q][h] = row16_sum_first(s);
       }
-    }
-  __syncthreads();
-  for (int lr = tid; lr < BM; lr += NT) {
-    const int64_t r = m0 + lr;
-    if (r < n && rd.target[lr] != ignore_index) {
-      pm[r * vblocks + vb] =
-          fmaxf(fmaxf(rd.red[0][lr], rd.red[1][lr]), fmaxf(rd.red[2][lr], rd.red[3][lr]));
-      ps[r * vblocks + vb] = (rd.sum[0][lr] + rd.sum[1][lr]) + (rd.sum[2][lr] + rd.sum[3][lr]);
+      const int off = rd.code[lr] - col0;
+      if (off >= 0 && off < NJ * 16 && (off & 15) == li) {
+        float zt = acc[i][0][q];
+#pragma unroll
+        for (int j = 1; j < NJ; ++j)
+          if ((off >> 4) == j) zt = acc[i][j][q];
+        rd.tval[lr] = zt;
+      }
     }
   }
+  if (li == 0) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lr = row0 + i * 16 + 4 * g + q;
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) rd.sum[row0 + i * 16 + 4 * g + q][q0 + h] = part[i][q][h];
+  }
+  block_sync_lds();
+
+  for (int lr = tid; lr < BM; lr += NT) {
+    const int code = rd.code[lr];
+    if (code != -2) {
       const int64_t r = m0 + lr;
-      const int64_t t = rd.target[lr];
-      if (r < n && t != ignore_index && t >= 0 && t < v && t >= v0 + col0 &&
-          t < v0 + col0 + NJ * 16) {
-        const int off = static_cast<int>(t - v0 - col0);
-        if (off % 16 == li) {
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            if (off / 16 == j) pt[r] = acc[i][j][q];
-        }
-      }
+      const float4 s4 = *reinterpret_cast<const float4*>(rd.sum[lr]);
+      pm[r * vblocks + vb] = rd.tmax[lr];
+      ps[r * vblocks + vb] = (s4.x + s4.y) + (s4.z + s4.w);
+      if (code >= 0) pt[r] = rd.tval[lr];
     }
+  }
+}
+
+template <int MI, int NJ, int BM, int NT>
+__device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>& rd, int row0,
+                                               int col0, int li, int g, int tid, int64_t m0,
+                                               int64_t v0, int vb, int vblocks, int64_t v,
+                                               float* pm, float* ps, float* pt) {
+  // Columns >= v exist only in the last vocabulary block.  Their -inf takes
+  // no part in a maximum and adds an exact 0 to a sum; no target lies there.
+  if (v0 + BN > v) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (v0 + col0 + j * 16 + li >= v)
+#pragma unroll
+        for (int i = 0; i < MI; ++i) acc[i][j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
+  stats_epilogue_body<MI, NJ, BM, NT>(acc, rd, row0, col0, li, g, tid, m0, v0, vb, vblocks, v, pm,
+                                      ps, pt);
 }
 
 // ---------------------------------------------------------------------------
@@ -197,7 +253,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   tile_coords(xcd_logical(blockIdx.x, mblocks * vblocks), mblocks, vblocks, mb, vb);
   const int64_t m0 = static_cast<int64_t>(mb) * 256;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
-  if (tid < 256) sm.rd.target[tid] = (m0 + tid < n) ? targets[m0 + tid] : ignore_index;
+  if (tid < 256) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
 
   // Source rows past n / v are clamped to the last valid row: they only feed
   // outputs that are masked out, and every load stays in bounds.
@@ -276,7 +332,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   stats_epilogue<8, 4, 256, kDmaThreads>(acc, sm.rd, wm * 128, wn * 64, li, g, tid, m0, v0, vb,
-                                         vblocks, n, v, ignore_index, pm, ps, pt);
+                                         vblocks, v, pm, ps, pt);
 }
 
 // ---------------------------------------------------------------------------
@@ -309,7 +365,7 @@ __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
   const int vb = logical / mblocks;
   const int64_t m0 = static_cast<int64_t>(mb) * 128;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
-  if (tid < 128) sm.rd.target[tid] = (m0 + tid < n) ? targets[m0 + tid] : ignore_index;
+  if (tid < 128) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
 
   // Each thread moves 2 (A) + 4 (B) 16-byte chunks per K step: chunk p covers
   // row frow + 64p, columns [fk, fk + 8) of the step.  Rows past n / v are
@@ -369,7 +425,7 @@ __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
 #undef ITL_ST
 #undef ITL_STASH
   stats_epilogue<4, 8, 128, kRegThreads>(acc, sm.rd, wm * 64, wn * 128, li, g, tid, m0, v0, vb,
-                                         vblocks, n, v, ignore_index, pm, ps, pt);
+                                         vblocks, v, pm, ps, pt);
 }
 
 }  // namespace

@@ -57,7 +57,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // lane 8.  Other lanes of the row end with other, unused associations.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kDppXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
