@@ -164,27 +164,30 @@ def bench_fwd_bwd(args, torch, itl, synth):
     return out, sample
 
 
-def cpu_baseline_fwd_bwd(sample, rows):
-    """The float64 oracle (forward then backward) on the first `rows` rows
-    of the same workload, single process; D2H copies are excluded."""
-    import numpy as np
-
+def cpu_baseline_fwd_bwd(sample, max_rows, budget_s):
+    """The float64 oracle (forward then backward) on the leading rows of the
+    same workload, single process, in 64-row blocks until `budget_s` seconds
+    of oracle time are spent or `max_rows` rows are done.  Device-to-host
+    copies happen between blocks and are not timed."""
     import oracle
 
-    x = sample["x"][:rows].float().cpu().numpy()
-    t = sample["t"][:rows].cpu().numpy()
-    g = sample["g"][:rows].cpu().numpy()
-    t0 = time.perf_counter()
-    for r0 in range(0, rows, 128):
-        xs, ts, gs = x[r0:r0 + 128], t[r0:r0 + 128], g[r0:r0 + 128]
+    block = 64
+    done, spent = 0, 0.0
+    while done < max_rows and spent < budget_s:
+        r1 = min(max_rows, done + block)
+        xs = sample["x"][done:r1].float().cpu().numpy()
+        ts = sample["t"][done:r1].cpu().numpy()
+        gs = sample["g"][done:r1].cpu().numpy()
+        t0 = time.perf_counter()
         _, lse = oracle.logp_fwd(xs, ts)
         d = oracle.logp_bwd(xs, ts, gs, lse=lse)
+        spent += time.perf_counter() - t0
         del d
-    dt = time.perf_counter() - t0
-    del np
-    return {"value": round(rows / dt, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} rows of the same [8192, 151936] bf16 batch, "
-                      f"float64 numpy forward+backward in 128-row blocks, {dt:.1f} s",
+        done = r1
+    return {"value": round(done / spent, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} rows of the same [8192, 151936] bf16 batch, float64 "
+                      f"numpy forward+backward in {block}-row blocks, {spent:.1f} s of "
+                      "oracle time (one thread)",
             "cpu": cpu_model()}
 
 
@@ -282,6 +285,101 @@ def cpu_baseline_linear(sample, rows):
             "cpu": cpu_model()}
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic summaries from two rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE) of `bench.py --calibrate-copy`: counters are KiB per dispatch and
+# are scaled by what the same counter reads on the plain 1 GiB device copies
+# that --calibrate-copy runs first (1 GiB read + 1 GiB written each).
+# ---------------------------------------------------------------------------
+
+def _short_kernel(name):
+    base = name.replace("(anonymous namespace)", "").split("(")[0].split("<")[0]
+    return base.split("::")[-1].strip()
+
+
+def _counter_rows(run_dir, counter):
+    """(dispatch id, short kernel name, value) of every dispatch in the
+    counter_collection CSV files under run_dir."""
+    import csv
+    import glob
+
+    per = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (path, row["Dispatch_Id"])
+                name = _short_kernel(row["Kernel_Name"])
+                val = float(row["Counter_Value"])
+                if key in per:
+                    per[key] = (name, per[key][1] + val)
+                else:
+                    per[key] = (name, val)
+    return [(k[1], nm, v) for k, (nm, v) in sorted(per.items(), key=lambda kv: int(kv[0][1]))]
+
+
+def _algorithmic_bytes(workload, kernel):
+    """Algorithmic bytes per launch of a kernel on a workload: the logits of
+    active rows read once (forward and backward), the gradient written once
+    for every row, plus 16 B of per-row scalars; for the fused LM head the
+    weight and hidden states read once and the per-row outputs."""
+    if workload == "qwen3_8192x151936":
+        n, v = 8192, 151936
+        act = n - int(0.10 * n)
+        if kernel == "logp_bwd_kernel":
+            return act * v * 2 + n * v * 2 + n * 16
+        return act * v * 2 + n * 16
+    if workload == "qwen3_4096x151936":
+        n, v = 4096, 151936
+        return (n - int(0.05 * n)) * v * 2 + n * 16
+    if workload == "qwen3_4096x4096x151936":
+        n, h, v = 4096, 4096, 151936
+        return v * h * 2 + n * h * 2 + n * 16
+    raise ValueError(workload)
+
+
+def summarize_traffic(fetch_dir, write_dir, workload, kernels, fetch_cmd, write_cmd):
+    fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
+    write = _counter_rows(write_dir, "WRITE_SIZE")
+
+    def calib(rows):
+        vals = sorted(v for _, nm, v in rows if nm == "__amd_rocclr_copyBuffer")[-3:]
+        if len(vals) < 3:
+            raise SystemExit("no 1 GiB calibration copies found (run with --calibrate-copy)")
+        return sum(vals) / len(vals)
+
+    cf, cw = calib(fetch), calib(write)
+    written = []
+    for k in kernels:
+        fv = [v for _, nm, v in fetch if nm == k]
+        wv = [v for _, nm, v in write if nm == k]
+        if not fv or not wv:
+            raise SystemExit(f"kernel {k} not found in the counter runs")
+        f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
+        fs, ws = 1048576.0 / cf, 1048576.0 / cw
+        hbm = (f_kib * fs + w_kib * ws) * 1024.0
+        alg = _algorithmic_bytes(workload, k)
+        path = os.path.join(PROFILES, f"traffic_{k}_{workload}.txt")
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic of {k} on workload {workload}, from two rocprofv3 --pmc runs\n")
+            f.write(f"# fetch command: {fetch_cmd}\n# write command: {write_cmd}\n")
+            f.write("# counters are KiB per dispatch; scale factors come from the same counters "
+                    "read on\n# plain 1 GiB device copies (__amd_rocclr_copyBuffer, 1 GiB read + "
+                    "1 GiB written) in the same run\n")
+            f.write(f"kernel={k}\nworkload={workload}\n")
+            f.write(f"source_sha256_16={kernel_source_hash(k)}\n")
+            f.write(f"dispatches_fetch={len(fv)}\ndispatches_write={len(wv)}\n")
+            f.write(f"fetch_kib_per_dispatch={f_kib:.1f}\nwrite_kib_per_dispatch={w_kib:.1f}\n")
+            f.write(f"copy_fetch_kib_per_gib={cf:.1f}\ncopy_write_kib_per_gib={cw:.1f}\n")
+            f.write(f"fetch_scale={fs:.5f}\nwrite_scale={ws:.5f}\n")
+            f.write(f"hbm_bytes_per_launch={hbm:.0f}\nalgorithmic_bytes_per_launch={alg}\n")
+            f.write(f"traffic_over_algorithmic={hbm / alg:.4f}\n")
+        written.append(path)
+    return written
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,11 +388,25 @@ def main():
     ap.add_argument("--workload", default="fwd_bwd", choices=["fwd_bwd", "fwd", "linear"])
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows for the CPU oracle baseline (0 = workload default)")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0,
+                    help="oracle time budget of the CPU baseline (fwd_bwd workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run three plain 1 GiB device copies (a known byte count "
                          "for scaling HBM counters)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc output folders (FETCH_SIZE, "
+                         "WRITE_SIZE) of this workload into profiles/traffic_*.txt")
+    ap.add_argument("--pmc-commands", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"),
+                    default=("?", "?"), help="the two commands, recorded in the summaries")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        wl, ks = {"fwd_bwd": ("qwen3_8192x151936", ["logp_fwd_fused_kernel", "logp_bwd_kernel"]),
+                  "fwd": ("qwen3_4096x151936", ["logp_fwd_fused_kernel"]),
+                  "linear": ("qwen3_4096x4096x151936", ["linear_stats_dma"])}[args.workload]
+        for p in summarize_traffic(*args.summarize_traffic, wl, ks, *args.pmc_commands):
+            print(p)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(rows are independent, so data-parallel scaling needs no exchange); "
@@ -323,7 +435,8 @@ def main():
     out, sample = runner(args, torch, itl, synth)
     if sample is not None:
         if args.workload == "fwd_bwd":
-            out["cpu_baseline"] = cpu_baseline_fwd_bwd(sample, args.cpu_rows or 8192)
+            out["cpu_baseline"] = cpu_baseline_fwd_bwd(sample, args.cpu_rows or 8192,
+                                                       args.cpu_budget_s)
         elif args.workload == "linear":
             out["cpu_baseline"] = cpu_baseline_linear(sample, args.cpu_rows or 512)
     if "cpu_baseline" in out and out["cpu_baseline"]["value"]:
