@@ -76,6 +76,16 @@ def cpu_model():
     return "unknown"
 
 
+def ramp(torch, fn, seconds):
+    """Run fn() untimed until `seconds` of wall time have passed, so that the
+    GPU clocks have left their idle state before any warmup or timed step."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_events(torch, fn, steps):
     """Mean device time of fn() over `steps` calls, with events on the
     current stream (the stream every library call launches on)."""
@@ -109,6 +119,7 @@ def bench_fwd_bwd(args, torch, itl, synth):
         fwd()
         bwd()
 
+    ramp(torch, step, args.ramp_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -203,6 +214,7 @@ def bench_fwd(args, torch, itl, synth):
     def fwd():
         itl.logp_fwd(x, t, -100, w, logp_out=logp, lse_out=lse)
 
+    ramp(torch, fwd, args.ramp_s)
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
@@ -239,6 +251,7 @@ def bench_linear(args, torch, itl, synth):
     def run():
         itl.linear_logp_fwd(hid, wt, t, -100, 256, logp_out=logp, lse_out=lse, workspace=ws)
 
+    ramp(torch, run, args.ramp_s)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -385,6 +398,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ramp-s", type=float, default=0.5,
+                    help="untimed seconds of steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--workload", default="fwd_bwd", choices=["fwd_bwd", "fwd", "linear"])
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows for the CPU oracle baseline (0 = workload default)")

@@ -7,19 +7,23 @@
 
 namespace itl {
 
-constexpr int kBlock = 256;               // 4 waves
+constexpr int kBlock = 256;               // 4 waves (merge kernel, backward)
 constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kFwdBlock = 512;            // 8 waves per row in the forward kernels
+constexpr int kFwdWaves = kFwdBlock / kWave;
 constexpr int64_t kMaxRowBlocks = 1 << 20;  // grid-stride beyond this
+constexpr int64_t kMaxGridY = 65535;        // backward grid rows (grid-stride beyond)
 
 // ---------------------------------------------------------------------------
 // Single-launch forward ("Batch-Invariant LogP", Tensor Parallel with one
-// shard).  One workgroup per row (grid-stride over rows); wave w reduces the
-// tiles k = w, w + 4, ... and parks (m_k, s_k) in LDS; wave 0 merges them in
-// ascending order, copies the target logit and writes logp and lse.  Ignored
-// rows are not read.
+// shard).  One workgroup per row (grid-stride over rows); wave w of 8 reduces
+// the tiles k = w, w + 8, ... and parks (m_k, s_k) in LDS; wave 0 merges them
+// in ascending order, copies the target logit and writes logp and lse.
+// Ignored rows are not read.  Which wave reduces a tile changes no bit: the
+// tile statistic depends only on the tile.
 // ---------------------------------------------------------------------------
 template <typename T, int C, bool VEC>
-__global__ __launch_bounds__(kBlock) void logp_fwd_fused_kernel(
+__global__ __launch_bounds__(kFwdBlock) void logp_fwd_fused_kernel(
     const T* __restrict__ logits, int64_t ld, int64_t n, int64_t v,
     const int64_t* __restrict__ targets, int64_t ignore_index, int ntiles,
     float* __restrict__ logp, float* __restrict__ lse, int* __restrict__ status) {
@@ -39,7 +43,7 @@ __global__ __launch_bounds__(kBlock) void logp_fwd_fused_kernel(
       continue;
     }
     const T* row = logits + r * ld;
-    for (int k = wave; k < ntiles; k += kWavesPerBlock) {
+    for (int k = wave; k < ntiles; k += kFwdWaves) {
       float mk, sk;
       tile_stats<T, C, VEC>(row, static_cast<int64_t>(k) * W, v, mk, sk);
       if (lane == 0) {
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(kBlock) void logp_fwd_fused_kernel(
 // logit into pt[r].  Ignored rows are skipped (the merge never reads them).
 // ---------------------------------------------------------------------------
 template <typename T, int C, bool VEC>
-__global__ __launch_bounds__(kBlock) void logp_partials_kernel(
+__global__ __launch_bounds__(kFwdBlock) void logp_partials_kernel(
     const T* __restrict__ logits, int64_t ld, int64_t n, int64_t v,
     const int64_t* __restrict__ targets, int64_t ignore_index, int k_begin,
     int k_end, float* __restrict__ pm, float* __restrict__ ps,
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(kBlock) void logp_partials_kernel(
     const int64_t t = targets[r];
     if (t == ignore_index) continue;
     const T* row = logits + r * ld;
-    for (int k = k_begin + wave; k < k_end; k += kWavesPerBlock) {
+    for (int k = k_begin + wave; k < k_end; k += kFwdWaves) {
       float mk, sk;
       tile_stats<T, C, VEC>(row, static_cast<int64_t>(k) * W, v, mk, sk);
       if (lane == 0) {
@@ -133,8 +137,9 @@ __global__ __launch_bounds__(kBlock) void logp_merge_kernel(
 //   p = exp(x - lse);  u = 1 - p on the target column, -p elsewhere;
 //   d = g * u rounded to the logits dtype (RNE).
 // g * (-p) is computed as (-g) * p, which is the same IEEE product.
-// One workgroup per row (grid-stride); each thread moves 16-byte chunks, four
-// in flight.  Ignored rows are written +0 without reading the logits.
+// Grid: x = 256-chunk segments of a row, y = rows; one 16-byte chunk per
+// thread, non-temporal loads and stores.  Ignored rows are written +0 without
+// reading the logits.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const __bf16 a = static_cast<__bf16>(lo);
@@ -192,37 +197,35 @@ __global__ __launch_bounds__(kBlock) void logp_bwd_kernel(
     const float* __restrict__ lse, const float* __restrict__ grad, T* dlogits,
     int64_t ld_out) {
   constexpr int E = Elt<T>::kPerChunk;
-  constexpr int U = 4;
-  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+  // Thread (x, tid) owns the 16-byte chunk c = x * 256 + tid of every row it
+  // visits: consecutive workgroups walk along a row, so the whole launch
+  // streams the matrix in address order.
+  const int64_t j0 = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * E;
+  if (j0 >= v) return;
+  const bool full = VEC && j0 + E <= v;
+  for (int64_t r = blockIdx.y; r < n; r += gridDim.y) {
     const int64_t t = targets[r];
     T* orow = dlogits + r * ld_out;
-    const int64_t nchunk = VEC ? v / E : 0;
     if (t == ignore_index) {
-      for (int64_t c = threadIdx.x; c < nchunk; c += kBlock)
-        *reinterpret_cast<uint4*>(orow + c * E) = make_uint4(0u, 0u, 0u, 0u);
-      for (int64_t j = nchunk * E + threadIdx.x; j < v; j += kBlock) store_elem<T>(orow, j, 0.0f);
+      if (full) {
+        store_stream(orow + j0, make_uint4(0u, 0u, 0u, 0u));
+      } else {
+        for (int e = 0; e < E; ++e)
+          if (j0 + e < v) store_elem<T>(orow, j0 + e, 0.0f);
+      }
       continue;
     }
     const T* row = logits + r * ld;
     const float L = lse[r];
     const float g = grad[r];
     const float ng = -g;
-    for (int64_t c0 = threadIdx.x; c0 < nchunk; c0 += kBlock * U) {
-      uint4 q[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + u * kBlock;
-        if (c < nchunk) q[u] = *reinterpret_cast<const uint4*>(row + c * E);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + u * kBlock;
-        if (c < nchunk)
-          *reinterpret_cast<uint4*>(orow + c * E) = grad_chunk<T>(q[u], L, g, ng, c * E, t);
-      }
+    if (full) {
+      store_stream(orow + j0, grad_chunk<T>(load_stream(row + j0), L, g, ng, j0, t));
+    } else {
+      for (int e = 0; e < E; ++e)
+        if (j0 + e < v)
+          store_elem<T>(orow, j0 + e, grad_elem(Elt<T>::load(row, j0 + e), L, g, ng, j0 + e == t));
     }
-    for (int64_t j = nchunk * E + threadIdx.x; j < v; j += kBlock)
-      store_elem<T>(orow, j, grad_elem(Elt<T>::load(row, j), L, g, ng, j == t));
   }
 }
 
@@ -242,7 +245,7 @@ static void fused_dispatch(int chunks, const void* logits, int64_t ld, int64_t n
 #define ITL_FUSED(CC)                                                                   \
   case CC:                                                                              \
     hipLaunchKernelGGL((logp_fwd_fused_kernel<T, CC, VEC>), dim3(row_grid(n)),          \
-                       dim3(kBlock), lds, s, x, ld, n, v, targets, ignore, ntiles, logp, \
+                       dim3(kFwdBlock), lds, s, x, ld, n, v, targets, ignore, ntiles, logp, \
                        lse, status);                                                    \
     break;
   switch (chunks) { ITL_FUSED(1) ITL_FUSED(2) ITL_FUSED(4) ITL_FUSED(8) ITL_FUSED(16) }
@@ -257,7 +260,7 @@ static void partials_dispatch(int chunks, const void* logits, int64_t ld, int64_
 #define ITL_PART(CC)                                                                     \
   case CC:                                                                               \
     hipLaunchKernelGGL((logp_partials_kernel<T, CC, VEC>), dim3(row_grid(n)),            \
-                       dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, kb, ke, pm, ps, \
+                       dim3(kFwdBlock), 0, s, x, ld, n, v, targets, ignore, kb, ke, pm, ps, \
                        pt);                                                              \
     break;
   switch (chunks) { ITL_PART(1) ITL_PART(2) ITL_PART(4) ITL_PART(8) ITL_PART(16) }
@@ -303,7 +306,10 @@ void launch_fwd_merge(const float* pm, const float* ps, const float* pt, int64_t
 void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, int64_t v,
                 const int64_t* targets, int64_t ignore, const float* lse, const float* grad,
                 void* dlogits, int64_t ld_out, hipStream_t s) {
-  const dim3 grid(row_grid(n));
+  const int64_t per = dtype == kF32 ? 4 : 8;  // elements per 16-byte chunk
+  const int64_t chunks = (v + per - 1) / per;
+  const dim3 grid(static_cast<unsigned>((chunks + kBlock - 1) / kBlock),
+                  static_cast<unsigned>(n < kMaxGridY ? n : kMaxGridY));
   if (dtype == kF32) {
     const float* x = static_cast<const float*>(logits);
     float* d = static_cast<float*>(dlogits);
