@@ -27,7 +27,8 @@ Sources (page title -- section):
 * "[RFC][ROCm] End-to-end optimization of bitwise VIME R/R beyond native P/P"
   -- Workstream 3 (fused ROCm LM-head and linear logp): the logits are the
   product of the hidden states with the LM-head weight, and the same
-  statistics are taken over them without storing them.
+  statistics are taken over them without storing them; the backward may
+  recompute the fixed logit tiles from the saved LSE.
 
 Parity pins live in tests/test_oracle_pins.py; every function below is pinned
 there by closed forms, brute force, a library routine or an invariant.
@@ -163,6 +164,37 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100):
         z = linear_logits(h[r0:r1], weight)
         logp[r0:r1], lse[r0:r1] = logp_fwd(z, t[r0:r1], ignore_index)
     return logp, lse
+
+
+def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=None):
+    """Gradients of sum_r g_r * logp_r of the fused LM head, in float64.
+
+    "[RFC][ROCm] ..." -- Workstream 3 (the backward recomputes the logit
+    tiles from the saved LSE) and "Batch-Invariant LogP" -- Batch-Invariance
+    (the logit gradient is g * (onehot - softmax), zero on ignored rows):
+        z  = h @ W^T
+        dz = g * (onehot(t) - exp(z - lse))        (rows with t == ignore: 0)
+        dh = dz @ W,    dW = dz^T @ h
+    lse is the float64 row LSE of z (recomputed when not given).  Rows are
+    processed in blocks; dW sums the blocks in ascending row order.
+    Returns (dh [N, H], dW [V, H]) as float64."""
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    n = h.shape[0]
+    t = np.asarray(targets, dtype=np.int64).reshape(-1)
+    g = np.asarray(grad_logp, dtype=np.float64).reshape(-1)
+    if t.shape[0] != n or g.shape[0] != n:
+        raise ValueError("targets and grad_logp need one entry per row")
+    dh = np.zeros_like(h)
+    dw = np.zeros_like(w)
+    for r0 in range(0, n, ROW_CHUNK):
+        r1 = min(n, r0 + ROW_CHUNK)
+        z = linear_logits(h[r0:r1], w)
+        row_lse = None if lse is None else np.asarray(lse, dtype=np.float64).reshape(-1)[r0:r1]
+        dz = logp_bwd(z, t[r0:r1], g[r0:r1], ignore_index, lse=row_lse)
+        dh[r0:r1] = dz @ w
+        dw += dz.T @ h[r0:r1]
+    return dh, dw
 
 
 # ---------------------------------------------------------------------------

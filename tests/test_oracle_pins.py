@@ -340,3 +340,108 @@ def test_linear_brute_force():
         assert abs(logp[r] - _brute(z, t[r])) <= 1e-13
     with pytest.raises(ValueError):
         oracle.linear_logp_fwd(h, w.T, t)
+
+
+# ----- fused LM head backward --------------------------------------------------
+
+def _objective(h, w, t, g):
+    """sum_r g_r * logp_r written out with math.fsum (no numpy reductions)."""
+    total = []
+    for r in range(h.shape[0]):
+        if t[r] == -100:
+            continue
+        z = [math.fsum(float(h[r, k]) * float(w[j, k]) for k in range(h.shape[1]))
+             for j in range(w.shape[0])]
+        m = max(z)
+        lse = m + math.log(math.fsum(math.exp(a - m) for a in z))
+        total.append(g[r] * (z[t[r]] - lse))
+    return math.fsum(total)
+
+
+def test_linear_bwd_finite_difference():
+    """Central differences of sum g*logp in h and in W reproduce dh and dW
+    (a transposed product, a dropped g or a wrong sign fails)."""
+    rng = np.random.default_rng(21)
+    n, hd, v = 3, 4, 5
+    h = rng.normal(size=(n, hd))
+    w = rng.normal(size=(v, hd))
+    t = [2, -100, 4]
+    g = np.array([0.7, 1.3, -1.1])
+    dh, dw = oracle.linear_logp_bwd(h, w, t, g)
+    eps = 1e-6
+    for (arr, grad) in ((h, dh), (w, dw)):
+        for idx in np.ndindex(arr.shape):
+            a = arr.copy(); a[idx] += eps
+            b = arr.copy(); b[idx] -= eps
+            if arr is h:
+                fp, fm = _objective(a, w, t, g), _objective(b, w, t, g)
+            else:
+                fp, fm = _objective(h, a, t, g), _objective(h, b, t, g)
+            num = (fp - fm) / (2 * eps)
+            assert abs(num - grad[idx]) <= 1e-7, (idx, num, grad[idx])
+    assert np.all(dh[1] == 0.0)
+
+
+def test_linear_bwd_library_autograd():
+    """torch float64 autograd of log_softmax(h W^T).gather(t), weighted by g
+    ("Batch-Invariant LogP", Reference Semantics), gives the same dh, dW."""
+    rng = np.random.default_rng(22)
+    n, hd, v = 12, 16, 40
+    h = rng.normal(size=(n, hd))
+    w = rng.normal(size=(v, hd)) * 0.5
+    t = rng.integers(0, v, n)
+    t[5] = -100
+    g = rng.normal(size=n)
+    dh, dw = oracle.linear_logp_bwd(h, w, t, g)
+    th = torch.tensor(h, requires_grad=True)
+    tw = torch.tensor(w, requires_grad=True)
+    z = th @ tw.T
+    lp = torch.log_softmax(z, dim=-1)
+    tt = torch.tensor(t)
+    mask = tt != -100
+    sel = lp[mask].gather(1, tt[mask].unsqueeze(1)).squeeze(1)
+    (sel * torch.tensor(g)[mask]).sum().backward()
+    np.testing.assert_allclose(dh, th.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dw, tw.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_linear_bwd_identity_and_equal_rows():
+    """W = I: dz is logp_bwd of h itself, dh = dz and dW = dz^T h.  A weight
+    whose rows are all equal gives dh = 0 (each gradient row sums to 0)."""
+    rng = np.random.default_rng(23)
+    h = rng.normal(size=(9, 32))
+    t = rng.integers(0, 32, 9)
+    t[0] = -100
+    g = rng.normal(size=9)
+    dh, dw = oracle.linear_logp_bwd(h, np.eye(32), t, g)
+    dz = oracle.logp_bwd(h, t, g)
+    np.testing.assert_allclose(dh, dz, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(dw, dz.T @ h, rtol=1e-14, atol=1e-14)
+    w = np.tile(rng.normal(size=(1, 32)), (50, 1))
+    t2 = rng.integers(0, 50, 9)
+    dh2, _ = oracle.linear_logp_bwd(h, w, t2, g)
+    assert np.all(np.abs(dh2) <= 1e-12)
+
+
+def test_linear_bwd_ignored_rows_add_nothing():
+    """Appending ignored rows changes neither dW nor the other rows' dh; the
+    given lse is used (a shifted lse scales the softmax part)."""
+    rng = np.random.default_rng(24)
+    h = rng.normal(size=(6, 8))
+    w = rng.normal(size=(20, 8))
+    t = rng.integers(0, 20, 6)
+    g = rng.normal(size=6)
+    dh, dw = oracle.linear_logp_bwd(h, w, t, g)
+    h2 = np.vstack([h, rng.normal(size=(3, 8))])
+    t2 = np.concatenate([t, [-100, -100, -100]])
+    g2 = np.concatenate([g, [5.0, 6.0, 7.0]])
+    dh2, dw2 = oracle.linear_logp_bwd(h2, w, t2, g2)
+    np.testing.assert_allclose(dh2[:6], dh, rtol=0, atol=1e-15)
+    assert np.all(dh2[6:] == 0.0)
+    np.testing.assert_allclose(dw2, dw, rtol=1e-14, atol=1e-15)
+    _, lse = oracle.linear_logp_fwd(h, w, t)
+    dh3, _ = oracle.linear_logp_bwd(h, w, t, g, lse=lse + math.log(2.0))
+    z = h @ w.T
+    p = np.exp(z - lse[:, None])
+    want = dh - (-(g[:, None] * p * 0.5)) @ w
+    np.testing.assert_allclose(dh3, want, rtol=1e-12, atol=1e-13)
