@@ -12,7 +12,8 @@ prices the dominant kernel's algorithmic bytes against the MI355X HBM peak;
 cpu_baseline times the float64 CPU oracle on a bounded row sample of the same
 workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload fwd_bwd|fwd|linear]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+                    [--workload fwd_bwd|fwd|linear|linear_bwd]
 """
 
 import argparse
@@ -281,6 +282,46 @@ def bench_linear(args, torch, itl, synth):
     return out, sample
 
 
+def bench_linear_bwd(args, torch, itl, synth):
+    n, h, v = 4096, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB
+    dev = torch.device("cuda", 0)
+    c = synth.qwen3_linear(n=n, h=h, v=v, device=dev, ignore_frac=0.05)
+    hid, wt, t = c["hidden"], c["weight"], c["targets"]
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, 1055, dev)[0]
+    _, lse = itl.linear_logp_fwd(hid, wt, t)
+    dh = torch.empty(n, h, dtype=torch.float32, device=dev)
+    dw = torch.empty(v, h, dtype=torch.float32, device=dev)
+    ws = torch.empty(itl.lib().linear_logp_bwd_workspace_bytes(n, h, v, 256), dtype=torch.uint8,
+                     device=dev)
+
+    def run():
+        itl.linear_logp_bwd(hid, wt, t, lse, g, dhidden_out=dh, dweight_out=dw, workspace=ws)
+
+    ramp(torch, run, args.ramp_s)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ms = time_events(torch, run, args.steps)
+    flops = 3 * 2.0 * n * h * v  # z recomputed, dh = dz W, dW = dz^T h
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "rows/s and MFMA TFLOP/s (% of peak), fused LM-head+logp backward N=4096 "
+                  "H=4096 V=151936 bf16",
+        "value": round(n / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_lm_head_linear_logp_bwd", "n": n, "h": h, "v": v,
+                   "tile_width": 256, "outputs": "dh, dW fp32"},
+        "tflops": round(tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "linear_logp_bwd (all five launches: dz, two transposes, "
+                               "two products)"},
+    }, None
+
+
 def cpu_baseline_linear(sample, rows):
     import oracle
 
@@ -400,7 +441,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ramp-s", type=float, default=0.5,
                     help="untimed seconds of steps before the warmup steps (GPU clock ramp)")
-    ap.add_argument("--workload", default="fwd_bwd", choices=["fwd_bwd", "fwd", "linear"])
+    ap.add_argument("--workload", default="fwd_bwd",
+                    choices=["fwd_bwd", "fwd", "linear", "linear_bwd"])
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows for the CPU oracle baseline (0 = workload default)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
@@ -446,7 +488,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    runner = {"fwd_bwd": bench_fwd_bwd, "fwd": bench_fwd, "linear": bench_linear}[args.workload]
+    runner = {"fwd_bwd": bench_fwd_bwd, "fwd": bench_fwd, "linear": bench_linear,
+              "linear_bwd": bench_linear_bwd}[args.workload]
     out, sample = runner(args, torch, itl, synth)
     if sample is not None:
         if args.workload == "fwd_bwd":

@@ -173,6 +173,49 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight,
                         void* workspace, size_t workspace_bytes,
                         void* hip_stream);
 
+/*
+ * Workspace of linear_logp_bwd in bytes: W^T [h, Vp], h^T [h, Np], dz [Np, Vp]
+ * and dz^T [Vp, Np], all bf16, with Np, Vp = n, v rounded up to multiples of
+ * 256 (about 3.8 GB at n = 4096, h = 4096, v = 151936).  0 when n = 0 or for
+ * arguments linear_logp_bwd would reject.
+ */
+size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width);
+
+/*
+ * Backward of the fused LM head + log-probability ("[RFC][ROCm] End-to-end
+ * optimization of bitwise VIME R/R beyond native P/P", Workstream 3: the
+ * backward recomputes the fixed logit tiles from the saved LSE; "Batch-
+ * Invariant LogP", Batch-Invariance and Reference Semantics: the logit
+ * gradient is g * (onehot - softmax), zero on ignored rows):
+ *   z  = hidden weight^T          (recomputed with the forward's MFMA walk)
+ *   dz = RNE_bf16(g * (onehot(t) - exp(z - lse)))
+ *   dhidden = dz weight           (fp32 accumulation, K = vocabulary ascending)
+ *   dweight = dz^T hidden         (fp32 accumulation, K = tokens ascending)
+ * No product is split, so dhidden[r] depends only on row r and dweight is
+ * deterministic for a given row order.
+ *
+ *   hidden, ld_h, weight, ld_w, n, h, v, targets, ignore_index, tile_width:
+ *               as linear_logp_fwd (h a multiple of 64, tile_width 256,
+ *               16-byte aligned rows).
+ *   lse         fp32 [n] from linear_logp_fwd.
+ *   grad_logp   fp32 [n], the upstream gradient g.
+ *   out_dtype   LOGP_F32 (the accumulators) or LOGP_BF16 (RNE of them).
+ *   dhidden     [n, ld_dh] of out_dtype, or NULL to skip that product.
+ *   dweight     [v, ld_dw] of out_dtype, or NULL to skip that product (with
+ *               n = 0 it is written with zeros).  At least one is non-NULL.
+ *               Both are overwritten, not accumulated into.
+ *   workspace   at least linear_logp_bwd_workspace_bytes(...) bytes,
+ *               256-byte aligned (may be NULL when that is 0).
+ * Active targets outside [0, v) are not checked: such a row gets no one-hot
+ * term.
+ */
+int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                        int64_t n, int64_t h, int64_t v, const int64_t* targets,
+                        int64_t ignore_index, int32_t tile_width, const float* lse,
+                        const float* grad_logp, int32_t out_dtype, void* dhidden,
+                        int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
+                        size_t workspace_bytes, void* hip_stream);
+
 /* Short English text for a status code (static storage, host memory). */
 const char* logp_status_str(int32_t status);
 

@@ -9,6 +9,8 @@ from ._lib import LogpError, contract_id, lib, status_str  # noqa: F401
 from .ops import (  # noqa: F401
     LINEAR_TILE,
     batch_invariant_logp,
+    linear_logp,
+    linear_logp_bwd,
     linear_logp_fwd,
     logp_bwd,
     logp_fwd,

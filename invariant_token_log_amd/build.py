@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libinvariant_logp.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "logp_kernels.hip", "linear_logp.hip"]
+SOURCES = ["api.hip", "logp_kernels.hip", "linear_logp.hip", "linear_bwd.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

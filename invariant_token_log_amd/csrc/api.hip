@@ -177,6 +177,44 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
   return hip_status();
 }
 
+size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width) {
+  if (n < 0 || v < 1 || h < 64 || h % 64 || tile_width != itl::kLinearTile) return 0;
+  if (n == 0) return 0;
+  return static_cast<size_t>(itl::linear_bwd_layout(n, h, v).total);
+}
+
+int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                        int64_t n, int64_t h, int64_t v, const int64_t* targets,
+                        int64_t ignore_index, int32_t tile_width, const float* lse,
+                        const float* grad_logp, int32_t out_dtype, void* dhidden, int64_t ld_dh,
+                        void* dweight, int64_t ld_dw, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
+  if (n < 0 || v < 1 || h < 64 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
+  if (v > (int64_t{1} << 31) || n > (int64_t{1} << 31) ||
+      ((n + 255) / 256) * ((v + 255) / 256) > (int64_t{1} << 30) ||
+      ((v + 255) / 256) * ((h + 255) / 256) > (int64_t{1} << 30))
+    return LOGP_ERR_SHAPE;
+  if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
+  if (out_dtype != LOGP_F32 && out_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
+  if (!dhidden && !dweight) return LOGP_ERR_NULL;
+  if ((dhidden && ld_dh < h) || (dweight && ld_dw < h)) return LOGP_ERR_SHAPE;
+  if (n == 0 && !dweight) return LOGP_OK;
+  if (!weight || (n > 0 && (!hidden || !targets || !lse || !grad_logp))) return LOGP_ERR_NULL;
+  if ((n > 0 && !aligned16(hidden, ld_h, LOGP_BF16)) || !aligned16(weight, ld_w, LOGP_BF16))
+    return LOGP_ERR_ALIGN;
+  const size_t need = linear_logp_bwd_workspace_bytes(n, h, v, tile_width);
+  if (need && (!workspace || workspace_bytes < need ||
+               reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return LOGP_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  itl::launch_linear_bwd(static_cast<const uint16_t*>(hidden), ld_h,
+                         static_cast<const uint16_t*>(weight), ld_w, n, h, v, targets,
+                         ignore_index, lse, grad_logp, out_dtype == LOGP_BF16, dhidden, ld_dh,
+                         dweight, ld_dw, static_cast<char*>(workspace),
+                         static_cast<hipStream_t>(hip_stream));
+  return hip_status();
+}
+
 const char* logp_status_str(int32_t status) {
   switch (status) {
     case LOGP_OK: return "ok";
@@ -197,7 +235,8 @@ const char* logp_contract_id(void) {
   return "itl.logp.v1[tile=lane-asc-fold+xor1..32;tilestat=two-pass;merge=asc-fma;"
          "exp=v_exp_f32((a-b)*log2e);log=v_log_f32*ln2;bwd=rne(g*(onehot-p))]"
          "+itl.linear_logp.v1[mfma=f32_16x16x32_bf16;k=asc32-nosplit;tile=256;"
-         "tilestat=4x64(lane-asc-fold4+xor1..8)+(q0+q1)+(q2+q3)]/gfx950";
+         "tilestat=4x64(lane-asc-fold4+xor1..8)+(q0+q1)+(q2+q3);"
+         "bwd=dz:rne_bf16(g*(onehot-p)),dh:dz*W(k=vocab-asc32),dW:dz^T*h(k=token-asc32)]/gfx950";
 }
 
 }  // extern "C"

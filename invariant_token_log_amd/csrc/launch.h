@@ -37,4 +37,19 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
 
 constexpr int kLinearTile = 256;
 
+// Workspace of the fused LM-head backward (byte offsets): W^T [h, vp],
+// h^T [h, np], dz [np, vp], dz^T [vp, np], all bf16; np, vp = n, v rounded up
+// to multiples of 256.
+struct LinearBwdLayout {
+  int64_t np, vp;
+  int64_t wt, ht, dz, dzt, total;
+};
+LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
+
+// dh [n, h] and/or dW [v, h] (either may be null) as fp32 or bf16 (bf16_out).
+void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
+                       int64_t n, int64_t h, int64_t v, const int64_t* targets, int64_t ignore,
+                       const float* lse, const float* grad, bool bf16_out, void* dh,
+                       int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s);
+
 }  // namespace itl

@@ -1,0 +1,310 @@
+// Backward of the fused LM head + logp on gfx950 ("[RFC][ROCm] End-to-end
+// optimization of bitwise VIME R/R beyond native P/P", Workstream 3: the
+// backward recomputes the fixed logit tiles from the saved LSE; "Batch-
+// Invariant LogP", Batch-Invariance: the logit gradient is g * (onehot - p)).
+//
+//   z  = h W^T                (recomputed: the forward's MFMA tile and K walk,
+//                              so z has the forward's bits)
+//   dz = RNE_bf16(g * (onehot(t) - exp(z - lse)))   (0 on ignored and padded rows)
+//   dh = dz W                 (fp32 accumulators, K = vocabulary, ascending)
+//   dW = dz^T h               (fp32 accumulators, K = tokens, ascending)
+//
+// dz is rounded to bf16 once (the only rounding point besides the fp32
+// accumulators) because both products run on bf16 MFMA.  Every product is a
+// single ascending K walk with no split, so dh[r] depends only on row r (batch
+// invariant) and dW is deterministic for a given token order.
+//
+// Kernels (all on the 256 x 256 tile of mfma_gemm.h):
+//   linear_dz_kernel  : h x W^T tile -> dz tile in LDS -> dz [Np, Vp] and
+//                       dz^T [Vp, Np] (bf16, coalesced 16-byte stores);
+//   transpose_pad_bf16: W [V, H] -> W^T [H, Vp], h [N, H] -> h^T [H, Np], zero
+//                       padded, so that both products see K-contiguous operands;
+//   gemm_out_kernel   : C = A B^T with fp32 or RNE-bf16 output.
+// Np, Vp are N and V rounded up to multiples of 256; padded rows and columns
+// hold zeros and add exact zeros to the K walks.
+#include "launch.h"
+#include "logp_device.h"
+#include "mfma_gemm.h"
+
+namespace itl {
+
+namespace {
+
+using gemm::f32x4;
+
+constexpr int kT = gemm::kTile;
+constexpr int kDzStride = kT + 8;  // bf16 per LDS tile row (528 B, 16-byte aligned)
+
+__device__ __forceinline__ uint16_t bf16_bits(float d) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(d));
+}
+
+// dst[c][r] = r < rows ? src[r][c] : 0 for c < gridDim.x * 64 and r < rows_p
+// (a multiple of 64).  64 x 64 tiles through LDS; 16-byte global accesses.
+__global__ __launch_bounds__(256) void transpose_pad_bf16(const uint16_t* __restrict__ src,
+                                                          int64_t ld_src, int64_t rows,
+                                                          int64_t rows_p,
+                                                          uint16_t* __restrict__ dst,
+                                                          int64_t ld_dst) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int t = threadIdx.x;
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64; r0 < rows_p;
+       r0 += static_cast<int64_t>(gridDim.y) * 64) {
+    {
+      const int r = t / 4, cs = (t % 4) * 16;
+      uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+      if (r0 + r < rows) {
+        const uint16_t* p = src + (r0 + r) * ld_src + c0 + cs;
+        a = *reinterpret_cast<const uint4*>(p);
+        b = *reinterpret_cast<const uint4*>(p + 8);
+      }
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        tile[r][cs + 2 * e] = static_cast<uint16_t>(w[e] & 0xffffu);
+        tile[r][cs + 2 * e + 1] = static_cast<uint16_t>(w[e] >> 16);
+      }
+    }
+    __syncthreads();
+    {
+      const int c = t / 4, rs = (t % 4) * 16;
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w[e] = static_cast<uint32_t>(tile[rs + 2 * e][c]) |
+               (static_cast<uint32_t>(tile[rs + 2 * e + 1][c]) << 16);
+      uint16_t* p = dst + (c0 + c) * ld_dst + r0 + rs;
+      *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(p + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+    __syncthreads();
+  }
+}
+
+struct SmemDz {
+  union {
+    gemm::Stages st;                // main loop
+    uint16_t tile[kT][kDzStride];  // dz tile for the two layouts
+  } u;
+  float lse[kT];
+  float g[kT];
+  int code[kT];  // -2: no gradient (row past n or ignored); -1: target outside the block; else t - v0
+};
+
+__global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
+    const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
+    int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
+    const int64_t* __restrict__ targets, int64_t ignore_index, const float* __restrict__ lse,
+    const float* __restrict__ grad, uint16_t* __restrict__ dz, int64_t ld_dz,
+    uint16_t* __restrict__ dzt, int64_t ld_dzt) {
+  __shared__ __align__(16) SmemDz sm;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / 4, wn = wave % 4;
+  const int li = lane % 16, g = lane / 16;
+
+  int mb, vb;
+  gemm::tile_coords(gemm::xcd_logical(blockIdx.x, mblocks * vblocks), mblocks, vblocks, mb, vb);
+  const int64_t m0 = static_cast<int64_t>(mb) * kT;
+  const int64_t v0 = static_cast<int64_t>(vb) * kT;
+  if (tid < kT) {
+    const int64_t r = m0 + tid;
+    int code = -2;
+    float L = 0.0f, G = 0.0f;
+    if (r < n) {
+      const int64_t t = targets[r];
+      if (t != ignore_index) {
+        L = lse[r];
+        G = grad[r];
+        code = (t >= v0 && t < v0 + kT && t < v) ? static_cast<int>(t - v0) : -1;
+      }
+    }
+    sm.code[tid] = code;
+    sm.lse[tid] = L;
+    sm.g[tid] = G;
+  }
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  gemm::mainloop(sm.u.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
+                 static_cast<int>(hdim / gemm::kK), acc);
+  __syncthreads();
+
+  // p = exp(z - lse) with the forward's primitive; d = g (1 - p) on the
+  // target column, (-g) p elsewhere; RNE to bf16.
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = wm * 128 + i * 16 + 4 * g + q;
+      const int code = sm.code[lr];
+      const float L = sm.lse[lr], G = sm.g[lr];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int lc = wn * 64 + j * 16 + li;
+        float d = 0.0f;
+        if (code != -2 && v0 + lc < v) {
+          const float p = exp_sub(acc[i][j][q], L);
+          d = lc == code ? G * (1.0f - p) : (-G) * p;
+        }
+        sm.u.tile[lr][lc] = bf16_bits(d);
+      }
+    }
+  __syncthreads();
+  // dz rows: 256 rows x 32 chunks of 16 bytes.
+  for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
+    const int r = idx >> 5, c = (idx & 31) * 8;
+    store_stream(dz + (m0 + r) * ld_dz + v0 + c,
+                 *reinterpret_cast<const uint4*>(&sm.u.tile[r][c]));
+  }
+  // dz^T rows: 256 columns x 32 chunks of 8 rows; lanes walk the columns.
+  for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
+    const int c = idx & (kT - 1), r = (idx >> 8) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = static_cast<uint32_t>(sm.u.tile[r + 2 * e][c]) |
+             (static_cast<uint32_t>(sm.u.tile[r + 2 * e + 1][c]) << 16);
+    store_stream(dzt + (v0 + c) * ld_dzt + m0 + r, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+}
+
+// C[m_out, n_out] = A[., K] B[., K]^T on the mfma_gemm.h tile; BF16OUT rounds
+// the fp32 accumulators to bf16 (RNE) on the way out.
+template <bool BF16OUT>
+__global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int64_t arows, const uint16_t* __restrict__ B,
+    int64_t ldb, int64_t brows, int ksteps, int mblocks, int nblocks, int64_t m_out,
+    int64_t n_out, void* __restrict__ C, int64_t ldc) {
+  __shared__ __align__(16) gemm::Stages st;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / 4, wn = wave % 4;
+  const int li = lane % 16, g = lane / 16;
+  int mb, nb;
+  gemm::tile_coords(gemm::xcd_logical(blockIdx.x, mblocks * nblocks), mblocks, nblocks, mb, nb);
+  const int64_t m0 = static_cast<int64_t>(mb) * kT;
+  const int64_t n0 = static_cast<int64_t>(nb) * kT;
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  gemm::mainloop(st, A, lda, m0, arows, B, ldb, n0, brows, ksteps, acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = m0 + wm * 128 + i * 16 + 4 * g + q;
+      if (row >= m_out) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + wn * 64 + j * 16 + li;
+        if (col < n_out) {
+          if (BF16OUT)
+            static_cast<uint16_t*>(C)[row * ldc + col] = bf16_bits(acc[i][j][q]);
+          else
+            static_cast<float*>(C)[row * ldc + col] = acc[i][j][q];
+        }
+      }
+    }
+}
+
+// Zero rows x cols of C (a sum over no tokens).
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void fill_zero_kernel(void* C, int64_t ldc, int64_t rows,
+                                                        int64_t cols) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < rows * cols;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = i / cols, c = i - r * cols;
+    if (BF16OUT)
+      static_cast<uint16_t*>(C)[r * ldc + c] = 0;
+    else
+      static_cast<float*>(C)[r * ldc + c] = 0.0f;
+  }
+}
+
+int64_t round_tile(int64_t x) { return (x + kT - 1) / kT * kT; }
+
+// grid rows of a transpose over rows_p (grid-stride beyond 65535 blocks)
+unsigned tgrid(int64_t rows_p) {
+  const int64_t b = rows_p / 64;
+  return static_cast<unsigned>(b < 65535 ? b : 65535);
+}
+
+void launch_gemm(bool bf16, const uint16_t* A, int64_t lda, int64_t arows, const uint16_t* B,
+                 int64_t ldb, int64_t brows, int64_t k, int64_t m_out, int64_t n_out, void* C,
+                 int64_t ldc, hipStream_t s) {
+  const int mblocks = static_cast<int>((m_out + kT - 1) / kT);
+  const int nblocks = static_cast<int>((n_out + kT - 1) / kT);
+  const int ksteps = static_cast<int>(k / gemm::kK);
+  if (bf16)
+    hipLaunchKernelGGL(gemm_out_kernel<true>, dim3(mblocks * nblocks), dim3(gemm::kThreads), 0, s,
+                       A, lda, arows, B, ldb, brows, ksteps, mblocks, nblocks, m_out, n_out, C,
+                       ldc);
+  else
+    hipLaunchKernelGGL(gemm_out_kernel<false>, dim3(mblocks * nblocks), dim3(gemm::kThreads), 0,
+                       s, A, lda, arows, B, ldb, brows, ksteps, mblocks, nblocks, m_out, n_out, C,
+                       ldc);
+}
+
+}  // namespace
+
+LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
+  const int64_t np = round_tile(n), vp = round_tile(v);
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  LinearBwdLayout l;
+  l.np = np;
+  l.vp = vp;
+  l.wt = 0;
+  l.ht = l.wt + up(h * vp * 2);
+  l.dz = l.ht + up(h * np * 2);
+  l.dzt = l.dz + up(np * vp * 2);
+  l.total = l.dzt + up(vp * np * 2);
+  return l;
+}
+
+void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
+                       int64_t n, int64_t h, int64_t v, const int64_t* targets, int64_t ignore,
+                       const float* lse, const float* grad, bool bf16_out, void* dh,
+                       int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s) {
+  if (n == 0) {
+    // dh has no rows; dW is a sum over no tokens.
+    if (dw) {
+      const int64_t want = (v * h + 255) / 256;
+      const unsigned blocks = static_cast<unsigned>(want < 8192 ? want : 8192);
+      if (bf16_out)
+        hipLaunchKernelGGL(fill_zero_kernel<true>, dim3(blocks), dim3(256), 0, s, dw, ld_dw, v, h);
+      else
+        hipLaunchKernelGGL(fill_zero_kernel<false>, dim3(blocks), dim3(256), 0, s, dw, ld_dw, v, h);
+    }
+    return;
+  }
+  const LinearBwdLayout l = linear_bwd_layout(n, h, v);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + l.wt);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(ws + l.ht);
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + l.dz);
+  uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + l.dzt);
+  const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
+  hipLaunchKernelGGL(linear_dz_kernel, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0, s,
+                     hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets, ignore, lse,
+                     grad, dz, l.vp, dzt, l.np);
+  if (dh) {
+    hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
+                       dim3(256), 0, s, weight, ld_w, v, l.vp, wt, l.vp);
+    launch_gemm(bf16_out, dz, l.vp, l.np, wt, l.vp, h, l.vp, n, h, dh, ld_dh, s);
+  }
+  if (dw) {
+    hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.np)),
+                       dim3(256), 0, s, hidden, ld_h, n, l.np, ht, l.np);
+    launch_gemm(bf16_out, dzt, l.np, l.vp, ht, l.np, h, l.np, v, h, dw, ld_dw, s);
+  }
+}
+
+}  // namespace itl

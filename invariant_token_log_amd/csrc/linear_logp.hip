@@ -23,48 +23,28 @@
 // the grid.
 //
 // Two kernels share this contract:
-//   * linear_stats_dma (N > 128): 256 x 256 block, eight waves of 128 x 64 (two
-//     per SIMD, so each hides the other's LDS and barrier latency), operands
-//     streamed global -> LDS by direct 16-byte LDS loads through a four-stage
-//     ring (three K steps in flight), XOR-swizzled LDS rows;
+//   * linear_stats_dma (N > 128): the 256 x 256 MFMA tile of mfma_gemm.h,
+//     eight waves of 128 x 64 (two per SIMD, so each hides the other's LDS
+//     and barrier latency), operands streamed global -> LDS by direct 16-byte
+//     LDS loads through a four-stage ring;
 //   * linear_stats_regstage (N <= 128): 128 x 256 block, four waves of
 //     64 x 128, operands staged through registers into a double-buffered,
 //     padded LDS tile.
 #include "launch.h"
 #include "logp_device.h"
+#include "mfma_gemm.h"
 
 namespace itl {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using gemm::bf16x8;
+using gemm::f32x4;
+using gemm::tile_coords;
+using gemm::xcd_logical;
 
 constexpr int BN = kLinearTile;  // vocabulary columns per workgroup (= statistic tile)
-constexpr int BK = 32;           // K per MFMA step
-
-// Blocks are dealt round-robin to the 8 XCDs; give each XCD one contiguous
-// range of logical tiles so that a vocabulary block's weight rows are read
-// into one XCD's L2 only.
-__device__ __forceinline__ int xcd_logical(int b, int g) {
-  const int x = b % 8, y = b / 8, per = g / 8, rem = g % 8;
-  return x < rem ? x * (per + 1) + y : rem * (per + 1) + (x - rem) * per + y;
-}
-
-// Logical tile -> (row block, vocabulary block).  Tiles are grouped 8 row
-// blocks x 4 vocabulary blocks, so the ~32 workgroups an XCD runs at once
-// share each hidden slice 4 ways and each weight slice 8 ways in its L2.
-__device__ __forceinline__ void tile_coords(int logical, int mblocks, int vblocks, int& mb,
-                                            int& vb) {
-  const int vbg = logical / (mblocks * 4);
-  const int gv = min(4, vblocks - vbg * 4);
-  const int rem = logical - vbg * mblocks * 4;
-  const int mbg = rem / (8 * gv);
-  const int gm = min(8, mblocks - mbg * 8);
-  const int r2 = rem - mbg * 8 * gv;
-  mb = mbg * 8 + r2 % gm;
-  vb = vbg * 4 + r2 / gm;
-}
+constexpr int BK = gemm::kK;     // K per MFMA step
 
 template <int BM>
 struct Reduce {
@@ -205,37 +185,15 @@ __device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>&
 }
 
 // ---------------------------------------------------------------------------
-// linear_stats_dma: BM = 256, 8 waves (wm = wave / 4 picks 128 rows, wn =
-// wave % 4 picks 64 columns), four LDS stages filled by direct loads.
-// LDS stage layout: [A | B], each 256 rows x 32 bf16 (64 B per row, 16 KiB);
-// 16-byte chunk kc of row r sits in slot kc ^ swz(r), swz(r) = ((r>>1)^(r>>2))&3,
-// so the 16 rows of a fragment read (one 16-byte chunk per row) spread over
-// all banks.  One direct load instruction fills 1 KiB = 16 rows: lane L
-// writes row L/4, slot L%4, so it fetches chunk (L%4) ^ swz(L/4) of its row.
-// Wave w fills A blocks w, w+8 and B blocks w, w+8 of every stage.
+// linear_stats_dma: BM = 256, the mfma_gemm.h tile (hidden rows x weight rows),
+// statistic epilogue on its accumulators.
 // ---------------------------------------------------------------------------
-constexpr int kDmaThreads = 512;
-constexpr int kStages = 4;
-constexpr int kStageElems = 256 * BK;  // bf16 per operand per stage
+constexpr int kDmaThreads = gemm::kThreads;
 
 struct SmemDma {
-  uint16_t stage[kStages][2][kStageElems];  // 128 KiB
+  gemm::Stages st;  // 128 KiB
   Reduce<256> rd;
 };
-
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-// Issue this wave's 4 direct loads of K step `step` into LDS stage `s`.
-__device__ __forceinline__ void issue_step(SmemDma& sm, const uint16_t* a0, const uint16_t* a1,
-                                           const uint16_t* b0, const uint16_t* b1, int wave,
-                                           int s, int step) {
-  const int64_t k0 = static_cast<int64_t>(step) * BK;
-  constexpr int kBlk = 16 * BK;  // elements per 16-row block
-  __builtin_amdgcn_global_load_lds(a0 + k0, sm.stage[s][0] + wave * kBlk, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(b0 + k0, sm.stage[s][1] + wave * kBlk, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(a1 + k0, sm.stage[s][0] + (wave + 8) * kBlk, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(b1 + k0, sm.stage[s][1] + (wave + 8) * kBlk, 16, 0, 0);
-}
 
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
@@ -255,81 +213,13 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
   if (tid < 256) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
 
-  // Source rows past n / v are clamped to the last valid row: they only feed
-  // outputs that are masked out, and every load stays in bounds.
-  const int lrow = lane / 4;
-  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
-  const uint16_t* a0 = hidden + min(m0 + wave * 16 + lrow, n - 1) * ld_h + lk;
-  const uint16_t* a1 = hidden + min(m0 + (wave + 8) * 16 + lrow, n - 1) * ld_h + lk;
-  const uint16_t* b0 = weight + min(v0 + wave * 16 + lrow, v - 1) * ld_w + lk;
-  const uint16_t* b1 = weight + min(v0 + (wave + 8) * 16 + lrow, v - 1) * ld_w + lk;
-
   f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // Fragment offsets (elements) inside a stage: row wm*128 + li (+16 i) of A,
-  // row wn*64 + li (+16 j) of B, chunk g.
-  const int aoff = (wm * 128 + li) * BK + ((g ^ swz(li)) * 8);
-  const int boff = (wn * 64 + li) * BK + ((g ^ swz(li)) * 8);
-  const int ksteps = static_cast<int>(hdim / BK);
-
-  // Pipeline (ksteps is even: h is a multiple of 64).  Iteration kt runs the
-  // MFMAs of step kt on fragments already in registers while the fragments of
-  // step kt+1 are read from LDS and the direct loads of step kt+4 go out
-  // (steps kt+2, kt+3 are in flight).  Every iteration issues exactly 4 loads
-  // per wave and 12 fragment reads, so the wait counts are constant: past the
-  // end the loads re-fetch the last K step into the stage that is no longer
-  // read, and the extra fragment reads land in registers that are not used.
-  for (int st = 0; st < kStages; ++st)
-    issue_step(sm, a0, a1, b0, b1, wave, st, st < ksteps ? st : ksteps - 1);
-  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  bf16x8 xa[8], xb[4], ya[8], yb[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(sm.stage[0][1] + boff + j * 16 * BK);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const bf16x8*>(sm.stage[0][0] + aoff + i * 16 * BK);
-  // One step: this wave's reads of stage KT % 4 and its loads of step KT+1
-  // have landed (KT+2, KT+3 may still be in flight); after the barrier step
-  // KT+1 is in LDS for every wave and stage KT % 4 is free.  A bare
-  // s_barrier: the fence of __syncthreads would also wait for KT+2, KT+3.
-#define ITL_STEP(CA, CB, NA, NB, KT)                                                         \
-  {                                                                                          \
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");                              \
-    __builtin_amdgcn_s_barrier();                                                            \
-    issue_step(sm, a0, a1, b0, b1, wave, (KT) % kStages,                                     \
-               (KT) + kStages < ksteps ? (KT) + kStages : ksteps - 1);                       \
-    {                                                                                        \
-      const uint16_t* sa = sm.stage[((KT) + 1) % kStages][0];                                \
-      const uint16_t* sb = sm.stage[((KT) + 1) % kStages][1];                                \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
-        NB[j] = *reinterpret_cast<const bf16x8*>(sb + boff + j * 16 * BK);                   \
-      _Pragma("unroll") for (int i = 0; i < 8; ++i)                                          \
-        NA[i] = *reinterpret_cast<const bf16x8*>(sa + aoff + i * 16 * BK);                   \
-    }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                            \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0); \
-    /* Interleave so that the MFMA stream never waits behind the load issue: */              \
-    /* 4 x (1 direct load, then 3 x (2 MFMAs, 1 fragment read)), then 8 MFMAs. */            \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                          \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
-      _Pragma("unroll") for (int w = 0; w < 3; ++w) {                                        \
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                   \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
-      }                                                                                      \
-    }                                                                                        \
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                       \
-  }
-  for (int kt = 0; kt < ksteps; kt += 2) {
-    ITL_STEP(xa, xb, ya, yb, kt)
-    ITL_STEP(ya, yb, xa, xb, kt + 1)
-  }
-#undef ITL_STEP
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  gemm::mainloop(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v, static_cast<int>(hdim / BK),
+                 acc);
   __syncthreads();
   stats_epilogue<8, 4, 256, kDmaThreads>(acc, sm.rd, wm * 128, wn * 64, li, g, tid, m0, v0, vb,
                                          vblocks, v, pm, ps, pt);

@@ -1,0 +1,163 @@
+// 256 x 256 bf16 MFMA tile of C = A * B^T (both operands K-contiguous), the
+// product engine of the fused LM head and of its backward.
+//
+// Arithmetic (part of the fused-LM-head contract): every output is one fp32
+// accumulator fed by v_mfma_f32_16x16x32_bf16 over K in ascending steps of
+// 32, no split-K.  The accumulator may start from a caller-supplied value;
+// continuing a K walk from a stored accumulator gives the same bits as one
+// uninterrupted walk.
+//
+// Layout: 8 waves; wave w covers rows (w / 4) * 128 + [0, 128) and columns
+// (w % 4) * 64 + [0, 64) of the tile as acc[i][j][q] =
+//   C[row0 + i*16 + 4*g + q][col0 + j*16 + li],   li = lane % 16, g = lane / 16.
+// Operands stream global -> LDS by direct 16-byte loads through a four-stage
+// ring (three K steps in flight).  LDS stage layout: [A | B], each 256 rows x
+// 32 bf16 (64 B per row, 16 KiB); 16-byte chunk kc of row r sits in slot
+// kc ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3, so the 16 rows of a
+// fragment read (one 16-byte chunk per row) spread over all banks.  One
+// direct load instruction fills 1 KiB = 16 rows: lane L writes row L / 4,
+// slot L % 4, so it fetches chunk (L % 4) ^ swz(L / 4) of its row.  Wave w
+// fills A blocks w, w + 8 and B blocks w, w + 8 of every stage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace itl {
+namespace gemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 256;     // rows and columns of a workgroup tile
+constexpr int kK = 32;         // K per MFMA step
+constexpr int kThreads = 512;  // 8 waves
+constexpr int kStages = 4;
+constexpr int kStageElems = kTile * kK;  // bf16 per operand per stage
+
+struct Stages {
+  uint16_t s[kStages][2][kStageElems];  // 128 KiB
+};
+
+// Workgroups are dealt round-robin to the 8 XCDs; give each XCD one
+// contiguous range of logical tiles so that an operand slice is read into one
+// XCD's L2 only.
+__device__ __forceinline__ int xcd_logical(int b, int g) {
+  const int x = b % 8, y = b / 8, per = g / 8, rem = g % 8;
+  return x < rem ? x * (per + 1) + y : rem * (per + 1) + (x - rem) * per + y;
+}
+
+// Logical tile -> (row block, column block).  Tiles are grouped 8 row blocks
+// x 4 column blocks, so the ~32 workgroups an XCD runs at once share each A
+// slice 4 ways and each B slice 8 ways in its L2.
+__device__ __forceinline__ void tile_coords(int logical, int mblocks, int nblocks, int& mb,
+                                            int& nb) {
+  const int nbg = logical / (mblocks * 4);
+  const int gn = min(4, nblocks - nbg * 4);
+  const int rem = logical - nbg * mblocks * 4;
+  const int mbg = rem / (8 * gn);
+  const int gm = min(8, mblocks - mbg * 8);
+  const int r2 = rem - mbg * 8 * gn;
+  mb = mbg * 8 + r2 % gm;
+  nb = nbg * 4 + r2 / gm;
+}
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Issue this wave's 4 direct loads of K step `step` into LDS stage `s`.
+__device__ __forceinline__ void issue_step(Stages& sm, const uint16_t* a0, const uint16_t* a1,
+                                           const uint16_t* b0, const uint16_t* b1, int wave,
+                                           int s, int step) {
+  const int64_t k0 = static_cast<int64_t>(step) * kK;
+  constexpr int kBlk = 16 * kK;  // elements per 16-row block
+  __builtin_amdgcn_global_load_lds(a0 + k0, sm.s[s][0] + wave * kBlk, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(b0 + k0, sm.s[s][1] + wave * kBlk, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(a1 + k0, sm.s[s][0] + (wave + 8) * kBlk, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(b1 + k0, sm.s[s][1] + (wave + 8) * kBlk, 16, 0, 0);
+}
+
+// acc += A[a_row0 + 0..255, 0..K) * B[b_row0 + 0..255, 0..K)^T with K =
+// ksteps * 32 (ksteps even, >= 2).  Rows at or past a_rows / b_rows are read
+// from the last valid row instead (every load stays in bounds); they only
+// feed outputs the caller masks.  All 512 threads must call; on return every
+// direct load has landed and the stages may be reused after a barrier.
+__device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict__ A, int64_t lda,
+                                         int64_t a_row0, int64_t a_rows,
+                                         const uint16_t* __restrict__ B, int64_t ldb,
+                                         int64_t b_row0, int64_t b_rows, int ksteps,
+                                         f32x4 (&acc)[8][4]) {
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int wm = wave / 4, wn = wave % 4;
+  const int li = lane % 16, g = lane / 16;
+  const int lrow = lane / 4;
+  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
+  const uint16_t* a0 = A + min(a_row0 + wave * 16 + lrow, a_rows - 1) * lda + lk;
+  const uint16_t* a1 = A + min(a_row0 + (wave + 8) * 16 + lrow, a_rows - 1) * lda + lk;
+  const uint16_t* b0 = B + min(b_row0 + wave * 16 + lrow, b_rows - 1) * ldb + lk;
+  const uint16_t* b1 = B + min(b_row0 + (wave + 8) * 16 + lrow, b_rows - 1) * ldb + lk;
+
+  // Fragment offsets (elements) inside a stage: row wm*128 + li (+16 i) of A,
+  // row wn*64 + li (+16 j) of B, chunk g.
+  const int aoff = (wm * 128 + li) * kK + ((g ^ swz(li)) * 8);
+  const int boff = (wn * 64 + li) * kK + ((g ^ swz(li)) * 8);
+
+  // Pipeline.  Iteration kt runs the MFMAs of step kt on fragments already in
+  // registers while the fragments of step kt+1 are read from LDS and the
+  // direct loads of step kt+4 go out (steps kt+2, kt+3 are in flight).  Every
+  // iteration issues exactly 4 loads per wave and 12 fragment reads, so the
+  // wait counts are constant: past the end the loads re-fetch the last K step
+  // into the stage that is no longer read, and the extra fragment reads land
+  // in registers that are not used.
+  for (int st = 0; st < kStages; ++st)
+    issue_step(sm, a0, a1, b0, b1, wave, st, st < ksteps ? st : ksteps - 1);
+  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  bf16x8 xa[8], xb[4], ya[8], yb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(sm.s[0][1] + boff + j * 16 * kK);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const bf16x8*>(sm.s[0][0] + aoff + i * 16 * kK);
+  // One step: this wave's reads of stage KT % 4 and its loads of step KT+1
+  // have landed (KT+2, KT+3 may still be in flight); after the barrier step
+  // KT+1 is in LDS for every wave and stage KT % 4 is free.  A bare
+  // s_barrier: the fence of __syncthreads would also wait for KT+2, KT+3.
+#define ITL_STEP(CA, CB, NA, NB, KT)                                                         \
+  {                                                                                          \
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");                              \
+    __builtin_amdgcn_s_barrier();                                                            \
+    issue_step(sm, a0, a1, b0, b1, wave, (KT) % kStages,                                     \
+               (KT) + kStages < ksteps ? (KT) + kStages : ksteps - 1);                       \
+    {                                                                                        \
+      const uint16_t* sa = sm.s[((KT) + 1) % kStages][0];                                    \
+      const uint16_t* sb = sm.s[((KT) + 1) % kStages][1];                                    \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+        NB[j] = *reinterpret_cast<const bf16x8*>(sb + boff + j * 16 * kK);                   \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i)                                          \
+        NA[i] = *reinterpret_cast<const bf16x8*>(sa + aoff + i * 16 * kK);                   \
+    }                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                            \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0); \
+    /* Interleave so that the MFMA stream never waits behind the load issue: */              \
+    /* 4 x (1 direct load, then 3 x (2 MFMAs, 1 fragment read)), then 8 MFMAs. */            \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                          \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
+      _Pragma("unroll") for (int w = 0; w < 3; ++w) {                                        \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                   \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
+      }                                                                                      \
+    }                                                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                       \
+  }
+  for (int kt = 0; kt < ksteps; kt += 2) {
+    ITL_STEP(xa, xb, ya, yb, kt)
+    ITL_STEP(ya, yb, xa, xb, kt + 1)
+  }
+#undef ITL_STEP
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+}  // namespace gemm
+}  // namespace itl

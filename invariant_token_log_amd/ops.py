@@ -136,6 +136,86 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
     return logp_out, lse_out
 
 
+def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
+                    tile_width=LINEAR_TILE, need_dhidden=True, need_dweight=True,
+                    out_dtype=torch.float32, dhidden_out=None, dweight_out=None,
+                    workspace=None):
+    """Backward of the fused LM head + logp: (dhidden [N, H] or None,
+    dweight [V, H] or None) in out_dtype (float32 accumulators or their
+    bfloat16 rounding), from the forward's lse and the upstream gradient."""
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.stride(1) != 1 or weight.stride(1) != 1:
+        raise ValueError("hidden [N, H] and weight [V, H] need a contiguous last dimension")
+    if out_dtype not in _DTYPES:
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    n, h = hidden.shape
+    v, h2 = weight.shape
+    if h2 != h:
+        raise ValueError("hidden and weight must share H")
+    t1 = _targets(targets, n)
+    g = grad_logp.reshape(-1)
+    if g.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise TypeError("lse and grad_logp must be float32")
+    if g.numel() != n or lse.numel() != n or not g.is_contiguous() or not lse.is_contiguous():
+        raise ValueError("lse and grad_logp must be contiguous with one entry per row")
+    dev = hidden.device
+    if need_dhidden and dhidden_out is None:
+        dhidden_out = torch.empty(n, h, dtype=out_dtype, device=dev)
+    if need_dweight and dweight_out is None:
+        dweight_out = torch.empty(v, h, dtype=out_dtype, device=dev)
+    dh = dhidden_out if need_dhidden else None
+    dw = dweight_out if need_dweight else None
+    for o, rows in ((dh, n), (dw, v)):
+        if o is not None and (o.dtype != out_dtype or o.dim() != 2 or o.shape[0] != rows
+                              or o.shape[1] != h or o.stride(1) != 1):
+            raise ValueError("output buffers must be [rows, H] of out_dtype, rows contiguous")
+    L = _lib.lib()
+    need = L.linear_logp_bwd_workspace_bytes(n, h, v, tile_width)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
+    ld_h = hidden.stride(0) if n > 1 else h
+    ld_w = weight.stride(0) if v > 1 else h
+    st = L.linear_logp_bwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
+                           t1.data_ptr(), int(ignore_index), int(tile_width), lse.data_ptr(),
+                           g.data_ptr(), _DTYPES[out_dtype],
+                           dh.data_ptr() if dh is not None else None,
+                           (dh.stride(0) if n > 1 else h) if dh is not None else 0,
+                           dw.data_ptr() if dw is not None else None,
+                           (dw.stride(0) if v > 1 else h) if dw is not None else 0,
+                           ws_ptr, ws_len, _stream(dev))
+    check("linear_logp_bwd", st)
+    return dh, dw
+
+
+class _LinearLogp(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, hidden, weight, targets, ignore_index):
+        logp, lse = linear_logp_fwd(hidden, weight, targets, ignore_index)
+        ctx.save_for_backward(hidden, weight, targets, lse)
+        ctx.ignore_index = ignore_index
+        return logp
+
+    @staticmethod
+    def backward(ctx, grad):
+        hidden, weight, targets, lse = ctx.saved_tensors
+        g = grad.to(torch.float32).contiguous()
+        dh, dw = linear_logp_bwd(hidden, weight, targets, lse, g, ctx.ignore_index,
+                                 need_dhidden=ctx.needs_input_grad[0],
+                                 need_dweight=ctx.needs_input_grad[1],
+                                 out_dtype=torch.bfloat16)
+        return dh, dw, None, None
+
+
+def linear_logp(hidden, weight, target_ids, ignore_index=-100):
+    """Differentiable fused LM head + selected-token log-probability:
+    hidden bf16 [N, H], weight bf16 [V, H] -> float32 logp [N]; backward fills
+    the bf16 gradients of hidden and weight through linear_logp_bwd."""
+    return _LinearLogp.apply(hidden, weight, target_ids, ignore_index)
+
+
 class _BatchInvariantLogp(torch.autograd.Function):
     @staticmethod
     def forward(ctx, logits, targets, ignore_index, tile_width, validate):

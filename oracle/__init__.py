@@ -4,6 +4,7 @@ from .logp_oracle import (  # noqa: F401
     InvalidTargetError,
     linear_logits,
     linear_logp_bwd,
+    linear_logp_bwd_weight_rows,
     linear_logp_fwd,
     logp_bwd,
     logp_fwd,

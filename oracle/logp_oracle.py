@@ -166,7 +166,8 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100):
     return logp, lse
 
 
-def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=None):
+def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=None,
+                    need_dweight=True):
     """Gradients of sum_r g_r * logp_r of the fused LM head, in float64.
 
     "[RFC][ROCm] ..." -- Workstream 3 (the backward recomputes the logit
@@ -177,7 +178,7 @@ def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=N
         dh = dz @ W,    dW = dz^T @ h
     lse is the float64 row LSE of z (recomputed when not given).  Rows are
     processed in blocks; dW sums the blocks in ascending row order.
-    Returns (dh [N, H], dW [V, H]) as float64."""
+    Returns (dh [N, H], dW [V, H]) as float64 (dW is None when not needed)."""
     h = np.asarray(hidden, dtype=np.float64)
     w = np.asarray(weight, dtype=np.float64)
     n = h.shape[0]
@@ -186,15 +187,41 @@ def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=N
     if t.shape[0] != n or g.shape[0] != n:
         raise ValueError("targets and grad_logp need one entry per row")
     dh = np.zeros_like(h)
-    dw = np.zeros_like(w)
+    dw = np.zeros_like(w) if need_dweight else None
     for r0 in range(0, n, ROW_CHUNK):
         r1 = min(n, r0 + ROW_CHUNK)
         z = linear_logits(h[r0:r1], w)
         row_lse = None if lse is None else np.asarray(lse, dtype=np.float64).reshape(-1)[r0:r1]
         dz = logp_bwd(z, t[r0:r1], g[r0:r1], ignore_index, lse=row_lse)
         dh[r0:r1] = dz @ w
-        dw += dz.T @ h[r0:r1]
+        if need_dweight:
+            dw += dz.T @ h[r0:r1]
     return dh, dw
+
+
+def linear_logp_bwd_weight_rows(hidden, weight, targets, grad_logp, vocab_rows,
+                                ignore_index=-100, lse=None):
+    """Rows `vocab_rows` of dW = dz^T h from linear_logp_bwd, without forming
+    the other vocabulary rows: dW[j] = sum_r g_r ([t_r == j] - exp(z[r, j] -
+    lse_r)) h[r] over active rows, z[:, j] = h W[j]^T.  lse (float64 [N]) is
+    the full-row LSE; it is recomputed from all of W when not given (the
+    expensive part).  Returns float64 [len(vocab_rows), H]."""
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    n = h.shape[0]
+    t = np.asarray(targets, dtype=np.int64).reshape(-1)
+    g = np.asarray(grad_logp, dtype=np.float64).reshape(-1)
+    active, _ = _active_mask(t, ignore_index, w.shape[0])
+    if lse is None:
+        _, lse = linear_logp_fwd(h, w, t, ignore_index)
+    lse = np.asarray(lse, dtype=np.float64).reshape(-1)
+    cols = np.asarray(vocab_rows, dtype=np.int64).reshape(-1)
+    z = h @ w[cols].T                                   # [N, J]
+    p = np.exp(z - lse[:, None])
+    onehot = (t[:, None] == cols[None, :]).astype(np.float64)
+    dz = g[:, None] * (onehot - p)
+    dz[~active] = 0.0
+    return dz.T @ h
 
 
 # ---------------------------------------------------------------------------

@@ -127,3 +127,36 @@ def test_linear_argument_errors(L):
     need = L.linear_logp_fwd_workspace_bytes(8, 151936, 256)
     assert need == 256 + 2 * 256 * (-(-(594 * 8 * 4) // 256)) + 256
     assert L.linear_logp_fwd_workspace_bytes(8, 151936, 512) == 0
+
+
+def test_linear_bwd_argument_errors(L):
+    def lb(**kw):
+        a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
+                 targets=FAKE, tile=256, lse=FAKE, g=FAKE, out=0, dh=FAKE, ld_dh=4096,
+                 dw=FAKE, ld_dw=4096, ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        return L.linear_logp_bwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
+                                 a["v"], a["targets"], -100, a["tile"], a["lse"], a["g"],
+                                 a["out"], a["dh"], a["ld_dh"], a["dw"], a["ld_dw"], a["ws"],
+                                 a["ws_bytes"], None)
+    assert lb(tile=512) == _lib.LOGP_ERR_TILE
+    assert lb(h=100, ld_h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
+    assert lb(h=0, ld_h=0, ld_w=0) == _lib.LOGP_ERR_SHAPE
+    assert lb(ld_dh=100) == _lib.LOGP_ERR_SHAPE
+    assert lb(ld_dw=100) == _lib.LOGP_ERR_SHAPE
+    assert lb(out=7) == _lib.LOGP_ERR_DTYPE
+    assert lb(dh=None, dw=None) == _lib.LOGP_ERR_NULL
+    for k in ("h_ptr", "w_ptr", "targets", "lse", "g"):
+        assert lb(**{k: None}) == _lib.LOGP_ERR_NULL, k
+    assert lb(h_ptr=FAKE + 2) == _lib.LOGP_ERR_ALIGN
+    assert lb(ld_w=4100) == _lib.LOGP_ERR_ALIGN
+    assert lb(ws_bytes=16) == _lib.LOGP_ERR_WORKSPACE
+    assert lb(ws=FAKE + 16) == _lib.LOGP_ERR_WORKSPACE
+    assert lb(n=0, h_ptr=None, targets=None, lse=None, g=None, dw=None) == _lib.LOGP_OK
+    # workspace: W^T, h^T, dz, dz^T in bf16 with 256-padded n and v
+    np_, vp = 256, 152064
+    need = L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 256)
+    assert need == 2 * (4096 * vp + 4096 * np_ + 2 * np_ * vp)
+    assert L.linear_logp_bwd_workspace_bytes(0, 4096, 151936, 256) == 0
+    assert L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 4096) == 0
+    assert L.linear_logp_bwd_workspace_bytes(8, 100, 151936, 256) == 0

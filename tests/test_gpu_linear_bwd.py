@@ -1,0 +1,185 @@
+"""GPU parity and invariance of the fused LM-head backward (linear_logp_bwd)
+against the float64 oracle ("[RFC][ROCm] End-to-end optimization of bitwise
+VIME R/R beyond native P/P", Workstream 3: the backward recomputes the fixed
+logit tiles from the saved LSE; "Batch-Invariant LogP", Batch-Invariance).
+
+Tolerance (derived, elementwise).  The kernel rounds dz = g (onehot - p) to
+bf16 once (at most 2^-9 relative), its z and lse differ from float64 by far
+less than EPS_Z, and the fp32 K walks add at most K/32 roundings.  So
+    |dh - dh64| <= 2^-8 sum_j |dz64[r, j]| |W[j, k]| + |g| p_t EPS_Z |W[t, k]| + 1e-6
+and the same with (tokens, h) in place of (vocabulary, W) for dW; the second
+term covers the target column, where 1 - p may cancel."""
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_token_log_amd as itl
+import oracle
+import synth
+from gpu_helpers import bits, dev
+
+pytestmark = pytest.mark.gpu
+
+REL = 2.0 ** -8
+EPS_Z = 1e-3
+ABS = 1e-6
+
+
+def _f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def _dz64(h, w, t, g, lse64):
+    z = h @ w.T
+    p = np.exp(z - lse64[:, None])
+    active = t != -100
+    onehot = np.zeros_like(p)
+    onehot[np.flatnonzero(active), t[active]] = 1.0
+    dz = g[:, None] * (onehot - p)
+    dz[~active] = 0.0
+    return dz, p
+
+
+def _bounds(h, w, t, g, lse64, need_dweight=True):
+    """Elementwise bounds for dh [N, H] and dW [V, H] (comparison rule only)."""
+    dz, p = _dz64(h, w, t, g, lse64)
+    active = t != -100
+    pt = np.zeros(len(t))
+    pt[active] = p[np.flatnonzero(active), t[active]]
+    tgt = np.zeros_like(dz)
+    tgt[np.flatnonzero(active), t[active]] = np.abs(g[active]) * pt[active] * EPS_Z
+    bh = REL * (np.abs(dz) @ np.abs(w)) + tgt @ np.abs(w) + ABS
+    if not need_dweight:
+        return bh, None
+    bw = REL * (np.abs(dz).T @ np.abs(h)) + tgt.T @ np.abs(h) + ABS
+    return bh, bw
+
+
+def _case(n, hd, v, seed, ignore_frac=0.05):
+    c = synth.qwen3_linear(seed=seed, n=n, h=hd, v=v, device=dev(), ignore_frac=ignore_frac)
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=seed + 50)[0].to(dev())
+    return c["hidden"], c["weight"], c["targets"], g
+
+
+@pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (200, 128, 1000), (1, 64, 256),
+                                    (129, 512, 529), (300, 512, 4096), (257, 64, 300)])
+def test_parity_small(n, hd, v):
+    h, w, t, g = _case(n, hd, v, seed=n * 7 + v)
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    dh, dw = itl.linear_logp_bwd(h, w, t, lse, g)
+    hn, wn, tn, gn = _f64(h), _f64(w), t.cpu().numpy(), _f64(g)
+    dh64, dw64 = oracle.linear_logp_bwd(hn, wn, tn, gn)
+    _, lse64 = oracle.linear_logp_fwd(hn, wn, tn)
+    bh, bw = _bounds(hn, wn, tn, gn, lse64)
+    eh = np.abs(_f64(dh) - dh64)
+    ew = np.abs(_f64(dw) - dw64)
+    assert (eh <= bh).all(), (np.argwhere(eh > bh)[:5], eh.max())
+    assert (ew <= bw).all(), (np.argwhere(ew > bw)[:5], ew.max())
+    ign = torch.from_numpy(tn == -100).to(dev())
+    assert (bits(dh[ign]) == 0).all()
+
+
+def test_bf16_output_is_rne_of_fp32():
+    h, w, t, g = _case(130, 256, 1000, seed=3)
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    dh, dw = itl.linear_logp_bwd(h, w, t, lse, g)
+    bh, bw = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=torch.bfloat16)
+    assert torch.equal(bh.view(torch.int16), dh.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(bw.view(torch.int16), dw.to(torch.bfloat16).view(torch.int16))
+
+
+def test_dh_rows_batch_invariant():
+    """dh[r] depends only on row r: alone, permuted, among other rows."""
+    h, w, t, g = _case(300, 256, 2000, seed=5)
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    dh, _ = itl.linear_logp_bwd(h, w, t, lse, g, need_dweight=False)
+    b0 = bits(dh)
+    for r in [0, 5, 255, 256, 299]:
+        d1, _ = itl.linear_logp_bwd(h[r:r + 1].contiguous(), w, t[r:r + 1].contiguous(),
+                                    lse[r:r + 1].contiguous(), g[r:r + 1].contiguous(),
+                                    need_dweight=False)
+        assert torch.equal(bits(d1), b0[r:r + 1]), r
+    perm = torch.randperm(300, generator=torch.Generator().manual_seed(2)).to(dev())
+    dp, _ = itl.linear_logp_bwd(h[perm].contiguous(), w, t[perm].contiguous(),
+                                lse[perm].contiguous(), g[perm].contiguous(), need_dweight=False)
+    assert torch.equal(bits(dp), b0[perm.cpu()])
+
+
+def test_dw_deterministic_and_ignored_rows_neutral():
+    """dW repeats bit for bit; appending ignored rows (zero dz rows at the end
+    of the token walk) leaves it unchanged; each product alone equals the pair."""
+    h, w, t, g = _case(200, 128, 1500, seed=9)
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    dh, dw = itl.linear_logp_bwd(h, w, t, lse, g)
+    dh2, dw2 = itl.linear_logp_bwd(h, w, t, lse, g)
+    assert torch.equal(bits(dw), bits(dw2)) and torch.equal(bits(dh), bits(dh2))
+    _, dw_only = itl.linear_logp_bwd(h, w, t, lse, g, need_dhidden=False)
+    dh_only, _ = itl.linear_logp_bwd(h, w, t, lse, g, need_dweight=False)
+    assert torch.equal(bits(dw_only), bits(dw)) and torch.equal(bits(dh_only), bits(dh))
+    extra = synth.normal_matrix(100, 128, 1.0, torch.bfloat16, seed=10).to(dev())
+    h3 = torch.cat([h, extra])
+    t3 = torch.cat([t, torch.full((100,), -100, device=dev())])
+    g3 = torch.cat([g, torch.ones(100, device=dev())])
+    l3 = torch.cat([lse, torch.zeros(100, device=dev())])
+    dh3, dw3 = itl.linear_logp_bwd(h3, w, t3, l3, g3)
+    assert torch.equal(bits(dw3), bits(dw))
+    assert torch.equal(bits(dh3[:200]), bits(dh)) and (bits(dh3[200:]) == 0).all()
+
+
+def test_zero_rows_give_zero_dweight():
+    w = synth.normal_matrix(300, 64, 0.02, torch.bfloat16, seed=1).to(dev())
+    h = torch.empty(0, 64, dtype=torch.bfloat16, device=dev())
+    t = torch.empty(0, dtype=torch.int64, device=dev())
+    e = torch.empty(0, dtype=torch.float32, device=dev())
+    dwo = torch.full((300, 64), 7.0, device=dev())
+    _, dw = itl.linear_logp_bwd(h, w, t, e, e, need_dhidden=False, dweight_out=dwo)
+    assert (bits(dw) == 0).all()
+
+
+def test_autograd_matches_direct_call():
+    """linear_logp(...).sum().backward() gives the bf16 gradients of a direct
+    call with g = 1."""
+    h, w, t, _ = _case(96, 128, 700, seed=11)
+    hh = h.clone().requires_grad_(True)
+    ww = w.clone().requires_grad_(True)
+    out = itl.linear_logp(hh, ww, t)
+    out.sum().backward()
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    dh, dw = itl.linear_logp_bwd(h, w, t, lse, torch.ones(96, device=dev()),
+                                 out_dtype=torch.bfloat16)
+    assert hh.grad.dtype == torch.bfloat16 and ww.grad.dtype == torch.bfloat16
+    assert torch.equal(hh.grad.view(torch.int16), dh.view(torch.int16))
+    assert torch.equal(ww.grad.view(torch.int16), dw.view(torch.int16))
+
+
+def test_full_size_sampled():
+    """Qwen3-8B LM head (N = 4096, H = 4096, V = 151936) at the benchmarked
+    launch: sampled rows of dh and sampled vocabulary rows of dW against the
+    float64 oracle (the full-row LSE comes from the oracle's own forward)."""
+    h, w, t, g = _case(4096, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB, seed=1005, ignore_frac=0.05)
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    dh, dw = itl.linear_logp_bwd(h, w, t, lse, g)
+    torch.cuda.synchronize()
+    hn, wn, tn, gn = _f64(h), _f64(w), t.cpu().numpy(), _f64(g)
+    rows = np.array(list(range(0, 4096, 293)) + [4095])
+    dh64, _ = oracle.linear_logp_bwd(hn[rows], wn, tn[rows], gn[rows], need_dweight=False)
+    _, lse_rows = oracle.linear_logp_fwd(hn[rows], wn, tn[rows])
+    bh, _ = _bounds(hn[rows], wn, tn[rows], gn[rows], lse_rows, need_dweight=False)
+    eh = np.abs(_f64(dh)[rows] - dh64)
+    assert (eh <= bh).all(), (np.argwhere(eh > bh)[:5], eh.max())
+    _, lse64 = oracle.linear_logp_fwd(hn, wn, tn)
+    active_targets = np.unique(tn[tn != -100])
+    vr = np.unique(np.concatenate([[0, 1, 4095, 151935], active_targets[::400]]))
+    dw64 = oracle.linear_logp_bwd_weight_rows(hn, wn, tn, gn, vr, lse=lse64)
+    # bound of the sampled rows (comparison rule only): dz of columns vr
+    act = tn != -100
+    pp = np.exp(hn @ wn[vr].T - lse64[:, None])
+    hit = (tn[:, None] == vr[None, :]) & act[:, None]
+    dzz = gn[:, None] * (hit.astype(np.float64) - pp)
+    dzz[~act] = 0.0
+    tgt = np.where(hit, np.abs(gn)[:, None] * pp * EPS_Z, 0.0)
+    bw = REL * (np.abs(dzz).T @ np.abs(hn)) + tgt.T @ np.abs(hn) + ABS
+    ew = np.abs(_f64(dw)[vr] - dw64)
+    assert (ew <= bw).all(), (np.argwhere(ew > bw)[:5], ew.max())
+    assert torch.isfinite(dh).all() and torch.isfinite(dw).all()

@@ -445,3 +445,21 @@ def test_linear_bwd_ignored_rows_add_nothing():
     p = np.exp(z - lse[:, None])
     want = dh - (-(g[:, None] * p * 0.5)) @ w
     np.testing.assert_allclose(dh3, want, rtol=1e-12, atol=1e-13)
+
+
+def test_linear_bwd_weight_rows_matches_full():
+    """The sampled-row dW equals the full dW rows (and its own lse path)."""
+    rng = np.random.default_rng(25)
+    h = rng.normal(size=(20, 16))
+    w = rng.normal(size=(70, 16)) * 0.3
+    t = rng.integers(0, 70, 20)
+    t[[2, 7]] = -100
+    t[3] = 11
+    g = rng.normal(size=20)
+    _, dw = oracle.linear_logp_bwd(h, w, t, g)
+    rows = [0, 11, 69, 11, 35]
+    got = oracle.linear_logp_bwd_weight_rows(h, w, t, g, rows)
+    np.testing.assert_allclose(got, dw[rows], rtol=1e-12, atol=1e-14)
+    _, lse = oracle.linear_logp_fwd(h, w, t)
+    got2 = oracle.linear_logp_bwd_weight_rows(h, w, t, g, rows, lse=lse)
+    np.testing.assert_array_equal(got, got2)
