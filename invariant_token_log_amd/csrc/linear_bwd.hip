@@ -15,8 +15,9 @@
 // invariant) and dW is deterministic for a given token order.
 //
 // Kernels (all on the 256 x 256 tile of mfma_gemm.h):
-//   linear_dz_kernel  : h x W^T tile -> dz tile in LDS -> dz [Np, Vp] and
-//                       dz^T [Vp, Np] (bf16, coalesced 16-byte stores);
+//   linear_dz_kernel  : h x W^T tile -> dz in registers -> transposed, then
+//                       row-major LDS tile -> dz^T [Vp, Np] and dz [Np, Vp]
+//                       (bf16, whole 512-byte row segments per store pass);
 //   transpose_pad_bf16: W [V, H] -> W^T [H, Vp], h [N, H] -> h^T [H, Np], zero
 //                       padded, so that both products see K-contiguous operands;
 //   gemm_out_kernel   : C = A B^T with fp32 or RNE-bf16 output.
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void transpose_pad_bf16(const uint16_t* __rest
 struct SmemDz {
   union {
     gemm::Stages st;                // main loop
-    uint16_t tile[kT][kDzStride];  // dz tile for the two layouts
+    uint16_t tile[kT][kDzStride];  // dz tile, one layout at a time
   } u;
   float lse[kT];
   float g[kT];
@@ -136,41 +137,71 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   __syncthreads();
 
   // p = exp(z - lse) with the forward's primitive; d = g (1 - p) on the
-  // target column, (-g) p elsewhere; RNE to bf16.
+  // target column, (-g) p elsewhere; RNE to bf16.  Lane (li, g) holds rows
+  // 4g .. 4g+3 of each 16 x 16 block, so its four values of a column pack
+  // into 8 contiguous bytes of the transposed tile.
+  uint32_t dv[8][4][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    float L[4], G[4];
+    int code[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int lr = wm * 128 + i * 16 + 4 * g + q;
-      const int code = sm.code[lr];
-      const float L = sm.lse[lr], G = sm.g[lr];
+      code[q] = sm.code[lr];
+      L[q] = sm.lse[lr];
+      G[q] = sm.g[lr];
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int lc = wn * 64 + j * 16 + li;
+    for (int j = 0; j < 4; ++j) {
+      const int lc = wn * 64 + j * 16 + li;
+      uint16_t b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         float d = 0.0f;
-        if (code != -2 && v0 + lc < v) {
-          const float p = exp_sub(acc[i][j][q], L);
-          d = lc == code ? G * (1.0f - p) : (-G) * p;
+        if (code[q] != -2 && v0 + lc < v) {
+          const float p = exp_sub(acc[i][j][q], L[q]);
+          d = lc == code[q] ? G[q] * (1.0f - p) : (-G[q]) * p;
         }
-        sm.u.tile[lr][lc] = bf16_bits(d);
+        b[q] = bf16_bits(d);
       }
+      dv[i][j][0] = static_cast<uint32_t>(b[0]) | (static_cast<uint32_t>(b[1]) << 16);
+      dv[i][j][1] = static_cast<uint32_t>(b[2]) | (static_cast<uint32_t>(b[3]) << 16);
+    }
+  }
+  // dz^T: tile[c][r] (column-major), then 256 rows of dz^T x 32 chunks.
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int lc = wn * 64 + j * 16 + li;
+      const int lr = wm * 128 + i * 16 + 4 * g;
+      *reinterpret_cast<uint2*>(&sm.u.tile[lc][lr]) = make_uint2(dv[i][j][0], dv[i][j][1]);
     }
   __syncthreads();
-  // dz rows: 256 rows x 32 chunks of 16 bytes.
+  for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
+    const int c = idx >> 5, r = (idx & 31) * 8;
+    store_stream(dzt + (v0 + c) * ld_dzt + m0 + r,
+                 *reinterpret_cast<const uint4*>(&sm.u.tile[c][r]));
+  }
+  __syncthreads();
+  // dz: tile[r][c] (row-major), then 256 rows of dz x 32 chunks.
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int lc = wn * 64 + j * 16 + li;
+      const int lr = wm * 128 + i * 16 + 4 * g;
+      sm.u.tile[lr][lc] = static_cast<uint16_t>(dv[i][j][0] & 0xffffu);
+      sm.u.tile[lr + 1][lc] = static_cast<uint16_t>(dv[i][j][0] >> 16);
+      sm.u.tile[lr + 2][lc] = static_cast<uint16_t>(dv[i][j][1] & 0xffffu);
+      sm.u.tile[lr + 3][lc] = static_cast<uint16_t>(dv[i][j][1] >> 16);
+    }
+  __syncthreads();
   for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
     const int r = idx >> 5, c = (idx & 31) * 8;
     store_stream(dz + (m0 + r) * ld_dz + v0 + c,
                  *reinterpret_cast<const uint4*>(&sm.u.tile[r][c]));
-  }
-  // dz^T rows: 256 columns x 32 chunks of 8 rows; lanes walk the columns.
-  for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
-    const int c = idx & (kT - 1), r = (idx >> 8) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = static_cast<uint32_t>(sm.u.tile[r + 2 * e][c]) |
-             (static_cast<uint32_t>(sm.u.tile[r + 2 * e + 1][c]) << 16);
-    store_stream(dzt + (v0 + c) * ld_dzt + m0 + r, make_uint4(w[0], w[1], w[2], w[3]));
   }
 }
 
