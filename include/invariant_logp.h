@@ -62,10 +62,18 @@ enum logp_status {
   LOGP_ERR_HIP = 9        /* a HIP launch or copy failed */
 };
 
-/* Logits element types. */
+/* Logits element types ("Batch-Invariant LogP", Tensor Contract: fp32 / fp16
+ * / bf16 logits). */
 enum logp_dtype {
-  LOGP_F32 = 0,  /* IEEE binary32 */
-  LOGP_BF16 = 1  /* bfloat16, widened exactly to fp32 before any arithmetic */
+  LOGP_F32 = 0,   /* IEEE binary32 */
+  LOGP_BF16 = 1,  /* bfloat16, widened exactly to fp32 before any arithmetic */
+  LOGP_F16 = 2    /* IEEE binary16, widened exactly to fp32 before any arithmetic */
+};
+
+/* Target index types (the Tensor Contract's integer target_ids). */
+enum logp_index_dtype {
+  LOGP_I64 = 0,  /* int64 */
+  LOGP_I32 = 1   /* int32 */
 };
 
 /*
@@ -81,14 +89,15 @@ size_t logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width,
  * Selected-token log-probability and row LSE ("Batch-Invariant LogP",
  * Entry Point, Tensor Contract and Tensor Parallel).
  *
- *   logits        [n, ld] row-major, first v columns used; dtype LOGP_F32 or
- *                 LOGP_BF16.  Any alignment is accepted; rows whose start is
- *                 16-byte aligned stream with 128-bit loads.
- *   targets       int64 [n].
+ *   logits        [n, ld] row-major, first v columns used; dtype LOGP_F32,
+ *                 LOGP_BF16 or LOGP_F16.  Any alignment is accepted; rows
+ *                 whose start is 16-byte aligned stream with 128-bit loads.
+ *   targets       [n] of target_dtype (LOGP_I64 or LOGP_I32; LOGP_ERR_DTYPE
+ *                 otherwise).
  *   ignore_index  rows with this target give logp = +0, lse = +0 and are not
  *                 read.
  *   tile_width    vocabulary tile width W: 512, 1024, 2048, 4096 or 8192 for
- *                 bf16; 256, 512, 1024, 2048 or 4096 for fp32.  T =
+ *                 bf16 and fp16; 256, 512, 1024, 2048 or 4096 for fp32.  T =
  *                 ceil(v / W) must not exceed 4096.  W is part of the
  *                 arithmetic contract (it fixes the summation tree).
  *   num_shards    S >= 1, v % S == 0: the vocabulary is split into S nominal
@@ -108,9 +117,9 @@ size_t logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width,
  *                 bytes (may be NULL when that is 0), 256-byte aligned.
  */
 int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
-                 int64_t ld, const int64_t* targets, int64_t ignore_index,
-                 int32_t tile_width, int32_t num_shards, int32_t validate,
-                 float* logp_out, float* lse_out, void* workspace,
+                 int64_t ld, const void* targets, int32_t target_dtype,
+                 int64_t ignore_index, int32_t tile_width, int32_t num_shards,
+                 int32_t validate, float* logp_out, float* lse_out, void* workspace,
                  size_t workspace_bytes, void* hip_stream);
 
 /*
@@ -121,7 +130,8 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
  *   dlogits[r, j] = RNE_dtype( g[r] * u ),  u = 1 - p if j == t_r, else -p,
  *   p = exp(x[r, j] - lse[r]) with the same exp primitive as the forward.
  *
- *   logits, dtype, n, v, ld, targets, ignore_index: as for logp_fwd.
+ *   logits, dtype, n, v, ld, targets, target_dtype, ignore_index: as for
+ *               logp_fwd.
  *   tile_width  accepted for symmetry with logp_fwd and checked the same
  *               way; it does not change any bit (the backward is elementwise).
  *   lse         fp32 [n] from logp_fwd.
@@ -133,9 +143,10 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
  *               undefined.  A row with an invalid target gets u = -p.
  */
 int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
-                 int64_t ld, const int64_t* targets, int64_t ignore_index,
-                 int32_t tile_width, const float* lse, const float* grad_logp,
-                 void* dlogits_out, int64_t ld_out, void* hip_stream);
+                 int64_t ld, const void* targets, int32_t target_dtype,
+                 int64_t ignore_index, int32_t tile_width, const float* lse,
+                 const float* grad_logp, void* dlogits_out, int64_t ld_out,
+                 void* hip_stream);
 
 /*
  * Workspace of linear_logp_fwd in bytes: the [T, n] partials (m, s) for
@@ -161,16 +172,16 @@ size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width)
  *               block).
  *   hidden, weight, ld_h and ld_w must give 16-byte aligned rows
  *   (LOGP_ERR_ALIGN otherwise).
- *   targets, ignore_index, logp_out, lse_out (may be NULL): as logp_fwd,
- *   with no validation (invalid active targets give logp = NaN).
+ *   targets, target_dtype, ignore_index, logp_out, lse_out (may be NULL): as
+ *   logp_fwd, with no validation (invalid active targets give logp = NaN).
  *   workspace   at least linear_logp_fwd_workspace_bytes(...) bytes,
  *               256-byte aligned.
  */
 int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight,
                         int64_t ld_w, int64_t n, int64_t h, int64_t v,
-                        const int64_t* targets, int64_t ignore_index,
-                        int32_t tile_width, float* logp_out, float* lse_out,
-                        void* workspace, size_t workspace_bytes,
+                        const void* targets, int32_t target_dtype,
+                        int64_t ignore_index, int32_t tile_width, float* logp_out,
+                        float* lse_out, void* workspace, size_t workspace_bytes,
                         void* hip_stream);
 
 /*
@@ -194,7 +205,8 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  * No product is split, so dhidden[r] depends only on row r and dweight is
  * deterministic for a given row order.
  *
- *   hidden, ld_h, weight, ld_w, n, h, v, targets, ignore_index, tile_width:
+ *   hidden, ld_h, weight, ld_w, n, h, v, targets, target_dtype,
+ *   ignore_index, tile_width:
  *               as linear_logp_fwd (h a multiple of 64, tile_width 256,
  *               16-byte aligned rows).
  *   lse         fp32 [n] from linear_logp_fwd.
@@ -210,8 +222,9 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  * term.
  */
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
-                        int64_t n, int64_t h, int64_t v, const int64_t* targets,
-                        int64_t ignore_index, int32_t tile_width, const float* lse,
+                        int64_t n, int64_t h, int64_t v, const void* targets,
+                        int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
+                        const float* lse,
                         const float* grad_logp, int32_t out_dtype, void* dhidden,
                         int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
                         size_t workspace_bytes, void* hip_stream);

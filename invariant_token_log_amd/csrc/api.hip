@@ -12,13 +12,25 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Chunks per lane for a supported (dtype, tile width), else 0.
 int chunks_for(int32_t dtype, int32_t w) {
-  const int per = dtype == LOGP_BF16 ? 512 : 256;  // one 16-byte chunk per lane
+  const int per = dtype == LOGP_F32 ? 256 : 512;  // one 16-byte chunk per lane
   if (w < per || w % per) return 0;
   const int c = w / per;
   return (c == 1 || c == 2 || c == 4 || c == 8 || c == 16) ? c : 0;
 }
 
-int elt_size(int32_t dtype) { return dtype == LOGP_BF16 ? 2 : 4; }
+int elt_size(int32_t dtype) { return dtype == LOGP_F32 ? 4 : 2; }
+
+bool valid_dtype(int32_t dtype) {
+  return dtype == LOGP_F32 || dtype == LOGP_BF16 || dtype == LOGP_F16;
+}
+
+bool valid_index(int32_t target_dtype) {
+  return target_dtype == LOGP_I64 || target_dtype == LOGP_I32;
+}
+
+itl::Targets targets_of(const void* p, int32_t target_dtype) {
+  return itl::Targets{p, target_dtype == LOGP_I32 ? 1 : 0};
+}
 
 bool aligned16(const void* p, int64_t ld, int32_t dtype) {
   return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * elt_size(dtype)) % 16 == 0);
@@ -26,7 +38,7 @@ bool aligned16(const void* p, int64_t ld, int32_t dtype) {
 
 // Common checks of logp_fwd / logp_bwd that involve no pointer.
 int32_t check_stream_args(int32_t dtype, int64_t n, int64_t v, int64_t ld, int32_t w) {
-  if (dtype != LOGP_F32 && dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
+  if (!valid_dtype(dtype)) return LOGP_ERR_DTYPE;
   if (n < 0 || v < 1 || ld < v) return LOGP_ERR_SHAPE;
   if (chunks_for(dtype, w) == 0) return LOGP_ERR_TILE;
   if ((v + w - 1) / w > kMaxTiles) return LOGP_ERR_SHAPE;
@@ -44,7 +56,8 @@ FwdLayout fwd_layout(int64_t n, int64_t ntiles, int32_t shards, int32_t validate
     l.total = validate ? kAlign : 0;
     return l;
   }
-  const size_t table = round_up(static_cast<size_t>(ntiles) * static_cast<size_t>(n) * sizeof(float));
+  const size_t table =
+      round_up(static_cast<size_t>(ntiles) * static_cast<size_t>(n) * sizeof(float));
   l.pm = kAlign;
   l.ps = l.pm + table;
   l.pt = l.ps + table;
@@ -70,11 +83,13 @@ size_t logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width, int32_
 }
 
 int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_t ld,
-                 const int64_t* targets, int64_t ignore_index, int32_t tile_width,
-                 int32_t num_shards, int32_t validate, float* logp_out, float* lse_out,
-                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+                 const void* targets, int32_t target_dtype, int64_t ignore_index,
+                 int32_t tile_width, int32_t num_shards, int32_t validate, float* logp_out,
+                 float* lse_out, void* workspace, size_t workspace_bytes, void* hip_stream) {
   int32_t st = check_stream_args(dtype, n, v, ld, tile_width);
   if (st != LOGP_OK) return st;
+  if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
+  const itl::Targets tg = targets_of(targets, target_dtype);
   if (num_shards < 1 || v % num_shards) return LOGP_ERR_SHARDS;
   const int ntiles = static_cast<int>((v + tile_width - 1) / tile_width);
   const FwdLayout lay = fwd_layout(n, ntiles, num_shards, validate);
@@ -93,7 +108,7 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
   (void)hipGetLastError();
   if (status && hipMemsetAsync(status, 0, sizeof(int), s) != hipSuccess) return LOGP_ERR_HIP;
   if (num_shards == 1) {
-    itl::launch_fwd_fused(dtype, vec, chunks, logits, ld, n, v, targets, ignore_index, ntiles,
+    itl::launch_fwd_fused(dtype, vec, chunks, logits, ld, n, v, tg, ignore_index, ntiles,
                           logp_out, lse_out, status, s);
   } else {
     float* pm = reinterpret_cast<float*>(ws + lay.pm);
@@ -105,10 +120,10 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
       const int kb = static_cast<int>((sh * per + tile_width - 1) / tile_width);
       const int ke = static_cast<int>(((sh + 1) * per + tile_width - 1) / tile_width);
       if (ke > kb)
-        itl::launch_fwd_partials(dtype, vec, chunks, logits, ld, n, v, targets, ignore_index, kb,
+        itl::launch_fwd_partials(dtype, vec, chunks, logits, ld, n, v, tg, ignore_index, kb,
                                  ke, pm, ps, pt, s);
     }
-    itl::launch_fwd_merge(pm, ps, pt, n, ntiles, 1, n, v, targets, ignore_index, logp_out,
+    itl::launch_fwd_merge(pm, ps, pt, n, ntiles, 1, n, v, tg, ignore_index, logp_out,
                           lse_out, status, s);
   }
   st = hip_status();
@@ -124,17 +139,19 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
 }
 
 int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_t ld,
-                 const int64_t* targets, int64_t ignore_index, int32_t tile_width,
-                 const float* lse, const float* grad_logp, void* dlogits_out, int64_t ld_out,
-                 void* hip_stream) {
+                 const void* targets, int32_t target_dtype, int64_t ignore_index,
+                 int32_t tile_width, const float* lse, const float* grad_logp, void* dlogits_out,
+                 int64_t ld_out, void* hip_stream) {
   int32_t st = check_stream_args(dtype, n, v, ld, tile_width);
   if (st != LOGP_OK) return st;
+  if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
   if (ld_out < v) return LOGP_ERR_SHAPE;
   if (n == 0) return LOGP_OK;
   if (!logits || !targets || !lse || !grad_logp || !dlogits_out) return LOGP_ERR_NULL;
   const bool vec = aligned16(logits, ld, dtype) && aligned16(dlogits_out, ld_out, dtype);
   (void)hipGetLastError();
-  itl::launch_bwd(dtype, vec, logits, ld, n, v, targets, ignore_index, lse, grad_logp,
+  itl::launch_bwd(dtype, vec, logits, ld, n, v, targets_of(targets, target_dtype), ignore_index,
+                  lse, grad_logp,
                   dlogits_out, ld_out, static_cast<hipStream_t>(hip_stream));
   return hip_status();
 }
@@ -146,11 +163,13 @@ size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width)
 }
 
 int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
-                        int64_t n, int64_t h, int64_t v, const int64_t* targets,
-                        int64_t ignore_index, int32_t tile_width, float* logp_out,
-                        float* lse_out, void* workspace, size_t workspace_bytes,
-                        void* hip_stream) {
+                        int64_t n, int64_t h, int64_t v, const void* targets,
+                        int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
+                        float* logp_out, float* lse_out, void* workspace,
+                        size_t workspace_bytes, void* hip_stream) {
   if (n < 0 || v < 1 || h < 1 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
+  if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
+  const itl::Targets tg = targets_of(targets, target_dtype);
   if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
   const int64_t ntiles = (v + tile_width - 1) / tile_width;
   if (ntiles > (int64_t{1} << 24) || (n + 127) / 128 * ntiles > (int64_t{1} << 30))
@@ -170,9 +189,9 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
   float* pt = reinterpret_cast<float*>(ws + lay.pt);
   (void)hipGetLastError();
   itl::launch_linear_partials(static_cast<const uint16_t*>(hidden), ld_h,
-                              static_cast<const uint16_t*>(weight), ld_w, n, h, v, targets,
+                              static_cast<const uint16_t*>(weight), ld_w, n, h, v, tg,
                               ignore_index, pm, ps, pt, s);
-  itl::launch_fwd_merge(pm, ps, pt, n, static_cast<int>(ntiles), ntiles, 1, v, targets,
+  itl::launch_fwd_merge(pm, ps, pt, n, static_cast<int>(ntiles), ntiles, 1, v, tg,
                         ignore_index, logp_out, lse_out, nullptr, s);
   return hip_status();
 }
@@ -184,8 +203,9 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
 }
 
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
-                        int64_t n, int64_t h, int64_t v, const int64_t* targets,
-                        int64_t ignore_index, int32_t tile_width, const float* lse,
+                        int64_t n, int64_t h, int64_t v, const void* targets,
+                        int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
+                        const float* lse,
                         const float* grad_logp, int32_t out_dtype, void* dhidden, int64_t ld_dh,
                         void* dweight, int64_t ld_dw, void* workspace, size_t workspace_bytes,
                         void* hip_stream) {
@@ -196,6 +216,7 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
     return LOGP_ERR_SHAPE;
   if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
   if (out_dtype != LOGP_F32 && out_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
+  if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
   if (!dhidden && !dweight) return LOGP_ERR_NULL;
   if ((dhidden && ld_dh < h) || (dweight && ld_dw < h)) return LOGP_ERR_SHAPE;
   if (n == 0 && !dweight) return LOGP_OK;
@@ -208,8 +229,9 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
     return LOGP_ERR_WORKSPACE;
   (void)hipGetLastError();
   itl::launch_linear_bwd(static_cast<const uint16_t*>(hidden), ld_h,
-                         static_cast<const uint16_t*>(weight), ld_w, n, h, v, targets,
-                         ignore_index, lse, grad_logp, out_dtype == LOGP_BF16, dhidden, ld_dh,
+                         static_cast<const uint16_t*>(weight), ld_w, n, h, v,
+                         targets_of(targets, target_dtype), ignore_index, lse, grad_logp,
+                         out_dtype == LOGP_BF16, dhidden, ld_dh,
                          dweight, ld_dw, static_cast<char*>(workspace),
                          static_cast<hipStream_t>(hip_stream));
   return hip_status();

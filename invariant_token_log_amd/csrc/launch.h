@@ -7,32 +7,44 @@
 
 namespace itl {
 
-enum { kF32 = 0, kBF16 = 1 };
+enum { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+// Row targets as the caller stores them (int64 or int32), widened to int64 on
+// read.  Kernels take the pointer as a __restrict__ parameter and build this
+// view inside, so that uniform target reads stay scalar loads.
+struct Targets {
+  const void* p;
+  int32_t is32;
+  __host__ __device__ __forceinline__ int64_t operator[](int64_t r) const {
+    return is32 ? static_cast<int64_t>(static_cast<const int32_t*>(p)[r])
+                : static_cast<const int64_t*>(p)[r];
+  }
+};
 
 void launch_fwd_fused(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
-                      int64_t n, int64_t v, const int64_t* targets, int64_t ignore,
+                      int64_t n, int64_t v, Targets targets, int64_t ignore,
                       int ntiles, float* logp, float* lse, int* status, hipStream_t s);
 
 void launch_fwd_partials(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
-                         int64_t n, int64_t v, const int64_t* targets, int64_t ignore,
+                         int64_t n, int64_t v, Targets targets, int64_t ignore,
                          int k_begin, int k_end, float* pm, float* ps, float* pt,
                          hipStream_t s);
 
 // Partial (r, k) of the [n, T] / [T, n] tables sits at r * row_stride + k * tile_stride.
 void launch_fwd_merge(const float* pm, const float* ps, const float* pt, int64_t n,
                       int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
-                      const int64_t* targets, int64_t ignore, float* logp, float* lse,
+                      Targets targets, int64_t ignore, float* logp, float* lse,
                       int* status, hipStream_t s);
 
 void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, int64_t v,
-                const int64_t* targets, int64_t ignore, const float* lse, const float* grad,
+                Targets targets, int64_t ignore, const float* lse, const float* grad,
                 void* dlogits, int64_t ld_out, hipStream_t s);
 
 // Fused LM-head statistics: writes the row-major [n, T] partials and the
 // target logits of every active row (T = ceil(v / 256)).
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
                             int64_t ld_w, int64_t n, int64_t h, int64_t v,
-                            const int64_t* targets, int64_t ignore, float* pm, float* ps,
+                            Targets targets, int64_t ignore, float* pm, float* ps,
                             float* pt, hipStream_t s);
 
 constexpr int kLinearTile = 256;
@@ -48,7 +60,7 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
 
 // dh [n, h] and/or dW [v, h] (either may be null) as fp32 or bf16 (bf16_out).
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
-                       int64_t n, int64_t h, int64_t v, const int64_t* targets, int64_t ignore,
+                       int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
                        const float* lse, const float* grad, bool bf16_out, void* dh,
                        int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s);
 

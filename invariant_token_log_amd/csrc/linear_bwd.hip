@@ -90,15 +90,19 @@ struct SmemDz {
   } u;
   float lse[kT];
   float g[kT];
-  int code[kT];  // -2: no gradient (row past n or ignored); -1: target outside the block; else t - v0
+  // -2: no gradient (row past n or ignored); -1: target outside the block;
+  // else t - v0
+  int code[kT];
 };
 
 __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
-    const int64_t* __restrict__ targets, int64_t ignore_index, const float* __restrict__ lse,
+    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
+    const float* __restrict__ lse,
     const float* __restrict__ grad, uint16_t* __restrict__ dz, int64_t ld_dz,
     uint16_t* __restrict__ dzt, int64_t ld_dzt) {
+  const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemDz sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -302,7 +306,7 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
 }
 
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
-                       int64_t n, int64_t h, int64_t v, const int64_t* targets, int64_t ignore,
+                       int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
                        const float* lse, const float* grad, bool bf16_out, void* dh,
                        int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s) {
   if (n == 0) {
@@ -324,7 +328,8 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + l.dzt);
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
   hipLaunchKernelGGL(linear_dz_kernel, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0, s,
-                     hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets, ignore, lse,
+                     hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
+                       targets.is32, ignore, lse,
                      grad, dz, l.vp, dzt, l.np);
   if (dh) {
     hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),

@@ -58,7 +58,7 @@ struct Reduce {
 // Per-row code for the epilogue: -2 = no statistics (row past n, or its
 // target is ignore_index), -1 = target column outside this vocabulary block,
 // else the target column minus v0.
-__device__ __forceinline__ int row_code(int64_t r, int64_t n, const int64_t* targets,
+__device__ __forceinline__ int row_code(int64_t r, int64_t n, Targets targets,
                                         int64_t ignore_index, int64_t v0, int64_t v) {
   if (r >= n) return -2;
   const int64_t t = targets[r];
@@ -198,8 +198,9 @@ struct SmemDma {
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
-    const int64_t* __restrict__ targets, int64_t ignore_index, float* __restrict__ pm,
+    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
     float* __restrict__ ps, float* __restrict__ pt) {
+  const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemDma sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -241,8 +242,9 @@ struct SmemReg {
 __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
-    const int64_t* __restrict__ targets, int64_t ignore_index, float* __restrict__ pm,
+    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
     float* __restrict__ ps, float* __restrict__ pt) {
+  const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemReg sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -296,10 +298,12 @@ __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
     bf16x8 a[4], b[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(&sm.a[buf][(wm * 64 + i * 16 + li) * kLdsStride + g * 8]);
+      a[i] = *reinterpret_cast<const bf16x8*>(
+          &sm.a[buf][(wm * 64 + i * 16 + li) * kLdsStride + g * 8]);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(&sm.b[buf][(wn * 128 + j * 16 + li) * kLdsStride + g * 8]);
+      b[j] = *reinterpret_cast<const bf16x8*>(
+          &sm.b[buf][(wn * 128 + j * 16 + li) * kLdsStride + g * 8]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -322,18 +326,20 @@ __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
 
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
                             int64_t ld_w, int64_t n, int64_t h, int64_t v,
-                            const int64_t* targets, int64_t ignore, float* pm, float* ps,
+                            Targets targets, int64_t ignore, float* pm, float* ps,
                             float* pt, hipStream_t s) {
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
   if (n <= 128) {
     const int mblocks = static_cast<int>((n + 127) / 128);
     hipLaunchKernelGGL(linear_stats_regstage, dim3(mblocks * vblocks), dim3(kRegThreads), 0, s,
-                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets, ignore,
+                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
+                       targets.is32, ignore,
                        pm, ps, pt);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     hipLaunchKernelGGL(linear_stats_dma, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,
-                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets, ignore,
+                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
+                       targets.is32, ignore,
                        pm, ps, pt);
   }
 }

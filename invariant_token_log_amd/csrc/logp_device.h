@@ -90,11 +90,15 @@ template <> struct Elt<float> {
   static constexpr int kPerChunk = 4;  // 16 bytes
   __device__ static float load(const float* p, int64_t i) { return p[i]; }
 };
-template <> struct Elt<uint16_t> {
+template <> struct Elt<uint16_t> {  // bfloat16 bits
   static constexpr int kPerChunk = 8;  // 16 bytes
   __device__ static float load(const uint16_t* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
   }
+};
+template <> struct Elt<_Float16> {  // IEEE binary16, widened exactly (v_cvt_f32_f16)
+  static constexpr int kPerChunk = 8;  // 16 bytes
+  __device__ static float load(const _Float16* p, int64_t i) { return static_cast<float>(p[i]); }
 };
 
 // 16-byte streaming accesses with the non-temporal hint: the logits are read
@@ -113,6 +117,27 @@ __device__ __forceinline__ void store_stream(void* p, uint4 v) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// Widen the elements of one 16-byte chunk to fp32 (exact for every type).
+template <typename T>
+__device__ __forceinline__ void widen_chunk(const uint4 q, float (&x)[Elt<T>::kPerChunk]) {
+  if constexpr (Elt<T>::kPerChunk == 4) {
+    x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
+    x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
+  } else if constexpr (sizeof(T) == 2 && __is_same(T, _Float16)) {
+    x[0] = f16_lo(q.x); x[1] = f16_hi(q.x); x[2] = f16_lo(q.y); x[3] = f16_hi(q.y);
+    x[4] = f16_lo(q.z); x[5] = f16_hi(q.z); x[6] = f16_lo(q.w); x[7] = f16_hi(q.w);
+  } else {
+    x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x); x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
+    x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z); x[6] = bf16_lo(q.w); x[7] = bf16_hi(q.w);
+  }
+}
 
 // Widen one 16-byte chunk that starts at element c of a row; elements at or
 // beyond v become -inf and are not read.  VEC: the chunk start is 16-byte
@@ -122,16 +147,7 @@ __device__ __forceinline__ void load_chunk(const T* row, int64_t c, int64_t v,
                                            float (&x)[Elt<T>::kPerChunk]) {
   constexpr int E = Elt<T>::kPerChunk;
   if (VEC && c + E <= v) {
-    const uint4 q = load_stream(row + c);
-    if constexpr (E == 4) {
-      x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
-      x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
-    } else {
-      x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x);
-      x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
-      x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z);
-      x[6] = bf16_lo(q.w); x[7] = bf16_hi(q.w);
-    }
+    widen_chunk<T>(load_stream(row + c), x);
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e)

@@ -25,8 +25,9 @@ constexpr int64_t kMaxGridY = 65535;        // backward grid rows (grid-stride b
 template <typename T, int C, bool VEC>
 __global__ __launch_bounds__(kFwdBlock) void logp_fwd_fused_kernel(
     const T* __restrict__ logits, int64_t ld, int64_t n, int64_t v,
-    const int64_t* __restrict__ targets, int64_t ignore_index, int ntiles,
+    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, int ntiles,
     float* __restrict__ logp, float* __restrict__ lse, int* __restrict__ status) {
+  const Targets targets{tgt, tgt32};
   extern __shared__ float lds[];
   float* lm = lds;
   float* ls = lds + ntiles;
@@ -68,15 +69,17 @@ __global__ __launch_bounds__(kFwdBlock) void logp_fwd_fused_kernel(
 
 // ---------------------------------------------------------------------------
 // Shard partials: the same tile statistic over the tiles [k_begin, k_end) a
-// shard owns, written to the tile-major [T, n] tables pm / ps.  The owner of the target's tile copies the target
-// logit into pt[r].  Ignored rows are skipped (the merge never reads them).
+// shard owns, written to the tile-major [T, n] tables pm / ps.  The owner of
+// the target's tile copies the target logit into pt[r].  Ignored rows are
+// skipped (the merge never reads them).
 // ---------------------------------------------------------------------------
 template <typename T, int C, bool VEC>
 __global__ __launch_bounds__(kFwdBlock) void logp_partials_kernel(
     const T* __restrict__ logits, int64_t ld, int64_t n, int64_t v,
-    const int64_t* __restrict__ targets, int64_t ignore_index, int k_begin,
+    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, int k_begin,
     int k_end, float* __restrict__ pm, float* __restrict__ ps,
     float* __restrict__ pt) {
+  const Targets targets{tgt, tgt32};
   constexpr int W = C * kWave * Elt<T>::kPerChunk;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -107,8 +110,9 @@ __global__ __launch_bounds__(kFwdBlock) void logp_partials_kernel(
 __global__ __launch_bounds__(kBlock) void logp_merge_kernel(
     const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ pt,
     int64_t n, int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
-    const int64_t* __restrict__ targets, int64_t ignore_index, float* __restrict__ logp,
+    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ logp,
     float* __restrict__ lse, int* __restrict__ status) {
+  const Targets targets{tgt, tgt32};
   const int lane = threadIdx.x % kWave;
   const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
   for (int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; r < n;
@@ -148,10 +152,22 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const _Float16 a = static_cast<_Float16>(lo);  // v_cvt_f16_f32: round to nearest even
+  const _Float16 b = static_cast<_Float16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
 template <typename T> __device__ __forceinline__ void store_elem(T* p, int64_t i, float d);
-template <> __device__ __forceinline__ void store_elem<float>(float* p, int64_t i, float d) { p[i] = d; }
+template <> __device__ __forceinline__ void store_elem<float>(float* p, int64_t i, float d) {
+  p[i] = d;
+}
 template <> __device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, int64_t i, float d) {
   p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(d));
+}
+template <> __device__ __forceinline__ void store_elem<_Float16>(_Float16* p, int64_t i, float d) {
+  p[i] = static_cast<_Float16>(d);
 }
 
 __device__ __forceinline__ float grad_elem(float x, float L, float g, float ng, bool is_target) {
@@ -164,13 +180,7 @@ __device__ __forceinline__ uint4 grad_chunk(const uint4 q, float L, float g, flo
                                             int64_t c, int64_t t) {
   constexpr int E = Elt<T>::kPerChunk;
   float x[E];
-  if constexpr (E == 4) {
-    x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
-    x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
-  } else {
-    x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x); x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
-    x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z); x[6] = bf16_lo(q.w); x[7] = bf16_hi(q.w);
-  }
+  widen_chunk<T>(q, x);
   float d[E];
   if (t >= c && t < c + E) {
 #pragma unroll
@@ -183,6 +193,9 @@ __device__ __forceinline__ uint4 grad_chunk(const uint4 q, float L, float g, flo
   if constexpr (E == 4) {
     o.x = __float_as_uint(d[0]); o.y = __float_as_uint(d[1]);
     o.z = __float_as_uint(d[2]); o.w = __float_as_uint(d[3]);
+  } else if constexpr (__is_same(T, _Float16)) {
+    o.x = pack_f16(d[0], d[1]); o.y = pack_f16(d[2], d[3]);
+    o.z = pack_f16(d[4], d[5]); o.w = pack_f16(d[6], d[7]);
   } else {
     o.x = pack_bf16(d[0], d[1]); o.y = pack_bf16(d[2], d[3]);
     o.z = pack_bf16(d[4], d[5]); o.w = pack_bf16(d[6], d[7]);
@@ -193,9 +206,10 @@ __device__ __forceinline__ uint4 grad_chunk(const uint4 q, float L, float g, flo
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kBlock) void logp_bwd_kernel(
     const T* logits, int64_t ld, int64_t n, int64_t v,
-    const int64_t* __restrict__ targets, int64_t ignore_index,
+    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse, const float* __restrict__ grad, T* dlogits,
     int64_t ld_out) {
+  const Targets targets{tgt, tgt32};
   constexpr int E = Elt<T>::kPerChunk;
   // Thread (x, tid) owns the 16-byte chunk c = x * 256 + tid of every row it
   // visits: consecutive workgroups walk along a row, so the whole launch
@@ -238,15 +252,15 @@ static unsigned row_grid(int64_t n) {
 
 template <typename T, bool VEC>
 static void fused_dispatch(int chunks, const void* logits, int64_t ld, int64_t n, int64_t v,
-                           const int64_t* targets, int64_t ignore, int ntiles, float* logp,
-                           float* lse, int* status, hipStream_t s) {
+                           Targets tg, int64_t ignore, int ntiles, float* logp, float* lse,
+                           int* status, hipStream_t s) {
   const size_t lds = static_cast<size_t>(ntiles) * 2 * sizeof(float);
   const T* x = static_cast<const T*>(logits);
-#define ITL_FUSED(CC)                                                                   \
-  case CC:                                                                              \
-    hipLaunchKernelGGL((logp_fwd_fused_kernel<T, CC, VEC>), dim3(row_grid(n)),          \
-                       dim3(kFwdBlock), lds, s, x, ld, n, v, targets, ignore, ntiles, logp, \
-                       lse, status);                                                    \
+#define ITL_FUSED(CC)                                                                        \
+  case CC:                                                                                   \
+    hipLaunchKernelGGL((logp_fwd_fused_kernel<T, CC, VEC>), dim3(row_grid(n)),               \
+                       dim3(kFwdBlock), lds, s, x, ld, n, v, tg.p, tg.is32, ignore, ntiles, \
+                       logp, lse, status);                                                   \
     break;
   switch (chunks) { ITL_FUSED(1) ITL_FUSED(2) ITL_FUSED(4) ITL_FUSED(8) ITL_FUSED(16) }
 #undef ITL_FUSED
@@ -254,73 +268,89 @@ static void fused_dispatch(int chunks, const void* logits, int64_t ld, int64_t n
 
 template <typename T, bool VEC>
 static void partials_dispatch(int chunks, const void* logits, int64_t ld, int64_t n,
-                              int64_t v, const int64_t* targets, int64_t ignore, int kb,
-                              int ke, float* pm, float* ps, float* pt, hipStream_t s) {
+                              int64_t v, Targets tg, int64_t ignore, int kb, int ke, float* pm,
+                              float* ps, float* pt, hipStream_t s) {
   const T* x = static_cast<const T*>(logits);
-#define ITL_PART(CC)                                                                     \
-  case CC:                                                                               \
-    hipLaunchKernelGGL((logp_partials_kernel<T, CC, VEC>), dim3(row_grid(n)),            \
-                       dim3(kFwdBlock), 0, s, x, ld, n, v, targets, ignore, kb, ke, pm, ps, \
-                       pt);                                                              \
+#define ITL_PART(CC)                                                                           \
+  case CC:                                                                                     \
+    hipLaunchKernelGGL((logp_partials_kernel<T, CC, VEC>), dim3(row_grid(n)),                  \
+                       dim3(kFwdBlock), 0, s, x, ld, n, v, tg.p, tg.is32, ignore, kb, ke, pm, \
+                       ps, pt);                                                                \
     break;
   switch (chunks) { ITL_PART(1) ITL_PART(2) ITL_PART(4) ITL_PART(8) ITL_PART(16) }
 #undef ITL_PART
 }
 
 void launch_fwd_fused(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
-                      int64_t n, int64_t v, const int64_t* targets, int64_t ignore,
-                      int ntiles, float* logp, float* lse, int* status, hipStream_t s) {
+                      int64_t n, int64_t v, Targets tg, int64_t ignore, int ntiles,
+                      float* logp, float* lse, int* status, hipStream_t s) {
+#define ITL_F(TT, VV) \
+  fused_dispatch<TT, VV>(chunks, logits, ld, n, v, tg, ignore, ntiles, logp, lse, status, s)
   if (dtype == kF32) {
-    if (vec) fused_dispatch<float, true>(chunks, logits, ld, n, v, targets, ignore, ntiles, logp, lse, status, s);
-    else fused_dispatch<float, false>(chunks, logits, ld, n, v, targets, ignore, ntiles, logp, lse, status, s);
+    if (vec) ITL_F(float, true); else ITL_F(float, false);
+  } else if (dtype == kF16) {
+    if (vec) ITL_F(_Float16, true); else ITL_F(_Float16, false);
   } else {
-    if (vec) fused_dispatch<uint16_t, true>(chunks, logits, ld, n, v, targets, ignore, ntiles, logp, lse, status, s);
-    else fused_dispatch<uint16_t, false>(chunks, logits, ld, n, v, targets, ignore, ntiles, logp, lse, status, s);
+    if (vec) ITL_F(uint16_t, true); else ITL_F(uint16_t, false);
   }
+#undef ITL_F
 }
 
 void launch_fwd_partials(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
-                         int64_t n, int64_t v, const int64_t* targets, int64_t ignore,
-                         int k_begin, int k_end, float* pm, float* ps, float* pt,
-                         hipStream_t s) {
+                         int64_t n, int64_t v, Targets tg, int64_t ignore, int k_begin,
+                         int k_end, float* pm, float* ps, float* pt, hipStream_t s) {
+#define ITL_P(TT, VV) \
+  partials_dispatch<TT, VV>(chunks, logits, ld, n, v, tg, ignore, k_begin, k_end, pm, ps, pt, s)
   if (dtype == kF32) {
-    if (vec) partials_dispatch<float, true>(chunks, logits, ld, n, v, targets, ignore, k_begin, k_end, pm, ps, pt, s);
-    else partials_dispatch<float, false>(chunks, logits, ld, n, v, targets, ignore, k_begin, k_end, pm, ps, pt, s);
+    if (vec) ITL_P(float, true); else ITL_P(float, false);
+  } else if (dtype == kF16) {
+    if (vec) ITL_P(_Float16, true); else ITL_P(_Float16, false);
   } else {
-    if (vec) partials_dispatch<uint16_t, true>(chunks, logits, ld, n, v, targets, ignore, k_begin, k_end, pm, ps, pt, s);
-    else partials_dispatch<uint16_t, false>(chunks, logits, ld, n, v, targets, ignore, k_begin, k_end, pm, ps, pt, s);
+    if (vec) ITL_P(uint16_t, true); else ITL_P(uint16_t, false);
   }
+#undef ITL_P
 }
 
 void launch_fwd_merge(const float* pm, const float* ps, const float* pt, int64_t n,
                       int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
-                      const int64_t* targets, int64_t ignore, float* logp, float* lse,
-                      int* status, hipStream_t s) {
+                      Targets tg, int64_t ignore, float* logp, float* lse, int* status,
+                      hipStream_t s) {
   int64_t blocks = (n + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > kMaxRowBlocks) blocks = kMaxRowBlocks;
   hipLaunchKernelGGL(logp_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                     s, pm, ps, pt, n, ntiles, row_stride, tile_stride, v, targets, ignore, logp,
-                     lse, status);
+                     s, pm, ps, pt, n, ntiles, row_stride, tile_stride, v, tg.p, tg.is32, ignore,
+                     logp, lse, status);
+}
+
+template <typename T>
+static void bwd_dispatch(bool vec, dim3 grid, const void* logits, int64_t ld, int64_t n,
+                         int64_t v, Targets tg, int64_t ignore, const float* lse,
+                         const float* grad, void* dlogits, int64_t ld_out, hipStream_t s) {
+  const T* x = static_cast<const T*>(logits);
+  T* d = static_cast<T*>(dlogits);
+  if (vec)
+    hipLaunchKernelGGL((logp_bwd_kernel<T, true>), grid, dim3(kBlock), 0, s, x, ld, n, v, tg.p,
+                       tg.is32, ignore, lse, grad, d, ld_out);
+  else
+    hipLaunchKernelGGL((logp_bwd_kernel<T, false>), grid, dim3(kBlock), 0, s, x, ld, n, v, tg.p,
+                       tg.is32, ignore, lse, grad, d, ld_out);
 }
 
 void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, int64_t v,
-                const int64_t* targets, int64_t ignore, const float* lse, const float* grad,
-                void* dlogits, int64_t ld_out, hipStream_t s) {
+                Targets tg, int64_t ignore, const float* lse, const float* grad, void* dlogits,
+                int64_t ld_out, hipStream_t s) {
   const int64_t per = dtype == kF32 ? 4 : 8;  // elements per 16-byte chunk
   const int64_t chunks = (v + per - 1) / per;
   const dim3 grid(static_cast<unsigned>((chunks + kBlock - 1) / kBlock),
                   static_cast<unsigned>(n < kMaxGridY ? n : kMaxGridY));
-  if (dtype == kF32) {
-    const float* x = static_cast<const float*>(logits);
-    float* d = static_cast<float*>(dlogits);
-    if (vec) hipLaunchKernelGGL((logp_bwd_kernel<float, true>), grid, dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, lse, grad, d, ld_out);
-    else hipLaunchKernelGGL((logp_bwd_kernel<float, false>), grid, dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, lse, grad, d, ld_out);
-  } else {
-    const uint16_t* x = static_cast<const uint16_t*>(logits);
-    uint16_t* d = static_cast<uint16_t*>(dlogits);
-    if (vec) hipLaunchKernelGGL((logp_bwd_kernel<uint16_t, true>), grid, dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, lse, grad, d, ld_out);
-    else hipLaunchKernelGGL((logp_bwd_kernel<uint16_t, false>), grid, dim3(kBlock), 0, s, x, ld, n, v, targets, ignore, lse, grad, d, ld_out);
-  }
+  if (dtype == kF32)
+    bwd_dispatch<float>(vec, grid, logits, ld, n, v, tg, ignore, lse, grad, dlogits, ld_out, s);
+  else if (dtype == kF16)
+    bwd_dispatch<_Float16>(vec, grid, logits, ld, n, v, tg, ignore, lse, grad, dlogits, ld_out,
+                           s);
+  else
+    bwd_dispatch<uint16_t>(vec, grid, logits, ld, n, v, tg, ignore, lse, grad, dlogits, ld_out,
+                           s);
 }
 
 }  // namespace itl

@@ -116,9 +116,11 @@ __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict_
   __builtin_amdgcn_s_barrier();
   bf16x8 xa[8], xb[4], ya[8], yb[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(sm.s[0][1] + boff + j * 16 * kK);
+  for (int j = 0; j < 4; ++j)
+    xb[j] = *reinterpret_cast<const bf16x8*>(sm.s[0][1] + boff + j * 16 * kK);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const bf16x8*>(sm.s[0][0] + aoff + i * 16 * kK);
+  for (int i = 0; i < 8; ++i)
+    xa[i] = *reinterpret_cast<const bf16x8*>(sm.s[0][0] + aoff + i * 16 * kK);
   // One step: this wave's reads of stage KT % 4 and its loads of step KT+1
   // have landed (KT+2, KT+3 may still be in flight); after the barrier step
   // KT+1 is in LDS for every wave and stage KT % 4 is free.  A bare

@@ -9,14 +9,15 @@ LogpError.
 import torch
 
 from . import _lib
-from ._lib import LOGP_BF16, LOGP_F32, check
+from ._lib import LOGP_BF16, LOGP_F16, LOGP_F32, LOGP_I32, LOGP_I64, check
 
-_DTYPES = {torch.float32: LOGP_F32, torch.bfloat16: LOGP_BF16}
+_DTYPES = {torch.float32: LOGP_F32, torch.bfloat16: LOGP_BF16, torch.float16: LOGP_F16}
+_INDEX = {torch.int64: LOGP_I64, torch.int32: LOGP_I32}
 
 
 def _dtype_code(t):
     if t.dtype not in _DTYPES:
-        raise TypeError(f"logits dtype {t.dtype} is not supported (float32, bfloat16)")
+        raise TypeError(f"logits dtype {t.dtype} is not supported (float32, bfloat16, float16)")
     return _DTYPES[t.dtype]
 
 
@@ -37,8 +38,8 @@ def _rows(x):
 
 
 def _targets(t, n):
-    if t.dtype != torch.int64:
-        raise TypeError("targets must be int64")
+    if t.dtype not in _INDEX:
+        raise TypeError("targets must be int64 or int32")
     if not t.is_cuda:
         raise ValueError("targets must be on a ROCm device")
     t1 = t.reshape(-1)
@@ -72,8 +73,9 @@ def logp_fwd(logits, targets, ignore_index=-100, tile_width=4096, num_shards=1,
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = L.logp_fwd(x2.data_ptr(), _dtype_code(logits), n, v, ld, t1.data_ptr(),
-                    int(ignore_index), int(tile_width), int(num_shards), int(bool(validate)),
-                    logp_out.data_ptr(), lse_out.data_ptr(), ws_ptr, ws_len, _stream(dev))
+                    _INDEX[t1.dtype], int(ignore_index), int(tile_width), int(num_shards),
+                    int(bool(validate)), logp_out.data_ptr(), lse_out.data_ptr(), ws_ptr, ws_len,
+                    _stream(dev))
     check("logp_fwd", st)
     return logp_out.view(targets.shape), lse_out
 
@@ -95,7 +97,8 @@ def logp_bwd(logits, targets, lse, grad_logp, ignore_index=-100, tile_width=4096
     if v2 != v or d2.shape[0] != n or dlogits_out.dtype != logits.dtype:
         raise ValueError("dlogits_out must match the logits shape and dtype")
     st = _lib.lib().logp_bwd(x2.data_ptr(), _dtype_code(logits), n, v, ld, t1.data_ptr(),
-                             int(ignore_index), int(tile_width), lse.data_ptr(),
+                             _INDEX[t1.dtype], int(ignore_index), int(tile_width),
+                             lse.data_ptr(),
                              g.data_ptr(), d2.data_ptr(), ld_out, _stream(logits.device))
     check("logp_bwd", st)
     return dlogits_out
@@ -129,7 +132,7 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
     ld_h = hidden.stride(0) if n > 1 else h
     ld_w = weight.stride(0) if v > 1 else h
     st = L.linear_logp_fwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
-                           t1.data_ptr(), int(ignore_index), int(tile_width),
+                           t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
                            logp_out.data_ptr(), lse_out.data_ptr(), workspace.data_ptr(),
                            workspace.numel(), _stream(dev))
     check("linear_logp_fwd", st)
@@ -147,7 +150,7 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
         raise TypeError("hidden and weight must be bfloat16")
     if hidden.dim() != 2 or weight.dim() != 2 or hidden.stride(1) != 1 or weight.stride(1) != 1:
         raise ValueError("hidden [N, H] and weight [V, H] need a contiguous last dimension")
-    if out_dtype not in _DTYPES:
+    if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
     n, h = hidden.shape
     v, h2 = weight.shape
@@ -179,7 +182,8 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     ld_h = hidden.stride(0) if n > 1 else h
     ld_w = weight.stride(0) if v > 1 else h
     st = L.linear_logp_bwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
-                           t1.data_ptr(), int(ignore_index), int(tile_width), lse.data_ptr(),
+                           t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index),
+                           int(tile_width), lse.data_ptr(),
                            g.data_ptr(), _DTYPES[out_dtype],
                            dh.data_ptr() if dh is not None else None,
                            (dh.stride(0) if n > 1 else h) if dh is not None else 0,

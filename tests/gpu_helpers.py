@@ -85,10 +85,15 @@ def assert_grad_parity(d_gpu, d_ref, x, lse_ref, g, targets, ignore_index=-100, 
     budget = gg * p * (ATOL + RTOL * np.abs(x - lse_ref[:, None])) + 1e-6 * np.abs(d_ref)
     if d_gpu.dtype == torch.bfloat16:
         ok = (d >= rne_bf16(d_ref - budget)) & (d <= rne_bf16(d_ref + budget))
+    elif d_gpu.dtype == torch.float16:
+        # numpy's float64 -> float16 cast rounds to nearest even, subnormals included
+        lo = (d_ref - budget).astype(np.float16).astype(np.float64)
+        hi = (d_ref + budget).astype(np.float16).astype(np.float64)
+        ok = (d >= lo) & (d <= hi)
     else:
         ok = np.abs(d - d_ref) <= BWD_RTOL * np.abs(d_ref) + budget
     bad = ~ok & active[:, None]
     assert not bad.any(), (what, np.argwhere(bad)[:8], d[bad][:8], d_ref[bad][:8])
     if (~active).any():
         raw = d_gpu.reshape(d_ref.shape)[torch.from_numpy(~active).to(d_gpu.device)]
-        assert (raw.view(torch.int16 if raw.dtype == torch.bfloat16 else torch.int32) == 0).all()
+        assert (raw.view(torch.int32 if raw.dtype == torch.float32 else torch.int16) == 0).all()

@@ -52,14 +52,16 @@ def test_strings(L):
 FAKE = 0x10000  # a non-NULL address that the checks never dereference
 
 
-def _fwd(L, logits=FAKE, dtype=1, n=4, v=151936, ld=None, targets=FAKE, w=4096, shards=1,
-         validate=0, logp=FAKE, lse=FAKE, ws=None, ws_bytes=0):
-    return L.logp_fwd(logits, dtype, n, v, v if ld is None else ld, targets, -100, w, shards,
-                      validate, logp, lse, ws, ws_bytes, None)
+def _fwd(L, logits=FAKE, dtype=1, n=4, v=151936, ld=None, targets=FAKE, tdt=0, w=4096,
+         shards=1, validate=0, logp=FAKE, lse=FAKE, ws=None, ws_bytes=0):
+    return L.logp_fwd(logits, dtype, n, v, v if ld is None else ld, targets, tdt, -100, w,
+                      shards, validate, logp, lse, ws, ws_bytes, None)
 
 
 def test_fwd_argument_errors(L):
-    assert _fwd(L, dtype=2) == _lib.LOGP_ERR_DTYPE
+    assert _fwd(L, dtype=3) == _lib.LOGP_ERR_DTYPE
+    assert _fwd(L, tdt=2) == _lib.LOGP_ERR_DTYPE
+    assert _fwd(L, dtype=2, w=256, v=4096) == _lib.LOGP_ERR_TILE  # fp16 tiles start at 512
     assert _fwd(L, n=-1) == _lib.LOGP_ERR_SHAPE
     assert _fwd(L, v=0) == _lib.LOGP_ERR_SHAPE
     assert _fwd(L, ld=100) == _lib.LOGP_ERR_SHAPE
@@ -95,12 +97,13 @@ def test_fwd_workspace_sizes(L):
 
 def test_bwd_argument_errors(L):
     def bwd(**kw):
-        a = dict(logits=FAKE, dtype=1, n=4, v=151936, ld=151936, targets=FAKE, w=4096,
+        a = dict(logits=FAKE, dtype=1, n=4, v=151936, ld=151936, targets=FAKE, tdt=0, w=4096,
                  lse=FAKE, g=FAKE, d=FAKE, ld_out=151936)
         a.update(kw)
         return L.logp_bwd(a["logits"], a["dtype"], a["n"], a["v"], a["ld"], a["targets"],
-                          -100, a["w"], a["lse"], a["g"], a["d"], a["ld_out"], None)
+                          a["tdt"], -100, a["w"], a["lse"], a["g"], a["d"], a["ld_out"], None)
     assert bwd(dtype=5) == _lib.LOGP_ERR_DTYPE
+    assert bwd(tdt=-1) == _lib.LOGP_ERR_DTYPE
     assert bwd(ld_out=10) == _lib.LOGP_ERR_SHAPE
     assert bwd(w=100) == _lib.LOGP_ERR_TILE
     for k in ("logits", "targets", "lse", "g", "d"):
@@ -111,11 +114,12 @@ def test_bwd_argument_errors(L):
 def test_linear_argument_errors(L):
     def lin(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
-                 targets=FAKE, tile=256, logp=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40)
+                 targets=FAKE, tdt=0, tile=256, logp=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_fwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
-                                 a["v"], a["targets"], -100, a["tile"], a["logp"], a["lse"],
-                                 a["ws"], a["ws_bytes"], None)
+                                 a["v"], a["targets"], a["tdt"], -100, a["tile"], a["logp"],
+                                 a["lse"], a["ws"], a["ws_bytes"], None)
+    assert lin(tdt=9) == _lib.LOGP_ERR_DTYPE
     assert lin(tile=4096) == _lib.LOGP_ERR_TILE
     assert lin(h=100, ld_h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
     assert lin(ld_h=10) == _lib.LOGP_ERR_SHAPE
@@ -132,13 +136,15 @@ def test_linear_argument_errors(L):
 def test_linear_bwd_argument_errors(L):
     def lb(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
-                 targets=FAKE, tile=256, lse=FAKE, g=FAKE, out=0, dh=FAKE, ld_dh=4096,
+                 targets=FAKE, tdt=0, tile=256, lse=FAKE, g=FAKE, out=0, dh=FAKE, ld_dh=4096,
                  dw=FAKE, ld_dw=4096, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_bwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
-                                 a["v"], a["targets"], -100, a["tile"], a["lse"], a["g"],
-                                 a["out"], a["dh"], a["ld_dh"], a["dw"], a["ld_dw"], a["ws"],
-                                 a["ws_bytes"], None)
+                                 a["v"], a["targets"], a["tdt"], -100, a["tile"], a["lse"],
+                                 a["g"], a["out"], a["dh"], a["ld_dh"], a["dw"], a["ld_dw"],
+                                 a["ws"], a["ws_bytes"], None)
+    assert lb(tdt=5) == _lib.LOGP_ERR_DTYPE
+    assert lb(out=2) == _lib.LOGP_ERR_DTYPE
     assert lb(tile=512) == _lib.LOGP_ERR_TILE
     assert lb(h=100, ld_h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
     assert lb(h=0, ld_h=0, ld_w=0) == _lib.LOGP_ERR_SHAPE

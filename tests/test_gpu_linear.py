@@ -86,3 +86,10 @@ def test_full_size_sampled():
     ref = _oracle(h[rows], w, t[rows])
     assert_logp_parity(logp[rows], lse[rows], *ref, t[rows], what="linear full")
     assert torch.isfinite(logp).all()
+
+
+def test_int32_targets_same_bits():
+    c = synth.qwen3_linear(seed=77, n=140, h=256, v=3000, device=dev(), ignore_frac=0.05)
+    a, la = itl.linear_logp_fwd(c["hidden"], c["weight"], c["targets"])
+    b, lb = itl.linear_logp_fwd(c["hidden"], c["weight"], c["targets"].to(torch.int32))
+    assert torch.equal(bits(a), bits(b)) and torch.equal(bits(la), bits(lb))

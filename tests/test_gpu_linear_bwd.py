@@ -183,3 +183,11 @@ def test_full_size_sampled():
     ew = np.abs(_f64(dw)[vr] - dw64)
     assert (ew <= bw).all(), (np.argwhere(ew > bw)[:5], ew.max())
     assert torch.isfinite(dh).all() and torch.isfinite(dw).all()
+
+
+def test_int32_targets_same_bits():
+    h, w, t, g = _case(140, 128, 900, seed=41)
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    dh, dw = itl.linear_logp_bwd(h, w, t, lse, g)
+    dh2, dw2 = itl.linear_logp_bwd(h, w, t.to(torch.int32), lse, g)
+    assert torch.equal(bits(dh), bits(dh2)) and torch.equal(bits(dw), bits(dw2))

@@ -124,3 +124,25 @@ def test_full_size_sampled():
     assert (d[ign].view(torch.int16) == 0).all()
     rs = d[~ign][:512].float().sum(dim=1).abs() / g[~ign][:512].abs()
     assert (rs < 0.05).all()
+
+
+@pytest.mark.parametrize("v,w", [(300, 512), (V, 4096)])
+def test_fp16_backward(v, w):
+    """fp16 dlogits: each value is the nearest fp16 (subnormals included) of
+    the fp32 gradient within the error budget."""
+    n = 24
+    x = synth.normal_matrix(n, v, 3.0, torch.float16, seed=v + 3).to(dev())
+    t = synth.uniform_targets(n, v, seed=v + 4, ignore_rows=torch.tensor([1])).to(dev())
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=v + 5)[0].to(dev())
+    d = _check(x, t, g, w, f"fp16 {v}")
+    assert d.dtype == torch.float16
+
+
+def test_int32_targets_same_bits():
+    x = synth.normal_matrix(16, 3000, 2.0, torch.bfloat16, seed=31).to(dev())
+    t = synth.uniform_targets(16, 3000, seed=32, ignore_rows=torch.tensor([3])).to(dev())
+    g = torch.linspace(-2, 2, 16, device=dev())
+    _, lse = itl.logp_fwd(x, t, -100, 512)
+    a = itl.logp_bwd(x, t, lse, g, -100, 512)
+    b = itl.logp_bwd(x, t.to(torch.int32), lse, g, -100, 512)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -252,3 +252,27 @@ def test_full_size_sampled():
     a = (c["targets"] != -100)
     assert (logp[a] <= 0).all()
     assert (bits(logp[~a]) == 0).all()
+
+
+@pytest.mark.parametrize("v,w", [(300, 512), (4099, 1024), (151936, 4096)])
+def test_fp16_logits(v, w):
+    """fp16 logits ("Batch-Invariant LogP", Tensor Contract: fp32 / fp16 /
+    bf16) widen exactly; parity with the oracle on the same fp16 values."""
+    n = 33
+    x = synth.normal_matrix(n, v, 3.0, torch.float16, seed=v + 1).to(dev())
+    t = synth.uniform_targets(n, v, seed=v + 2, ignore_rows=torch.tensor([4])).to(dev())
+    logp, lse = itl.logp_fwd(x, t, -100, w)
+    assert_logp_parity(logp, lse, *_oracle(x, t), t, what=f"fp16 {v}")
+    a = (t != -100)
+    assert (logp[a] <= 0).all()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_int32_targets_same_bits(dtype):
+    """int32 targets give the same bits as int64 targets (all S)."""
+    x = synth.normal_matrix(40, 5000, 2.0, dtype, seed=12).to(dev())
+    t = synth.uniform_targets(40, 5000, seed=13, ignore_rows=torch.tensor([0, 39])).to(dev())
+    for s in (1, 2):
+        a, la = itl.logp_fwd(x, t, -100, 512, s)
+        b, lb = itl.logp_fwd(x, t.to(torch.int32), -100, 512, s)
+        assert torch.equal(bits(a), bits(b)) and torch.equal(bits(la), bits(lb))
