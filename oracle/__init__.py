@@ -2,6 +2,9 @@
 
 from .logp_oracle import (  # noqa: F401
     InvalidTargetError,
+    entropy,
+    entropy_bwd,
+    linear_entropy,
     linear_logits,
     linear_logp_bwd,
     linear_logp_bwd_weight_rows,

@@ -24,6 +24,12 @@ Sources (page title -- section):
   largest tile max, and the target logit is copied from its owner.
 * "Batch-Invariant LogP" -- Batch-Invariance: the backward writes
   g * (onehot - softmax) per row tile from the saved per-row LSE.
+* "Batch-Invariant LogP" -- VIME CP=2 runtime provider: full-vocabulary
+  entropy is returned on request, merged in the same fixed order as the LSE.
+* "[RFC][ROCm] ..." -- Workstream 3, proposed operator: temperature,
+  return_entropy and return_logits options of the fused LM head; temperature
+  is applied at one contract-defined point (here: the logits are divided by
+  it before any statistic).
 * "[RFC][ROCm] End-to-end optimization of bitwise VIME R/R beyond native P/P"
   -- Workstream 3 (fused ROCm LM-head and linear logp): the logits are the
   product of the hidden states with the LM-head weight, and the same
@@ -135,6 +141,46 @@ def logp_bwd(logits, targets, grad_logp, ignore_index=-100, lse=None):
     return d
 
 
+def entropy(logits, targets, ignore_index=-100):
+    """Full-vocabulary entropy of each row's softmax, in float64.
+
+    H = -sum_j p_j log p_j with p_j = exp(x_j - lse) ("Batch-Invariant
+    LogP", VIME CP=2 runtime provider: entropy over the whole vocabulary).
+    Ignored rows give 0 (reading: like their logp).  Returns H [N]."""
+    x2 = _as_2d(logits)
+    n, v = x2.shape
+    active, t = _active_mask(targets, ignore_index, v)
+    ent = np.zeros(n, dtype=np.float64)
+    _, lse = logp_fwd(x2, t, ignore_index)
+    for r0 in range(0, n, ROW_CHUNK):
+        r1 = min(n, r0 + ROW_CHUNK)
+        rows = np.flatnonzero(active[r0:r1]) + r0
+        if rows.size == 0:
+            continue
+        logp_all = x2[rows].astype(np.float64) - lse[rows][:, None]
+        ent[rows] = -(np.exp(logp_all) * logp_all).sum(axis=1)
+    return ent
+
+
+def entropy_bwd(logits, targets, grad_entropy, ignore_index=-100):
+    """Gradient of sum_r gH_r * H_r with respect to the logits, in float64:
+    dH/dx_j = -p_j (log p_j + H).  Ignored rows get 0.  Returns [N, V]."""
+    x2 = _as_2d(logits)
+    n, v = x2.shape
+    active, t = _active_mask(targets, ignore_index, v)
+    gh = np.asarray(grad_entropy, dtype=np.float64).reshape(-1)
+    _, lse = logp_fwd(x2, t, ignore_index)
+    ent = entropy(x2, t, ignore_index)
+    d = np.zeros((n, v), dtype=np.float64)
+    rows = np.flatnonzero(active)
+    for c0 in range(0, rows.size, ROW_CHUNK):
+        rr = rows[c0:c0 + ROW_CHUNK]
+        logp_all = x2[rr].astype(np.float64) - lse[rr][:, None]
+        p = np.exp(logp_all)
+        d[rr] = -gh[rr][:, None] * p * (logp_all + ent[rr][:, None])
+    return d
+
+
 def linear_logits(hidden, weight):
     """Logits of the LM head: z = h @ W^T in float64.
 
@@ -149,11 +195,13 @@ def linear_logits(hidden, weight):
     return h @ w.T
 
 
-def linear_logp_fwd(hidden, weight, targets, ignore_index=-100):
-    """Fused LM-head + selected log-probability: logp_fwd(h @ W^T).
+def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, temperature=1.0):
+    """Fused LM-head + selected log-probability: logp_fwd(h @ W^T / T).
 
     "[RFC][ROCm] ..." -- Workstream 3.  The fused kernel never stores z; the
-    oracle does, a row block at a time.  Returns (logp [N], lse [N])."""
+    oracle does, a row block at a time.  The temperature T divides the logits
+    before any statistic (the proposed operator's temperature option).
+    Returns (logp [N], lse [N]) of the scaled logits."""
     h = np.asarray(hidden)
     n = h.shape[0]
     t = np.asarray(targets, dtype=np.int64).reshape(-1)
@@ -161,23 +209,38 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100):
     lse = np.zeros(n, dtype=np.float64)
     for r0 in range(0, n, ROW_CHUNK):
         r1 = min(n, r0 + ROW_CHUNK)
-        z = linear_logits(h[r0:r1], weight)
+        z = linear_logits(h[r0:r1], weight) / float(temperature)
         logp[r0:r1], lse[r0:r1] = logp_fwd(z, t[r0:r1], ignore_index)
     return logp, lse
 
 
+def linear_entropy(hidden, weight, targets, ignore_index=-100, temperature=1.0):
+    """Entropy of the fused LM head's softmax over h @ W^T / T, per row."""
+    h = np.asarray(hidden)
+    n = h.shape[0]
+    t = np.asarray(targets, dtype=np.int64).reshape(-1)
+    ent = np.zeros(n, dtype=np.float64)
+    for r0 in range(0, n, ROW_CHUNK):
+        r1 = min(n, r0 + ROW_CHUNK)
+        z = linear_logits(h[r0:r1], weight) / float(temperature)
+        ent[r0:r1] = entropy(z, t[r0:r1], ignore_index)
+    return ent
+
+
 def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=None,
-                    need_dweight=True):
-    """Gradients of sum_r g_r * logp_r of the fused LM head, in float64.
+                    need_dweight=True, temperature=1.0, grad_entropy=None):
+    """Gradients of sum_r (g_r logp_r + gH_r H_r) of the fused LM head, in
+    float64.
 
     "[RFC][ROCm] ..." -- Workstream 3 (the backward recomputes the logit
     tiles from the saved LSE) and "Batch-Invariant LogP" -- Batch-Invariance
     (the logit gradient is g * (onehot - softmax), zero on ignored rows):
-        z  = h @ W^T
-        dz = g * (onehot(t) - exp(z - lse))        (rows with t == ignore: 0)
-        dh = dz @ W,    dW = dz^T @ h
-    lse is the float64 row LSE of z (recomputed when not given).  Rows are
-    processed in blocks; dW sums the blocks in ascending row order.
+        x  = h @ W^T / T,  p = exp(x - lse)
+        dx = g * (onehot(t) - p) - gH * p * (log p + H)   (rows with t == ignore: 0)
+        dz = dx / T,   dh = dz @ W,   dW = dz^T @ h
+    lse is the float64 row LSE of x (recomputed when not given); the entropy
+    term is present only when grad_entropy is given.  Rows are processed in
+    blocks; dW sums the blocks in ascending row order.
     Returns (dh [N, H], dW [V, H]) as float64 (dW is None when not needed)."""
     h = np.asarray(hidden, dtype=np.float64)
     w = np.asarray(weight, dtype=np.float64)
@@ -190,9 +253,13 @@ def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=N
     dw = np.zeros_like(w) if need_dweight else None
     for r0 in range(0, n, ROW_CHUNK):
         r1 = min(n, r0 + ROW_CHUNK)
-        z = linear_logits(h[r0:r1], w)
+        x = linear_logits(h[r0:r1], w) / float(temperature)
         row_lse = None if lse is None else np.asarray(lse, dtype=np.float64).reshape(-1)[r0:r1]
-        dz = logp_bwd(z, t[r0:r1], g[r0:r1], ignore_index, lse=row_lse)
+        dx = logp_bwd(x, t[r0:r1], g[r0:r1], ignore_index, lse=row_lse)
+        if grad_entropy is not None:
+            gh = np.asarray(grad_entropy, dtype=np.float64).reshape(-1)[r0:r1]
+            dx = dx + entropy_bwd(x, t[r0:r1], gh, ignore_index)
+        dz = dx / float(temperature)
         dh[r0:r1] = dz @ w
         if need_dweight:
             dw += dz.T @ h[r0:r1]
@@ -200,28 +267,35 @@ def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=N
 
 
 def linear_logp_bwd_weight_rows(hidden, weight, targets, grad_logp, vocab_rows,
-                                ignore_index=-100, lse=None):
-    """Rows `vocab_rows` of dW = dz^T h from linear_logp_bwd, without forming
-    the other vocabulary rows: dW[j] = sum_r g_r ([t_r == j] - exp(z[r, j] -
-    lse_r)) h[r] over active rows, z[:, j] = h W[j]^T.  lse (float64 [N]) is
-    the full-row LSE; it is recomputed from all of W when not given (the
-    expensive part).  Returns float64 [len(vocab_rows), H]."""
+                                ignore_index=-100, lse=None, temperature=1.0,
+                                grad_entropy=None, ent=None):
+    """Rows `vocab_rows` of dW from linear_logp_bwd, without forming the other
+    vocabulary rows: dW[j] = sum_r dz[r, j] h[r] over active rows, with
+    x[:, j] = h W[j]^T / T, p = exp(x - lse) and
+    dz[r, j] = (g_r ([t_r == j] - p) - gH_r p (x - lse + H_r)) / T.
+    lse and H (float64 [N]) are full-row statistics; they are recomputed from
+    all of W when not given (the expensive part).
+    Returns float64 [len(vocab_rows), H]."""
     h = np.asarray(hidden, dtype=np.float64)
     w = np.asarray(weight, dtype=np.float64)
-    n = h.shape[0]
     t = np.asarray(targets, dtype=np.int64).reshape(-1)
     g = np.asarray(grad_logp, dtype=np.float64).reshape(-1)
     active, _ = _active_mask(t, ignore_index, w.shape[0])
     if lse is None:
-        _, lse = linear_logp_fwd(h, w, t, ignore_index)
+        _, lse = linear_logp_fwd(h, w, t, ignore_index, temperature)
     lse = np.asarray(lse, dtype=np.float64).reshape(-1)
     cols = np.asarray(vocab_rows, dtype=np.int64).reshape(-1)
-    z = h @ w[cols].T                                   # [N, J]
-    p = np.exp(z - lse[:, None])
+    x = (h @ w[cols].T) / float(temperature)          # [N, J]
+    p = np.exp(x - lse[:, None])
     onehot = (t[:, None] == cols[None, :]).astype(np.float64)
-    dz = g[:, None] * (onehot - p)
-    dz[~active] = 0.0
-    return dz.T @ h
+    dx = g[:, None] * (onehot - p)
+    if grad_entropy is not None:
+        if ent is None:
+            ent = linear_entropy(h, w, t, ignore_index, temperature)
+        gh = np.asarray(grad_entropy, dtype=np.float64).reshape(-1)
+        dx = dx - gh[:, None] * p * ((x - lse[:, None]) + np.asarray(ent)[:, None])
+    dx[~active] = 0.0
+    return (dx / float(temperature)).T @ h
 
 
 # ---------------------------------------------------------------------------

@@ -463,3 +463,101 @@ def test_linear_bwd_weight_rows_matches_full():
     _, lse = oracle.linear_logp_fwd(h, w, t)
     got2 = oracle.linear_logp_bwd_weight_rows(h, w, t, g, rows, lse=lse)
     np.testing.assert_array_equal(got, got2)
+
+
+# ----- entropy and temperature -------------------------------------------------
+
+def test_entropy_closed_forms():
+    """Uniform row: H = log V.  Two-level row (k entries a, V-k entries b):
+    H = -k q_a log q_a - (V-k) q_b log q_b with q = e^x / (k e^a + (V-k) e^b),
+    written out with math.  Ignored rows: 0."""
+    v = 1000
+    x = np.zeros((2, v))
+    x[1, :7] = 3.0
+    x[1, 7:] = -1.5
+    h = oracle.entropy(x, [3, -100])
+    assert abs(h[0] - math.log(v)) <= 1e-12
+    assert h[1] == 0.0
+    h2 = oracle.entropy(x[1:], [0])[0]
+    k, a, b = 7, 3.0, -1.5
+    zsum = k * math.exp(a) + (v - k) * math.exp(b)
+    qa, qb = math.exp(a) / zsum, math.exp(b) / zsum
+    want = -k * qa * math.log(qa) - (v - k) * qb * math.log(qb)
+    assert abs(h2 - want) <= 1e-12
+
+
+def test_entropy_library_and_bounds():
+    """torch.distributions.Categorical(logits).entropy() in float64; 0 <= H
+    <= log V; shift invariance."""
+    rng = np.random.default_rng(31)
+    x = rng.normal(scale=3.0, size=(20, 500))
+    t = rng.integers(0, 500, 20)
+    h = oracle.entropy(x, t)
+    ref = torch.distributions.Categorical(logits=torch.tensor(x)).entropy().numpy()
+    np.testing.assert_allclose(h, ref, rtol=1e-12, atol=1e-12)
+    assert (h >= 0).all() and (h <= math.log(500) + 1e-12).all()
+    np.testing.assert_allclose(oracle.entropy(x + 7.25, t), h, rtol=1e-12, atol=1e-12)
+
+
+def test_entropy_bwd_finite_difference():
+    rng = np.random.default_rng(32)
+    x = rng.normal(size=(3, 6))
+    t = [1, -100, 5]
+    gh = np.array([0.4, 2.0, -1.3])
+    d = oracle.entropy_bwd(x, t, gh)
+    eps = 1e-6
+    for idx in np.ndindex(x.shape):
+        a = x.copy(); a[idx] += eps
+        b = x.copy(); b[idx] -= eps
+        num = (np.dot(gh, oracle.entropy(a, t)) - np.dot(gh, oracle.entropy(b, t))) / (2 * eps)
+        assert abs(num - d[idx]) <= 1e-8, (idx, num, d[idx])
+    assert np.all(d[1] == 0.0)
+
+
+def test_linear_temperature_and_entropy_autograd():
+    """torch float64 autograd of g * logp + gH * entropy of softmax(h W^T / T)
+    gives the oracle's dh, dW; the oracle's forward matches too."""
+    rng = np.random.default_rng(33)
+    n, hd, v, temp = 10, 12, 30, 0.7
+    h = rng.normal(size=(n, hd))
+    w = rng.normal(size=(v, hd)) * 0.5
+    t = rng.integers(0, v, n)
+    t[4] = -100
+    g = rng.normal(size=n)
+    gh = rng.normal(size=n)
+    logp, lse = oracle.linear_logp_fwd(h, w, t, temperature=temp)
+    ent = oracle.linear_entropy(h, w, t, temperature=temp)
+    dh, dw = oracle.linear_logp_bwd(h, w, t, g, temperature=temp, grad_entropy=gh)
+    th = torch.tensor(h, requires_grad=True)
+    tw = torch.tensor(w, requires_grad=True)
+    lp = torch.log_softmax((th @ tw.T) / temp, dim=-1)
+    tt = torch.tensor(t)
+    mask = tt != -100
+    sel = lp[mask].gather(1, tt[mask].unsqueeze(1)).squeeze(1)
+    ent_t = -(lp.exp() * lp).sum(-1)[mask]
+    np.testing.assert_allclose(logp[mask.numpy()], sel.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ent[mask.numpy()], ent_t.detach().numpy(), rtol=1e-12, atol=1e-12)
+    assert ent[4] == 0.0
+    ((sel * torch.tensor(g)[mask]).sum() + (ent_t * torch.tensor(gh)[mask]).sum()).backward()
+    np.testing.assert_allclose(dh, th.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dw, tw.grad.numpy(), rtol=1e-11, atol=1e-12)
+    rows = [0, 7, 29]
+    got = oracle.linear_logp_bwd_weight_rows(h, w, t, g, rows, temperature=temp,
+                                             grad_entropy=gh)
+    np.testing.assert_allclose(got, dw[rows], rtol=1e-11, atol=1e-13)
+
+
+def test_linear_temperature_limits():
+    """T -> large makes every row uniform (logp -> -log V, H -> log V); T = 1
+    is the plain fused operator."""
+    rng = np.random.default_rng(34)
+    h = rng.normal(size=(4, 8))
+    w = rng.normal(size=(50, 8))
+    t = [0, 1, 2, 49]
+    lp, _ = oracle.linear_logp_fwd(h, w, t, temperature=1e9)
+    np.testing.assert_allclose(lp, -math.log(50), atol=1e-7)
+    np.testing.assert_allclose(oracle.linear_entropy(h, w, t, temperature=1e9), math.log(50),
+                               atol=1e-7)
+    a = oracle.linear_logp_fwd(h, w, t)
+    b = oracle.linear_logp_fwd(h, w, t, temperature=1.0)
+    assert np.array_equal(a[0], b[0])
