@@ -59,7 +59,8 @@ enum logp_status {
   LOGP_ERR_SHARDS = 6,    /* num_shards < 1 or not a divisor of v */
   LOGP_ERR_WORKSPACE = 7, /* workspace NULL or smaller than required */
   LOGP_ERR_TARGET = 8,    /* validate = 1 found an active target outside [0, v) */
-  LOGP_ERR_HIP = 9        /* a HIP launch or copy failed */
+  LOGP_ERR_HIP = 9,       /* a HIP launch or copy failed */
+  LOGP_ERR_VALUE = 10     /* a scalar argument is out of range (temperature) */
 };
 
 /* Logits element types ("Batch-Invariant LogP", Tensor Contract: fp32 / fp16
@@ -79,8 +80,9 @@ enum logp_index_dtype {
 /*
  * Workspace of logp_fwd, in bytes.  It is 0 for num_shards == 1 with
  * validate == 0 (the fused single-launch path).  Otherwise it holds the
- * [T, n] tile partials (m and s, fp32), the copied target logits [n] and a
- * 256-byte status block.  Returns 0 for arguments logp_fwd would reject.
+ * [T, n] tile partials (m, s and the entropy moment w, fp32), the copied
+ * target logits [n] and a 256-byte status block.  Returns 0 for arguments
+ * logp_fwd would reject.
  */
 size_t logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width,
                                 int32_t num_shards, int32_t validate);
@@ -113,14 +115,23 @@ size_t logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width,
  *                 returns LOGP_ERR_TARGET if any such row was seen.
  *   logp_out      fp32 [n].
  *   lse_out       fp32 [n], may be NULL.  Saved for logp_bwd.
+ *   entropy_out   fp32 [n] or NULL: the full-vocabulary entropy
+ *                 H = -sum_j p_j log p_j of each row ("Batch-Invariant LogP",
+ *                 VIME CP=2 runtime provider: entropy on request, merged in
+ *                 the same fixed order).  Each tile also folds
+ *                 w = sum e^(x - m) (x - m) in its sumexp tree; the merge
+ *                 folds b = fma(fma(s_k, m_k - M, w_k), e^(m_k - M), b) next
+ *                 to the LSE chain and H = log(acc) - b / acc.  Ignored rows
+ *                 give 0.  logp and lse have the same bits with or without it.
  *   workspace     device buffer of at least logp_fwd_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0), 256-byte aligned.
  */
 int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
                  int64_t ld, const void* targets, int32_t target_dtype,
                  int64_t ignore_index, int32_t tile_width, int32_t num_shards,
-                 int32_t validate, float* logp_out, float* lse_out, void* workspace,
-                 size_t workspace_bytes, void* hip_stream);
+                 int32_t validate, float* logp_out, float* lse_out,
+                 float* entropy_out, void* workspace, size_t workspace_bytes,
+                 void* hip_stream);
 
 /*
  * Gradient of logp with respect to the logits ("Batch-Invariant LogP",
@@ -128,7 +139,9 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
  * LSE; Reference Semantics: ignored rows get a zero gradient).
  *
  *   dlogits[r, j] = RNE_dtype( g[r] * u ),  u = 1 - p if j == t_r, else -p,
- *   p = exp(x[r, j] - lse[r]) with the same exp primitive as the forward.
+ *   p = exp(x[r, j] - lse[r]) with the same exp primitive as the forward;
+ *   with the entropy term, -gH[r] p (x - lse[r] + H[r]) is added by one fma
+ *   before the rounding.
  *
  *   logits, dtype, n, v, ld, targets, target_dtype, ignore_index: as for
  *               logp_fwd.
@@ -136,6 +149,9 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
  *               way; it does not change any bit (the backward is elementwise).
  *   lse         fp32 [n] from logp_fwd.
  *   grad_logp   fp32 [n], the upstream gradient g.
+ *   entropy, grad_entropy
+ *               fp32 [n] each, both NULL (no entropy term) or both set: the
+ *               row entropy from logp_fwd and its upstream gradient gH.
  *   dlogits_out [n, ld_out] of the logits dtype; ld_out >= v; columns >= v
  *               are not written.  Ignored rows are written +0 without reading
  *               the logits.  It may be exactly the logits buffer (same
@@ -145,11 +161,12 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
 int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
                  int64_t ld, const void* targets, int32_t target_dtype,
                  int64_t ignore_index, int32_t tile_width, const float* lse,
-                 const float* grad_logp, void* dlogits_out, int64_t ld_out,
+                 const float* grad_logp, const float* entropy,
+                 const float* grad_entropy, void* dlogits_out, int64_t ld_out,
                  void* hip_stream);
 
 /*
- * Workspace of linear_logp_fwd in bytes: the [T, n] partials (m, s) for
+ * Workspace of linear_logp_fwd in bytes: the [n, T] partials (m, s, w) for
  * T = ceil(v / tile_width) and the copied target logits [n].  Returns 0 for
  * arguments linear_logp_fwd would reject.
  */
@@ -172,17 +189,27 @@ size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width)
  *               block).
  *   hidden, weight, ld_h and ld_w must give 16-byte aligned rows
  *   (LOGP_ERR_ALIGN otherwise).
- *   targets, target_dtype, ignore_index, logp_out, lse_out (may be NULL): as
- *   logp_fwd, with no validation (invalid active targets give logp = NaN).
+ *   targets, target_dtype, ignore_index, logp_out, lse_out (may be NULL),
+ *   entropy_out (may be NULL): as logp_fwd, with no validation (invalid
+ *   active targets give logp = NaN), taken over the scaled logits.
+ *   temperature finite and > 0 (LOGP_ERR_VALUE otherwise): the logits enter
+ *               every statistic as z * fl32(1 / temperature) (the proposed
+ *               operator's temperature, applied at this one point); 1 leaves
+ *               them unchanged.
+ *   logits_out  [n, ld_logits] (ld_logits >= v) of logits_dtype (LOGP_F32 or
+ *               LOGP_BF16, RNE) receiving the unscaled z, or NULL ("return
+ *               logits" for sampling).  logp, lse and entropy have the same
+ *               bits either way.
  *   workspace   at least linear_logp_fwd_workspace_bytes(...) bytes,
  *               256-byte aligned.
  */
 int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight,
                         int64_t ld_w, int64_t n, int64_t h, int64_t v,
                         const void* targets, int32_t target_dtype,
-                        int64_t ignore_index, int32_t tile_width, float* logp_out,
-                        float* lse_out, void* workspace, size_t workspace_bytes,
-                        void* hip_stream);
+                        int64_t ignore_index, int32_t tile_width, float temperature,
+                        float* logp_out, float* lse_out, float* entropy_out,
+                        void* logits_out, int32_t logits_dtype, int64_t ld_logits,
+                        void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * Workspace of linear_logp_bwd in bytes: W^T [h, Vp], h^T [h, Np], dz [Np, Vp]
@@ -199,7 +226,9 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  * Invariant LogP", Batch-Invariance and Reference Semantics: the logit
  * gradient is g * (onehot - softmax), zero on ignored rows):
  *   z  = hidden weight^T          (recomputed with the forward's MFMA walk)
- *   dz = RNE_bf16(g * (onehot(t) - exp(z - lse)))
+ *   x  = z * fl32(1 / temperature)
+ *   dz = RNE_bf16((g * (onehot(t) - p) - gH p (x - lse + H)) * fl32(1 / temperature)),
+ *        p = exp(x - lse), the entropy term only when requested
  *   dhidden = dz weight           (fp32 accumulation, K = vocabulary ascending)
  *   dweight = dz^T hidden         (fp32 accumulation, K = tokens ascending)
  * No product is split, so dhidden[r] depends only on row r and dweight is
@@ -209,8 +238,12 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *   ignore_index, tile_width:
  *               as linear_logp_fwd (h a multiple of 64, tile_width 256,
  *               16-byte aligned rows).
+ *   temperature as linear_logp_fwd (the forward's value).
  *   lse         fp32 [n] from linear_logp_fwd.
  *   grad_logp   fp32 [n], the upstream gradient g.
+ *   entropy, grad_entropy
+ *               fp32 [n] each, both NULL or both set: the forward's entropy
+ *               and its upstream gradient gH.
  *   out_dtype   LOGP_F32 (the accumulators) or LOGP_BF16 (RNE of them).
  *   dhidden     [n, ld_dh] of out_dtype, or NULL to skip that product.
  *   dweight     [v, ld_dw] of out_dtype, or NULL to skip that product (with
@@ -224,10 +257,10 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
-                        const float* lse,
-                        const float* grad_logp, int32_t out_dtype, void* dhidden,
-                        int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
-                        size_t workspace_bytes, void* hip_stream);
+                        float temperature, const float* lse, const float* grad_logp,
+                        const float* entropy, const float* grad_entropy, int32_t out_dtype,
+                        void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
+                        void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Short English text for a status code (static storage, host memory). */
 const char* logp_status_str(int32_t status);

@@ -32,6 +32,11 @@ itl::Targets targets_of(const void* p, int32_t target_dtype) {
   return itl::Targets{p, target_dtype == LOGP_I32 ? 1 : 0};
 }
 
+// Temperature of the fused LM head: finite and > 0.  The logits are
+// multiplied by its reciprocal rounded once to fp32 (1 stays exactly 1).
+bool valid_temperature(float t) { return t > 0.0f && t <= 3.4e38f; }
+float inv_temperature(float t) { return static_cast<float>(1.0 / static_cast<double>(t)); }
+
 bool aligned16(const void* p, int64_t ld, int32_t dtype) {
   return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * elt_size(dtype)) % 16 == 0);
 }
@@ -45,14 +50,15 @@ int32_t check_stream_args(int32_t dtype, int64_t n, int64_t v, int64_t ld, int32
   return LOGP_OK;
 }
 
-// Workspace layout of logp_fwd: [status block | pm (T*n) | ps (T*n) | pt (n)].
+// Workspace layout of logp_fwd and of the fused LM head's partials:
+// [status block | pm | ps | pw | pt (n)], each table T x n fp32.
 struct FwdLayout {
-  size_t pm, ps, pt, total;
+  size_t pm, ps, pw, pt, total;
 };
 
-FwdLayout fwd_layout(int64_t n, int64_t ntiles, int32_t shards, int32_t validate) {
-  FwdLayout l{0, 0, 0, 0};
-  if (shards == 1) {
+FwdLayout fwd_layout(int64_t n, int64_t ntiles, bool tables, int32_t validate) {
+  FwdLayout l{0, 0, 0, 0, 0};
+  if (!tables) {
     l.total = validate ? kAlign : 0;
     return l;
   }
@@ -60,7 +66,8 @@ FwdLayout fwd_layout(int64_t n, int64_t ntiles, int32_t shards, int32_t validate
       round_up(static_cast<size_t>(ntiles) * static_cast<size_t>(n) * sizeof(float));
   l.pm = kAlign;
   l.ps = l.pm + table;
-  l.pt = l.ps + table;
+  l.pw = l.ps + table;
+  l.pt = l.pw + table;
   l.total = l.pt + round_up(static_cast<size_t>(n) * sizeof(float));
   return l;
 }
@@ -79,20 +86,21 @@ size_t logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width, int32_
       check_stream_args(LOGP_F32, n, v, v, tile_width) != LOGP_OK)
     return 0;
   if (num_shards < 1 || v % num_shards) return 0;
-  return fwd_layout(n, (v + tile_width - 1) / tile_width, num_shards, validate).total;
+  return fwd_layout(n, (v + tile_width - 1) / tile_width, num_shards > 1, validate).total;
 }
 
 int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_t ld,
                  const void* targets, int32_t target_dtype, int64_t ignore_index,
                  int32_t tile_width, int32_t num_shards, int32_t validate, float* logp_out,
-                 float* lse_out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                 float* lse_out, float* entropy_out, void* workspace, size_t workspace_bytes,
+                 void* hip_stream) {
   int32_t st = check_stream_args(dtype, n, v, ld, tile_width);
   if (st != LOGP_OK) return st;
   if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
   const itl::Targets tg = targets_of(targets, target_dtype);
   if (num_shards < 1 || v % num_shards) return LOGP_ERR_SHARDS;
   const int ntiles = static_cast<int>((v + tile_width - 1) / tile_width);
-  const FwdLayout lay = fwd_layout(n, ntiles, num_shards, validate);
+  const FwdLayout lay = fwd_layout(n, ntiles, num_shards > 1, validate);
   if (n == 0) return LOGP_OK;
   if (!logits || !targets || !logp_out) return LOGP_ERR_NULL;
   if (lay.total) {
@@ -109,10 +117,11 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
   if (status && hipMemsetAsync(status, 0, sizeof(int), s) != hipSuccess) return LOGP_ERR_HIP;
   if (num_shards == 1) {
     itl::launch_fwd_fused(dtype, vec, chunks, logits, ld, n, v, tg, ignore_index, ntiles,
-                          logp_out, lse_out, status, s);
+                          logp_out, lse_out, entropy_out, status, s);
   } else {
     float* pm = reinterpret_cast<float*>(ws + lay.pm);
     float* ps = reinterpret_cast<float*>(ws + lay.ps);
+    float* pw = entropy_out ? reinterpret_cast<float*>(ws + lay.pw) : nullptr;
     float* pt = reinterpret_cast<float*>(ws + lay.pt);
     const int64_t per = v / num_shards;
     for (int32_t sh = 0; sh < num_shards; ++sh) {
@@ -121,10 +130,10 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
       const int ke = static_cast<int>(((sh + 1) * per + tile_width - 1) / tile_width);
       if (ke > kb)
         itl::launch_fwd_partials(dtype, vec, chunks, logits, ld, n, v, tg, ignore_index, kb,
-                                 ke, pm, ps, pt, s);
+                                 ke, pm, ps, pw, pt, s);
     }
-    itl::launch_fwd_merge(pm, ps, pt, n, ntiles, 1, n, v, tg, ignore_index, logp_out,
-                          lse_out, status, s);
+    itl::launch_fwd_merge(pm, ps, pw, pt, n, ntiles, 1, n, v, tg, ignore_index, logp_out,
+                          lse_out, entropy_out, status, s);
   }
   st = hip_status();
   if (st != LOGP_OK) return st;
@@ -140,7 +149,8 @@ int32_t logp_fwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
 
 int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_t ld,
                  const void* targets, int32_t target_dtype, int64_t ignore_index,
-                 int32_t tile_width, const float* lse, const float* grad_logp, void* dlogits_out,
+                 int32_t tile_width, const float* lse, const float* grad_logp,
+                 const float* entropy, const float* grad_entropy, void* dlogits_out,
                  int64_t ld_out, void* hip_stream) {
   int32_t st = check_stream_args(dtype, n, v, ld, tile_width);
   if (st != LOGP_OK) return st;
@@ -148,33 +158,38 @@ int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
   if (ld_out < v) return LOGP_ERR_SHAPE;
   if (n == 0) return LOGP_OK;
   if (!logits || !targets || !lse || !grad_logp || !dlogits_out) return LOGP_ERR_NULL;
+  if ((entropy == nullptr) != (grad_entropy == nullptr)) return LOGP_ERR_NULL;
   const bool vec = aligned16(logits, ld, dtype) && aligned16(dlogits_out, ld_out, dtype);
   (void)hipGetLastError();
   itl::launch_bwd(dtype, vec, logits, ld, n, v, targets_of(targets, target_dtype), ignore_index,
-                  lse, grad_logp,
-                  dlogits_out, ld_out, static_cast<hipStream_t>(hip_stream));
+                  lse, grad_logp, entropy, grad_entropy, dlogits_out, ld_out,
+                  static_cast<hipStream_t>(hip_stream));
   return hip_status();
 }
 
 size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width) {
   if (n < 0 || v < 1 || tile_width != itl::kLinearTile) return 0;
   const int64_t ntiles = (v + tile_width - 1) / tile_width;
-  return fwd_layout(n, ntiles, 2, 0).total;
+  return fwd_layout(n, ntiles, true, 0).total;
 }
 
 int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
-                        float* logp_out, float* lse_out, void* workspace,
-                        size_t workspace_bytes, void* hip_stream) {
+                        float temperature, float* logp_out, float* lse_out, float* entropy_out,
+                        void* logits_out, int32_t logits_dtype, int64_t ld_logits,
+                        void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (n < 0 || v < 1 || h < 1 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
   if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
+  if (logits_out && logits_dtype != LOGP_F32 && logits_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
+  if (logits_out && ld_logits < v) return LOGP_ERR_SHAPE;
+  if (!valid_temperature(temperature)) return LOGP_ERR_VALUE;
   const itl::Targets tg = targets_of(targets, target_dtype);
   if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
   const int64_t ntiles = (v + tile_width - 1) / tile_width;
   if (ntiles > (int64_t{1} << 24) || (n + 127) / 128 * ntiles > (int64_t{1} << 30))
     return LOGP_ERR_SHAPE;
-  const FwdLayout lay = fwd_layout(n, ntiles, 2, 0);
+  const FwdLayout lay = fwd_layout(n, ntiles, true, 0);
   if (n == 0) return LOGP_OK;
   if (!hidden || !weight || !targets || !logp_out) return LOGP_ERR_NULL;
   if (!aligned16(hidden, ld_h, LOGP_BF16) || !aligned16(weight, ld_w, LOGP_BF16))
@@ -186,13 +201,15 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
   char* ws = static_cast<char*>(workspace);
   float* pm = reinterpret_cast<float*>(ws + lay.pm);
   float* ps = reinterpret_cast<float*>(ws + lay.ps);
+  float* pw = entropy_out ? reinterpret_cast<float*>(ws + lay.pw) : nullptr;
   float* pt = reinterpret_cast<float*>(ws + lay.pt);
   (void)hipGetLastError();
   itl::launch_linear_partials(static_cast<const uint16_t*>(hidden), ld_h,
                               static_cast<const uint16_t*>(weight), ld_w, n, h, v, tg,
-                              ignore_index, pm, ps, pt, s);
-  itl::launch_fwd_merge(pm, ps, pt, n, static_cast<int>(ntiles), ntiles, 1, v, tg,
-                        ignore_index, logp_out, lse_out, nullptr, s);
+                              ignore_index, pm, ps, pt, inv_temperature(temperature), pw,
+                              logits_out, logits_dtype == LOGP_BF16 ? 1 : 0, ld_logits, s);
+  itl::launch_fwd_merge(pm, ps, pw, pt, n, static_cast<int>(ntiles), ntiles, 1, v, tg,
+                        ignore_index, logp_out, lse_out, entropy_out, nullptr, s);
   return hip_status();
 }
 
@@ -205,10 +222,10 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
-                        const float* lse,
-                        const float* grad_logp, int32_t out_dtype, void* dhidden, int64_t ld_dh,
-                        void* dweight, int64_t ld_dw, void* workspace, size_t workspace_bytes,
-                        void* hip_stream) {
+                        float temperature, const float* lse, const float* grad_logp,
+                        const float* entropy, const float* grad_entropy, int32_t out_dtype,
+                        void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
+                        void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (n < 0 || v < 1 || h < 64 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
   if (v > (int64_t{1} << 31) || n > (int64_t{1} << 31) ||
       ((n + 255) / 256) * ((v + 255) / 256) > (int64_t{1} << 30) ||
@@ -217,10 +234,12 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
   if (out_dtype != LOGP_F32 && out_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
   if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
+  if (!valid_temperature(temperature)) return LOGP_ERR_VALUE;
   if (!dhidden && !dweight) return LOGP_ERR_NULL;
   if ((dhidden && ld_dh < h) || (dweight && ld_dw < h)) return LOGP_ERR_SHAPE;
   if (n == 0 && !dweight) return LOGP_OK;
   if (!weight || (n > 0 && (!hidden || !targets || !lse || !grad_logp))) return LOGP_ERR_NULL;
+  if ((entropy == nullptr) != (grad_entropy == nullptr)) return LOGP_ERR_NULL;
   if ((n > 0 && !aligned16(hidden, ld_h, LOGP_BF16)) || !aligned16(weight, ld_w, LOGP_BF16))
     return LOGP_ERR_ALIGN;
   const size_t need = linear_logp_bwd_workspace_bytes(n, h, v, tile_width);
@@ -231,9 +250,9 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   itl::launch_linear_bwd(static_cast<const uint16_t*>(hidden), ld_h,
                          static_cast<const uint16_t*>(weight), ld_w, n, h, v,
                          targets_of(targets, target_dtype), ignore_index, lse, grad_logp,
-                         out_dtype == LOGP_BF16, dhidden, ld_dh,
-                         dweight, ld_dw, static_cast<char*>(workspace),
-                         static_cast<hipStream_t>(hip_stream));
+                         inv_temperature(temperature), entropy, grad_entropy,
+                         out_dtype == LOGP_BF16, dhidden, ld_dh, dweight, ld_dw,
+                         static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream));
   return hip_status();
 }
 
@@ -249,6 +268,7 @@ const char* logp_status_str(int32_t status) {
     case LOGP_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LOGP_ERR_TARGET: return "an active target lies outside [0, v)";
     case LOGP_ERR_HIP: return "HIP launch or copy failed";
+    case LOGP_ERR_VALUE: return "invalid scalar argument (temperature)";
     default: return "unknown status";
   }
 }
@@ -258,7 +278,11 @@ const char* logp_contract_id(void) {
          "exp=v_exp_f32((a-b)*log2e);log=v_log_f32*ln2;bwd=rne(g*(onehot-p))]"
          "+itl.linear_logp.v1[mfma=f32_16x16x32_bf16;k=asc32-nosplit;tile=256;"
          "tilestat=4x64(lane-asc-fold4+xor1..8)+(q0+q1)+(q2+q3);"
-         "bwd=dz:rne_bf16(g*(onehot-p)),dh:dz*W(k=vocab-asc32),dW:dz^T*h(k=token-asc32)]/gfx950";
+         "temp=z*fl32(1/T);"
+         "bwd=dz:rne_bf16((g*(onehot-p)+fma(-gH,p*(x-lse+H)))*fl32(1/T)),"
+         "dh:dz*W(k=vocab-asc32),dW:dz^T*h(k=token-asc32)]"
+         "+entropy[w=sum e*(x-m) same tree;merge b=fma(fma(s,m-M,w),e,b);H=log(acc)-b/acc]"
+         "/gfx950";
 }
 
 }  // extern "C"

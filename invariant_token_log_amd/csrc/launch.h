@@ -22,30 +22,35 @@ struct Targets {
 };
 
 void launch_fwd_fused(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
-                      int64_t n, int64_t v, Targets targets, int64_t ignore,
-                      int ntiles, float* logp, float* lse, int* status, hipStream_t s);
+                      int64_t n, int64_t v, Targets targets, int64_t ignore, int ntiles,
+                      float* logp, float* lse, float* ent, int* status, hipStream_t s);
 
+// pw == nullptr: no entropy moment.
 void launch_fwd_partials(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
-                         int64_t n, int64_t v, Targets targets, int64_t ignore,
-                         int k_begin, int k_end, float* pm, float* ps, float* pt,
-                         hipStream_t s);
+                         int64_t n, int64_t v, Targets targets, int64_t ignore, int k_begin,
+                         int k_end, float* pm, float* ps, float* pw, float* pt, hipStream_t s);
 
 // Partial (r, k) of the [n, T] / [T, n] tables sits at r * row_stride + k * tile_stride.
-void launch_fwd_merge(const float* pm, const float* ps, const float* pt, int64_t n,
-                      int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
-                      Targets targets, int64_t ignore, float* logp, float* lse,
+// ent == nullptr: no entropy (pw unused).
+void launch_fwd_merge(const float* pm, const float* ps, const float* pw, const float* pt,
+                      int64_t n, int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
+                      Targets targets, int64_t ignore, float* logp, float* lse, float* ent,
                       int* status, hipStream_t s);
 
+// ent == nullptr: no entropy term (gent unused).
 void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, int64_t v,
                 Targets targets, int64_t ignore, const float* lse, const float* grad,
-                void* dlogits, int64_t ld_out, hipStream_t s);
+                const float* ent, const float* gent, void* dlogits, int64_t ld_out,
+                hipStream_t s);
 
-// Fused LM-head statistics: writes the row-major [n, T] partials and the
-// target logits of every active row (T = ceil(v / 256)).
+// Fused LM-head statistics: writes the row-major [n, T] partials (and the
+// entropy moments when pw is set) and the target logits of every active row
+// (T = ceil(v / 256)).  The logits are multiplied by inv_t before any
+// statistic; z (optional) receives the unscaled logits, fp32 or bf16.
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
-                            int64_t ld_w, int64_t n, int64_t h, int64_t v,
-                            Targets targets, int64_t ignore, float* pm, float* ps,
-                            float* pt, hipStream_t s);
+                            int64_t ld_w, int64_t n, int64_t h, int64_t v, Targets targets,
+                            int64_t ignore, float* pm, float* ps, float* pt, float inv_t,
+                            float* pw, void* z, int32_t z_bf16, int64_t ld_z, hipStream_t s);
 
 constexpr int kLinearTile = 256;
 
@@ -59,9 +64,12 @@ struct LinearBwdLayout {
 LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
 
 // dh [n, h] and/or dW [v, h] (either may be null) as fp32 or bf16 (bf16_out).
+// inv_t: reciprocal temperature (1 = none); ent / gent: row entropy and its
+// upstream gradient (both null = no entropy term).
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
-                       const float* lse, const float* grad, bool bf16_out, void* dh,
-                       int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s);
+                       const float* lse, const float* grad, float inv_t, const float* ent,
+                       const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
+                       int64_t ld_dw, char* ws, hipStream_t s);
 
 }  // namespace itl

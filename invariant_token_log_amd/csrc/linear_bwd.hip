@@ -90,6 +90,8 @@ struct SmemDz {
   } u;
   float lse[kT];
   float g[kT];
+  float ent[kT];  // row entropy (entropy term only)
+  float ngh[kT];  // -gH (entropy term only)
   // -2: no gradient (row past n or ignored); -1: target outside the block;
   // else t - v0
   int code[kT];
@@ -100,7 +102,8 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse,
-    const float* __restrict__ grad, uint16_t* __restrict__ dz, int64_t ld_dz,
+    const float* __restrict__ grad, float inv_t, const float* __restrict__ ent,
+    const float* __restrict__ gent, uint16_t* __restrict__ dz, int64_t ld_dz,
     uint16_t* __restrict__ dzt, int64_t ld_dzt) {
   const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemDz sm;
@@ -117,18 +120,24 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   if (tid < kT) {
     const int64_t r = m0 + tid;
     int code = -2;
-    float L = 0.0f, G = 0.0f;
+    float L = 0.0f, G = 0.0f, H = 0.0f, NGH = 0.0f;
     if (r < n) {
       const int64_t t = targets[r];
       if (t != ignore_index) {
         L = lse[r];
         G = grad[r];
+        if (ent) {
+          H = ent[r];
+          NGH = -gent[r];
+        }
         code = (t >= v0 && t < v0 + kT && t < v) ? static_cast<int>(t - v0) : -1;
       }
     }
     sm.code[tid] = code;
     sm.lse[tid] = L;
     sm.g[tid] = G;
+    sm.ent[tid] = H;
+    sm.ngh[tid] = NGH;
   }
 
   f32x4 acc[8][4];
@@ -140,14 +149,18 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
                  static_cast<int>(hdim / gemm::kK), acc);
   __syncthreads();
 
-  // p = exp(z - lse) with the forward's primitive; d = g (1 - p) on the
-  // target column, (-g) p elsewhere; RNE to bf16.  Lane (li, g) holds rows
-  // 4g .. 4g+3 of each 16 x 16 block, so its four values of a column pack
-  // into 8 contiguous bytes of the transposed tile.
+  // x = z (* 1/T); p = exp(x - lse) with the forward's primitive; d = g (1 - p)
+  // on the target column, (-g) p elsewhere, plus -gH p (x - lse + H) with the
+  // entropy term (one fma, the -inf clamp of ent_term); d (* 1/T) for dz; RNE
+  // to bf16.  Lane (li, g) holds rows 4g .. 4g+3 of each 16 x 16 block, so its
+  // four values of a column pack into 8 contiguous bytes of the transposed
+  // tile.
+  const bool scaled = inv_t != 1.0f;
+  const bool with_ent = ent != nullptr;
   uint32_t dv[8][4][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float L[4], G[4];
+    float L[4], G[4], H[4], NGH[4];
     int code[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -155,6 +168,8 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
       code[q] = sm.code[lr];
       L[q] = sm.lse[lr];
       G[q] = sm.g[lr];
+      H[q] = sm.ent[lr];
+      NGH[q] = sm.ngh[lr];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -164,8 +179,12 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
       for (int q = 0; q < 4; ++q) {
         float d = 0.0f;
         if (code[q] != -2 && v0 + lc < v) {
-          const float p = exp_sub(acc[i][j][q], L[q]);
+          const float x = scaled ? acc[i][j][q] * inv_t : acc[i][j][q];
+          const float dl = x - L[q];  // exp_sub(x, L) in two steps
+          const float p = __builtin_amdgcn_exp2f(dl * kLog2e);
           d = lc == code[q] ? G[q] * (1.0f - p) : (-G[q]) * p;
+          if (with_ent) d = fmaf(NGH[q], p * fmaxf(dl + H[q], -FLT_MAX), d);
+          if (scaled) d = d * inv_t;
         }
         b[q] = bf16_bits(d);
       }
@@ -307,8 +326,9 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
 
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
-                       const float* lse, const float* grad, bool bf16_out, void* dh,
-                       int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s) {
+                       const float* lse, const float* grad, float inv_t, const float* ent,
+                       const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
+                       int64_t ld_dw, char* ws, hipStream_t s) {
   if (n == 0) {
     // dh has no rows; dW is a sum over no tokens.
     if (dw) {
@@ -329,8 +349,7 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
   hipLaunchKernelGGL(linear_dz_kernel, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0, s,
                      hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                       targets.is32, ignore, lse,
-                     grad, dz, l.vp, dzt, l.np);
+                       targets.is32, ignore, lse, grad, inv_t, ent, gent, dz, l.vp, dzt, l.np);
   if (dh) {
     hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
                        dim3(256), 0, s, weight, ld_w, v, l.vp, wt, l.vp);

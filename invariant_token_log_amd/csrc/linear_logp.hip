@@ -50,6 +50,7 @@ template <int BM>
 struct Reduce {
   float red[BM][4];  // per-row quarter maxima
   float sum[BM][4];  // per-row quarter sums
+  float wsum[BM][4]; // per-row quarter entropy moments (when requested)
   float tmax[BM];    // per-row tile maximum
   float tval[BM];    // target logit, when the target column is in this block
   int code[BM];      // row_code() of each row
@@ -79,11 +80,12 @@ __device__ __forceinline__ void block_sync_lds() {
 // where its NJ column groups form NJ / 4 whole quarters starting at quarter
 // col0 / 64.  NT = threads of the workgroup.  rd.code must be filled, and
 // accumulators of columns >= v must already hold -inf.
-template <int MI, int NJ, int BM, int NT>
+template <int MI, int NJ, int BM, int NT, bool ENT>
 __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], Reduce<BM>& rd,
                                                     int row0, int col0, int li, int g, int tid,
                                                     int64_t m0, int64_t v0, int vb, int vblocks,
-                                                    int64_t v, float* pm, float* ps, float* pt) {
+                                                    int64_t v, float* pm, float* ps, float* pw,
+                                                    float* pt) {
   constexpr int NQ = NJ / 4;  // quarters held by this wave
   const int q0 = col0 / 64;
   auto z = [&](int i, int j, int q) { return acc[i][j][q]; };
@@ -116,10 +118,12 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
   }
   block_sync_lds();
 
-  // Pass 2: quarter sums against the tile maximum; the one lane holding the
+  // Pass 2: quarter sums against the tile maximum (and, with ENT, the
+  // entropy moments sum e (z - m), same tree); the one lane holding the
   // target column of a row parks z[r, t] in LDS.  The empty asm keeps the
   // LDS reads of row group i from being hoisted above group i - 1, which
   // would hold every row's operands in registers at once.
+  float wpart[ENT ? MI : 1][4][NQ];
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     asm volatile("" ::: "memory");
@@ -129,10 +133,23 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
       const float m = rd.tmax[lr];
 #pragma unroll
       for (int h = 0; h < NQ; ++h) {
-        float s = exp_sub(z(i, 4 * h, q), m);
+        if constexpr (ENT) {
+          float s = 0.0f, w = 0.0f;
 #pragma unroll
-        for (int j = 4 * h + 1; j < 4 * h + 4; ++j) s = s + exp_sub(z(i, j, q), m);
-        part[i][q][h] = row16_sum_first(s);
+          for (int j = 4 * h; j < 4 * h + 4; ++j) {
+            const float d = z(i, j, q) - m;  // exp_sub(z, m) in two steps
+            const float e = __builtin_amdgcn_exp2f(d * kLog2e);
+            s = j == 4 * h ? e : s + e;
+            w = ent_term(e, d, w);
+          }
+          part[i][q][h] = row16_sum_first(s);
+          wpart[i][q][h] = row16_sum_first(w);
+        } else {
+          float s = exp_sub(z(i, 4 * h, q), m);
+#pragma unroll
+          for (int j = 4 * h + 1; j < 4 * h + 4; ++j) s = s + exp_sub(z(i, j, q), m);
+          part[i][q][h] = row16_sum_first(s);
+        }
       }
       const int off = rd.code[lr] - col0;
       if (off >= 0 && off < NJ * 16 && (off & 15) == li) {
@@ -150,7 +167,10 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int h = 0; h < NQ; ++h) rd.sum[row0 + i * 16 + 4 * g + q][q0 + h] = part[i][q][h];
+        for (int h = 0; h < NQ; ++h) {
+          rd.sum[row0 + i * 16 + 4 * g + q][q0 + h] = part[i][q][h];
+          if constexpr (ENT) rd.wsum[row0 + i * 16 + 4 * g + q][q0 + h] = wpart[i][q][h];
+        }
   }
   block_sync_lds();
 
@@ -161,16 +181,60 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
       const float4 s4 = *reinterpret_cast<const float4*>(rd.sum[lr]);
       pm[r * vblocks + vb] = rd.tmax[lr];
       ps[r * vblocks + vb] = (s4.x + s4.y) + (s4.z + s4.w);
+      if constexpr (ENT) {
+        const float4 w4 = *reinterpret_cast<const float4*>(rd.wsum[lr]);
+        pw[r * vblocks + vb] = (w4.x + w4.y) + (w4.z + w4.w);
+      }
       if (code >= 0) pt[r] = rd.tval[lr];
     }
   }
 }
 
+// Optional outputs of the forward statistic kernels: the temperature's
+// reciprocal (logits are multiplied by it before any statistic), the entropy
+// moment table and the unscaled logits.
+struct LinearExtras {
+  float inv_t;      // 1 = no temperature
+  float* pw;        // [n, T] entropy moments, or null
+  void* z;          // [n, ld_z] unscaled logits (fp32 or bf16), or null
+  int32_t z_bf16;
+  int64_t ld_z;
+};
+
 template <int MI, int NJ, int BM, int NT>
 __device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>& rd, int row0,
                                                int col0, int li, int g, int tid, int64_t m0,
-                                               int64_t v0, int vb, int vblocks, int64_t v,
-                                               float* pm, float* ps, float* pt) {
+                                               int64_t v0, int vb, int vblocks, int64_t n,
+                                               int64_t v, float* pm, float* ps, float* pt,
+                                               const LinearExtras& ex) {
+  // The unscaled logits, when asked for: they are the accumulators as they
+  // are (the statistics below do not change them).
+  if (ex.z) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t r = m0 + row0 + i * 16 + 4 * g + q;
+        if (r >= n) continue;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int64_t c = v0 + col0 + j * 16 + li;
+          if (c >= v) continue;
+          if (ex.z_bf16)
+            static_cast<uint16_t*>(ex.z)[r * ex.ld_z + c] =
+                __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][q]));
+          else
+            static_cast<float*>(ex.z)[r * ex.ld_z + c] = acc[i][j][q];
+        }
+      }
+  }
+  // Temperature: x = z * (1 / T) on every accumulator before any statistic.
+  if (ex.inv_t != 1.0f) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = acc[i][j] * ex.inv_t;
+  }
   // Columns >= v exist only in the last vocabulary block.  Their -inf takes
   // no part in a maximum and adds an exact 0 to a sum; no target lies there.
   if (v0 + BN > v) {
@@ -180,8 +244,12 @@ __device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>&
 #pragma unroll
         for (int i = 0; i < MI; ++i) acc[i][j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
-  stats_epilogue_body<MI, NJ, BM, NT>(acc, rd, row0, col0, li, g, tid, m0, v0, vb, vblocks, v, pm,
-                                      ps, pt);
+  if (ex.pw)
+    stats_epilogue_body<MI, NJ, BM, NT, true>(acc, rd, row0, col0, li, g, tid, m0, v0, vb,
+                                              vblocks, v, pm, ps, ex.pw, pt);
+  else
+    stats_epilogue_body<MI, NJ, BM, NT, false>(acc, rd, row0, col0, li, g, tid, m0, v0, vb,
+                                               vblocks, v, pm, ps, ex.pw, pt);
 }
 
 // ---------------------------------------------------------------------------
@@ -199,7 +267,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
-    float* __restrict__ ps, float* __restrict__ pt) {
+    float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
   const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemDma sm;
   const int tid = threadIdx.x;
@@ -223,7 +291,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
                  acc);
   __syncthreads();
   stats_epilogue<8, 4, 256, kDmaThreads>(acc, sm.rd, wm * 128, wn * 64, li, g, tid, m0, v0, vb,
-                                         vblocks, v, pm, ps, pt);
+                                         vblocks, n, v, pm, ps, pt, ex);
 }
 
 // ---------------------------------------------------------------------------
@@ -243,7 +311,7 @@ __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
-    float* __restrict__ ps, float* __restrict__ pt) {
+    float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
   const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemReg sm;
   const int tid = threadIdx.x;
@@ -319,28 +387,27 @@ __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
 #undef ITL_ST
 #undef ITL_STASH
   stats_epilogue<4, 8, 128, kRegThreads>(acc, sm.rd, wm * 64, wn * 128, li, g, tid, m0, v0, vb,
-                                         vblocks, v, pm, ps, pt);
+                                         vblocks, n, v, pm, ps, pt, ex);
 }
 
 }  // namespace
 
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
-                            int64_t ld_w, int64_t n, int64_t h, int64_t v,
-                            Targets targets, int64_t ignore, float* pm, float* ps,
-                            float* pt, hipStream_t s) {
+                            int64_t ld_w, int64_t n, int64_t h, int64_t v, Targets targets,
+                            int64_t ignore, float* pm, float* ps, float* pt, float inv_t,
+                            float* pw, void* z, int32_t z_bf16, int64_t ld_z, hipStream_t s) {
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
+  const LinearExtras ex{inv_t, pw, z, z_bf16, ld_z};
   if (n <= 128) {
     const int mblocks = static_cast<int>((n + 127) / 128);
     hipLaunchKernelGGL(linear_stats_regstage, dim3(mblocks * vblocks), dim3(kRegThreads), 0, s,
                        hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                       targets.is32, ignore,
-                       pm, ps, pt);
+                       targets.is32, ignore, pm, ps, pt, ex);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     hipLaunchKernelGGL(linear_stats_dma, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,
                        hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                       targets.is32, ignore,
-                       pm, ps, pt);
+                       targets.is32, ignore, pm, ps, pt, ex);
   }
 }
 

@@ -11,6 +11,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 
 namespace itl {
@@ -156,9 +157,22 @@ __device__ __forceinline__ void load_chunk(const T* row, int64_t c, int64_t v,
 }
 
 // ---------------------------------------------------------------------------
+// Entropy moment.  Next to s = sum e_j, e_j = e^(x_j - m), a tile can carry
+//   w = sum e_j * (x_j - m)
+// folded in the same tree as s (one fma per term).  A term whose x_j is -inf
+// (a padding column or a masked logit) has e_j = 0 and must add nothing: its
+// difference is clamped to -FLT_MAX, so the product is an exact -0 instead of
+// 0 * (-inf) = NaN.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ent_term(float e, float d, float w) {
+  return fmaf(e, fmaxf(d, -FLT_MAX), w);
+}
+
+// ---------------------------------------------------------------------------
 // Tile statistic ("Batch-Invariant LogP", Tensor Parallel, step 2): one wave
 // reduces the W = C * 64 * E columns [col0, col0 + W) of one row to
-//   m = max x,   s = sum exp(x - m)   (fp32, two passes over registers).
+//   m = max x,   s = sum exp(x - m)   (fp32, two passes over registers),
+// and, with ENT, the entropy moment w of the same terms.
 // Layout: lane l holds chunks j = 0..C-1 covering the tile-local elements
 // [(j * 64 + l) * E, +E), so every chunk load is one coalesced 1 KiB wave
 // access.  Summation tree: each lane folds its C * E terms in ascending
@@ -167,9 +181,9 @@ __device__ __forceinline__ void load_chunk(const T* row, int64_t c, int64_t v,
 // column index inside the tile, on W and on the dtype.  Padding columns
 // (>= v) contribute exp(-inf) = +0, which leaves every partial sum unchanged.
 // ---------------------------------------------------------------------------
-template <typename T, int C, bool VEC>
+template <typename T, int C, bool VEC, bool ENT = false>
 __device__ __forceinline__ void tile_stats(const T* row, int64_t col0, int64_t v,
-                                           float& m_out, float& s_out) {
+                                           float& m_out, float& s_out, float* w_out = nullptr) {
   constexpr int E = Elt<T>::kPerChunk;
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int W = C * kWave * E;
@@ -190,53 +204,80 @@ __device__ __forceinline__ void tile_stats(const T* row, int64_t col0, int64_t v
 #pragma unroll
     for (int e = 0; e < E; ++e) m = fmaxf(m, x[j][e]);
   m = wave_max(m);
-  float s = 0.0f;
+  float s = 0.0f, w = 0.0f;
 #pragma unroll
   for (int j = 0; j < C; ++j)
 #pragma unroll
-    for (int e = 0; e < E; ++e) s = s + exp_sub(x[j][e], m);
+    for (int e = 0; e < E; ++e) {
+      if constexpr (ENT) {
+        const float d = x[j][e] - m;  // exp_sub(x, m) evaluated in two steps
+        const float ex = __builtin_amdgcn_exp2f(d * kLog2e);
+        s = s + ex;
+        w = ent_term(ex, d, w);
+      } else {
+        s = s + exp_sub(x[j][e], m);
+      }
+    }
   m_out = m;
   s_out = wave_sum(s);
+  if constexpr (ENT) *w_out = wave_sum(w);
 }
 
 // ---------------------------------------------------------------------------
 // Fixed-order merge ("Batch-Invariant LogP", Tensor Parallel, step 4):
 //   M = max_k m_k;  acc = +0;  for k = 0 .. T-1:  acc = fma(s_k, e^(m_k - M), acc)
 //   (tiles with m_k = -inf skipped: they hold no column);  LSE = M + log(acc).
+// With ENT the same loop also folds b = fma(y_k, e^(m_k - M), b), y_k =
+// fma(s_k, m_k - M, w_k) = sum over the tile of e^(x - M) (x - M) scaled back
+// by e^(M - m_k), and the full-vocabulary entropy is
+//   H = log(acc) - b / acc          (= LSE - sum_j p_j x_j).
 // One wave evaluates one row: the max and the T exponentials are spread over
 // the lanes (the max is exact in any order; each exponential is the same
-// function of the same two values), then the ascending fma chain runs over
+// function of the same two values), then the ascending fma chains run over
 // them in tile order, 64 tiles at a time, with every operand read back
 // exactly from the lane that computed it.  Partial k of the row is read at
-// m[k * stride], s[k * stride].  All 64 lanes must call; all return the LSE.
+// m[k * stride], s[k * stride] (w[k * stride]).  All 64 lanes must call; all
+// return the LSE (and H).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float lane_value(float x, int j) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
 }
 
-template <typename P>
-__device__ __forceinline__ float merge_lse(P m, P s, int ntiles, int64_t stride) {
+template <bool ENT, typename P>
+__device__ __forceinline__ float merge_lse_t(P m, P s, P w, int ntiles, int64_t stride,
+                                             float* ent) {
   const int lane = threadIdx.x & (kWave - 1);
   float mx = -INFINITY;
   for (int k = lane; k < ntiles; k += kWave) mx = fmaxf(mx, m[k * stride]);
   const float big_m = wave_max(mx);
-  float acc = 0.0f;
+  float acc = 0.0f, b = 0.0f;
   for (int c = 0; c < ntiles; c += kWave) {
     const int k = c + lane;
-    float mk = -INFINITY, sk = 0.0f;
+    float mk = -INFINITY, sk = 0.0f, yk = 0.0f;
     if (k < ntiles) {
       mk = m[k * stride];
       sk = s[k * stride];
+      if constexpr (ENT) yk = fmaf(sk, mk - big_m, w[k * stride]);
     }
     // e_k >= 0 always (or NaN); -1 marks a tile without columns.
     const float ek = mk != -INFINITY ? exp_sub(mk, big_m) : -1.0f;
     const int cnt = ntiles - c < kWave ? ntiles - c : kWave;
     for (int j = 0; j < cnt; ++j) {
       const float e = lane_value(ek, j);
-      if (e != -1.0f) acc = fmaf(lane_value(sk, j), e, acc);
+      if (e != -1.0f) {
+        acc = fmaf(lane_value(sk, j), e, acc);
+        if constexpr (ENT) b = fmaf(lane_value(yk, j), e, b);
+      }
     }
   }
-  return big_m + log_nat(acc);
+  const float la = log_nat(acc);
+  if constexpr (ENT) *ent = la - b / acc;
+  return big_m + la;
+}
+
+template <typename P>
+__device__ __forceinline__ float merge_lse(P m, P s, int ntiles, int64_t stride) {
+  return merge_lse_t<false>(m, s, s, ntiles, stride, nullptr);
 }
 
 // Final combine (step 6): logp = target_logit - LSE, or NaN for an active row

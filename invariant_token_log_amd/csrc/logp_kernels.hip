@@ -17,20 +17,22 @@ constexpr int64_t kMaxGridY = 65535;        // backward grid rows (grid-stride b
 // ---------------------------------------------------------------------------
 // Single-launch forward ("Batch-Invariant LogP", Tensor Parallel with one
 // shard).  One workgroup per row (grid-stride over rows); wave w of 8 reduces
-// the tiles k = w, w + 8, ... and parks (m_k, s_k) in LDS; wave 0 merges them
-// in ascending order, copies the target logit and writes logp and lse.
-// Ignored rows are not read.  Which wave reduces a tile changes no bit: the
-// tile statistic depends only on the tile.
+// the tiles k = w, w + 8, ... and parks (m_k, s_k[, w_k]) in LDS; wave 0
+// merges them in ascending order, copies the target logit and writes logp,
+// lse (and the entropy with ENT).  Ignored rows are not read.  Which wave
+// reduces a tile changes no bit: the tile statistic depends only on the tile.
 // ---------------------------------------------------------------------------
-template <typename T, int C, bool VEC>
+template <typename T, int C, bool VEC, bool ENT>
 __global__ __launch_bounds__(kFwdBlock) void logp_fwd_fused_kernel(
     const T* __restrict__ logits, int64_t ld, int64_t n, int64_t v,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, int ntiles,
-    float* __restrict__ logp, float* __restrict__ lse, int* __restrict__ status) {
+    float* __restrict__ logp, float* __restrict__ lse, float* __restrict__ ent,
+    int* __restrict__ status) {
   const Targets targets{tgt, tgt32};
   extern __shared__ float lds[];
   float* lm = lds;
   float* ls = lds + ntiles;
+  float* lw = lds + 2 * ntiles;  // ENT only
   constexpr int W = C * kWave * Elt<T>::kPerChunk;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -40,26 +42,30 @@ __global__ __launch_bounds__(kFwdBlock) void logp_fwd_fused_kernel(
       if (threadIdx.x == 0) {
         logp[r] = 0.0f;
         if (lse) lse[r] = 0.0f;
+        if (ENT) ent[r] = 0.0f;
       }
       continue;
     }
     const T* row = logits + r * ld;
     for (int k = wave; k < ntiles; k += kFwdWaves) {
-      float mk, sk;
-      tile_stats<T, C, VEC>(row, static_cast<int64_t>(k) * W, v, mk, sk);
+      float mk, sk, wk;
+      tile_stats<T, C, VEC, ENT>(row, static_cast<int64_t>(k) * W, v, mk, sk, &wk);
       if (lane == 0) {
         lm[k] = mk;
         ls[k] = sk;
+        if (ENT) lw[k] = wk;
       }
     }
     __syncthreads();
     if (wave == 0) {
-      const float L = merge_lse(lm, ls, ntiles, 1);
+      float h = 0.0f;
+      const float L = merge_lse_t<ENT>(lm, ls, lw, ntiles, 1, &h);
       if (lane == 0) {
         const bool valid = t >= 0 && t < v;
         const float xt = valid ? Elt<T>::load(row, t) : 0.0f;
         logp[r] = combine(xt, L, valid);
         if (lse) lse[r] = L;
+        if (ENT) ent[r] = h;
         if (!valid && status) status[0] = 1;
       }
     }
@@ -69,15 +75,15 @@ __global__ __launch_bounds__(kFwdBlock) void logp_fwd_fused_kernel(
 
 // ---------------------------------------------------------------------------
 // Shard partials: the same tile statistic over the tiles [k_begin, k_end) a
-// shard owns, written to the tile-major [T, n] tables pm / ps.  The owner of
-// the target's tile copies the target logit into pt[r].  Ignored rows are
-// skipped (the merge never reads them).
+// shard owns, written to the tile-major [T, n] tables pm / ps (/ pw with ENT).
+// The owner of the target's tile copies the target logit into pt[r].  Ignored
+// rows are skipped (the merge never reads them).
 // ---------------------------------------------------------------------------
-template <typename T, int C, bool VEC>
+template <typename T, int C, bool VEC, bool ENT>
 __global__ __launch_bounds__(kFwdBlock) void logp_partials_kernel(
     const T* __restrict__ logits, int64_t ld, int64_t n, int64_t v,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, int k_begin,
-    int k_end, float* __restrict__ pm, float* __restrict__ ps,
+    int k_end, float* __restrict__ pm, float* __restrict__ ps, float* __restrict__ pw,
     float* __restrict__ pt) {
   const Targets targets{tgt, tgt32};
   constexpr int W = C * kWave * Elt<T>::kPerChunk;
@@ -88,11 +94,12 @@ __global__ __launch_bounds__(kFwdBlock) void logp_partials_kernel(
     if (t == ignore_index) continue;
     const T* row = logits + r * ld;
     for (int k = k_begin + wave; k < k_end; k += kFwdWaves) {
-      float mk, sk;
-      tile_stats<T, C, VEC>(row, static_cast<int64_t>(k) * W, v, mk, sk);
+      float mk, sk, wk;
+      tile_stats<T, C, VEC, ENT>(row, static_cast<int64_t>(k) * W, v, mk, sk, &wk);
       if (lane == 0) {
         pm[static_cast<int64_t>(k) * n + r] = mk;
         ps[static_cast<int64_t>(k) * n + r] = sk;
+        if (ENT) pw[static_cast<int64_t>(k) * n + r] = wk;
       }
     }
     if (threadIdx.x == 0 && t >= 0 && t < v &&
@@ -102,16 +109,18 @@ __global__ __launch_bounds__(kFwdBlock) void logp_partials_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Merge of gathered partials: one wave per row, the same merge_lse and
-// combine as the single-launch forward.  Partial (r, k) sits at
+// Merge of gathered partials: one wave per row, the same merge and combine as
+// the single-launch forward.  Partial (r, k) sits at
 // p[r * row_stride + k * tile_stride] (tile-major [T, n] tables from the
 // shard launches, row-major [n, T] tables from the fused LM head).
 // ---------------------------------------------------------------------------
+template <bool ENT>
 __global__ __launch_bounds__(kBlock) void logp_merge_kernel(
-    const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ pt,
-    int64_t n, int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
-    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ logp,
-    float* __restrict__ lse, int* __restrict__ status) {
+    const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ pw,
+    const float* __restrict__ pt, int64_t n, int ntiles, int64_t row_stride,
+    int64_t tile_stride, int64_t v, const void* __restrict__ tgt, int32_t tgt32,
+    int64_t ignore_index, float* __restrict__ logp, float* __restrict__ lse,
+    float* __restrict__ ent, int* __restrict__ status) {
   const Targets targets{tgt, tgt32};
   const int lane = threadIdx.x % kWave;
   const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
@@ -122,14 +131,18 @@ __global__ __launch_bounds__(kBlock) void logp_merge_kernel(
       if (lane == 0) {
         logp[r] = 0.0f;
         if (lse) lse[r] = 0.0f;
+        if (ENT) ent[r] = 0.0f;
       }
       continue;
     }
-    const float L = merge_lse(pm + r * row_stride, ps + r * row_stride, ntiles, tile_stride);
+    float h = 0.0f;
+    const float L = merge_lse_t<ENT>(pm + r * row_stride, ps + r * row_stride,
+                                     pw + r * row_stride, ntiles, tile_stride, &h);
     if (lane == 0) {
       const bool valid = t >= 0 && t < v;
       logp[r] = combine(valid ? pt[r] : 0.0f, L, valid);
       if (lse) lse[r] = L;
+      if (ENT) ent[r] = h;
       if (!valid && status) status[0] = 1;
     }
   }
@@ -170,24 +183,42 @@ template <> __device__ __forceinline__ void store_elem<_Float16>(_Float16* p, in
   p[i] = static_cast<_Float16>(d);
 }
 
-__device__ __forceinline__ float grad_elem(float x, float L, float g, float ng, bool is_target) {
-  const float p = exp_sub(x, L);
-  return is_target ? g * (1.0f - p) : ng * p;
+// Per-row constants of the gradient: lse, g, -g and, with the entropy term,
+// the row entropy H and -gH.
+struct GradRow {
+  float L, g, ng, H, ngh;
+};
+
+// d = g (1 - p) on the target column, (-g) p elsewhere, p = e^(x - lse); with
+// ENT the entropy gradient -gH p (log p + H) is added by one fma, log p taken
+// as x - lse (the subtraction of exp_sub, kept).  A -inf logit has p = 0 and
+// its entropy term is clamped to an exact -0.
+template <bool ENT>
+__device__ __forceinline__ float grad_val(float x, const GradRow& q, bool is_target) {
+  if constexpr (ENT) {
+    const float dl = x - q.L;  // exp_sub(x, L) in two steps
+    const float p = __builtin_amdgcn_exp2f(dl * kLog2e);
+    const float d = is_target ? q.g * (1.0f - p) : q.ng * p;
+    return fmaf(q.ngh, p * fmaxf(dl + q.H, -FLT_MAX), d);
+  } else {
+    const float p = exp_sub(x, q.L);
+    return is_target ? q.g * (1.0f - p) : q.ng * p;
+  }
 }
 
-template <typename T>
-__device__ __forceinline__ uint4 grad_chunk(const uint4 q, float L, float g, float ng,
-                                            int64_t c, int64_t t) {
+template <typename T, bool ENT>
+__device__ __forceinline__ uint4 grad_chunk(const uint4 q, const GradRow& gr, int64_t c,
+                                            int64_t t) {
   constexpr int E = Elt<T>::kPerChunk;
   float x[E];
   widen_chunk<T>(q, x);
   float d[E];
   if (t >= c && t < c + E) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) d[e] = grad_elem(x[e], L, g, ng, c + e == t);
+    for (int e = 0; e < E; ++e) d[e] = grad_val<ENT>(x[e], gr, c + e == t);
   } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) d[e] = ng * exp_sub(x[e], L);
+    for (int e = 0; e < E; ++e) d[e] = grad_val<ENT>(x[e], gr, false);
   }
   uint4 o;
   if constexpr (E == 4) {
@@ -203,11 +234,12 @@ __device__ __forceinline__ uint4 grad_chunk(const uint4 q, float L, float g, flo
   return o;
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool ENT>
 __global__ __launch_bounds__(kBlock) void logp_bwd_kernel(
     const T* logits, int64_t ld, int64_t n, int64_t v,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
-    const float* __restrict__ lse, const float* __restrict__ grad, T* dlogits,
+    const float* __restrict__ lse, const float* __restrict__ grad,
+    const float* __restrict__ ent, const float* __restrict__ gent, T* dlogits,
     int64_t ld_out) {
   const Targets targets{tgt, tgt32};
   constexpr int E = Elt<T>::kPerChunk;
@@ -230,15 +262,18 @@ __global__ __launch_bounds__(kBlock) void logp_bwd_kernel(
       continue;
     }
     const T* row = logits + r * ld;
-    const float L = lse[r];
-    const float g = grad[r];
-    const float ng = -g;
+    GradRow gr;
+    gr.L = lse[r];
+    gr.g = grad[r];
+    gr.ng = -gr.g;
+    gr.H = ENT ? ent[r] : 0.0f;
+    gr.ngh = ENT ? -gent[r] : 0.0f;
     if (full) {
-      store_stream(orow + j0, grad_chunk<T>(load_stream(row + j0), L, g, ng, j0, t));
+      store_stream(orow + j0, grad_chunk<T, ENT>(load_stream(row + j0), gr, j0, t));
     } else {
       for (int e = 0; e < E; ++e)
         if (j0 + e < v)
-          store_elem<T>(orow, j0 + e, grad_elem(Elt<T>::load(row, j0 + e), L, g, ng, j0 + e == t));
+          store_elem<T>(orow, j0 + e, grad_val<ENT>(Elt<T>::load(row, j0 + e), gr, j0 + e == t));
     }
   }
 }
@@ -250,107 +285,110 @@ static unsigned row_grid(int64_t n) {
   return static_cast<unsigned>(n < kMaxRowBlocks ? n : kMaxRowBlocks);
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool ENT>
 static void fused_dispatch(int chunks, const void* logits, int64_t ld, int64_t n, int64_t v,
                            Targets tg, int64_t ignore, int ntiles, float* logp, float* lse,
-                           int* status, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(ntiles) * 2 * sizeof(float);
+                           float* ent, int* status, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(ntiles) * (ENT ? 3 : 2) * sizeof(float);
   const T* x = static_cast<const T*>(logits);
 #define ITL_FUSED(CC)                                                                        \
   case CC:                                                                                   \
-    hipLaunchKernelGGL((logp_fwd_fused_kernel<T, CC, VEC>), dim3(row_grid(n)),               \
+    hipLaunchKernelGGL((logp_fwd_fused_kernel<T, CC, VEC, ENT>), dim3(row_grid(n)),          \
                        dim3(kFwdBlock), lds, s, x, ld, n, v, tg.p, tg.is32, ignore, ntiles, \
-                       logp, lse, status);                                                   \
+                       logp, lse, ent, status);                                              \
     break;
   switch (chunks) { ITL_FUSED(1) ITL_FUSED(2) ITL_FUSED(4) ITL_FUSED(8) ITL_FUSED(16) }
 #undef ITL_FUSED
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool ENT>
 static void partials_dispatch(int chunks, const void* logits, int64_t ld, int64_t n,
                               int64_t v, Targets tg, int64_t ignore, int kb, int ke, float* pm,
-                              float* ps, float* pt, hipStream_t s) {
+                              float* ps, float* pw, float* pt, hipStream_t s) {
   const T* x = static_cast<const T*>(logits);
 #define ITL_PART(CC)                                                                           \
   case CC:                                                                                     \
-    hipLaunchKernelGGL((logp_partials_kernel<T, CC, VEC>), dim3(row_grid(n)),                  \
+    hipLaunchKernelGGL((logp_partials_kernel<T, CC, VEC, ENT>), dim3(row_grid(n)),             \
                        dim3(kFwdBlock), 0, s, x, ld, n, v, tg.p, tg.is32, ignore, kb, ke, pm, \
-                       ps, pt);                                                                \
+                       ps, pw, pt);                                                            \
     break;
   switch (chunks) { ITL_PART(1) ITL_PART(2) ITL_PART(4) ITL_PART(8) ITL_PART(16) }
 #undef ITL_PART
 }
 
+// Instantiate a dispatcher for the dtype, the load path and the entropy flag.
+#define ITL_TYPED(FN, DTYPE, VECF, ENTF, ...)                                        \
+  do {                                                                               \
+    if ((DTYPE) == kF32) {                                                           \
+      if (VECF) { if (ENTF) FN<float, true, true>(__VA_ARGS__);                      \
+                  else FN<float, true, false>(__VA_ARGS__); }                        \
+      else { if (ENTF) FN<float, false, true>(__VA_ARGS__);                          \
+             else FN<float, false, false>(__VA_ARGS__); }                            \
+    } else if ((DTYPE) == kF16) {                                                    \
+      if (VECF) { if (ENTF) FN<_Float16, true, true>(__VA_ARGS__);                   \
+                  else FN<_Float16, true, false>(__VA_ARGS__); }                     \
+      else { if (ENTF) FN<_Float16, false, true>(__VA_ARGS__);                       \
+             else FN<_Float16, false, false>(__VA_ARGS__); }                         \
+    } else {                                                                         \
+      if (VECF) { if (ENTF) FN<uint16_t, true, true>(__VA_ARGS__);                   \
+                  else FN<uint16_t, true, false>(__VA_ARGS__); }                     \
+      else { if (ENTF) FN<uint16_t, false, true>(__VA_ARGS__);                       \
+             else FN<uint16_t, false, false>(__VA_ARGS__); }                         \
+    }                                                                                \
+  } while (0)
+
 void launch_fwd_fused(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
                       int64_t n, int64_t v, Targets tg, int64_t ignore, int ntiles,
-                      float* logp, float* lse, int* status, hipStream_t s) {
-#define ITL_F(TT, VV) \
-  fused_dispatch<TT, VV>(chunks, logits, ld, n, v, tg, ignore, ntiles, logp, lse, status, s)
-  if (dtype == kF32) {
-    if (vec) ITL_F(float, true); else ITL_F(float, false);
-  } else if (dtype == kF16) {
-    if (vec) ITL_F(_Float16, true); else ITL_F(_Float16, false);
-  } else {
-    if (vec) ITL_F(uint16_t, true); else ITL_F(uint16_t, false);
-  }
-#undef ITL_F
+                      float* logp, float* lse, float* ent, int* status, hipStream_t s) {
+  ITL_TYPED(fused_dispatch, dtype, vec, ent != nullptr, chunks, logits, ld, n, v, tg, ignore,
+            ntiles, logp, lse, ent, status, s);
 }
 
 void launch_fwd_partials(int dtype, bool vec, int chunks, const void* logits, int64_t ld,
                          int64_t n, int64_t v, Targets tg, int64_t ignore, int k_begin,
-                         int k_end, float* pm, float* ps, float* pt, hipStream_t s) {
-#define ITL_P(TT, VV) \
-  partials_dispatch<TT, VV>(chunks, logits, ld, n, v, tg, ignore, k_begin, k_end, pm, ps, pt, s)
-  if (dtype == kF32) {
-    if (vec) ITL_P(float, true); else ITL_P(float, false);
-  } else if (dtype == kF16) {
-    if (vec) ITL_P(_Float16, true); else ITL_P(_Float16, false);
-  } else {
-    if (vec) ITL_P(uint16_t, true); else ITL_P(uint16_t, false);
-  }
-#undef ITL_P
+                         int k_end, float* pm, float* ps, float* pw, float* pt, hipStream_t s) {
+  ITL_TYPED(partials_dispatch, dtype, vec, pw != nullptr, chunks, logits, ld, n, v, tg, ignore,
+            k_begin, k_end, pm, ps, pw, pt, s);
 }
 
-void launch_fwd_merge(const float* pm, const float* ps, const float* pt, int64_t n,
-                      int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
-                      Targets tg, int64_t ignore, float* logp, float* lse, int* status,
-                      hipStream_t s) {
+void launch_fwd_merge(const float* pm, const float* ps, const float* pw, const float* pt,
+                      int64_t n, int ntiles, int64_t row_stride, int64_t tile_stride, int64_t v,
+                      Targets tg, int64_t ignore, float* logp, float* lse, float* ent,
+                      int* status, hipStream_t s) {
   int64_t blocks = (n + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > kMaxRowBlocks) blocks = kMaxRowBlocks;
-  hipLaunchKernelGGL(logp_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                     s, pm, ps, pt, n, ntiles, row_stride, tile_stride, v, tg.p, tg.is32, ignore,
-                     logp, lse, status);
+  if (ent)
+    hipLaunchKernelGGL(logp_merge_kernel<true>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kBlock), 0, s, pm, ps, pw, pt, n, ntiles, row_stride, tile_stride,
+                       v, tg.p, tg.is32, ignore, logp, lse, ent, status);
+  else
+    hipLaunchKernelGGL(logp_merge_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kBlock), 0, s, pm, ps, ps, pt, n, ntiles, row_stride, tile_stride,
+                       v, tg.p, tg.is32, ignore, logp, lse, ent, status);
 }
 
-template <typename T>
-static void bwd_dispatch(bool vec, dim3 grid, const void* logits, int64_t ld, int64_t n,
-                         int64_t v, Targets tg, int64_t ignore, const float* lse,
-                         const float* grad, void* dlogits, int64_t ld_out, hipStream_t s) {
-  const T* x = static_cast<const T*>(logits);
-  T* d = static_cast<T*>(dlogits);
-  if (vec)
-    hipLaunchKernelGGL((logp_bwd_kernel<T, true>), grid, dim3(kBlock), 0, s, x, ld, n, v, tg.p,
-                       tg.is32, ignore, lse, grad, d, ld_out);
-  else
-    hipLaunchKernelGGL((logp_bwd_kernel<T, false>), grid, dim3(kBlock), 0, s, x, ld, n, v, tg.p,
-                       tg.is32, ignore, lse, grad, d, ld_out);
+template <typename T, bool VEC, bool ENT>
+static void bwd_dispatch(dim3 grid, const void* logits, int64_t ld, int64_t n, int64_t v,
+                         Targets tg, int64_t ignore, const float* lse, const float* grad,
+                         const float* ent, const float* gent, void* dlogits, int64_t ld_out,
+                         hipStream_t s) {
+  hipLaunchKernelGGL((logp_bwd_kernel<T, VEC, ENT>), grid, dim3(kBlock), 0, s,
+                     static_cast<const T*>(logits), ld, n, v, tg.p, tg.is32, ignore, lse, grad,
+                     ent, gent, static_cast<T*>(dlogits), ld_out);
 }
 
 void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, int64_t v,
-                Targets tg, int64_t ignore, const float* lse, const float* grad, void* dlogits,
-                int64_t ld_out, hipStream_t s) {
+                Targets tg, int64_t ignore, const float* lse, const float* grad,
+                const float* ent, const float* gent, void* dlogits, int64_t ld_out,
+                hipStream_t s) {
   const int64_t per = dtype == kF32 ? 4 : 8;  // elements per 16-byte chunk
   const int64_t chunks = (v + per - 1) / per;
   const dim3 grid(static_cast<unsigned>((chunks + kBlock - 1) / kBlock),
                   static_cast<unsigned>(n < kMaxGridY ? n : kMaxGridY));
-  if (dtype == kF32)
-    bwd_dispatch<float>(vec, grid, logits, ld, n, v, tg, ignore, lse, grad, dlogits, ld_out, s);
-  else if (dtype == kF16)
-    bwd_dispatch<_Float16>(vec, grid, logits, ld, n, v, tg, ignore, lse, grad, dlogits, ld_out,
-                           s);
-  else
-    bwd_dispatch<uint16_t>(vec, grid, logits, ld, n, v, tg, ignore, lse, grad, dlogits, ld_out,
-                           s);
+  ITL_TYPED(bwd_dispatch, dtype, vec, ent != nullptr, grid, logits, ld, n, v, tg, ignore, lse,
+            grad, ent, gent, dlogits, ld_out, s);
 }
+
+#undef ITL_TYPED
 
 }  // namespace itl

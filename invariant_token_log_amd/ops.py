@@ -54,10 +54,25 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _row_vector(x, n, name):
+    if x is None:
+        return None
+    x1 = x.reshape(-1)
+    if x1.dtype != torch.float32 or x1.numel() != n or not x1.is_contiguous():
+        raise ValueError(f"{name} must be contiguous float32 with one entry per row")
+    return x1
+
+
 def logp_fwd(logits, targets, ignore_index=-100, tile_width=4096, num_shards=1,
-             validate=False, logp_out=None, lse_out=None, workspace=None):
+             validate=False, logp_out=None, lse_out=None, workspace=None,
+             return_entropy=False, entropy_out=None):
     """Selected-token log-probability.  Returns (logp shaped like targets,
-    lse [N]) as float32."""
+    lse [N]) as float32, and the row entropy [N] as a third element when
+    return_entropy is set."""
     x2, v, ld = _rows(logits)
     n = x2.shape[0]
     t1 = _targets(targets, n)
@@ -66,31 +81,38 @@ def logp_fwd(logits, targets, ignore_index=-100, tile_width=4096, num_shards=1,
         logp_out = torch.empty(n, dtype=torch.float32, device=dev)
     if lse_out is None:
         lse_out = torch.empty(n, dtype=torch.float32, device=dev)
+    if return_entropy and entropy_out is None:
+        entropy_out = torch.empty(n, dtype=torch.float32, device=dev)
+    ent = entropy_out if return_entropy else None
     L = _lib.lib()
     need = L.logp_fwd_workspace_bytes(n, v, tile_width, num_shards, int(bool(validate)))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = L.logp_fwd(x2.data_ptr(), _dtype_code(logits), n, v, ld, t1.data_ptr(),
                     _INDEX[t1.dtype], int(ignore_index), int(tile_width), int(num_shards),
-                    int(bool(validate)), logp_out.data_ptr(), lse_out.data_ptr(), ws_ptr, ws_len,
-                    _stream(dev))
+                    int(bool(validate)), logp_out.data_ptr(), lse_out.data_ptr(), _ptr(ent),
+                    _ptr(workspace), ws_len, _stream(dev))
     check("logp_fwd", st)
+    if return_entropy:
+        return logp_out.view(targets.shape), lse_out, ent
     return logp_out.view(targets.shape), lse_out
 
 
 def logp_bwd(logits, targets, lse, grad_logp, ignore_index=-100, tile_width=4096,
-             dlogits_out=None):
-    """dlogits = g * (onehot - softmax) in the logits dtype, shaped like logits."""
+             dlogits_out=None, entropy=None, grad_entropy=None):
+    """dlogits = g * (onehot - softmax) (- gH * p * (log p + H) when the row
+    entropy and its upstream gradient are given) in the logits dtype, shaped
+    like logits."""
     x2, v, ld = _rows(logits)
     n = x2.shape[0]
     t1 = _targets(targets, n)
-    g = grad_logp.reshape(-1)
-    if g.dtype != torch.float32 or lse.dtype != torch.float32:
-        raise TypeError("lse and grad_logp must be float32")
-    if g.numel() != n or lse.numel() != n or not g.is_contiguous() or not lse.is_contiguous():
-        raise ValueError("lse and grad_logp must be contiguous with one entry per row")
+    g = _row_vector(grad_logp, n, "grad_logp")
+    lse = _row_vector(lse, n, "lse")
+    ent = _row_vector(entropy, n, "entropy")
+    gent = _row_vector(grad_entropy, n, "grad_entropy")
+    if (ent is None) != (gent is None):
+        raise ValueError("entropy and grad_entropy go together")
     if dlogits_out is None:
         dlogits_out = torch.empty_like(logits)
     d2, v2, ld_out = _rows(dlogits_out)
@@ -98,8 +120,8 @@ def logp_bwd(logits, targets, lse, grad_logp, ignore_index=-100, tile_width=4096
         raise ValueError("dlogits_out must match the logits shape and dtype")
     st = _lib.lib().logp_bwd(x2.data_ptr(), _dtype_code(logits), n, v, ld, t1.data_ptr(),
                              _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                             lse.data_ptr(),
-                             g.data_ptr(), d2.data_ptr(), ld_out, _stream(logits.device))
+                             lse.data_ptr(), g.data_ptr(), _ptr(ent), _ptr(gent),
+                             d2.data_ptr(), ld_out, _stream(logits.device))
     check("logp_bwd", st)
     return dlogits_out
 
@@ -107,10 +129,7 @@ def logp_bwd(logits, targets, lse, grad_logp, ignore_index=-100, tile_width=4096
 LINEAR_TILE = 256
 
 
-def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEAR_TILE,
-                    logp_out=None, lse_out=None, workspace=None):
-    """Fused LM-head + selected-token log-probability without storing logits.
-    hidden bf16 [N, H], weight bf16 [V, H].  Returns (logp [N], lse [N])."""
+def _linear_operands(hidden, weight):
     if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
         raise TypeError("hidden and weight must be bfloat16")
     if hidden.dim() != 2 or weight.dim() != 2 or hidden.stride(1) != 1 or weight.stride(1) != 1:
@@ -119,49 +138,74 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
     v, h2 = weight.shape
     if h2 != h:
         raise ValueError("hidden and weight must share H")
+    ld_h = hidden.stride(0) if n > 1 else h
+    ld_w = weight.stride(0) if v > 1 else h
+    return n, h, v, ld_h, ld_w
+
+
+def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEAR_TILE,
+                    logp_out=None, lse_out=None, workspace=None, temperature=1.0,
+                    return_entropy=False, entropy_out=None, return_logits=False,
+                    logits_dtype=torch.bfloat16, logits_out=None):
+    """Fused LM-head + selected-token log-probability without storing logits.
+    hidden bf16 [N, H], weight bf16 [V, H].  Returns (logp [N], lse [N]), then
+    the entropy [N] with return_entropy and the unscaled logits [N, V] with
+    return_logits.  The statistics see the logits times 1 / temperature."""
+    n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     t1 = _targets(targets, n)
     dev = hidden.device
     if logp_out is None:
         logp_out = torch.empty(n, dtype=torch.float32, device=dev)
     if lse_out is None:
         lse_out = torch.empty(n, dtype=torch.float32, device=dev)
+    if return_entropy and entropy_out is None:
+        entropy_out = torch.empty(n, dtype=torch.float32, device=dev)
+    ent = entropy_out if return_entropy else None
+    if logits_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("logits_dtype must be float32 or bfloat16")
+    if return_logits and logits_out is None:
+        logits_out = torch.empty(n, v, dtype=logits_dtype, device=dev)
+    z = logits_out if return_logits else None
+    if z is not None and (z.dtype != logits_dtype or z.dim() != 2 or tuple(z.shape) != (n, v)
+                          or z.stride(1) != 1):
+        raise ValueError("logits_out must be [N, V] of logits_dtype with contiguous rows")
     L = _lib.lib()
     need = L.linear_logp_fwd_workspace_bytes(n, v, tile_width)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    ld_h = hidden.stride(0) if n > 1 else h
-    ld_w = weight.stride(0) if v > 1 else h
     st = L.linear_logp_fwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
                            t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                           logp_out.data_ptr(), lse_out.data_ptr(), workspace.data_ptr(),
-                           workspace.numel(), _stream(dev))
+                           float(temperature), logp_out.data_ptr(), lse_out.data_ptr(),
+                           _ptr(ent), _ptr(z), _DTYPES[logits_dtype],
+                           (z.stride(0) if n > 1 else v) if z is not None else 0,
+                           workspace.data_ptr(), workspace.numel(), _stream(dev))
     check("linear_logp_fwd", st)
-    return logp_out, lse_out
+    out = (logp_out, lse_out)
+    if return_entropy:
+        out += (ent,)
+    if return_logits:
+        out += (z,)
+    return out
 
 
 def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                     tile_width=LINEAR_TILE, need_dhidden=True, need_dweight=True,
                     out_dtype=torch.float32, dhidden_out=None, dweight_out=None,
-                    workspace=None):
+                    workspace=None, temperature=1.0, entropy=None, grad_entropy=None):
     """Backward of the fused LM head + logp: (dhidden [N, H] or None,
     dweight [V, H] or None) in out_dtype (float32 accumulators or their
-    bfloat16 rounding), from the forward's lse and the upstream gradient."""
-    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
-        raise TypeError("hidden and weight must be bfloat16")
-    if hidden.dim() != 2 or weight.dim() != 2 or hidden.stride(1) != 1 or weight.stride(1) != 1:
-        raise ValueError("hidden [N, H] and weight [V, H] need a contiguous last dimension")
+    bfloat16 rounding), from the forward's lse (and entropy) and the upstream
+    gradients."""
+    n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
-    n, h = hidden.shape
-    v, h2 = weight.shape
-    if h2 != h:
-        raise ValueError("hidden and weight must share H")
     t1 = _targets(targets, n)
-    g = grad_logp.reshape(-1)
-    if g.dtype != torch.float32 or lse.dtype != torch.float32:
-        raise TypeError("lse and grad_logp must be float32")
-    if g.numel() != n or lse.numel() != n or not g.is_contiguous() or not lse.is_contiguous():
-        raise ValueError("lse and grad_logp must be contiguous with one entry per row")
+    g = _row_vector(grad_logp, n, "grad_logp")
+    lse = _row_vector(lse, n, "lse")
+    ent = _row_vector(entropy, n, "entropy")
+    gent = _row_vector(grad_entropy, n, "grad_entropy")
+    if (ent is None) != (gent is None):
+        raise ValueError("entropy and grad_entropy go together")
     dev = hidden.device
     if need_dhidden and dhidden_out is None:
         dhidden_out = torch.empty(n, h, dtype=out_dtype, device=dev)
@@ -177,69 +221,91 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     need = L.linear_logp_bwd_workspace_bytes(n, h, v, tile_width)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() if workspace is not None else 0
-    ld_h = hidden.stride(0) if n > 1 else h
-    ld_w = weight.stride(0) if v > 1 else h
     st = L.linear_logp_bwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
-                           t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index),
-                           int(tile_width), lse.data_ptr(),
-                           g.data_ptr(), _DTYPES[out_dtype],
-                           dh.data_ptr() if dh is not None else None,
+                           t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
+                           float(temperature), lse.data_ptr(), g.data_ptr(), _ptr(ent),
+                           _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
                            (dh.stride(0) if n > 1 else h) if dh is not None else 0,
-                           dw.data_ptr() if dw is not None else None,
-                           (dw.stride(0) if v > 1 else h) if dw is not None else 0,
-                           ws_ptr, ws_len, _stream(dev))
+                           _ptr(dw), (dw.stride(0) if v > 1 else h) if dw is not None else 0,
+                           _ptr(workspace), ws_len, _stream(dev))
     check("linear_logp_bwd", st)
     return dh, dw
 
 
-class _LinearLogp(torch.autograd.Function):
-    @staticmethod
-    def forward(ctx, hidden, weight, targets, ignore_index):
-        logp, lse = linear_logp_fwd(hidden, weight, targets, ignore_index)
-        ctx.save_for_backward(hidden, weight, targets, lse)
-        ctx.ignore_index = ignore_index
-        return logp
-
-    @staticmethod
-    def backward(ctx, grad):
-        hidden, weight, targets, lse = ctx.saved_tensors
-        g = grad.to(torch.float32).contiguous()
-        dh, dw = linear_logp_bwd(hidden, weight, targets, lse, g, ctx.ignore_index,
-                                 need_dhidden=ctx.needs_input_grad[0],
-                                 need_dweight=ctx.needs_input_grad[1],
-                                 out_dtype=torch.bfloat16)
-        return dh, dw, None, None
-
-
-def linear_logp(hidden, weight, target_ids, ignore_index=-100):
-    """Differentiable fused LM head + selected-token log-probability:
-    hidden bf16 [N, H], weight bf16 [V, H] -> float32 logp [N]; backward fills
-    the bf16 gradients of hidden and weight through linear_logp_bwd."""
-    return _LinearLogp.apply(hidden, weight, target_ids, ignore_index)
+def _grad_or_zeros(g, ref):
+    return torch.zeros_like(ref) if g is None else g.to(torch.float32).contiguous()
 
 
 class _BatchInvariantLogp(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, logits, targets, ignore_index, tile_width, validate):
-        logp, lse = logp_fwd(logits, targets, ignore_index, tile_width, 1, validate)
-        ctx.save_for_backward(logits, targets, lse)
+    def forward(ctx, logits, targets, ignore_index, tile_width, validate, with_entropy):
+        out = logp_fwd(logits, targets, ignore_index, tile_width, 1, validate,
+                       return_entropy=with_entropy)
+        logp, lse = out[0], out[1]
+        ent = out[2] if with_entropy else None
+        ctx.save_for_backward(logits, targets, lse, ent)
         ctx.ignore_index = ignore_index
         ctx.tile_width = tile_width
+        ctx.with_entropy = with_entropy
+        if with_entropy:
+            return logp, ent.view(targets.shape)
         return logp
 
     @staticmethod
-    def backward(ctx, grad):
-        logits, targets, lse = ctx.saved_tensors
-        g = grad.to(torch.float32).contiguous()
-        d = logp_bwd(logits, targets, lse, g, ctx.ignore_index, ctx.tile_width)
-        return d, None, None, None, None
+    def backward(ctx, grad, *rest):
+        logits, targets, lse, ent = ctx.saved_tensors
+        g = _grad_or_zeros(grad, lse).reshape(-1)
+        gent = _grad_or_zeros(rest[0], lse).reshape(-1) if ctx.with_entropy else None
+        d = logp_bwd(logits, targets, lse, g, ctx.ignore_index, ctx.tile_width,
+                     entropy=ent if ctx.with_entropy else None, grad_entropy=gent)
+        return d, None, None, None, None, None
 
 
 def batch_invariant_logp(logits, target_ids, ignore_index=-100, tile_width=4096,
-                         validate=False):
+                         validate=False, return_entropy=False):
     """Differentiable selected-token log-probability ("Batch-Invariant LogP",
-    Entry Point): logits [*lead, V] -> float32 [*lead]; backward fills the
-    logits gradient through logp_bwd."""
-    return _BatchInvariantLogp.apply(logits, target_ids, ignore_index, tile_width, validate)
+    Entry Point): logits [*lead, V] -> float32 [*lead]; with return_entropy,
+    also the differentiable full-vocabulary entropy [*lead].  The backward
+    fills the logits gradient through logp_bwd."""
+    return _BatchInvariantLogp.apply(logits, target_ids, ignore_index, tile_width, validate,
+                                     return_entropy)
+
+
+class _LinearLogp(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, hidden, weight, targets, ignore_index, temperature, with_entropy):
+        out = linear_logp_fwd(hidden, weight, targets, ignore_index, temperature=temperature,
+                              return_entropy=with_entropy)
+        logp, lse = out[0], out[1]
+        ent = out[2] if with_entropy else None
+        ctx.save_for_backward(hidden, weight, targets, lse, ent)
+        ctx.ignore_index = ignore_index
+        ctx.temperature = temperature
+        ctx.with_entropy = with_entropy
+        if with_entropy:
+            return logp, ent
+        return logp
+
+    @staticmethod
+    def backward(ctx, grad, *rest):
+        hidden, weight, targets, lse, ent = ctx.saved_tensors
+        g = _grad_or_zeros(grad, lse)
+        gent = _grad_or_zeros(rest[0], lse) if ctx.with_entropy else None
+        dh, dw = linear_logp_bwd(hidden, weight, targets, lse, g, ctx.ignore_index,
+                                 need_dhidden=ctx.needs_input_grad[0],
+                                 need_dweight=ctx.needs_input_grad[1],
+                                 out_dtype=torch.bfloat16, temperature=ctx.temperature,
+                                 entropy=ent if ctx.with_entropy else None, grad_entropy=gent)
+        return dh, dw, None, None, None, None
+
+
+def linear_logp(hidden, weight, target_ids, ignore_index=-100, temperature=1.0,
+                return_entropy=False):
+    """Differentiable fused LM head + selected-token log-probability:
+    hidden bf16 [N, H], weight bf16 [V, H] -> float32 logp [N] (and the
+    entropy [N] with return_entropy) of softmax(hidden weight^T / temperature);
+    backward fills the bf16 gradients of hidden and weight through
+    linear_logp_bwd."""
+    return _LinearLogp.apply(hidden, weight, target_ids, ignore_index, temperature,
+                             return_entropy)

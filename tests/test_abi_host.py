@@ -53,9 +53,9 @@ FAKE = 0x10000  # a non-NULL address that the checks never dereference
 
 
 def _fwd(L, logits=FAKE, dtype=1, n=4, v=151936, ld=None, targets=FAKE, tdt=0, w=4096,
-         shards=1, validate=0, logp=FAKE, lse=FAKE, ws=None, ws_bytes=0):
+         shards=1, validate=0, logp=FAKE, lse=FAKE, ent=None, ws=None, ws_bytes=0):
     return L.logp_fwd(logits, dtype, n, v, v if ld is None else ld, targets, tdt, -100, w,
-                      shards, validate, logp, lse, ws, ws_bytes, None)
+                      shards, validate, logp, lse, ent, ws, ws_bytes, None)
 
 
 def test_fwd_argument_errors(L):
@@ -89,8 +89,8 @@ def test_fwd_workspace_sizes(L):
     assert L.logp_fwd_workspace_bytes(n, v, 4096, 1, 1) == 256
     table = -(-(38 * n * 4) // 256) * 256
     rows = -(-(n * 4) // 256) * 256
-    for s in (2, 4):
-        assert L.logp_fwd_workspace_bytes(n, v, 4096, s, 0) == 256 + 2 * table + rows
+    for s in (2, 4):  # m, s and the entropy moment w, then the target logits
+        assert L.logp_fwd_workspace_bytes(n, v, 4096, s, 0) == 256 + 3 * table + rows
     assert L.logp_fwd_workspace_bytes(n, v, 1000, 1, 0) == 0  # rejected tile
     assert L.logp_fwd_workspace_bytes(n, v, 4096, 3, 0) == 0  # rejected shards
 
@@ -98,10 +98,13 @@ def test_fwd_workspace_sizes(L):
 def test_bwd_argument_errors(L):
     def bwd(**kw):
         a = dict(logits=FAKE, dtype=1, n=4, v=151936, ld=151936, targets=FAKE, tdt=0, w=4096,
-                 lse=FAKE, g=FAKE, d=FAKE, ld_out=151936)
+                 lse=FAKE, g=FAKE, ent=None, gent=None, d=FAKE, ld_out=151936)
         a.update(kw)
         return L.logp_bwd(a["logits"], a["dtype"], a["n"], a["v"], a["ld"], a["targets"],
-                          a["tdt"], -100, a["w"], a["lse"], a["g"], a["d"], a["ld_out"], None)
+                          a["tdt"], -100, a["w"], a["lse"], a["g"], a["ent"], a["gent"],
+                          a["d"], a["ld_out"], None)
+    assert bwd(ent=FAKE) == _lib.LOGP_ERR_NULL  # entropy without its gradient
+    assert bwd(gent=FAKE) == _lib.LOGP_ERR_NULL
     assert bwd(dtype=5) == _lib.LOGP_ERR_DTYPE
     assert bwd(tdt=-1) == _lib.LOGP_ERR_DTYPE
     assert bwd(ld_out=10) == _lib.LOGP_ERR_SHAPE
@@ -114,11 +117,17 @@ def test_bwd_argument_errors(L):
 def test_linear_argument_errors(L):
     def lin(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
-                 targets=FAKE, tdt=0, tile=256, logp=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40)
+                 targets=FAKE, tdt=0, tile=256, temp=1.0, logp=FAKE, lse=FAKE, ent=None,
+                 z=None, zdt=1, ldz=0, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_fwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
-                                 a["v"], a["targets"], a["tdt"], -100, a["tile"], a["logp"],
-                                 a["lse"], a["ws"], a["ws_bytes"], None)
+                                 a["v"], a["targets"], a["tdt"], -100, a["tile"], a["temp"],
+                                 a["logp"], a["lse"], a["ent"], a["z"], a["zdt"], a["ldz"],
+                                 a["ws"], a["ws_bytes"], None)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert lin(temp=bad) == _lib.LOGP_ERR_VALUE, bad
+    assert lin(z=FAKE, zdt=2, ldz=151936) == _lib.LOGP_ERR_DTYPE
+    assert lin(z=FAKE, zdt=0, ldz=100) == _lib.LOGP_ERR_SHAPE
     assert lin(tdt=9) == _lib.LOGP_ERR_DTYPE
     assert lin(tile=4096) == _lib.LOGP_ERR_TILE
     assert lin(h=100, ld_h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
@@ -129,20 +138,23 @@ def test_linear_argument_errors(L):
     assert lin(ws_bytes=16) == _lib.LOGP_ERR_WORKSPACE
     assert lin(n=0, h_ptr=None, w_ptr=None) == _lib.LOGP_OK
     need = L.linear_logp_fwd_workspace_bytes(8, 151936, 256)
-    assert need == 256 + 2 * 256 * (-(-(594 * 8 * 4) // 256)) + 256
+    assert need == 256 + 3 * 256 * (-(-(594 * 8 * 4) // 256)) + 256
     assert L.linear_logp_fwd_workspace_bytes(8, 151936, 512) == 0
 
 
 def test_linear_bwd_argument_errors(L):
     def lb(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
-                 targets=FAKE, tdt=0, tile=256, lse=FAKE, g=FAKE, out=0, dh=FAKE, ld_dh=4096,
-                 dw=FAKE, ld_dw=4096, ws=FAKE, ws_bytes=1 << 40)
+                 targets=FAKE, tdt=0, tile=256, temp=1.0, lse=FAKE, g=FAKE, ent=None,
+                 gent=None, out=0, dh=FAKE, ld_dh=4096, dw=FAKE, ld_dw=4096, ws=FAKE,
+                 ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_bwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
-                                 a["v"], a["targets"], a["tdt"], -100, a["tile"], a["lse"],
-                                 a["g"], a["out"], a["dh"], a["ld_dh"], a["dw"], a["ld_dw"],
-                                 a["ws"], a["ws_bytes"], None)
+                                 a["v"], a["targets"], a["tdt"], -100, a["tile"], a["temp"],
+                                 a["lse"], a["g"], a["ent"], a["gent"], a["out"], a["dh"],
+                                 a["ld_dh"], a["dw"], a["ld_dw"], a["ws"], a["ws_bytes"], None)
+    assert lb(temp=0.0) == _lib.LOGP_ERR_VALUE
+    assert lb(ent=FAKE) == _lib.LOGP_ERR_NULL
     assert lb(tdt=5) == _lib.LOGP_ERR_DTYPE
     assert lb(out=2) == _lib.LOGP_ERR_DTYPE
     assert lb(tile=512) == _lib.LOGP_ERR_TILE
