@@ -12,6 +12,7 @@ from .logp_oracle import (  # noqa: F401
     logp_bwd,
     logp_fwd,
     merge_partials,
+    round_bf16,
     num_tiles,
     shard_tile_ranges,
     tile_partials,

@@ -35,6 +35,11 @@ Sources (page title -- section):
   product of the hidden states with the LM-head weight, and the same
   statistics are taken over them without storing them; the backward may
   recompute the fixed logit tiles from the saved LSE.
+* "[RFC][ROCm] ..." -- Contract-versioned arithmetic change (the FP32/BF16
+  rounding points belong to the contract) and Workstream 1, item 4 (a fused
+  epilogue rounds to BF16 explicitly before the next step sees the value):
+  the bf16-rounded-logits variant rounds z to bf16 (round to nearest, ties to
+  even) before any statistic, as an unfused bf16 LM head would store it.
 
 Parity pins live in tests/test_oracle_pins.py; every function below is pinned
 there by closed forms, brute force, a library routine or an invariant.
@@ -195,12 +200,40 @@ def linear_logits(hidden, weight):
     return h @ w.T
 
 
-def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, temperature=1.0):
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even, and
+    return them as float64.
+
+    bfloat16 keeps 8 significant bits and the float32 exponent range: inside
+    a binade [2^(e-1), 2^e) its values are the multiples of 2^(e-8); below
+    the smallest normal 2^-126 the spacing stays 2^-133; magnitudes from
+    (2 - 2^-8) * 2^127 up round to infinity.  Written from that definition
+    (frexp gives the binade, rint rounds half to even); NaN and infinities
+    pass through."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    e = np.maximum(e, -125)
+    r = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def _lm_logits(h, w, temperature, round_logits):
+    """x = z / T with z = h @ W^T, rounded to bf16 first in the variant."""
+    z = linear_logits(h, w)
+    if round_logits:
+        z = round_bf16(z)
+    return z / float(temperature)
+
+
+def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, temperature=1.0,
+                    round_logits=False):
     """Fused LM-head + selected log-probability: logp_fwd(h @ W^T / T).
 
     "[RFC][ROCm] ..." -- Workstream 3.  The fused kernel never stores z; the
     oracle does, a row block at a time.  The temperature T divides the logits
-    before any statistic (the proposed operator's temperature option).
+    before any statistic (the proposed operator's temperature option); with
+    round_logits, z is rounded to bf16 before that (the variant contract).
     Returns (logp [N], lse [N]) of the scaled logits."""
     h = np.asarray(hidden)
     n = h.shape[0]
@@ -209,12 +242,13 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, temperature=1.0)
     lse = np.zeros(n, dtype=np.float64)
     for r0 in range(0, n, ROW_CHUNK):
         r1 = min(n, r0 + ROW_CHUNK)
-        z = linear_logits(h[r0:r1], weight) / float(temperature)
+        z = _lm_logits(h[r0:r1], weight, temperature, round_logits)
         logp[r0:r1], lse[r0:r1] = logp_fwd(z, t[r0:r1], ignore_index)
     return logp, lse
 
 
-def linear_entropy(hidden, weight, targets, ignore_index=-100, temperature=1.0):
+def linear_entropy(hidden, weight, targets, ignore_index=-100, temperature=1.0,
+                   round_logits=False):
     """Entropy of the fused LM head's softmax over h @ W^T / T, per row."""
     h = np.asarray(hidden)
     n = h.shape[0]
@@ -222,13 +256,13 @@ def linear_entropy(hidden, weight, targets, ignore_index=-100, temperature=1.0):
     ent = np.zeros(n, dtype=np.float64)
     for r0 in range(0, n, ROW_CHUNK):
         r1 = min(n, r0 + ROW_CHUNK)
-        z = linear_logits(h[r0:r1], weight) / float(temperature)
+        z = _lm_logits(h[r0:r1], weight, temperature, round_logits)
         ent[r0:r1] = entropy(z, t[r0:r1], ignore_index)
     return ent
 
 
 def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=None,
-                    need_dweight=True, temperature=1.0, grad_entropy=None):
+                    need_dweight=True, temperature=1.0, grad_entropy=None, round_logits=False):
     """Gradients of sum_r (g_r logp_r + gH_r H_r) of the fused LM head, in
     float64.
 
@@ -253,7 +287,7 @@ def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=N
     dw = np.zeros_like(w) if need_dweight else None
     for r0 in range(0, n, ROW_CHUNK):
         r1 = min(n, r0 + ROW_CHUNK)
-        x = linear_logits(h[r0:r1], w) / float(temperature)
+        x = _lm_logits(h[r0:r1], w, temperature, round_logits)
         row_lse = None if lse is None else np.asarray(lse, dtype=np.float64).reshape(-1)[r0:r1]
         dx = logp_bwd(x, t[r0:r1], g[r0:r1], ignore_index, lse=row_lse)
         if grad_entropy is not None:
@@ -268,7 +302,7 @@ def linear_logp_bwd(hidden, weight, targets, grad_logp, ignore_index=-100, lse=N
 
 def linear_logp_bwd_weight_rows(hidden, weight, targets, grad_logp, vocab_rows,
                                 ignore_index=-100, lse=None, temperature=1.0,
-                                grad_entropy=None, ent=None):
+                                grad_entropy=None, ent=None, round_logits=False):
     """Rows `vocab_rows` of dW from linear_logp_bwd, without forming the other
     vocabulary rows: dW[j] = sum_r dz[r, j] h[r] over active rows, with
     x[:, j] = h W[j]^T / T, p = exp(x - lse) and
@@ -282,16 +316,16 @@ def linear_logp_bwd_weight_rows(hidden, weight, targets, grad_logp, vocab_rows,
     g = np.asarray(grad_logp, dtype=np.float64).reshape(-1)
     active, _ = _active_mask(t, ignore_index, w.shape[0])
     if lse is None:
-        _, lse = linear_logp_fwd(h, w, t, ignore_index, temperature)
+        _, lse = linear_logp_fwd(h, w, t, ignore_index, temperature, round_logits)
     lse = np.asarray(lse, dtype=np.float64).reshape(-1)
     cols = np.asarray(vocab_rows, dtype=np.int64).reshape(-1)
-    x = (h @ w[cols].T) / float(temperature)          # [N, J]
+    x = _lm_logits(h, w[cols], temperature, round_logits)   # [N, J]
     p = np.exp(x - lse[:, None])
     onehot = (t[:, None] == cols[None, :]).astype(np.float64)
     dx = g[:, None] * (onehot - p)
     if grad_entropy is not None:
         if ent is None:
-            ent = linear_entropy(h, w, t, ignore_index, temperature)
+            ent = linear_entropy(h, w, t, ignore_index, temperature, round_logits)
         gh = np.asarray(grad_entropy, dtype=np.float64).reshape(-1)
         dx = dx - gh[:, None] * p * ((x - lse[:, None]) + np.asarray(ent)[:, None])
     dx[~active] = 0.0

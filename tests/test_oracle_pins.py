@@ -561,3 +561,90 @@ def test_linear_temperature_limits():
     a = oracle.linear_logp_fwd(h, w, t)
     b = oracle.linear_logp_fwd(h, w, t, temperature=1.0)
     assert np.array_equal(a[0], b[0])
+
+
+# ----- bf16-rounded-logits variant ---------------------------------------------
+
+def _torch_bf16(x32):
+    """float32 -> bfloat16 -> float64 by torch's conversion (round to nearest
+    even), the library routine the oracle's rounding is pinned against."""
+    return torch.from_numpy(np.asarray(x32, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def test_round_bf16_matches_library():
+    """round_bf16 equals torch's float32 -> bfloat16 conversion on float32
+    values across the exponent range, on exact ties (even neighbour wins),
+    on subnormals and at the overflow threshold."""
+    rng = np.random.default_rng(40)
+    mant = rng.uniform(1.0, 2.0, 20000)
+    expo = rng.integers(-140, 128, 20000)
+    x = (np.where(rng.random(20000) < 0.5, -1.0, 1.0) * np.ldexp(mant, expo)).astype(np.float32)
+    bits = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32)
+    y = bits.view(np.float32)
+    y = y[np.isfinite(y)]
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -126 * (1 + 2 ** -8),
+                     3 * 2 ** -135, 2 ** -134, 2 ** -133, 5 * 2 ** -135,
+                     255.5 * 2.0 ** 120, 255.25 * 2.0 ** 120, 65504.0, 0.0, -0.0],
+                    dtype=np.float32)
+    for v in (x, y, ties):
+        got = oracle.round_bf16(v.astype(np.float64))
+        want = _torch_bf16(v)
+        assert np.array_equal(got, want), v[got != want][:5]
+    assert oracle.round_bf16(1 + 2 ** -8) == 1.0
+    assert oracle.round_bf16(1 + 3 * 2 ** -8) == 1 + 2 ** -6
+    assert oracle.round_bf16(255.5 * 2.0 ** 120) == math.inf
+    assert np.isnan(oracle.round_bf16(np.nan))
+
+
+def test_round_bf16_idempotent_on_bf16_values():
+    """Values that are already bfloat16 come back unchanged."""
+    rng = np.random.default_rng(41)
+    v = _torch_bf16(rng.normal(size=5000).astype(np.float32) * 100)
+    assert np.array_equal(oracle.round_bf16(v), v)
+
+
+def test_linear_round_logits_exact_when_representable():
+    """When every logit is already a bf16 value (small integers here), the
+    rounded variant gives the plain fused operator's results exactly."""
+    rng = np.random.default_rng(42)
+    h = rng.integers(-2, 3, size=(7, 16)).astype(np.float64)
+    w = rng.integers(-2, 3, size=(40, 16)).astype(np.float64)
+    t = rng.integers(0, 40, 7)
+    t[3] = -100
+    g = rng.normal(size=7)
+    a = oracle.linear_logp_fwd(h, w, t, temperature=1.3)
+    b = oracle.linear_logp_fwd(h, w, t, temperature=1.3, round_logits=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    da = oracle.linear_logp_bwd(h, w, t, g)
+    db = oracle.linear_logp_bwd(h, w, t, g, round_logits=True)
+    assert np.array_equal(da[0], db[0]) and np.array_equal(da[1], db[1])
+
+
+def test_linear_round_logits_closed_form():
+    """h = [1, 1], W = [[1, 2^-9], [0, 0], [-1, 2^-7 + 2^-9]]: z = [1 + 2^-9,
+    0, -1 + 5 * 2^-9] rounds to [1, 0, -1 + 2^-7].  Above 1 the spacing is
+    2^-7, so 1 + 2^-9 goes down to 1; below 1 it is 2^-8, and
+    -1 + 5 * 2^-9 = -253.5 / 256 is a tie between -253 / 256 and -254 / 256,
+    which goes to the even -254 / 256.  logp, lse, entropy and the gradients
+    then follow from the rounded row in closed form; the plain operator uses
+    the unrounded row."""
+    h = np.array([[1.0, 1.0]])
+    w = np.array([[1.0, 2.0 ** -9], [0.0, 0.0], [-1.0, 2.0 ** -7 + 2.0 ** -9]])
+    zr = np.array([1.0, 0.0, -1.0 + 2.0 ** -7])
+    z = np.array([1.0 + 2.0 ** -9, 0.0, -1.0 + 5 * 2.0 ** -9])
+    assert np.array_equal(oracle.round_bf16(z), zr)
+    for t in range(3):
+        for rnd, row in ((True, zr), (False, z)):
+            lse = math.log(sum(math.exp(c) for c in row))
+            lp, ls = oracle.linear_logp_fwd(h, w, [t], round_logits=rnd)
+            assert abs(ls[0] - lse) < 1e-15 and abs(lp[0] - (row[t] - lse)) < 1e-15
+            p = np.exp(row - lse)
+            ent = -(p * (row - lse)).sum()
+            assert abs(oracle.linear_entropy(h, w, [t], round_logits=rnd)[0] - ent) < 1e-15
+            g = 0.75
+            dz = g * ((np.arange(3) == t) - p)
+            dh, dw = oracle.linear_logp_bwd(h, w, [t], [g], round_logits=rnd)
+            np.testing.assert_allclose(dh[0], dz @ w, rtol=0, atol=1e-15)
+            np.testing.assert_allclose(dw, np.outer(dz, h[0]), rtol=0, atol=1e-15)
+            got = oracle.linear_logp_bwd_weight_rows(h, w, [t], [g], [2, 0], round_logits=rnd)
+            np.testing.assert_allclose(got, np.outer(dz, h[0])[[2, 0]], rtol=0, atol=1e-15)
