@@ -77,6 +77,17 @@ enum logp_index_dtype {
   LOGP_I32 = 1   /* int32 */
 };
 
+/* Rounding point of the fused LM head's logits ("[RFC][ROCm] End-to-end
+ * optimization of bitwise VIME R/R beyond native P/P": the FP32/BF16 rounding
+ * points belong to the versioned arithmetic contract, and a fused epilogue
+ * performs a required BF16 round explicitly before the next step sees the
+ * value).  LOGP_ROUND_BF16 selects the variant contract whose statistics see
+ * the logits an unfused bf16 LM head would store. */
+enum logp_rounding {
+  LOGP_ROUND_NONE = 0,  /* statistics on the fp32 accumulators */
+  LOGP_ROUND_BF16 = 1   /* statistics on RNE_bf16(accumulator), widened exactly */
+};
+
 /*
  * Workspace of logp_fwd, in bytes.  It is 0 for num_shards == 1 with
  * validate == 0 (the fused single-launch path).  Otherwise it holds the
@@ -196,6 +207,11 @@ size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width)
  *               every statistic as z * fl32(1 / temperature) (the proposed
  *               operator's temperature, applied at this one point); 1 leaves
  *               them unchanged.
+ *   logits_rounding
+ *               LOGP_ROUND_NONE: z is the fp32 accumulator.  LOGP_ROUND_BF16:
+ *               z is replaced by RNE_bf16(accumulator) before anything else
+ *               (logits output, temperature, every statistic, the target
+ *               copy).  Other values: LOGP_ERR_VALUE.
  *   logits_out  [n, ld_logits] (ld_logits >= v) of logits_dtype (LOGP_F32 or
  *               LOGP_BF16, RNE) receiving the unscaled z, or NULL ("return
  *               logits" for sampling).  logp, lse and entropy have the same
@@ -207,7 +223,8 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight,
                         int64_t ld_w, int64_t n, int64_t h, int64_t v,
                         const void* targets, int32_t target_dtype,
                         int64_t ignore_index, int32_t tile_width, float temperature,
-                        float* logp_out, float* lse_out, float* entropy_out,
+                        int32_t logits_rounding, float* logp_out, float* lse_out,
+                        float* entropy_out,
                         void* logits_out, int32_t logits_dtype, int64_t ld_logits,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
@@ -225,7 +242,8 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  * backward recomputes the fixed logit tiles from the saved LSE; "Batch-
  * Invariant LogP", Batch-Invariance and Reference Semantics: the logit
  * gradient is g * (onehot - softmax), zero on ignored rows):
- *   z  = hidden weight^T          (recomputed with the forward's MFMA walk)
+ *   z  = hidden weight^T          (recomputed with the forward's MFMA walk,
+ *                                  RNE_bf16 under LOGP_ROUND_BF16)
  *   x  = z * fl32(1 / temperature)
  *   dz = RNE_bf16((g * (onehot(t) - p) - gH p (x - lse + H)) * fl32(1 / temperature)),
  *        p = exp(x - lse), the entropy term only when requested
@@ -238,7 +256,10 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *   ignore_index, tile_width:
  *               as linear_logp_fwd (h a multiple of 64, tile_width 256,
  *               16-byte aligned rows).
- *   temperature as linear_logp_fwd (the forward's value).
+ *   temperature, logits_rounding
+ *               as linear_logp_fwd (the forward's values; the rounding is
+ *               passed straight through, as an unfused bf16 LM head's
+ *               gradient is).
  *   lse         fp32 [n] from linear_logp_fwd.
  *   grad_logp   fp32 [n], the upstream gradient g.
  *   entropy, grad_entropy
@@ -257,8 +278,9 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
-                        float temperature, const float* lse, const float* grad_logp,
-                        const float* entropy, const float* grad_entropy, int32_t out_dtype,
+                        float temperature, int32_t logits_rounding, const float* lse,
+                        const float* grad_logp, const float* entropy,
+                        const float* grad_entropy, int32_t out_dtype,
                         void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
 

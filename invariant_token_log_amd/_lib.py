@@ -27,6 +27,8 @@ LOGP_F16 = 2
 
 LOGP_I64 = 0
 LOGP_I32 = 1
+LOGP_ROUND_NONE = 0
+LOGP_ROUND_BF16 = 1
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 _f32 = ctypes.c_float
@@ -39,10 +41,11 @@ _SIGNATURES = {
                         _vp, _vp, _vp, _i64, _vp]),
     "linear_logp_fwd_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "linear_logp_fwd": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
-                               _i32, _f32, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _sz, _vp]),
+                               _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _sz,
+                               _vp]),
     "linear_logp_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "linear_logp_bwd": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
-                               _i32, _f32, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i64,
+                               _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i64,
                                _vp, _sz, _vp]),
     "logp_status_str": (ctypes.c_char_p, [_i32]),
     "logp_contract_id": (ctypes.c_char_p, []),

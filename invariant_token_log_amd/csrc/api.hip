@@ -36,6 +36,7 @@ itl::Targets targets_of(const void* p, int32_t target_dtype) {
 // multiplied by its reciprocal rounded once to fp32 (1 stays exactly 1).
 bool valid_temperature(float t) { return t > 0.0f && t <= 3.4e38f; }
 float inv_temperature(float t) { return static_cast<float>(1.0 / static_cast<double>(t)); }
+bool valid_rounding(int32_t r) { return r == LOGP_ROUND_NONE || r == LOGP_ROUND_BF16; }
 
 bool aligned16(const void* p, int64_t ld, int32_t dtype) {
   return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * elt_size(dtype)) % 16 == 0);
@@ -176,14 +177,15 @@ size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width)
 int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
-                        float temperature, float* logp_out, float* lse_out, float* entropy_out,
-                        void* logits_out, int32_t logits_dtype, int64_t ld_logits,
-                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+                        float temperature, int32_t logits_rounding, float* logp_out,
+                        float* lse_out, float* entropy_out, void* logits_out,
+                        int32_t logits_dtype, int64_t ld_logits, void* workspace,
+                        size_t workspace_bytes, void* hip_stream) {
   if (n < 0 || v < 1 || h < 1 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
   if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
   if (logits_out && logits_dtype != LOGP_F32 && logits_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
   if (logits_out && ld_logits < v) return LOGP_ERR_SHAPE;
-  if (!valid_temperature(temperature)) return LOGP_ERR_VALUE;
+  if (!valid_temperature(temperature) || !valid_rounding(logits_rounding)) return LOGP_ERR_VALUE;
   const itl::Targets tg = targets_of(targets, target_dtype);
   if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
   const int64_t ntiles = (v + tile_width - 1) / tile_width;
@@ -206,8 +208,9 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
   (void)hipGetLastError();
   itl::launch_linear_partials(static_cast<const uint16_t*>(hidden), ld_h,
                               static_cast<const uint16_t*>(weight), ld_w, n, h, v, tg,
-                              ignore_index, pm, ps, pt, inv_temperature(temperature), pw,
-                              logits_out, logits_dtype == LOGP_BF16 ? 1 : 0, ld_logits, s);
+                              ignore_index, pm, ps, pt, inv_temperature(temperature),
+                              logits_rounding == LOGP_ROUND_BF16 ? 1 : 0, pw, logits_out,
+                              logits_dtype == LOGP_BF16 ? 1 : 0, ld_logits, s);
   itl::launch_fwd_merge(pm, ps, pw, pt, n, static_cast<int>(ntiles), ntiles, 1, v, tg,
                         ignore_index, logp_out, lse_out, entropy_out, nullptr, s);
   return hip_status();
@@ -222,10 +225,11 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
-                        float temperature, const float* lse, const float* grad_logp,
-                        const float* entropy, const float* grad_entropy, int32_t out_dtype,
-                        void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
-                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+                        float temperature, int32_t logits_rounding, const float* lse,
+                        const float* grad_logp, const float* entropy,
+                        const float* grad_entropy, int32_t out_dtype, void* dhidden,
+                        int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
+                        size_t workspace_bytes, void* hip_stream) {
   if (n < 0 || v < 1 || h < 64 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
   if (v > (int64_t{1} << 31) || n > (int64_t{1} << 31) ||
       ((n + 255) / 256) * ((v + 255) / 256) > (int64_t{1} << 30) ||
@@ -234,7 +238,7 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
   if (out_dtype != LOGP_F32 && out_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
   if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
-  if (!valid_temperature(temperature)) return LOGP_ERR_VALUE;
+  if (!valid_temperature(temperature) || !valid_rounding(logits_rounding)) return LOGP_ERR_VALUE;
   if (!dhidden && !dweight) return LOGP_ERR_NULL;
   if ((dhidden && ld_dh < h) || (dweight && ld_dw < h)) return LOGP_ERR_SHAPE;
   if (n == 0 && !dweight) return LOGP_OK;
@@ -250,7 +254,8 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   itl::launch_linear_bwd(static_cast<const uint16_t*>(hidden), ld_h,
                          static_cast<const uint16_t*>(weight), ld_w, n, h, v,
                          targets_of(targets, target_dtype), ignore_index, lse, grad_logp,
-                         inv_temperature(temperature), entropy, grad_entropy,
+                         inv_temperature(temperature), logits_rounding == LOGP_ROUND_BF16 ? 1 : 0,
+                         entropy, grad_entropy,
                          out_dtype == LOGP_BF16, dhidden, ld_dh, dweight, ld_dw,
                          static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream));
   return hip_status();
@@ -268,7 +273,7 @@ const char* logp_status_str(int32_t status) {
     case LOGP_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LOGP_ERR_TARGET: return "an active target lies outside [0, v)";
     case LOGP_ERR_HIP: return "HIP launch or copy failed";
-    case LOGP_ERR_VALUE: return "invalid scalar argument (temperature)";
+    case LOGP_ERR_VALUE: return "invalid scalar argument (temperature or logits rounding)";
     default: return "unknown status";
   }
 }
@@ -282,6 +287,7 @@ const char* logp_contract_id(void) {
          "bwd=dz:rne_bf16((g*(onehot-p)+fma(-gH,p*(x-lse+H)))*fl32(1/T)),"
          "dh:dz*W(k=vocab-asc32),dW:dz^T*h(k=token-asc32)]"
          "+entropy[w=sum e*(x-m) same tree;merge b=fma(fma(s,m-M,w),e,b);H=log(acc)-b/acc]"
+         "+itl.linear_logp_bf16z.v1[as itl.linear_logp.v1 with z=rne_bf16(acc) first]"
          "/gfx950";
 }
 

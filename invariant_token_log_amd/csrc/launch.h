@@ -50,7 +50,8 @@ void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, 
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
                             int64_t ld_w, int64_t n, int64_t h, int64_t v, Targets targets,
                             int64_t ignore, float* pm, float* ps, float* pt, float inv_t,
-                            float* pw, void* z, int32_t z_bf16, int64_t ld_z, hipStream_t s);
+                            int32_t round_bf16, float* pw, void* z, int32_t z_bf16, int64_t ld_z,
+                            hipStream_t s);
 
 constexpr int kLinearTile = 256;
 
@@ -68,8 +69,8 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
 // upstream gradient (both null = no entropy term).
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
-                       const float* lse, const float* grad, float inv_t, const float* ent,
-                       const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
-                       int64_t ld_dw, char* ws, hipStream_t s);
+                       const float* lse, const float* grad, float inv_t, int32_t round_bf16,
+                       const float* ent, const float* gent, bool bf16_out, void* dh,
+                       int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s);
 
 }  // namespace itl

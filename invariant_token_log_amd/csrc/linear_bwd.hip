@@ -102,8 +102,9 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse,
-    const float* __restrict__ grad, float inv_t, const float* __restrict__ ent,
-    const float* __restrict__ gent, uint16_t* __restrict__ dz, int64_t ld_dz,
+    const float* __restrict__ grad, float inv_t, int32_t round_bf16,
+    const float* __restrict__ ent, const float* __restrict__ gent, uint16_t* __restrict__ dz,
+    int64_t ld_dz,
     uint16_t* __restrict__ dzt, int64_t ld_dzt) {
   const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemDz sm;
@@ -149,7 +150,9 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
                  static_cast<int>(hdim / gemm::kK), acc);
   __syncthreads();
 
-  // x = z (* 1/T); p = exp(x - lse) with the forward's primitive; d = g (1 - p)
+  // z = the accumulator (RNE_bf16 of it in the bf16-rounded variant, whose
+  // gradient passes the rounding unchanged); x = z (* 1/T); p = exp(x - lse)
+  // with the forward's primitive; d = g (1 - p)
   // on the target column, (-g) p elsewhere, plus -gH p (x - lse + H) with the
   // entropy term (one fma, the -inf clamp of ent_term); d (* 1/T) for dz; RNE
   // to bf16.  Lane (li, g) holds rows 4g .. 4g+3 of each 16 x 16 block, so its
@@ -179,7 +182,9 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
       for (int q = 0; q < 4; ++q) {
         float d = 0.0f;
         if (code[q] != -2 && v0 + lc < v) {
-          const float x = scaled ? acc[i][j][q] * inv_t : acc[i][j][q];
+          const float z =
+              round_bf16 ? static_cast<float>(static_cast<__bf16>(acc[i][j][q])) : acc[i][j][q];
+          const float x = scaled ? z * inv_t : z;
           const float dl = x - L[q];  // exp_sub(x, L) in two steps
           const float p = __builtin_amdgcn_exp2f(dl * kLog2e);
           d = lc == code[q] ? G[q] * (1.0f - p) : (-G[q]) * p;
@@ -326,9 +331,9 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
 
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
-                       const float* lse, const float* grad, float inv_t, const float* ent,
-                       const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
-                       int64_t ld_dw, char* ws, hipStream_t s) {
+                       const float* lse, const float* grad, float inv_t, int32_t round_bf16,
+                       const float* ent, const float* gent, bool bf16_out, void* dh,
+                       int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s) {
   if (n == 0) {
     // dh has no rows; dW is a sum over no tokens.
     if (dw) {
@@ -349,7 +354,8 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
   hipLaunchKernelGGL(linear_dz_kernel, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0, s,
                      hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                       targets.is32, ignore, lse, grad, inv_t, ent, gent, dz, l.vp, dzt, l.np);
+                     targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, l.vp,
+                     dzt, l.np);
   if (dh) {
     hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
                        dim3(256), 0, s, weight, ld_w, v, l.vp, wt, l.vp);

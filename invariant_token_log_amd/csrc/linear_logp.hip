@@ -190,11 +190,12 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
   }
 }
 
-// Optional outputs of the forward statistic kernels: the temperature's
-// reciprocal (logits are multiplied by it before any statistic), the entropy
-// moment table and the unscaled logits.
+// Options of the forward statistic kernels: the logits' rounding point, the
+// temperature's reciprocal (logits are multiplied by it before any
+// statistic), the entropy moment table and the unscaled logits.
 struct LinearExtras {
   float inv_t;      // 1 = no temperature
+  int32_t round_bf16;  // 1 = z is RNE_bf16 of the accumulator
   float* pw;        // [n, T] entropy moments, or null
   void* z;          // [n, ld_z] unscaled logits (fp32 or bf16), or null
   int32_t z_bf16;
@@ -207,6 +208,18 @@ __device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>&
                                                int64_t v0, int vb, int vblocks, int64_t n,
                                                int64_t v, float* pm, float* ps, float* pt,
                                                const LinearExtras& ex) {
+  // The bf16-rounded variant: z becomes RNE_bf16(accumulator), widened
+  // exactly, before anything reads it (logits output, temperature, every
+  // statistic and the target copy).
+  if (ex.round_bf16) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[i][j][q] = static_cast<float>(static_cast<__bf16>(acc[i][j][q]));
+  }
   // The unscaled logits, when asked for: they are the accumulators as they
   // are (the statistics below do not change them).
   if (ex.z) {
@@ -395,9 +408,10 @@ __global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
                             int64_t ld_w, int64_t n, int64_t h, int64_t v, Targets targets,
                             int64_t ignore, float* pm, float* ps, float* pt, float inv_t,
-                            float* pw, void* z, int32_t z_bf16, int64_t ld_z, hipStream_t s) {
+                            int32_t round_bf16, float* pw, void* z, int32_t z_bf16, int64_t ld_z,
+                            hipStream_t s) {
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
-  const LinearExtras ex{inv_t, pw, z, z_bf16, ld_z};
+  const LinearExtras ex{inv_t, round_bf16, pw, z, z_bf16, ld_z};
   if (n <= 128) {
     const int mblocks = static_cast<int>((n + 127) / 128);
     hipLaunchKernelGGL(linear_stats_regstage, dim3(mblocks * vblocks), dim3(kRegThreads), 0, s,

@@ -143,14 +143,20 @@ def _linear_operands(hidden, weight):
     return n, h, v, ld_h, ld_w
 
 
+def _rounding(round_logits):
+    return _lib.LOGP_ROUND_BF16 if round_logits else _lib.LOGP_ROUND_NONE
+
+
 def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEAR_TILE,
                     logp_out=None, lse_out=None, workspace=None, temperature=1.0,
                     return_entropy=False, entropy_out=None, return_logits=False,
-                    logits_dtype=torch.bfloat16, logits_out=None):
+                    logits_dtype=torch.bfloat16, logits_out=None, round_logits=False):
     """Fused LM-head + selected-token log-probability without storing logits.
     hidden bf16 [N, H], weight bf16 [V, H].  Returns (logp [N], lse [N]), then
     the entropy [N] with return_entropy and the unscaled logits [N, V] with
-    return_logits.  The statistics see the logits times 1 / temperature."""
+    return_logits.  The statistics see the logits times 1 / temperature; with
+    round_logits the logits are first rounded to bf16 (RNE), as an unfused
+    bf16 LM head would store them."""
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     t1 = _targets(targets, n)
     dev = hidden.device
@@ -175,8 +181,8 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = L.linear_logp_fwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
                            t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                           float(temperature), logp_out.data_ptr(), lse_out.data_ptr(),
-                           _ptr(ent), _ptr(z), _DTYPES[logits_dtype],
+                           float(temperature), _rounding(round_logits), logp_out.data_ptr(),
+                           lse_out.data_ptr(), _ptr(ent), _ptr(z), _DTYPES[logits_dtype],
                            (z.stride(0) if n > 1 else v) if z is not None else 0,
                            workspace.data_ptr(), workspace.numel(), _stream(dev))
     check("linear_logp_fwd", st)
@@ -191,11 +197,12 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
 def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                     tile_width=LINEAR_TILE, need_dhidden=True, need_dweight=True,
                     out_dtype=torch.float32, dhidden_out=None, dweight_out=None,
-                    workspace=None, temperature=1.0, entropy=None, grad_entropy=None):
+                    workspace=None, temperature=1.0, entropy=None, grad_entropy=None,
+                    round_logits=False):
     """Backward of the fused LM head + logp: (dhidden [N, H] or None,
     dweight [V, H] or None) in out_dtype (float32 accumulators or their
     bfloat16 rounding), from the forward's lse (and entropy) and the upstream
-    gradients."""
+    gradients.  temperature and round_logits must be the forward's."""
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
@@ -224,7 +231,8 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     ws_len = workspace.numel() if workspace is not None else 0
     st = L.linear_logp_bwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
                            t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                           float(temperature), lse.data_ptr(), g.data_ptr(), _ptr(ent),
+                           float(temperature), _rounding(round_logits), lse.data_ptr(),
+                           g.data_ptr(), _ptr(ent),
                            _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
                            (dh.stride(0) if n > 1 else h) if dh is not None else 0,
                            _ptr(dw), (dw.stride(0) if v > 1 else h) if dw is not None else 0,
@@ -274,15 +282,17 @@ def batch_invariant_logp(logits, target_ids, ignore_index=-100, tile_width=4096,
 
 class _LinearLogp(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, hidden, weight, targets, ignore_index, temperature, with_entropy):
+    def forward(ctx, hidden, weight, targets, ignore_index, temperature, with_entropy,
+                round_logits):
         out = linear_logp_fwd(hidden, weight, targets, ignore_index, temperature=temperature,
-                              return_entropy=with_entropy)
+                              return_entropy=with_entropy, round_logits=round_logits)
         logp, lse = out[0], out[1]
         ent = out[2] if with_entropy else None
         ctx.save_for_backward(hidden, weight, targets, lse, ent)
         ctx.ignore_index = ignore_index
         ctx.temperature = temperature
         ctx.with_entropy = with_entropy
+        ctx.round_logits = round_logits
         if with_entropy:
             return logp, ent
         return logp
@@ -296,16 +306,18 @@ class _LinearLogp(torch.autograd.Function):
                                  need_dhidden=ctx.needs_input_grad[0],
                                  need_dweight=ctx.needs_input_grad[1],
                                  out_dtype=torch.bfloat16, temperature=ctx.temperature,
-                                 entropy=ent if ctx.with_entropy else None, grad_entropy=gent)
-        return dh, dw, None, None, None, None
+                                 entropy=ent if ctx.with_entropy else None, grad_entropy=gent,
+                                 round_logits=ctx.round_logits)
+        return dh, dw, None, None, None, None, None
 
 
 def linear_logp(hidden, weight, target_ids, ignore_index=-100, temperature=1.0,
-                return_entropy=False):
+                return_entropy=False, round_logits=False):
     """Differentiable fused LM head + selected-token log-probability:
     hidden bf16 [N, H], weight bf16 [V, H] -> float32 logp [N] (and the
     entropy [N] with return_entropy) of softmax(hidden weight^T / temperature);
-    backward fills the bf16 gradients of hidden and weight through
-    linear_logp_bwd."""
+    round_logits rounds the logits to bf16 first (the unfused bf16 LM head's
+    values; the gradient passes the rounding unchanged).  Backward fills the
+    bf16 gradients of hidden and weight through linear_logp_bwd."""
     return _LinearLogp.apply(hidden, weight, target_ids, ignore_index, temperature,
-                             return_entropy)
+                             return_entropy, round_logits)

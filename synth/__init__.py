@@ -158,3 +158,20 @@ def qwen3_linear(seed=1005, n=4096, h=QWEN3_HIDDEN, v=QWEN3_VOCAB,
     targets = uniform_targets(n, v, seed + 3, ign, device=device)
     return dict(hidden=hidden, weight=weight, targets=targets,
                 ignore_index=IGNORE_INDEX)
+
+
+def lattice_linear(seed, n, h, v, device="cpu", ignore_frac=0.0, w_den=1024, w_max=127):
+    """LM-head operands on small lattices: hidden entries uniform in {-1, 0,
+    1}, weight entries k / w_den with k uniform in [-w_max, w_max] (both
+    exact in bf16 for w_max < 256), uniform targets.  Every product and
+    partial sum of h @ W^T is then a multiple of 1 / w_den below
+    h * w_max / w_den in magnitude (19 bits at h = 4096 with the defaults),
+    so any float32 accumulation order gives the exact value, while typical
+    values carry more significant bits than bf16 keeps."""
+    g = _gen(seed, "cpu")
+    hidden = (torch.randint(-1, 2, (n, h), generator=g).to(torch.bfloat16)).to(device)
+    k = torch.randint(-w_max, w_max + 1, (v, h), generator=g)
+    weight = (k.to(torch.float32) / w_den).to(torch.bfloat16).to(device)
+    ign = choose_rows(n, ignore_frac, seed + 2) if ignore_frac else None
+    targets = uniform_targets(n, v, seed + 3, ign, device=device)
+    return dict(hidden=hidden, weight=weight, targets=targets, ignore_index=IGNORE_INDEX)

@@ -117,15 +117,17 @@ def test_bwd_argument_errors(L):
 def test_linear_argument_errors(L):
     def lin(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
-                 targets=FAKE, tdt=0, tile=256, temp=1.0, logp=FAKE, lse=FAKE, ent=None,
-                 z=None, zdt=1, ldz=0, ws=FAKE, ws_bytes=1 << 40)
+                 targets=FAKE, tdt=0, tile=256, temp=1.0, rnd=0, logp=FAKE, lse=FAKE,
+                 ent=None, z=None, zdt=1, ldz=0, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_fwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
                                  a["v"], a["targets"], a["tdt"], -100, a["tile"], a["temp"],
-                                 a["logp"], a["lse"], a["ent"], a["z"], a["zdt"], a["ldz"],
-                                 a["ws"], a["ws_bytes"], None)
+                                 a["rnd"], a["logp"], a["lse"], a["ent"], a["z"], a["zdt"],
+                                 a["ldz"], a["ws"], a["ws_bytes"], None)
     for bad in (0.0, -1.0, float("inf"), float("nan")):
         assert lin(temp=bad) == _lib.LOGP_ERR_VALUE, bad
+    for bad in (-1, 2, 7):
+        assert lin(rnd=bad) == _lib.LOGP_ERR_VALUE, bad
     assert lin(z=FAKE, zdt=2, ldz=151936) == _lib.LOGP_ERR_DTYPE
     assert lin(z=FAKE, zdt=0, ldz=100) == _lib.LOGP_ERR_SHAPE
     assert lin(tdt=9) == _lib.LOGP_ERR_DTYPE
@@ -145,15 +147,17 @@ def test_linear_argument_errors(L):
 def test_linear_bwd_argument_errors(L):
     def lb(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
-                 targets=FAKE, tdt=0, tile=256, temp=1.0, lse=FAKE, g=FAKE, ent=None,
-                 gent=None, out=0, dh=FAKE, ld_dh=4096, dw=FAKE, ld_dw=4096, ws=FAKE,
-                 ws_bytes=1 << 40)
+                 targets=FAKE, tdt=0, tile=256, temp=1.0, rnd=0, lse=FAKE, g=FAKE,
+                 ent=None, gent=None, out=0, dh=FAKE, ld_dh=4096, dw=FAKE, ld_dw=4096,
+                 ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_bwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
                                  a["v"], a["targets"], a["tdt"], -100, a["tile"], a["temp"],
-                                 a["lse"], a["g"], a["ent"], a["gent"], a["out"], a["dh"],
-                                 a["ld_dh"], a["dw"], a["ld_dw"], a["ws"], a["ws_bytes"], None)
+                                 a["rnd"], a["lse"], a["g"], a["ent"], a["gent"], a["out"],
+                                 a["dh"], a["ld_dh"], a["dw"], a["ld_dw"], a["ws"],
+                                 a["ws_bytes"], None)
     assert lb(temp=0.0) == _lib.LOGP_ERR_VALUE
+    assert lb(rnd=3) == _lib.LOGP_ERR_VALUE
     assert lb(ent=FAKE) == _lib.LOGP_ERR_NULL
     assert lb(tdt=5) == _lib.LOGP_ERR_DTYPE
     assert lb(out=2) == _lib.LOGP_ERR_DTYPE
