@@ -33,7 +33,8 @@ KERNEL_SOURCES = {
     "logp_bwd_kernel": ["invariant_token_log_amd/csrc/logp_kernels.hip",
                         "invariant_token_log_amd/csrc/logp_device.h"],
     "linear_stats_dma": ["invariant_token_log_amd/csrc/linear_logp.hip",
-                                 "invariant_token_log_amd/csrc/logp_device.h"],
+                         "invariant_token_log_amd/csrc/mfma_gemm.h",
+                         "invariant_token_log_amd/csrc/logp_device.h"],
 }
 
 
