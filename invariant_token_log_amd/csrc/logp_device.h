@@ -259,15 +259,22 @@ __device__ __forceinline__ float merge_lse_t(P m, P s, P w, int ntiles, int64_t 
       sk = s[k * stride];
       if constexpr (ENT) yk = fmaf(sk, mk - big_m, w[k * stride]);
     }
-    // e_k >= 0 always (or NaN); -1 marks a tile without columns.
-    const float ek = mk != -INFINITY ? exp_sub(mk, big_m) : -1.0f;
+    // A tile without columns (m_k = -inf) enters as s_k = e_k = y_k = 0, the
+    // same fold as skipping it without a branch per tile: fma(0, 0, x) = x
+    // for every x but -0, which it turns into +0.  acc is never negative; b
+    // only reaches the result through log(acc) - b / acc, where the sign of
+    // a zero b makes no difference (log(acc) is never -0).
+    const bool live = mk != -INFINITY;
+    const float ek = live ? exp_sub(mk, big_m) : 0.0f;
+    if (!live) {
+      sk = 0.0f;
+      yk = 0.0f;
+    }
     const int cnt = ntiles - c < kWave ? ntiles - c : kWave;
     for (int j = 0; j < cnt; ++j) {
       const float e = lane_value(ek, j);
-      if (e != -1.0f) {
-        acc = fmaf(lane_value(sk, j), e, acc);
-        if constexpr (ENT) b = fmaf(lane_value(yk, j), e, b);
-      }
+      acc = fmaf(lane_value(sk, j), e, acc);
+      if constexpr (ENT) b = fmaf(lane_value(yk, j), e, b);
     }
   }
   const float la = log_nat(acc);
