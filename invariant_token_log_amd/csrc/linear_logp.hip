@@ -27,9 +27,10 @@
 //     eight waves of 128 x 64 (two per SIMD, so each hides the other's LDS
 //     and barrier latency), operands streamed global -> LDS by direct 16-byte
 //     LDS loads through a four-stage ring;
-//   * linear_stats_regstage (N <= 128): 128 x 256 block, four waves of
-//     64 x 128, operands staged through registers into a double-buffered,
-//     padded LDS tile.
+//   * linear_stats_narrow (N <= 128): the 128 x 256 narrow tile of
+//     mfma_gemm.h, eight waves of 32 x 128, the same direct loads through a
+//     five-stage ring (few rows give little arithmetic per weight byte, so
+//     the tile is bound by the bytes it keeps in flight).
 #include "launch.h"
 #include "logp_device.h"
 #include "mfma_gemm.h"
@@ -38,7 +39,6 @@ namespace itl {
 
 namespace {
 
-using gemm::bf16x8;
 using gemm::f32x4;
 using gemm::tile_coords;
 using gemm::xcd_logical;
@@ -308,98 +308,45 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
 }
 
 // ---------------------------------------------------------------------------
-// linear_stats_regstage: BM = 128, 4 waves (wm = wave / 2 picks 64 rows, wn =
-// wave % 2 picks 128 columns), register staging, padded double buffer.
+// linear_stats_narrow: BM = 128 for few hidden rows (N <= 128), the narrow
+// mfma_gemm.h tile with five direct-load stages; same K walk and epilogue
+// tree as linear_stats_dma, so a row gets the same bits on either path.
 // ---------------------------------------------------------------------------
-constexpr int kRegThreads = 256;
-constexpr int kLdsStride = BK + 8;  // bf16 elements per LDS row (80 B: breaks bank aliasing)
-
-struct SmemReg {
-  uint16_t a[2][128 * kLdsStride];
-  uint16_t b[2][BN * kLdsStride];
+struct SmemNarrow {
+  gemm::StagesNarrow st;  // 120 KiB
   Reduce<128> rd;
 };
 
-__global__ __launch_bounds__(kRegThreads) void linear_stats_regstage(
+__global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
     float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
   const Targets targets{tgt, tgt32};
-  __shared__ __align__(16) SmemReg sm;
+  __shared__ __align__(16) SmemNarrow sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 2, wn = wave % 2;
   const int li = lane % 16, g = lane / 16;
 
   const int logical = xcd_logical(blockIdx.x, mblocks * vblocks);
   const int mb = logical % mblocks;
   const int vb = logical / mblocks;
-  const int64_t m0 = static_cast<int64_t>(mb) * 128;
+  const int64_t m0 = static_cast<int64_t>(mb) * gemm::kNarrowRows;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
-  if (tid < 128) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
+  if (tid < gemm::kNarrowRows)
+    sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
 
-  // Each thread moves 2 (A) + 4 (B) 16-byte chunks per K step: chunk p covers
-  // row frow + 64p, columns [fk, fk + 8) of the step.  Rows past n / v are
-  // clamped to the last valid row.  Straight-line code keeps the staging
-  // values in registers.
-  const int frow = tid / 4, fk = (tid % 4) * 8;
-  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
-#define ITL_LD(DST, BASE, LD, R0, LIM, P, K0)                                              \
-  {                                                                                        \
-    const int64_t gr = min((R0) + frow + (P) * 64, (LIM) - 1);                             \
-    DST = *reinterpret_cast<const uint4*>((BASE) + gr * (LD) + (K0) + fk);                 \
-  }
-#define ITL_FETCH(K0)                                                                      \
-  ITL_LD(ra0, hidden, ld_h, m0, n, 0, K0) ITL_LD(ra1, hidden, ld_h, m0, n, 1, K0)         \
-  ITL_LD(rb0, weight, ld_w, v0, v, 0, K0) ITL_LD(rb1, weight, ld_w, v0, v, 1, K0)         \
-  ITL_LD(rb2, weight, ld_w, v0, v, 2, K0) ITL_LD(rb3, weight, ld_w, v0, v, 3, K0)
-#define ITL_ST(ARR, P, SRC) \
-  *reinterpret_cast<uint4*>(&(ARR)[(frow + (P) * 64) * kLdsStride + fk]) = SRC;
-#define ITL_STASH(BUF)                                                                     \
-  ITL_ST(sm.a[BUF], 0, ra0) ITL_ST(sm.a[BUF], 1, ra1) ITL_ST(sm.b[BUF], 0, rb0)           \
-  ITL_ST(sm.b[BUF], 1, rb1) ITL_ST(sm.b[BUF], 2, rb2) ITL_ST(sm.b[BUF], 3, rb3)
-
-  f32x4 acc[4][8];
+  f32x4 acc[2][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int ksteps = static_cast<int>(hdim / BK);
-  ITL_FETCH(0)
-  ITL_STASH(0)
+  gemm::mainloop_narrow(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
+                        static_cast<int>(hdim / BK), acc);
   __syncthreads();
-  for (int kt = 0; kt < ksteps; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ksteps) {
-      ITL_FETCH(static_cast<int64_t>(kt + 1) * BK)
-    }
-    bf16x8 a[4], b[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(
-          &sm.a[buf][(wm * 64 + i * 16 + li) * kLdsStride + g * 8]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(
-          &sm.b[buf][(wn * 128 + j * 16 + li) * kLdsStride + g * 8]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    if (kt + 1 < ksteps) {
-      ITL_STASH(buf ^ 1)
-    }
-    __syncthreads();
-  }
-#undef ITL_LD
-#undef ITL_FETCH
-#undef ITL_ST
-#undef ITL_STASH
-  stats_epilogue<4, 8, 128, kRegThreads>(acc, sm.rd, wm * 64, wn * 128, li, g, tid, m0, v0, vb,
+  stats_epilogue<2, 8, 128, kDmaThreads>(acc, sm.rd, wm * 32, wn * 128, li, g, tid, m0, v0, vb,
                                          vblocks, n, v, pm, ps, pt, ex);
 }
 
@@ -412,11 +359,10 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                             hipStream_t s) {
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
   const LinearExtras ex{inv_t, round_bf16, pw, z, z_bf16, ld_z};
-  if (n <= 128) {
-    const int mblocks = static_cast<int>((n + 127) / 128);
-    hipLaunchKernelGGL(linear_stats_regstage, dim3(mblocks * vblocks), dim3(kRegThreads), 0, s,
-                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                       targets.is32, ignore, pm, ps, pt, ex);
+  if (n <= gemm::kNarrowRows) {
+    hipLaunchKernelGGL(linear_stats_narrow, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden, ld_h,
+                       weight, ld_w, n, h, v, 1, vblocks, targets.p, targets.is32, ignore, pm,
+                       ps, pt, ex);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     hipLaunchKernelGGL(linear_stats_dma, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,

@@ -161,5 +161,98 @@ __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict_
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Narrow tile for few hidden rows: 128 A rows x 256 B rows, the same MFMA
+// form, K walk and LDS chunk layout as the 256 x 256 tile, so every output
+// gets the same bits.  8 waves; wave w covers rows (w / 2) * 32 + [0, 32) and
+// columns (w % 2) * 128 + [0, 128) as accN[i][j][q] = C[row0 + i*16 + 4*g +
+// q][col0 + j*16 + li].  Five stages (four K steps in flight, 96 KiB per
+// workgroup) because with so little arithmetic per byte the tile is bound by
+// how many bytes it keeps in flight.  Wave w fills A block w and B blocks w,
+// w + 8 of every stage.
+// ---------------------------------------------------------------------------
+constexpr int kNarrowRows = 128;
+constexpr int kNarrowStages = 5;
+
+struct StagesNarrow {
+  uint16_t a[kNarrowStages][kNarrowRows * kK];  // 8 KiB each
+  uint16_t b[kNarrowStages][kTile * kK];        // 16 KiB each
+};
+
+// acc += A[a_row0 + 0..127, 0..K) * B[b_row0 + 0..255, 0..K)^T, K = ksteps * 32
+// (ksteps even, >= 2); rows at or past a_rows / b_rows are read from the last
+// valid row.  All 512 threads must call; on return every direct load has
+// landed and the stages may be reused after a barrier.
+__device__ __forceinline__ void mainloop_narrow(StagesNarrow& sm, const uint16_t* __restrict__ A,
+                                                int64_t lda, int64_t a_row0, int64_t a_rows,
+                                                const uint16_t* __restrict__ B, int64_t ldb,
+                                                int64_t b_row0, int64_t b_rows, int ksteps,
+                                                f32x4 (&acc)[2][8]) {
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int wm = wave / 2, wn = wave % 2;
+  const int li = lane % 16, g = lane / 16;
+  const int lrow = lane / 4;
+  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
+  const uint16_t* a0 = A + min(a_row0 + wave * 16 + lrow, a_rows - 1) * lda + lk;
+  const uint16_t* b0 = B + min(b_row0 + wave * 16 + lrow, b_rows - 1) * ldb + lk;
+  const uint16_t* b1 = B + min(b_row0 + (wave + 8) * 16 + lrow, b_rows - 1) * ldb + lk;
+  const int aoff = (wm * 32 + li) * kK + ((g ^ swz(li)) * 8);
+  const int boff = (wn * 128 + li) * kK + ((g ^ swz(li)) * 8);
+  constexpr int kBlk = 16 * kK;
+  auto issue_step = [&](int s, int step) {
+    const int64_t k0 = static_cast<int64_t>(step) * kK;
+    __builtin_amdgcn_global_load_lds(a0 + k0, sm.a[s] + wave * kBlk, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b0 + k0, sm.b[s] + wave * kBlk, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b1 + k0, sm.b[s] + (wave + 8) * kBlk, 16, 0, 0);
+  };
+  // Iteration kt: MFMAs of step kt on fragments in registers, fragment reads
+  // of step kt+1, direct loads of step kt+5 (kt+2 .. kt+4 in flight).  Every
+  // iteration issues 3 loads per wave, so the wait counts are constant; past
+  // the end the loads re-fetch the last K step into a stage no longer read.
+  for (int st = 0; st < kNarrowStages; ++st) issue_step(st, st < ksteps ? st : ksteps - 1);
+  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  bf16x8 xa[2], xb[8], ya[2], yb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(sm.b[0] + boff + j * 16 * kK);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) xa[i] = *reinterpret_cast<const bf16x8*>(sm.a[0] + aoff + i * 16 * kK);
+  int cur = 0;  // stage of step kt
+#define ITL_NSTEP(CA, CB, NA, NB, KT)                                                        \
+  {                                                                                          \
+    asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)" ::: "memory");                              \
+    __builtin_amdgcn_s_barrier();                                                            \
+    const int nxt = cur + 1 == kNarrowStages ? 0 : cur + 1;                                  \
+    issue_step(cur, (KT) + kNarrowStages < ksteps ? (KT) + kNarrowStages : ksteps - 1);      \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                            \
+      NB[j] = *reinterpret_cast<const bf16x8*>(sm.b[nxt] + boff + j * 16 * kK);              \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
+      NA[i] = *reinterpret_cast<const bf16x8*>(sm.a[nxt] + aoff + i * 16 * kK);              \
+    cur = nxt;                                                                               \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
+      _Pragma("unroll") for (int j = 0; j < 8; ++j)                                          \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0); \
+    /* 3 x (1 direct load, 3 x (1 MFMA, 1 fragment read)), 1 MFMA + 1 read, 6 MFMAs */      \
+    _Pragma("unroll") for (int u = 0; u < 3; ++u) {                                          \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
+      _Pragma("unroll") for (int w = 0; w < 3; ++w) {                                        \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
+      }                                                                                      \
+    }                                                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);                                       \
+  }
+  for (int kt = 0; kt < ksteps; kt += 2) {
+    ITL_NSTEP(xa, xb, ya, yb, kt)
+    ITL_NSTEP(ya, yb, xa, xb, kt + 1)
+  }
+#undef ITL_NSTEP
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 }  // namespace gemm
 }  // namespace itl

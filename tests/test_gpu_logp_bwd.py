@@ -146,3 +146,24 @@ def test_int32_targets_same_bits():
     a = itl.logp_bwd(x, t, lse, g, -100, 512)
     b = itl.logp_bwd(x, t.to(torch.int32), lse, g, -100, 512)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_tall_batch_grid_stride():
+    """More rows than one grid dimension holds (65535): the backward walks the
+    rows grid-stride, the forward runs one workgroup per row; parity on every
+    element, the 2-shard forward has the same bits, and dlogits of the rows
+    past 65535 equal those of the same rows computed alone."""
+    n, v = 70000, 512
+    x = synth.normal_matrix(n, v, 3.0, torch.bfloat16, seed=71).to(dev())
+    ign = synth.choose_rows(n, 0.05, seed=72)
+    t = synth.uniform_targets(n, v, seed=73, ignore_rows=ign).to(dev())
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=74)[0].to(dev())
+    d = _check(x, t, g, 512, "tall")
+    logp1, lse1 = itl.logp_fwd(x, t, -100, 512)
+    logp2, lse2 = itl.logp_fwd(x, t, -100, 512, num_shards=2)
+    assert torch.equal(logp1.view(torch.int32), logp2.view(torch.int32))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+    tail = slice(65530, n)
+    d_tail = itl.logp_bwd(x[tail].contiguous(), t[tail].contiguous(), lse1[tail].contiguous(),
+                          g[tail].contiguous(), -100, 512)
+    assert torch.equal(d_tail.view(torch.int16), d[tail].view(torch.int16))
