@@ -260,6 +260,18 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *               as linear_logp_fwd (the forward's values; the rounding is
  *               passed straight through, as an unfused bf16 LM head's
  *               gradient is).
+ *   saved_logits, saved_dtype, ld_saved
+ *               NULL: z is recomputed on the MFMA tile (no [n, v] memory is
+ *               kept between forward and backward).  Otherwise the
+ *               forward's unscaled logits output ([n, ld_saved], ld_saved
+ *               >= v, 16-byte aligned rows, else LOGP_ERR_SHAPE /
+ *               LOGP_ERR_ALIGN), read instead of recomputing z: the
+ *               "retain logits" side of the memory trade-off the fused
+ *               operator's backward leaves open.  The values are the same,
+ *               so dhidden and dweight have the same bits either way.
+ *               saved_dtype LOGP_F32, or LOGP_BF16 only with
+ *               LOGP_ROUND_BF16 (where the bf16 logits are exactly z);
+ *               otherwise LOGP_ERR_DTYPE.
  *   lse         fp32 [n] from linear_logp_fwd.
  *   grad_logp   fp32 [n], the upstream gradient g.
  *   entropy, grad_entropy
@@ -278,7 +290,8 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
-                        float temperature, int32_t logits_rounding, const float* lse,
+                        float temperature, int32_t logits_rounding, const void* saved_logits,
+                        int32_t saved_dtype, int64_t ld_saved, const float* lse,
                         const float* grad_logp, const float* entropy,
                         const float* grad_entropy, int32_t out_dtype,
                         void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,

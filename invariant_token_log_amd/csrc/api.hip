@@ -225,7 +225,8 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
-                        float temperature, int32_t logits_rounding, const float* lse,
+                        float temperature, int32_t logits_rounding, const void* saved_logits,
+                        int32_t saved_dtype, int64_t ld_saved, const float* lse,
                         const float* grad_logp, const float* entropy,
                         const float* grad_entropy, int32_t out_dtype, void* dhidden,
                         int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
@@ -239,6 +240,13 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   if (out_dtype != LOGP_F32 && out_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
   if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
   if (!valid_temperature(temperature) || !valid_rounding(logits_rounding)) return LOGP_ERR_VALUE;
+  if (saved_logits) {
+    if (saved_dtype != LOGP_F32 &&
+        !(saved_dtype == LOGP_BF16 && logits_rounding == LOGP_ROUND_BF16))
+      return LOGP_ERR_DTYPE;
+    if (ld_saved < v) return LOGP_ERR_SHAPE;
+    if (!aligned16(saved_logits, ld_saved, saved_dtype)) return LOGP_ERR_ALIGN;
+  }
   if (!dhidden && !dweight) return LOGP_ERR_NULL;
   if ((dhidden && ld_dh < h) || (dweight && ld_dw < h)) return LOGP_ERR_SHAPE;
   if (n == 0 && !dweight) return LOGP_OK;
@@ -253,7 +261,8 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   (void)hipGetLastError();
   itl::launch_linear_bwd(static_cast<const uint16_t*>(hidden), ld_h,
                          static_cast<const uint16_t*>(weight), ld_w, n, h, v,
-                         targets_of(targets, target_dtype), ignore_index, lse, grad_logp,
+                         targets_of(targets, target_dtype), ignore_index, saved_logits,
+                         saved_dtype == LOGP_BF16 ? 1 : 0, ld_saved, lse, grad_logp,
                          inv_temperature(temperature), logits_rounding == LOGP_ROUND_BF16 ? 1 : 0,
                          entropy, grad_entropy,
                          out_dtype == LOGP_BF16, dhidden, ld_dh, dweight, ld_dw,

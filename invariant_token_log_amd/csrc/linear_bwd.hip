@@ -83,6 +83,24 @@ __global__ __launch_bounds__(256) void transpose_pad_bf16(const uint16_t* __rest
   }
 }
 
+// One element of the logit gradient.  z = the logit (RNE_bf16 of it in the
+// bf16-rounded variant, whose gradient passes the rounding unchanged);
+// x = z (* 1/T); p = exp(x - lse) with the forward's primitive; d = g (1 - p)
+// on the target column, (-g) p elsewhere, plus -gH p (x - lse + H) with the
+// entropy term (one fma, the -inf clamp of ent_term); d (* 1/T) for dz.
+__device__ __forceinline__ float dz_value(float zacc, float L, float G, float H, float NGH,
+                                          bool is_target, float inv_t, bool scaled,
+                                          bool with_ent, int32_t round_bf16) {
+  const float z = round_bf16 ? static_cast<float>(static_cast<__bf16>(zacc)) : zacc;
+  const float x = scaled ? z * inv_t : z;
+  const float dl = x - L;  // exp_sub(x, L) in two steps
+  const float p = __builtin_amdgcn_exp2f(dl * kLog2e);
+  float d = is_target ? G * (1.0f - p) : (-G) * p;
+  if (with_ent) d = fmaf(NGH, p * fmaxf(dl + H, -FLT_MAX), d);
+  if (scaled) d = d * inv_t;
+  return d;
+}
+
 struct SmemDz {
   union {
     gemm::Stages st;                // main loop
@@ -150,14 +168,10 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
                  static_cast<int>(hdim / gemm::kK), acc);
   __syncthreads();
 
-  // z = the accumulator (RNE_bf16 of it in the bf16-rounded variant, whose
-  // gradient passes the rounding unchanged); x = z (* 1/T); p = exp(x - lse)
-  // with the forward's primitive; d = g (1 - p)
-  // on the target column, (-g) p elsewhere, plus -gH p (x - lse + H) with the
-  // entropy term (one fma, the -inf clamp of ent_term); d (* 1/T) for dz; RNE
-  // to bf16.  Lane (li, g) holds rows 4g .. 4g+3 of each 16 x 16 block, so its
-  // four values of a column pack into 8 contiguous bytes of the transposed
-  // tile.
+  // dz of every element (dz_value; 0 on ignored / padded rows and columns),
+  // rounded to bf16.  Lane (li, g) holds rows 4g .. 4g+3 of each 16 x 16
+  // block, so its four values of a column pack into 8 contiguous bytes of the
+  // transposed tile.
   const bool scaled = inv_t != 1.0f;
   const bool with_ent = ent != nullptr;
   uint32_t dv[8][4][2];
@@ -180,17 +194,10 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
       uint16_t b[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float d = 0.0f;
-        if (code[q] != -2 && v0 + lc < v) {
-          const float z =
-              round_bf16 ? static_cast<float>(static_cast<__bf16>(acc[i][j][q])) : acc[i][j][q];
-          const float x = scaled ? z * inv_t : z;
-          const float dl = x - L[q];  // exp_sub(x, L) in two steps
-          const float p = __builtin_amdgcn_exp2f(dl * kLog2e);
-          d = lc == code[q] ? G[q] * (1.0f - p) : (-G[q]) * p;
-          if (with_ent) d = fmaf(NGH[q], p * fmaxf(dl + H[q], -FLT_MAX), d);
-          if (scaled) d = d * inv_t;
-        }
+        const float d = code[q] != -2 && v0 + lc < v
+                            ? dz_value(acc[i][j][q], L[q], G[q], H[q], NGH[q], lc == code[q],
+                                       inv_t, scaled, with_ent, round_bf16)
+                            : 0.0f;
         b[q] = bf16_bits(d);
       }
       dv[i][j][0] = static_cast<uint32_t>(b[0]) | (static_cast<uint32_t>(b[1]) << 16);
@@ -230,6 +237,118 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     const int r = idx >> 5, c = (idx & 31) * 8;
     store_stream(dz + (m0 + r) * ld_dz + v0 + c,
                  *reinterpret_cast<const uint4*>(&sm.u.tile[r][c]));
+  }
+}
+
+// dz and dz^T from the forward's saved unscaled logits (fp32, or bf16 with
+// ZBF16; [n, ld_z], 16-byte aligned rows) instead of the recomputed product:
+// the same values through the same dz_value, so the same bits.  64 x 64
+// tiles of [Np, Vp]: thread (r = tid / 4, 16 columns from (tid % 4) * 16)
+// reads its 16 logits with 16-byte loads, writes its 16 dz along the row,
+// and the tile leaves transposed through LDS for dz^T.  Rows past n or
+// ignored, and columns past v, get 0 without reading the logits.
+constexpr int kST = 64;
+
+template <bool ZBF16>
+__global__ __launch_bounds__(256) void linear_dz_saved_kernel(
+    const void* __restrict__ zsaved, int64_t ld_z, int64_t n, int64_t v, int64_t np_rows,
+    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
+    const float* __restrict__ lse, const float* __restrict__ grad, float inv_t,
+    int32_t round_bf16, const float* __restrict__ ent, const float* __restrict__ gent,
+    uint16_t* __restrict__ dz, int64_t ld_dz, uint16_t* __restrict__ dzt, int64_t ld_dzt) {
+  const Targets targets{tgt, tgt32};
+  __shared__ uint16_t tile[kST][kST + 8];
+  const int tid = threadIdx.x;
+  const int r = tid / 4, cs = (tid % 4) * 16;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kST;
+  const bool scaled = inv_t != 1.0f;
+  const bool with_ent = ent != nullptr;
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.y) * kST; r0 < np_rows;
+       r0 += static_cast<int64_t>(gridDim.y) * kST) {
+    const int64_t row = r0 + r;
+    int64_t t = ignore_index;
+    float L = 0.0f, G = 0.0f, H = 0.0f, NGH = 0.0f;
+    if (row < n) {
+      t = targets[row];
+      if (t != ignore_index) {
+        L = lse[row];
+        G = grad[row];
+        if (with_ent) {
+          H = ent[row];
+          NGH = -gent[row];
+        }
+      }
+    }
+    const bool live = row < n && t != ignore_index;
+    float zv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) zv[u] = 0.0f;
+    const int64_t col = c0 + cs;
+    if (live) {
+      if (col + 16 <= v) {
+        if constexpr (ZBF16) {
+          const uint16_t* p = static_cast<const uint16_t*>(zsaved) + row * ld_z + col;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint4 w = load_stream(p + 8 * h);
+            const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              zv[8 * h + 2 * e] = bf16_lo(q[e]);
+              zv[8 * h + 2 * e + 1] = bf16_hi(q[e]);
+            }
+          }
+        } else {
+          const float* p = static_cast<const float*>(zsaved) + row * ld_z + col;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint4 w = load_stream(p + 4 * h);
+            zv[4 * h] = __uint_as_float(w.x);
+            zv[4 * h + 1] = __uint_as_float(w.y);
+            zv[4 * h + 2] = __uint_as_float(w.z);
+            zv[4 * h + 3] = __uint_as_float(w.w);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (col + u < v)
+            zv[u] = ZBF16 ? bf16_lo(static_cast<const uint16_t*>(zsaved)[row * ld_z + col + u])
+                          : static_cast<const float*>(zsaved)[row * ld_z + col + u];
+      }
+    }
+    uint32_t packed[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t b[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int u = 2 * e + k;
+        const float d = live && col + u < v
+                            ? dz_value(zv[u], L, G, H, NGH, col + u == t, inv_t, scaled,
+                                       with_ent, round_bf16)
+                            : 0.0f;
+        b[k] = bf16_bits(d);
+        tile[r][cs + u] = b[k];
+      }
+      packed[e] = static_cast<uint32_t>(b[0]) | (static_cast<uint32_t>(b[1]) << 16);
+    }
+    uint16_t* o = dz + row * ld_dz + col;
+    store_stream(o, make_uint4(packed[0], packed[1], packed[2], packed[3]));
+    store_stream(o + 8, make_uint4(packed[4], packed[5], packed[6], packed[7]));
+    __syncthreads();
+    {
+      const int c = tid / 4, rs = (tid % 4) * 16;
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w[e] = static_cast<uint32_t>(tile[rs + 2 * e][c]) |
+               (static_cast<uint32_t>(tile[rs + 2 * e + 1][c]) << 16);
+      uint16_t* q = dzt + (c0 + c) * ld_dzt + r0 + rs;
+      store_stream(q, make_uint4(w[0], w[1], w[2], w[3]));
+      store_stream(q + 8, make_uint4(w[4], w[5], w[6], w[7]));
+    }
+    __syncthreads();
   }
 }
 
@@ -331,9 +450,10 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
 
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
-                       const float* lse, const float* grad, float inv_t, int32_t round_bf16,
-                       const float* ent, const float* gent, bool bf16_out, void* dh,
-                       int64_t ld_dh, void* dw, int64_t ld_dw, char* ws, hipStream_t s) {
+                       const void* zsaved, int32_t z_bf16, int64_t ld_z, const float* lse,
+                       const float* grad, float inv_t, int32_t round_bf16, const float* ent,
+                       const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
+                       int64_t ld_dw, char* ws, hipStream_t s) {
   if (n == 0) {
     // dh has no rows; dW is a sum over no tokens.
     if (dw) {
@@ -352,10 +472,23 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + l.dz);
   uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + l.dzt);
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
-  hipLaunchKernelGGL(linear_dz_kernel, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0, s,
-                     hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                     targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, l.vp,
-                     dzt, l.np);
+  if (!zsaved) {
+    hipLaunchKernelGGL(linear_dz_kernel, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0, s,
+                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
+                       targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, l.vp,
+                       dzt, l.np);
+  } else {
+    const int64_t rb = l.np / kST;
+    const dim3 grid(static_cast<unsigned>(l.vp / kST), static_cast<unsigned>(rb < 65535 ? rb : 65535));
+    if (z_bf16)
+      hipLaunchKernelGGL(linear_dz_saved_kernel<true>, grid, dim3(256), 0, s, zsaved, ld_z, n, v,
+                         l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16, ent,
+                         gent, dz, l.vp, dzt, l.np);
+    else
+      hipLaunchKernelGGL(linear_dz_saved_kernel<false>, grid, dim3(256), 0, s, zsaved, ld_z, n,
+                         v, l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
+                         ent, gent, dz, l.vp, dzt, l.np);
+  }
   if (dh) {
     hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
                        dim3(256), 0, s, weight, ld_w, v, l.vp, wt, l.vp);

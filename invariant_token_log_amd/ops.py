@@ -198,11 +198,13 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                     tile_width=LINEAR_TILE, need_dhidden=True, need_dweight=True,
                     out_dtype=torch.float32, dhidden_out=None, dweight_out=None,
                     workspace=None, temperature=1.0, entropy=None, grad_entropy=None,
-                    round_logits=False):
+                    round_logits=False, saved_logits=None):
     """Backward of the fused LM head + logp: (dhidden [N, H] or None,
     dweight [V, H] or None) in out_dtype (float32 accumulators or their
     bfloat16 rounding), from the forward's lse (and entropy) and the upstream
-    gradients.  temperature and round_logits must be the forward's."""
+    gradients.  temperature and round_logits must be the forward's.
+    saved_logits: the forward's logits output ([N, V] float32, or bfloat16
+    with round_logits), read instead of recomputing h W^T; same bits."""
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
@@ -224,6 +226,10 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
         if o is not None and (o.dtype != out_dtype or o.dim() != 2 or o.shape[0] != rows
                               or o.shape[1] != h or o.stride(1) != 1):
             raise ValueError("output buffers must be [rows, H] of out_dtype, rows contiguous")
+    z = saved_logits
+    if z is not None and (z.dim() != 2 or tuple(z.shape) != (n, v) or z.stride(1) != 1
+                          or z.dtype not in (torch.float32, torch.bfloat16)):
+        raise ValueError("saved_logits must be [N, V] float32 / bfloat16 with contiguous rows")
     L = _lib.lib()
     need = L.linear_logp_bwd_workspace_bytes(n, h, v, tile_width)
     if need and workspace is None:
@@ -231,7 +237,9 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     ws_len = workspace.numel() if workspace is not None else 0
     st = L.linear_logp_bwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
                            t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                           float(temperature), _rounding(round_logits), lse.data_ptr(),
+                           float(temperature), _rounding(round_logits), _ptr(z),
+                           _DTYPES[z.dtype] if z is not None else 0,
+                           max(z.stride(0), v) if z is not None else 0, lse.data_ptr(),
                            g.data_ptr(), _ptr(ent),
                            _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
                            (dh.stride(0) if n > 1 else h) if dh is not None else 0,
@@ -280,15 +288,28 @@ def batch_invariant_logp(logits, target_ids, ignore_index=-100, tile_width=4096,
                                      return_entropy)
 
 
+def _padded_logits(n, v, dtype, device):
+    """[n, v] view of a buffer whose rows are padded to 16 bytes, so the
+    backward can read it with 16-byte loads."""
+    per = 16 // torch.empty((), dtype=dtype).element_size()
+    ld = (v + per - 1) // per * per
+    return torch.empty(n, ld, dtype=dtype, device=device)[:, :v]
+
+
 class _LinearLogp(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, targets, ignore_index, temperature, with_entropy,
-                round_logits):
+                round_logits, save_logits):
+        zdt = torch.bfloat16 if round_logits else torch.float32
+        zbuf = _padded_logits(hidden.shape[0], weight.shape[0], zdt, hidden.device) \
+            if save_logits else None
         out = linear_logp_fwd(hidden, weight, targets, ignore_index, temperature=temperature,
-                              return_entropy=with_entropy, round_logits=round_logits)
+                              return_entropy=with_entropy, round_logits=round_logits,
+                              return_logits=save_logits, logits_dtype=zdt, logits_out=zbuf)
         logp, lse = out[0], out[1]
         ent = out[2] if with_entropy else None
-        ctx.save_for_backward(hidden, weight, targets, lse, ent)
+        z = out[-1] if save_logits else None
+        ctx.save_for_backward(hidden, weight, targets, lse, ent, z)
         ctx.ignore_index = ignore_index
         ctx.temperature = temperature
         ctx.with_entropy = with_entropy
@@ -299,7 +320,7 @@ class _LinearLogp(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad, *rest):
-        hidden, weight, targets, lse, ent = ctx.saved_tensors
+        hidden, weight, targets, lse, ent, z = ctx.saved_tensors
         g = _grad_or_zeros(grad, lse)
         gent = _grad_or_zeros(rest[0], lse) if ctx.with_entropy else None
         dh, dw = linear_logp_bwd(hidden, weight, targets, lse, g, ctx.ignore_index,
@@ -307,17 +328,19 @@ class _LinearLogp(torch.autograd.Function):
                                  need_dweight=ctx.needs_input_grad[1],
                                  out_dtype=torch.bfloat16, temperature=ctx.temperature,
                                  entropy=ent if ctx.with_entropy else None, grad_entropy=gent,
-                                 round_logits=ctx.round_logits)
-        return dh, dw, None, None, None, None, None
+                                 round_logits=ctx.round_logits, saved_logits=z)
+        return dh, dw, None, None, None, None, None, None
 
 
 def linear_logp(hidden, weight, target_ids, ignore_index=-100, temperature=1.0,
-                return_entropy=False, round_logits=False):
+                return_entropy=False, round_logits=False, save_logits=False):
     """Differentiable fused LM head + selected-token log-probability:
     hidden bf16 [N, H], weight bf16 [V, H] -> float32 logp [N] (and the
     entropy [N] with return_entropy) of softmax(hidden weight^T / temperature);
     round_logits rounds the logits to bf16 first (the unfused bf16 LM head's
     values; the gradient passes the rounding unchanged).  Backward fills the
-    bf16 gradients of hidden and weight through linear_logp_bwd."""
+    bf16 gradients of hidden and weight through linear_logp_bwd, recomputing
+    the logits, or, with save_logits, reading the logits the forward kept
+    ([N, V] float32, bfloat16 with round_logits; same bits, more memory)."""
     return _LinearLogp.apply(hidden, weight, target_ids, ignore_index, temperature,
-                             return_entropy, round_logits)
+                             return_entropy, round_logits, save_logits)

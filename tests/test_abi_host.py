@@ -147,17 +147,23 @@ def test_linear_argument_errors(L):
 def test_linear_bwd_argument_errors(L):
     def lb(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
-                 targets=FAKE, tdt=0, tile=256, temp=1.0, rnd=0, lse=FAKE, g=FAKE,
-                 ent=None, gent=None, out=0, dh=FAKE, ld_dh=4096, dw=FAKE, ld_dw=4096,
-                 ws=FAKE, ws_bytes=1 << 40)
+                 targets=FAKE, tdt=0, tile=256, temp=1.0, rnd=0, z=None, zdt=0, ldz=0,
+                 lse=FAKE, g=FAKE, ent=None, gent=None, out=0, dh=FAKE, ld_dh=4096, dw=FAKE,
+                 ld_dw=4096, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_bwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
                                  a["v"], a["targets"], a["tdt"], -100, a["tile"], a["temp"],
-                                 a["rnd"], a["lse"], a["g"], a["ent"], a["gent"], a["out"],
-                                 a["dh"], a["ld_dh"], a["dw"], a["ld_dw"], a["ws"],
-                                 a["ws_bytes"], None)
+                                 a["rnd"], a["z"], a["zdt"], a["ldz"], a["lse"], a["g"],
+                                 a["ent"], a["gent"], a["out"], a["dh"], a["ld_dh"], a["dw"],
+                                 a["ld_dw"], a["ws"], a["ws_bytes"], None)
     assert lb(temp=0.0) == _lib.LOGP_ERR_VALUE
     assert lb(rnd=3) == _lib.LOGP_ERR_VALUE
+    # saved logits: fp32, or bf16 only in the bf16-rounded contract
+    assert lb(z=FAKE, zdt=_lib.LOGP_BF16, ldz=151936) == _lib.LOGP_ERR_DTYPE
+    assert lb(z=FAKE, zdt=_lib.LOGP_F16, ldz=151936, rnd=1) == _lib.LOGP_ERR_DTYPE
+    assert lb(z=FAKE, zdt=_lib.LOGP_F32, ldz=100) == _lib.LOGP_ERR_SHAPE
+    assert lb(z=FAKE + 4, zdt=_lib.LOGP_F32, ldz=151936) == _lib.LOGP_ERR_ALIGN
+    assert lb(z=FAKE, zdt=_lib.LOGP_F32, ldz=151937) == _lib.LOGP_ERR_ALIGN
     assert lb(ent=FAKE) == _lib.LOGP_ERR_NULL
     assert lb(tdt=5) == _lib.LOGP_ERR_DTYPE
     assert lb(out=2) == _lib.LOGP_ERR_DTYPE

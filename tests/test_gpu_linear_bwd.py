@@ -191,3 +191,52 @@ def test_int32_targets_same_bits():
     dh, dw = itl.linear_logp_bwd(h, w, t, lse, g)
     dh2, dw2 = itl.linear_logp_bwd(h, w, t.to(torch.int32), lse, g)
     assert torch.equal(bits(dh), bits(dh2)) and torch.equal(bits(dw), bits(dw2))
+
+
+@pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (257, 64, 300), (129, 512, 529)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_saved_logits_same_bits(n, hd, v, out_dtype):
+    """Reading the forward's saved fp32 logits instead of recomputing h W^T
+    gives dh and dW with the same bits (with temperature and entropy too).
+    Unpadded rows of a ragged V are refused (16-byte rows are required)."""
+    h, w, t, g = _case(n, hd, v, seed=n + 3 * v)
+    gh = synth.normal_matrix(1, n, 1.0, torch.float32, seed=n + 9)[0].to(dev())
+    for temp, with_ent in ((1.0, False), (0.8, True)):
+        # rows of the saved logits padded to 16 bytes (a ragged V would not be)
+        zbuf = torch.empty(n, (v + 3) // 4 * 4, dtype=torch.float32, device=dev())[:, :v]
+        out = itl.linear_logp_fwd(h, w, t, temperature=temp, return_entropy=with_ent,
+                                  return_logits=True, logits_dtype=torch.float32,
+                                  logits_out=zbuf)
+        lse, z = out[1], out[-1]
+        ent = out[2] if with_ent else None
+        kw = dict(out_dtype=out_dtype, temperature=temp, entropy=ent,
+                  grad_entropy=gh if with_ent else None)
+        dh0, dw0 = itl.linear_logp_bwd(h, w, t, lse, g, **kw)
+        dh1, dw1 = itl.linear_logp_bwd(h, w, t, lse, g, saved_logits=z, **kw)
+        assert torch.equal(dh0, dh1) and torch.equal(dw0, dw1), (temp, with_ent)
+    if v % 4:
+        _, lse, z = itl.linear_logp_fwd(h, w, t, return_logits=True, logits_dtype=torch.float32)
+        with pytest.raises(itl.LogpError):
+            itl.linear_logp_bwd(h, w, t, lse, g, saved_logits=z)
+
+
+def test_saved_bf16_logits_rounded_variant():
+    """In the bf16-rounded contract the bf16 logits output is exactly z, so
+    reading it gives the recomputed gradient's bits; the autograd function
+    with save_logits matches the default one."""
+    c = synth.lattice_linear(seed=93, n=200, h=256, v=1000, device=dev(), ignore_frac=0.05)
+    h, w, t = c["hidden"], c["weight"], c["targets"]
+    g = synth.normal_matrix(1, 200, 1.0, torch.float32, seed=94)[0].to(dev())
+    _, lse, z = itl.linear_logp_fwd(h, w, t, round_logits=True, return_logits=True)
+    assert z.dtype == torch.bfloat16
+    dh0, dw0 = itl.linear_logp_bwd(h, w, t, lse, g, round_logits=True)
+    dh1, dw1 = itl.linear_logp_bwd(h, w, t, lse, g, round_logits=True, saved_logits=z)
+    assert torch.equal(dh0, dh1) and torch.equal(dw0, dw1)
+    for rnd in (False, True):
+        grads = []
+        for save in (False, True):
+            hh = h.clone().requires_grad_(True)
+            ww = w.clone().requires_grad_(True)
+            (itl.linear_logp(hh, ww, t, round_logits=rnd, save_logits=save) * g).sum().backward()
+            grads.append((hh.grad, ww.grad))
+        assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
