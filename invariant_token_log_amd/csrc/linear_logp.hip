@@ -27,10 +27,10 @@
 //     eight waves of 128 x 64 (two per SIMD, so each hides the other's LDS
 //     and barrier latency), operands streamed global -> LDS by direct 16-byte
 //     LDS loads through a four-stage ring;
-//   * linear_stats_narrow (N <= 128): the 128 x 256 narrow tile of
-//     mfma_gemm.h, eight waves of 32 x 128, the same direct loads through a
-//     five-stage ring (few rows give little arithmetic per weight byte, so
-//     the tile is bound by the bytes it keeps in flight).
+//   * linear_stats_narrow<64 / 128> (N <= 64 / N <= 128): the narrow tiles
+//     of mfma_gemm.h, eight waves of 16 / 32 x 128, the same direct loads
+//     (few rows give little arithmetic per weight byte, so these tiles are
+//     bound by the bytes they keep in flight).
 #include "launch.h"
 #include "logp_device.h"
 #include "mfma_gemm.h"
@@ -308,22 +308,26 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
 }
 
 // ---------------------------------------------------------------------------
-// linear_stats_narrow: BM = 128 for few hidden rows (N <= 128), the narrow
-// mfma_gemm.h tile with five direct-load stages; same K walk and epilogue
-// tree as linear_stats_dma, so a row gets the same bits on either path.
+// linear_stats_narrow<ROWS>: the narrow mfma_gemm.h tiles for few hidden rows
+// (N <= 64: ROWS = 64, two workgroups per CU; N <= 128: ROWS = 128); same K
+// walk and epilogue tree as linear_stats_dma, so a row gets the same bits on
+// every path.
 // ---------------------------------------------------------------------------
+template <int ROWS>
 struct SmemNarrow {
-  gemm::StagesNarrow st;  // 120 KiB
-  Reduce<128> rd;
+  gemm::StagesNarrow<ROWS> st;
+  Reduce<ROWS> rd;
 };
 
+template <int ROWS>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
     float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
+  constexpr int MI = gemm::NarrowCfg<ROWS>::kMI;
   const Targets targets{tgt, tgt32};
-  __shared__ __align__(16) SmemNarrow sm;
+  __shared__ __align__(16) SmemNarrow<ROWS> sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -333,21 +337,20 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
   const int logical = xcd_logical(blockIdx.x, mblocks * vblocks);
   const int mb = logical % mblocks;
   const int vb = logical / mblocks;
-  const int64_t m0 = static_cast<int64_t>(mb) * gemm::kNarrowRows;
+  const int64_t m0 = static_cast<int64_t>(mb) * ROWS;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
-  if (tid < gemm::kNarrowRows)
-    sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
+  if (tid < ROWS) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
 
-  f32x4 acc[2][8];
+  f32x4 acc[MI][8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  gemm::mainloop_narrow(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
-                        static_cast<int>(hdim / BK), acc);
+  gemm::mainloop_narrow<ROWS>(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
+                              static_cast<int>(hdim / BK), acc);
   __syncthreads();
-  stats_epilogue<2, 8, 128, kDmaThreads>(acc, sm.rd, wm * 32, wn * 128, li, g, tid, m0, v0, vb,
-                                         vblocks, n, v, pm, ps, pt, ex);
+  stats_epilogue<MI, 8, ROWS, kDmaThreads>(acc, sm.rd, wm * (ROWS / 4), wn * 128, li, g, tid,
+                                           m0, v0, vb, vblocks, n, v, pm, ps, pt, ex);
 }
 
 }  // namespace
@@ -359,10 +362,14 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                             hipStream_t s) {
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
   const LinearExtras ex{inv_t, round_bf16, pw, z, z_bf16, ld_z};
-  if (n <= gemm::kNarrowRows) {
-    hipLaunchKernelGGL(linear_stats_narrow, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden, ld_h,
-                       weight, ld_w, n, h, v, 1, vblocks, targets.p, targets.is32, ignore, pm,
-                       ps, pt, ex);
+  if (n <= 64) {
+    hipLaunchKernelGGL(linear_stats_narrow<64>, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden,
+                       ld_h, weight, ld_w, n, h, v, 1, vblocks, targets.p, targets.is32, ignore,
+                       pm, ps, pt, ex);
+  } else if (n <= 128) {
+    hipLaunchKernelGGL(linear_stats_narrow<128>, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden,
+                       ld_h, weight, ld_w, n, h, v, 1, vblocks, targets.p, targets.is32, ignore,
+                       pm, ps, pt, ex);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     hipLaunchKernelGGL(linear_stats_dma, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,

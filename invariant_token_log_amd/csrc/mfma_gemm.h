@@ -162,32 +162,53 @@ __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Narrow tile for few hidden rows: 128 A rows x 256 B rows, the same MFMA
-// form, K walk and LDS chunk layout as the 256 x 256 tile, so every output
-// gets the same bits.  8 waves; wave w covers rows (w / 2) * 32 + [0, 32) and
-// columns (w % 2) * 128 + [0, 128) as accN[i][j][q] = C[row0 + i*16 + 4*g +
-// q][col0 + j*16 + li].  Five stages (four K steps in flight, 96 KiB per
-// workgroup) because with so little arithmetic per byte the tile is bound by
-// how many bytes it keeps in flight.  Wave w fills A block w and B blocks w,
-// w + 8 of every stage.
+// Narrow tiles for few hidden rows: ROWS (64 or 128) A rows x 256 B rows,
+// the same MFMA form, K walk and LDS chunk layout as the 256 x 256 tile, so
+// every output gets the same bits.  8 waves; wave w covers rows
+// (w / 2) * (ROWS / 4) + [0, ROWS / 4) and columns (w % 2) * 128 + [0, 128)
+// as acc[i][j][q] = C[row0 + i*16 + 4*g + q][col0 + j*16 + li], i < ROWS /
+// 64.  With so little arithmetic per weight byte the tile is bound by the
+// bytes it keeps in flight: ROWS = 128 runs five stages (96 KiB in flight,
+// one workgroup per CU); ROWS = 64 runs three stages of 20 KiB so that two
+// workgroups share a CU (594 vocabulary tiles then take two rounds of 512
+// instead of three of 256).  Wave w fills B blocks w, w + 8 and, for w <
+// ROWS / 16, A block w of every stage.
 // ---------------------------------------------------------------------------
-constexpr int kNarrowRows = 128;
-constexpr int kNarrowStages = 5;
-
-struct StagesNarrow {
-  uint16_t a[kNarrowStages][kNarrowRows * kK];  // 8 KiB each
-  uint16_t b[kNarrowStages][kTile * kK];        // 16 KiB each
+template <int ROWS>
+struct NarrowCfg {
+  static constexpr int kStages = ROWS == 128 ? 5 : 3;
+  static constexpr int kMI = ROWS / 64;
 };
 
-// acc += A[a_row0 + 0..127, 0..K) * B[b_row0 + 0..255, 0..K)^T, K = ksteps * 32
-// (ksteps even, >= 2); rows at or past a_rows / b_rows are read from the last
-// valid row.  All 512 threads must call; on return every direct load has
-// landed and the stages may be reused after a barrier.
-__device__ __forceinline__ void mainloop_narrow(StagesNarrow& sm, const uint16_t* __restrict__ A,
-                                                int64_t lda, int64_t a_row0, int64_t a_rows,
+template <int ROWS>
+struct StagesNarrow {
+  uint16_t a[NarrowCfg<ROWS>::kStages][ROWS * kK];
+  uint16_t b[NarrowCfg<ROWS>::kStages][kTile * kK];  // 16 KiB each
+};
+
+// s_waitcnt vmcnt(N) with N a template constant.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// acc += A[a_row0 + 0..ROWS-1, 0..K) * B[b_row0 + 0..255, 0..K)^T, K =
+// ksteps * 32 (ksteps even, >= 2); rows at or past a_rows / b_rows are read
+// from the last valid row.  All 512 threads must call; on return every
+// direct load has landed and the stages may be reused after a barrier.
+template <int ROWS>
+__device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
+                                                const uint16_t* __restrict__ A, int64_t lda,
+                                                int64_t a_row0, int64_t a_rows,
                                                 const uint16_t* __restrict__ B, int64_t ldb,
                                                 int64_t b_row0, int64_t b_rows, int ksteps,
-                                                f32x4 (&acc)[2][8]) {
+                                                f32x4 (&acc)[NarrowCfg<ROWS>::kMI][8]) {
+  constexpr int S = NarrowCfg<ROWS>::kStages;
+  constexpr int MI = NarrowCfg<ROWS>::kMI;
   const int tid = threadIdx.x;
   const int lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -195,56 +216,53 @@ __device__ __forceinline__ void mainloop_narrow(StagesNarrow& sm, const uint16_t
   const int li = lane % 16, g = lane / 16;
   const int lrow = lane / 4;
   const int lk = ((lane % 4) ^ swz(lrow)) * 8;
-  const uint16_t* a0 = A + min(a_row0 + wave * 16 + lrow, a_rows - 1) * lda + lk;
+  const bool has_a = wave < ROWS / 16;  // uniform
+  const uint16_t* a0 = A + min(a_row0 + (has_a ? wave : 0) * 16 + lrow, a_rows - 1) * lda + lk;
   const uint16_t* b0 = B + min(b_row0 + wave * 16 + lrow, b_rows - 1) * ldb + lk;
   const uint16_t* b1 = B + min(b_row0 + (wave + 8) * 16 + lrow, b_rows - 1) * ldb + lk;
-  const int aoff = (wm * 32 + li) * kK + ((g ^ swz(li)) * 8);
+  const int aoff = (wm * (ROWS / 4) + li) * kK + ((g ^ swz(li)) * 8);
   const int boff = (wn * 128 + li) * kK + ((g ^ swz(li)) * 8);
   constexpr int kBlk = 16 * kK;
   auto issue_step = [&](int s, int step) {
     const int64_t k0 = static_cast<int64_t>(step) * kK;
-    __builtin_amdgcn_global_load_lds(a0 + k0, sm.a[s] + wave * kBlk, 16, 0, 0);
+    if (has_a) __builtin_amdgcn_global_load_lds(a0 + k0, sm.a[s] + wave * kBlk, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(b0 + k0, sm.b[s] + wave * kBlk, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(b1 + k0, sm.b[s] + (wave + 8) * kBlk, 16, 0, 0);
   };
   // Iteration kt: MFMAs of step kt on fragments in registers, fragment reads
-  // of step kt+1, direct loads of step kt+5 (kt+2 .. kt+4 in flight).  Every
-  // iteration issues 3 loads per wave, so the wait counts are constant; past
-  // the end the loads re-fetch the last K step into a stage no longer read.
-  for (int st = 0; st < kNarrowStages; ++st) issue_step(st, st < ksteps ? st : ksteps - 1);
-  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  // of step kt+1, direct loads of step kt+S (kt+2 .. kt+S-1 in flight).
+  // Every iteration issues the same loads per wave (3 with an A block, else
+  // 2), so the wait counts are constant per wave; past the end the loads
+  // re-fetch the last K step into a stage no longer read.
+  for (int st = 0; st < S; ++st) issue_step(st, st < ksteps ? st : ksteps - 1);
+  if (has_a)
+    wait_vm<(S - 1) * 3>();
+  else
+    wait_vm<(S - 1) * 2>();
   __builtin_amdgcn_s_barrier();
-  bf16x8 xa[2], xb[8], ya[2], yb[8];
+  bf16x8 xa[MI], xb[8], ya[MI], yb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(sm.b[0] + boff + j * 16 * kK);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) xa[i] = *reinterpret_cast<const bf16x8*>(sm.a[0] + aoff + i * 16 * kK);
+  for (int i = 0; i < MI; ++i) xa[i] = *reinterpret_cast<const bf16x8*>(sm.a[0] + aoff + i * 16 * kK);
   int cur = 0;  // stage of step kt
 #define ITL_NSTEP(CA, CB, NA, NB, KT)                                                        \
   {                                                                                          \
-    asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)" ::: "memory");                              \
+    if (has_a)                                                                               \
+      wait_vm_lgkm0<(S - 2) * 3>();                                                          \
+    else                                                                                     \
+      wait_vm_lgkm0<(S - 2) * 2>();                                                          \
     __builtin_amdgcn_s_barrier();                                                            \
-    const int nxt = cur + 1 == kNarrowStages ? 0 : cur + 1;                                  \
-    issue_step(cur, (KT) + kNarrowStages < ksteps ? (KT) + kNarrowStages : ksteps - 1);      \
+    const int nxt = cur + 1 == S ? 0 : cur + 1;                                              \
+    issue_step(cur, (KT) + S < ksteps ? (KT) + S : ksteps - 1);                              \
     _Pragma("unroll") for (int j = 0; j < 8; ++j)                                            \
       NB[j] = *reinterpret_cast<const bf16x8*>(sm.b[nxt] + boff + j * 16 * kK);              \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
       NA[i] = *reinterpret_cast<const bf16x8*>(sm.a[nxt] + aoff + i * 16 * kK);              \
     cur = nxt;                                                                               \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                            \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
       _Pragma("unroll") for (int j = 0; j < 8; ++j)                                          \
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0); \
-    /* 3 x (1 direct load, 3 x (1 MFMA, 1 fragment read)), 1 MFMA + 1 read, 6 MFMAs */      \
-    _Pragma("unroll") for (int u = 0; u < 3; ++u) {                                          \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
-      _Pragma("unroll") for (int w = 0; w < 3; ++w) {                                        \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
-      }                                                                                      \
-    }                                                                                        \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);                                       \
   }
   for (int kt = 0; kt < ksteps; kt += 2) {
     ITL_NSTEP(xa, xb, ya, yb, kt)

@@ -96,14 +96,16 @@ def test_int32_targets_same_bits():
 
 
 def test_narrow_and_wide_tiles_same_bits():
-    """N <= 128 runs the 128-row tile, N > 128 the 256-row tile: the same rows
-    get the same bits from both (logp, lse, entropy and the logits output)."""
+    """N <= 64 runs the 64-row tile, N <= 128 the 128-row tile, N > 128 the
+    256-row tile: the same rows get the same bits from all three (logp, lse,
+    entropy and the logits output)."""
     c = synth.qwen3_linear(seed=91, n=129, h=512, v=3000, device=dev(), ignore_frac=0.05)
     h, w, t = c["hidden"], c["weight"], c["targets"]
     wide = itl.linear_logp_fwd(h, w, t, return_entropy=True, return_logits=True,
                                logits_dtype=torch.float32)
-    narrow = itl.linear_logp_fwd(h[:128].contiguous(), w, t[:128].contiguous(),
-                                 return_entropy=True, return_logits=True,
-                                 logits_dtype=torch.float32)
-    for a, b in zip(wide, narrow):
-        assert torch.equal(bits(a[:128]), bits(b))
+    for rows in (128, 65, 64, 1):
+        narrow = itl.linear_logp_fwd(h[:rows].contiguous(), w, t[:rows].contiguous(),
+                                     return_entropy=True, return_logits=True,
+                                     logits_dtype=torch.float32)
+        for a, b in zip(wide, narrow):
+            assert torch.equal(bits(a[:rows]), bits(b)), rows
