@@ -4,7 +4,8 @@
 // Invariant LogP", Batch-Invariance: the logit gradient is g * (onehot - p)).
 //
 //   z  = h W^T                (recomputed: the forward's MFMA tile and K walk,
-//                              so z has the forward's bits)
+//                              so z has the forward's bits; or read from the
+//                              forward's saved logits, the same values)
 //   dz = RNE_bf16(g * (onehot(t) - exp(z - lse)))   (0 on ignored and padded rows)
 //   dh = dz W                 (fp32 accumulators, K = vocabulary, ascending)
 //   dW = dz^T h               (fp32 accumulators, K = tokens, ascending)
@@ -14,10 +15,12 @@
 // single ascending K walk with no split, so dh[r] depends only on row r (batch
 // invariant) and dW is deterministic for a given token order.
 //
-// Kernels (all on the 256 x 256 tile of mfma_gemm.h):
+// Kernels (the products on the 256 x 256 tile of mfma_gemm.h):
 //   linear_dz_kernel  : h x W^T tile -> dz in registers -> transposed, then
 //                       row-major LDS tile -> dz^T [Vp, Np] and dz [Np, Vp]
 //                       (bf16, whole 512-byte row segments per store pass);
+//   linear_dz_saved_kernel: the same dz and dz^T from saved logits, 64 x 64
+//                       tiles streamed through LDS;
 //   transpose_pad_bf16: W [V, H] -> W^T [H, Vp], h [N, H] -> h^T [H, Np], zero
 //                       padded, so that both products see K-contiguous operands;
 //   gemm_out_kernel   : C = A B^T with fp32 or RNE-bf16 output.
