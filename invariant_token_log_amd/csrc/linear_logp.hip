@@ -200,14 +200,71 @@ struct LinearExtras {
   void* z;          // [n, ld_z] unscaled logits (fp32 or bf16), or null
   int32_t z_bf16;
   int64_t ld_z;
+  int32_t z_vec;    // z and its rows are 16-byte aligned: staged 16-byte stores
 };
 
-template <int MI, int NJ, int BM, int NT>
-__device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>& rd, int row0,
-                                               int col0, int li, int g, int tid, int64_t m0,
-                                               int64_t v0, int vb, int vblocks, int64_t n,
-                                               int64_t v, float* pm, float* ps, float* pt,
-                                               const LinearExtras& ex) {
+// Logits output through LDS: the tile's accumulators go to `scratch` (the
+// main loop's stages, free by now) a row chunk at a time, then leave as
+// whole 16-byte pieces along the rows (the accumulator layout would store
+// 4 or 2 bytes per lane).  RPC rows per chunk: the largest power-of-two part
+// of the tile that fits.
+template <typename E, int MI, int NJ, int BM, int NT, int SCRATCH>
+__device__ __forceinline__ void store_logits_staged(const f32x4 (&acc)[MI][NJ], void* scratch,
+                                                    int row0, int col0, int li, int g, int tid,
+                                                    int64_t m0, int64_t v0, int64_t n,
+                                                    int64_t v, E* z, int64_t ld_z) {
+  constexpr int kPer = 16 / static_cast<int>(sizeof(E));  // elements per 16-byte piece
+  constexpr int kStride = BN + kPer;                       // padded LDS row
+  constexpr int kRowBytes = kStride * static_cast<int>(sizeof(E));
+  constexpr int RPC = BM * kRowBytes <= SCRATCH       ? BM
+                      : BM / 2 * kRowBytes <= SCRATCH ? BM / 2
+                      : BM / 4 * kRowBytes <= SCRATCH ? BM / 4
+                                                      : BM / 8;
+  static_assert(RPC * kRowBytes <= SCRATCH && RPC % 16 == 0, "logits chunk does not fit");
+  E* tile = static_cast<E*>(scratch);
+  for (int c = 0; c < BM / RPC; ++c) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int lr0 = row0 + i * 16 - c * RPC;  // uniform
+      if (lr0 < 0 || lr0 >= RPC) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const float x = acc[i][j][q];
+          E e;
+          if constexpr (sizeof(E) == 2)
+            e = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+          else
+            e = x;
+          tile[(lr0 + 4 * g + q) * kStride + col0 + j * 16 + li] = e;
+        }
+    }
+    __syncthreads();
+    constexpr int kCpr = BN / kPer;  // pieces per row
+    for (int idx = tid; idx < RPC * kCpr; idx += NT) {
+      const int lr = idx / kCpr, pc = (idx % kCpr) * kPer;
+      const int64_t r = m0 + c * RPC + lr, col = v0 + pc;
+      if (r >= n) continue;
+      E* dst = z + r * ld_z + col;
+      const E* src = tile + lr * kStride + pc;
+      if (col + kPer <= v) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int u = 0; u < kPer; ++u)
+          if (col + u < v) dst[u] = src[u];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int MI, int NJ, int BM, int NT, int SCRATCH>
+__device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>& rd, void* scratch,
+                                               int row0, int col0, int li, int g, int tid,
+                                               int64_t m0, int64_t v0, int vb, int vblocks,
+                                               int64_t n, int64_t v, float* pm, float* ps,
+                                               float* pt, const LinearExtras& ex) {
   // The bf16-rounded variant: z becomes RNE_bf16(accumulator), widened
   // exactly, before anything reads it (logits output, temperature, every
   // statistic and the target copy).
@@ -222,7 +279,16 @@ __device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>&
   }
   // The unscaled logits, when asked for: they are the accumulators as they
   // are (the statistics below do not change them).
-  if (ex.z) {
+  if (ex.z && ex.z_vec) {
+    if (ex.z_bf16)
+      store_logits_staged<uint16_t, MI, NJ, BM, NT, SCRATCH>(acc, scratch, row0, col0, li, g, tid,
+                                                             m0, v0, n, v,
+                                                             static_cast<uint16_t*>(ex.z), ex.ld_z);
+    else
+      store_logits_staged<float, MI, NJ, BM, NT, SCRATCH>(acc, scratch, row0, col0, li, g, tid, m0,
+                                                          v0, n, v, static_cast<float*>(ex.z),
+                                                          ex.ld_z);
+  } else if (ex.z) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -303,7 +369,8 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   gemm::mainloop(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v, static_cast<int>(hdim / BK),
                  acc);
   __syncthreads();
-  stats_epilogue<8, 4, 256, kDmaThreads>(acc, sm.rd, wm * 128, wn * 64, li, g, tid, m0, v0, vb,
+  stats_epilogue<8, 4, 256, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * 128, wn * 64, li,
+                                                        g, tid, m0, v0, vb,
                                          vblocks, n, v, pm, ps, pt, ex);
 }
 
@@ -349,7 +416,8 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
   gemm::mainloop_narrow<ROWS>(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
                               static_cast<int>(hdim / BK), acc);
   __syncthreads();
-  stats_epilogue<MI, 8, ROWS, kDmaThreads>(acc, sm.rd, wm * (ROWS / 4), wn * 128, li, g, tid,
+  stats_epilogue<MI, 8, ROWS, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * (ROWS / 4),
+                                                          wn * 128, li, g, tid,
                                            m0, v0, vb, vblocks, n, v, pm, ps, pt, ex);
 }
 
@@ -361,7 +429,9 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                             int32_t round_bf16, float* pw, void* z, int32_t z_bf16, int64_t ld_z,
                             hipStream_t s) {
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
-  const LinearExtras ex{inv_t, round_bf16, pw, z, z_bf16, ld_z};
+  const int32_t z_vec = z && reinterpret_cast<uintptr_t>(z) % 16 == 0 &&
+                        (ld_z * (z_bf16 ? 2 : 4)) % 16 == 0;
+  const LinearExtras ex{inv_t, round_bf16, pw, z, z_bf16, ld_z, z_vec};
   if (n <= 64) {
     hipLaunchKernelGGL(linear_stats_narrow<64>, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden,
                        ld_h, weight, ld_w, n, h, v, 1, vblocks, targets.p, targets.is32, ignore,
