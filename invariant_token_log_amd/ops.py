@@ -89,10 +89,11 @@ def logp_fwd(logits, targets, ignore_index=-100, tile_width=4096, num_shards=1,
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = L.logp_fwd(x2.data_ptr(), _dtype_code(logits), n, v, ld, t1.data_ptr(),
-                    _INDEX[t1.dtype], int(ignore_index), int(tile_width), int(num_shards),
-                    int(bool(validate)), logp_out.data_ptr(), lse_out.data_ptr(), _ptr(ent),
-                    _ptr(workspace), ws_len, _stream(dev))
+    with torch.cuda.device(dev):
+        st = L.logp_fwd(x2.data_ptr(), _dtype_code(logits), n, v, ld, t1.data_ptr(),
+                        _INDEX[t1.dtype], int(ignore_index), int(tile_width), int(num_shards),
+                        int(bool(validate)), logp_out.data_ptr(), lse_out.data_ptr(), _ptr(ent),
+                        _ptr(workspace), ws_len, _stream(dev))
     check("logp_fwd", st)
     if return_entropy:
         return logp_out.view(targets.shape), lse_out, ent
@@ -118,10 +119,11 @@ def logp_bwd(logits, targets, lse, grad_logp, ignore_index=-100, tile_width=4096
     d2, v2, ld_out = _rows(dlogits_out)
     if v2 != v or d2.shape[0] != n or dlogits_out.dtype != logits.dtype:
         raise ValueError("dlogits_out must match the logits shape and dtype")
-    st = _lib.lib().logp_bwd(x2.data_ptr(), _dtype_code(logits), n, v, ld, t1.data_ptr(),
-                             _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                             lse.data_ptr(), g.data_ptr(), _ptr(ent), _ptr(gent),
-                             d2.data_ptr(), ld_out, _stream(logits.device))
+    with torch.cuda.device(logits.device):
+        st = _lib.lib().logp_bwd(x2.data_ptr(), _dtype_code(logits), n, v, ld, t1.data_ptr(),
+                                 _INDEX[t1.dtype], int(ignore_index), int(tile_width),
+                                 lse.data_ptr(), g.data_ptr(), _ptr(ent), _ptr(gent),
+                                 d2.data_ptr(), ld_out, _stream(logits.device))
     check("logp_bwd", st)
     return dlogits_out
 
@@ -179,12 +181,13 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
     need = L.linear_logp_fwd_workspace_bytes(n, v, tile_width)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = L.linear_logp_fwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
-                           t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                           float(temperature), _rounding(round_logits), logp_out.data_ptr(),
-                           lse_out.data_ptr(), _ptr(ent), _ptr(z), _DTYPES[logits_dtype],
-                           (z.stride(0) if n > 1 else v) if z is not None else 0,
-                           workspace.data_ptr(), workspace.numel(), _stream(dev))
+    with torch.cuda.device(dev):
+        st = L.linear_logp_fwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
+                               t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
+                               float(temperature), _rounding(round_logits), logp_out.data_ptr(),
+                               lse_out.data_ptr(), _ptr(ent), _ptr(z), _DTYPES[logits_dtype],
+                               (z.stride(0) if n > 1 else v) if z is not None else 0,
+                               workspace.data_ptr(), workspace.numel(), _stream(dev))
     check("linear_logp_fwd", st)
     out = (logp_out, lse_out)
     if return_entropy:
@@ -235,16 +238,17 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_len = workspace.numel() if workspace is not None else 0
-    st = L.linear_logp_bwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
-                           t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                           float(temperature), _rounding(round_logits), _ptr(z),
-                           _DTYPES[z.dtype] if z is not None else 0,
-                           max(z.stride(0), v) if z is not None else 0, lse.data_ptr(),
-                           g.data_ptr(), _ptr(ent),
-                           _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
-                           (dh.stride(0) if n > 1 else h) if dh is not None else 0,
-                           _ptr(dw), (dw.stride(0) if v > 1 else h) if dw is not None else 0,
-                           _ptr(workspace), ws_len, _stream(dev))
+    with torch.cuda.device(dev):
+        st = L.linear_logp_bwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
+                               t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
+                               float(temperature), _rounding(round_logits), _ptr(z),
+                               _DTYPES[z.dtype] if z is not None else 0,
+                               max(z.stride(0), v) if z is not None else 0, lse.data_ptr(),
+                               g.data_ptr(), _ptr(ent),
+                               _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
+                               (dh.stride(0) if n > 1 else h) if dh is not None else 0,
+                               _ptr(dw), (dw.stride(0) if v > 1 else h) if dw is not None else 0,
+                               _ptr(workspace), ws_len, _stream(dev))
     check("linear_logp_bwd", st)
     return dh, dw
 
