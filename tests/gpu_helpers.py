@@ -8,6 +8,10 @@ import torch
 # ATOL + RTOL * |ref| (the bound the logp path is held to).
 ATOL = 1e-5
 RTOL = 1e-5
+# The hardware exponential returns no subnormals: exp values below the
+# smallest normal float32 come out as +0, so a gradient element may be +-0
+# where the exact one is below |g| * FLT_MIN.
+FLT_MIN = 2.0 ** -126
 # Relative tolerance of fp32 dlogits against the unrounded float64 gradient
 # (bf16 dlogits are checked against their two bf16 neighbours instead, since
 # rounding to bf16 alone moves a value by up to 2^-8 = 3.9e-3 relative).
@@ -68,8 +72,9 @@ def assert_grad_parity(d_gpu, d_ref, x, lse_ref, g, targets, ignore_index=-100, 
     """dlogits against the unrounded float64 gradient d64.
 
     The fp32 value d32 the kernel rounds may differ from d64 by the forward's
-    lse tolerance carried through exp plus a few fp32 ulp:
-        budget = |g| * p * (ATOL + RTOL * |x - lse|) + 1e-6 * |d64|.
+    lse tolerance carried through exp plus a few fp32 ulp, and by |g| times
+    the smallest normal float32 where exp flushes to +0:
+        budget = |g| * p * (ATOL + RTOL * |x - lse|) + 1e-6 * |d64| + |g| * FLT_MIN.
     fp32 outputs: |gpu - d64| <= BWD_RTOL * |d64| + budget.
     bf16 outputs: rounding to bf16 alone moves a value by up to 2^-8
     relative, more than BWD_RTOL, so the check is sharper instead: RNE is
@@ -82,13 +87,15 @@ def assert_grad_parity(d_gpu, d_ref, x, lse_ref, g, targets, ignore_index=-100, 
     active = t != ignore_index
     p = np.exp(x - lse_ref[:, None])
     gg = np.abs(np.asarray(g, dtype=np.float64).reshape(-1))[:, None]
-    budget = gg * p * (ATOL + RTOL * np.abs(x - lse_ref[:, None])) + 1e-6 * np.abs(d_ref)
+    budget = (gg * p * (ATOL + RTOL * np.abs(x - lse_ref[:, None])) + 1e-6 * np.abs(d_ref)
+              + gg * FLT_MIN)
     if d_gpu.dtype == torch.bfloat16:
         ok = (d >= rne_bf16(d_ref - budget)) & (d <= rne_bf16(d_ref + budget))
     elif d_gpu.dtype == torch.float16:
         # numpy's float64 -> float16 cast rounds to nearest even, subnormals included
-        lo = (d_ref - budget).astype(np.float16).astype(np.float64)
-        hi = (d_ref + budget).astype(np.float16).astype(np.float64)
+        with np.errstate(over="ignore"):  # bounds past the float16 range become +-inf
+            lo = (d_ref - budget).astype(np.float16).astype(np.float64)
+            hi = (d_ref + budget).astype(np.float16).astype(np.float64)
         ok = (d >= lo) & (d <= hi)
     else:
         ok = np.abs(d - d_ref) <= BWD_RTOL * np.abs(d_ref) + budget

@@ -1,0 +1,115 @@
+"""Randomised GPU parity and invariance (hypothesis, fixed derivation so runs
+repeat): random small shapes, dtypes, tile widths, shard counts, row
+strides, target index types, ignored and out-of-range-free targets, logit
+scales, entropy and temperature, each checked against the float64 oracle
+with the bounds of the targeted tests, plus bitwise invariance of a row
+computed alone and of sharded against unsharded forwards."""
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import invariant_token_log_amd as itl
+import oracle
+import synth
+from gpu_helpers import assert_grad_parity, assert_logp_parity, bits, dev, to_np
+from test_gpu_entropy import _ent_ok, _grad_ent_ok
+
+pytestmark = pytest.mark.gpu
+
+SETTINGS = settings(max_examples=40, deadline=None, derandomize=True, database=None,
+                    suppress_health_check=list(HealthCheck))
+
+
+@st.composite
+def stream_cases(draw):
+    dtype = draw(st.sampled_from([torch.float32, torch.bfloat16, torch.float16]))
+    unit = 256 if dtype == torch.float32 else 512  # widths: unit x 1, 2, 4, 8, 16
+    w = draw(st.sampled_from([unit * k for k in (1, 2, 4, 8, 16)]))
+    v = draw(st.integers(1, 6000))
+    n = draw(st.integers(1, 48))
+    shards = draw(st.sampled_from([s for s in (1, 2, 3, 4) if v % s == 0]))
+    pad = draw(st.sampled_from([0, 0, 8, 13]))
+    scale = draw(st.sampled_from([0.1, 3.0, 20.0]))
+    n_ign = draw(st.integers(0, n))
+    tdt = draw(st.sampled_from([torch.int64, torch.int32]))
+    ent = draw(st.booleans())
+    seed = draw(st.integers(0, 2 ** 30))
+    return dict(dtype=dtype, w=w, v=v, n=n, shards=shards, pad=pad, scale=scale, n_ign=n_ign,
+                tdt=tdt, ent=ent, seed=seed)
+
+
+@SETTINGS
+@given(stream_cases())
+def test_fuzz_streaming(c):
+    n, v, dtype = c["n"], c["v"], c["dtype"]
+    base = synth.normal_matrix(n, v + c["pad"], c["scale"], dtype, seed=c["seed"]).to(dev())
+    x = base[:, :v]  # row stride v + pad
+    ign = torch.randperm(n, generator=torch.Generator().manual_seed(c["seed"]))[:c["n_ign"]]
+    t = synth.uniform_targets(n, v, seed=c["seed"] + 1, ignore_rows=ign).to(dev()).to(c["tdt"])
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=c["seed"] + 2)[0].to(dev())
+    what = str({k: (str(val) if k in ("dtype", "tdt") else val) for k, val in c.items()})
+    out = itl.logp_fwd(x, t, -100, c["w"], num_shards=c["shards"], return_entropy=c["ent"])
+    x64 = to_np(x)
+    tn = t.cpu().numpy().astype(np.int64)
+    ref_logp, ref_lse = oracle.logp_fwd(x64, tn)
+    assert_logp_parity(out[0], out[1], ref_logp, ref_lse, t, what=what)
+    if c["ent"]:
+        _ent_ok(out[2], x64, tn, what)
+    # sharded and unsharded forwards agree bit for bit; a row alone too
+    one = itl.logp_fwd(x, t, -100, c["w"], return_entropy=c["ent"])
+    for a, b in zip(out, one):
+        assert torch.equal(bits(a), bits(b)), what
+    r = n // 2
+    alone = itl.logp_fwd(x[r:r + 1], t[r:r + 1], -100, c["w"], return_entropy=c["ent"])
+    for a, b in zip(one, alone):
+        assert torch.equal(bits(a)[r:r + 1], bits(b)), what
+    # backward against the oracle's gradient at the oracle's lse
+    if c["ent"]:
+        gh = synth.normal_matrix(1, n, 1.0, torch.float32, seed=c["seed"] + 3)[0].to(dev())
+        d = itl.logp_bwd(x, t, one[1], g, -100, c["w"], entropy=one[2], grad_entropy=gh)
+    else:
+        d = itl.logp_bwd(x, t, one[1], g, -100, c["w"])
+        d64 = oracle.logp_bwd(x64, tn, to_np(g), lse=ref_lse)
+    if c["ent"]:
+        _grad_ent_ok(d, x64, tn, to_np(g), to_np(gh), what)
+    else:
+        assert_grad_parity(d, d64, x64, ref_lse, to_np(g), t, what=what)
+    dalone = itl.logp_bwd(x[r:r + 1], t[r:r + 1], one[1][r:r + 1], g[r:r + 1], -100, c["w"],
+                          entropy=one[2][r:r + 1] if c["ent"] else None,
+                          grad_entropy=gh[r:r + 1] if c["ent"] else None)
+    assert torch.equal(d[r:r + 1].contiguous().view(torch.int16 if dtype != torch.float32
+                                                    else torch.int32),
+                       dalone.view(torch.int16 if dtype != torch.float32 else torch.int32)), what
+
+
+@st.composite
+def linear_cases(draw):
+    return dict(n=draw(st.integers(1, 300)), h=draw(st.sampled_from([64, 128, 256, 512])),
+                v=draw(st.integers(1, 3000)), temp=draw(st.sampled_from([1.0, 0.7, 2.0])),
+                ent=draw(st.booleans()), n_ign=draw(st.integers(0, 5)),
+                seed=draw(st.integers(0, 2 ** 30)))
+
+
+@SETTINGS
+@given(linear_cases())
+def test_fuzz_linear(c):
+    n, h, v = c["n"], c["h"], c["v"]
+    hid = synth.normal_matrix(n, h, 1.0, torch.bfloat16, seed=c["seed"]).to(dev())
+    w = synth.normal_matrix(v, h, 0.05, torch.bfloat16, seed=c["seed"] + 1).to(dev())
+    ign = torch.randperm(n, generator=torch.Generator().manual_seed(c["seed"]))[:min(c["n_ign"], n)]
+    t = synth.uniform_targets(n, v, seed=c["seed"] + 2, ignore_rows=ign).to(dev())
+    what = str(c)
+    out = itl.linear_logp_fwd(hid, w, t, temperature=c["temp"], return_entropy=c["ent"])
+    hn, wn, tn = to_np(hid), to_np(w), t.cpu().numpy()
+    ref = oracle.linear_logp_fwd(hn, wn, tn, temperature=c["temp"])
+    assert_logp_parity(out[0], out[1], *ref, t, what=what)
+    if c["ent"]:
+        _ent_ok(out[2], (hn @ wn.T) / c["temp"], tn, what)
+    r = n // 2
+    alone = itl.linear_logp_fwd(hid[r:r + 1].contiguous(), w, t[r:r + 1].contiguous(),
+                                temperature=c["temp"], return_entropy=c["ent"])
+    for a, b in zip(out, alone):
+        assert torch.equal(bits(a)[r:r + 1], bits(b)), what
