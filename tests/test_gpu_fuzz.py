@@ -113,3 +113,32 @@ def test_fuzz_linear(c):
                                 temperature=c["temp"], return_entropy=c["ent"])
     for a, b in zip(out, alone):
         assert torch.equal(bits(a)[r:r + 1], bits(b)), what
+
+
+@settings(max_examples=20, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(linear_cases())
+def test_fuzz_linear_bwd(c):
+    """dh and dW against the float64 oracle by the fused backward's bound, and
+    the saved-logits path with the same bits."""
+    from test_gpu_linear_bwd import _bounds
+
+    n, h, v = c["n"], c["h"], c["v"]
+    hid = synth.normal_matrix(n, h, 1.0, torch.bfloat16, seed=c["seed"]).to(dev())
+    w = synth.normal_matrix(v, h, 0.05, torch.bfloat16, seed=c["seed"] + 1).to(dev())
+    ign = torch.randperm(n, generator=torch.Generator().manual_seed(c["seed"]))[:min(c["n_ign"], n)]
+    t = synth.uniform_targets(n, v, seed=c["seed"] + 2, ignore_rows=ign).to(dev())
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=c["seed"] + 3)[0].to(dev())
+    what = str(c)
+    zbuf = torch.empty(n, (v + 3) // 4 * 4, dtype=torch.float32, device=dev())[:, :v]
+    _, lse, z = itl.linear_logp_fwd(hid, w, t, return_logits=True, logits_dtype=torch.float32,
+                                    logits_out=zbuf)
+    dh, dw = itl.linear_logp_bwd(hid, w, t, lse, g)
+    dh2, dw2 = itl.linear_logp_bwd(hid, w, t, lse, g, saved_logits=z)
+    assert torch.equal(dh, dh2) and torch.equal(dw, dw2), what
+    hn, wn, tn, gn = to_np(hid), to_np(w), t.cpu().numpy(), to_np(g)
+    dh64, dw64 = oracle.linear_logp_bwd(hn, wn, tn, gn)
+    _, lse64 = oracle.linear_logp_fwd(hn, wn, tn)
+    bh, bw = _bounds(hn, wn, tn, gn, lse64)
+    assert (np.abs(to_np(dh) - dh64) <= bh).all(), what
+    assert (np.abs(to_np(dw) - dw64) <= bw).all(), what
