@@ -283,7 +283,7 @@ def bench_linear(args, torch, itl, synth):
     return out, sample
 
 
-def bench_linear_bwd(args, torch, itl, synth, saved=False):
+def bench_linear_bwd(args, torch, itl, synth, saved=False, prepared=False):
     n, h, v = 4096, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB
     dev = torch.device("cuda", 0)
     c = synth.qwen3_linear(n=n, h=h, v=v, device=dev, ignore_frac=0.05)
@@ -294,6 +294,8 @@ def bench_linear_bwd(args, torch, itl, synth, saved=False):
     _, lse, *rest = itl.linear_logp_fwd(hid, wt, t, return_logits=saved,
                                         logits_dtype=torch.float32)
     z = rest[0] if saved else None
+    # prepared: W^T made once per weight version, outside the timed step
+    wtp = itl.prepare_weight(wt) if prepared else None
     dh = torch.empty(n, h, dtype=torch.float32, device=dev)
     dw = torch.empty(v, h, dtype=torch.float32, device=dev)
     ws = torch.empty(itl.lib().linear_logp_bwd_workspace_bytes(n, h, v, 256), dtype=torch.uint8,
@@ -301,7 +303,7 @@ def bench_linear_bwd(args, torch, itl, synth, saved=False):
 
     def run():
         itl.linear_logp_bwd(hid, wt, t, lse, g, dhidden_out=dh, dweight_out=dw, workspace=ws,
-                            saved_logits=z)
+                            saved_logits=z, weight_t=wtp)
 
     ramp(torch, run, args.ramp_s)
     for _ in range(args.warmup):
@@ -314,18 +316,20 @@ def bench_linear_bwd(args, torch, itl, synth, saved=False):
     return {
         "metric": "rows/s and MFMA TFLOP/s (% of peak), fused LM-head+logp backward N=4096 "
                   "H=4096 V=151936 bf16" + (", logits saved by the forward (fp32)" if saved
-                                            else ", logits recomputed"),
+                                            else ", logits recomputed")
+                  + (", prepared W^T" if prepared else ""),
         "value": round(n / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen3_8b_lm_head_linear_logp_bwd" + ("_saved" if saved else ""),
+        "config": {"workload": "qwen3_8b_lm_head_linear_logp_bwd" + ("_saved" if saved else "")
+                   + ("_prepared" if prepared else ""),
                    "n": n, "h": h, "v": v, "tile_width": 256, "outputs": "dh, dW fp32"},
         "tflops": round(tflops, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "linear_logp_bwd (all five launches: dz, two transposes, "
+                     "kernel": "linear_logp_bwd (all launches: dz, the transposes, "
                                "two products)"},
         "extra_memory_bytes": n * v * 4 if saved else 0,
     }, None
@@ -451,7 +455,8 @@ def main():
     ap.add_argument("--ramp-s", type=float, default=0.5,
                     help="untimed seconds of steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--workload", default="fwd_bwd",
-                    choices=["fwd_bwd", "fwd", "linear", "linear_bwd", "linear_bwd_saved"])
+                    choices=["fwd_bwd", "fwd", "linear", "linear_bwd", "linear_bwd_saved",
+                             "linear_bwd_prepared"])
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows for the CPU oracle baseline (0 = workload default)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
@@ -499,7 +504,9 @@ def main():
         del src, dst
     runner = {"fwd_bwd": bench_fwd_bwd, "fwd": bench_fwd, "linear": bench_linear,
               "linear_bwd": bench_linear_bwd,
-              "linear_bwd_saved": lambda *a: bench_linear_bwd(*a, saved=True)}[args.workload]
+              "linear_bwd_saved": lambda *a: bench_linear_bwd(*a, saved=True),
+              "linear_bwd_prepared": lambda *a: bench_linear_bwd(*a, prepared=True)}[
+                  args.workload]
     out, sample = runner(args, torch, itl, synth)
     if sample is not None:
         if args.workload == "fwd_bwd":

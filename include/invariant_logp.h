@@ -272,6 +272,14 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *               saved_dtype LOGP_F32, or LOGP_BF16 only with
  *               LOGP_ROUND_BF16 (where the bf16 logits are exactly z);
  *               otherwise LOGP_ERR_DTYPE.
+ *   weight_t, ld_wt
+ *               NULL: the backward transposes weight into the workspace for
+ *               dhidden.  Otherwise W^T prepared by
+ *               linear_logp_prepare_weight from this weight (ld_wt >=
+ *               round_up(v, 256), 16-byte aligned rows), used instead: the
+ *               same values, so the same bits, without the transpose (the
+ *               "prepared weights" reused while the weight does not change,
+ *               e.g. over the micro-batches of one optimiser step).
  *   lse         fp32 [n] from linear_logp_fwd.
  *   grad_logp   fp32 [n], the upstream gradient g.
  *   entropy, grad_entropy
@@ -291,11 +299,25 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
                         float temperature, int32_t logits_rounding, const void* saved_logits,
-                        int32_t saved_dtype, int64_t ld_saved, const float* lse,
-                        const float* grad_logp, const float* entropy,
-                        const float* grad_entropy, int32_t out_dtype,
+                        int32_t saved_dtype, int64_t ld_saved, const void* weight_t,
+                        int64_t ld_wt, const float* lse, const float* grad_logp,
+                        const float* entropy, const float* grad_entropy, int32_t out_dtype,
                         void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Prepared LM-head weight for the backward ("[RFC][ROCm] End-to-end
+ * optimization of bitwise VIME R/R beyond native P/P", Workstream 3: prepared
+ * [K, N] weights are reused and refreshed when the weight changes): writes
+ * W^T [h, ld_wt] bf16 from weight [v, ld_w], columns v .. round_up(v, 256) - 1
+ * zero.  h a multiple of 64, ld_wt >= round_up(v, 256) (LOGP_ERR_SHAPE),
+ * 16-byte aligned rows (LOGP_ERR_ALIGN).  The caller owns weight_t and
+ * prepares it again whenever the weight changes.  linear_logp_weight_t_bytes
+ * gives h * round_up(v, 256) * 2 (0 for arguments that are refused).
+ */
+size_t linear_logp_weight_t_bytes(int64_t v, int64_t h);
+int32_t linear_logp_prepare_weight(const void* weight, int64_t ld_w, int64_t v, int64_t h,
+                                   void* weight_t, int64_t ld_wt, void* hip_stream);
 
 /* Short English text for a status code (static storage, host memory). */
 const char* logp_status_str(int32_t status);

@@ -14,4 +14,5 @@ from .ops import (  # noqa: F401
     linear_logp_fwd,
     logp_bwd,
     logp_fwd,
+    prepare_weight,
 )

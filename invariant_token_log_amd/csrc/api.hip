@@ -226,9 +226,10 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
                         float temperature, int32_t logits_rounding, const void* saved_logits,
-                        int32_t saved_dtype, int64_t ld_saved, const float* lse,
-                        const float* grad_logp, const float* entropy,
-                        const float* grad_entropy, int32_t out_dtype, void* dhidden,
+                        int32_t saved_dtype, int64_t ld_saved, const void* weight_t,
+                        int64_t ld_wt, const float* lse, const float* grad_logp,
+                        const float* entropy, const float* grad_entropy, int32_t out_dtype,
+                        void* dhidden,
                         int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
                         size_t workspace_bytes, void* hip_stream) {
   if (n < 0 || v < 1 || h < 64 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
@@ -247,6 +248,10 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
     if (ld_saved < v) return LOGP_ERR_SHAPE;
     if (!aligned16(saved_logits, ld_saved, saved_dtype)) return LOGP_ERR_ALIGN;
   }
+  if (weight_t) {
+    if (ld_wt < (v + 255) / 256 * 256) return LOGP_ERR_SHAPE;
+    if (!aligned16(weight_t, ld_wt, LOGP_BF16)) return LOGP_ERR_ALIGN;
+  }
   if (!dhidden && !dweight) return LOGP_ERR_NULL;
   if ((dhidden && ld_dh < h) || (dweight && ld_dw < h)) return LOGP_ERR_SHAPE;
   if (n == 0 && !dweight) return LOGP_OK;
@@ -262,11 +267,32 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   itl::launch_linear_bwd(static_cast<const uint16_t*>(hidden), ld_h,
                          static_cast<const uint16_t*>(weight), ld_w, n, h, v,
                          targets_of(targets, target_dtype), ignore_index, saved_logits,
-                         saved_dtype == LOGP_BF16 ? 1 : 0, ld_saved, lse, grad_logp,
+                         saved_dtype == LOGP_BF16 ? 1 : 0, ld_saved,
+                         static_cast<const uint16_t*>(weight_t), ld_wt, lse, grad_logp,
                          inv_temperature(temperature), logits_rounding == LOGP_ROUND_BF16 ? 1 : 0,
                          entropy, grad_entropy,
                          out_dtype == LOGP_BF16, dhidden, ld_dh, dweight, ld_dw,
                          static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream));
+  return hip_status();
+}
+
+size_t linear_logp_weight_t_bytes(int64_t v, int64_t h) {
+  if (v < 1 || h < 64 || h % 64) return 0;
+  return static_cast<size_t>(h) * static_cast<size_t>((v + 255) / 256 * 256) * 2;
+}
+
+int32_t linear_logp_prepare_weight(const void* weight, int64_t ld_w, int64_t v, int64_t h,
+                                   void* weight_t, int64_t ld_wt, void* hip_stream) {
+  if (v < 1 || h < 64 || h % 64 || ld_w < h || ld_wt < (v + 255) / 256 * 256)
+    return LOGP_ERR_SHAPE;
+  if (v > (int64_t{1} << 31)) return LOGP_ERR_SHAPE;
+  if (!weight || !weight_t) return LOGP_ERR_NULL;
+  if (!aligned16(weight, ld_w, LOGP_BF16) || !aligned16(weight_t, ld_wt, LOGP_BF16))
+    return LOGP_ERR_ALIGN;
+  (void)hipGetLastError();
+  itl::launch_prepare_weight(static_cast<const uint16_t*>(weight), ld_w, v, h,
+                             static_cast<uint16_t*>(weight_t), ld_wt,
+                             static_cast<hipStream_t>(hip_stream));
   return hip_status();
 }
 

@@ -68,12 +68,18 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
 // inv_t: reciprocal temperature (1 = none); ent / gent: row entropy and its
 // upstream gradient (both null = no entropy term).  zsaved (fp32, or bf16
 // with z_bf16; [n, ld_z]) holds the forward's unscaled logits to read instead
-// of recomputing them, or is null.
+// of recomputing them, or is null.  weight_t (or null) is the caller's
+// prepared W^T, used for dh instead of transposing W into the workspace.
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
-                       const void* zsaved, int32_t z_bf16, int64_t ld_z, const float* lse,
+                       const void* zsaved, int32_t z_bf16, int64_t ld_z,
+                       const uint16_t* weight_t, int64_t ld_wt, const float* lse,
                        const float* grad, float inv_t, int32_t round_bf16, const float* ent,
                        const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
                        int64_t ld_dw, char* ws, hipStream_t s);
+
+// W^T [h, ld_wt] with columns v .. round_up(v, 256) - 1 zero, from W [v, ld_w].
+void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int64_t h,
+                           uint16_t* weight_t, int64_t ld_wt, hipStream_t s);
 
 }  // namespace itl

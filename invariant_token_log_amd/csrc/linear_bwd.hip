@@ -453,7 +453,8 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
 
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
-                       const void* zsaved, int32_t z_bf16, int64_t ld_z, const float* lse,
+                       const void* zsaved, int32_t z_bf16, int64_t ld_z,
+                       const uint16_t* weight_t, int64_t ld_wt, const float* lse,
                        const float* grad, float inv_t, int32_t round_bf16, const float* ent,
                        const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
                        int64_t ld_dw, char* ws, hipStream_t s) {
@@ -493,15 +494,27 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
                          ent, gent, dz, l.vp, dzt, l.np);
   }
   if (dh) {
-    hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
-                       dim3(256), 0, s, weight, ld_w, v, l.vp, wt, l.vp);
-    launch_gemm(bf16_out, dz, l.vp, l.np, wt, l.vp, h, l.vp, n, h, dh, ld_dh, s);
+    if (weight_t) {
+      // the caller's prepared W^T (linear_logp_prepare_weight): same values
+      launch_gemm(bf16_out, dz, l.vp, l.np, weight_t, ld_wt, h, l.vp, n, h, dh, ld_dh, s);
+    } else {
+      hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
+                         dim3(256), 0, s, weight, ld_w, v, l.vp, wt, l.vp);
+      launch_gemm(bf16_out, dz, l.vp, l.np, wt, l.vp, h, l.vp, n, h, dh, ld_dh, s);
+    }
   }
   if (dw) {
     hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.np)),
                        dim3(256), 0, s, hidden, ld_h, n, l.np, ht, l.np);
     launch_gemm(bf16_out, dzt, l.np, l.vp, ht, l.np, h, l.np, v, h, dw, ld_dw, s);
   }
+}
+
+void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int64_t h,
+                           uint16_t* weight_t, int64_t ld_wt, hipStream_t s) {
+  const int64_t vp = round_tile(v);
+  hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(vp)),
+                     dim3(256), 0, s, weight, ld_w, v, vp, weight_t, ld_wt);
 }
 
 }  // namespace itl

@@ -201,13 +201,15 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                     tile_width=LINEAR_TILE, need_dhidden=True, need_dweight=True,
                     out_dtype=torch.float32, dhidden_out=None, dweight_out=None,
                     workspace=None, temperature=1.0, entropy=None, grad_entropy=None,
-                    round_logits=False, saved_logits=None):
+                    round_logits=False, saved_logits=None, weight_t=None):
     """Backward of the fused LM head + logp: (dhidden [N, H] or None,
     dweight [V, H] or None) in out_dtype (float32 accumulators or their
     bfloat16 rounding), from the forward's lse (and entropy) and the upstream
     gradients.  temperature and round_logits must be the forward's.
     saved_logits: the forward's logits output ([N, V] float32, or bfloat16
-    with round_logits), read instead of recomputing h W^T; same bits."""
+    with round_logits), read instead of recomputing h W^T; same bits.
+    weight_t: prepare_weight(weight), used for dhidden instead of transposing
+    the weight on every call; same bits."""
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
@@ -233,6 +235,12 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     if z is not None and (z.dim() != 2 or tuple(z.shape) != (n, v) or z.stride(1) != 1
                           or z.dtype not in (torch.float32, torch.bfloat16)):
         raise ValueError("saved_logits must be [N, V] float32 / bfloat16 with contiguous rows")
+    wt = weight_t
+    if wt is not None and (wt.dtype != torch.bfloat16 or wt.dim() != 2 or wt.shape[0] != h
+                           or wt.shape[1] < _round256(v) or wt.stride(1) != 1
+                           or wt.device != dev):
+        raise ValueError("weight_t must be prepare_weight(weight): [H, >= round_up(V, 256)] "
+                         "bfloat16 with contiguous rows on the weight's device")
     L = _lib.lib()
     need = L.linear_logp_bwd_workspace_bytes(n, h, v, tile_width)
     if need and workspace is None:
@@ -243,7 +251,8 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                                t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
                                float(temperature), _rounding(round_logits), _ptr(z),
                                _DTYPES[z.dtype] if z is not None else 0,
-                               max(z.stride(0), v) if z is not None else 0, lse.data_ptr(),
+                               max(z.stride(0), v) if z is not None else 0, _ptr(wt),
+                               wt.stride(0) if wt is not None else 0, lse.data_ptr(),
                                g.data_ptr(), _ptr(ent),
                                _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
                                (dh.stride(0) if n > 1 else h) if dh is not None else 0,
@@ -251,6 +260,34 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                                _ptr(workspace), ws_len, _stream(dev))
     check("linear_logp_bwd", st)
     return dh, dw
+
+
+def _round256(x):
+    return (x + 255) // 256 * 256
+
+
+def prepare_weight(weight, out=None):
+    """W^T of the LM-head weight [V, H] bfloat16 as the fused backward reads
+    it: [H, round_up(V, 256)] bfloat16, columns V.. zero.  Reuse it over the
+    backward calls of one weight version and prepare it again after the
+    weight changes (an optimiser step, a weight update)."""
+    if weight.dtype != torch.bfloat16 or weight.dim() != 2 or weight.stride(1) != 1:
+        raise ValueError("weight must be [V, H] bfloat16 with contiguous rows")
+    v, h = weight.shape
+    if not weight.is_cuda:
+        raise ValueError("weight must be a GPU tensor")
+    if out is None:
+        out = torch.empty(h, _round256(v), dtype=torch.bfloat16, device=weight.device)
+    if (out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[0] != h
+            or out.shape[1] < _round256(v) or out.stride(1) != 1):
+        raise ValueError("out must be [H, >= round_up(V, 256)] bfloat16 with contiguous rows")
+    L = _lib.lib()
+    with torch.cuda.device(weight.device):
+        st = L.linear_logp_prepare_weight(weight.data_ptr(), weight.stride(0) if v > 1 else h,
+                                          v, h, out.data_ptr(), out.stride(0),
+                                          _stream(weight.device))
+    check("linear_logp_prepare_weight", st)
+    return out
 
 
 def _grad_or_zeros(g, ref):
@@ -303,7 +340,7 @@ def _padded_logits(n, v, dtype, device):
 class _LinearLogp(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, targets, ignore_index, temperature, with_entropy,
-                round_logits, save_logits):
+                round_logits, save_logits, weight_t):
         zdt = torch.bfloat16 if round_logits else torch.float32
         zbuf = _padded_logits(hidden.shape[0], weight.shape[0], zdt, hidden.device) \
             if save_logits else None
@@ -318,6 +355,7 @@ class _LinearLogp(torch.autograd.Function):
         ctx.temperature = temperature
         ctx.with_entropy = with_entropy
         ctx.round_logits = round_logits
+        ctx.weight_t = weight_t
         if with_entropy:
             return logp, ent
         return logp
@@ -332,12 +370,13 @@ class _LinearLogp(torch.autograd.Function):
                                  need_dweight=ctx.needs_input_grad[1],
                                  out_dtype=torch.bfloat16, temperature=ctx.temperature,
                                  entropy=ent if ctx.with_entropy else None, grad_entropy=gent,
-                                 round_logits=ctx.round_logits, saved_logits=z)
-        return dh, dw, None, None, None, None, None, None
+                                 round_logits=ctx.round_logits, saved_logits=z,
+                                 weight_t=ctx.weight_t)
+        return dh, dw, None, None, None, None, None, None, None
 
 
 def linear_logp(hidden, weight, target_ids, ignore_index=-100, temperature=1.0,
-                return_entropy=False, round_logits=False, save_logits=False):
+                return_entropy=False, round_logits=False, save_logits=False, weight_t=None):
     """Differentiable fused LM head + selected-token log-probability:
     hidden bf16 [N, H], weight bf16 [V, H] -> float32 logp [N] (and the
     entropy [N] with return_entropy) of softmax(hidden weight^T / temperature);
@@ -345,6 +384,8 @@ def linear_logp(hidden, weight, target_ids, ignore_index=-100, temperature=1.0,
     values; the gradient passes the rounding unchanged).  Backward fills the
     bf16 gradients of hidden and weight through linear_logp_bwd, recomputing
     the logits, or, with save_logits, reading the logits the forward kept
-    ([N, V] float32, bfloat16 with round_logits; same bits, more memory)."""
+    ([N, V] float32, bfloat16 with round_logits; same bits, more memory).
+    weight_t: prepare_weight(weight) of this weight version, reused by the
+    backward instead of transposing the weight again (same bits)."""
     return _LinearLogp.apply(hidden, weight, target_ids, ignore_index, temperature,
-                             return_entropy, round_logits, save_logits)
+                             return_entropy, round_logits, save_logits, weight_t)

@@ -148,14 +148,14 @@ def test_linear_bwd_argument_errors(L):
     def lb(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
                  targets=FAKE, tdt=0, tile=256, temp=1.0, rnd=0, z=None, zdt=0, ldz=0,
-                 lse=FAKE, g=FAKE, ent=None, gent=None, out=0, dh=FAKE, ld_dh=4096, dw=FAKE,
-                 ld_dw=4096, ws=FAKE, ws_bytes=1 << 40)
+                 wt=None, ldwt=0, lse=FAKE, g=FAKE, ent=None, gent=None, out=0, dh=FAKE,
+                 ld_dh=4096, dw=FAKE, ld_dw=4096, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_bwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
                                  a["v"], a["targets"], a["tdt"], -100, a["tile"], a["temp"],
-                                 a["rnd"], a["z"], a["zdt"], a["ldz"], a["lse"], a["g"],
-                                 a["ent"], a["gent"], a["out"], a["dh"], a["ld_dh"], a["dw"],
-                                 a["ld_dw"], a["ws"], a["ws_bytes"], None)
+                                 a["rnd"], a["z"], a["zdt"], a["ldz"], a["wt"], a["ldwt"],
+                                 a["lse"], a["g"], a["ent"], a["gent"], a["out"], a["dh"],
+                                 a["ld_dh"], a["dw"], a["ld_dw"], a["ws"], a["ws_bytes"], None)
     assert lb(temp=0.0) == _lib.LOGP_ERR_VALUE
     assert lb(rnd=3) == _lib.LOGP_ERR_VALUE
     # saved logits: fp32, or bf16 only in the bf16-rounded contract
@@ -164,6 +164,10 @@ def test_linear_bwd_argument_errors(L):
     assert lb(z=FAKE, zdt=_lib.LOGP_F32, ldz=100) == _lib.LOGP_ERR_SHAPE
     assert lb(z=FAKE + 4, zdt=_lib.LOGP_F32, ldz=151936) == _lib.LOGP_ERR_ALIGN
     assert lb(z=FAKE, zdt=_lib.LOGP_F32, ldz=151937) == _lib.LOGP_ERR_ALIGN
+    # prepared W^T: at least round_up(v, 256) columns, 16-byte aligned rows
+    assert lb(wt=FAKE, ldwt=151936) == _lib.LOGP_ERR_SHAPE
+    assert lb(wt=FAKE, ldwt=152065) == _lib.LOGP_ERR_ALIGN
+    assert lb(wt=FAKE + 2, ldwt=152064) == _lib.LOGP_ERR_ALIGN
     assert lb(ent=FAKE) == _lib.LOGP_ERR_NULL
     assert lb(tdt=5) == _lib.LOGP_ERR_DTYPE
     assert lb(out=2) == _lib.LOGP_ERR_DTYPE
@@ -188,3 +192,24 @@ def test_linear_bwd_argument_errors(L):
     assert L.linear_logp_bwd_workspace_bytes(0, 4096, 151936, 256) == 0
     assert L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 4096) == 0
     assert L.linear_logp_bwd_workspace_bytes(8, 100, 151936, 256) == 0
+
+
+def test_prepare_weight_argument_errors(L):
+    def pw(**kw):
+        a = dict(w=FAKE, ld_w=4096, v=151936, h=4096, wt=FAKE, ldwt=152064)
+        a.update(kw)
+        return L.linear_logp_prepare_weight(a["w"], a["ld_w"], a["v"], a["h"], a["wt"],
+                                            a["ldwt"], None)
+    assert pw(ldwt=151936) == _lib.LOGP_ERR_SHAPE
+    assert pw(v=0) == _lib.LOGP_ERR_SHAPE
+    assert pw(h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
+    assert pw(ld_w=4000) == _lib.LOGP_ERR_SHAPE
+    assert pw(w=None) == _lib.LOGP_ERR_NULL
+    assert pw(wt=None) == _lib.LOGP_ERR_NULL
+    assert pw(ldwt=152065) == _lib.LOGP_ERR_ALIGN
+    assert pw(ld_w=4100) == _lib.LOGP_ERR_ALIGN
+    assert pw(w=FAKE + 2) == _lib.LOGP_ERR_ALIGN
+    assert L.linear_logp_weight_t_bytes(151936, 4096) == 4096 * 152064 * 2
+    assert L.linear_logp_weight_t_bytes(1, 64) == 64 * 256 * 2
+    assert L.linear_logp_weight_t_bytes(0, 4096) == 0
+    assert L.linear_logp_weight_t_bytes(151936, 100) == 0

@@ -240,3 +240,34 @@ def test_saved_bf16_logits_rounded_variant():
             (itl.linear_logp(hh, ww, t, round_logits=rnd, save_logits=save) * g).sum().backward()
             grads.append((hh.grad, ww.grad))
         assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
+
+
+@pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (257, 64, 300), (1, 128, 529)])
+def test_prepared_weight_same_bits(n, hd, v):
+    """prepare_weight writes W^T with zero columns up to round_up(V, 256);
+    the backward reading it gives dh (and dW) with the same bits as the one
+    that transposes the weight itself, also through autograd, with a wider
+    row stride and after the buffer held other values."""
+    h, w, t, g = _case(n, hd, v, seed=7 * n + v)
+    vp = (v + 255) // 256 * 256
+    wt = itl.prepare_weight(w)
+    assert wt.shape == (hd, vp) and wt.dtype == torch.bfloat16
+    assert torch.equal(wt[:, :v], w.T) and not wt[:, v:].any()
+    wide = torch.full((hd, vp + 64), 7.0, dtype=torch.bfloat16, device=dev())
+    wt2 = itl.prepare_weight(w, out=wide)
+    assert torch.equal(wt2[:, :vp], wt) and bool((wt2[:, vp:] == 7.0).all())
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        dh0, dw0 = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype)
+        for prep in (wt, wt2):
+            dh1, dw1 = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype, weight_t=prep)
+            assert torch.equal(dh0, dh1) and torch.equal(dw0, dw1)
+    with pytest.raises(ValueError):
+        itl.linear_logp_bwd(h, w, t, lse, g, weight_t=wt[:, : vp - 256])
+    grads = []
+    for prep in (None, wt):
+        hh = h.clone().requires_grad_(True)
+        ww = w.clone().requires_grad_(True)
+        (itl.linear_logp(hh, ww, t, weight_t=prep) * g).sum().backward()
+        grads.append((hh.grad, ww.grad))
+    assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
