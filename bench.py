@@ -247,8 +247,8 @@ def bench_linear(args, torch, itl, synth):
     hid, wt, t = c["hidden"], c["weight"], c["targets"]
     logp = torch.empty(n, dtype=torch.float32, device=dev)
     lse = torch.empty(n, dtype=torch.float32, device=dev)
-    ws = torch.empty(itl.lib().linear_logp_fwd_workspace_bytes(n, v, 256), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(itl.lib().linear_logp_fwd_workspace_bytes(n, h, v, 256),
+                     dtype=torch.uint8, device=dev)
 
     def run():
         itl.linear_logp_fwd(hid, wt, t, -100, 256, logp_out=logp, lse_out=lse, workspace=ws)

@@ -178,10 +178,11 @@ int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
 
 /*
  * Workspace of linear_logp_fwd in bytes: the [n, T] partials (m, s, w) for
- * T = ceil(v / tile_width) and the copied target logits [n].  Returns 0 for
- * arguments linear_logp_fwd would reject.
+ * T = ceil(v / tile_width), the copied target logits [n] and, for n > 128, a
+ * copy of hidden re-laid for the product's loads (round_up(n, 256) * h * 2
+ * bytes).  Returns 0 for arguments linear_logp_fwd would reject.
  */
-size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width);
+size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width);
 
 /*
  * Fused LM-head + selected-token log-probability ("[RFC][ROCm] End-to-end
@@ -229,10 +230,11 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * Workspace of linear_logp_bwd in bytes: W^T [h, Vp], h^T [h, Np], dz [Np, Vp]
- * and dz^T [Vp, Np], all bf16, with Np, Vp = n, v rounded up to multiples of
- * 256 (about 3.8 GB at n = 4096, h = 4096, v = 151936).  0 when n = 0 or for
- * arguments linear_logp_bwd would reject.
+ * Workspace of linear_logp_bwd in bytes: W^T [h, Vp], h^T [h, Np], dz [Np, Vp],
+ * dz^T [Vp, Np] and a copy of hidden [Np, h], all bf16 and re-laid for the
+ * products' loads, with Np, Vp = n, v rounded up to multiples of 256 (about
+ * 3.8 GB at n = 4096, h = 4096, v = 151936).  0 when n = 0 or for arguments
+ * linear_logp_bwd would reject.
  */
 size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width);
 
@@ -272,12 +274,13 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *               saved_dtype LOGP_F32, or LOGP_BF16 only with
  *               LOGP_ROUND_BF16 (where the bf16 logits are exactly z);
  *               otherwise LOGP_ERR_DTYPE.
- *   weight_t, ld_wt
+ *   weight_t, weight_t_bytes
  *               NULL: the backward transposes weight into the workspace for
- *               dhidden.  Otherwise W^T prepared by
- *               linear_logp_prepare_weight from this weight (ld_wt >=
- *               round_up(v, 256), 16-byte aligned rows), used instead: the
- *               same values, so the same bits, without the transpose (the
+ *               dhidden.  Otherwise the buffer linear_logp_prepare_weight
+ *               filled from this weight (weight_t_bytes >=
+ *               linear_logp_weight_t_bytes(v, h), else LOGP_ERR_SHAPE;
+ *               16-byte aligned, else LOGP_ERR_ALIGN), used instead: the same
+ *               values, so the same bits, without the transpose (the
  *               "prepared weights" reused while the weight does not change,
  *               e.g. over the micro-batches of one optimiser step).
  *   lse         fp32 [n] from linear_logp_fwd.
@@ -300,7 +303,7 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
                         float temperature, int32_t logits_rounding, const void* saved_logits,
                         int32_t saved_dtype, int64_t ld_saved, const void* weight_t,
-                        int64_t ld_wt, const float* lse, const float* grad_logp,
+                        size_t weight_t_bytes, const float* lse, const float* grad_logp,
                         const float* entropy, const float* grad_entropy, int32_t out_dtype,
                         void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
@@ -308,16 +311,19 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
 /*
  * Prepared LM-head weight for the backward ("[RFC][ROCm] End-to-end
  * optimization of bitwise VIME R/R beyond native P/P", Workstream 3: prepared
- * [K, N] weights are reused and refreshed when the weight changes): writes
- * W^T [h, ld_wt] bf16 from weight [v, ld_w], columns v .. round_up(v, 256) - 1
- * zero.  h a multiple of 64, ld_wt >= round_up(v, 256) (LOGP_ERR_SHAPE),
- * 16-byte aligned rows (LOGP_ERR_ALIGN).  The caller owns weight_t and
- * prepares it again whenever the weight changes.  linear_logp_weight_t_bytes
- * gives h * round_up(v, 256) * 2 (0 for arguments that are refused).
+ * [K, N] weights are reused and refreshed when the weight changes): fills
+ * weight_t (device, caller-owned, weight_t_bytes >= linear_logp_weight_t_bytes
+ * (v, h), 16-byte aligned) with W^T of weight [v, ld_w] bf16 in the layout
+ * the backward's dhidden product reads (opaque to the caller; bf16, the
+ * vocabulary padded with zeros to round_up(v, 256)).  h a multiple of 64.
+ * Errors: LOGP_ERR_SHAPE (sizes, a short buffer), LOGP_ERR_NULL,
+ * LOGP_ERR_ALIGN (weight rows or weight_t not 16-byte aligned).  Prepare
+ * again whenever the weight changes.  linear_logp_weight_t_bytes gives
+ * h * round_up(v, 256) * 2 (0 for arguments that are refused).
  */
 size_t linear_logp_weight_t_bytes(int64_t v, int64_t h);
 int32_t linear_logp_prepare_weight(const void* weight, int64_t ld_w, int64_t v, int64_t h,
-                                   void* weight_t, int64_t ld_wt, void* hip_stream);
+                                   void* weight_t, size_t weight_t_bytes, void* hip_stream);
 
 /* Short English text for a status code (static storage, host memory). */
 const char* logp_status_str(int32_t status);

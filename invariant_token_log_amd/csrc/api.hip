@@ -73,6 +73,13 @@ FwdLayout fwd_layout(int64_t n, int64_t ntiles, bool tables, int32_t validate) {
   return l;
 }
 
+// The fused forward's workspace: the partial tables, then the blocked hidden.
+size_t linear_fwd_total(int64_t n, int64_t h, int64_t ntiles, size_t* hb_offset) {
+  const size_t tables = fwd_layout(n, ntiles, true, 0).total;
+  if (hb_offset) *hb_offset = round_up(tables);
+  return round_up(tables) + round_up(static_cast<size_t>(itl::linear_fwd_blocked_bytes(n, h)));
+}
+
 int32_t hip_status() {
   return hipGetLastError() == hipSuccess ? LOGP_OK : LOGP_ERR_HIP;
 }
@@ -168,10 +175,10 @@ int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v, int64_
   return hip_status();
 }
 
-size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t v, int32_t tile_width) {
-  if (n < 0 || v < 1 || tile_width != itl::kLinearTile) return 0;
+size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width) {
+  if (n < 0 || v < 1 || h < 64 || h % 64 || tile_width != itl::kLinearTile) return 0;
   const int64_t ntiles = (v + tile_width - 1) / tile_width;
-  return fwd_layout(n, ntiles, true, 0).total;
+  return linear_fwd_total(n, h, ntiles, nullptr);
 }
 
 int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
@@ -192,11 +199,13 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
   if (ntiles > (int64_t{1} << 24) || (n + 127) / 128 * ntiles > (int64_t{1} << 30))
     return LOGP_ERR_SHAPE;
   const FwdLayout lay = fwd_layout(n, ntiles, true, 0);
+  size_t hb_off = 0;
+  const size_t need = linear_fwd_total(n, h, ntiles, &hb_off);
   if (n == 0) return LOGP_OK;
   if (!hidden || !weight || !targets || !logp_out) return LOGP_ERR_NULL;
   if (!aligned16(hidden, ld_h, LOGP_BF16) || !aligned16(weight, ld_w, LOGP_BF16))
     return LOGP_ERR_ALIGN;
-  if (!workspace || workspace_bytes < lay.total ||
+  if (!workspace || workspace_bytes < need ||
       reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return LOGP_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -210,7 +219,8 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
                               static_cast<const uint16_t*>(weight), ld_w, n, h, v, tg,
                               ignore_index, pm, ps, pt, inv_temperature(temperature),
                               logits_rounding == LOGP_ROUND_BF16 ? 1 : 0, pw, logits_out,
-                              logits_dtype == LOGP_BF16 ? 1 : 0, ld_logits, s);
+                              logits_dtype == LOGP_BF16 ? 1 : 0, ld_logits,
+                              reinterpret_cast<uint16_t*>(ws + hb_off), s);
   itl::launch_fwd_merge(pm, ps, pw, pt, n, static_cast<int>(ntiles), ntiles, 1, v, tg,
                         ignore_index, logp_out, lse_out, entropy_out, nullptr, s);
   return hip_status();
@@ -227,7 +237,7 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
                         float temperature, int32_t logits_rounding, const void* saved_logits,
                         int32_t saved_dtype, int64_t ld_saved, const void* weight_t,
-                        int64_t ld_wt, const float* lse, const float* grad_logp,
+                        size_t weight_t_bytes, const float* lse, const float* grad_logp,
                         const float* entropy, const float* grad_entropy, int32_t out_dtype,
                         void* dhidden,
                         int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
@@ -249,8 +259,8 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
     if (!aligned16(saved_logits, ld_saved, saved_dtype)) return LOGP_ERR_ALIGN;
   }
   if (weight_t) {
-    if (ld_wt < (v + 255) / 256 * 256) return LOGP_ERR_SHAPE;
-    if (!aligned16(weight_t, ld_wt, LOGP_BF16)) return LOGP_ERR_ALIGN;
+    if (weight_t_bytes < linear_logp_weight_t_bytes(v, h)) return LOGP_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(weight_t) % 16) return LOGP_ERR_ALIGN;
   }
   if (!dhidden && !dweight) return LOGP_ERR_NULL;
   if ((dhidden && ld_dh < h) || (dweight && ld_dw < h)) return LOGP_ERR_SHAPE;
@@ -268,7 +278,7 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                          static_cast<const uint16_t*>(weight), ld_w, n, h, v,
                          targets_of(targets, target_dtype), ignore_index, saved_logits,
                          saved_dtype == LOGP_BF16 ? 1 : 0, ld_saved,
-                         static_cast<const uint16_t*>(weight_t), ld_wt, lse, grad_logp,
+                         static_cast<const uint16_t*>(weight_t), lse, grad_logp,
                          inv_temperature(temperature), logits_rounding == LOGP_ROUND_BF16 ? 1 : 0,
                          entropy, grad_entropy,
                          out_dtype == LOGP_BF16, dhidden, ld_dh, dweight, ld_dw,
@@ -282,16 +292,15 @@ size_t linear_logp_weight_t_bytes(int64_t v, int64_t h) {
 }
 
 int32_t linear_logp_prepare_weight(const void* weight, int64_t ld_w, int64_t v, int64_t h,
-                                   void* weight_t, int64_t ld_wt, void* hip_stream) {
-  if (v < 1 || h < 64 || h % 64 || ld_w < h || ld_wt < (v + 255) / 256 * 256)
-    return LOGP_ERR_SHAPE;
-  if (v > (int64_t{1} << 31)) return LOGP_ERR_SHAPE;
+                                   void* weight_t, size_t weight_t_bytes, void* hip_stream) {
+  if (v < 1 || h < 64 || h % 64 || ld_w < h || v > (int64_t{1} << 31)) return LOGP_ERR_SHAPE;
+  if (weight_t_bytes < linear_logp_weight_t_bytes(v, h)) return LOGP_ERR_SHAPE;
   if (!weight || !weight_t) return LOGP_ERR_NULL;
-  if (!aligned16(weight, ld_w, LOGP_BF16) || !aligned16(weight_t, ld_wt, LOGP_BF16))
+  if (!aligned16(weight, ld_w, LOGP_BF16) || reinterpret_cast<uintptr_t>(weight_t) % 16)
     return LOGP_ERR_ALIGN;
   (void)hipGetLastError();
   itl::launch_prepare_weight(static_cast<const uint16_t*>(weight), ld_w, v, h,
-                             static_cast<uint16_t*>(weight_t), ld_wt,
+                             static_cast<uint16_t*>(weight_t),
                              static_cast<hipStream_t>(hip_stream));
   return hip_status();
 }

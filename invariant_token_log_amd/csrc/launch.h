@@ -46,21 +46,29 @@ void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, 
 // Fused LM-head statistics: writes the row-major [n, T] partials (and the
 // entropy moments when pw is set) and the target logits of every active row
 // (T = ceil(v / 256)).  The logits are multiplied by inv_t before any
-// statistic; z (optional) receives the unscaled logits, fp32 or bf16.
+// statistic; z (optional) receives the unscaled logits, fp32 or bf16.  hb:
+// linear_fwd_blocked_bytes(n, h) bytes of scratch for the K32-blocked copy of
+// hidden (unused, may be null, when that is 0).
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
                             int64_t ld_w, int64_t n, int64_t h, int64_t v, Targets targets,
                             int64_t ignore, float* pm, float* ps, float* pt, float inv_t,
                             int32_t round_bf16, float* pw, void* z, int32_t z_bf16, int64_t ld_z,
-                            hipStream_t s);
+                            uint16_t* hb, hipStream_t s);
+
+// Bytes of the forward's blocked hidden copy: round_up(n, 256) * h * 2 when
+// the 256-row tile runs (n > 128), else 0.
+int64_t linear_fwd_blocked_bytes(int64_t n, int64_t h);
 
 constexpr int kLinearTile = 256;
 
 // Workspace of the fused LM-head backward (byte offsets): W^T [h, vp],
 // h^T [h, np], dz [np, vp], dz^T [vp, np], all bf16; np, vp = n, v rounded up
 // to multiples of 256.
+// Workspace of the fused backward (byte offsets): W^T, h^T, dz, dz^T and the
+// blocked h, all K32-blocked bf16 with N, V padded to np, vp.
 struct LinearBwdLayout {
   int64_t np, vp;
-  int64_t wt, ht, dz, dzt, total;
+  int64_t wt, ht, dz, dzt, hb, total;
 };
 LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
 
@@ -69,17 +77,24 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
 // upstream gradient (both null = no entropy term).  zsaved (fp32, or bf16
 // with z_bf16; [n, ld_z]) holds the forward's unscaled logits to read instead
 // of recomputing them, or is null.  weight_t (or null) is the caller's
-// prepared W^T, used for dh instead of transposing W into the workspace.
+// prepared W^T (launch_prepare_weight), used for dh instead of transposing W
+// into the workspace.
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
                        const void* zsaved, int32_t z_bf16, int64_t ld_z,
-                       const uint16_t* weight_t, int64_t ld_wt, const float* lse,
+                       const uint16_t* weight_t, const float* lse,
                        const float* grad, float inv_t, int32_t round_bf16, const float* ent,
                        const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
                        int64_t ld_dw, char* ws, hipStream_t s);
 
-// W^T [h, ld_wt] with columns v .. round_up(v, 256) - 1 zero, from W [v, ld_w].
+// W^T [h rows, K = round_up(v, 256)] K32-blocked (mfma_gemm.h), columns v ..
+// zero, from W [v, ld_w].
 void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int64_t h,
-                           uint16_t* weight_t, int64_t ld_wt, hipStream_t s);
+                           uint16_t* weight_t, hipStream_t s);
+
+// dst = the K32-blocked [rows_p, K = k] copy of src [rows, ld] (rows_p, k
+// multiples of 16 and 32; rows past `rows` zero).
+void launch_block_rows(const uint16_t* src, int64_t ld, int64_t rows, int64_t rows_p, int64_t k,
+                       uint16_t* dst, hipStream_t s);
 
 }  // namespace itl

@@ -16,16 +16,19 @@
 // invariant) and dW is deterministic for a given token order.
 //
 // Kernels (the products on the 256 x 256 tile of mfma_gemm.h):
+//   block_rows_bf16   : h [N, H] -> the K32-blocked copy the recomputed
+//                       product reads;
 //   linear_dz_kernel  : h x W^T tile -> dz in registers -> transposed, then
-//                       row-major LDS tile -> dz^T [Vp, Np] and dz [Np, Vp]
-//                       (bf16, whole 512-byte row segments per store pass);
+//                       row-major LDS tile -> dz^T [Vp, Np] and dz [Np, Vp];
 //   linear_dz_saved_kernel: the same dz and dz^T from saved logits, 64 x 64
 //                       tiles streamed through LDS;
-//   transpose_pad_bf16: W [V, H] -> W^T [H, Vp], h [N, H] -> h^T [H, Np], zero
-//                       padded, so that both products see K-contiguous operands;
+//   transpose_block_bf16: W [V, H] -> W^T [H, Vp], h [N, H] -> h^T [H, Np];
 //   gemm_out_kernel   : C = A B^T with fp32 or RNE-bf16 output.
-// Np, Vp are N and V rounded up to multiples of 256; padded rows and columns
-// hold zeros and add exact zeros to the K walks.
+// Every operand the backward writes for a product (dz, dz^T, W^T, h^T and
+// the blocked h) is in the K32-blocked layout of mfma_gemm.h: the same
+// values, read with whole-line loads.  Np, Vp are N and V rounded up to
+// multiples of 256; padded rows and columns hold zeros and add exact zeros to
+// the K walks.
 #include "launch.h"
 #include "logp_device.h"
 #include "mfma_gemm.h"
@@ -43,13 +46,13 @@ __device__ __forceinline__ uint16_t bf16_bits(float d) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(d));
 }
 
-// dst[c][r] = r < rows ? src[r][c] : 0 for c < gridDim.x * 64 and r < rows_p
-// (a multiple of 64).  64 x 64 tiles through LDS; 16-byte global accesses.
-__global__ __launch_bounds__(256) void transpose_pad_bf16(const uint16_t* __restrict__ src,
-                                                          int64_t ld_src, int64_t rows,
-                                                          int64_t rows_p,
-                                                          uint16_t* __restrict__ dst,
-                                                          int64_t ld_dst) {
+// dst = the K32-blocked [gridDim.x * 64 rows, K = rows_p] operand with
+// element (c, r) = r < rows ? src[r][c] : 0 (rows_p a multiple of 64).  64 x 64
+// tiles through LDS; 16-byte global accesses.
+__global__ __launch_bounds__(256) void transpose_block_bf16(const uint16_t* __restrict__ src,
+                                                            int64_t ld_src, int64_t rows,
+                                                            int64_t rows_p,
+                                                            uint16_t* __restrict__ dst) {
   __shared__ uint16_t tile[64][64 + 2];
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int t = threadIdx.x;
@@ -78,11 +81,28 @@ __global__ __launch_bounds__(256) void transpose_pad_bf16(const uint16_t* __rest
       for (int e = 0; e < 8; ++e)
         w[e] = static_cast<uint32_t>(tile[rs + 2 * e][c]) |
                (static_cast<uint32_t>(tile[rs + 2 * e + 1][c]) << 16);
-      uint16_t* p = dst + (c0 + c) * ld_dst + r0 + rs;
+      uint16_t* p = dst + gemm::kblocked_index(c0 + c, r0 + rs, rows_p / gemm::kK);
       *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
       *reinterpret_cast<uint4*>(p + 8) = make_uint4(w[4], w[5], w[6], w[7]);
     }
     __syncthreads();
+  }
+}
+
+// dst = the K32-blocked [rows_p, K = k] copy of src [rows, k] (rows past
+// rows zero); one 16-byte chunk per thread in destination order.
+__global__ __launch_bounds__(256) void block_rows_bf16(const uint16_t* __restrict__ src,
+                                                       int64_t ld, int64_t rows, int64_t rows_p,
+                                                       int64_t k, uint16_t* __restrict__ dst) {
+  const int64_t ksteps = k / gemm::kK, chunks = rows_p * (k / 8);
+  for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    // chunk c: 16-row block rb, K step ks, row r16 of the block, quarter q
+    const int64_t q = c & 3, r16 = (c >> 2) & 15, t = c >> 6;
+    const int64_t ks = t % ksteps, row = (t / ksteps) * 16 + r16;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (row < rows) x = *reinterpret_cast<const uint4*>(src + row * ld + ks * gemm::kK + q * 8);
+    *reinterpret_cast<uint4*>(dst + c * 8) = x;
   }
 }
 
@@ -125,8 +145,7 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     const float* __restrict__ lse,
     const float* __restrict__ grad, float inv_t, int32_t round_bf16,
     const float* __restrict__ ent, const float* __restrict__ gent, uint16_t* __restrict__ dz,
-    int64_t ld_dz,
-    uint16_t* __restrict__ dzt, int64_t ld_dzt) {
+    uint16_t* __restrict__ dzt) {
   const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemDz sm;
   const int tid = threadIdx.x;
@@ -167,8 +186,9 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  gemm::mainloop(sm.u.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
-                 static_cast<int>(hdim / gemm::kK), acc);
+  // hidden: K32-blocked with mblocks * 256 rows
+  gemm::mainloop<true, false>(sm.u.st, hidden, 0, m0, static_cast<int64_t>(mblocks) * kT, weight,
+                              ld_w, v0, v, static_cast<int>(hdim / gemm::kK), acc);
   __syncthreads();
 
   // dz of every element (dz_value; 0 on ignored / padded rows and columns),
@@ -207,7 +227,10 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
       dv[i][j][1] = static_cast<uint32_t>(b[2]) | (static_cast<uint32_t>(b[3]) << 16);
     }
   }
-  // dz^T: tile[c][r] (column-major), then 256 rows of dz^T x 32 chunks.
+  // dz^T: tile[c][r] (column-major), then out in K32-blocked order: 128
+  // pieces of 16 rows x 32 tokens, one contiguous KiB each.
+  const int64_t np_steps = static_cast<int64_t>(mblocks) * (kT / gemm::kK);
+  const int64_t vp_steps = static_cast<int64_t>(vblocks) * (kT / gemm::kK);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -218,12 +241,13 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     }
   __syncthreads();
   for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
-    const int c = idx >> 5, r = (idx & 31) * 8;
-    store_stream(dzt + (v0 + c) * ld_dzt + m0 + r,
+    const int piece = idx >> 6, e = idx & 63;
+    const int c = (piece >> 3) * 16 + (e >> 2), r = (piece & 7) * 32 + (e & 3) * 8;
+    store_stream(dzt + gemm::kblocked_index(v0 + c, m0 + r, np_steps),
                  *reinterpret_cast<const uint4*>(&sm.u.tile[c][r]));
   }
   __syncthreads();
-  // dz: tile[r][c] (row-major), then 256 rows of dz x 32 chunks.
+  // dz: tile[r][c] (row-major), then out in K32-blocked order.
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -237,8 +261,9 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     }
   __syncthreads();
   for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
-    const int r = idx >> 5, c = (idx & 31) * 8;
-    store_stream(dz + (m0 + r) * ld_dz + v0 + c,
+    const int piece = idx >> 6, e = idx & 63;
+    const int r = (piece >> 3) * 16 + (e >> 2), c = (piece & 7) * 32 + (e & 3) * 8;
+    store_stream(dz + gemm::kblocked_index(m0 + r, v0 + c, vp_steps),
                  *reinterpret_cast<const uint4*>(&sm.u.tile[r][c]));
   }
 }
@@ -248,8 +273,9 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
 // the same values through the same dz_value, so the same bits.  64 x 64
 // tiles of [Np, Vp]: thread (r = tid / 4, 16 columns from (tid % 4) * 16)
 // reads its 16 logits with 16-byte loads, writes its 16 dz along the row,
-// and the tile leaves transposed through LDS for dz^T.  Rows past n or
-// ignored, and columns past v, get 0 without reading the logits.
+// and the tile leaves transposed through LDS for dz^T (both K32-blocked).
+// Rows past n or ignored, and columns past v, get 0 without reading the
+// logits.
 constexpr int kST = 64;
 
 template <bool ZBF16>
@@ -258,7 +284,7 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse, const float* __restrict__ grad, float inv_t,
     int32_t round_bf16, const float* __restrict__ ent, const float* __restrict__ gent,
-    uint16_t* __restrict__ dz, int64_t ld_dz, uint16_t* __restrict__ dzt, int64_t ld_dzt) {
+    int64_t vp_cols, uint16_t* __restrict__ dz, uint16_t* __restrict__ dzt) {
   const Targets targets{tgt, tgt32};
   __shared__ uint16_t tile[kST][kST + 8];
   const int tid = threadIdx.x;
@@ -336,7 +362,7 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
       }
       packed[e] = static_cast<uint32_t>(b[0]) | (static_cast<uint32_t>(b[1]) << 16);
     }
-    uint16_t* o = dz + row * ld_dz + col;
+    uint16_t* o = dz + gemm::kblocked_index(row, col, vp_cols / gemm::kK);
     store_stream(o, make_uint4(packed[0], packed[1], packed[2], packed[3]));
     store_stream(o + 8, make_uint4(packed[4], packed[5], packed[6], packed[7]));
     __syncthreads();
@@ -347,7 +373,7 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
       for (int e = 0; e < 8; ++e)
         w[e] = static_cast<uint32_t>(tile[rs + 2 * e][c]) |
                (static_cast<uint32_t>(tile[rs + 2 * e + 1][c]) << 16);
-      uint16_t* q = dzt + (c0 + c) * ld_dzt + r0 + rs;
+      uint16_t* q = dzt + gemm::kblocked_index(c0 + c, r0 + rs, np_rows / gemm::kK);
       store_stream(q, make_uint4(w[0], w[1], w[2], w[3]));
       store_stream(q + 8, make_uint4(w[4], w[5], w[6], w[7]));
     }
@@ -355,8 +381,9 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
   }
 }
 
-// C[m_out, n_out] = A[., K] B[., K]^T on the mfma_gemm.h tile; BF16OUT rounds
-// the fp32 accumulators to bf16 (RNE) on the way out.
+// C[m_out, n_out] = A[., K] B[., K]^T on the mfma_gemm.h tile, both operands
+// K32-blocked; BF16OUT rounds the fp32 accumulators to bf16 (RNE) on the way
+// out.
 template <bool BF16OUT>
 __global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t arows, const uint16_t* __restrict__ B,
@@ -377,7 +404,7 @@ __global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  gemm::mainloop(st, A, lda, m0, arows, B, ldb, n0, brows, ksteps, acc);
+  gemm::mainloop<true, true>(st, A, lda, m0, arows, B, ldb, n0, brows, ksteps, acc);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -419,20 +446,20 @@ unsigned tgrid(int64_t rows_p) {
   return static_cast<unsigned>(b < 65535 ? b : 65535);
 }
 
-void launch_gemm(bool bf16, const uint16_t* A, int64_t lda, int64_t arows, const uint16_t* B,
-                 int64_t ldb, int64_t brows, int64_t k, int64_t m_out, int64_t n_out, void* C,
-                 int64_t ldc, hipStream_t s) {
+// C = A B^T, A [arows, k] and B [brows, k] K32-blocked.
+void launch_gemm(bool bf16, const uint16_t* A, int64_t arows, const uint16_t* B, int64_t brows,
+                 int64_t k, int64_t m_out, int64_t n_out, void* C, int64_t ldc, hipStream_t s) {
   const int mblocks = static_cast<int>((m_out + kT - 1) / kT);
   const int nblocks = static_cast<int>((n_out + kT - 1) / kT);
   const int ksteps = static_cast<int>(k / gemm::kK);
   if (bf16)
     hipLaunchKernelGGL(gemm_out_kernel<true>, dim3(mblocks * nblocks), dim3(gemm::kThreads), 0, s,
-                       A, lda, arows, B, ldb, brows, ksteps, mblocks, nblocks, m_out, n_out, C,
-                       ldc);
+                       A, int64_t{0}, arows, B, int64_t{0}, brows, ksteps, mblocks, nblocks,
+                       m_out, n_out, C, ldc);
   else
     hipLaunchKernelGGL(gemm_out_kernel<false>, dim3(mblocks * nblocks), dim3(gemm::kThreads), 0,
-                       s, A, lda, arows, B, ldb, brows, ksteps, mblocks, nblocks, m_out, n_out, C,
-                       ldc);
+                       s, A, int64_t{0}, arows, B, int64_t{0}, brows, ksteps, mblocks, nblocks,
+                       m_out, n_out, C, ldc);
 }
 
 }  // namespace
@@ -447,14 +474,15 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
   l.ht = l.wt + up(h * vp * 2);
   l.dz = l.ht + up(h * np * 2);
   l.dzt = l.dz + up(np * vp * 2);
-  l.total = l.dzt + up(vp * np * 2);
+  l.hb = l.dzt + up(vp * np * 2);
+  l.total = l.hb + up(np * h * 2);
   return l;
 }
 
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
                        const void* zsaved, int32_t z_bf16, int64_t ld_z,
-                       const uint16_t* weight_t, int64_t ld_wt, const float* lse,
+                       const uint16_t* weight_t, const float* lse,
                        const float* grad, float inv_t, int32_t round_bf16, const float* ent,
                        const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
                        int64_t ld_dw, char* ws, hipStream_t s) {
@@ -475,46 +503,55 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + l.ht);
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + l.dz);
   uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + l.dzt);
+  uint16_t* hb = reinterpret_cast<uint16_t*>(ws + l.hb);
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
   if (!zsaved) {
+    launch_block_rows(hidden, ld_h, n, l.np, h, hb, s);
     hipLaunchKernelGGL(linear_dz_kernel, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0, s,
-                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                       targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, l.vp,
-                       dzt, l.np);
+                       hb, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
+                       targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, dzt);
   } else {
     const int64_t rb = l.np / kST;
     const dim3 grid(static_cast<unsigned>(l.vp / kST), static_cast<unsigned>(rb < 65535 ? rb : 65535));
     if (z_bf16)
       hipLaunchKernelGGL(linear_dz_saved_kernel<true>, grid, dim3(256), 0, s, zsaved, ld_z, n, v,
                          l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16, ent,
-                         gent, dz, l.vp, dzt, l.np);
+                         gent, l.vp, dz, dzt);
     else
       hipLaunchKernelGGL(linear_dz_saved_kernel<false>, grid, dim3(256), 0, s, zsaved, ld_z, n,
                          v, l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
-                         ent, gent, dz, l.vp, dzt, l.np);
+                         ent, gent, l.vp, dz, dzt);
   }
   if (dh) {
-    if (weight_t) {
-      // the caller's prepared W^T (linear_logp_prepare_weight): same values
-      launch_gemm(bf16_out, dz, l.vp, l.np, weight_t, ld_wt, h, l.vp, n, h, dh, ld_dh, s);
-    } else {
-      hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
-                         dim3(256), 0, s, weight, ld_w, v, l.vp, wt, l.vp);
-      launch_gemm(bf16_out, dz, l.vp, l.np, wt, l.vp, h, l.vp, n, h, dh, ld_dh, s);
+    // W^T: the caller's prepared copy (linear_logp_prepare_weight, the same
+    // values) or made here
+    if (!weight_t) {
+      hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
+                         dim3(256), 0, s, weight, ld_w, v, l.vp, wt);
+      weight_t = wt;
     }
+    launch_gemm(bf16_out, dz, l.np, weight_t, h, l.vp, n, h, dh, ld_dh, s);
   }
   if (dw) {
-    hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.np)),
-                       dim3(256), 0, s, hidden, ld_h, n, l.np, ht, l.np);
-    launch_gemm(bf16_out, dzt, l.np, l.vp, ht, l.np, h, l.np, v, h, dw, ld_dw, s);
+    hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.np)),
+                       dim3(256), 0, s, hidden, ld_h, n, l.np, ht);
+    launch_gemm(bf16_out, dzt, l.vp, ht, h, l.np, v, h, dw, ld_dw, s);
   }
 }
 
 void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int64_t h,
-                           uint16_t* weight_t, int64_t ld_wt, hipStream_t s) {
+                           uint16_t* weight_t, hipStream_t s) {
   const int64_t vp = round_tile(v);
-  hipLaunchKernelGGL(transpose_pad_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(vp)),
-                     dim3(256), 0, s, weight, ld_w, v, vp, weight_t, ld_wt);
+  hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(vp)),
+                     dim3(256), 0, s, weight, ld_w, v, vp, weight_t);
+}
+
+void launch_block_rows(const uint16_t* src, int64_t ld, int64_t rows, int64_t rows_p, int64_t k,
+                       uint16_t* dst, hipStream_t s) {
+  const int64_t want = (rows_p * (k / 8) + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(block_rows_bf16, dim3(blocks), dim3(256), 0, s, src, ld, rows, rows_p, k,
+                     dst);
 }
 
 }  // namespace itl

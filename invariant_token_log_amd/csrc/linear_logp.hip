@@ -366,8 +366,9 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  gemm::mainloop(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v, static_cast<int>(hdim / BK),
-                 acc);
+  // hidden: K32-blocked with mblocks * 256 rows
+  gemm::mainloop<true, false>(sm.st, hidden, 0, m0, static_cast<int64_t>(mblocks) * 256, weight,
+                              ld_w, v0, v, static_cast<int>(hdim / BK), acc);
   __syncthreads();
   stats_epilogue<8, 4, 256, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * 128, wn * 64, li,
                                                         g, tid, m0, v0, vb,
@@ -427,7 +428,7 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                             int64_t ld_w, int64_t n, int64_t h, int64_t v, Targets targets,
                             int64_t ignore, float* pm, float* ps, float* pt, float inv_t,
                             int32_t round_bf16, float* pw, void* z, int32_t z_bf16, int64_t ld_z,
-                            hipStream_t s) {
+                            uint16_t* hb, hipStream_t s) {
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
   const int32_t z_vec = z && reinterpret_cast<uintptr_t>(z) % 16 == 0 &&
                         (ld_z * (z_bf16 ? 2 : 4)) % 16 == 0;
@@ -442,10 +443,15 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                        pm, ps, pt, ex);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
+    launch_block_rows(hidden, ld_h, n, static_cast<int64_t>(mblocks) * 256, h, hb, s);
     hipLaunchKernelGGL(linear_stats_dma, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,
-                       hidden, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
+                       hb, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
                        targets.is32, ignore, pm, ps, pt, ex);
   }
+}
+
+int64_t linear_fwd_blocked_bytes(int64_t n, int64_t h) {
+  return n > 128 ? (n + 255) / 256 * 256 * h * 2 : 0;
 }
 
 }  // namespace itl

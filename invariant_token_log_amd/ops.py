@@ -178,7 +178,7 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
                           or z.stride(1) != 1):
         raise ValueError("logits_out must be [N, V] of logits_dtype with contiguous rows")
     L = _lib.lib()
-    need = L.linear_logp_fwd_workspace_bytes(n, v, tile_width)
+    need = L.linear_logp_fwd_workspace_bytes(n, h, v, tile_width)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
@@ -236,12 +236,10 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                           or z.dtype not in (torch.float32, torch.bfloat16)):
         raise ValueError("saved_logits must be [N, V] float32 / bfloat16 with contiguous rows")
     wt = weight_t
-    if wt is not None and (wt.dtype != torch.bfloat16 or wt.dim() != 2 or wt.shape[0] != h
-                           or wt.shape[1] < _round256(v) or wt.stride(1) != 1
-                           or wt.device != dev):
-        raise ValueError("weight_t must be prepare_weight(weight): [H, >= round_up(V, 256)] "
-                         "bfloat16 with contiguous rows on the weight's device")
     L = _lib.lib()
+    if wt is not None and (not wt.is_contiguous() or wt.device != dev
+                           or wt.numel() * wt.element_size() < L.linear_logp_weight_t_bytes(v, h)):
+        raise ValueError("weight_t must be prepare_weight(weight) on the weight's device")
     need = L.linear_logp_bwd_workspace_bytes(n, h, v, tile_width)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -252,7 +250,8 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                                float(temperature), _rounding(round_logits), _ptr(z),
                                _DTYPES[z.dtype] if z is not None else 0,
                                max(z.stride(0), v) if z is not None else 0, _ptr(wt),
-                               wt.stride(0) if wt is not None else 0, lse.data_ptr(),
+                               wt.numel() * wt.element_size() if wt is not None else 0,
+                               lse.data_ptr(),
                                g.data_ptr(), _ptr(ent),
                                _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
                                (dh.stride(0) if n > 1 else h) if dh is not None else 0,
@@ -262,29 +261,30 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     return dh, dw
 
 
-def _round256(x):
-    return (x + 255) // 256 * 256
-
-
 def prepare_weight(weight, out=None):
-    """W^T of the LM-head weight [V, H] bfloat16 as the fused backward reads
-    it: [H, round_up(V, 256)] bfloat16, columns V.. zero.  Reuse it over the
-    backward calls of one weight version and prepare it again after the
-    weight changes (an optimiser step, a weight update)."""
+    """The LM-head weight [V, H] bfloat16 prepared for the fused backward's
+    dhidden product (W^T, vocabulary padded with zeros to a multiple of 256,
+    in the library's own layout): a uint8 buffer of
+    linear_logp_weight_t_bytes(V, H) bytes (or `out`, a contiguous buffer at
+    least that large).  Reuse it over the backward calls of one weight
+    version and prepare it again after the weight changes (an optimiser
+    step, a weight update)."""
     if weight.dtype != torch.bfloat16 or weight.dim() != 2 or weight.stride(1) != 1:
         raise ValueError("weight must be [V, H] bfloat16 with contiguous rows")
     v, h = weight.shape
     if not weight.is_cuda:
         raise ValueError("weight must be a GPU tensor")
-    if out is None:
-        out = torch.empty(h, _round256(v), dtype=torch.bfloat16, device=weight.device)
-    if (out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[0] != h
-            or out.shape[1] < _round256(v) or out.stride(1) != 1):
-        raise ValueError("out must be [H, >= round_up(V, 256)] bfloat16 with contiguous rows")
     L = _lib.lib()
+    need = L.linear_logp_weight_t_bytes(v, h)
+    if need == 0:
+        raise ValueError("H must be a positive multiple of 64")
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=weight.device)
+    if not out.is_contiguous() or out.numel() * out.element_size() < need:
+        raise ValueError(f"out must be a contiguous buffer of at least {need} bytes")
     with torch.cuda.device(weight.device):
         st = L.linear_logp_prepare_weight(weight.data_ptr(), weight.stride(0) if v > 1 else h,
-                                          v, h, out.data_ptr(), out.stride(0),
+                                          v, h, out.data_ptr(), out.numel() * out.element_size(),
                                           _stream(weight.device))
     check("linear_logp_prepare_weight", st)
     return out

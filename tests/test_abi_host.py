@@ -139,9 +139,13 @@ def test_linear_argument_errors(L):
     assert lin(ld_w=4100) == _lib.LOGP_ERR_ALIGN
     assert lin(ws_bytes=16) == _lib.LOGP_ERR_WORKSPACE
     assert lin(n=0, h_ptr=None, w_ptr=None) == _lib.LOGP_OK
-    need = L.linear_logp_fwd_workspace_bytes(8, 151936, 256)
+    need = L.linear_logp_fwd_workspace_bytes(8, 4096, 151936, 256)
     assert need == 256 + 3 * 256 * (-(-(594 * 8 * 4) // 256)) + 256
-    assert L.linear_logp_fwd_workspace_bytes(8, 151936, 512) == 0
+    assert L.linear_logp_fwd_workspace_bytes(8, 4096, 151936, 512) == 0
+    assert L.linear_logp_fwd_workspace_bytes(8, 100, 151936, 256) == 0
+    # n > 128: plus the re-laid hidden copy, 256-row padded
+    tables = 256 + 3 * 256 * (-(-(594 * 200 * 4) // 256)) + 256 * (-(-(200 * 4) // 256))
+    assert L.linear_logp_fwd_workspace_bytes(200, 4096, 151936, 256) == tables + 256 * 4096 * 2
 
 
 def test_linear_bwd_argument_errors(L):
@@ -164,10 +168,9 @@ def test_linear_bwd_argument_errors(L):
     assert lb(z=FAKE, zdt=_lib.LOGP_F32, ldz=100) == _lib.LOGP_ERR_SHAPE
     assert lb(z=FAKE + 4, zdt=_lib.LOGP_F32, ldz=151936) == _lib.LOGP_ERR_ALIGN
     assert lb(z=FAKE, zdt=_lib.LOGP_F32, ldz=151937) == _lib.LOGP_ERR_ALIGN
-    # prepared W^T: at least round_up(v, 256) columns, 16-byte aligned rows
-    assert lb(wt=FAKE, ldwt=151936) == _lib.LOGP_ERR_SHAPE
-    assert lb(wt=FAKE, ldwt=152065) == _lib.LOGP_ERR_ALIGN
-    assert lb(wt=FAKE + 2, ldwt=152064) == _lib.LOGP_ERR_ALIGN
+    # prepared weight: at least linear_logp_weight_t_bytes, 16-byte aligned
+    assert lb(wt=FAKE, ldwt=4096 * 152064 * 2 - 1) == _lib.LOGP_ERR_SHAPE
+    assert lb(wt=FAKE + 8, ldwt=4096 * 152064 * 2) == _lib.LOGP_ERR_ALIGN
     assert lb(ent=FAKE) == _lib.LOGP_ERR_NULL
     assert lb(tdt=5) == _lib.LOGP_ERR_DTYPE
     assert lb(out=2) == _lib.LOGP_ERR_DTYPE
@@ -185,10 +188,11 @@ def test_linear_bwd_argument_errors(L):
     assert lb(ws_bytes=16) == _lib.LOGP_ERR_WORKSPACE
     assert lb(ws=FAKE + 16) == _lib.LOGP_ERR_WORKSPACE
     assert lb(n=0, h_ptr=None, targets=None, lse=None, g=None, dw=None) == _lib.LOGP_OK
-    # workspace: W^T, h^T, dz, dz^T in bf16 with 256-padded n and v
+    # workspace: W^T, h^T, dz, dz^T and the re-laid hidden in bf16 with
+    # 256-padded n and v
     np_, vp = 256, 152064
     need = L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 256)
-    assert need == 2 * (4096 * vp + 4096 * np_ + 2 * np_ * vp)
+    assert need == 2 * (4096 * vp + 4096 * np_ + 2 * np_ * vp + np_ * 4096)
     assert L.linear_logp_bwd_workspace_bytes(0, 4096, 151936, 256) == 0
     assert L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 4096) == 0
     assert L.linear_logp_bwd_workspace_bytes(8, 100, 151936, 256) == 0
@@ -196,17 +200,17 @@ def test_linear_bwd_argument_errors(L):
 
 def test_prepare_weight_argument_errors(L):
     def pw(**kw):
-        a = dict(w=FAKE, ld_w=4096, v=151936, h=4096, wt=FAKE, ldwt=152064)
+        a = dict(w=FAKE, ld_w=4096, v=151936, h=4096, wt=FAKE, ldwt=4096 * 152064 * 2)
         a.update(kw)
         return L.linear_logp_prepare_weight(a["w"], a["ld_w"], a["v"], a["h"], a["wt"],
                                             a["ldwt"], None)
-    assert pw(ldwt=151936) == _lib.LOGP_ERR_SHAPE
+    assert pw(ldwt=4096 * 152064 * 2 - 2) == _lib.LOGP_ERR_SHAPE
     assert pw(v=0) == _lib.LOGP_ERR_SHAPE
     assert pw(h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
     assert pw(ld_w=4000) == _lib.LOGP_ERR_SHAPE
     assert pw(w=None) == _lib.LOGP_ERR_NULL
     assert pw(wt=None) == _lib.LOGP_ERR_NULL
-    assert pw(ldwt=152065) == _lib.LOGP_ERR_ALIGN
+    assert pw(wt=FAKE + 8) == _lib.LOGP_ERR_ALIGN
     assert pw(ld_w=4100) == _lib.LOGP_ERR_ALIGN
     assert pw(w=FAKE + 2) == _lib.LOGP_ERR_ALIGN
     assert L.linear_logp_weight_t_bytes(151936, 4096) == 4096 * 152064 * 2

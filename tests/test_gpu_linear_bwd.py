@@ -242,20 +242,31 @@ def test_saved_bf16_logits_rounded_variant():
         assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
 
 
+def _blocked_wt(w, v, hd):
+    """W^T [H, round_up(V, 256)] (zero columns past V) in the K32-blocked
+    order of the product loads: element (r, k) at
+    ((r // 16) * (Vp // 32) + k // 32) * 512 + (r % 16) * 32 + k % 32."""
+    vp = (v + 255) // 256 * 256
+    wt = np.zeros((hd, vp), dtype=np.uint16)
+    wt[:, :v] = w.view(torch.int16).cpu().numpy().astype(np.uint16).T
+    return wt.reshape(hd // 16, 16, vp // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
+
+
 @pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (257, 64, 300), (1, 128, 529)])
 def test_prepared_weight_same_bits(n, hd, v):
-    """prepare_weight writes W^T with zero columns up to round_up(V, 256);
-    the backward reading it gives dh (and dW) with the same bits as the one
-    that transposes the weight itself, also through autograd, with a wider
-    row stride and after the buffer held other values."""
+    """prepare_weight writes W^T (zero columns up to round_up(V, 256)) in the
+    blocked order; the backward reading it gives dh (and dW) with the same
+    bits as the one that transposes the weight itself, also through
+    autograd, into a larger buffer and after the buffer held other values."""
     h, w, t, g = _case(n, hd, v, seed=7 * n + v)
-    vp = (v + 255) // 256 * 256
+    need = itl.lib().linear_logp_weight_t_bytes(v, hd)
     wt = itl.prepare_weight(w)
-    assert wt.shape == (hd, vp) and wt.dtype == torch.bfloat16
-    assert torch.equal(wt[:, :v], w.T) and not wt[:, v:].any()
-    wide = torch.full((hd, vp + 64), 7.0, dtype=torch.bfloat16, device=dev())
-    wt2 = itl.prepare_weight(w, out=wide)
-    assert torch.equal(wt2[:, :vp], wt) and bool((wt2[:, vp:] == 7.0).all())
+    assert wt.dtype == torch.uint8 and wt.numel() == need
+    got = wt.view(torch.int16).cpu().numpy().astype(np.uint16)
+    assert np.array_equal(got, _blocked_wt(w, v, hd))
+    big = torch.full((need + 4096,), 7, dtype=torch.uint8, device=dev())
+    wt2 = itl.prepare_weight(w, out=big)
+    assert torch.equal(wt2[:need], wt) and bool((wt2[need:] == 7).all())
     _, lse = itl.linear_logp_fwd(h, w, t)
     for out_dtype in (torch.float32, torch.bfloat16):
         dh0, dw0 = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype)
@@ -263,7 +274,7 @@ def test_prepared_weight_same_bits(n, hd, v):
             dh1, dw1 = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype, weight_t=prep)
             assert torch.equal(dh0, dh1) and torch.equal(dw0, dw1)
     with pytest.raises(ValueError):
-        itl.linear_logp_bwd(h, w, t, lse, g, weight_t=wt[:, : vp - 256])
+        itl.linear_logp_bwd(h, w, t, lse, g, weight_t=wt[: need - 256])
     grads = []
     for prep in (None, wt):
         hh = h.clone().requires_grad_(True)
