@@ -240,7 +240,7 @@ def bench_fwd(args, torch, itl, synth):
     }, None
 
 
-def bench_linear(args, torch, itl, synth):
+def bench_linear(args, torch, itl, synth, prepared=False):
     n, h, v = 4096, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB
     dev = torch.device("cuda", 0)
     c = synth.qwen3_linear(n=n, h=h, v=v, device=dev)
@@ -249,9 +249,13 @@ def bench_linear(args, torch, itl, synth):
     lse = torch.empty(n, dtype=torch.float32, device=dev)
     ws = torch.empty(itl.lib().linear_logp_fwd_workspace_bytes(n, h, v, 256),
                      dtype=torch.uint8, device=dev)
+    # prepared: the weight re-laid once per weight version, outside the timed
+    # calls
+    pw = itl.prepare_weight(wt) if prepared else None
 
     def run():
-        itl.linear_logp_fwd(hid, wt, t, -100, 256, logp_out=logp, lse_out=lse, workspace=ws)
+        itl.linear_logp_fwd(hid, wt, t, -100, 256, logp_out=logp, lse_out=lse, workspace=ws,
+                            prepared_weight=pw)
 
     ramp(torch, run, args.ramp_s)
     for _ in range(args.warmup):
@@ -262,20 +266,21 @@ def bench_linear(args, torch, itl, synth):
     tflops = flops / (ms * 1e-3) / 1e12
     out = {
         "metric": "rows/s and MFMA TFLOP/s (% of peak), fused LM-head+logp N=4096 H=4096 "
-                  "V=151936 bf16",
+                  "V=151936 bf16" + (", prepared weight" if prepared else ""),
         "value": round(n / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen3_8b_lm_head_linear_logp", "n": n, "h": h, "v": v,
-                   "tile_width": 256},
+        "config": {"workload": "qwen3_8b_lm_head_linear_logp" + ("_prepared" if prepared else ""),
+                   "n": n, "h": h, "v": v, "tile_width": 256},
         "tflops": round(tflops, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("linear_stats_dma",
-                                                 "qwen3_4096x4096x151936"),
-                     "kernel": "linear_stats_dma"},
+                     "traffic": None if prepared else measured_traffic(
+                         "linear_stats_dma", "qwen3_4096x4096x151936"),
+                     "kernel": "linear_logp_fwd (all launches: blocking the hidden rows, "
+                               "linear_stats_dma, the merge; linear_stats_dma is 98% of it)"},
     }
     sample = None
     if not args.no_cpu_baseline:
@@ -294,7 +299,8 @@ def bench_linear_bwd(args, torch, itl, synth, saved=False, prepared=False):
     _, lse, *rest = itl.linear_logp_fwd(hid, wt, t, return_logits=saved,
                                         logits_dtype=torch.float32)
     z = rest[0] if saved else None
-    # prepared: W^T made once per weight version, outside the timed step
+    # prepared: the weight re-laid once per weight version, outside the timed
+    # step
     wtp = itl.prepare_weight(wt) if prepared else None
     dh = torch.empty(n, h, dtype=torch.float32, device=dev)
     dw = torch.empty(v, h, dtype=torch.float32, device=dev)
@@ -303,7 +309,7 @@ def bench_linear_bwd(args, torch, itl, synth, saved=False, prepared=False):
 
     def run():
         itl.linear_logp_bwd(hid, wt, t, lse, g, dhidden_out=dh, dweight_out=dw, workspace=ws,
-                            saved_logits=z, weight_t=wtp)
+                            saved_logits=z, prepared_weight=wtp)
 
     ramp(torch, run, args.ramp_s)
     for _ in range(args.warmup):
@@ -317,7 +323,7 @@ def bench_linear_bwd(args, torch, itl, synth, saved=False, prepared=False):
         "metric": "rows/s and MFMA TFLOP/s (% of peak), fused LM-head+logp backward N=4096 "
                   "H=4096 V=151936 bf16" + (", logits saved by the forward (fp32)" if saved
                                             else ", logits recomputed")
-                  + (", prepared W^T" if prepared else ""),
+                  + (", prepared weight" if prepared else ""),
         "value": round(n / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -456,7 +462,7 @@ def main():
                     help="untimed seconds of steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--workload", default="fwd_bwd",
                     choices=["fwd_bwd", "fwd", "linear", "linear_bwd", "linear_bwd_saved",
-                             "linear_bwd_prepared"])
+                             "linear_bwd_prepared", "linear_prepared"])
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows for the CPU oracle baseline (0 = workload default)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
@@ -505,8 +511,8 @@ def main():
     runner = {"fwd_bwd": bench_fwd_bwd, "fwd": bench_fwd, "linear": bench_linear,
               "linear_bwd": bench_linear_bwd,
               "linear_bwd_saved": lambda *a: bench_linear_bwd(*a, saved=True),
-              "linear_bwd_prepared": lambda *a: bench_linear_bwd(*a, prepared=True)}[
-                  args.workload]
+              "linear_bwd_prepared": lambda *a: bench_linear_bwd(*a, prepared=True),
+              "linear_prepared": lambda *a: bench_linear(*a, prepared=True)}[args.workload]
     out, sample = runner(args, torch, itl, synth)
     if sample is not None:
         if args.workload == "fwd_bwd":

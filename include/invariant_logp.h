@@ -177,6 +177,27 @@ int32_t logp_bwd(const void* logits, int32_t dtype, int64_t n, int64_t v,
                  void* hip_stream);
 
 /*
+ * Prepared LM-head weight ("[RFC][ROCm] End-to-end optimization of bitwise
+ * VIME R/R beyond native P/P", Workstream 3: prepared [K, N] weights are
+ * reused and refreshed when the weight changes): fills `prepared` (device,
+ * caller-owned, prepared_bytes >= linear_logp_prepared_bytes(v, h), 16-byte
+ * aligned) from weight [v, ld_w] bf16 with the weight re-laid for the
+ * products' loads: the weight itself (for the forward and the backward's
+ * recomputed logits) and its transpose (for the backward's dhidden), both
+ * bf16 with the vocabulary padded with zeros to round_up(v, 256), in a
+ * layout private to the library.  linear_logp_fwd and linear_logp_bwd read
+ * it instead of the weight where it helps and give the same bits.  h a
+ * multiple of 64.  Errors: LOGP_ERR_SHAPE (sizes, a short buffer),
+ * LOGP_ERR_NULL, LOGP_ERR_ALIGN (weight rows or prepared not 16-byte
+ * aligned).  Prepare again whenever the weight changes; a prepared buffer of
+ * another weight gives wrong results, unchecked.  linear_logp_prepared_bytes
+ * gives 2 * h * round_up(v, 256) * 2 (0 for arguments that are refused).
+ */
+size_t linear_logp_prepared_bytes(int64_t v, int64_t h);
+int32_t linear_logp_prepare_weight(const void* weight, int64_t ld_w, int64_t v, int64_t h,
+                                   void* prepared, size_t prepared_bytes, void* hip_stream);
+
+/*
  * Workspace of linear_logp_fwd in bytes: the [n, T] partials (m, s, w) for
  * T = ceil(v / tile_width), the copied target logits [n] and, for n > 128, a
  * copy of hidden re-laid for the product's loads (round_up(n, 256) * h * 2
@@ -217,6 +238,10 @@ size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *               LOGP_BF16, RNE) receiving the unscaled z, or NULL ("return
  *               logits" for sampling).  logp, lse and entropy have the same
  *               bits either way.
+ *   prepared, prepared_bytes
+ *               NULL, or linear_logp_prepare_weight's buffer for this weight
+ *               (short: LOGP_ERR_SHAPE; not 16-byte aligned: LOGP_ERR_ALIGN),
+ *               read instead of weight for n > 128; the same bits.
  *   workspace   at least linear_logp_fwd_workspace_bytes(...) bytes,
  *               256-byte aligned.
  */
@@ -227,6 +252,7 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight,
                         int32_t logits_rounding, float* logp_out, float* lse_out,
                         float* entropy_out,
                         void* logits_out, int32_t logits_dtype, int64_t ld_logits,
+                        const void* prepared, size_t prepared_bytes,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
@@ -274,15 +300,14 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *               saved_dtype LOGP_F32, or LOGP_BF16 only with
  *               LOGP_ROUND_BF16 (where the bf16 logits are exactly z);
  *               otherwise LOGP_ERR_DTYPE.
- *   weight_t, weight_t_bytes
+ *   prepared, prepared_bytes
  *               NULL: the backward transposes weight into the workspace for
- *               dhidden.  Otherwise the buffer linear_logp_prepare_weight
- *               filled from this weight (weight_t_bytes >=
- *               linear_logp_weight_t_bytes(v, h), else LOGP_ERR_SHAPE;
- *               16-byte aligned, else LOGP_ERR_ALIGN), used instead: the same
- *               values, so the same bits, without the transpose (the
- *               "prepared weights" reused while the weight does not change,
- *               e.g. over the micro-batches of one optimiser step).
+ *               dhidden.  Otherwise linear_logp_prepare_weight's buffer for
+ *               this weight (short: LOGP_ERR_SHAPE; not 16-byte aligned:
+ *               LOGP_ERR_ALIGN), read instead: the same values, so the same
+ *               bits, without the transpose (the prepared weight is reused
+ *               while the weight does not change, e.g. over the micro-batches
+ *               of one optimiser step).
  *   lse         fp32 [n] from linear_logp_fwd.
  *   grad_logp   fp32 [n], the upstream gradient g.
  *   entropy, grad_entropy
@@ -302,28 +327,11 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
                         float temperature, int32_t logits_rounding, const void* saved_logits,
-                        int32_t saved_dtype, int64_t ld_saved, const void* weight_t,
-                        size_t weight_t_bytes, const float* lse, const float* grad_logp,
+                        int32_t saved_dtype, int64_t ld_saved, const void* prepared,
+                        size_t prepared_bytes, const float* lse, const float* grad_logp,
                         const float* entropy, const float* grad_entropy, int32_t out_dtype,
                         void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
-
-/*
- * Prepared LM-head weight for the backward ("[RFC][ROCm] End-to-end
- * optimization of bitwise VIME R/R beyond native P/P", Workstream 3: prepared
- * [K, N] weights are reused and refreshed when the weight changes): fills
- * weight_t (device, caller-owned, weight_t_bytes >= linear_logp_weight_t_bytes
- * (v, h), 16-byte aligned) with W^T of weight [v, ld_w] bf16 in the layout
- * the backward's dhidden product reads (opaque to the caller; bf16, the
- * vocabulary padded with zeros to round_up(v, 256)).  h a multiple of 64.
- * Errors: LOGP_ERR_SHAPE (sizes, a short buffer), LOGP_ERR_NULL,
- * LOGP_ERR_ALIGN (weight rows or weight_t not 16-byte aligned).  Prepare
- * again whenever the weight changes.  linear_logp_weight_t_bytes gives
- * h * round_up(v, 256) * 2 (0 for arguments that are refused).
- */
-size_t linear_logp_weight_t_bytes(int64_t v, int64_t h);
-int32_t linear_logp_prepare_weight(const void* weight, int64_t ld_w, int64_t v, int64_t h,
-                                   void* weight_t, size_t weight_t_bytes, void* hip_stream);
 
 /* Short English text for a status code (static storage, host memory). */
 const char* logp_status_str(int32_t status);

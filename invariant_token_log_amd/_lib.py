@@ -42,12 +42,12 @@ _SIGNATURES = {
     "linear_logp_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "linear_logp_fwd": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
                                _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _sz,
-                               _vp]),
+                               _vp, _sz, _vp]),
     "linear_logp_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "linear_logp_bwd": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
                                _i32, _f32, _i32, _vp, _i32, _i64, _vp, _sz, _vp, _vp, _vp, _vp,
                                _i32, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
-    "linear_logp_weight_t_bytes": (_sz, [_i64, _i64]),
+    "linear_logp_prepared_bytes": (_sz, [_i64, _i64]),
     "linear_logp_prepare_weight": (_i32, [_vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "logp_status_str": (ctypes.c_char_p, [_i32]),
     "logp_contract_id": (ctypes.c_char_p, []),

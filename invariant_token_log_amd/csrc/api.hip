@@ -186,8 +186,9 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
                         float temperature, int32_t logits_rounding, float* logp_out,
                         float* lse_out, float* entropy_out, void* logits_out,
-                        int32_t logits_dtype, int64_t ld_logits, void* workspace,
-                        size_t workspace_bytes, void* hip_stream) {
+                        int32_t logits_dtype, int64_t ld_logits, const void* prepared,
+                        size_t prepared_bytes, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
   if (n < 0 || v < 1 || h < 1 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
   if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
   if (logits_out && logits_dtype != LOGP_F32 && logits_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
@@ -205,6 +206,10 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
   if (!hidden || !weight || !targets || !logp_out) return LOGP_ERR_NULL;
   if (!aligned16(hidden, ld_h, LOGP_BF16) || !aligned16(weight, ld_w, LOGP_BF16))
     return LOGP_ERR_ALIGN;
+  if (prepared) {
+    if (prepared_bytes < linear_logp_prepared_bytes(v, h)) return LOGP_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(prepared) % 16) return LOGP_ERR_ALIGN;
+  }
   if (!workspace || workspace_bytes < need ||
       reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return LOGP_ERR_WORKSPACE;
@@ -220,6 +225,9 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
                               ignore_index, pm, ps, pt, inv_temperature(temperature),
                               logits_rounding == LOGP_ROUND_BF16 ? 1 : 0, pw, logits_out,
                               logits_dtype == LOGP_BF16 ? 1 : 0, ld_logits,
+                              prepared ? itl::prepared_blocked_w(
+                                             static_cast<const uint16_t*>(prepared))
+                                       : nullptr,
                               reinterpret_cast<uint16_t*>(ws + hb_off), s);
   itl::launch_fwd_merge(pm, ps, pw, pt, n, static_cast<int>(ntiles), ntiles, 1, v, tg,
                         ignore_index, logp_out, lse_out, entropy_out, nullptr, s);
@@ -236,8 +244,8 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int64_t n, int64_t h, int64_t v, const void* targets,
                         int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
                         float temperature, int32_t logits_rounding, const void* saved_logits,
-                        int32_t saved_dtype, int64_t ld_saved, const void* weight_t,
-                        size_t weight_t_bytes, const float* lse, const float* grad_logp,
+                        int32_t saved_dtype, int64_t ld_saved, const void* prepared,
+                        size_t prepared_bytes, const float* lse, const float* grad_logp,
                         const float* entropy, const float* grad_entropy, int32_t out_dtype,
                         void* dhidden,
                         int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
@@ -258,9 +266,9 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
     if (ld_saved < v) return LOGP_ERR_SHAPE;
     if (!aligned16(saved_logits, ld_saved, saved_dtype)) return LOGP_ERR_ALIGN;
   }
-  if (weight_t) {
-    if (weight_t_bytes < linear_logp_weight_t_bytes(v, h)) return LOGP_ERR_SHAPE;
-    if (reinterpret_cast<uintptr_t>(weight_t) % 16) return LOGP_ERR_ALIGN;
+  if (prepared) {
+    if (prepared_bytes < linear_logp_prepared_bytes(v, h)) return LOGP_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(prepared) % 16) return LOGP_ERR_ALIGN;
   }
   if (!dhidden && !dweight) return LOGP_ERR_NULL;
   if ((dhidden && ld_dh < h) || (dweight && ld_dw < h)) return LOGP_ERR_SHAPE;
@@ -278,7 +286,7 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                          static_cast<const uint16_t*>(weight), ld_w, n, h, v,
                          targets_of(targets, target_dtype), ignore_index, saved_logits,
                          saved_dtype == LOGP_BF16 ? 1 : 0, ld_saved,
-                         static_cast<const uint16_t*>(weight_t), lse, grad_logp,
+                         static_cast<const uint16_t*>(prepared), lse, grad_logp,
                          inv_temperature(temperature), logits_rounding == LOGP_ROUND_BF16 ? 1 : 0,
                          entropy, grad_entropy,
                          out_dtype == LOGP_BF16, dhidden, ld_dh, dweight, ld_dw,
@@ -286,21 +294,21 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   return hip_status();
 }
 
-size_t linear_logp_weight_t_bytes(int64_t v, int64_t h) {
-  if (v < 1 || h < 64 || h % 64) return 0;
-  return static_cast<size_t>(h) * static_cast<size_t>((v + 255) / 256 * 256) * 2;
+size_t linear_logp_prepared_bytes(int64_t v, int64_t h) {
+  if (v < 1 || h < 64 || h % 64 || v > (int64_t{1} << 31)) return 0;
+  return static_cast<size_t>(itl::prepared_bytes(v, h));
 }
 
 int32_t linear_logp_prepare_weight(const void* weight, int64_t ld_w, int64_t v, int64_t h,
-                                   void* weight_t, size_t weight_t_bytes, void* hip_stream) {
+                                   void* prepared, size_t prepared_bytes, void* hip_stream) {
   if (v < 1 || h < 64 || h % 64 || ld_w < h || v > (int64_t{1} << 31)) return LOGP_ERR_SHAPE;
-  if (weight_t_bytes < linear_logp_weight_t_bytes(v, h)) return LOGP_ERR_SHAPE;
-  if (!weight || !weight_t) return LOGP_ERR_NULL;
-  if (!aligned16(weight, ld_w, LOGP_BF16) || reinterpret_cast<uintptr_t>(weight_t) % 16)
+  if (prepared_bytes < linear_logp_prepared_bytes(v, h)) return LOGP_ERR_SHAPE;
+  if (!weight || !prepared) return LOGP_ERR_NULL;
+  if (!aligned16(weight, ld_w, LOGP_BF16) || reinterpret_cast<uintptr_t>(prepared) % 16)
     return LOGP_ERR_ALIGN;
   (void)hipGetLastError();
   itl::launch_prepare_weight(static_cast<const uint16_t*>(weight), ld_w, v, h,
-                             static_cast<uint16_t*>(weight_t),
+                             static_cast<uint16_t*>(prepared),
                              static_cast<hipStream_t>(hip_stream));
   return hip_status();
 }

@@ -46,14 +46,16 @@ void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, 
 // Fused LM-head statistics: writes the row-major [n, T] partials (and the
 // entropy moments when pw is set) and the target logits of every active row
 // (T = ceil(v / 256)).  The logits are multiplied by inv_t before any
-// statistic; z (optional) receives the unscaled logits, fp32 or bf16.  hb:
+// statistic; z (optional) receives the unscaled logits, fp32 or bf16.  wblk:
+// the K32-blocked weight of a prepared weight (prepared_blocked_w), or null;
+// the 256-row tile then reads it instead of weight (the same values).  hb:
 // linear_fwd_blocked_bytes(n, h) bytes of scratch for the K32-blocked copy of
 // hidden (unused, may be null, when that is 0).
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,
                             int64_t ld_w, int64_t n, int64_t h, int64_t v, Targets targets,
                             int64_t ignore, float* pm, float* ps, float* pt, float inv_t,
                             int32_t round_bf16, float* pw, void* z, int32_t z_bf16, int64_t ld_z,
-                            uint16_t* hb, hipStream_t s);
+                            const uint16_t* wblk, uint16_t* hb, hipStream_t s);
 
 // Bytes of the forward's blocked hidden copy: round_up(n, 256) * h * 2 when
 // the 256-row tile runs (n > 128), else 0.
@@ -76,21 +78,26 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
 // inv_t: reciprocal temperature (1 = none); ent / gent: row entropy and its
 // upstream gradient (both null = no entropy term).  zsaved (fp32, or bf16
 // with z_bf16; [n, ld_z]) holds the forward's unscaled logits to read instead
-// of recomputing them, or is null.  weight_t (or null) is the caller's
-// prepared W^T (launch_prepare_weight), used for dh instead of transposing W
-// into the workspace.
+// of recomputing them, or is null.  prepared (or null) is the caller's
+// prepared weight (launch_prepare_weight): its blocked W feeds the recomputed
+// product and its W^T the dh product instead of a transpose of W into the
+// workspace.
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
                        const void* zsaved, int32_t z_bf16, int64_t ld_z,
-                       const uint16_t* weight_t, const float* lse,
+                       const uint16_t* prepared, const float* lse,
                        const float* grad, float inv_t, int32_t round_bf16, const float* ent,
                        const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
                        int64_t ld_dw, char* ws, hipStream_t s);
 
-// W^T [h rows, K = round_up(v, 256)] K32-blocked (mfma_gemm.h), columns v ..
-// zero, from W [v, ld_w].
+// Prepared weight, bf16, both parts K32-blocked (mfma_gemm.h) with vp =
+// round_up(v, 256): W [vp rows, K = h] (rows v.. zero), then W^T [h rows,
+// K = vp] (columns v.. zero), from W [v, ld_w]; prepared_bytes(v, h) bytes.
+int64_t prepared_bytes(int64_t v, int64_t h);
+inline const uint16_t* prepared_blocked_w(const uint16_t* p) { return p; }
+const uint16_t* prepared_blocked_wt(const uint16_t* p, int64_t v, int64_t h);
 void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int64_t h,
-                           uint16_t* weight_t, hipStream_t s);
+                           uint16_t* prepared, hipStream_t s);
 
 // dst = the K32-blocked [rows_p, K = k] copy of src [rows, ld] (rows_p, k
 // multiples of 16 and 32; rows past `rows` zero).

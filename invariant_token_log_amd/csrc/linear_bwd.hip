@@ -138,6 +138,9 @@ struct SmemDz {
   int code[kT];
 };
 
+// hidden K32-blocked (mblocks * 256 rows); weight row-major, or K32-blocked
+// with vblocks * 256 rows when WBLK (a prepared weight).
+template <bool WBLK>
 __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
@@ -186,9 +189,9 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // hidden: K32-blocked with mblocks * 256 rows
-  gemm::mainloop<true, false>(sm.u.st, hidden, 0, m0, static_cast<int64_t>(mblocks) * kT, weight,
-                              ld_w, v0, v, static_cast<int>(hdim / gemm::kK), acc);
+  gemm::mainloop<true, WBLK>(sm.u.st, hidden, 0, m0, static_cast<int64_t>(mblocks) * kT, weight,
+                             ld_w, v0, WBLK ? static_cast<int64_t>(vblocks) * kT : v,
+                             static_cast<int>(hdim / gemm::kK), acc);
   __syncthreads();
 
   // dz of every element (dz_value; 0 on ignored / padded rows and columns),
@@ -482,7 +485,7 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
                        const void* zsaved, int32_t z_bf16, int64_t ld_z,
-                       const uint16_t* weight_t, const float* lse,
+                       const uint16_t* prepared, const float* lse,
                        const float* grad, float inv_t, int32_t round_bf16, const float* ent,
                        const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
                        int64_t ld_dw, char* ws, hipStream_t s) {
@@ -507,9 +510,15 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
   if (!zsaved) {
     launch_block_rows(hidden, ld_h, n, l.np, h, hb, s);
-    hipLaunchKernelGGL(linear_dz_kernel, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0, s,
-                       hb, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                       targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, dzt);
+    if (prepared)
+      hipLaunchKernelGGL(linear_dz_kernel<true>, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0,
+                         s, hb, ld_h, prepared_blocked_w(prepared), int64_t{0}, n, h, v, mblocks,
+                         vblocks, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
+                         ent, gent, dz, dzt);
+    else
+      hipLaunchKernelGGL(linear_dz_kernel<false>, dim3(mblocks * vblocks), dim3(gemm::kThreads),
+                         0, s, hb, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
+                         targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, dzt);
   } else {
     const int64_t rb = l.np / kST;
     const dim3 grid(static_cast<unsigned>(l.vp / kST), static_cast<unsigned>(rb < 65535 ? rb : 65535));
@@ -525,12 +534,11 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   if (dh) {
     // W^T: the caller's prepared copy (linear_logp_prepare_weight, the same
     // values) or made here
-    if (!weight_t) {
+    const uint16_t* wtb = prepared ? prepared_blocked_wt(prepared, v, h) : wt;
+    if (!prepared)
       hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
                          dim3(256), 0, s, weight, ld_w, v, l.vp, wt);
-      weight_t = wt;
-    }
-    launch_gemm(bf16_out, dz, l.np, weight_t, h, l.vp, n, h, dh, ld_dh, s);
+    launch_gemm(bf16_out, dz, l.np, wtb, h, l.vp, n, h, dh, ld_dh, s);
   }
   if (dw) {
     hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.np)),
@@ -539,11 +547,18 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   }
 }
 
+int64_t prepared_bytes(int64_t v, int64_t h) { return 2 * h * round_tile(v) * 2; }
+
+const uint16_t* prepared_blocked_wt(const uint16_t* p, int64_t v, int64_t h) {
+  return p + h * round_tile(v);
+}
+
 void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int64_t h,
-                           uint16_t* weight_t, hipStream_t s) {
+                           uint16_t* prepared, hipStream_t s) {
   const int64_t vp = round_tile(v);
+  launch_block_rows(weight, ld_w, v, vp, h, prepared, s);
   hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(vp)),
-                     dim3(256), 0, s, weight, ld_w, v, vp, weight_t);
+                     dim3(256), 0, s, weight, ld_w, v, vp, prepared + h * vp);
 }
 
 void launch_block_rows(const uint16_t* src, int64_t ld, int64_t rows, int64_t rows_p, int64_t k,

@@ -342,6 +342,9 @@ struct SmemDma {
   Reduce<256> rd;
 };
 
+// hidden K32-blocked (mblocks * 256 rows); weight row-major, or K32-blocked
+// with round_up(v, 256) rows when WBLK (a prepared weight).
+template <bool WBLK>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
@@ -366,9 +369,9 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // hidden: K32-blocked with mblocks * 256 rows
-  gemm::mainloop<true, false>(sm.st, hidden, 0, m0, static_cast<int64_t>(mblocks) * 256, weight,
-                              ld_w, v0, v, static_cast<int>(hdim / BK), acc);
+  gemm::mainloop<true, WBLK>(sm.st, hidden, 0, m0, static_cast<int64_t>(mblocks) * 256, weight,
+                             ld_w, v0, WBLK ? static_cast<int64_t>(vblocks) * BN : v,
+                             static_cast<int>(hdim / BK), acc);
   __syncthreads();
   stats_epilogue<8, 4, 256, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * 128, wn * 64, li,
                                                         g, tid, m0, v0, vb,
@@ -428,7 +431,7 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                             int64_t ld_w, int64_t n, int64_t h, int64_t v, Targets targets,
                             int64_t ignore, float* pm, float* ps, float* pt, float inv_t,
                             int32_t round_bf16, float* pw, void* z, int32_t z_bf16, int64_t ld_z,
-                            uint16_t* hb, hipStream_t s) {
+                            const uint16_t* wblk, uint16_t* hb, hipStream_t s) {
   const int vblocks = static_cast<int>((v + BN - 1) / BN);
   const int32_t z_vec = z && reinterpret_cast<uintptr_t>(z) % 16 == 0 &&
                         (ld_z * (z_bf16 ? 2 : 4)) % 16 == 0;
@@ -444,9 +447,14 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     launch_block_rows(hidden, ld_h, n, static_cast<int64_t>(mblocks) * 256, h, hb, s);
-    hipLaunchKernelGGL(linear_stats_dma, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,
-                       hb, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                       targets.is32, ignore, pm, ps, pt, ex);
+    if (wblk)
+      hipLaunchKernelGGL(linear_stats_dma<true>, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,
+                         hb, ld_h, wblk, int64_t{0}, n, h, v, mblocks, vblocks, targets.p,
+                         targets.is32, ignore, pm, ps, pt, ex);
+    else
+      hipLaunchKernelGGL(linear_stats_dma<false>, dim3(mblocks * vblocks), dim3(kDmaThreads), 0,
+                         s, hb, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
+                         targets.is32, ignore, pm, ps, pt, ex);
   }
 }
 

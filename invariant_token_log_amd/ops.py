@@ -152,13 +152,15 @@ def _rounding(round_logits):
 def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEAR_TILE,
                     logp_out=None, lse_out=None, workspace=None, temperature=1.0,
                     return_entropy=False, entropy_out=None, return_logits=False,
-                    logits_dtype=torch.bfloat16, logits_out=None, round_logits=False):
+                    logits_dtype=torch.bfloat16, logits_out=None, round_logits=False,
+                    prepared_weight=None):
     """Fused LM-head + selected-token log-probability without storing logits.
     hidden bf16 [N, H], weight bf16 [V, H].  Returns (logp [N], lse [N]), then
     the entropy [N] with return_entropy and the unscaled logits [N, V] with
     return_logits.  The statistics see the logits times 1 / temperature; with
     round_logits the logits are first rounded to bf16 (RNE), as an unfused
-    bf16 LM head would store them."""
+    bf16 LM head would store them.  prepared_weight: prepare_weight(weight),
+    read instead of the weight (same bits)."""
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     t1 = _targets(targets, n)
     dev = hidden.device
@@ -178,6 +180,7 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
                           or z.stride(1) != 1):
         raise ValueError("logits_out must be [N, V] of logits_dtype with contiguous rows")
     L = _lib.lib()
+    pw = _prepared(prepared_weight, L, v, h, dev)
     need = L.linear_logp_fwd_workspace_bytes(n, h, v, tile_width)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -187,7 +190,8 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
                                float(temperature), _rounding(round_logits), logp_out.data_ptr(),
                                lse_out.data_ptr(), _ptr(ent), _ptr(z), _DTYPES[logits_dtype],
                                (z.stride(0) if n > 1 else v) if z is not None else 0,
-                               workspace.data_ptr(), workspace.numel(), _stream(dev))
+                               _ptr(pw), _nbytes(pw), workspace.data_ptr(), workspace.numel(),
+                               _stream(dev))
     check("linear_logp_fwd", st)
     out = (logp_out, lse_out)
     if return_entropy:
@@ -201,15 +205,15 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                     tile_width=LINEAR_TILE, need_dhidden=True, need_dweight=True,
                     out_dtype=torch.float32, dhidden_out=None, dweight_out=None,
                     workspace=None, temperature=1.0, entropy=None, grad_entropy=None,
-                    round_logits=False, saved_logits=None, weight_t=None):
+                    round_logits=False, saved_logits=None, prepared_weight=None):
     """Backward of the fused LM head + logp: (dhidden [N, H] or None,
     dweight [V, H] or None) in out_dtype (float32 accumulators or their
     bfloat16 rounding), from the forward's lse (and entropy) and the upstream
     gradients.  temperature and round_logits must be the forward's.
     saved_logits: the forward's logits output ([N, V] float32, or bfloat16
     with round_logits), read instead of recomputing h W^T; same bits.
-    weight_t: prepare_weight(weight), used for dhidden instead of transposing
-    the weight on every call; same bits."""
+    prepared_weight: prepare_weight(weight), read instead of the weight and
+    its transpose made on every call; same bits."""
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
@@ -235,11 +239,8 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     if z is not None and (z.dim() != 2 or tuple(z.shape) != (n, v) or z.stride(1) != 1
                           or z.dtype not in (torch.float32, torch.bfloat16)):
         raise ValueError("saved_logits must be [N, V] float32 / bfloat16 with contiguous rows")
-    wt = weight_t
     L = _lib.lib()
-    if wt is not None and (not wt.is_contiguous() or wt.device != dev
-                           or wt.numel() * wt.element_size() < L.linear_logp_weight_t_bytes(v, h)):
-        raise ValueError("weight_t must be prepare_weight(weight) on the weight's device")
+    pw = _prepared(prepared_weight, L, v, h, dev)
     need = L.linear_logp_bwd_workspace_bytes(n, h, v, tile_width)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -249,9 +250,8 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                                t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
                                float(temperature), _rounding(round_logits), _ptr(z),
                                _DTYPES[z.dtype] if z is not None else 0,
-                               max(z.stride(0), v) if z is not None else 0, _ptr(wt),
-                               wt.numel() * wt.element_size() if wt is not None else 0,
-                               lse.data_ptr(),
+                               max(z.stride(0), v) if z is not None else 0, _ptr(pw),
+                               _nbytes(pw), lse.data_ptr(),
                                g.data_ptr(), _ptr(ent),
                                _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
                                (dh.stride(0) if n > 1 else h) if dh is not None else 0,
@@ -261,21 +261,33 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     return dh, dw
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def _prepared(p, L, v, h, dev):
+    if p is not None and (not p.is_contiguous() or p.device != dev
+                          or _nbytes(p) < L.linear_logp_prepared_bytes(v, h)):
+        raise ValueError("prepared_weight must be prepare_weight(weight) on the weight's device")
+    return p
+
+
 def prepare_weight(weight, out=None):
-    """The LM-head weight [V, H] bfloat16 prepared for the fused backward's
-    dhidden product (W^T, vocabulary padded with zeros to a multiple of 256,
-    in the library's own layout): a uint8 buffer of
-    linear_logp_weight_t_bytes(V, H) bytes (or `out`, a contiguous buffer at
-    least that large).  Reuse it over the backward calls of one weight
-    version and prepare it again after the weight changes (an optimiser
-    step, a weight update)."""
+    """The LM-head weight [V, H] bfloat16 re-laid for the fused products'
+    loads (the weight and its transpose, vocabulary padded with zeros to a
+    multiple of 256, in the library's own layout): a uint8 buffer of
+    linear_logp_prepared_bytes(V, H) bytes (or `out`, a contiguous buffer at
+    least that large) for linear_logp_fwd / linear_logp_bwd.  Reuse it over
+    the calls of one weight version and prepare it again after the weight
+    changes (an optimiser step, a weight update): a stale one gives wrong
+    results."""
     if weight.dtype != torch.bfloat16 or weight.dim() != 2 or weight.stride(1) != 1:
         raise ValueError("weight must be [V, H] bfloat16 with contiguous rows")
     v, h = weight.shape
     if not weight.is_cuda:
         raise ValueError("weight must be a GPU tensor")
     L = _lib.lib()
-    need = L.linear_logp_weight_t_bytes(v, h)
+    need = L.linear_logp_prepared_bytes(v, h)
     if need == 0:
         raise ValueError("H must be a positive multiple of 64")
     if out is None:
@@ -340,13 +352,14 @@ def _padded_logits(n, v, dtype, device):
 class _LinearLogp(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, targets, ignore_index, temperature, with_entropy,
-                round_logits, save_logits, weight_t):
+                round_logits, save_logits, prepared_weight):
         zdt = torch.bfloat16 if round_logits else torch.float32
         zbuf = _padded_logits(hidden.shape[0], weight.shape[0], zdt, hidden.device) \
             if save_logits else None
         out = linear_logp_fwd(hidden, weight, targets, ignore_index, temperature=temperature,
                               return_entropy=with_entropy, round_logits=round_logits,
-                              return_logits=save_logits, logits_dtype=zdt, logits_out=zbuf)
+                              return_logits=save_logits, logits_dtype=zdt, logits_out=zbuf,
+                              prepared_weight=prepared_weight)
         logp, lse = out[0], out[1]
         ent = out[2] if with_entropy else None
         z = out[-1] if save_logits else None
@@ -355,7 +368,7 @@ class _LinearLogp(torch.autograd.Function):
         ctx.temperature = temperature
         ctx.with_entropy = with_entropy
         ctx.round_logits = round_logits
-        ctx.weight_t = weight_t
+        ctx.prepared_weight = prepared_weight
         if with_entropy:
             return logp, ent
         return logp
@@ -371,12 +384,13 @@ class _LinearLogp(torch.autograd.Function):
                                  out_dtype=torch.bfloat16, temperature=ctx.temperature,
                                  entropy=ent if ctx.with_entropy else None, grad_entropy=gent,
                                  round_logits=ctx.round_logits, saved_logits=z,
-                                 weight_t=ctx.weight_t)
+                                 prepared_weight=ctx.prepared_weight)
         return dh, dw, None, None, None, None, None, None, None
 
 
 def linear_logp(hidden, weight, target_ids, ignore_index=-100, temperature=1.0,
-                return_entropy=False, round_logits=False, save_logits=False, weight_t=None):
+                return_entropy=False, round_logits=False, save_logits=False,
+                prepared_weight=None):
     """Differentiable fused LM head + selected-token log-probability:
     hidden bf16 [N, H], weight bf16 [V, H] -> float32 logp [N] (and the
     entropy [N] with return_entropy) of softmax(hidden weight^T / temperature);
@@ -385,7 +399,7 @@ def linear_logp(hidden, weight, target_ids, ignore_index=-100, temperature=1.0,
     bf16 gradients of hidden and weight through linear_logp_bwd, recomputing
     the logits, or, with save_logits, reading the logits the forward kept
     ([N, V] float32, bfloat16 with round_logits; same bits, more memory).
-    weight_t: prepare_weight(weight) of this weight version, reused by the
-    backward instead of transposing the weight again (same bits)."""
+    prepared_weight: prepare_weight(weight) of this weight version, read by
+    the forward and the backward instead of the weight (same bits)."""
     return _LinearLogp.apply(hidden, weight, target_ids, ignore_index, temperature,
-                             return_entropy, round_logits, save_logits, weight_t)
+                             return_entropy, round_logits, save_logits, prepared_weight)

@@ -118,12 +118,12 @@ def test_linear_argument_errors(L):
     def lin(**kw):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
                  targets=FAKE, tdt=0, tile=256, temp=1.0, rnd=0, logp=FAKE, lse=FAKE,
-                 ent=None, z=None, zdt=1, ldz=0, ws=FAKE, ws_bytes=1 << 40)
+                 ent=None, z=None, zdt=1, ldz=0, pw=None, pwb=0, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_fwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
                                  a["v"], a["targets"], a["tdt"], -100, a["tile"], a["temp"],
                                  a["rnd"], a["logp"], a["lse"], a["ent"], a["z"], a["zdt"],
-                                 a["ldz"], a["ws"], a["ws_bytes"], None)
+                                 a["ldz"], a["pw"], a["pwb"], a["ws"], a["ws_bytes"], None)
     for bad in (0.0, -1.0, float("inf"), float("nan")):
         assert lin(temp=bad) == _lib.LOGP_ERR_VALUE, bad
     for bad in (-1, 2, 7):
@@ -132,6 +132,9 @@ def test_linear_argument_errors(L):
     assert lin(z=FAKE, zdt=0, ldz=100) == _lib.LOGP_ERR_SHAPE
     assert lin(tdt=9) == _lib.LOGP_ERR_DTYPE
     assert lin(tile=4096) == _lib.LOGP_ERR_TILE
+    # prepared weight: at least linear_logp_prepared_bytes, 16-byte aligned
+    assert lin(pw=FAKE, pwb=2491416576 - 1) == _lib.LOGP_ERR_SHAPE
+    assert lin(pw=FAKE + 8, pwb=2491416576) == _lib.LOGP_ERR_ALIGN
     assert lin(h=100, ld_h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
     assert lin(ld_h=10) == _lib.LOGP_ERR_SHAPE
     assert lin(h_ptr=None) == _lib.LOGP_ERR_NULL
@@ -168,9 +171,9 @@ def test_linear_bwd_argument_errors(L):
     assert lb(z=FAKE, zdt=_lib.LOGP_F32, ldz=100) == _lib.LOGP_ERR_SHAPE
     assert lb(z=FAKE + 4, zdt=_lib.LOGP_F32, ldz=151936) == _lib.LOGP_ERR_ALIGN
     assert lb(z=FAKE, zdt=_lib.LOGP_F32, ldz=151937) == _lib.LOGP_ERR_ALIGN
-    # prepared weight: at least linear_logp_weight_t_bytes, 16-byte aligned
-    assert lb(wt=FAKE, ldwt=4096 * 152064 * 2 - 1) == _lib.LOGP_ERR_SHAPE
-    assert lb(wt=FAKE + 8, ldwt=4096 * 152064 * 2) == _lib.LOGP_ERR_ALIGN
+    # prepared weight: at least linear_logp_prepared_bytes, 16-byte aligned
+    assert lb(wt=FAKE, ldwt=2491416576 - 1) == _lib.LOGP_ERR_SHAPE
+    assert lb(wt=FAKE + 8, ldwt=2491416576) == _lib.LOGP_ERR_ALIGN
     assert lb(ent=FAKE) == _lib.LOGP_ERR_NULL
     assert lb(tdt=5) == _lib.LOGP_ERR_DTYPE
     assert lb(out=2) == _lib.LOGP_ERR_DTYPE
@@ -200,11 +203,11 @@ def test_linear_bwd_argument_errors(L):
 
 def test_prepare_weight_argument_errors(L):
     def pw(**kw):
-        a = dict(w=FAKE, ld_w=4096, v=151936, h=4096, wt=FAKE, ldwt=4096 * 152064 * 2)
+        a = dict(w=FAKE, ld_w=4096, v=151936, h=4096, wt=FAKE, ldwt=2491416576)
         a.update(kw)
         return L.linear_logp_prepare_weight(a["w"], a["ld_w"], a["v"], a["h"], a["wt"],
                                             a["ldwt"], None)
-    assert pw(ldwt=4096 * 152064 * 2 - 2) == _lib.LOGP_ERR_SHAPE
+    assert pw(ldwt=2491416576 - 2) == _lib.LOGP_ERR_SHAPE
     assert pw(v=0) == _lib.LOGP_ERR_SHAPE
     assert pw(h=100, ld_w=100) == _lib.LOGP_ERR_SHAPE
     assert pw(ld_w=4000) == _lib.LOGP_ERR_SHAPE
@@ -213,7 +216,8 @@ def test_prepare_weight_argument_errors(L):
     assert pw(wt=FAKE + 8) == _lib.LOGP_ERR_ALIGN
     assert pw(ld_w=4100) == _lib.LOGP_ERR_ALIGN
     assert pw(w=FAKE + 2) == _lib.LOGP_ERR_ALIGN
-    assert L.linear_logp_weight_t_bytes(151936, 4096) == 4096 * 152064 * 2
-    assert L.linear_logp_weight_t_bytes(1, 64) == 64 * 256 * 2
-    assert L.linear_logp_weight_t_bytes(0, 4096) == 0
-    assert L.linear_logp_weight_t_bytes(151936, 100) == 0
+    # the weight and its transpose, vocabulary padded to 256
+    assert L.linear_logp_prepared_bytes(151936, 4096) == 2 * 4096 * 152064 * 2
+    assert L.linear_logp_prepared_bytes(1, 64) == 2 * 64 * 256 * 2
+    assert L.linear_logp_prepared_bytes(0, 4096) == 0
+    assert L.linear_logp_prepared_bytes(151936, 100) == 0

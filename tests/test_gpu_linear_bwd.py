@@ -242,43 +242,62 @@ def test_saved_bf16_logits_rounded_variant():
         assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
 
 
-def _blocked_wt(w, v, hd):
-    """W^T [H, round_up(V, 256)] (zero columns past V) in the K32-blocked
-    order of the product loads: element (r, k) at
-    ((r // 16) * (Vp // 32) + k // 32) * 512 + (r % 16) * 32 + k % 32."""
-    vp = (v + 255) // 256 * 256
-    wt = np.zeros((hd, vp), dtype=np.uint16)
-    wt[:, :v] = w.view(torch.int16).cpu().numpy().astype(np.uint16).T
-    return wt.reshape(hd // 16, 16, vp // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
+def _blocked(x, rows_p, k):
+    """x [rows, k] (bf16 bits as uint16) padded with zero rows to rows_p, in
+    the K32-blocked order of the product loads: element (r, c) at
+    ((r // 16) * (k // 32) + c // 32) * 512 + (r % 16) * 32 + c % 32."""
+    out = np.zeros((rows_p, k), dtype=np.uint16)
+    out[: x.shape[0]] = x
+    return out.reshape(rows_p // 16, 16, k // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
 
 
-@pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (257, 64, 300), (1, 128, 529)])
+@pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (257, 64, 300), (1, 128, 529),
+                                    (300, 128, 1000)])
 def test_prepared_weight_same_bits(n, hd, v):
-    """prepare_weight writes W^T (zero columns up to round_up(V, 256)) in the
-    blocked order; the backward reading it gives dh (and dW) with the same
-    bits as the one that transposes the weight itself, also through
-    autograd, into a larger buffer and after the buffer held other values."""
+    """prepare_weight writes the weight [Vp, H] and its transpose [H, Vp]
+    (zero vocabulary padding up to Vp = round_up(V, 256)) in the blocked
+    order; the forward and the backward reading it give the same bits as the
+    calls without it, also through autograd, into a larger buffer and after
+    the buffer held other values."""
     h, w, t, g = _case(n, hd, v, seed=7 * n + v)
-    need = itl.lib().linear_logp_weight_t_bytes(v, hd)
-    wt = itl.prepare_weight(w)
-    assert wt.dtype == torch.uint8 and wt.numel() == need
-    got = wt.view(torch.int16).cpu().numpy().astype(np.uint16)
-    assert np.array_equal(got, _blocked_wt(w, v, hd))
+    vp = (v + 255) // 256 * 256
+    need = itl.lib().linear_logp_prepared_bytes(v, hd)
+    assert need == 2 * hd * vp * 2
+    pw = itl.prepare_weight(w)
+    assert pw.dtype == torch.uint8 and pw.numel() == need
+    got = pw.view(torch.int16).cpu().numpy().astype(np.uint16)
+    wn = w.view(torch.int16).cpu().numpy().astype(np.uint16)
+    assert np.array_equal(got[: hd * vp], _blocked(wn, vp, hd))
+    wt = np.zeros((hd, vp), dtype=np.uint16)
+    wt[:, :v] = wn.T
+    assert np.array_equal(got[hd * vp:], _blocked(wt, hd, vp))
     big = torch.full((need + 4096,), 7, dtype=torch.uint8, device=dev())
-    wt2 = itl.prepare_weight(w, out=big)
-    assert torch.equal(wt2[:need], wt) and bool((wt2[need:] == 7).all())
+    pw2 = itl.prepare_weight(w, out=big)
+    assert torch.equal(pw2[:need], pw) and bool((pw2[need:] == 7).all())
+    for temp, with_ent in ((1.0, False), (0.7, True)):
+        ref = itl.linear_logp_fwd(h, w, t, temperature=temp, return_entropy=with_ent,
+                                  return_logits=True, logits_dtype=torch.float32)
+        for prep in (pw, pw2):
+            got_f = itl.linear_logp_fwd(h, w, t, temperature=temp, return_entropy=with_ent,
+                                        return_logits=True, logits_dtype=torch.float32,
+                                        prepared_weight=prep)
+            for a, b in zip(ref, got_f):
+                assert torch.equal(bits(a), bits(b))
     _, lse = itl.linear_logp_fwd(h, w, t)
     for out_dtype in (torch.float32, torch.bfloat16):
         dh0, dw0 = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype)
-        for prep in (wt, wt2):
-            dh1, dw1 = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype, weight_t=prep)
+        for prep in (pw, pw2):
+            dh1, dw1 = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype,
+                                           prepared_weight=prep)
             assert torch.equal(dh0, dh1) and torch.equal(dw0, dw1)
     with pytest.raises(ValueError):
-        itl.linear_logp_bwd(h, w, t, lse, g, weight_t=wt[: need - 256])
+        itl.linear_logp_bwd(h, w, t, lse, g, prepared_weight=pw[: need - 256])
+    with pytest.raises(ValueError):
+        itl.linear_logp_fwd(h, w, t, prepared_weight=pw[: need - 256])
     grads = []
-    for prep in (None, wt):
+    for prep in (None, pw):
         hh = h.clone().requires_grad_(True)
         ww = w.clone().requires_grad_(True)
-        (itl.linear_logp(hh, ww, t, weight_t=prep) * g).sum().backward()
+        (itl.linear_logp(hh, ww, t, prepared_weight=prep) * g).sum().backward()
         grads.append((hh.grad, ww.grad))
     assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
