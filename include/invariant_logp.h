@@ -241,7 +241,7 @@ size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *   prepared, prepared_bytes
  *               NULL, or linear_logp_prepare_weight's buffer for this weight
  *               (short: LOGP_ERR_SHAPE; not 16-byte aligned: LOGP_ERR_ALIGN),
- *               read instead of weight for n > 128; the same bits.
+ *               read instead of weight; the same bits.
  *   workspace   at least linear_logp_fwd_workspace_bytes(...) bytes,
  *               256-byte aligned.
  */

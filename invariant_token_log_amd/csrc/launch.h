@@ -48,7 +48,7 @@ void launch_bwd(int dtype, bool vec, const void* logits, int64_t ld, int64_t n, 
 // (T = ceil(v / 256)).  The logits are multiplied by inv_t before any
 // statistic; z (optional) receives the unscaled logits, fp32 or bf16.  wblk:
 // the K32-blocked weight of a prepared weight (prepared_blocked_w), or null;
-// the 256-row tile then reads it instead of weight (the same values).  hb:
+// the tiles then read it instead of weight (the same values).  hb:
 // linear_fwd_blocked_bytes(n, h) bytes of scratch for the K32-blocked copy of
 // hidden (unused, may be null, when that is 0).
 void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight,

@@ -390,7 +390,7 @@ struct SmemNarrow {
   Reduce<ROWS> rd;
 };
 
-template <int ROWS>
+template <int ROWS, bool WBLK>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
@@ -417,8 +417,9 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  gemm::mainloop_narrow<ROWS>(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
-                              static_cast<int>(hdim / BK), acc);
+  gemm::mainloop_narrow<ROWS, WBLK>(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0,
+                                    WBLK ? static_cast<int64_t>(vblocks) * BN : v,
+                                    static_cast<int>(hdim / BK), acc);
   __syncthreads();
   stats_epilogue<MI, 8, ROWS, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * (ROWS / 4),
                                                           wn * 128, li, g, tid,
@@ -436,14 +437,14 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
   const int32_t z_vec = z && reinterpret_cast<uintptr_t>(z) % 16 == 0 &&
                         (ld_z * (z_bf16 ? 2 : 4)) % 16 == 0;
   const LinearExtras ex{inv_t, round_bf16, pw, z, z_bf16, ld_z, z_vec};
-  if (n <= 64) {
-    hipLaunchKernelGGL(linear_stats_narrow<64>, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden,
-                       ld_h, weight, ld_w, n, h, v, 1, vblocks, targets.p, targets.is32, ignore,
-                       pm, ps, pt, ex);
-  } else if (n <= 128) {
-    hipLaunchKernelGGL(linear_stats_narrow<128>, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden,
-                       ld_h, weight, ld_w, n, h, v, 1, vblocks, targets.p, targets.is32, ignore,
-                       pm, ps, pt, ex);
+  // the narrow tiles read a prepared (K32-blocked) weight when there is one
+  const uint16_t* wn = wblk ? wblk : weight;
+  const int64_t ldn = wblk ? 0 : ld_w;
+  if (n <= 128) {
+    auto kern = n <= 64 ? (wblk ? linear_stats_narrow<64, true> : linear_stats_narrow<64, false>)
+                        : (wblk ? linear_stats_narrow<128, true> : linear_stats_narrow<128, false>);
+    hipLaunchKernelGGL(kern, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden, ld_h, wn, ldn, n, h,
+                       v, 1, vblocks, targets.p, targets.is32, ignore, pm, ps, pt, ex);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     launch_block_rows(hidden, ld_h, n, static_cast<int64_t>(mblocks) * 256, h, hb, s);

@@ -231,10 +231,11 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 // acc += A[a_row0 + 0..ROWS-1, 0..K) * B[b_row0 + 0..255, 0..K)^T, K =
-// ksteps * 32 (ksteps even, >= 2); rows at or past a_rows / b_rows are read
-// from the last valid row.  All 512 threads must call; on return every
-// direct load has landed and the stages may be reused after a barrier.
-template <int ROWS>
+// ksteps * 32 (ksteps even, >= 2); A row-major, B row-major or K32-blocked
+// (BBLK); rows at or past a_rows / b_rows are read from the last valid row
+// (block).  All 512 threads must call; on return every direct load has landed
+// and the stages may be reused after a barrier.
+template <int ROWS, bool BBLK = false>
 __device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
                                                 const uint16_t* __restrict__ A, int64_t lda,
                                                 int64_t a_row0, int64_t a_rows,
@@ -252,16 +253,17 @@ __device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
   const int lk = ((lane % 4) ^ swz(lrow)) * 8;
   const bool has_a = wave < ROWS / 16;  // uniform
   const uint16_t* a0 = A + min(a_row0 + (has_a ? wave : 0) * 16 + lrow, a_rows - 1) * lda + lk;
-  const uint16_t* b0 = B + min(b_row0 + wave * 16 + lrow, b_rows - 1) * ldb + lk;
-  const uint16_t* b1 = B + min(b_row0 + (wave + 8) * 16 + lrow, b_rows - 1) * ldb + lk;
+  const uint16_t* b0 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, ksteps, wave, lrow, lk);
+  const uint16_t* b1 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, ksteps, wave + 8, lrow, lk);
+  constexpr int SB = BBLK ? 512 : kK;
   const int aoff = (wm * (ROWS / 4) + li) * kK + ((g ^ swz(li)) * 8);
   const int boff = (wn * 128 + li) * kK + ((g ^ swz(li)) * 8);
   constexpr int kBlk = 16 * kK;
   auto issue_step = [&](int s, int step) {
-    const int64_t k0 = static_cast<int64_t>(step) * kK;
+    const int64_t k0 = static_cast<int64_t>(step) * kK, kb = static_cast<int64_t>(step) * SB;
     if (has_a) __builtin_amdgcn_global_load_lds(a0 + k0, sm.a[s] + wave * kBlk, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b0 + k0, sm.b[s] + wave * kBlk, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b1 + k0, sm.b[s] + (wave + 8) * kBlk, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b0 + kb, sm.b[s] + wave * kBlk, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b1 + kb, sm.b[s] + (wave + 8) * kBlk, 16, 0, 0);
   };
   // Iteration kt: MFMAs of step kt on fragments in registers, fragment reads
   // of step kt+1, direct loads of step kt+S (kt+2 .. kt+S-1 in flight).
