@@ -113,6 +113,11 @@ def test_fuzz_linear(c):
                                 temperature=c["temp"], return_entropy=c["ent"])
     for a, b in zip(out, alone):
         assert torch.equal(bits(a)[r:r + 1], bits(b)), what
+    # the prepared weight gives the same bits (every tile shape reads it)
+    prep = itl.linear_logp_fwd(hid, w, t, temperature=c["temp"], return_entropy=c["ent"],
+                               prepared_weight=itl.prepare_weight(w))
+    for a, b in zip(out, prep):
+        assert torch.equal(bits(a), bits(b)), what
 
 
 @settings(max_examples=20, deadline=None, derandomize=True, database=None,
@@ -120,7 +125,7 @@ def test_fuzz_linear(c):
 @given(linear_cases())
 def test_fuzz_linear_bwd(c):
     """dh and dW against the float64 oracle by the fused backward's bound, and
-    the saved-logits path with the same bits."""
+    the saved-logits and prepared-weight paths with the same bits."""
     from test_gpu_linear_bwd import _bounds
 
     n, h, v = c["n"], c["h"], c["v"]
@@ -136,6 +141,8 @@ def test_fuzz_linear_bwd(c):
     dh, dw = itl.linear_logp_bwd(hid, w, t, lse, g)
     dh2, dw2 = itl.linear_logp_bwd(hid, w, t, lse, g, saved_logits=z)
     assert torch.equal(dh, dh2) and torch.equal(dw, dw2), what
+    dh3, dw3 = itl.linear_logp_bwd(hid, w, t, lse, g, prepared_weight=itl.prepare_weight(w))
+    assert torch.equal(dh, dh3) and torch.equal(dw, dw3), what
     hn, wn, tn, gn = to_np(hid), to_np(w), t.cpu().numpy(), to_np(g)
     dh64, dw64 = oracle.linear_logp_bwd(hn, wn, tn, gn)
     _, lse64 = oracle.linear_logp_fwd(hn, wn, tn)

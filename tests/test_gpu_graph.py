@@ -74,3 +74,43 @@ def test_graph_replays_fused_lm_head():
         torch.cuda.synchronize()
         for a, b in zip(out, ref):
             assert torch.equal(bits(a), bits(b)), seed
+
+
+@pytest.mark.parametrize("prepared", [False, True])
+def test_graph_replays_fused_fwd_bwd_256_tile(prepared):
+    """N > 128 (the 256-row tile, which first re-lays the hidden rows): a
+    captured fused forward + backward, with or without a prepared weight,
+    replayed with new hidden rows and targets, gives the eager bits."""
+    n, h, v = 300, 128, 1000
+    hid = torch.empty(n, h, dtype=torch.bfloat16, device=dev())
+    t = torch.empty(n, dtype=torch.int64, device=dev())
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=40)[0].to(dev())
+    w = synth.normal_matrix(v, h, 0.05, torch.bfloat16, seed=41).to(dev())
+    pw = itl.prepare_weight(w) if prepared else None
+    hid.copy_(synth.normal_matrix(n, h, 1.0, torch.bfloat16, seed=42).to(dev()))
+    t.copy_(synth.uniform_targets(n, v, seed=43).to(dev()))
+
+    def step():
+        logp, lse = itl.linear_logp_fwd(hid, w, t, prepared_weight=pw)
+        dh, dw = itl.linear_logp_bwd(hid, w, t, lse, g, prepared_weight=pw)
+        return logp, lse, dh, dw
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = step()
+    for seed in (51, 52, 53):
+        hid.copy_(synth.normal_matrix(n, h, 1.0, torch.bfloat16, seed=seed).to(dev()))
+        t.copy_(synth.uniform_targets(n, v, seed=seed + 1,
+                                      ignore_rows=torch.tensor([seed % n])).to(dev()))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = step()
+        torch.cuda.synchronize()
+        for a, b in zip(out, ref):
+            assert torch.equal(bits(a), bits(b)), seed
