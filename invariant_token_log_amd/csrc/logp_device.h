@@ -33,16 +33,77 @@ __device__ __forceinline__ float log_nat(float a) {
   return __builtin_amdgcn_logf(a) * kLn2;
 }
 
-// XOR butterfly over the 64 lanes of a wave, offsets 1, 2, 4, ..., 32.  Every
-// lane ends with the same value: at each level both partners add the same
-// two operands (addition commutes exactly).
+// Lane moves for the reductions below.  DPP within rows of 16 lanes: quad
+// permutes, row rotations (rotating right by n hands lane i the value of lane
+// i - n mod 16) and mirrors (lane i <- lane 15 - i; half mirror: lane i <-
+// lane 7 - i within each 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor12 = 0x12C;  // lane i <- lane i + 4 (mod 16)
+constexpr int kDppRowRor8 = 0x128;   // lane i <- lane i + 8 (mod 16)
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15 - i
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7 - i (within 8)
+
+// XOR butterfly over the 64 lanes of a wave, offsets 1, 2, 4, ..., 32: at
+// level o every lane combines its value with that of lane i ^ o, and every
+// lane ends with the same value (both partners combine the same two operands;
+// addition and max commute exactly).  The partners come from lane moves
+// without LDS: quad permutes give lanes i ^ 1 and i ^ 2 exactly; after those
+// levels the four lanes of a quad hold one value, so the half mirror (lane
+// 7 - i, in the other quad of the 8) supplies the value of lane i ^ 4; then
+// the eight lanes of each half row agree and the row mirror (lane 15 - i, in
+// the other half) supplies lane i ^ 8.  Offsets 16 and 32 use gfx950's
+// permlane swaps of a value with itself: after v_permlane16_swap one operand
+// holds rows (0, 0, 2, 2) and the other rows (1, 1, 3, 3), so combining the
+// two gives every lane op(row r, row r ^ 1); v_permlane32_swap does the same
+// for the two halves of the wave.
+__device__ __forceinline__ float swap_combine16(float x, bool is_max) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return is_max ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float swap_combine32(float x, bool is_max) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return is_max ? fmaxf(a, b) : a + b;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_mov<kDppXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_mov<kDppRowMirror>(x));
+  x = swap_combine16(x, true);
+  return swap_combine32(x, true);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = x + dpp_mov<kDppXor1>(x);
+  x = x + dpp_mov<kDppXor2>(x);
+  x = x + dpp_mov<kDppRowHalfMirror>(x);
+  x = x + dpp_mov<kDppRowMirror>(x);
+  x = swap_combine16(x, false);
+  return swap_combine32(x, false);
+}
+
+// The same butterfly with every partner fetched through the LDS crossbar
+// (ds_bpermute): the same partners, so the same bits, but the moves use the
+// LDS unit instead of vector ALU issue.  Wide tiles, whose per-lane work
+// already keeps the ALU busy, reduce this way; narrow tiles, where the
+// butterfly's latency dominates, use the lane moves above.
+__device__ __forceinline__ float wave_max_lds(float x) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
   return x;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
+__device__ __forceinline__ float wave_sum_lds(float x) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) x = x + __shfl_xor(x, o, kWave);
   return x;
@@ -56,15 +117,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 // then row rotations (a rotation right by n hands lane i the value of lane
 // i - n mod 16), by 12 so that lane 0 reads lane 4, and by 8 so that it reads
 // lane 8.  Other lanes of the row end with other, unused associations.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-constexpr int kDppXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
-constexpr int kDppRowRor12 = 0x12C;  // lane i <- lane i + 4 (mod 16)
-constexpr int kDppRowRor8 = 0x128;   // lane i <- lane i + 8 (mod 16)
-
 __device__ __forceinline__ float row16_sum_first(float x) {
   x = x + dpp_mov<kDppXor1>(x);
   x = x + dpp_mov<kDppXor2>(x);
@@ -203,7 +255,9 @@ __device__ __forceinline__ void tile_stats(const T* row, int64_t col0, int64_t v
   for (int j = 0; j < C; ++j)
 #pragma unroll
     for (int e = 0; e < E; ++e) m = fmaxf(m, x[j][e]);
-  m = wave_max(m);
+  // lane moves for tiles of at most 16 elements per lane, LDS crossbar above
+  constexpr bool kLds = C * E > 16;
+  m = kLds ? wave_max_lds(m) : wave_max(m);
   float s = 0.0f, w = 0.0f;
 #pragma unroll
   for (int j = 0; j < C; ++j)
@@ -219,8 +273,8 @@ __device__ __forceinline__ void tile_stats(const T* row, int64_t col0, int64_t v
       }
     }
   m_out = m;
-  s_out = wave_sum(s);
-  if constexpr (ENT) *w_out = wave_sum(w);
+  s_out = kLds ? wave_sum_lds(s) : wave_sum(s);
+  if constexpr (ENT) *w_out = kLds ? wave_sum_lds(w) : wave_sum(w);
 }
 
 // ---------------------------------------------------------------------------
