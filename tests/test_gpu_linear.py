@@ -86,6 +86,10 @@ def test_full_size_sampled():
     ref = _oracle(h[rows], w, t[rows])
     assert_logp_parity(logp[rows], lse[rows], *ref, t[rows], what="linear full")
     assert torch.isfinite(logp).all()
+    # the prepared weight (the forward's blocked copy) gives the same bits
+    pw = itl.prepare_weight(w)
+    lp2, lse2 = itl.linear_logp_fwd(h, w, t, prepared_weight=pw)
+    assert torch.equal(bits(lp2), bits(logp)) and torch.equal(bits(lse2), bits(lse))
 
 
 def test_int32_targets_same_bits():

@@ -160,6 +160,10 @@ def test_full_size_sampled():
     h, w, t, g = _case(4096, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB, seed=1005, ignore_frac=0.05)
     _, lse = itl.linear_logp_fwd(h, w, t)
     dh, dw = itl.linear_logp_bwd(h, w, t, lse, g)
+    # the prepared weight gives the same bits at full size
+    dh2, dw2 = itl.linear_logp_bwd(h, w, t, lse, g, prepared_weight=itl.prepare_weight(w))
+    assert torch.equal(bits(dh2), bits(dh)) and torch.equal(bits(dw2), bits(dw))
+    del dh2, dw2
     torch.cuda.synchronize()
     hn, wn, tn, gn = _f64(h), _f64(w), t.cpu().numpy(), _f64(g)
     rows = np.array(list(range(0, 4096, 293)) + [4095])
