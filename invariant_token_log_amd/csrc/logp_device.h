@@ -285,60 +285,81 @@ __device__ __forceinline__ void tile_stats(const T* row, int64_t col0, int64_t v
 // fma(s_k, m_k - M, w_k) = sum over the tile of e^(x - M) (x - M) scaled back
 // by e^(M - m_k), and the full-vocabulary entropy is
 //   H = log(acc) - b / acc          (= LSE - sum_j p_j x_j).
-// One wave evaluates one row: the max and the T exponentials are spread over
-// the lanes (the max is exact in any order; each exponential is the same
-// function of the same two values), then the ascending fma chains run over
-// them in tile order, 64 tiles at a time, with every operand read back
-// exactly from the lane that computed it.  Partial k of the row is read at
+// One wave evaluates one row.  The row's partials are loaded up front, PRE
+// chunks of 64 tiles per lane at a time, so the loads of a row overlap instead
+// of waiting one chunk after another.  The max is exact in any order; each
+// exponential is the same function of the same two values, whichever lane
+// takes it.  The ascending fma chains then run over the tiles in order, 64 at a
+// time: each lane parks its (s_k, e_k[, y_k]) in a wave-private LDS stage and
+// every lane folds the 64 entries by broadcast reads, so each step of the
+// chain is one fma on exact copies of the operands.  Entries past the last
+// tile are zeros: fma(0, 0, x) = x for every x but -0, and neither acc nor b
+// is ever -0 (both start at +0 and an exact zero sum rounds to +0), so the
+// fold may run on to a multiple of 8.  Partial k of the row is read at
 // m[k * stride], s[k * stride] (w[k * stride]).  All 64 lanes must call; all
 // return the LSE (and H).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float lane_value(float x, int j) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
-}
+struct MergeStage {
+  float2 se[kWave];  // (s_k, e_k) of the 64 tiles being folded
+  float y[kWave];    // y_k (entropy)
+};
 
-template <bool ENT, typename P>
+template <bool ENT, int PRE, typename P>
 __device__ __forceinline__ float merge_lse_t(P m, P s, P w, int ntiles, int64_t stride,
-                                             float* ent) {
+                                             MergeStage& st, float* ent) {
   const int lane = threadIdx.x & (kWave - 1);
+  constexpr int kGroup = PRE * kWave;  // tiles held in registers at once
+  float mr[PRE], sr[PRE], wr[ENT ? PRE : 1];
+  auto load = [&](int g0, bool with_sw) {
+#pragma unroll
+    for (int c = 0; c < PRE; ++c) {
+      const int k = g0 + c * kWave + lane;
+      const bool in = k < ntiles;
+      mr[c] = in ? m[k * stride] : -INFINITY;
+      if (with_sw) {
+        sr[c] = in ? s[k * stride] : 0.0f;
+        if constexpr (ENT) wr[c] = in ? w[k * stride] : 0.0f;
+      }
+    }
+  };
+  const bool one_group = ntiles <= kGroup;
   float mx = -INFINITY;
-  for (int k = lane; k < ntiles; k += kWave) mx = fmaxf(mx, m[k * stride]);
+  for (int g0 = 0; g0 < ntiles; g0 += kGroup) {
+    load(g0, one_group);
+#pragma unroll
+    for (int c = 0; c < PRE; ++c) mx = fmaxf(mx, mr[c]);
+  }
   const float big_m = wave_max(mx);
   float acc = 0.0f, b = 0.0f;
-  for (int c = 0; c < ntiles; c += kWave) {
-    const int k = c + lane;
-    float mk = -INFINITY, sk = 0.0f, yk = 0.0f;
-    if (k < ntiles) {
-      mk = m[k * stride];
-      sk = s[k * stride];
-      if constexpr (ENT) yk = fmaf(sk, mk - big_m, w[k * stride]);
-    }
-    // A tile without columns (m_k = -inf) enters as s_k = e_k = y_k = 0, the
-    // same fold as skipping it without a branch per tile: fma(0, 0, x) = x
-    // for every x but -0, which it turns into +0.  acc is never negative; b
-    // only reaches the result through log(acc) - b / acc, where the sign of
-    // a zero b makes no difference (log(acc) is never -0).
-    const bool live = mk != -INFINITY;
-    const float ek = live ? exp_sub(mk, big_m) : 0.0f;
-    if (!live) {
-      sk = 0.0f;
-      yk = 0.0f;
-    }
-    const int cnt = ntiles - c < kWave ? ntiles - c : kWave;
-    for (int j = 0; j < cnt; ++j) {
-      const float e = lane_value(ek, j);
-      acc = fmaf(lane_value(sk, j), e, acc);
-      if constexpr (ENT) b = fmaf(lane_value(yk, j), e, b);
+  for (int g0 = 0; g0 < ntiles; g0 += kGroup) {
+    if (!one_group) load(g0, true);
+#pragma unroll
+    for (int c = 0; c < PRE; ++c) {
+      const int c0 = g0 + c * kWave;
+      if (c0 < ntiles) {
+        // A tile without columns (m_k = -inf) enters as s_k = e_k = y_k = 0,
+        // the same fold as skipping it (see above).
+        const bool live = mr[c] != -INFINITY;
+        const float ek = live ? exp_sub(mr[c], big_m) : 0.0f;
+        st.se[lane] = make_float2(live ? sr[c] : 0.0f, ek);
+        if constexpr (ENT) st.y[lane] = live ? fmaf(sr[c], mr[c] - big_m, wr[c]) : 0.0f;
+        __builtin_amdgcn_wave_barrier();
+        const int cnt = ntiles - c0 < kWave ? ntiles - c0 : kWave;
+        for (int j0 = 0; j0 < cnt; j0 += 8) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float2 p = st.se[j0 + j];
+            acc = fmaf(p.x, p.y, acc);
+            if constexpr (ENT) b = fmaf(st.y[j0 + j], p.y, b);
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   }
   const float la = log_nat(acc);
   if constexpr (ENT) *ent = la - b / acc;
   return big_m + la;
-}
-
-template <typename P>
-__device__ __forceinline__ float merge_lse(P m, P s, int ntiles, int64_t stride) {
-  return merge_lse_t<false>(m, s, s, ntiles, stride, nullptr);
 }
 
 // Final combine (step 6): logp = target_logit - LSE, or NaN for an active row

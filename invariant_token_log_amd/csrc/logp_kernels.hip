@@ -13,6 +13,7 @@ constexpr int kFwdBlock = 512;            // 8 waves per row in the forward kern
 constexpr int kFwdWaves = kFwdBlock / kWave;
 constexpr int64_t kMaxRowBlocks = 1 << 20;  // grid-stride beyond this
 constexpr int64_t kMaxGridY = 65535;        // backward grid rows (grid-stride beyond)
+constexpr int kMergeChunks = 16;             // merge: 64-tile chunks a lane loads at once
 
 // ---------------------------------------------------------------------------
 // Single-launch forward ("Batch-Invariant LogP", Tensor Parallel with one
@@ -30,6 +31,7 @@ __global__ __launch_bounds__(kFwdBlock) void logp_fwd_fused_kernel(
     int* __restrict__ status) {
   const Targets targets{tgt, tgt32};
   extern __shared__ float lds[];
+  __shared__ MergeStage stage;  // wave 0's merge
   float* lm = lds;
   float* ls = lds + ntiles;
   float* lw = lds + 2 * ntiles;  // ENT only
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(kFwdBlock) void logp_fwd_fused_kernel(
     __syncthreads();
     if (wave == 0) {
       float h = 0.0f;
-      const float L = merge_lse_t<ENT>(lm, ls, lw, ntiles, 1, &h);
+      const float L = merge_lse_t<ENT, 1>(lm, ls, lw, ntiles, 1, stage, &h);
       if (lane == 0) {
         const bool valid = t >= 0 && t < v;
         const float xt = valid ? Elt<T>::load(row, t) : 0.0f;
@@ -122,6 +124,7 @@ __global__ __launch_bounds__(kBlock) void logp_merge_kernel(
     int64_t ignore_index, float* __restrict__ logp, float* __restrict__ lse,
     float* __restrict__ ent, int* __restrict__ status) {
   const Targets targets{tgt, tgt32};
+  __shared__ MergeStage stage[kWavesPerBlock];
   const int lane = threadIdx.x % kWave;
   const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
   for (int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; r < n;
@@ -136,8 +139,9 @@ __global__ __launch_bounds__(kBlock) void logp_merge_kernel(
       continue;
     }
     float h = 0.0f;
-    const float L = merge_lse_t<ENT>(pm + r * row_stride, ps + r * row_stride,
-                                     pw + r * row_stride, ntiles, tile_stride, &h);
+    const float L = merge_lse_t<ENT, kMergeChunks>(pm + r * row_stride, ps + r * row_stride,
+                                                   pw + r * row_stride, ntiles, tile_stride,
+                                                   stage[threadIdx.x / kWave], &h);
     if (lane == 0) {
       const bool valid = t >= 0 && t < v;
       logp[r] = combine(valid ? pt[r] : 0.0f, L, valid);
