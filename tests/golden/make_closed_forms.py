@@ -66,6 +66,11 @@ CASES = [
      [77777, 0, 151935]),
     ("spike_v4096_small", 4096, {"kind": "spike", "col": 5, "height": 4.0},
      [5, 6]),
+    # Logits far outside exp's float64 range (|x| > 709): only a shifted
+    # log-sum-exp evaluates these rows.
+    ("uniform_v8_big", 8, {"kind": "constant", "value": 1000.0}, [0, 7]),
+    ("two_level_v8_big", 8, {"kind": "two_level", "a": 800.0, "b": -800.0, "k": 2},
+     [0, 5]),
 ]
 
 
