@@ -147,6 +147,25 @@ def test_shards_small_tiles(shards):
     assert_logp_parity(l2, s2, *_oracle(x, t), t, what="small shards")
 
 
+def test_many_tiles_merge_groups():
+    """More than 1024 tiles per row (fp32, 256-wide tiles, V = 300000: 1172
+    tiles): the merge holds at most 1024 tiles per lane group in registers
+    (64 in the single-launch forward), so every path folds several groups.
+    S = 1, 2 and 4 give the same bits (entropy included) and match the
+    oracle."""
+    v, n = 300000, 6
+    x = synth.normal_matrix(n, v, 3.0, torch.float32, seed=31).to(dev())
+    x[2, 299999] = 45.0  # a spike in the last, ragged tile
+    t = synth.uniform_targets(n, v, seed=32, ignore_rows=torch.tensor([4])).to(dev())
+    t[2] = 299999
+    l1, s1, e1 = itl.logp_fwd(x, t, -100, 256, 1, return_entropy=True)
+    for shards in (2, 4):
+        ls, ss, es = itl.logp_fwd(x, t, -100, 256, shards, return_entropy=True)
+        assert torch.equal(bits(ls), bits(l1)) and torch.equal(bits(ss), bits(s1)), shards
+        assert torch.equal(bits(es), bits(e1)), shards
+    assert_logp_parity(l1, s1, *_oracle(x, t), t, what="1172 tiles")
+
+
 def test_row_invariance(qwen_small):
     """A row's bits do not depend on the batch: alone, reversed, permuted,
     packed among random neighbours, repeated, on another stream."""
