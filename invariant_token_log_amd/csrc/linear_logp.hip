@@ -100,7 +100,7 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
       for (int h = 0; h < NQ; ++h) {
         float m = z(i, 4 * h, q);
 #pragma unroll
-        for (int j = 4 * h + 1; j < 4 * h + 4; ++j) m = fmaxf(m, z(i, j, q));
+        for (int j = 4 * h + 1; j < 4 * h + 4; ++j) m = max_exact(m, z(i, j, q));
         part[i][q][h] = row16_max_first(m);
       }
   if (li == 0) {
@@ -114,7 +114,7 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
   block_sync_lds();
   for (int lr = tid; lr < BM; lr += NT) {
     const float4 r4 = *reinterpret_cast<const float4*>(rd.red[lr]);
-    rd.tmax[lr] = fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w));
+    rd.tmax[lr] = max_exact(max_exact(r4.x, r4.y), max_exact(r4.z, r4.w));
   }
   block_sync_lds();
 

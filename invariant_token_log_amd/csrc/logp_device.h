@@ -125,11 +125,23 @@ __device__ __forceinline__ float row16_sum_first(float x) {
   return x;
 }
 
+// The exact maximum of the LM-head statistics: IEEE maximum, which gfx950
+// evaluates as v_maximum3_f32 on its operands as they are (fmaxf makes the
+// compiler quiet each operand first, one more instruction per value).  On
+// non-NaN values it equals fmaxf except that -0 orders below +0; the LM-head
+// logits are never -0 (every accumulator starts at +0), and a tile maximum of
+// either zero gives the same partial sums and merge anyway.  A NaN logit
+// makes the tile maximum NaN, and with it the row's LSE, as its sum already
+// would.
+__device__ __forceinline__ float max_exact(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 __device__ __forceinline__ float row16_max_first(float x) {
-  x = fmaxf(x, dpp_mov<kDppXor1>(x));
-  x = fmaxf(x, dpp_mov<kDppXor2>(x));
-  x = fmaxf(x, dpp_mov<kDppRowRor12>(x));
-  x = fmaxf(x, dpp_mov<kDppRowRor8>(x));
+  x = max_exact(x, dpp_mov<kDppXor1>(x));
+  x = max_exact(x, dpp_mov<kDppXor2>(x));
+  x = max_exact(x, dpp_mov<kDppRowRor12>(x));
+  x = max_exact(x, dpp_mov<kDppRowRor8>(x));
   return x;
 }
 
