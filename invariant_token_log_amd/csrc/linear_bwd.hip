@@ -111,16 +111,20 @@ __global__ __launch_bounds__(256) void block_rows_bf16(const uint16_t* __restric
 // x = z (* 1/T); p = exp(x - lse) with the forward's primitive; d = g (1 - p)
 // on the target column, (-g) p elsewhere, plus -gH p (x - lse + H) with the
 // entropy term (one fma, the -inf clamp of ent_term); d (* 1/T) for dz.
+// PLAIN: the caller knows that no option is on (no rounding, T = 1, no
+// entropy term), so the options cost nothing; the operations left are the
+// same, so the bits are too.
+template <bool PLAIN = false>
 __device__ __forceinline__ float dz_value(float zacc, float L, float G, float H, float NGH,
                                           bool is_target, float inv_t, bool scaled,
                                           bool with_ent, int32_t round_bf16) {
-  const float z = round_bf16 ? static_cast<float>(static_cast<__bf16>(zacc)) : zacc;
-  const float x = scaled ? z * inv_t : z;
+  const float z = !PLAIN && round_bf16 ? static_cast<float>(static_cast<__bf16>(zacc)) : zacc;
+  const float x = !PLAIN && scaled ? z * inv_t : z;
   const float dl = x - L;  // exp_sub(x, L) in two steps
   const float p = __builtin_amdgcn_exp2f(dl * kLog2e);
   float d = is_target ? G * (1.0f - p) : (-G) * p;
-  if (with_ent) d = fmaf(NGH, p * fmaxf(dl + H, -FLT_MAX), d);
-  if (scaled) d = d * inv_t;
+  if (!PLAIN && with_ent) d = fmaf(NGH, p * fmaxf(dl + H, -FLT_MAX), d);
+  if (!PLAIN && scaled) d = d * inv_t;
   return d;
 }
 
@@ -139,8 +143,10 @@ struct SmemDz {
 };
 
 // hidden K32-blocked (mblocks * 256 rows); weight row-major, or K32-blocked
-// with vblocks * 256 rows when WBLK (a prepared weight).
-template <bool WBLK>
+// with vblocks * 256 rows when WBLK (a prepared weight).  PLAIN: launched
+// only when no option is on (no rounding, T = 1, no entropy term), so the
+// epilogue skips their operations instead of selecting around them.
+template <bool WBLK, bool PLAIN>
 __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
@@ -221,8 +227,9 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float d = code[q] != -2 && v0 + lc < v
-                            ? dz_value(acc[i][j][q], L[q], G[q], H[q], NGH[q], lc == code[q],
-                                       inv_t, scaled, with_ent, round_bf16)
+                            ? dz_value<PLAIN>(acc[i][j][q], L[q], G[q], H[q], NGH[q],
+                                              lc == code[q], inv_t, scaled, with_ent,
+                                              round_bf16)
                             : 0.0f;
         b[q] = bf16_bits(d);
       }
@@ -510,15 +517,19 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
   if (!zsaved) {
     launch_block_rows(hidden, ld_h, n, l.np, h, hb, s);
-    if (prepared)
-      hipLaunchKernelGGL(linear_dz_kernel<true>, dim3(mblocks * vblocks), dim3(gemm::kThreads), 0,
-                         s, hb, ld_h, prepared_blocked_w(prepared), int64_t{0}, n, h, v, mblocks,
-                         vblocks, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
-                         ent, gent, dz, dzt);
-    else
-      hipLaunchKernelGGL(linear_dz_kernel<false>, dim3(mblocks * vblocks), dim3(gemm::kThreads),
-                         0, s, hb, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                         targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, dzt);
+    const bool plain = inv_t == 1.0f && !ent && !round_bf16;
+    const uint16_t* wop = prepared ? prepared_blocked_w(prepared) : weight;
+    const int64_t ldw = prepared ? int64_t{0} : ld_w;
+#define ITL_DZ(WB, PL)                                                                           \
+  hipLaunchKernelGGL((linear_dz_kernel<WB, PL>), dim3(mblocks * vblocks), dim3(gemm::kThreads), \
+                     0, s, hb, ld_h, wop, ldw, n, h, v, mblocks, vblocks, targets.p,            \
+                     targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, dzt)
+    if (prepared) {
+      if (plain) ITL_DZ(true, true); else ITL_DZ(true, false);
+    } else {
+      if (plain) ITL_DZ(false, true); else ITL_DZ(false, false);
+    }
+#undef ITL_DZ
   } else {
     const int64_t rb = l.np / kST;
     const dim3 grid(static_cast<unsigned>(l.vp / kST), static_cast<unsigned>(rb < 65535 ? rb : 65535));
