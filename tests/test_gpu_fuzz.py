@@ -3,7 +3,12 @@ repeat): random small shapes, dtypes, tile widths, shard counts, row
 strides, target index types, ignored and out-of-range-free targets, logit
 scales, entropy and temperature, each checked against the float64 oracle
 with the bounds of the targeted tests, plus bitwise invariance of a row
-computed alone and of sharded against unsharded forwards."""
+computed alone and of sharded against unsharded forwards.
+
+ITL_FUZZ_EXAMPLES=N (N > 0) replaces the fixed derivation by N fresh random
+examples per test, a deeper search for a one-off run."""
+
+import os
 
 import numpy as np
 import pytest
@@ -19,8 +24,17 @@ from test_gpu_entropy import _ent_ok, _grad_ent_ok
 
 pytestmark = pytest.mark.gpu
 
-SETTINGS = settings(max_examples=40, deadline=None, derandomize=True, database=None,
+_DEEP = int(os.environ.get("ITL_FUZZ_EXAMPLES", "0"))
+
+
+def _settings(n):
+    """n derandomized examples, or ITL_FUZZ_EXAMPLES fresh random ones."""
+    return settings(max_examples=_DEEP if _DEEP > 0 else n, deadline=None,
+                    derandomize=_DEEP <= 0, database=None,
                     suppress_health_check=list(HealthCheck))
+
+
+SETTINGS = _settings(40)
 
 
 @st.composite
@@ -120,8 +134,7 @@ def test_fuzz_linear(c):
         assert torch.equal(bits(a), bits(b)), what
 
 
-@settings(max_examples=20, deadline=None, derandomize=True, database=None,
-          suppress_health_check=list(HealthCheck))
+@_settings(20)
 @given(linear_cases())
 def test_fuzz_linear_bwd(c):
     """dh and dW against the float64 oracle by the fused backward's bound, and
