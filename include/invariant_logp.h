@@ -78,11 +78,11 @@ enum logp_index_dtype {
 };
 
 /* Rounding point of the fused LM head's logits ("[RFC][ROCm] End-to-end
- * optimization of bitwise VIME R/R beyond native P/P": the FP32/BF16 rounding
- * points belong to the versioned arithmetic contract, and a fused epilogue
- * performs a required BF16 round explicitly before the next step sees the
- * value).  LOGP_ROUND_BF16 selects the variant contract whose statistics see
- * the logits an unfused bf16 LM head would store. */
+ * optimization of bitwise VIME R/R beyond native P/P", Contract-versioned
+ * arithmetic change and Workstream 1).  Where a value is rounded to bf16 is
+ * part of a contract version, so fusing two steps must keep a bf16 rounding
+ * that the unfused pair had.  LOGP_ROUND_BF16 selects the variant contract
+ * whose statistics see the bf16 logits an unfused bf16 LM head stores. */
 enum logp_rounding {
   LOGP_ROUND_NONE = 0,  /* statistics on the fp32 accumulators */
   LOGP_ROUND_BF16 = 1   /* statistics on RNE_bf16(accumulator), widened exactly */
@@ -225,7 +225,8 @@ size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *   targets, target_dtype, ignore_index, logp_out, lse_out (may be NULL),
  *   entropy_out (may be NULL): as logp_fwd, with no validation (invalid
  *   active targets give logp = NaN), taken over the scaled logits.
- *   temperature finite and > 0 (LOGP_ERR_VALUE otherwise): the logits enter
+ *   temperature finite and > 0 with a finite fp32 reciprocal, i.e. at least
+ *               about 2.9e-39 (LOGP_ERR_VALUE otherwise): the logits enter
  *               every statistic as z * fl32(1 / temperature) (the proposed
  *               operator's temperature, applied at this one point); 1 leaves
  *               them unchanged.

@@ -3,6 +3,8 @@
 #include "invariant_logp.h"
 #include "launch.h"
 
+#include <cmath>
+
 namespace {
 
 constexpr int kMaxTiles = 4096;
@@ -32,10 +34,15 @@ itl::Targets targets_of(const void* p, int32_t target_dtype) {
   return itl::Targets{p, target_dtype == LOGP_I32 ? 1 : 0};
 }
 
-// Temperature of the fused LM head: finite and > 0.  The logits are
-// multiplied by its reciprocal rounded once to fp32 (1 stays exactly 1).
-bool valid_temperature(float t) { return t > 0.0f && t <= 3.4e38f; }
+// Temperature of the fused LM head.  The logits are multiplied by its
+// reciprocal rounded once to fp32 (1 stays exactly 1), so a temperature is
+// usable when it is finite, > 0 and that reciprocal is finite too (below
+// about 2.9e-39 it overflows to +inf, which would turn every logit into inf
+// or NaN).
 float inv_temperature(float t) { return static_cast<float>(1.0 / static_cast<double>(t)); }
+bool valid_temperature(float t) {
+  return std::isfinite(t) && t > 0.0f && std::isfinite(inv_temperature(t));
+}
 bool valid_rounding(int32_t r) { return r == LOGP_ROUND_NONE || r == LOGP_ROUND_BF16; }
 
 bool aligned16(const void* p, int64_t ld, int32_t dtype) {

@@ -221,3 +221,23 @@ def test_prepare_weight_argument_errors(L):
     assert L.linear_logp_prepared_bytes(1, 64) == 2 * 64 * 256 * 2
     assert L.linear_logp_prepared_bytes(0, 4096) == 0
     assert L.linear_logp_prepared_bytes(151936, 100) == 0
+
+
+def test_temperature_bounds(L):
+    """A temperature is usable when it is finite, > 0 and its fp32 reciprocal
+    is finite: below about 2.9e-39 the reciprocal overflows and is refused;
+    FLT_MAX passes the check (the call then stops at a NULL pointer)."""
+    def lin(temp, h_ptr=FAKE):
+        return L.linear_logp_fwd(h_ptr, 4096, FAKE, 4096, 8, 4096, 151936, FAKE, 0, -100, 256,
+                                 temp, 0, FAKE, FAKE, None, None, 1, 0, None, 0, FAKE, 1 << 40,
+                                 None)
+    flt_max = 3.4028234663852886e38
+    for bad in (1e-39, 1.0e-45, 2.0e-39):
+        assert lin(bad) == _lib.LOGP_ERR_VALUE, bad
+    for ok in (3.0e-38, 1.0, flt_max):
+        assert lin(ok, h_ptr=None) == _lib.LOGP_ERR_NULL, ok
+    lb = L.linear_logp_bwd(FAKE, 4096, FAKE, 4096, 8, 4096, 151936, FAKE, 0, -100, 256, 1e-39,
+                           0, None, 0, 0, None, 0, FAKE, FAKE, None, None, 0, FAKE, 4096, FAKE,
+                           4096, FAKE, 1 << 40, None)
+    assert lb == _lib.LOGP_ERR_VALUE
+
