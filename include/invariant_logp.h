@@ -60,7 +60,11 @@ enum logp_status {
   LOGP_ERR_WORKSPACE = 7, /* workspace NULL or smaller than required */
   LOGP_ERR_TARGET = 8,    /* validate = 1 found an active target outside [0, v) */
   LOGP_ERR_HIP = 9,       /* a HIP launch or copy failed */
-  LOGP_ERR_VALUE = 10     /* a scalar argument is out of range (temperature) */
+  LOGP_ERR_VALUE = 10,    /* a scalar argument is out of range (temperature,
+                             rounding), or the stream is not on the current
+                             device (linear_logp_fwd_noalloc) */
+  LOGP_ERR_SCRATCH = 11   /* linear_logp_fwd_noalloc: the call needs more than
+                             LOGP_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 /* Logits element types ("Batch-Invariant LogP", Tensor Contract: fp32 / fp16
@@ -255,6 +259,42 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight,
                         void* logits_out, int32_t logits_dtype, int64_t ld_logits,
                         const void* prepared, size_t prepared_bytes,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Size of the static scratch array behind linear_logp_fwd_noalloc: 64 MiB of
+ * device memory on every GPU the library runs on, held until the process
+ * ends.
+ */
+#define LOGP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * linear_logp_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus workspace and
+ * workspace_bytes), same kernels, same bits as linear_logp_fwd.
+ *
+ * Scratch: the library's static device array of LOGP_NOALLOC_SCRATCH_BYTES
+ * bytes stands in for the workspace.  The call needs
+ * linear_logp_fwd_workspace_bytes(n, h, v, tile_width) <=
+ * LOGP_NOALLOC_SCRATCH_BYTES (at h = 4096, v = 151936 that is n <= 4352;
+ * n <= 128 needs only the partial tables, 7 KiB per row at that v), else it
+ * returns LOGP_ERR_SCRATCH with nothing enqueued.  It calls no allocator.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (no value in it has to start at zero: each one read is first
+ * written by the same call), so calls that overlap on one GPU (two streams,
+ * or two host threads) race and must be serialised by the caller.
+ * The first call on a device looks up the array's device address with that
+ * device current; hip_stream must belong to the current device
+ * (LOGP_ERR_VALUE otherwise).  Make that first call outside graph capture.
+ */
+int32_t linear_logp_fwd_noalloc(const void* hidden, int64_t ld_h, const void* weight,
+                                int64_t ld_w, int64_t n, int64_t h, int64_t v,
+                                const void* targets, int32_t target_dtype,
+                                int64_t ignore_index, int32_t tile_width, float temperature,
+                                int32_t logits_rounding, float* logp_out, float* lse_out,
+                                float* entropy_out,
+                                void* logits_out, int32_t logits_dtype, int64_t ld_logits,
+                                const void* prepared, size_t prepared_bytes, void* hip_stream);
 
 /*
  * Workspace of linear_logp_bwd in bytes: W^T [h, Vp], h^T [h, Np], dz [Np, Vp],

@@ -5,13 +5,14 @@ in include/invariant_logp.h); this package only marshals PyTorch tensors into
 it.  There is no CPU or PyTorch fallback: a missing library raises.
 """
 
-from ._lib import LogpError, contract_id, lib, status_str  # noqa: F401
+from ._lib import NOALLOC_SCRATCH_BYTES, LogpError, contract_id, lib, status_str  # noqa: F401
 from .ops import (  # noqa: F401
     LINEAR_TILE,
     batch_invariant_logp,
     linear_logp,
     linear_logp_bwd,
     linear_logp_fwd,
+    linear_logp_fwd_noalloc,
     logp_bwd,
     logp_fwd,
     prepare_weight,

@@ -20,6 +20,8 @@ LOGP_ERR_WORKSPACE = 7
 LOGP_ERR_TARGET = 8
 LOGP_ERR_HIP = 9
 LOGP_ERR_VALUE = 10
+LOGP_ERR_SCRATCH = 11
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LOGP_NOALLOC_SCRATCH_BYTES
 
 LOGP_F32 = 0
 LOGP_BF16 = 1
@@ -43,6 +45,9 @@ _SIGNATURES = {
     "linear_logp_fwd": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
                                _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _sz,
                                _vp, _sz, _vp]),
+    "linear_logp_fwd_noalloc": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
+                                       _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _vp,
+                                       _sz, _vp]),
     "linear_logp_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "linear_logp_bwd": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
                                _i32, _f32, _i32, _vp, _i32, _i64, _vp, _sz, _vp, _vp, _vp, _vp,

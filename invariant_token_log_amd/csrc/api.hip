@@ -4,6 +4,7 @@
 #include "launch.h"
 
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -89,6 +90,101 @@ size_t linear_fwd_total(int64_t n, int64_t h, int64_t ntiles, size_t* hb_offset)
 
 int32_t hip_status() {
   return hipGetLastError() == hipSuccess ? LOGP_OK : LOGP_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of linear_logp_fwd_noalloc: one array per GPU (each device
+// that loads the library holds its own copy until the process ends).  In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device (hipGetSymbolAddress with that
+// device current) and only that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) unsigned char scratch[LOGP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).  The stream, when given, must belong to the
+// current device.
+int32_t static_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LOGP_ERR_HIP;
+  if (s) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return LOGP_ERR_HIP;
+    if (sdev != dev) return LOGP_ERR_VALUE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LOGP_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LOGP_OK;
+}
+
+// linear_logp_fwd with the caller's workspace, or (use_static) with the
+// current device's static scratch array in its place.
+int32_t linear_fwd_run(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                       int64_t n, int64_t h, int64_t v, const void* targets,
+                       int32_t target_dtype, int64_t ignore_index, int32_t tile_width,
+                       float temperature, int32_t logits_rounding, float* logp_out,
+                       float* lse_out, float* entropy_out, void* logits_out,
+                       int32_t logits_dtype, int64_t ld_logits, const void* prepared,
+                       size_t prepared_bytes, void* workspace, size_t workspace_bytes,
+                       bool use_static, void* hip_stream) {
+
+  if (n < 0 || v < 1 || h < 1 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
+  if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
+  if (logits_out && logits_dtype != LOGP_F32 && logits_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
+  if (logits_out && ld_logits < v) return LOGP_ERR_SHAPE;
+  if (!valid_temperature(temperature) || !valid_rounding(logits_rounding)) return LOGP_ERR_VALUE;
+  const itl::Targets tg = targets_of(targets, target_dtype);
+  if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
+  const int64_t ntiles = (v + tile_width - 1) / tile_width;
+  if (ntiles > (int64_t{1} << 24) || (n + 127) / 128 * ntiles > (int64_t{1} << 30))
+    return LOGP_ERR_SHAPE;
+  const FwdLayout lay = fwd_layout(n, ntiles, true, 0);
+  size_t hb_off = 0;
+  const size_t need = linear_fwd_total(n, h, ntiles, &hb_off);
+  if (n == 0) return LOGP_OK;
+  if (!hidden || !weight || !targets || !logp_out) return LOGP_ERR_NULL;
+  if (!aligned16(hidden, ld_h, LOGP_BF16) || !aligned16(weight, ld_w, LOGP_BF16))
+    return LOGP_ERR_ALIGN;
+  if (prepared) {
+    if (prepared_bytes < linear_logp_prepared_bytes(v, h)) return LOGP_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(prepared) % 16) return LOGP_ERR_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (use_static) {
+    if (need > LOGP_NOALLOC_SCRATCH_BYTES) return LOGP_ERR_SCRATCH;
+    const int32_t st = static_scratch(s, &workspace);
+    if (st != LOGP_OK) return st;
+  } else if (!workspace || workspace_bytes < need ||
+             reinterpret_cast<uintptr_t>(workspace) % kAlign) {
+    return LOGP_ERR_WORKSPACE;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* pm = reinterpret_cast<float*>(ws + lay.pm);
+  float* ps = reinterpret_cast<float*>(ws + lay.ps);
+  float* pw = entropy_out ? reinterpret_cast<float*>(ws + lay.pw) : nullptr;
+  float* pt = reinterpret_cast<float*>(ws + lay.pt);
+  (void)hipGetLastError();
+  itl::launch_linear_partials(static_cast<const uint16_t*>(hidden), ld_h,
+                              static_cast<const uint16_t*>(weight), ld_w, n, h, v, tg,
+                              ignore_index, pm, ps, pt, inv_temperature(temperature),
+                              logits_rounding == LOGP_ROUND_BF16 ? 1 : 0, pw, logits_out,
+                              logits_dtype == LOGP_BF16 ? 1 : 0, ld_logits,
+                              prepared ? itl::prepared_blocked_w(
+                                             static_cast<const uint16_t*>(prepared))
+                                       : nullptr,
+                              reinterpret_cast<uint16_t*>(ws + hb_off), s);
+  itl::launch_fwd_merge(pm, ps, pw, pt, n, static_cast<int>(ntiles), ntiles, 1, v, tg,
+                        ignore_index, logp_out, lse_out, entropy_out, nullptr, s);
+  return hip_status();
 }
 
 }  // namespace
@@ -196,49 +292,23 @@ int32_t linear_logp_fwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int32_t logits_dtype, int64_t ld_logits, const void* prepared,
                         size_t prepared_bytes, void* workspace, size_t workspace_bytes,
                         void* hip_stream) {
-  if (n < 0 || v < 1 || h < 1 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
-  if (!valid_index(target_dtype)) return LOGP_ERR_DTYPE;
-  if (logits_out && logits_dtype != LOGP_F32 && logits_dtype != LOGP_BF16) return LOGP_ERR_DTYPE;
-  if (logits_out && ld_logits < v) return LOGP_ERR_SHAPE;
-  if (!valid_temperature(temperature) || !valid_rounding(logits_rounding)) return LOGP_ERR_VALUE;
-  const itl::Targets tg = targets_of(targets, target_dtype);
-  if (tile_width != itl::kLinearTile) return LOGP_ERR_TILE;
-  const int64_t ntiles = (v + tile_width - 1) / tile_width;
-  if (ntiles > (int64_t{1} << 24) || (n + 127) / 128 * ntiles > (int64_t{1} << 30))
-    return LOGP_ERR_SHAPE;
-  const FwdLayout lay = fwd_layout(n, ntiles, true, 0);
-  size_t hb_off = 0;
-  const size_t need = linear_fwd_total(n, h, ntiles, &hb_off);
-  if (n == 0) return LOGP_OK;
-  if (!hidden || !weight || !targets || !logp_out) return LOGP_ERR_NULL;
-  if (!aligned16(hidden, ld_h, LOGP_BF16) || !aligned16(weight, ld_w, LOGP_BF16))
-    return LOGP_ERR_ALIGN;
-  if (prepared) {
-    if (prepared_bytes < linear_logp_prepared_bytes(v, h)) return LOGP_ERR_SHAPE;
-    if (reinterpret_cast<uintptr_t>(prepared) % 16) return LOGP_ERR_ALIGN;
-  }
-  if (!workspace || workspace_bytes < need ||
-      reinterpret_cast<uintptr_t>(workspace) % kAlign)
-    return LOGP_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  char* ws = static_cast<char*>(workspace);
-  float* pm = reinterpret_cast<float*>(ws + lay.pm);
-  float* ps = reinterpret_cast<float*>(ws + lay.ps);
-  float* pw = entropy_out ? reinterpret_cast<float*>(ws + lay.pw) : nullptr;
-  float* pt = reinterpret_cast<float*>(ws + lay.pt);
-  (void)hipGetLastError();
-  itl::launch_linear_partials(static_cast<const uint16_t*>(hidden), ld_h,
-                              static_cast<const uint16_t*>(weight), ld_w, n, h, v, tg,
-                              ignore_index, pm, ps, pt, inv_temperature(temperature),
-                              logits_rounding == LOGP_ROUND_BF16 ? 1 : 0, pw, logits_out,
-                              logits_dtype == LOGP_BF16 ? 1 : 0, ld_logits,
-                              prepared ? itl::prepared_blocked_w(
-                                             static_cast<const uint16_t*>(prepared))
-                                       : nullptr,
-                              reinterpret_cast<uint16_t*>(ws + hb_off), s);
-  itl::launch_fwd_merge(pm, ps, pw, pt, n, static_cast<int>(ntiles), ntiles, 1, v, tg,
-                        ignore_index, logp_out, lse_out, entropy_out, nullptr, s);
-  return hip_status();
+  return linear_fwd_run(hidden, ld_h, weight, ld_w, n, h, v, targets, target_dtype,
+                        ignore_index, tile_width, temperature, logits_rounding, logp_out, lse_out,
+                        entropy_out, logits_out, logits_dtype, ld_logits, prepared,
+                        prepared_bytes, workspace, workspace_bytes, false, hip_stream);
+}
+
+int32_t linear_logp_fwd_noalloc(const void* hidden, int64_t ld_h, const void* weight,
+                                int64_t ld_w, int64_t n, int64_t h, int64_t v,
+                                const void* targets, int32_t target_dtype, int64_t ignore_index,
+                                int32_t tile_width, float temperature, int32_t logits_rounding,
+                                float* logp_out, float* lse_out, float* entropy_out,
+                                void* logits_out, int32_t logits_dtype, int64_t ld_logits,
+                                const void* prepared, size_t prepared_bytes, void* hip_stream) {
+  return linear_fwd_run(hidden, ld_h, weight, ld_w, n, h, v, targets, target_dtype,
+                        ignore_index, tile_width, temperature, logits_rounding, logp_out, lse_out,
+                        entropy_out, logits_out, logits_dtype, ld_logits, prepared,
+                        prepared_bytes, nullptr, 0, true, hip_stream);
 }
 
 size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width) {
@@ -332,7 +402,10 @@ const char* logp_status_str(int32_t status) {
     case LOGP_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LOGP_ERR_TARGET: return "an active target lies outside [0, v)";
     case LOGP_ERR_HIP: return "HIP launch or copy failed";
-    case LOGP_ERR_VALUE: return "invalid scalar argument (temperature or logits rounding)";
+    case LOGP_ERR_VALUE:
+      return "invalid scalar argument (temperature, logits rounding, or a stream of another device)";
+    case LOGP_ERR_SCRATCH:
+      return "the call needs more scratch than the no-allocation entry point's static buffer holds";
     default: return "unknown status";
   }
 }

@@ -161,6 +161,29 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
     round_logits the logits are first rounded to bf16 (RNE), as an unfused
     bf16 LM head would store them.  prepared_weight: prepare_weight(weight),
     read instead of the weight (same bits)."""
+    return _linear_fwd(hidden, weight, targets, ignore_index, tile_width, logp_out, lse_out,
+                       workspace, temperature, return_entropy, entropy_out, return_logits,
+                       logits_dtype, logits_out, round_logits, prepared_weight, noalloc=False)
+
+
+def linear_logp_fwd_noalloc(hidden, weight, targets, ignore_index=-100,
+                            tile_width=LINEAR_TILE, logp_out=None, lse_out=None,
+                            temperature=1.0, return_entropy=False, entropy_out=None,
+                            return_logits=False, logits_dtype=torch.bfloat16, logits_out=None,
+                            round_logits=False, prepared_weight=None):
+    """linear_logp_fwd through the entry point that takes no workspace: the
+    library's static per-GPU scratch array stands in for it (see
+    NOALLOC_SCRATCH_BYTES for its size).  Pass every output buffer to keep
+    the call free of allocations (e.g. under graph capture); calls that
+    overlap on one GPU race on the shared array."""
+    return _linear_fwd(hidden, weight, targets, ignore_index, tile_width, logp_out, lse_out,
+                       None, temperature, return_entropy, entropy_out, return_logits,
+                       logits_dtype, logits_out, round_logits, prepared_weight, noalloc=True)
+
+
+def _linear_fwd(hidden, weight, targets, ignore_index, tile_width, logp_out, lse_out,
+                workspace, temperature, return_entropy, entropy_out, return_logits,
+                logits_dtype, logits_out, round_logits, prepared_weight, noalloc):
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
     t1 = _targets(targets, n)
     dev = hidden.device
@@ -181,18 +204,21 @@ def linear_logp_fwd(hidden, weight, targets, ignore_index=-100, tile_width=LINEA
         raise ValueError("logits_out must be [N, V] of logits_dtype with contiguous rows")
     L = _lib.lib()
     pw = _prepared(prepared_weight, L, v, h, dev)
-    need = L.linear_logp_fwd_workspace_bytes(n, h, v, tile_width)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = (hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v, t1.data_ptr(),
+            _INDEX[t1.dtype], int(ignore_index), int(tile_width), float(temperature),
+            _rounding(round_logits), logp_out.data_ptr(), lse_out.data_ptr(), _ptr(ent), _ptr(z),
+            _DTYPES[logits_dtype], (z.stride(0) if n > 1 else v) if z is not None else 0,
+            _ptr(pw), _nbytes(pw))
     with torch.cuda.device(dev):
-        st = L.linear_logp_fwd(hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v,
-                               t1.data_ptr(), _INDEX[t1.dtype], int(ignore_index), int(tile_width),
-                               float(temperature), _rounding(round_logits), logp_out.data_ptr(),
-                               lse_out.data_ptr(), _ptr(ent), _ptr(z), _DTYPES[logits_dtype],
-                               (z.stride(0) if n > 1 else v) if z is not None else 0,
-                               _ptr(pw), _nbytes(pw), workspace.data_ptr(), workspace.numel(),
-                               _stream(dev))
-    check("linear_logp_fwd", st)
+        if noalloc:
+            st = L.linear_logp_fwd_noalloc(*args, _stream(dev))
+        else:
+            if workspace is None:
+                need = L.linear_logp_fwd_workspace_bytes(n, h, v, tile_width)
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            st = L.linear_logp_fwd(*args, workspace.data_ptr(), _nbytes(workspace),
+                                   _stream(dev))
+    check("linear_logp_fwd_noalloc" if noalloc else "linear_logp_fwd", st)
     out = (logp_out, lse_out)
     if return_entropy:
         out += (ent,)

@@ -241,3 +241,26 @@ def test_temperature_bounds(L):
                            4096, FAKE, 1 << 40, None)
     assert lb == _lib.LOGP_ERR_VALUE
 
+
+def test_noalloc_argument_errors(L):
+    """linear_logp_fwd_noalloc runs linear_logp_fwd's checks, then refuses a
+    problem whose workspace exceeds the static scratch array, all before any
+    HIP call."""
+    def na(**kw):
+        a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, n=8, h=4096, v=151936, temp=1.0, logp=FAKE)
+        a.update(kw)
+        return L.linear_logp_fwd_noalloc(a["h_ptr"], a["ld_h"], a["w_ptr"], 4096, a["n"],
+                                         a["h"], a["v"], FAKE, 0, -100, 256, a["temp"], 0,
+                                         a["logp"], FAKE, None, None, 1, 0, None, 0, None)
+    assert na(temp=0.0) == _lib.LOGP_ERR_VALUE
+    assert na(h_ptr=None) == _lib.LOGP_ERR_NULL
+    assert na(h_ptr=FAKE + 2) == _lib.LOGP_ERR_ALIGN
+    assert na(ld_h=10) == _lib.LOGP_ERR_SHAPE
+    assert na(n=0, h_ptr=None, w_ptr=None, logp=None) == _lib.LOGP_OK
+    # N = 8192 at the Qwen3-8B head needs ~125 MB > 64 MiB of scratch
+    assert L.linear_logp_fwd_workspace_bytes(8192, 4096, 151936, 256) > _lib.NOALLOC_SCRATCH_BYTES
+    assert na(n=8192) == _lib.LOGP_ERR_SCRATCH
+    # the largest N that fits at that head: 4352 (17 blocks of 256 rows)
+    assert L.linear_logp_fwd_workspace_bytes(4352, 4096, 151936, 256) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert L.linear_logp_fwd_workspace_bytes(4353, 4096, 151936, 256) > _lib.NOALLOC_SCRATCH_BYTES
+    assert "scratch" in itl.status_str(_lib.LOGP_ERR_SCRATCH)
