@@ -118,19 +118,59 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
   }
   block_sync_lds();
 
-  // Pass 2: quarter sums against the tile maximum (and, with ENT, the
-  // entropy moments sum e (z - m), same tree); the one lane holding the
-  // target column of a row parks z[r, t] in LDS.  The empty asm keeps the
-  // LDS reads of row group i from being hoisted above group i - 1, which
-  // would hold every row's operands in registers at once.
+  // Pass 2.  The lane's rows are 4 consecutive rows per row group i, so their
+  // codes and tile maxima come in as one 16-byte LDS read per group, all
+  // issued before any use.  First the target copies: the one lane holding
+  // the target column of a row parks z[r, t] in LDS.  A wave's 64 columns
+  // hold a target only now and then, so the hit tests run branch-free and
+  // one wave-uniform branch enters the copy only when some lane has a hit.
+  // Then the quarter sums against the tile maximum (and, with ENT, the
+  // entropy moments sum e (z - m), same tree) as one branch-free block, so
+  // that the exponentials of all row groups interleave.
+  int4 code4[MI];
+  float4 m4[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int lr = row0 + i * 16 + 4 * g;
+    code4[i] = *reinterpret_cast<const int4*>(&rd.code[lr]);
+    m4[i] = *reinterpret_cast<const float4*>(&rd.tmax[lr]);
+  }
+  // 1 when this lane holds the target column of a row with this code (the
+  // code is -1 or -2 for rows whose target is elsewhere or absent)
+  auto holds_target = [&](int code) {
+    const unsigned off = static_cast<unsigned>(code - col0);
+    return static_cast<int>(off < static_cast<unsigned>(NJ * 16)) &
+           static_cast<int>((off & 15u) == static_cast<unsigned>(li));
+  };
+  int any_hit = 0;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+    any_hit |= holds_target(code4[i].x) | holds_target(code4[i].y) | holds_target(code4[i].z) |
+               holds_target(code4[i].w);
+  if (__builtin_amdgcn_ballot_w64(any_hit != 0)) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int c4[4] = {code4[i].x, code4[i].y, code4[i].z, code4[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (holds_target(c4[q])) {
+          const int off = c4[q] - col0;
+          float zt = acc[i][0][q];
+#pragma unroll
+          for (int j = 1; j < NJ; ++j)
+            if ((off >> 4) == j) zt = acc[i][j][q];
+          rd.tval[row0 + i * 16 + 4 * g + q] = zt;
+        }
+      }
+    }
+  }
   float wpart[ENT ? MI : 1][4][NQ];
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    asm volatile("" ::: "memory");
+    const float mq[4] = {m4[i].x, m4[i].y, m4[i].z, m4[i].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int lr = row0 + i * 16 + 4 * g + q;
-      const float m = rd.tmax[lr];
+      const float m = mq[q];
 #pragma unroll
       for (int h = 0; h < NQ; ++h) {
         if constexpr (ENT) {
@@ -150,14 +190,6 @@ __device__ __forceinline__ void stats_epilogue_body(const f32x4 (&acc)[MI][NJ], 
           for (int j = 4 * h + 1; j < 4 * h + 4; ++j) s = s + exp_sub(z(i, j, q), m);
           part[i][q][h] = row16_sum_first(s);
         }
-      }
-      const int off = rd.code[lr] - col0;
-      if (off >= 0 && off < NJ * 16 && (off & 15) == li) {
-        float zt = acc[i][0][q];
-#pragma unroll
-        for (int j = 1; j < NJ; ++j)
-          if ((off >> 4) == j) zt = acc[i][j][q];
-        rd.tval[lr] = zt;
       }
     }
   }
