@@ -19,6 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libinvariant_logp.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "logp_kernels.hip", "linear_logp.hip", "linear_bwd.hip"]
+# bandwidth probes that bench.py times next to the kernels (not part of the
+# library's C ABI)
+PROBE_PATH = os.path.join(HERE, "libitl_ceiling.so")
+PROBE_SOURCES = ["ceiling.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -42,11 +46,10 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def build(verbose=False):
-    """Compile every HIP source into LIB_PATH (always recompiles)."""
-    tmp = LIB_PATH + ".tmp"
+def _compile(sources, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,7 +63,15 @@ def build(verbose=False):
             if "-packed-fp32-ops' is not a recognized feature" not in ln]
     if verbose and rest:
         sys.stderr.write("\n".join(rest) + "\n")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False):
+    """Compile every HIP source into LIB_PATH, and the bandwidth probes into
+    PROBE_PATH (always recompiles)."""
+    _compile(SOURCES, LIB_PATH, verbose)
+    _compile(PROBE_SOURCES, PROBE_PATH, verbose)
     return LIB_PATH
 
 
@@ -68,7 +79,7 @@ def asm(out_dir, verbose=False):
     """Write the gfx950 assembly of every source (for reading the code the
     compiler produced: reductions, conversions, absence of contraction)."""
     os.makedirs(out_dir, exist_ok=True)
-    for s in SOURCES:
+    for s in SOURCES + PROBE_SOURCES:
         out = os.path.join(out_dir, s.replace(".hip", ".s"))
         cmd = [hipcc(), *[f for f in FLAGS if f not in ("-shared", "-fPIC")],
                "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC,
