@@ -450,7 +450,7 @@ def linear_fwd_stats(args, torch, itl, synth, prepared, ctx=None):
     return res, (hid, wt, t)
 
 
-def linear_bwd_stats(args, torch, itl, synth, saved=False, prepared=False):
+def linear_bwd_stats(args, torch, itl, synth, saved=False, prepared=False, vocab_chunk=0):
     n, h, v, hid, wt, t = _linear_case(torch, synth, ignore_frac=0.05)
     dev = hid.device
     g = synth.normal_matrix(1, n, 1.0, torch.float32, 1055, dev)[0]
@@ -464,18 +464,21 @@ def linear_bwd_stats(args, torch, itl, synth, saved=False, prepared=False):
     wtp = itl.prepare_weight(wt) if prepared else None
     dh = torch.empty(n, h, dtype=torch.float32, device=dev)
     dw = torch.empty(v, h, dtype=torch.float32, device=dev)
-    ws = torch.empty(itl.lib().linear_logp_bwd_workspace_bytes(n, h, v, 256), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(itl.linear_logp_bwd_workspace_bytes(n, h, v, prepared=prepared,
+                                                         saved_logits=saved,
+                                                         vocab_chunk=vocab_chunk),
+                     dtype=torch.uint8, device=dev)
 
     def run():
         itl.linear_logp_bwd(hid, wt, t, lse, g, dhidden_out=dh, dweight_out=dw, workspace=ws,
-                            saved_logits=z, prepared_weight=wtp)
+                            saved_logits=z, prepared_weight=wtp, vocab_chunk=vocab_chunk)
 
     st = timed(torch, run, args)
     # z recomputed (not when saved), dh = dz W, dW = dz^T h
     flops = (2 if saved else 3) * 2.0 * n * h * v
     res = _mfma_entry(st, flops)
     res["workspace_bytes"] = ws.numel()
+    res["vocab_chunk"] = vocab_chunk or "default"
     return res, n * v * 4 if saved else 0
 
 
@@ -524,7 +527,7 @@ def standalone_linear(args, torch, itl, synth, ctx, prepared):
 
 
 def standalone_linear_bwd(args, torch, itl, synth, ctx, saved=False, prepared=False):
-    r, extra = linear_bwd_stats(args, torch, itl, synth, saved, prepared)
+    r, extra = linear_bwd_stats(args, torch, itl, synth, saved, prepared, args.vocab_chunk)
     n = 4096
     return {
         "metric": "rows/s and MFMA TFLOP/s (% of peak), fused LM-head+logp backward N=4096 "
@@ -546,6 +549,7 @@ def standalone_linear_bwd(args, torch, itl, synth, ctx, saved=False, prepared=Fa
                      "kernel": "linear_logp_bwd (all launches: dz, the transposes, "
                                "two products)"},
         "extra_memory_bytes": extra, "workspace_bytes": r["workspace_bytes"],
+        "vocab_chunk": r["vocab_chunk"],
     }
 
 
@@ -561,6 +565,11 @@ def default_secondary(args, torch, itl, synth, ctx):
     torch.cuda.empty_cache()
     r, _ = linear_bwd_stats(args, torch, itl, synth)
     sec["linear_bwd_qwen3_4096x4096x151936"] = r
+    torch.cuda.empty_cache()
+    # the memory trade-off: the whole vocabulary in one chunk (largest
+    # workspace, fewest launches), the same bits
+    r, _ = linear_bwd_stats(args, torch, itl, synth, vocab_chunk=synth.QWEN3_VOCAB)
+    sec["linear_bwd_one_chunk_qwen3_4096x4096x151936"] = r
     torch.cuda.empty_cache()
     return sec
 
@@ -784,6 +793,8 @@ def main():
                              "linear_bwd_prepared", "linear_prepared"])
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows for the fused LM head's CPU oracle baseline (0 = 512)")
+    ap.add_argument("--vocab-chunk", type=int, default=0,
+                    help="fused backward workloads: vocabulary columns per pass (0 = default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="default workload: skip the measurements after the headline")

@@ -296,14 +296,29 @@ int32_t linear_logp_fwd_noalloc(const void* hidden, int64_t ld_h, const void* we
                                 void* logits_out, int32_t logits_dtype, int64_t ld_logits,
                                 const void* prepared, size_t prepared_bytes, void* hip_stream);
 
+/* Options of a linear_logp_bwd call, for its workspace size. */
+enum logp_bwd_flags {
+  LOGP_BWD_DHIDDEN = 1,       /* dhidden requested */
+  LOGP_BWD_DWEIGHT = 2,       /* dweight requested */
+  LOGP_BWD_PREPARED = 4,      /* a prepared weight is passed */
+  LOGP_BWD_SAVED_LOGITS = 8,  /* the forward's logits are passed (no recompute) */
+  LOGP_BWD_BF16_OUT = 16      /* out_dtype is LOGP_BF16 */
+};
+
 /*
- * Workspace of linear_logp_bwd in bytes: W^T [h, Vp], h^T [h, Np], dz [Np, Vp],
- * dz^T [Vp, Np] and a copy of hidden [Np, h], all bf16 and re-laid for the
- * products' loads, with Np, Vp = n, v rounded up to multiples of 256 (about
- * 3.8 GB at n = 4096, h = 4096, v = 151936).  0 when n = 0 or for arguments
- * linear_logp_bwd would reject.
+ * Workspace of linear_logp_bwd in bytes for a call with these options
+ * (flags: logp_bwd_flags of the call) and vocabulary chunk (vocab_chunk: as
+ * linear_logp_bwd's).  The backward walks the vocabulary in chunks, so the
+ * workspace holds one chunk's dz and dz^T (bf16, [Np, C] and [C, Np]), the
+ * chunk's W^T (bf16 [h, C], none with a prepared weight), a re-laid copy of
+ * hidden ([Np, h], none with saved logits), hidden^T ([h, Np], only for
+ * dweight) and, for bf16 dhidden over several chunks, the fp32 dhidden
+ * between chunks ([n, h]); Np = n rounded up to 256, C = the chunk width.
+ * About 0.87 GB at n = h = 4096, v = 151936 with the default chunk and both
+ * outputs (0.60 GB with a prepared weight).  0 when n = 0 or for arguments linear_logp_bwd would reject.
  */
-size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width);
+size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width,
+                                       int32_t flags, int64_t vocab_chunk);
 
 /*
  * Backward of the fused LM head + log-probability ("[RFC][ROCm] End-to-end
@@ -358,9 +373,18 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *   dhidden     [n, ld_dh] of out_dtype, or NULL to skip that product.
  *   dweight     [v, ld_dw] of out_dtype, or NULL to skip that product (with
  *               n = 0 it is written with zeros).  At least one is non-NULL.
- *               Both are overwritten, not accumulated into.
- *   workspace   at least linear_logp_bwd_workspace_bytes(...) bytes,
- *               256-byte aligned (may be NULL when that is 0).
+ *               Both are overwritten, not accumulated into (an fp32 dhidden
+ *               holds partial sums while the call runs).
+ *   vocab_chunk vocabulary columns per pass (rounded up to a multiple of 256;
+ *               0 = the library's default, 32768).  Per chunk the backward
+ *               forms dz for those columns, finishes their dweight rows (K =
+ *               every token, ascending) and continues the dhidden
+ *               accumulators (K = vocabulary, ascending across the chunks).
+ *               Any value gives the same bits; it trades workspace for
+ *               launches.  Negative: LOGP_ERR_SHAPE.
+ *   workspace   at least linear_logp_bwd_workspace_bytes(n, h, v, tile_width,
+ *               <this call's flags>, vocab_chunk) bytes, 256-byte aligned
+ *               (may be NULL when that is 0).
  * Active targets outside [0, v) are not checked: such a row gets no one-hot
  * term.
  */
@@ -372,7 +396,8 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                         size_t prepared_bytes, const float* lse, const float* grad_logp,
                         const float* entropy, const float* grad_entropy, int32_t out_dtype,
                         void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
-                        void* workspace, size_t workspace_bytes, void* hip_stream);
+                        int64_t vocab_chunk, void* workspace, size_t workspace_bytes,
+                        void* hip_stream);
 
 /* Short English text for a status code (static storage, host memory). */
 const char* logp_status_str(int32_t status);

@@ -32,6 +32,12 @@ LOGP_I32 = 1
 LOGP_ROUND_NONE = 0
 LOGP_ROUND_BF16 = 1
 
+LOGP_BWD_DHIDDEN = 1
+LOGP_BWD_DWEIGHT = 2
+LOGP_BWD_PREPARED = 4
+LOGP_BWD_SAVED_LOGITS = 8
+LOGP_BWD_BF16_OUT = 16
+
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 _f32 = ctypes.c_float
 
@@ -48,10 +54,10 @@ _SIGNATURES = {
     "linear_logp_fwd_noalloc": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
                                        _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _vp,
                                        _sz, _vp]),
-    "linear_logp_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "linear_logp_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i64]),
     "linear_logp_bwd": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64,
                                _i32, _f32, _i32, _vp, _i32, _i64, _vp, _sz, _vp, _vp, _vp, _vp,
-                               _i32, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+                               _i32, _vp, _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
     "linear_logp_prepared_bytes": (_sz, [_i64, _i64]),
     "linear_logp_prepare_weight": (_i32, [_vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "logp_status_str": (ctypes.c_char_p, [_i32]),

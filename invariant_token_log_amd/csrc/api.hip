@@ -8,6 +8,11 @@
 
 namespace {
 
+static_assert(itl::kBwdDhidden == LOGP_BWD_DHIDDEN && itl::kBwdDweight == LOGP_BWD_DWEIGHT &&
+                  itl::kBwdPrepared == LOGP_BWD_PREPARED &&
+                  itl::kBwdSaved == LOGP_BWD_SAVED_LOGITS && itl::kBwdBf16Out == LOGP_BWD_BF16_OUT,
+              "backward option flags");
+
 constexpr int kMaxTiles = 4096;
 constexpr size_t kAlign = 256;
 
@@ -311,10 +316,12 @@ int32_t linear_logp_fwd_noalloc(const void* hidden, int64_t ld_h, const void* we
                         prepared_bytes, nullptr, 0, true, hip_stream);
 }
 
-size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width) {
+size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width,
+                                       int32_t flags, int64_t vocab_chunk) {
   if (n < 0 || v < 1 || h < 64 || h % 64 || tile_width != itl::kLinearTile) return 0;
+  if (vocab_chunk < 0 || flags < 0 || flags > 31) return 0;
   if (n == 0) return 0;
-  return static_cast<size_t>(itl::linear_bwd_layout(n, h, v).total);
+  return static_cast<size_t>(itl::linear_bwd_layout(n, h, v, flags, vocab_chunk).total);
 }
 
 int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
@@ -324,10 +331,11 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                         int32_t saved_dtype, int64_t ld_saved, const void* prepared,
                         size_t prepared_bytes, const float* lse, const float* grad_logp,
                         const float* entropy, const float* grad_entropy, int32_t out_dtype,
-                        void* dhidden,
-                        int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace,
-                        size_t workspace_bytes, void* hip_stream) {
+                        void* dhidden, int64_t ld_dh, void* dweight, int64_t ld_dw,
+                        int64_t vocab_chunk, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
   if (n < 0 || v < 1 || h < 64 || h % 64 || ld_h < h || ld_w < h) return LOGP_ERR_SHAPE;
+  if (vocab_chunk < 0 || vocab_chunk > (int64_t{1} << 40)) return LOGP_ERR_SHAPE;
   if (v > (int64_t{1} << 31) || n > (int64_t{1} << 31) ||
       ((n + 255) / 256) * ((v + 255) / 256) > (int64_t{1} << 30) ||
       ((v + 255) / 256) * ((h + 255) / 256) > (int64_t{1} << 30))
@@ -354,7 +362,11 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
   if ((entropy == nullptr) != (grad_entropy == nullptr)) return LOGP_ERR_NULL;
   if ((n > 0 && !aligned16(hidden, ld_h, LOGP_BF16)) || !aligned16(weight, ld_w, LOGP_BF16))
     return LOGP_ERR_ALIGN;
-  const size_t need = linear_logp_bwd_workspace_bytes(n, h, v, tile_width);
+  const int32_t flags = (dhidden ? LOGP_BWD_DHIDDEN : 0) | (dweight ? LOGP_BWD_DWEIGHT : 0) |
+                        (prepared ? LOGP_BWD_PREPARED : 0) |
+                        (saved_logits ? LOGP_BWD_SAVED_LOGITS : 0) |
+                        (out_dtype == LOGP_BF16 ? LOGP_BWD_BF16_OUT : 0);
+  const size_t need = linear_logp_bwd_workspace_bytes(n, h, v, tile_width, flags, vocab_chunk);
   if (need && (!workspace || workspace_bytes < need ||
                reinterpret_cast<uintptr_t>(workspace) % kAlign))
     return LOGP_ERR_WORKSPACE;
@@ -366,7 +378,7 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
                          static_cast<const uint16_t*>(prepared), lse, grad_logp,
                          inv_temperature(temperature), logits_rounding == LOGP_ROUND_BF16 ? 1 : 0,
                          entropy, grad_entropy,
-                         out_dtype == LOGP_BF16, dhidden, ld_dh, dweight, ld_dw,
+                         out_dtype == LOGP_BF16, dhidden, ld_dh, dweight, ld_dw, vocab_chunk,
                          static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream));
   return hip_status();
 }

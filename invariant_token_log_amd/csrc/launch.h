@@ -63,16 +63,22 @@ int64_t linear_fwd_blocked_bytes(int64_t n, int64_t h);
 
 constexpr int kLinearTile = 256;
 
-// Workspace of the fused LM-head backward (byte offsets): W^T [h, vp],
-// h^T [h, np], dz [np, vp], dz^T [vp, np], all bf16; np, vp = n, v rounded up
-// to multiples of 256.
-// Workspace of the fused backward (byte offsets): W^T, h^T, dz, dz^T and the
-// blocked h, all K32-blocked bf16 with N, V padded to np, vp.
+// Fused LM-head backward.  The vocabulary is walked in chunks of vc columns
+// (a multiple of 256; kDefaultChunk unless the caller asks for another), so
+// the workspace holds one chunk's dz_c [np, vc] and dz_c^T [vc, np], W^T_c
+// [h, vc] (no prepared weight), the blocked hidden rows [np, h] (logits
+// recomputed), h^T [h, np] (dW), and the fp32 dh [n, h] between chunks (bf16
+// dh over several chunks); only the regions the call uses (flags).  Byte
+// offsets, -1 for a region not used; np, vp = n, v rounded up to 256.
+constexpr int64_t kDefaultChunk = 32768;
+enum { kBwdDhidden = 1, kBwdDweight = 2, kBwdPrepared = 4, kBwdSaved = 8, kBwdBf16Out = 16 };
 struct LinearBwdLayout {
-  int64_t np, vp;
-  int64_t wt, ht, dz, dzt, hb, total;
+  int64_t np, vp, vc;
+  int64_t hb, ht, dz, dzt, wt, dh32, total;
 };
-LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
+int64_t linear_bwd_chunk(int64_t v, int64_t vocab_chunk);
+LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v, int32_t flags,
+                                  int64_t vocab_chunk);
 
 // dh [n, h] and/or dW [v, h] (either may be null) as fp32 or bf16 (bf16_out).
 // inv_t: reciprocal temperature (1 = none); ent / gent: row entropy and its
@@ -80,15 +86,16 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v);
 // with z_bf16; [n, ld_z]) holds the forward's unscaled logits to read instead
 // of recomputing them, or is null.  prepared (or null) is the caller's
 // prepared weight (launch_prepare_weight): its blocked W feeds the recomputed
-// product and its W^T the dh product instead of a transpose of W into the
-// workspace.
+// product and its W^T the dh product instead of transposing W into the
+// workspace.  vocab_chunk: columns per chunk (0 = kDefaultChunk), any value
+// gives the same bits; ws: linear_bwd_layout(...).total bytes.
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
                        const void* zsaved, int32_t z_bf16, int64_t ld_z,
                        const uint16_t* prepared, const float* lse,
                        const float* grad, float inv_t, int32_t round_bf16, const float* ent,
                        const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
-                       int64_t ld_dw, char* ws, hipStream_t s);
+                       int64_t ld_dw, int64_t vocab_chunk, char* ws, hipStream_t s);
 
 // Prepared weight, bf16, both parts K32-blocked (mfma_gemm.h) with vp =
 // round_up(v, 256): W [vp rows, K = h] (rows v.. zero), then W^T [h rows,

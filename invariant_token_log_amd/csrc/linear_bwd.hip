@@ -15,17 +15,30 @@
 // single ascending K walk with no split, so dh[r] depends only on row r (batch
 // invariant) and dW is deterministic for a given token order.
 //
+// The vocabulary is walked in chunks of whole 256-column tiles (the
+// caller's vocab_chunk, default kDefaultChunk columns); per chunk [c0, c1):
+//   dz_c, dz_c^T = the chunk's columns of dz (recomputed tiles, or the saved
+//                  logits);
+//   dW[c0:c1]    = dz_c^T h        (K = all tokens, ascending: final rows);
+//   dh          += dz_c W[c0:c1]   (K = the chunk's vocabulary, ascending,
+//                                   continuing the fp32 accumulators the
+//                                   previous chunk stored).
+// Continuing a K walk from stored fp32 accumulators gives the same bits as
+// one walk, so the chunk width changes the memory the backward needs, not a
+// bit of dh or dW.
+//
 // Kernels (the products on the 256 x 256 tile of mfma_gemm.h):
 //   block_rows_bf16   : h [N, H] -> the K32-blocked copy the recomputed
 //                       product reads;
-//   linear_dz_kernel  : h x W^T tile -> dz in registers -> transposed, then
-//                       row-major LDS tile -> dz^T [Vp, Np] and dz [Np, Vp];
-//   linear_dz_saved_kernel: the same dz and dz^T from saved logits, 64 x 64
-//                       tiles streamed through LDS;
-//   transpose_block_bf16: W [V, H] -> W^T [H, Vp], h [N, H] -> h^T [H, Np];
-//   gemm_out_kernel   : C = A B^T with fp32 or RNE-bf16 output.
-// Every operand the backward writes for a product (dz, dz^T, W^T, h^T and
-// the blocked h) is in the K32-blocked layout of mfma_gemm.h: the same
+//   linear_dz_kernel  : h x W^T tile of one chunk -> dz in registers ->
+//                       transposed, then row-major LDS tile -> dz_c^T and dz_c;
+//   linear_dz_saved_kernel: the same dz_c and dz_c^T from saved logits, 32 x
+//                       256 tiles through LDS;
+//   transpose_blocked : W[c0:c1] -> W^T_c [H, c1 - c0], h -> h^T [H, Np]
+//                       (32 x 256 tiles through LDS);
+//   gemm_out_kernel   : C = A B^T (+ stored C) with fp32 or RNE-bf16 output.
+// Every operand the backward writes for a product (dz_c, dz_c^T, W^T_c, h^T
+// and the blocked h) is in the K32-blocked layout of mfma_gemm.h: the same
 // values, read with whole-line loads.  Np, Vp are N and V rounded up to
 // multiples of 256; padded rows and columns hold zeros and add exact zeros to
 // the K walks.
@@ -46,45 +59,65 @@ __device__ __forceinline__ uint16_t bf16_bits(float d) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(d));
 }
 
-// dst = the K32-blocked [gridDim.x * 64 rows, K = rows_p] operand with
-// element (c, r) = r < rows ? src[r][c] : 0 (rows_p a multiple of 64).  64 x 64
-// tiles through LDS; 16-byte global accesses.
-__global__ __launch_bounds__(256) void transpose_block_bf16(const uint16_t* __restrict__ src,
-                                                            int64_t ld_src, int64_t rows,
-                                                            int64_t rows_p,
-                                                            uint16_t* __restrict__ dst) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int t = threadIdx.x;
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64; r0 < rows_p;
-       r0 += static_cast<int64_t>(gridDim.y) * 64) {
-    {
-      const int r = t / 4, cs = (t % 4) * 16;
-      uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
-      if (r0 + r < rows) {
-        const uint16_t* p = src + (r0 + r) * ld_src + c0 + cs;
-        a = *reinterpret_cast<const uint4*>(p);
-        b = *reinterpret_cast<const uint4*>(p + 8);
-      }
-      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// 32 x 256 tiles of bf16 staged in LDS for the transposing kernels (rows
+// padded to 264 elements: 16-byte aligned, and the 8-row gathers of the
+// transposed reads fall on different banks).
+constexpr int kTR = 32, kTC = 256, kTS = kTC + 8;
+
+// The 16-byte piece of the transposed tile that starts at tile row rq (a
+// multiple of 8) in column c: tile[rq + 0..7][c] packed low to high.
+__device__ __forceinline__ uint4 gather_column8(const uint16_t (*tile)[kTS], int rq, int c) {
+  uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        tile[r][cs + 2 * e] = static_cast<uint16_t>(w[e] & 0xffffu);
-        tile[r][cs + 2 * e + 1] = static_cast<uint16_t>(w[e] >> 16);
-      }
+  for (int e = 0; e < 4; ++e)
+    w[e] = static_cast<uint32_t>(tile[rq + 2 * e][c]) |
+           (static_cast<uint32_t>(tile[rq + 2 * e + 1][c]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Writes the tile transposed: column c (< cols_here) becomes destination row
+// c_dst0 + c of the K32-blocked dst (K steps per 16-row block: ksteps), its
+// 32 tile rows the K range [k0, k0 + 32).  16 pieces of 1 KiB, one 16-byte
+// chunk per thread and step.
+__device__ __forceinline__ void store_transposed(const uint16_t (*tile)[kTS], uint16_t* dst,
+                                                 int64_t c_dst0, int cols_here, int64_t k0,
+                                                 int64_t ksteps, int tid) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = tid + 256 * u;
+    const int p = q >> 6, e = q & 63;
+    const int c = p * 16 + (e >> 2), rq = (e & 3) * 8;
+    if (c < cols_here)
+      store_stream(dst + gemm::kblocked_index(c_dst0 + c, k0 + rq, ksteps),
+                   gather_column8(tile, rq, c));
+  }
+}
+
+// dst = the K32-blocked [cols, K = rows_p] operand with element (c, r) =
+// r < rows ? src[r * ld + c] : 0 (cols a multiple of 16, rows_p of 32).
+// Tiles of 32 source rows x 256 source columns: every thread loads 16-byte
+// chunks of whole 512-byte row segments, the tile leaves as 1 KiB pieces.
+// Grid: x = column tiles, y = row tiles (grid-stride beyond gridDim.y).
+__global__ __launch_bounds__(256) void transpose_blocked(const uint16_t* __restrict__ src,
+                                                         int64_t ld, int64_t rows,
+                                                         int64_t rows_p, int64_t cols,
+                                                         uint16_t* __restrict__ dst) {
+  __shared__ __align__(16) uint16_t tile[kTR][kTS];
+  const int tid = threadIdx.x;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTC;
+  const int cols_here = static_cast<int>(cols - c0 < kTC ? cols - c0 : kTC);
+  const int64_t ksteps = rows_p / gemm::kK;
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.y) * kTR; r0 < rows_p;
+       r0 += static_cast<int64_t>(gridDim.y) * kTR) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid >> 5) + 8 * u, ch = (tid & 31) * 8;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (r0 + r < rows && ch < cols_here) x = load_stream(src + (r0 + r) * ld + c0 + ch);
+      *reinterpret_cast<uint4*>(&tile[r][ch]) = x;
     }
     __syncthreads();
-    {
-      const int c = t / 4, rs = (t % 4) * 16;
-      uint32_t w[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        w[e] = static_cast<uint32_t>(tile[rs + 2 * e][c]) |
-               (static_cast<uint32_t>(tile[rs + 2 * e + 1][c]) << 16);
-      uint16_t* p = dst + gemm::kblocked_index(c0 + c, r0 + rs, rows_p / gemm::kK);
-      *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-      *reinterpret_cast<uint4*>(p + 8) = make_uint4(w[4], w[5], w[6], w[7]);
-    }
+    store_transposed(tile, dst, c0, cols_here, r0, ksteps, tid);
     __syncthreads();
   }
 }
@@ -142,15 +175,18 @@ struct SmemDz {
   int code[kT];
 };
 
-// hidden K32-blocked (mblocks * 256 rows); weight row-major, or K32-blocked
-// with vblocks * 256 rows when WBLK (a prepared weight).  PLAIN: launched
-// only when no option is on (no rounding, T = 1, no entropy term), so the
+// dz of the vocabulary chunk of vcb 256-column blocks starting at block vb0:
+// dz_c [Np, K = vcb * 256] and dz_c^T [vcb * 256, K = Np], both K32-blocked
+// with the chunk's own columns (either may be null: not stored).  hidden
+// K32-blocked (mblocks * 256 rows); weight row-major, or K32-blocked with
+// vblocks * 256 rows when WBLK (a prepared weight).  PLAIN: launched only
+// when no option is on (no rounding, T = 1, no entropy term), so the
 // epilogue skips their operations instead of selecting around them.
 template <bool WBLK, bool PLAIN>
 __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
-    int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
-    const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
+    int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks, int vb0,
+    int vcb, const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse,
     const float* __restrict__ grad, float inv_t, int32_t round_bf16,
     const float* __restrict__ ent, const float* __restrict__ gent, uint16_t* __restrict__ dz,
@@ -164,9 +200,10 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   const int li = lane % 16, g = lane / 16;
 
   int mb, vb;
-  gemm::tile_coords(gemm::xcd_logical(blockIdx.x, mblocks * vblocks), mblocks, vblocks, mb, vb);
+  gemm::tile_coords(gemm::xcd_logical(blockIdx.x, mblocks * vcb), mblocks, vcb, mb, vb);
   const int64_t m0 = static_cast<int64_t>(mb) * kT;
-  const int64_t v0 = static_cast<int64_t>(vb) * kT;
+  const int64_t vl0 = static_cast<int64_t>(vb) * kT;          // column inside the chunk
+  const int64_t v0 = static_cast<int64_t>(vb0) * kT + vl0;    // vocabulary column
   if (tid < kT) {
     const int64_t r = m0 + tid;
     int code = -2;
@@ -195,9 +232,11 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  gemm::mainloop<true, WBLK>(sm.u.st, hidden, 0, m0, static_cast<int64_t>(mblocks) * kT, weight,
-                             ld_w, v0, WBLK ? static_cast<int64_t>(vblocks) * kT : v,
-                             static_cast<int>(hdim / gemm::kK), acc);
+  const int ksteps = static_cast<int>(hdim / gemm::kK);
+  const int64_t kblk = static_cast<int64_t>(ksteps) * 512;  // blocked: 16-row block stride
+  gemm::mainloop<true, WBLK>(sm.u.st, hidden, kblk, m0, static_cast<int64_t>(mblocks) * kT, weight,
+                             WBLK ? kblk : ld_w, v0, WBLK ? static_cast<int64_t>(vblocks) * kT : v,
+                             ksteps, acc);
   __syncthreads();
 
   // dz of every element (dz_value; 0 on ignored / padded rows and columns),
@@ -240,23 +279,26 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   // dz^T: tile[c][r] (column-major), then out in K32-blocked order: 128
   // pieces of 16 rows x 32 tokens, one contiguous KiB each.
   const int64_t np_steps = static_cast<int64_t>(mblocks) * (kT / gemm::kK);
-  const int64_t vp_steps = static_cast<int64_t>(vblocks) * (kT / gemm::kK);
+  const int64_t vc_steps = static_cast<int64_t>(vcb) * (kT / gemm::kK);
+  if (dzt) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int lc = wn * 64 + j * 16 + li;
-      const int lr = wm * 128 + i * 16 + 4 * g;
-      *reinterpret_cast<uint2*>(&sm.u.tile[lc][lr]) = make_uint2(dv[i][j][0], dv[i][j][1]);
+      for (int j = 0; j < 4; ++j) {
+        const int lc = wn * 64 + j * 16 + li;
+        const int lr = wm * 128 + i * 16 + 4 * g;
+        *reinterpret_cast<uint2*>(&sm.u.tile[lc][lr]) = make_uint2(dv[i][j][0], dv[i][j][1]);
+      }
+    __syncthreads();
+    for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
+      const int piece = idx >> 6, e = idx & 63;
+      const int c = (piece >> 3) * 16 + (e >> 2), r = (piece & 7) * 32 + (e & 3) * 8;
+      store_stream(dzt + gemm::kblocked_index(vl0 + c, m0 + r, np_steps),
+                   *reinterpret_cast<const uint4*>(&sm.u.tile[c][r]));
     }
-  __syncthreads();
-  for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
-    const int piece = idx >> 6, e = idx & 63;
-    const int c = (piece >> 3) * 16 + (e >> 2), r = (piece & 7) * 32 + (e & 3) * 8;
-    store_stream(dzt + gemm::kblocked_index(v0 + c, m0 + r, np_steps),
-                 *reinterpret_cast<const uint4*>(&sm.u.tile[c][r]));
+    __syncthreads();
   }
-  __syncthreads();
+  if (!dz) return;
   // dz: tile[r][c] (row-major), then out in K32-blocked order.
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -273,132 +315,157 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
     const int piece = idx >> 6, e = idx & 63;
     const int r = (piece >> 3) * 16 + (e >> 2), c = (piece & 7) * 32 + (e & 3) * 8;
-    store_stream(dz + gemm::kblocked_index(m0 + r, v0 + c, vp_steps),
+    store_stream(dz + gemm::kblocked_index(m0 + r, vl0 + c, vc_steps),
                  *reinterpret_cast<const uint4*>(&sm.u.tile[r][c]));
   }
 }
 
-// dz and dz^T from the forward's saved unscaled logits (fp32, or bf16 with
-// ZBF16; [n, ld_z], 16-byte aligned rows) instead of the recomputed product:
-// the same values through the same dz_value, so the same bits.  64 x 64
-// tiles of [Np, Vp]: thread (r = tid / 4, 16 columns from (tid % 4) * 16)
-// reads its 16 logits with 16-byte loads, writes its 16 dz along the row,
-// and the tile leaves transposed through LDS for dz^T (both K32-blocked).
-// Rows past n or ignored, and columns past v, get 0 without reading the
-// logits.
-constexpr int kST = 64;
-
+// dz_c and dz_c^T of the vocabulary chunk [c0, c0 + cols_p) from the
+// forward's saved unscaled logits (fp32, or bf16 with ZBF16; [n, ld_z],
+// 16-byte aligned rows) instead of the recomputed product: the same values
+// through the same dz_value, so the same bits.  Tiles of 32 rows x 256
+// chunk columns: the logits of a row segment come in as 16-byte non-temporal
+// loads of whole 512-byte (bf16) or 1 KiB (fp32) pieces, the bf16 dz goes
+// to an LDS tile, and leaves as 1 KiB K32-blocked pieces: along the rows for
+// dz_c [Np, K = cols_p], transposed for dz_c^T [cols_p, K = Np] (either may
+// be null: not stored).  Rows past n or ignored, and columns past v, get 0
+// without reading the logits.  Grid: x = row tiles, y = column tiles
+// (grid-stride beyond gridDim.y): neighbouring workgroups take neighbouring
+// 32-row tiles, so each one's dz_c^T pieces continue the previous one's in
+// memory.
 template <bool ZBF16>
 __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
     const void* __restrict__ zsaved, int64_t ld_z, int64_t n, int64_t v, int64_t np_rows,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse, const float* __restrict__ grad, float inv_t,
     int32_t round_bf16, const float* __restrict__ ent, const float* __restrict__ gent,
-    int64_t vp_cols, uint16_t* __restrict__ dz, uint16_t* __restrict__ dzt) {
+    int64_t c0, int64_t cols_p, uint16_t* __restrict__ dz, uint16_t* __restrict__ dzt) {
   const Targets targets{tgt, tgt32};
-  __shared__ uint16_t tile[kST][kST + 8];
+  __shared__ __align__(16) uint16_t tile[kTR][kTS];
+  __shared__ float rowc[kTR][4];  // lse, g, entropy, -gH of each tile row
+  __shared__ int64_t rowt[kTR];   // target (ignore_index: no gradient)
   const int tid = threadIdx.x;
-  const int r = tid / 4, cs = (tid % 4) * 16;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kST;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTR;
   const bool scaled = inv_t != 1.0f;
   const bool with_ent = ent != nullptr;
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.y) * kST; r0 < np_rows;
-       r0 += static_cast<int64_t>(gridDim.y) * kST) {
-    const int64_t row = r0 + r;
-    int64_t t = ignore_index;
-    float L = 0.0f, G = 0.0f, H = 0.0f, NGH = 0.0f;
-    if (row < n) {
-      t = targets[row];
-      if (t != ignore_index) {
-        L = lse[row];
-        G = grad[row];
-        if (with_ent) {
-          H = ent[row];
-          NGH = -gent[row];
+  constexpr int E = ZBF16 ? 8 : 4;         // elements per 16-byte chunk
+  constexpr int CPR = kTC / E;             // chunks per tile row
+  constexpr int RPS = 256 / CPR;           // tile rows per step of the block
+  const int64_t vc_steps = cols_p / gemm::kK, np_steps = np_rows / gemm::kK;
+  for (int64_t cl0 = static_cast<int64_t>(blockIdx.y) * kTC; cl0 < cols_p;
+       cl0 += static_cast<int64_t>(gridDim.y) * kTC) {
+    const int64_t col0 = c0 + cl0;  // vocabulary column of the tile
+    if (tid < kTR) {
+      const int64_t row = r0 + tid;
+      int64_t t = ignore_index;
+      float L = 0.0f, G = 0.0f, H = 0.0f, NGH = 0.0f;
+      if (row < n) {
+        t = targets[row];
+        if (t != ignore_index) {
+          L = lse[row];
+          G = grad[row];
+          if (with_ent) {
+            H = ent[row];
+            NGH = -gent[row];
+          }
         }
       }
+      rowt[tid] = row < n ? t : ignore_index;
+      rowc[tid][0] = L;
+      rowc[tid][1] = G;
+      rowc[tid][2] = H;
+      rowc[tid][3] = NGH;
     }
-    const bool live = row < n && t != ignore_index;
-    float zv[16];
+    __syncthreads();
+    // All of this thread's loads go out before any arithmetic: chunk u is
+    // row tid / CPR + RPS u, columns (tid % CPR) E + [0, E).
+    constexpr int NU = kTR / RPS;
+    const int ch = (tid % CPR) * E;
+    const int64_t col = col0 + ch;
+    const bool whole = col + E <= v;  // the chunk lies inside the row
+    uint4 w[NU];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) zv[u] = 0.0f;
-    const int64_t col = c0 + cs;
-    if (live) {
-      if (col + 16 <= v) {
-        if constexpr (ZBF16) {
-          const uint16_t* p = static_cast<const uint16_t*>(zsaved) + row * ld_z + col;
+    for (int u = 0; u < NU; ++u) {
+      const int r = tid / CPR + RPS * u;
+      const int64_t row = r0 + r;
+      w[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (whole && row < n && rowt[r] != ignore_index)
+        w[u] = load_stream(static_cast<const char*>(zsaved) +
+                           (row * ld_z + col) * (ZBF16 ? 2 : 4));
+    }
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint4 w = load_stream(p + 8 * h);
-            const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+    for (int u = 0; u < NU; ++u) {
+      const int r = tid / CPR + RPS * u;
+      const int64_t row = r0 + r;
+      const int64_t t = rowt[r];
+      const bool live = row < n && t != ignore_index;
+      float zv[E];
+      const uint32_t q[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      if constexpr (ZBF16) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              zv[8 * h + 2 * e] = bf16_lo(q[e]);
-              zv[8 * h + 2 * e + 1] = bf16_hi(q[e]);
-            }
-          }
-        } else {
-          const float* p = static_cast<const float*>(zsaved) + row * ld_z + col;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const uint4 w = load_stream(p + 4 * h);
-            zv[4 * h] = __uint_as_float(w.x);
-            zv[4 * h + 1] = __uint_as_float(w.y);
-            zv[4 * h + 2] = __uint_as_float(w.z);
-            zv[4 * h + 3] = __uint_as_float(w.w);
-          }
+        for (int e = 0; e < 4; ++e) {
+          zv[2 * e] = bf16_lo(q[e]);
+          zv[2 * e + 1] = bf16_hi(q[e]);
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (col + u < v)
-            zv[u] = ZBF16 ? bf16_lo(static_cast<const uint16_t*>(zsaved)[row * ld_z + col + u])
-                          : static_cast<const float*>(zsaved)[row * ld_z + col + u];
+        for (int e = 0; e < 4; ++e) zv[e] = __uint_as_float(q[e]);
       }
-    }
-    uint32_t packed[8];
+      if (live && !whole) {  // the row's last, partial chunk: element loads
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t b[2];
+        for (int e = 0; e < E; ++e)
+          zv[e] = col + e < v
+                      ? (ZBF16 ? bf16_lo(static_cast<const uint16_t*>(zsaved)[row * ld_z + col + e])
+                               : static_cast<const float*>(zsaved)[row * ld_z + col + e])
+                      : 0.0f;
+      }
+      const float L = rowc[r][0], G = rowc[r][1], H = rowc[r][2], NGH = rowc[r][3];
+      uint16_t b[E];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int u = 2 * e + k;
-        const float d = live && col + u < v
-                            ? dz_value(zv[u], L, G, H, NGH, col + u == t, inv_t, scaled,
+      for (int e = 0; e < E; ++e) {
+        const float d = live && col + e < v
+                            ? dz_value(zv[e], L, G, H, NGH, col + e == t, inv_t, scaled,
                                        with_ent, round_bf16)
                             : 0.0f;
-        b[k] = bf16_bits(d);
-        tile[r][cs + u] = b[k];
+        b[e] = bf16_bits(d);
       }
-      packed[e] = static_cast<uint32_t>(b[0]) | (static_cast<uint32_t>(b[1]) << 16);
+      if constexpr (ZBF16) {
+        *reinterpret_cast<uint4*>(&tile[r][ch]) =
+            make_uint4(b[0] | (uint32_t(b[1]) << 16), b[2] | (uint32_t(b[3]) << 16),
+                       b[4] | (uint32_t(b[5]) << 16), b[6] | (uint32_t(b[7]) << 16));
+      } else {
+        *reinterpret_cast<uint2*>(&tile[r][ch]) =
+            make_uint2(b[0] | (uint32_t(b[1]) << 16), b[2] | (uint32_t(b[3]) << 16));
+      }
     }
-    uint16_t* o = dz + gemm::kblocked_index(row, col, vp_cols / gemm::kK);
-    store_stream(o, make_uint4(packed[0], packed[1], packed[2], packed[3]));
-    store_stream(o + 8, make_uint4(packed[4], packed[5], packed[6], packed[7]));
     __syncthreads();
-    {
-      const int c = tid / 4, rs = (tid % 4) * 16;
-      uint32_t w[8];
+    if (dz) {
+      // along the rows: pieces (16-row block rb, K step ks) of the tile
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        w[e] = static_cast<uint32_t>(tile[rs + 2 * e][c]) |
-               (static_cast<uint32_t>(tile[rs + 2 * e + 1][c]) << 16);
-      uint16_t* q = dzt + gemm::kblocked_index(c0 + c, r0 + rs, np_rows / gemm::kK);
-      store_stream(q, make_uint4(w[0], w[1], w[2], w[3]));
-      store_stream(q + 8, make_uint4(w[4], w[5], w[6], w[7]));
+      for (int u = 0; u < 4; ++u) {
+        const int q = tid + 256 * u;
+        const int p = q >> 6, e = q & 63;
+        const int rb = p >> 3, ks = p & 7;
+        const int r = rb * 16 + (e >> 2), c = ks * 32 + (e & 3) * 8;
+        store_stream(dz + gemm::kblocked_index(r0 + r, cl0 + c, vc_steps),
+                     *reinterpret_cast<const uint4*>(&tile[r][c]));
+      }
     }
+    if (dzt) store_transposed(tile, dzt, cl0, kTC, r0, np_steps, tid);
     __syncthreads();
   }
 }
 
 // C[m_out, n_out] = A[., K] B[., K]^T on the mfma_gemm.h tile, both operands
-// K32-blocked; BF16OUT rounds the fp32 accumulators to bf16 (RNE) on the way
-// out.
+// K32-blocked (lda / ldb: elements between 16-row blocks, so A and B may be a
+// K range of a wider operand); the accumulators start from Cin (fp32,
+// [m_out, ldcin]) when it is set, else from zero, and continue its K walk.
+// BF16OUT rounds the fp32 accumulators to bf16 (RNE) on the way out.
 template <bool BF16OUT>
 __global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t arows, const uint16_t* __restrict__ B,
     int64_t ldb, int64_t brows, int ksteps, int mblocks, int nblocks, int64_t m_out,
-    int64_t n_out, void* __restrict__ C, int64_t ldc) {
+    int64_t n_out, const float* Cin, int64_t ldcin, void* C, int64_t ldc) {
   __shared__ __align__(16) gemm::Stages st;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -414,6 +481,20 @@ __global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (Cin) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = m0 + wm * 128 + i * 16 + 4 * g + q;
+        if (row >= m_out) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = n0 + wn * 64 + j * 16 + li;
+          if (col < n_out) acc[i][j][q] = Cin[row * ldcin + col];
+        }
+      }
+  }
   gemm::mainloop<true, true>(st, A, lda, m0, arows, B, ldb, n0, brows, ksteps, acc);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -450,42 +531,73 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(void* C, int64_t ldc, in
 
 int64_t round_tile(int64_t x) { return (x + kT - 1) / kT * kT; }
 
-// grid rows of a transpose over rows_p (grid-stride beyond 65535 blocks)
-unsigned tgrid(int64_t rows_p) {
-  const int64_t b = rows_p / 64;
-  return static_cast<unsigned>(b < 65535 ? b : 65535);
+// grid of a tile walk over rows_p rows in kTR-row tiles (grid-stride beyond
+// 65535 row tiles) and cols columns in kTC-column tiles
+dim3 tile_grid(int64_t rows_p, int64_t cols) {
+  const int64_t rt = rows_p / kTR;
+  return dim3(static_cast<unsigned>((cols + kTC - 1) / kTC),
+              static_cast<unsigned>(rt < 65535 ? rt : 65535));
 }
 
-// C = A B^T, A [arows, k] and B [brows, k] K32-blocked.
-void launch_gemm(bool bf16, const uint16_t* A, int64_t arows, const uint16_t* B, int64_t brows,
-                 int64_t k, int64_t m_out, int64_t n_out, void* C, int64_t ldc, hipStream_t s) {
+// dst = the K32-blocked [cols, K = rows_p] transpose of src [rows, ld]
+// (rows past `rows` zero).
+void launch_transpose(const uint16_t* src, int64_t ld, int64_t rows, int64_t rows_p,
+                      int64_t cols, uint16_t* dst, hipStream_t s) {
+  hipLaunchKernelGGL(transpose_blocked, tile_grid(rows_p, cols), dim3(256), 0, s, src, ld, rows,
+                     rows_p, cols, dst);
+}
+
+// C = A B^T (+ Cin), A [arows, k] and B [brows, k] K32-blocked with 16-row
+// block strides lda, ldb (elements).
+void launch_gemm(bool bf16, const uint16_t* A, int64_t lda, int64_t arows, const uint16_t* B,
+                 int64_t ldb, int64_t brows, int64_t k, int64_t m_out, int64_t n_out,
+                 const float* cin, int64_t ldcin, void* C, int64_t ldc, hipStream_t s) {
   const int mblocks = static_cast<int>((m_out + kT - 1) / kT);
   const int nblocks = static_cast<int>((n_out + kT - 1) / kT);
   const int ksteps = static_cast<int>(k / gemm::kK);
   if (bf16)
     hipLaunchKernelGGL(gemm_out_kernel<true>, dim3(mblocks * nblocks), dim3(gemm::kThreads), 0, s,
-                       A, int64_t{0}, arows, B, int64_t{0}, brows, ksteps, mblocks, nblocks,
-                       m_out, n_out, C, ldc);
+                       A, lda, arows, B, ldb, brows, ksteps, mblocks, nblocks, m_out, n_out, cin,
+                       ldcin, C, ldc);
   else
     hipLaunchKernelGGL(gemm_out_kernel<false>, dim3(mblocks * nblocks), dim3(gemm::kThreads), 0,
-                       s, A, int64_t{0}, arows, B, int64_t{0}, brows, ksteps, mblocks, nblocks,
-                       m_out, n_out, C, ldc);
+                       s, A, lda, arows, B, ldb, brows, ksteps, mblocks, nblocks, m_out, n_out, cin,
+                       ldcin, C, ldc);
 }
 
 }  // namespace
 
-LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v) {
-  const int64_t np = round_tile(n), vp = round_tile(v);
-  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+int64_t linear_bwd_chunk(int64_t v, int64_t vocab_chunk) {
+  const int64_t vp = round_tile(v);
+  const int64_t c = vocab_chunk > 0 ? round_tile(vocab_chunk) : kDefaultChunk;
+  return c < vp ? c : vp;
+}
+
+LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v, int32_t flags,
+                                  int64_t vocab_chunk) {
+  const bool need_dh = flags & kBwdDhidden, need_dw = flags & kBwdDweight;
+  const bool prepared = flags & kBwdPrepared, saved = flags & kBwdSaved;
   LinearBwdLayout l;
-  l.np = np;
-  l.vp = vp;
-  l.wt = 0;
-  l.ht = l.wt + up(h * vp * 2);
-  l.dz = l.ht + up(h * np * 2);
-  l.dzt = l.dz + up(np * vp * 2);
-  l.hb = l.dzt + up(vp * np * 2);
-  l.total = l.hb + up(np * h * 2);
+  l.np = round_tile(n);
+  l.vp = round_tile(v);
+  l.vc = linear_bwd_chunk(v, vocab_chunk);
+  const int64_t nchunks = (l.vp + l.vc - 1) / l.vc;
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  int64_t off = 0;
+  auto take = [&](bool use, int64_t bytes) {
+    if (!use) return int64_t{-1};
+    const int64_t at = off;
+    off += up(bytes);
+    return at;
+  };
+  l.hb = take(!saved, l.np * h * 2);                      // blocked h for the recompute
+  l.ht = take(need_dw, h * l.np * 2);                     // h^T for dW
+  l.dz = take(need_dh, l.np * l.vc * 2);                  // dz_c for dh
+  l.dzt = take(need_dw, l.vc * l.np * 2);                 // dz_c^T for dW
+  l.wt = take(need_dh && !prepared, h * l.vc * 2);        // W^T_c for dh
+  l.dh32 = take(need_dh && (flags & kBwdBf16Out) && nchunks > 1,
+                n * h * 4);                               // fp32 dh between chunks
+  l.total = off;
   return l;
 }
 
@@ -495,7 +607,7 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
                        const uint16_t* prepared, const float* lse,
                        const float* grad, float inv_t, int32_t round_bf16, const float* ent,
                        const float* gent, bool bf16_out, void* dh, int64_t ld_dh, void* dw,
-                       int64_t ld_dw, char* ws, hipStream_t s) {
+                       int64_t ld_dw, int64_t vocab_chunk, char* ws, hipStream_t s) {
   if (n == 0) {
     // dh has no rows; dW is a sum over no tokens.
     if (dw) {
@@ -508,54 +620,85 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
     }
     return;
   }
-  const LinearBwdLayout l = linear_bwd_layout(n, h, v);
-  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + l.wt);
-  uint16_t* ht = reinterpret_cast<uint16_t*>(ws + l.ht);
-  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + l.dz);
-  uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + l.dzt);
-  uint16_t* hb = reinterpret_cast<uint16_t*>(ws + l.hb);
+  const int32_t flags = (dh ? kBwdDhidden : 0) | (dw ? kBwdDweight : 0) |
+                        (prepared ? kBwdPrepared : 0) | (zsaved ? kBwdSaved : 0) |
+                        (bf16_out ? kBwdBf16Out : 0);
+  const LinearBwdLayout l = linear_bwd_layout(n, h, v, flags, vocab_chunk);
+  auto at = [&](int64_t off) { return off < 0 ? nullptr : reinterpret_cast<uint16_t*>(ws + off); };
+  uint16_t* hb = at(l.hb);
+  uint16_t* ht = at(l.ht);
+  uint16_t* dz = at(l.dz);
+  uint16_t* dzt = at(l.dzt);
+  uint16_t* wt = at(l.wt);
+  float* dh32 = l.dh32 < 0 ? nullptr : reinterpret_cast<float*>(ws + l.dh32);
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
-  if (!zsaved) {
-    launch_block_rows(hidden, ld_h, n, l.np, h, hb, s);
-    const bool plain = inv_t == 1.0f && !ent && !round_bf16;
-    const uint16_t* wop = prepared ? prepared_blocked_w(prepared) : weight;
-    const int64_t ldw = prepared ? int64_t{0} : ld_w;
-#define ITL_DZ(WB, PL)                                                                           \
-  hipLaunchKernelGGL((linear_dz_kernel<WB, PL>), dim3(mblocks * vblocks), dim3(gemm::kThreads), \
-                     0, s, hb, ld_h, wop, ldw, n, h, v, mblocks, vblocks, targets.p,            \
+  const int64_t hsteps = h / gemm::kK, npsteps = l.np / gemm::kK, vpsteps = l.vp / gemm::kK;
+  const bool plain = inv_t == 1.0f && !ent && !round_bf16;
+  const uint16_t* wop = prepared ? prepared_blocked_w(prepared) : weight;
+  const int64_t ldw = prepared ? int64_t{0} : ld_w;
+  if (!zsaved) launch_block_rows(hidden, ld_h, n, l.np, h, hb, s);
+  if (dw) launch_transpose(hidden, ld_h, n, l.np, h, ht, s);
+  for (int64_t c0 = 0; c0 < l.vp; c0 += l.vc) {
+    const int64_t c1 = c0 + l.vc < l.vp ? c0 + l.vc : l.vp;
+    const int64_t cols = c1 - c0, csteps = cols / gemm::kK;
+    const int vb0 = static_cast<int>(c0 / kT), vcb = static_cast<int>(cols / kT);
+    const bool first = c0 == 0, last = c1 == l.vp;
+    // dz_c and dz_c^T of the chunk's columns
+    if (!zsaved) {
+#define ITL_DZ(WB, PL)                                                                            \
+  hipLaunchKernelGGL((linear_dz_kernel<WB, PL>), dim3(mblocks * vcb), dim3(gemm::kThreads), 0,   \
+                     s, hb, ld_h, wop, ldw, n, h, v, mblocks, vblocks, vb0, vcb, targets.p,      \
                      targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, dzt)
-    if (prepared) {
-      if (plain) ITL_DZ(true, true); else ITL_DZ(true, false);
-    } else {
-      if (plain) ITL_DZ(false, true); else ITL_DZ(false, false);
-    }
+      if (prepared) {
+        if (plain) ITL_DZ(true, true); else ITL_DZ(true, false);
+      } else {
+        if (plain) ITL_DZ(false, true); else ITL_DZ(false, false);
+      }
 #undef ITL_DZ
-  } else {
-    const int64_t rb = l.np / kST;
-    const dim3 grid(static_cast<unsigned>(l.vp / kST), static_cast<unsigned>(rb < 65535 ? rb : 65535));
-    if (z_bf16)
-      hipLaunchKernelGGL(linear_dz_saved_kernel<true>, grid, dim3(256), 0, s, zsaved, ld_z, n, v,
-                         l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16, ent,
-                         gent, l.vp, dz, dzt);
-    else
-      hipLaunchKernelGGL(linear_dz_saved_kernel<false>, grid, dim3(256), 0, s, zsaved, ld_z, n,
-                         v, l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
-                         ent, gent, l.vp, dz, dzt);
+    } else {
+      const int64_t ct = cols / kTC;
+      const dim3 grid(static_cast<unsigned>(l.np / kTR), static_cast<unsigned>(ct < 65535 ? ct : 65535));
+      if (z_bf16)
+        hipLaunchKernelGGL(linear_dz_saved_kernel<true>, grid, dim3(256), 0, s, zsaved, ld_z, n, v,
+                           l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
+                           ent, gent, c0, cols, dz, dzt);
+      else
+        hipLaunchKernelGGL(linear_dz_saved_kernel<false>, grid, dim3(256), 0, s, zsaved, ld_z, n,
+                           v, l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
+                           ent, gent, c0, cols, dz, dzt);
+    }
+    // dW[c0, c1) = dz_c^T h: K = every token, ascending (final rows)
+    if (dw && c0 < v) {
+      const int64_t rows = (c1 < v ? c1 : v) - c0;
+      launch_gemm(bf16_out, dzt, npsteps * 512, cols, ht, npsteps * 512, h, l.np, rows, h,
+                  nullptr, 0,
+                  static_cast<char*>(dw) + c0 * ld_dw * (bf16_out ? 2 : 4), ld_dw, s);
+    }
+    // dh += dz_c W[c0, c1): K = the chunk's vocabulary, continuing the fp32
+    // accumulators of the previous chunks (in dh itself for fp32 output, in
+    // dh32 for bf16 output, rounded on the last chunk)
+    if (dh) {
+      const uint16_t* wtc;
+      int64_t ldwt;
+      if (prepared) {  // the prepared W^T [h, Vp]: columns [c0, c1)
+        wtc = prepared_blocked_wt(prepared, v, h) + (c0 / gemm::kK) * 512;
+        ldwt = vpsteps * 512;
+      } else {  // W[c0, c1) transposed into the workspace
+        const int64_t rows = c0 < v ? (c1 < v ? c1 : v) - c0 : 0;
+        launch_transpose(weight + c0 * ld_w, ld_w, rows, cols, h, wt, s);
+        wtc = wt;
+        ldwt = csteps * 512;
+      }
+      const float* cin = first ? nullptr : (dh32 ? dh32 : static_cast<const float*>(dh));
+      const int64_t ldcin = dh32 ? h : ld_dh;
+      const bool out_bf16 = bf16_out && last;
+      void* cout = bf16_out && !last ? static_cast<void*>(dh32) : dh;
+      const int64_t ldc = bf16_out && !last ? h : ld_dh;
+      launch_gemm(out_bf16, dz, csteps * 512, l.np, wtc, ldwt, h, cols, n, h, cin, ldcin, cout,
+                  ldc, s);
+    }
   }
-  if (dh) {
-    // W^T: the caller's prepared copy (linear_logp_prepare_weight, the same
-    // values) or made here
-    const uint16_t* wtb = prepared ? prepared_blocked_wt(prepared, v, h) : wt;
-    if (!prepared)
-      hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.vp)),
-                         dim3(256), 0, s, weight, ld_w, v, l.vp, wt);
-    launch_gemm(bf16_out, dz, l.np, wtb, h, l.vp, n, h, dh, ld_dh, s);
-  }
-  if (dw) {
-    hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(l.np)),
-                       dim3(256), 0, s, hidden, ld_h, n, l.np, ht);
-    launch_gemm(bf16_out, dzt, l.vp, ht, h, l.np, v, h, dw, ld_dw, s);
-  }
+  (void)hsteps;
 }
 
 int64_t prepared_bytes(int64_t v, int64_t h) { return 2 * h * round_tile(v) * 2; }
@@ -568,8 +711,7 @@ void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int6
                            uint16_t* prepared, hipStream_t s) {
   const int64_t vp = round_tile(v);
   launch_block_rows(weight, ld_w, v, vp, h, prepared, s);
-  hipLaunchKernelGGL(transpose_block_bf16, dim3(static_cast<unsigned>(h / 64), tgrid(vp)),
-                     dim3(256), 0, s, weight, ld_w, v, vp, prepared + h * vp);
+  launch_transpose(weight, ld_w, v, vp, h, prepared + h * vp, s);
 }
 
 void launch_block_rows(const uint16_t* src, int64_t ld, int64_t rows, int64_t rows_p, int64_t k,

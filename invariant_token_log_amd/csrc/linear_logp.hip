@@ -401,9 +401,11 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  gemm::mainloop<true, WBLK>(sm.st, hidden, 0, m0, static_cast<int64_t>(mblocks) * 256, weight,
-                             ld_w, v0, WBLK ? static_cast<int64_t>(vblocks) * BN : v,
-                             static_cast<int>(hdim / BK), acc);
+  const int ksteps = static_cast<int>(hdim / BK);
+  const int64_t kblk = static_cast<int64_t>(ksteps) * 512;  // blocked: 16-row block stride
+  gemm::mainloop<true, WBLK>(sm.st, hidden, kblk, m0, static_cast<int64_t>(mblocks) * 256, weight,
+                             WBLK ? kblk : ld_w, v0, WBLK ? static_cast<int64_t>(vblocks) * BN : v,
+                             ksteps, acc);
   __syncthreads();
   stats_epilogue<8, 4, 256, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * 128, wn * 64, li,
                                                         g, tid, m0, v0, vb,
@@ -449,9 +451,10 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  gemm::mainloop_narrow<ROWS, WBLK>(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0,
-                                    WBLK ? static_cast<int64_t>(vblocks) * BN : v,
-                                    static_cast<int>(hdim / BK), acc);
+  const int ksteps = static_cast<int>(hdim / BK);
+  gemm::mainloop_narrow<ROWS, WBLK>(sm.st, hidden, ld_h, m0, n, weight,
+                                    WBLK ? static_cast<int64_t>(ksteps) * 512 : ld_w, v0,
+                                    WBLK ? static_cast<int64_t>(vblocks) * BN : v, ksteps, acc);
   __syncthreads();
   stats_epilogue<MI, 8, ROWS, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * (ROWS / 4),
                                                           wn * 128, li, g, tid,

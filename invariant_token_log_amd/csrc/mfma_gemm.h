@@ -23,7 +23,10 @@
 // (kblocked_index): the 16 rows x 32 K piece that one direct load
 // instruction fills is one contiguous KiB, element (r, k) at
 // ((r / 16) * ksteps + k / 32) * 512 + (r % 16) * 32 + k % 32, rows padded to
-// a multiple of 16 with zeros.  A blocked operand makes every load
+// a multiple of 16 with zeros; a product may read the K range [k0, k0 + K)
+// of a wider blocked operand by starting at its piece k0 / 32 and passing
+// ksteps * 512 (the operand's full width) as the distance between 16-row
+// blocks.  A blocked operand makes every load
 // instruction read eight whole 128-byte lines instead of sixteen half lines
 // (measured: 9% more MFMA throughput with both operands blocked).  The layout
 // moves bytes only, so the products have the same bits.
@@ -94,25 +97,26 @@ __device__ __forceinline__ void issue_step(Stages& sm, const uint16_t* a0, const
 }
 
 // This lane's chunk of 16-row block `blk` (counted from row0, a multiple of
-// 16) of an operand at K step 0.  Rows at or past `rows` are read from the
-// last valid row (row-major) or the last 16-row block (K32-blocked, whose
+// 16) of an operand at K step 0.  ld: elements between rows (row-major) or
+// between 16-row blocks (K32-blocked).  Rows at or past `rows` are read from
+// the last valid row (row-major) or the last 16-row block (K32-blocked, whose
 // rows are padded to a multiple of 16): every load stays in bounds, and those
 // rows only feed outputs the caller masks.
 template <bool BLOCKED>
 __device__ __forceinline__ const uint16_t* lane_chunk(const uint16_t* X, int64_t ld,
-                                                      int64_t row0, int64_t rows, int ksteps,
-                                                      int blk, int lrow, int lk) {
+                                                      int64_t row0, int64_t rows, int blk,
+                                                      int lrow, int lk) {
   if constexpr (BLOCKED)
-    return X + min(row0 / 16 + blk, (rows + 15) / 16 - 1) * (static_cast<int64_t>(ksteps) * 512) +
-           lrow * 32 + lk;
+    return X + min(row0 / 16 + blk, (rows + 15) / 16 - 1) * ld + lrow * 32 + lk;
   else
     return X + min(row0 + blk * 16 + lrow, rows - 1) * ld + lk;
 }
 
 // acc += A[a_row0 + 0..255, 0..K) * B[b_row0 + 0..255, 0..K)^T with K =
 // ksteps * 32 (ksteps even, >= 2); ABLK / BBLK: the operand is K32-blocked
-// with this ksteps (then its ld is not used).  All 512 threads must call; on return
-// every direct load has landed and the stages may be reused after a barrier.
+// and its lda / ldb is the distance between 16-row blocks in elements (512
+// times the operand's K steps).  All 512 threads must call; on return every
+// direct load has landed and the stages may be reused after a barrier.
 template <bool ABLK = false, bool BBLK = false>
 __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict__ A, int64_t lda,
                                          int64_t a_row0, int64_t a_rows,
@@ -127,10 +131,10 @@ __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict_
   const int li = lane % 16, g = lane / 16;
   const int lrow = lane / 4;
   const int lk = ((lane % 4) ^ swz(lrow)) * 8;
-  const uint16_t* a0 = lane_chunk<ABLK>(A, lda, a_row0, a_rows, ksteps, wave, lrow, lk);
-  const uint16_t* a1 = lane_chunk<ABLK>(A, lda, a_row0, a_rows, ksteps, wave + 8, lrow, lk);
-  const uint16_t* b0 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, ksteps, wave, lrow, lk);
-  const uint16_t* b1 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, ksteps, wave + 8, lrow, lk);
+  const uint16_t* a0 = lane_chunk<ABLK>(A, lda, a_row0, a_rows, wave, lrow, lk);
+  const uint16_t* a1 = lane_chunk<ABLK>(A, lda, a_row0, a_rows, wave + 8, lrow, lk);
+  const uint16_t* b0 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, wave, lrow, lk);
+  const uint16_t* b1 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, wave + 8, lrow, lk);
 
   // Fragment offsets (elements) inside a stage: row wm*128 + li (+16 i) of A,
   // row wn*64 + li (+16 j) of B, chunk g.
@@ -232,9 +236,10 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 // acc += A[a_row0 + 0..ROWS-1, 0..K) * B[b_row0 + 0..255, 0..K)^T, K =
 // ksteps * 32 (ksteps even, >= 2); A row-major, B row-major or K32-blocked
-// (BBLK); rows at or past a_rows / b_rows are read from the last valid row
-// (block).  All 512 threads must call; on return every direct load has landed
-// and the stages may be reused after a barrier.
+// (BBLK, ldb = distance between 16-row blocks); rows at or past a_rows /
+// b_rows are read from the last valid row (block).  All 512 threads must
+// call; on return every direct load has landed and the stages may be reused
+// after a barrier.
 template <int ROWS, bool BBLK = false>
 __device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
                                                 const uint16_t* __restrict__ A, int64_t lda,
@@ -253,8 +258,8 @@ __device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
   const int lk = ((lane % 4) ^ swz(lrow)) * 8;
   const bool has_a = wave < ROWS / 16;  // uniform
   const uint16_t* a0 = A + min(a_row0 + (has_a ? wave : 0) * 16 + lrow, a_rows - 1) * lda + lk;
-  const uint16_t* b0 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, ksteps, wave, lrow, lk);
-  const uint16_t* b1 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, ksteps, wave + 8, lrow, lk);
+  const uint16_t* b0 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, wave, lrow, lk);
+  const uint16_t* b1 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, wave + 8, lrow, lk);
   constexpr int SB = BBLK ? 512 : kK;
   const int aoff = (wm * (ROWS / 4) + li) * kK + ((g ^ swz(li)) * 8);
   const int boff = (wn * 128 + li) * kK + ((g ^ swz(li)) * 8);

@@ -185,6 +185,7 @@ def _linear_fwd(hidden, weight, targets, ignore_index, tile_width, logp_out, lse
                 workspace, temperature, return_entropy, entropy_out, return_logits,
                 logits_dtype, logits_out, round_logits, prepared_weight, noalloc):
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
+    pbuf = _prepared_buffer(prepared_weight, weight)
     t1 = _targets(targets, n)
     dev = hidden.device
     if logp_out is None:
@@ -203,7 +204,7 @@ def _linear_fwd(hidden, weight, targets, ignore_index, tile_width, logp_out, lse
                           or z.stride(1) != 1):
         raise ValueError("logits_out must be [N, V] of logits_dtype with contiguous rows")
     L = _lib.lib()
-    pw = _prepared(prepared_weight, L, v, h, dev)
+    pw = _prepared(pbuf, L, v, h, dev)
     args = (hidden.data_ptr(), ld_h, weight.data_ptr(), ld_w, n, h, v, t1.data_ptr(),
             _INDEX[t1.dtype], int(ignore_index), int(tile_width), float(temperature),
             _rounding(round_logits), logp_out.data_ptr(), lse_out.data_ptr(), _ptr(ent), _ptr(z),
@@ -227,11 +228,25 @@ def _linear_fwd(hidden, weight, targets, ignore_index, tile_width, logp_out, lse
     return out
 
 
+def linear_logp_bwd_workspace_bytes(n, h, v, need_dhidden=True, need_dweight=True,
+                                    prepared=False, saved_logits=False,
+                                    out_dtype=torch.float32, vocab_chunk=0,
+                                    tile_width=LINEAR_TILE):
+    """Workspace bytes linear_logp_bwd needs for a call with these options."""
+    flags = ((_lib.LOGP_BWD_DHIDDEN if need_dhidden else 0)
+             | (_lib.LOGP_BWD_DWEIGHT if need_dweight else 0)
+             | (_lib.LOGP_BWD_PREPARED if prepared else 0)
+             | (_lib.LOGP_BWD_SAVED_LOGITS if saved_logits else 0)
+             | (_lib.LOGP_BWD_BF16_OUT if out_dtype == torch.bfloat16 else 0))
+    return _lib.lib().linear_logp_bwd_workspace_bytes(n, h, v, tile_width, flags, vocab_chunk)
+
+
 def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                     tile_width=LINEAR_TILE, need_dhidden=True, need_dweight=True,
                     out_dtype=torch.float32, dhidden_out=None, dweight_out=None,
                     workspace=None, temperature=1.0, entropy=None, grad_entropy=None,
-                    round_logits=False, saved_logits=None, prepared_weight=None):
+                    round_logits=False, saved_logits=None, prepared_weight=None,
+                    vocab_chunk=0):
     """Backward of the fused LM head + logp: (dhidden [N, H] or None,
     dweight [V, H] or None) in out_dtype (float32 accumulators or their
     bfloat16 rounding), from the forward's lse (and entropy) and the upstream
@@ -239,8 +254,11 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
     saved_logits: the forward's logits output ([N, V] float32, or bfloat16
     with round_logits), read instead of recomputing h W^T; same bits.
     prepared_weight: prepare_weight(weight), read instead of the weight and
-    its transpose made on every call; same bits."""
+    its transpose made on every call; same bits.  vocab_chunk: vocabulary
+    columns per pass (0 = the library's default); any value gives the same
+    bits, smaller ones need less workspace."""
     n, h, v, ld_h, ld_w = _linear_operands(hidden, weight)
+    pbuf = _prepared_buffer(prepared_weight, weight)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
     t1 = _targets(targets, n)
@@ -266,8 +284,10 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                           or z.dtype not in (torch.float32, torch.bfloat16)):
         raise ValueError("saved_logits must be [N, V] float32 / bfloat16 with contiguous rows")
     L = _lib.lib()
-    pw = _prepared(prepared_weight, L, v, h, dev)
-    need = L.linear_logp_bwd_workspace_bytes(n, h, v, tile_width)
+    pw = _prepared(pbuf, L, v, h, dev)
+    need = linear_logp_bwd_workspace_bytes(n, h, v, dh is not None, dw is not None,
+                                           pw is not None, z is not None, out_dtype,
+                                           int(vocab_chunk), tile_width)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_len = workspace.numel() if workspace is not None else 0
@@ -282,7 +302,7 @@ def linear_logp_bwd(hidden, weight, targets, lse, grad_logp, ignore_index=-100,
                                _ptr(gent), _DTYPES[out_dtype], _ptr(dh),
                                (dh.stride(0) if n > 1 else h) if dh is not None else 0,
                                _ptr(dw), (dw.stride(0) if v > 1 else h) if dw is not None else 0,
-                               _ptr(workspace), ws_len, _stream(dev))
+                               int(vocab_chunk), _ptr(workspace), ws_len, _stream(dev))
     check("linear_logp_bwd", st)
     return dh, dw
 
@@ -291,22 +311,61 @@ def _nbytes(t):
     return t.numel() * t.element_size() if t is not None else 0
 
 
-def _prepared(p, L, v, h, dev):
-    if p is not None and (not p.is_contiguous() or p.device != dev
-                          or _nbytes(p) < L.linear_logp_prepared_bytes(v, h)):
-        raise ValueError("prepared_weight must be prepare_weight(weight) on the weight's device")
-    return p
+class PreparedWeight:
+    """What prepare_weight returns: `buffer`, the weight re-laid for the fused
+    products (uint8 device tensor), and the identity of the weight it was made
+    from (data pointer, shape, device and in-place version counter).  Every
+    use checks that identity, so a weight that was updated in place (an
+    optimiser step) or replaced is refused instead of giving wrong results."""
+
+    __slots__ = ("buffer", "weight_ptr", "shape", "device", "version")
+
+    def __init__(self, buffer, weight):
+        self.buffer = buffer
+        self.weight_ptr = weight.data_ptr()
+        self.shape = tuple(weight.shape)
+        self.device = weight.device
+        self.version = weight._version
+
+    def check(self, weight):
+        """Raise ValueError unless `weight` is the tensor this was prepared
+        from, unchanged since."""
+        if (weight.data_ptr() != self.weight_ptr or tuple(weight.shape) != self.shape
+                or weight.device != self.device):
+            raise ValueError("prepared_weight was prepared from another weight tensor; "
+                             "call prepare_weight(weight) for this one")
+        if weight._version != self.version:
+            raise ValueError("prepared_weight is stale: the weight changed in place after "
+                             "prepare_weight; prepare it again")
+
+
+def _prepared_buffer(p, weight):
+    """The prepared buffer for `weight`, after the identity check (before any
+    device work)."""
+    if p is None:
+        return None
+    if not isinstance(p, PreparedWeight):
+        raise TypeError("prepared_weight must be the result of prepare_weight(weight)")
+    p.check(weight)
+    return p.buffer
+
+
+def _prepared(buf, L, v, h, dev):
+    if buf is not None and (not buf.is_contiguous() or buf.device != dev
+                            or _nbytes(buf) < L.linear_logp_prepared_bytes(v, h)):
+        raise ValueError("prepared_weight's buffer is too small or not on the weight's device")
+    return buf
 
 
 def prepare_weight(weight, out=None):
     """The LM-head weight [V, H] bfloat16 re-laid for the fused products'
     loads (the weight and its transpose, vocabulary padded with zeros to a
-    multiple of 256, in the library's own layout): a uint8 buffer of
-    linear_logp_prepared_bytes(V, H) bytes (or `out`, a contiguous buffer at
-    least that large) for linear_logp_fwd / linear_logp_bwd.  Reuse it over
-    the calls of one weight version and prepare it again after the weight
-    changes (an optimiser step, a weight update): a stale one gives wrong
-    results."""
+    multiple of 256, in the library's own layout), as a PreparedWeight whose
+    `buffer` is a uint8 tensor of linear_logp_prepared_bytes(V, H) bytes (or
+    `out`, a contiguous buffer at least that large), for linear_logp_fwd,
+    linear_logp_bwd and linear_logp.  Reuse it over the calls of one weight
+    version; after the weight changes (an optimiser step, a weight update)
+    every use raises until it is prepared again."""
     if weight.dtype != torch.bfloat16 or weight.dim() != 2 or weight.stride(1) != 1:
         raise ValueError("weight must be [V, H] bfloat16 with contiguous rows")
     v, h = weight.shape
@@ -325,7 +384,7 @@ def prepare_weight(weight, out=None):
                                           v, h, out.data_ptr(), out.numel() * out.element_size(),
                                           _stream(weight.device))
     check("linear_logp_prepare_weight", st)
-    return out
+    return PreparedWeight(out, weight)
 
 
 def _grad_or_zeros(g, ref):
@@ -402,6 +461,8 @@ class _LinearLogp(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad, *rest):
         hidden, weight, targets, lse, ent, z = ctx.saved_tensors
+        if ctx.prepared_weight is not None:
+            ctx.prepared_weight.check(weight)
         g = _grad_or_zeros(grad, lse)
         gent = _grad_or_zeros(rest[0], lse) if ctx.with_entropy else None
         dh, dw = linear_logp_bwd(hidden, weight, targets, lse, g, ctx.ignore_index,

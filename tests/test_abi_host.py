@@ -156,13 +156,14 @@ def test_linear_bwd_argument_errors(L):
         a = dict(h_ptr=FAKE, ld_h=4096, w_ptr=FAKE, ld_w=4096, n=8, h=4096, v=151936,
                  targets=FAKE, tdt=0, tile=256, temp=1.0, rnd=0, z=None, zdt=0, ldz=0,
                  wt=None, ldwt=0, lse=FAKE, g=FAKE, ent=None, gent=None, out=0, dh=FAKE,
-                 ld_dh=4096, dw=FAKE, ld_dw=4096, ws=FAKE, ws_bytes=1 << 40)
+                 ld_dh=4096, dw=FAKE, ld_dw=4096, vc=0, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return L.linear_logp_bwd(a["h_ptr"], a["ld_h"], a["w_ptr"], a["ld_w"], a["n"], a["h"],
                                  a["v"], a["targets"], a["tdt"], -100, a["tile"], a["temp"],
                                  a["rnd"], a["z"], a["zdt"], a["ldz"], a["wt"], a["ldwt"],
                                  a["lse"], a["g"], a["ent"], a["gent"], a["out"], a["dh"],
-                                 a["ld_dh"], a["dw"], a["ld_dw"], a["ws"], a["ws_bytes"], None)
+                                 a["ld_dh"], a["dw"], a["ld_dw"], a["vc"], a["ws"],
+                                 a["ws_bytes"], None)
     assert lb(temp=0.0) == _lib.LOGP_ERR_VALUE
     assert lb(rnd=3) == _lib.LOGP_ERR_VALUE
     # saved logits: fp32, or bf16 only in the bf16-rounded contract
@@ -191,14 +192,47 @@ def test_linear_bwd_argument_errors(L):
     assert lb(ws_bytes=16) == _lib.LOGP_ERR_WORKSPACE
     assert lb(ws=FAKE + 16) == _lib.LOGP_ERR_WORKSPACE
     assert lb(n=0, h_ptr=None, targets=None, lse=None, g=None, dw=None) == _lib.LOGP_OK
-    # workspace: W^T, h^T, dz, dz^T and the re-laid hidden in bf16 with
-    # 256-padded n and v
-    np_, vp = 256, 152064
-    need = L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 256)
-    assert need == 2 * (4096 * vp + 4096 * np_ + 2 * np_ * vp + np_ * 4096)
-    assert L.linear_logp_bwd_workspace_bytes(0, 4096, 151936, 256) == 0
-    assert L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 4096) == 0
-    assert L.linear_logp_bwd_workspace_bytes(8, 100, 151936, 256) == 0
+    assert lb(vc=-1) == _lib.LOGP_ERR_SHAPE
+    # the workspace is checked against this call's own options: dh only,
+    # fp32 out, no prepared weight needs blocked h + dz_c + W^T_c
+    only_dh = L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 256, _lib.LOGP_BWD_DHIDDEN, 0)
+    both = L.linear_logp_bwd_workspace_bytes(8, 4096, 151936, 256,
+                                             _lib.LOGP_BWD_DHIDDEN | _lib.LOGP_BWD_DWEIGHT, 0)
+    assert only_dh < both
+    assert lb(dw=None, ws_bytes=only_dh - 1) == _lib.LOGP_ERR_WORKSPACE
+    assert lb(ws_bytes=both - 1) == _lib.LOGP_ERR_WORKSPACE
+
+
+def test_linear_bwd_workspace_sizes(L):
+    """Regions in use only: blocked h (recompute), h^T (dW), dz_c (dh), dz_c^T
+    (dW), W^T_c (dh without a prepared weight), fp32 dh between chunks (bf16
+    dh over several chunks); bf16 unless noted, Np = round_up(n, 256), chunk
+    C = min(round_up(vocab_chunk or 32768, 256), Vp)."""
+    B = _lib
+    n, h, v = 8, 4096, 151936
+    np_, vp, c = 256, 152064, 32768
+
+    def ws(flags, vc=0, nn=n):
+        return L.linear_logp_bwd_workspace_bytes(nn, h, v, 256, flags, vc)
+
+    both = B.LOGP_BWD_DHIDDEN | B.LOGP_BWD_DWEIGHT
+    assert ws(both) == 2 * (np_ * h + h * np_ + np_ * c + c * np_ + h * c)
+    assert ws(both | B.LOGP_BWD_PREPARED) == 2 * (np_ * h + h * np_ + np_ * c + c * np_)
+    assert ws(both | B.LOGP_BWD_SAVED_LOGITS) == 2 * (h * np_ + np_ * c + c * np_ + h * c)
+    assert ws(B.LOGP_BWD_DHIDDEN) == 2 * (np_ * h + np_ * c + h * c)
+    assert ws(B.LOGP_BWD_DWEIGHT) == 2 * (np_ * h + h * np_ + c * np_)
+    assert ws(both | B.LOGP_BWD_BF16_OUT) == ws(both) + n * h * 4  # fp32 dh between chunks
+    assert ws(both, vc=1000) == 2 * (np_ * h + h * np_ + np_ * 1024 + 1024 * np_ + h * 1024)
+    # one chunk over the whole vocabulary: no fp32 dh staging for bf16 output
+    one = ws(both, vc=v)
+    assert one == 2 * (np_ * h + h * np_ + np_ * vp + vp * np_ + h * vp)
+    assert ws(both | B.LOGP_BWD_BF16_OUT, vc=v) == one
+    # the benchmarked head: N = H = 4096 with both outputs stays under 1 GB
+    assert L.linear_logp_bwd_workspace_bytes(4096, 4096, v, 256, both, 0) < 1 << 30
+    assert ws(both, nn=0) == 0
+    assert L.linear_logp_bwd_workspace_bytes(8, 4096, v, 4096, both, 0) == 0
+    assert L.linear_logp_bwd_workspace_bytes(8, 100, v, 256, both, 0) == 0
+    assert ws(both, vc=-5) == 0
 
 
 def test_prepare_weight_argument_errors(L):
@@ -238,7 +272,7 @@ def test_temperature_bounds(L):
         assert lin(ok, h_ptr=None) == _lib.LOGP_ERR_NULL, ok
     lb = L.linear_logp_bwd(FAKE, 4096, FAKE, 4096, 8, 4096, 151936, FAKE, 0, -100, 256, 1e-39,
                            0, None, 0, 0, None, 0, FAKE, FAKE, None, None, 0, FAKE, 4096, FAKE,
-                           4096, FAKE, 1 << 40, None)
+                           4096, 0, FAKE, 1 << 40, None)
     assert lb == _lib.LOGP_ERR_VALUE
 
 

@@ -268,8 +268,8 @@ def test_prepared_weight_same_bits(n, hd, v):
     need = itl.lib().linear_logp_prepared_bytes(v, hd)
     assert need == 2 * hd * vp * 2
     pw = itl.prepare_weight(w)
-    assert pw.dtype == torch.uint8 and pw.numel() == need
-    got = pw.view(torch.int16).cpu().numpy().astype(np.uint16)
+    assert pw.buffer.dtype == torch.uint8 and pw.buffer.numel() == need
+    got = pw.buffer.view(torch.int16).cpu().numpy().astype(np.uint16)
     wn = w.view(torch.int16).cpu().numpy().astype(np.uint16)
     assert np.array_equal(got[: hd * vp], _blocked(wn, vp, hd))
     wt = np.zeros((hd, vp), dtype=np.uint16)
@@ -277,7 +277,7 @@ def test_prepared_weight_same_bits(n, hd, v):
     assert np.array_equal(got[hd * vp:], _blocked(wt, hd, vp))
     big = torch.full((need + 4096,), 7, dtype=torch.uint8, device=dev())
     pw2 = itl.prepare_weight(w, out=big)
-    assert torch.equal(pw2[:need], pw) and bool((pw2[need:] == 7).all())
+    assert torch.equal(pw2.buffer[:need], pw.buffer) and bool((pw2.buffer[need:] == 7).all())
     for temp, with_ent in ((1.0, False), (0.7, True)):
         ref = itl.linear_logp_fwd(h, w, t, temperature=temp, return_entropy=with_ent,
                                   return_logits=True, logits_dtype=torch.float32)
@@ -294,14 +294,77 @@ def test_prepared_weight_same_bits(n, hd, v):
             dh1, dw1 = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype,
                                            prepared_weight=prep)
             assert torch.equal(dh0, dh1) and torch.equal(dw0, dw1)
+    short = itl.PreparedWeight(pw.buffer[: need - 256], w)
     with pytest.raises(ValueError):
-        itl.linear_logp_bwd(h, w, t, lse, g, prepared_weight=pw[: need - 256])
+        itl.linear_logp_bwd(h, w, t, lse, g, prepared_weight=short)
     with pytest.raises(ValueError):
-        itl.linear_logp_fwd(h, w, t, prepared_weight=pw[: need - 256])
+        itl.linear_logp_fwd(h, w, t, prepared_weight=short)
     grads = []
-    for prep in (None, pw):
+    for prepare in (False, True):
         hh = h.clone().requires_grad_(True)
         ww = w.clone().requires_grad_(True)
+        prep = itl.prepare_weight(ww) if prepare else None
         (itl.linear_logp(hh, ww, t, prepared_weight=prep) * g).sum().backward()
         grads.append((hh.grad, ww.grad))
     assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
+
+
+def _bits_any(x):
+    return x.view(torch.int32 if x.dtype == torch.float32 else torch.int16)
+
+
+@pytest.mark.parametrize("n,hd,v", [(300, 128, 1000), (64, 256, 4096), (257, 64, 5000)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_vocab_chunk_same_bits(n, hd, v, out_dtype):
+    """The vocabulary chunk changes the workspace, not a bit: dh and dW from
+    chunks of 256, 512 and 768 columns and the default equal those of one
+    chunk over the whole vocabulary, with the logits recomputed, read from a
+    prepared weight or from the forward's saved logits, with the options on
+    (temperature, entropy term, bf16-rounded logits), and with only one of
+    the two outputs requested."""
+    h, w, t, g = _case(n, hd, v, seed=5 * n + v)
+    vp = (v + 255) // 256 * 256
+    pw = itl.prepare_weight(w)
+    gh = synth.normal_matrix(1, n, 0.5, torch.float32, seed=n + 3)[0].to(dev())
+    cases = [dict(), dict(prepared_weight=pw)]
+    for temp, ent, rnd in ((1.0, False, False), (0.7, True, False), (1.3, False, True)):
+        _, lse, *rest = itl.linear_logp_fwd(h, w, t, temperature=temp, return_entropy=ent,
+                                            round_logits=rnd, return_logits=True,
+                                            logits_dtype=torch.bfloat16 if rnd else torch.float32)
+        ent_t = rest[0] if ent else None
+        z = rest[-1]
+        opts = dict(temperature=temp, round_logits=rnd, entropy=ent_t,
+                    grad_entropy=gh if ent else None)
+        for extra in cases + [dict(saved_logits=z)]:
+            kw = dict(opts, **extra, out_dtype=out_dtype)
+            ref = itl.linear_logp_bwd(h, w, t, lse, g, vocab_chunk=vp, **kw)
+            for vc in (256, 512, 768, 0):
+                got = itl.linear_logp_bwd(h, w, t, lse, g, vocab_chunk=vc, **kw)
+                for a, b in zip(ref, got):
+                    assert torch.equal(_bits_any(a), _bits_any(b)), (vc, temp, ent, rnd,
+                                                                    list(extra))
+            dh_only, none_w = itl.linear_logp_bwd(h, w, t, lse, g, vocab_chunk=256,
+                                                  need_dweight=False, **kw)
+            none_h, dw_only = itl.linear_logp_bwd(h, w, t, lse, g, vocab_chunk=512,
+                                                  need_dhidden=False, **kw)
+            assert none_w is None and none_h is None
+            assert torch.equal(_bits_any(dh_only), _bits_any(ref[0]))
+            assert torch.equal(_bits_any(dw_only), _bits_any(ref[1]))
+
+
+def test_vocab_chunk_full_size_same_bits():
+    """The Qwen3-8B head (H = 4096, V = 151936) at N = 512: the default chunk
+    (the benchmarked launch sequence, 10 chunks) against one chunk over the
+    whole vocabulary, fp32 and bf16 outputs; and the default workspace stays
+    far below the one-chunk workspace."""
+    h, w, t, g = _case(512, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB, seed=77)
+    _, lse = itl.linear_logp_fwd(h, w, t)
+    vp = (synth.QWEN3_VOCAB + 255) // 256 * 256
+    for out_dtype in (torch.float32, torch.bfloat16):
+        one = itl.linear_logp_bwd(h, w, t, lse, g, vocab_chunk=vp, out_dtype=out_dtype)
+        dflt = itl.linear_logp_bwd(h, w, t, lse, g, out_dtype=out_dtype)
+        for a, b in zip(one, dflt):
+            assert torch.equal(_bits_any(a), _bits_any(b)), out_dtype
+    big = itl.linear_logp_bwd_workspace_bytes(512, 4096, synth.QWEN3_VOCAB, vocab_chunk=vp)
+    small = itl.linear_logp_bwd_workspace_bytes(512, 4096, synth.QWEN3_VOCAB)
+    assert small * 4 < big

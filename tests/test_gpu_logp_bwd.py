@@ -167,3 +167,28 @@ def test_tall_batch_grid_stride():
     d_tail = itl.logp_bwd(x[tail].contiguous(), t[tail].contiguous(), lse1[tail].contiguous(),
                           g[tail].contiguous(), -100, 512)
     assert torch.equal(d_tail.view(torch.int16), d[tail].view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_invalid_target_rows_get_minus_p(dtype):
+    """A row whose active target lies outside [0, V) gets d = RNE(-g p) on
+    every column: the gradient with no one-hot term.  Reference: the oracle's
+    gradient of the same row with a valid target t' (the oracle refuses an
+    invalid one) minus g at column t'.  Valid rows of the same batch keep the
+    plain parity, ignored rows stay +0."""
+    v = 5000
+    x = synth.normal_matrix(6, v, 2.0, dtype, seed=31).to(dev())
+    t = torch.tensor([1, v, -100, -1, v - 1, 123456789], device=dev())
+    g = synth.normal_matrix(1, 6, 1.0, torch.float32, seed=32)[0].to(dev())
+    _, lse = itl.logp_fwd(x, t, -100, 512)
+    d = itl.logp_bwd(x, t, lse, g, -100, 512)
+    xn = x.float().cpu().numpy().astype(np.float64)
+    gn = g.cpu().numpy().astype(np.float64)
+    tn = t.cpu().numpy()
+    t_valid = np.where((tn >= 0) & (tn < v), tn, 0)
+    t_valid[tn == -100] = -100
+    _, lse64 = oracle.logp_fwd(xn, t_valid)
+    d64 = oracle.logp_bwd(xn, t_valid, gn, lse=lse64)
+    invalid = np.flatnonzero((tn != -100) & ((tn < 0) | (tn >= v)))
+    d64[invalid, 0] -= gn[invalid]  # remove the one-hot term of the stand-in target 0
+    assert_grad_parity(d, d64, xn, lse64, gn, t, what="invalid targets")

@@ -246,6 +246,31 @@ def test_invalid_targets():
     np.testing.assert_allclose(to_np(logp)[[0, 4]], ref, atol=1e-5, rtol=1e-5)
 
 
+@pytest.mark.parametrize("shards", [1, 2, 4])
+def test_validate_invalid_targets_under_shards(shards):
+    """validate=1 under S = 1, 2, 4 shards: LOGP_ERR_TARGET after the sync;
+    rows with an active target outside [0, V) hold NaN and only those, the
+    ignored row +0, and every other output has the bits of the call without
+    validation (whose merge took the same path)."""
+    x = synth.normal_matrix(6, 5000, 1.0, torch.bfloat16, seed=2).to(dev())
+    t = torch.tensor([1, 5000, -100, -1, 4999, 123456789], device=dev())
+    ref_logp, ref_lse = itl.logp_fwd(x, t, -100, 512, num_shards=1, validate=False)
+    logp = torch.full((6,), 7.0, device=dev())
+    lse = torch.full((6,), 7.0, device=dev())
+    with pytest.raises(itl.LogpError) as ei:
+        itl.logp_fwd(x, t, -100, 512, num_shards=shards, validate=True, logp_out=logp,
+                     lse_out=lse)
+    assert ei.value.status == 8
+    got = logp.cpu()
+    assert torch.isnan(got[[1, 3, 5]]).all()
+    assert not torch.isnan(got[[0, 2, 4]]).any()
+    assert bits(logp)[2].item() == 0 and bits(lse)[2].item() == 0
+    ok = torch.tensor([0, 4])
+    assert torch.equal(bits(logp)[ok], bits(ref_logp)[ok])
+    # the LSE of a row does not depend on its target
+    assert torch.equal(bits(lse)[[0, 1, 3, 4, 5]], bits(ref_lse)[[0, 1, 3, 4, 5]])
+
+
 def test_empty_batch():
     x = torch.empty(0, V, dtype=torch.bfloat16, device=dev())
     t = torch.empty(0, dtype=torch.int64, device=dev())
