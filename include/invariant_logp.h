@@ -205,7 +205,9 @@ int32_t linear_logp_prepare_weight(const void* weight, int64_t ld_w, int64_t v, 
  * Workspace of linear_logp_fwd in bytes: the [n, T] partials (m, s, w) for
  * T = ceil(v / tile_width), the copied target logits [n] and, for n > 128, a
  * copy of hidden re-laid for the product's loads (round_up(n, 256) * h * 2
- * bytes).  Returns 0 for arguments linear_logp_fwd would reject.
+ * bytes) and 512 bytes of counters that hand out the product's last tiles
+ * to whichever part of the GPU is free first.  Returns 0 for arguments
+ * linear_logp_fwd would reject.
  */
 size_t linear_logp_fwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width);
 
@@ -315,7 +317,8 @@ enum logp_bwd_flags {
  * dweight) and, for bf16 dhidden over several chunks, the fp32 dhidden
  * between chunks ([n, h]); Np = n rounded up to 256, C = the chunk width.
  * About 0.87 GB at n = h = 4096, v = 151936 with the default chunk and both
- * outputs (0.60 GB with a prepared weight).  0 when n = 0 or for arguments linear_logp_bwd would reject.
+ * outputs (0.60 GB with a prepared weight).  0 when n = 0 or for arguments
+ * linear_logp_bwd would reject.
  */
 size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width,
                                        int32_t flags, int64_t vocab_chunk);

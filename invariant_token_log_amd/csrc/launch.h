@@ -57,11 +57,16 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                             int32_t round_bf16, float* pw, void* z, int32_t z_bf16, int64_t ld_z,
                             const uint16_t* wblk, uint16_t* hb, hipStream_t s);
 
-// Bytes of the forward's blocked hidden copy: round_up(n, 256) * h * 2 when
-// the 256-row tile runs (n > 128), else 0.
+// Bytes of the forward's scratch: the blocked hidden copy (round_up(n, 256)
+// * h * 2) and the tile-queue counters after it when the 256-row tile runs
+// (n > 128), else 0.
 int64_t linear_fwd_blocked_bytes(int64_t n, int64_t h);
 
 constexpr int kLinearTile = 256;
+
+// Compute units per XCD of the current device (its CU count / 8), looked up
+// once per device.
+int xcd_cus();
 
 // Fused LM-head backward.  The vocabulary is walked in chunks of vc columns
 // (a multiple of 256; kDefaultChunk unless the caller asks for another), so
@@ -107,8 +112,9 @@ void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int6
                            uint16_t* prepared, hipStream_t s);
 
 // dst = the K32-blocked [rows_p, K = k] copy of src [rows, ld] (rows_p, k
-// multiples of 16 and 32; rows past `rows` zero).
+// multiples of 16 and 32; rows past `rows` zero); also sets the nzero ints at
+// zero (may be null) to 0.
 void launch_block_rows(const uint16_t* src, int64_t ld, int64_t rows, int64_t rows_p, int64_t k,
-                       uint16_t* dst, hipStream_t s);
+                       uint16_t* dst, hipStream_t s, int* zero = nullptr, int nzero = 0);
 
 }  // namespace itl

@@ -123,10 +123,15 @@ __global__ __launch_bounds__(256) void transpose_blocked(const uint16_t* __restr
 }
 
 // dst = the K32-blocked [rows_p, K = k] copy of src [rows, k] (rows past
-// rows zero); one 16-byte chunk per thread in destination order.
+// rows zero); one 16-byte chunk per thread in destination order.  Block 0
+// also clears the nzero ints at zero (tile-queue counters of the launches
+// that follow).
 __global__ __launch_bounds__(256) void block_rows_bf16(const uint16_t* __restrict__ src,
                                                        int64_t ld, int64_t rows, int64_t rows_p,
-                                                       int64_t k, uint16_t* __restrict__ dst) {
+                                                       int64_t k, uint16_t* __restrict__ dst,
+                                                       int* __restrict__ zero, int nzero) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += 256) zero[i] = 0;
   const int64_t ksteps = k / gemm::kK, chunks = rows_p * (k / 8);
   for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < chunks;
        c += static_cast<int64_t>(gridDim.x) * 256) {
@@ -715,11 +720,11 @@ void launch_prepare_weight(const uint16_t* weight, int64_t ld_w, int64_t v, int6
 }
 
 void launch_block_rows(const uint16_t* src, int64_t ld, int64_t rows, int64_t rows_p, int64_t k,
-                       uint16_t* dst, hipStream_t s) {
+                       uint16_t* dst, hipStream_t s, int* zero, int nzero) {
   const int64_t want = (rows_p * (k / 8) + 255) / 256;
-  const unsigned blocks = static_cast<unsigned>(want < 8192 ? want : 8192);
+  const unsigned blocks = static_cast<unsigned>(want < 1 ? 1 : want < 8192 ? want : 8192);
   hipLaunchKernelGGL(block_rows_bf16, dim3(blocks), dim3(256), 0, s, src, ld, rows, rows_p, k,
-                     dst);
+                     dst, zero, nzero);
 }
 
 }  // namespace itl

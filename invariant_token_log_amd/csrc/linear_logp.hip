@@ -31,6 +31,8 @@
 //     of mfma_gemm.h, eight waves of 16 / 32 x 128, the same direct loads
 //     (few rows give little arithmetic per weight byte, so these tiles are
 //     bound by the bytes they keep in flight).
+#include <atomic>
+
 #include "launch.h"
 #include "logp_device.h"
 #include "mfma_gemm.h"
@@ -369,19 +371,24 @@ __device__ __forceinline__ void stats_epilogue(f32x4 (&acc)[MI][NJ], Reduce<BM>&
 // ---------------------------------------------------------------------------
 constexpr int kDmaThreads = gemm::kThreads;
 
+// One LDS object per kernel, the stage ring first: a second __shared__
+// variable moves the ring off the start of LDS, which measured 23% slower.
 struct SmemDma {
   gemm::Stages st;  // 128 KiB
   Reduce<256> rd;
+  int slot;         // tile-queue broadcast
 };
 
 // hidden K32-blocked (mblocks * 256 rows); weight row-major, or K32-blocked
-// with round_up(v, 256) rows when WBLK (a prepared weight).
+// with round_up(v, 256) rows when WBLK (a prepared weight).  Tiles come from
+// the mfma_gemm.h tile queue (counters `queue`, zero at launch; `queued` and
+// the grid from queue_plan).
 template <bool WBLK>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
-    float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
+    float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex, int* queue, int queued) {
   const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemDma sm;
   const int tid = threadIdx.x;
@@ -390,8 +397,10 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   const int wm = wave / 4, wn = wave % 4;
   const int li = lane % 16, g = lane / 16;
 
+  const int logical = gemm::queue_tile(queue, mblocks * vblocks, queued, &sm.slot);
+  if (logical < 0) return;
   int mb, vb;
-  tile_coords(xcd_logical(blockIdx.x, mblocks * vblocks), mblocks, vblocks, mb, vb);
+  tile_coords(logical, mblocks, vblocks, mb, vb);
   const int64_t m0 = static_cast<int64_t>(mb) * 256;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
   if (tid < 256) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
@@ -482,20 +491,42 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                        v, 1, vblocks, targets.p, targets.is32, ignore, pm, ps, pt, ex);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
-    launch_block_rows(hidden, ld_h, n, static_cast<int64_t>(mblocks) * 256, h, hb, s);
+    const int64_t np = static_cast<int64_t>(mblocks) * 256;
+    // the tile-queue counters follow the blocked hidden; block_rows clears them
+    int* queue = reinterpret_cast<int*>(hb + np * h);
+    launch_block_rows(hidden, ld_h, n, np, h, hb, s, queue, gemm::kQueueBytes / 4);
+    const gemm::QueuePlan qp = gemm::queue_plan(mblocks * vblocks, xcd_cus());
+    const dim3 grid(static_cast<unsigned>(qp.grid));
     if (wblk)
-      hipLaunchKernelGGL(linear_stats_dma<true>, dim3(mblocks * vblocks), dim3(kDmaThreads), 0, s,
-                         hb, ld_h, wblk, int64_t{0}, n, h, v, mblocks, vblocks, targets.p,
-                         targets.is32, ignore, pm, ps, pt, ex);
+      hipLaunchKernelGGL(linear_stats_dma<true>, grid, dim3(kDmaThreads), 0, s, hb, ld_h, wblk,
+                         int64_t{0}, n, h, v, mblocks, vblocks, targets.p, targets.is32, ignore,
+                         pm, ps, pt, ex, queue, qp.queued);
     else
-      hipLaunchKernelGGL(linear_stats_dma<false>, dim3(mblocks * vblocks), dim3(kDmaThreads), 0,
-                         s, hb, ld_h, weight, ld_w, n, h, v, mblocks, vblocks, targets.p,
-                         targets.is32, ignore, pm, ps, pt, ex);
+      hipLaunchKernelGGL(linear_stats_dma<false>, grid, dim3(kDmaThreads), 0, s, hb, ld_h, weight,
+                         ld_w, n, h, v, mblocks, vblocks, targets.p, targets.is32, ignore, pm, ps,
+                         pt, ex, queue, qp.queued);
   }
 }
 
+int xcd_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0 = not looked up yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 32;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+      cus = 256;
+    c = cus / 8;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 int64_t linear_fwd_blocked_bytes(int64_t n, int64_t h) {
-  return n > 128 ? (n + 255) / 256 * 256 * h * 2 : 0;
+  return n > 128 ? (n + 255) / 256 * 256 * h * 2 + gemm::kQueueBytes : 0;
 }
 
 }  // namespace itl

@@ -74,6 +74,85 @@ __device__ __forceinline__ void tile_coords(int logical, int mblocks, int nblock
   nb = nbg * 4 + r2 / gm;
 }
 
+// Logical tiles [first, last) of XCD x under xcd_logical's split of g tiles.
+__host__ __device__ __forceinline__ void xcd_range(int g, int x, int& first, int& last) {
+  const int per = g / 8, rem = g % 8;
+  first = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  last = first + per + (x < rem ? 1 : 0);
+}
+
+// ---------------------------------------------------------------------------
+// Tile queue.  The XCDs of one GPU do not run at the same speed (clocks and
+// memory paths differ), so with a static split the fastest XCD idles while
+// the slowest finishes its range.  Instead, the last `queued` tiles of each
+// XCD range are claimed at run time: workgroup b (XCD b % 8, slot b / 8)
+// takes the slot-th tile of its range while slot < range - queued, as
+// xcd_logical does; every later workgroup claims the next queued tile of its
+// own range from that range's counter, and once those are gone the next
+// queued tile of another range.  The grid carries `extra` workgroups per XCD
+// beyond the tiles, so that a fast XCD has workgroups to take over a slow
+// one's tail; a workgroup that finds every queue empty exits.  Each tile is
+// computed exactly once, by one workgroup, with the same arithmetic: the
+// schedule changes no bit of any output, whatever queued and extra are.
+//
+// The 8 counters sit 64 bytes apart (kQueueBytes) and must be zero when the
+// kernel starts; kernels that use them are preceded, on the same stream, by
+// a launch that clears them.  Claims are vector atomics.
+// ---------------------------------------------------------------------------
+constexpr int kQueued = 128;       // most queued tiles per XCD range
+constexpr int kQueueExtra = 64;    // most extra workgroups per XCD
+constexpr int kQueueStride = 16;   // ints between counters
+constexpr int kQueueBytes = 8 * kQueueStride * 4;
+
+struct QueuePlan {
+  int queued;  // queued tiles per XCD range
+  int extra;   // extra workgroups per XCD
+  int grid;    // tiles + 8 * extra
+};
+
+// The first round of every XCD (xcd_cus workgroups, one per CU) stays
+// static, since a single round has no tail to balance; of the rest, up to
+// kQueued tiles per range are queued.
+inline QueuePlan queue_plan(int tiles, int xcd_cus) {
+  const int per = tiles / 8;
+  int queued = per - xcd_cus;
+  queued = queued < 0 ? 0 : queued > kQueued ? kQueued : queued;
+  int extra = queued ? per / 8 : 0;
+  extra = extra > kQueueExtra ? kQueueExtra : extra;
+  return QueuePlan{queued, extra, tiles + 8 * extra};
+}
+
+__device__ __forceinline__ int queue_skip(int first, int last, int queued) {
+  return last - first > queued ? last - first - queued : 0;
+}
+
+// Next queued tile for a workgroup of XCD x, or -1 (one lane calls it).
+__device__ __forceinline__ int queue_claim(int* ctr, int x, int tiles, int queued) {
+  for (int d = 0; d < 8; ++d) {
+    const int y = (x + d) & 7;
+    int first, last;
+    xcd_range(tiles, y, first, last);
+    const int s = queue_skip(first, last, queued);
+    if (first + s >= last) continue;
+    const int t = atomicAdd(ctr + y * kQueueStride, 1);
+    if (first + s + t < last) return first + s + t;
+  }
+  return -1;
+}
+
+// This workgroup's logical tile, or -1 when it has none (the whole
+// workgroup then returns).  slot: an int of the kernel's LDS for the
+// broadcast.  All threads must call.
+__device__ __forceinline__ int queue_tile(int* ctr, int tiles, int queued, int* slot) {
+  const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+  int first, last;
+  xcd_range(tiles, x, first, last);
+  if (y < queue_skip(first, last, queued)) return first + y;
+  if (threadIdx.x == 0) *slot = queue_claim(ctr, x, tiles, queued);
+  __syncthreads();
+  return *slot;
+}
+
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 // Element (r, k) of a K32-blocked operand with ksteps = K / 32.

@@ -146,9 +146,11 @@ def test_linear_argument_errors(L):
     assert need == 256 + 3 * 256 * (-(-(594 * 8 * 4) // 256)) + 256
     assert L.linear_logp_fwd_workspace_bytes(8, 4096, 151936, 512) == 0
     assert L.linear_logp_fwd_workspace_bytes(8, 100, 151936, 256) == 0
-    # n > 128: plus the re-laid hidden copy, 256-row padded
+    # n > 128: plus the re-laid hidden copy, 256-row padded, and the 8
+    # tile-queue counters (64 bytes apart)
     tables = 256 + 3 * 256 * (-(-(594 * 200 * 4) // 256)) + 256 * (-(-(200 * 4) // 256))
-    assert L.linear_logp_fwd_workspace_bytes(200, 4096, 151936, 256) == tables + 256 * 4096 * 2
+    assert L.linear_logp_fwd_workspace_bytes(200, 4096, 151936, 256) == (
+        tables + 256 * 4096 * 2 + 512)
 
 
 def test_linear_bwd_argument_errors(L):
