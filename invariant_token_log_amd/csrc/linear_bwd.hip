@@ -466,21 +466,21 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
 // K range of a wider operand); the accumulators start from Cin (fp32,
 // [m_out, ldcin]) when it is set, else from zero, and continue its K walk.
 // BF16OUT rounds the fp32 accumulators to bf16 (RNE) on the way out.
-template <bool BF16OUT>
-__global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, int64_t arows, const uint16_t* __restrict__ B,
-    int64_t ldb, int64_t brows, int ksteps, int mblocks, int nblocks, int64_t m_out,
-    int64_t n_out, const float* Cin, int64_t ldcin, void* C, int64_t ldc) {
-  __shared__ __align__(16) gemm::Stages st;
+// One role's share of the tile (gemm::mainloop_role): each role runs its
+// own copy from the accumulator load to the store, so that no accumulator
+// crosses the branch between the two loop bodies.
+template <bool BF16OUT, bool LOADER>
+__device__ __forceinline__ void gemm_out_tile(gemm::Stages& st, const uint16_t* __restrict__ A,
+                                              int64_t lda, int64_t arows,
+                                              const uint16_t* __restrict__ B, int64_t ldb,
+                                              int64_t brows, int ksteps, int64_t m0, int64_t n0,
+                                              int64_t m_out, int64_t n_out, const float* Cin,
+                                              int64_t ldcin, void* C, int64_t ldc) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 4, wn = wave % 4;
   const int li = lane % 16, g = lane / 16;
-  int mb, nb;
-  gemm::tile_coords(gemm::xcd_logical(blockIdx.x, mblocks * nblocks), mblocks, nblocks, mb, nb);
-  const int64_t m0 = static_cast<int64_t>(mb) * kT;
-  const int64_t n0 = static_cast<int64_t>(nb) * kT;
   f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
         }
       }
   }
-  gemm::mainloop<true, true>(st, A, lda, m0, arows, B, ldb, n0, brows, ksteps, acc);
+  gemm::mainloop_role<true, true, LOADER>(st, A, lda, m0, arows, B, ldb, n0, brows, ksteps, acc);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -518,6 +518,24 @@ __global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
         }
       }
     }
+}
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int64_t arows, const uint16_t* __restrict__ B,
+    int64_t ldb, int64_t brows, int ksteps, int mblocks, int nblocks, int64_t m_out,
+    int64_t n_out, const float* Cin, int64_t ldcin, void* C, int64_t ldc) {
+  __shared__ __align__(16) gemm::Stages st;
+  int mb, nb;
+  gemm::tile_coords(gemm::xcd_logical(blockIdx.x, mblocks * nblocks), mblocks, nblocks, mb, nb);
+  const int64_t m0 = static_cast<int64_t>(mb) * kT;
+  const int64_t n0 = static_cast<int64_t>(nb) * kT;
+  if (gemm::loader_wave())
+    gemm_out_tile<BF16OUT, true>(st, A, lda, arows, B, ldb, brows, ksteps, m0, n0, m_out, n_out,
+                                 Cin, ldcin, C, ldc);
+  else
+    gemm_out_tile<BF16OUT, false>(st, A, lda, arows, B, ldb, brows, ksteps, m0, n0, m_out, n_out,
+                                  Cin, ldcin, C, ldc);
 }
 
 // Zero rows x cols of C (a sum over no tokens).

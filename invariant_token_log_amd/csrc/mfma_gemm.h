@@ -16,8 +16,8 @@
 // kc ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3, so the 16 rows of a
 // fragment read (one 16-byte chunk per row) spread over all banks.  One
 // direct load instruction fills 1 KiB = 16 rows: lane L writes row L / 4,
-// slot L % 4, so it fetches chunk (L % 4) ^ swz(L / 4) of its row.  Wave w
-// fills A blocks w, w + 8 and B blocks w, w + 8 of every stage.
+// slot L % 4, so it fetches chunk (L % 4) ^ swz(L / 4) of its row.  Waves
+// 0-3 fill the stages: wave w loads A and B blocks w, w + 4, w + 8, w + 12.
 //
 // Operand layouts.  Row-major: element (r, k) at r * ld + k.  K32-blocked
 // (kblocked_index): the 16 rows x 32 K piece that one direct load
@@ -160,21 +160,6 @@ __host__ __device__ constexpr int64_t kblocked_index(int64_t r, int64_t k, int64
   return ((r >> 4) * ksteps + (k >> 5)) * 512 + (r & 15) * 32 + (k & 31);
 }
 
-// Issue this wave's 4 direct loads of K step `step` into LDS stage `s`; SA,
-// SB: elements between consecutive K steps of one lane's A / B chunk (32
-// row-major, 512 K32-blocked).
-template <int SA, int SB>
-__device__ __forceinline__ void issue_step(Stages& sm, const uint16_t* a0, const uint16_t* a1,
-                                           const uint16_t* b0, const uint16_t* b1, int wave,
-                                           int s, int step) {
-  const int64_t ka = static_cast<int64_t>(step) * SA, kb = static_cast<int64_t>(step) * SB;
-  constexpr int kBlk = 16 * kK;  // elements per 16-row block
-  __builtin_amdgcn_global_load_lds(a0 + ka, sm.s[s][0] + wave * kBlk, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(b0 + kb, sm.s[s][1] + wave * kBlk, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(a1 + ka, sm.s[s][0] + (wave + 8) * kBlk, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(b1 + kb, sm.s[s][1] + (wave + 8) * kBlk, 16, 0, 0);
-}
-
 // This lane's chunk of 16-row block `blk` (counted from row0, a multiple of
 // 16) of an operand at K step 0.  ld: elements between rows (row-major) or
 // between 16-row blocks (K32-blocked).  Rows at or past `rows` are read from
@@ -191,6 +176,161 @@ __device__ __forceinline__ const uint16_t* lane_chunk(const uint16_t* X, int64_t
     return X + min(row0 + blk * 16 + lrow, rows - 1) * ld + lk;
 }
 
+// s_waitcnt vmcnt(N) with N a template constant.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// Direct loads of one operand by a loader wave: blocks wave + 4u (u < 4) of
+// its 16-row blocks.  K32-blocked: the blocks' element offsets are uniform
+// (scalar registers) and the lane adds its place in the 1 KiB piece;
+// row-major: one lane pointer per block (lane_chunk).  `at` gives the lane's
+// source at K step 0 plus k elements.
+template <bool BLOCKED>
+struct LoaderSrc {
+  const uint16_t* p[4];
+  int lofs;
+  __device__ __forceinline__ void init(const uint16_t* X, int64_t ld, int64_t row0, int64_t rows,
+                                       int wave, int lrow, int lk) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (BLOCKED)
+        p[u] = X + min(row0 / 16 + wave + 4 * u, (rows + 15) / 16 - 1) * ld;
+      else
+        p[u] = lane_chunk<false>(X, ld, row0, rows, wave + 4 * u, lrow, lk);
+    }
+    lofs = lrow * 32 + lk;
+  }
+  __device__ __forceinline__ const uint16_t* at(int u, int64_t k) const {
+    return BLOCKED ? p[u] + k + lofs : p[u] + k;
+  }
+};
+
+// Waves 0-3 (one per SIMD) issue all 32 direct loads of a K step (16 A and
+// 16 B blocks, 8 per wave) at the start of the step; waves 4-7 issue none,
+// so they never wait behind the memory pipeline and on every SIMD one wave
+// keeps the matrix core fed while the other queues its loads (measured on
+// the bare 256 x 256 product: 6% more throughput than 4 loads from every
+// wave spread over the step).
+constexpr int kLoaderWaves = 4;
+constexpr int kLoaderLoads = 8;  // per loader wave per K step
+
+// A loader wave's 8 direct loads of K step `step` into LDS stage `s`; SA,
+// SB: elements between consecutive K steps of one lane's A / B chunk (32
+// row-major, 512 K32-blocked).
+template <int SA, int SB, bool ABLK, bool BBLK>
+__device__ __forceinline__ void issue_loads(Stages& sm, const LoaderSrc<ABLK>& sa,
+                                            const LoaderSrc<BBLK>& sb, int wave, int s, int step) {
+  constexpr int kBlk = 16 * kK;  // elements per 16-row block
+  const int64_t ka = static_cast<int64_t>(step) * SA, kb = static_cast<int64_t>(step) * SB;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    __builtin_amdgcn_global_load_lds(sa.at(u, ka), sm.s[s][0] + (wave + 4 * u) * kBlk, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(sb.at(u, kb), sm.s[s][1] + (wave + 4 * u) * kBlk, 16, 0, 0);
+  }
+}
+
+// The main loop as run by one role: LOADER for waves 0-3, which issue the
+// direct loads, else waves 4-7.  The two roles run different instruction
+// orders: a loader issues its 8 loads right after the step's barrier and
+// then interleaves fragment reads with MFMAs; the others are free to start
+// on MFMAs the moment the barrier opens.  Every wave must call with its own
+// role (mainloop does that); acc, the arguments and the result are as for
+// mainloop.
+template <bool ABLK, bool BBLK, bool LOADER>
+__device__ __forceinline__ void mainloop_role(Stages& sm, const uint16_t* __restrict__ A,
+                                              int64_t lda, int64_t a_row0, int64_t a_rows,
+                                              const uint16_t* __restrict__ B, int64_t ldb,
+                                              int64_t b_row0, int64_t b_rows, int ksteps,
+                                              f32x4 (&acc)[8][4]) {
+  constexpr int SA = ABLK ? 512 : kK, SB = BBLK ? 512 : kK;
+  constexpr int NL = LOADER ? kLoaderLoads : 0;  // this wave's loads per step
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int wm = wave / 4, wn = wave % 4;
+  const int li = lane % 16, g = lane / 16;
+  const int lrow = lane / 4;
+  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
+  LoaderSrc<ABLK> sa;
+  LoaderSrc<BBLK> sb;
+  if constexpr (LOADER) {
+    sa.init(A, lda, a_row0, a_rows, wave, lrow, lk);
+    sb.init(B, ldb, b_row0, b_rows, wave, lrow, lk);
+  }
+#define ITL_ISSUE(S_, STEP_) \
+  if constexpr (LOADER) issue_loads<SA, SB>(sm, sa, sb, wave, (S_), (STEP_))
+
+  // Fragment offsets (elements) inside a stage: row wm*128 + li (+16 i) of A,
+  // row wn*64 + li (+16 j) of B, chunk g.
+  const int aoff = (wm * 128 + li) * kK + ((g ^ swz(li)) * 8);
+  const int boff = (wn * 64 + li) * kK + ((g ^ swz(li)) * 8);
+
+  // Pipeline.  Iteration kt runs the MFMAs of step kt on fragments already in
+  // registers while the fragments of step kt+1 are read from LDS and the
+  // direct loads of step kt+4 go out (steps kt+2, kt+3 are in flight).  Every
+  // iteration issues the same loads per wave and 12 fragment reads, so the
+  // wait counts are constant: past the end the loads re-fetch the last K step
+  // into the stage that is no longer read, and the extra fragment reads land
+  // in registers that are not used.
+  for (int st = 0; st < kStages; ++st) ITL_ISSUE(st, st < ksteps ? st : ksteps - 1);
+  wait_vm<(kStages - 1) * NL>();
+  __builtin_amdgcn_s_barrier();
+  bf16x8 xa[8], xb[4], ya[8], yb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    xb[j] = *reinterpret_cast<const bf16x8*>(sm.s[0][1] + boff + j * 16 * kK);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    xa[i] = *reinterpret_cast<const bf16x8*>(sm.s[0][0] + aoff + i * 16 * kK);
+  // One step: this wave's reads of stage KT % 4 and (loader) its loads of
+  // step KT+1 have landed (KT+2, KT+3 may still be in flight); after the
+  // barrier step KT+1 is in LDS for every wave and stage KT % 4 is free.  A
+  // bare s_barrier: the fence of __syncthreads would also wait for KT+2,
+  // KT+3.  Order: the loads first (loader), then 12 x (2 MFMAs, 1 fragment
+  // read), 8 MFMAs.
+#define ITL_STEP(CA, CB, NA, NB, KT)                                                         \
+  {                                                                                          \
+    wait_vm_lgkm0<(kStages - 2) * NL>();                                                     \
+    __builtin_amdgcn_s_barrier();                                                            \
+    ITL_ISSUE((KT) % kStages, (KT) + kStages < ksteps ? (KT) + kStages : ksteps - 1);        \
+    {                                                                                        \
+      const uint16_t* fa = sm.s[((KT) + 1) % kStages][0];                                    \
+      const uint16_t* fb = sm.s[((KT) + 1) % kStages][1];                                    \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+        NB[j] = *reinterpret_cast<const bf16x8*>(fb + boff + j * 16 * kK);                   \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i)                                          \
+        NA[i] = *reinterpret_cast<const bf16x8*>(fa + aoff + i * 16 * kK);                   \
+    }                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                            \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0); \
+    if constexpr (LOADER) __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);                \
+    _Pragma("unroll") for (int u = 0; u < 12; ++u) {                                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
+    }                                                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                       \
+  }
+  for (int kt = 0; kt < ksteps; kt += 2) {
+    ITL_STEP(xa, xb, ya, yb, kt)
+    ITL_STEP(ya, yb, xa, xb, kt + 1)
+  }
+#undef ITL_STEP
+#undef ITL_ISSUE
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// True for the waves that issue the direct loads (mainloop_role's LOADER).
+__device__ __forceinline__ bool loader_wave() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / 64) < kLoaderWaves;
+}
+
 // acc += A[a_row0 + 0..255, 0..K) * B[b_row0 + 0..255, 0..K)^T with K =
 // ksteps * 32 (ksteps even, >= 2); ABLK / BBLK: the operand is K32-blocked
 // and its lda / ldb is the distance between 16-row blocks in elements (512
@@ -202,81 +342,19 @@ __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict_
                                          const uint16_t* __restrict__ B, int64_t ldb,
                                          int64_t b_row0, int64_t b_rows, int ksteps,
                                          f32x4 (&acc)[8][4]) {
-  constexpr int SA = ABLK ? 512 : kK, SB = BBLK ? 512 : kK;
-  const int tid = threadIdx.x;
-  const int lane = tid % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int wm = wave / 4, wn = wave % 4;
-  const int li = lane % 16, g = lane / 16;
-  const int lrow = lane / 4;
-  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
-  const uint16_t* a0 = lane_chunk<ABLK>(A, lda, a_row0, a_rows, wave, lrow, lk);
-  const uint16_t* a1 = lane_chunk<ABLK>(A, lda, a_row0, a_rows, wave + 8, lrow, lk);
-  const uint16_t* b0 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, wave, lrow, lk);
-  const uint16_t* b1 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, wave + 8, lrow, lk);
-
-  // Fragment offsets (elements) inside a stage: row wm*128 + li (+16 i) of A,
-  // row wn*64 + li (+16 j) of B, chunk g.
-  const int aoff = (wm * 128 + li) * kK + ((g ^ swz(li)) * 8);
-  const int boff = (wn * 64 + li) * kK + ((g ^ swz(li)) * 8);
-
-  // Pipeline.  Iteration kt runs the MFMAs of step kt on fragments already in
-  // registers while the fragments of step kt+1 are read from LDS and the
-  // direct loads of step kt+4 go out (steps kt+2, kt+3 are in flight).  Every
-  // iteration issues exactly 4 loads per wave and 12 fragment reads, so the
-  // wait counts are constant: past the end the loads re-fetch the last K step
-  // into the stage that is no longer read, and the extra fragment reads land
-  // in registers that are not used.
-  for (int st = 0; st < kStages; ++st)
-    issue_step<SA, SB>(sm, a0, a1, b0, b1, wave, st, st < ksteps ? st : ksteps - 1);
-  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  bf16x8 xa[8], xb[4], ya[8], yb[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    xb[j] = *reinterpret_cast<const bf16x8*>(sm.s[0][1] + boff + j * 16 * kK);
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    xa[i] = *reinterpret_cast<const bf16x8*>(sm.s[0][0] + aoff + i * 16 * kK);
-  // One step: this wave's reads of stage KT % 4 and its loads of step KT+1
-  // have landed (KT+2, KT+3 may still be in flight); after the barrier step
-  // KT+1 is in LDS for every wave and stage KT % 4 is free.  A bare
-  // s_barrier: the fence of __syncthreads would also wait for KT+2, KT+3.
-#define ITL_STEP(CA, CB, NA, NB, KT)                                                         \
-  {                                                                                          \
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");                              \
-    __builtin_amdgcn_s_barrier();                                                            \
-    issue_step<SA, SB>(sm, a0, a1, b0, b1, wave, (KT) % kStages,                             \
-                       (KT) + kStages < ksteps ? (KT) + kStages : ksteps - 1);               \
-    {                                                                                        \
-      const uint16_t* sa = sm.s[((KT) + 1) % kStages][0];                                    \
-      const uint16_t* sb = sm.s[((KT) + 1) % kStages][1];                                    \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
-        NB[j] = *reinterpret_cast<const bf16x8*>(sb + boff + j * 16 * kK);                   \
-      _Pragma("unroll") for (int i = 0; i < 8; ++i)                                          \
-        NA[i] = *reinterpret_cast<const bf16x8*>(sa + aoff + i * 16 * kK);                   \
-    }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                            \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0); \
-    /* Interleave so that the MFMA stream never waits behind the load issue: */              \
-    /* 4 x (1 direct load, then 3 x (2 MFMAs, 1 fragment read)), then 8 MFMAs. */            \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                          \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
-      _Pragma("unroll") for (int w = 0; w < 3; ++w) {                                        \
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                   \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
-      }                                                                                      \
-    }                                                                                        \
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                       \
-  }
-  for (int kt = 0; kt < ksteps; kt += 2) {
-    ITL_STEP(xa, xb, ya, yb, kt)
-    ITL_STEP(ya, yb, xa, xb, kt + 1)
-  }
-#undef ITL_STEP
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (loader_wave())
+    mainloop_role<ABLK, BBLK, true>(sm, A, lda, a_row0, a_rows, B, ldb, b_row0, b_rows, ksteps,
+                                    acc);
+  else
+    mainloop_role<ABLK, BBLK, false>(sm, A, lda, a_row0, a_rows, B, ldb, b_row0, b_rows, ksteps,
+                                     acc);
 }
+
+// acc += A[a_row0 + 0..255, 0..K) * B[b_row0 + 0..255, 0..K)^T with K =
+// ksteps * 32 (ksteps even, >= 2); ABLK / BBLK: the operand is K32-blocked
+// and its lda / ldb is the distance between 16-row blocks in elements (512
+// times the operand's K steps).  All 512 threads must call; on return every
+// direct load has landed and the stages may be reused after a barrier.
 
 // ---------------------------------------------------------------------------
 // Narrow tiles for few hidden rows: ROWS (64 or 128) A rows x 256 B rows,
@@ -302,16 +380,6 @@ struct StagesNarrow {
   uint16_t a[NarrowCfg<ROWS>::kStages][ROWS * kK];
   uint16_t b[NarrowCfg<ROWS>::kStages][kTile * kK];  // 16 KiB each
 };
-
-// s_waitcnt vmcnt(N) with N a template constant.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
-}
 
 // acc += A[a_row0 + 0..ROWS-1, 0..K) * B[b_row0 + 0..255, 0..K)^T, K =
 // ksteps * 32 (ksteps even, >= 2); A row-major, B row-major or K32-blocked
