@@ -43,7 +43,16 @@ KERNEL_SOURCES = {
     "linear_stats_dma": ["invariant_token_log_amd/csrc/linear_logp.hip",
                          "invariant_token_log_amd/csrc/mfma_gemm.h",
                          "invariant_token_log_amd/csrc/logp_device.h"],
+    "linear_dz_saved_kernel": ["invariant_token_log_amd/csrc/linear_bwd.hip",
+                               "invariant_token_log_amd/csrc/mfma_gemm.h",
+                               "invariant_token_log_amd/csrc/logp_device.h"],
+    "transpose_blocked": ["invariant_token_log_amd/csrc/linear_bwd.hip",
+                          "invariant_token_log_amd/csrc/mfma_gemm.h",
+                          "invariant_token_log_amd/csrc/logp_device.h"],
 }
+# The fused backward at N = H = 4096, V = 151936 with 204 rows ignored and the
+# default vocabulary chunk (32768 columns: 5 chunks over Vp = 152064).
+LINEAR_BWD_CHUNKS = 5
 
 
 def kernel_source_hash(kernel):
@@ -677,7 +686,18 @@ def _algorithmic_bytes(workload, kernel):
     if workload == "qwen3_4096x4096x151936":
         n, h, v = 4096, 4096, 151936
         return v * h * 2 + n * h * 2 + n * 16
-    raise ValueError(workload)
+    if workload == "qwen3_4096x4096x151936_bwd_saved":
+        # per launch, averaged over one backward's launches: the saved-logits
+        # dz kernel reads the active rows' fp32 logits and writes dz_c and
+        # dz_c^T (bf16, padded to Vp columns) once per chunk; the transpose
+        # reads W and writes W^T_c per chunk, then h -> h^T once
+        n, h, v, vp = 4096, 4096, 151936, 152064
+        act = n - int(0.05 * n)
+        if kernel == "linear_dz_saved_kernel":
+            return (act * v * 4 + 2 * n * vp * 2) // LINEAR_BWD_CHUNKS
+        if kernel == "transpose_blocked":
+            return (v * h * 2 + vp * h * 2 + 2 * n * h * 2) // (LINEAR_BWD_CHUNKS + 1)
+    raise ValueError((workload, kernel))
 
 
 def summarize_traffic(fetch_dir, write_dir, workload, kernels, fetch_cmd, write_cmd):
@@ -810,7 +830,10 @@ def main():
     if args.summarize_traffic:
         wl, ks = {"fwd_bwd": ("qwen3_8192x151936", ["logp_fwd_fused_kernel", "logp_bwd_kernel"]),
                   "fwd": ("qwen3_4096x151936", ["logp_fwd_fused_kernel"]),
-                  "linear": ("qwen3_4096x4096x151936", ["linear_stats_dma"])}[args.workload]
+                  "linear": ("qwen3_4096x4096x151936", ["linear_stats_dma"]),
+                  "linear_bwd_saved": ("qwen3_4096x4096x151936_bwd_saved",
+                                       ["linear_dz_saved_kernel", "transpose_blocked"]),
+                  }[args.workload]
         for p in summarize_traffic(*args.summarize_traffic, wl, ks, *args.pmc_commands):
             print(p)
         return
