@@ -84,6 +84,27 @@ def measured_traffic(kernel, workload):
         return None
 
 
+def measured_valu(kernel, workload):
+    """VALU-busy percent of a streaming kernel from the committed rocprofv3
+    counter summary (profiles/valu_logp_fwd_bwd_<workload>.txt), or None when
+    absent or when the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"valu_logp_fwd_bwd_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    src, busy = None, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("source_sha256_16="):
+                src = line.strip().split("=", 1)[1]
+            elif line.startswith(kernel + ":"):
+                for item in line.split():
+                    if item.startswith("VALUBusy_pct="):
+                        busy = float(item.split("=", 1)[1])
+    if src != kernel_source_hash(kernel):
+        return None
+    return busy
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -358,6 +379,7 @@ def bench_fwd_bwd(args, torch, itl, synth, ctx):
     traffic = measured_traffic(dom, "qwen3_8192x151936")
     roofline = {"bound": "hbm", "achieved": kd["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kd["gbps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+                "valu_busy_pct": {k: measured_valu(k, "qwen3_8192x151936") for k in kernels},
                 "algorithmic_bytes_per_launch": kd["bytes"],
                 "measured_ceiling": dict(ceil, **{
                     "bwd_frac_of_copy": round(kernels["logp_bwd_kernel"]["gbps_median"]
