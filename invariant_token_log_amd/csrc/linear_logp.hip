@@ -380,13 +380,14 @@ struct SmemDma {
 };
 
 // hidden K32-blocked (mblocks * 256 rows); weight row-major, or K32-blocked
-// with round_up(v, 256) rows when WBLK (a prepared weight).  Tiles come from
-// the mfma_gemm.h tile queue (counters `queue`, zero at launch; `queued` and
-// the grid from queue_plan).
+// with round_up(v, 256) rows when WBLK (a prepared weight).  The grid covers
+// vocabulary blocks [0, vtiles) of the vblocks that index the partial
+// tables.  Tiles come from the mfma_gemm.h tile queue (counters `queue`, zero
+// at launch; `queued` and the grid from queue_plan).
 template <bool WBLK>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
-    int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
+    int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks, int vtiles,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
     float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex, int* queue, int queued) {
   const Targets targets{tgt, tgt32};
@@ -397,10 +398,10 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
   const int wm = wave / 4, wn = wave % 4;
   const int li = lane % 16, g = lane / 16;
 
-  const int logical = gemm::queue_tile(queue, mblocks * vblocks, queued, &sm.slot);
+  const int logical = gemm::queue_tile(queue, mblocks * vtiles, queued, &sm.slot);
   if (logical < 0) return;
   int mb, vb;
-  tile_coords(logical, mblocks, vblocks, mb, vb);
+  tile_coords(logical, mblocks, vtiles, mb, vb);
   const int64_t m0 = static_cast<int64_t>(mb) * 256;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
   if (tid < 256) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
@@ -423,9 +424,11 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
 
 // ---------------------------------------------------------------------------
 // linear_stats_narrow<ROWS>: the narrow mfma_gemm.h tiles for few hidden rows
-// (N <= 64: ROWS = 64, two workgroups per CU; N <= 128: ROWS = 128); same K
-// walk and epilogue tree as linear_stats_dma, so a row gets the same bits on
-// every path.
+// (N <= 64: ROWS = 64, two workgroups per CU; N <= 128: ROWS = 128), and for
+// the last vocabulary blocks of a larger N (below); same K walk and epilogue
+// tree as linear_stats_dma, so a row gets the same bits on every path.  hidden
+// row-major [n, ld_h], mblocks = ceil(n / ROWS) row blocks; the grid covers
+// vocabulary blocks [vb0, vb0 + vtiles).
 // ---------------------------------------------------------------------------
 template <int ROWS>
 struct SmemNarrow {
@@ -436,7 +439,8 @@ struct SmemNarrow {
 template <int ROWS, bool WBLK>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
-    int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks,
+    int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks, int vb0,
+    int vtiles,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index, float* __restrict__ pm,
     float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
   constexpr int MI = gemm::NarrowCfg<ROWS>::kMI;
@@ -448,9 +452,9 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
   const int wm = wave / 2, wn = wave % 2;
   const int li = lane % 16, g = lane / 16;
 
-  const int logical = xcd_logical(blockIdx.x, mblocks * vblocks);
+  const int logical = xcd_logical(blockIdx.x, mblocks * vtiles);
   const int mb = logical % mblocks;
-  const int vb = logical / mblocks;
+  const int vb = vb0 + logical / mblocks;
   const int64_t m0 = static_cast<int64_t>(mb) * ROWS;
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
   if (tid < ROWS) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
@@ -484,27 +488,39 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
   // the narrow tiles read a prepared (K32-blocked) weight when there is one
   const uint16_t* wn = wblk ? wblk : weight;
   const int64_t ldn = wblk ? 0 : ld_w;
+  auto narrow = [&](int rows, int mb, int vb0, int vt) {
+    auto kern = rows == 64 ? (wblk ? linear_stats_narrow<64, true> : linear_stats_narrow<64, false>)
+                           : (wblk ? linear_stats_narrow<128, true> : linear_stats_narrow<128, false>);
+    hipLaunchKernelGGL(kern, dim3(mb * vt), dim3(kDmaThreads), 0, s, hidden, ld_h, wn, ldn, n, h,
+                       v, mb, vblocks, vb0, vt, targets.p, targets.is32, ignore, pm, ps, pt, ex);
+  };
   if (n <= 128) {
-    auto kern = n <= 64 ? (wblk ? linear_stats_narrow<64, true> : linear_stats_narrow<64, false>)
-                        : (wblk ? linear_stats_narrow<128, true> : linear_stats_narrow<128, false>);
-    hipLaunchKernelGGL(kern, dim3(vblocks), dim3(kDmaThreads), 0, s, hidden, ld_h, wn, ldn, n, h,
-                       v, 1, vblocks, targets.p, targets.is32, ignore, pm, ps, pt, ex);
+    narrow(n <= 64 ? 64 : 128, 1, 0, vblocks);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     const int64_t np = static_cast<int64_t>(mblocks) * 256;
+    // Last round: when the 256 x 256 tiles leave the final round at most a
+    // quarter full, the last `tail` vocabulary blocks go to the 64-row tile
+    // instead (four times as many, four times smaller, the same bits), so
+    // that round spreads over the GPU.
+    const int cus = xcd_cus() * 8, tiles = mblocks * vblocks, rem = tiles % cus;
+    int tail = 0;
+    if (rem != 0 && rem <= cus / 4 && tiles > cus) tail = (rem + mblocks - 1) / mblocks;
+    const int vmain = vblocks - tail;
     // the tile-queue counters follow the blocked hidden; block_rows clears them
     int* queue = reinterpret_cast<int*>(hb + np * h);
     launch_block_rows(hidden, ld_h, n, np, h, hb, s, queue, gemm::kQueueBytes / 4);
-    const gemm::QueuePlan qp = gemm::queue_plan(mblocks * vblocks, xcd_cus());
+    const gemm::QueuePlan qp = gemm::queue_plan(mblocks * vmain, xcd_cus());
     const dim3 grid(static_cast<unsigned>(qp.grid));
     if (wblk)
       hipLaunchKernelGGL(linear_stats_dma<true>, grid, dim3(kDmaThreads), 0, s, hb, ld_h, wblk,
-                         int64_t{0}, n, h, v, mblocks, vblocks, targets.p, targets.is32, ignore,
-                         pm, ps, pt, ex, queue, qp.queued);
+                         int64_t{0}, n, h, v, mblocks, vblocks, vmain, targets.p, targets.is32,
+                         ignore, pm, ps, pt, ex, queue, qp.queued);
     else
       hipLaunchKernelGGL(linear_stats_dma<false>, grid, dim3(kDmaThreads), 0, s, hb, ld_h, weight,
-                         ld_w, n, h, v, mblocks, vblocks, targets.p, targets.is32, ignore, pm, ps,
-                         pt, ex, queue, qp.queued);
+                         ld_w, n, h, v, mblocks, vblocks, vmain, targets.p, targets.is32, ignore,
+                         pm, ps, pt, ex, queue, qp.queued);
+    if (tail) narrow(64, static_cast<int>((n + 63) / 64), vmain, tail);
   }
 }
 

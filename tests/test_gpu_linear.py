@@ -115,12 +115,15 @@ def test_narrow_and_wide_tiles_same_bits():
             assert torch.equal(bits(a[:rows]), bits(b)), rows
 
 
-@pytest.mark.parametrize("n,hd,v", [(300, 256, 190 * 256 + 77), (1000, 256, 40000)])
+@pytest.mark.parametrize("n,hd,v", [(300, 256, 190 * 256 + 77), (1000, 256, 40000),
+                                    (300, 256, 40000)])
 def test_tile_queue_grids(n, hd, v):
     """Tile counts where the 256-row kernel hands its last tiles out at run
     time (ranges of unequal length over the XCDs, extra workgroups that find
-    nothing left): every row has the bits the 64-row tile gives it alone,
-    repeated calls agree, and sampled rows match the oracle."""
+    nothing left), and (300 x 40000: 314 tiles, a final round under a quarter
+    full) where the last 29 vocabulary blocks go to the 64-row tile instead:
+    every row has the bits the 64-row tile gives it alone, repeated calls
+    agree, and sampled rows match the oracle."""
     c = synth.qwen3_linear(seed=n + 7, n=n, h=hd, v=v, device=dev(), ignore_frac=0.05)
     h, w, t = c["hidden"], c["weight"], c["targets"]
     wide = itl.linear_logp_fwd(h, w, t, return_entropy=True, return_logits=True,
