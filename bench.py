@@ -442,8 +442,8 @@ def secondary_fwd(args, torch, itl, synth, ctx):
     return res
 
 
-def _linear_case(torch, synth, ignore_frac=0.0):
-    n, h, v = 4096, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB
+def _linear_case(torch, synth, ignore_frac=0.0, n=4096):
+    h, v = synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB
     dev = torch.device("cuda", 0)
     c = synth.qwen3_linear(n=n, h=h, v=v, device=dev, ignore_frac=ignore_frac)
     return n, h, v, c["hidden"], c["weight"], c["targets"]
@@ -530,6 +530,51 @@ def standalone_fwd(args, torch, itl, synth, ctx):
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBS, 4), "traffic": r["traffic"],
                      "kernel": "logp_fwd_fused_kernel"},
+    }
+
+
+def linear_decode(args, torch, itl, synth, prepared):
+    """Decode-sized fused LM head (N = 1 and 64 rows, the narrow tile): the
+    weight streams from HBM once per call, so the rate is weight bytes / time
+    against the HBM peak."""
+    out = {}
+    for n in (1, 64):
+        _, h, v, hid, wt, t = _linear_case(torch, synth, n=n)
+        logp = torch.empty(n, dtype=torch.float32, device=hid.device)
+        lse = torch.empty(n, dtype=torch.float32, device=hid.device)
+        ws = torch.empty(max(itl.lib().linear_logp_fwd_workspace_bytes(n, h, v, 256), 1),
+                         dtype=torch.uint8, device=hid.device)
+        pw = itl.prepare_weight(wt) if prepared else None
+
+        def run():
+            itl.linear_logp_fwd(hid, wt, t, -100, 256, logp_out=logp, lse_out=lse, workspace=ws,
+                                prepared_weight=pw)
+
+        st = timed(torch, run, args)
+        d = _kernel_entry(st, v * h * 2 + n * h * 2 + n * 16)
+        d["rows"] = n
+        out[f"n{n}"] = d
+        del hid, wt, t, pw, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def standalone_linear_decode(args, torch, itl, synth, prepared):
+    r = linear_decode(args, torch, itl, synth, prepared)
+    d = r["n64"]
+    return {
+        "metric": "weight-stream GB/s (% of HBM peak), fused LM-head+logp decode N=64 H=4096 "
+                  "V=151936 bf16" + (", prepared weight" if prepared else ""),
+        "value": d["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": d["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_lm_head_linear_logp_decode"
+                               + ("_prepared" if prepared else ""),
+                   "n": 64, "h": 4096, "v": synth.QWEN3_VOCAB, "tile_width": 256},
+        "sizes": r,
+        "roofline": {"bound": "hbm", "achieved": d["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": d["hbm_frac"], "traffic": None,
+                     "kernel": "linear_logp_fwd (the 64-row tile and the merge)"},
     }
 
 
@@ -805,6 +850,8 @@ def run(args, ctx, pool, cores):
         out = standalone_fwd(args, torch, itl, synth, ctx)
     elif wl in ("linear", "linear_prepared"):
         out = standalone_linear(args, torch, itl, synth, ctx, wl == "linear_prepared")
+    elif wl in ("linear_decode", "linear_decode_prepared"):
+        out = standalone_linear_decode(args, torch, itl, synth, wl == "linear_decode_prepared")
     else:
         out = standalone_linear_bwd(args, torch, itl, synth, ctx,
                                     saved=wl == "linear_bwd_saved",
@@ -832,7 +879,8 @@ def main():
                     help="untimed seconds of launches before the warmup (GPU clock ramp)")
     ap.add_argument("--workload", default="fwd_bwd",
                     choices=["fwd_bwd", "fwd", "linear", "linear_bwd", "linear_bwd_saved",
-                             "linear_bwd_prepared", "linear_prepared"])
+                             "linear_bwd_prepared", "linear_prepared", "linear_decode",
+                             "linear_decode_prepared"])
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows for the fused LM head's CPU oracle baseline (0 = 512)")
     ap.add_argument("--vocab-chunk", type=int, default=0,

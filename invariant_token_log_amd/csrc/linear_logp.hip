@@ -436,7 +436,7 @@ struct SmemNarrow {
   Reduce<ROWS> rd;
 };
 
-template <int ROWS, bool WBLK>
+template <int ROWS, bool WBLK, bool NTB = false>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks, int vb0,
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / 4, wn = wave % 4;
   const int li = lane % 16, g = lane / 16;
 
   const int logical = xcd_logical(blockIdx.x, mblocks * vtiles);
@@ -459,18 +459,18 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
   const int64_t v0 = static_cast<int64_t>(vb) * BN;
   if (tid < ROWS) sm.rd.code[tid] = row_code(m0 + tid, n, targets, ignore_index, v0, v);
 
-  f32x4 acc[MI][8];
+  f32x4 acc[MI][4];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int ksteps = static_cast<int>(hdim / BK);
-  gemm::mainloop_narrow<ROWS, WBLK>(sm.st, hidden, ld_h, m0, n, weight,
+  gemm::mainloop_narrow<ROWS, WBLK, NTB && WBLK>(sm.st, hidden, ld_h, m0, n, weight,
                                     WBLK ? static_cast<int64_t>(ksteps) * 512 : ld_w, v0,
                                     WBLK ? static_cast<int64_t>(vblocks) * BN : v, ksteps, acc);
   __syncthreads();
-  stats_epilogue<MI, 8, ROWS, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * (ROWS / 4),
-                                                          wn * 128, li, g, tid,
+  stats_epilogue<MI, 4, ROWS, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * (ROWS / 2),
+                                                          wn * 64, li, g, tid,
                                            m0, v0, vb, vblocks, n, v, pm, ps, pt, ex);
 }
 
@@ -488,14 +488,21 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
   // the narrow tiles read a prepared (K32-blocked) weight when there is one
   const uint16_t* wn = wblk ? wblk : weight;
   const int64_t ldn = wblk ? 0 : ld_w;
-  auto narrow = [&](int rows, int mb, int vb0, int vt) {
-    auto kern = rows == 64 ? (wblk ? linear_stats_narrow<64, true> : linear_stats_narrow<64, false>)
-                           : (wblk ? linear_stats_narrow<128, true> : linear_stats_narrow<128, false>);
+  // once: every weight row is read by one workgroup only (a single row
+  // block), so a prepared weight streams with non-temporal loads
+  auto narrow = [&](int rows, int mb, int vb0, int vt, bool once) {
+    auto kern = rows == 64
+                    ? (wblk ? (once ? linear_stats_narrow<64, true, true>
+                                    : linear_stats_narrow<64, true, false>)
+                            : linear_stats_narrow<64, false>)
+                    : (wblk ? (once ? linear_stats_narrow<128, true, true>
+                                    : linear_stats_narrow<128, true, false>)
+                            : linear_stats_narrow<128, false>);
     hipLaunchKernelGGL(kern, dim3(mb * vt), dim3(kDmaThreads), 0, s, hidden, ld_h, wn, ldn, n, h,
                        v, mb, vblocks, vb0, vt, targets.p, targets.is32, ignore, pm, ps, pt, ex);
   };
   if (n <= 128) {
-    narrow(n <= 64 ? 64 : 128, 1, 0, vblocks);
+    narrow(n <= 64 ? 64 : 128, 1, 0, vblocks, true);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     const int64_t np = static_cast<int64_t>(mblocks) * 256;
@@ -520,7 +527,7 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
       hipLaunchKernelGGL(linear_stats_dma<false>, grid, dim3(kDmaThreads), 0, s, hb, ld_h, weight,
                          ld_w, n, h, v, mblocks, vblocks, vmain, targets.p, targets.is32, ignore,
                          pm, ps, pt, ex, queue, qp.queued);
-    if (tail) narrow(64, static_cast<int>((n + 63) / 64), vmain, tail);
+    if (tail) narrow(64, static_cast<int>((n + 63) / 64), vmain, tail, false);
   }
 }
 

@@ -360,9 +360,10 @@ __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict_
 // Narrow tiles for few hidden rows: ROWS (64 or 128) A rows x 256 B rows,
 // the same MFMA form, K walk and LDS chunk layout as the 256 x 256 tile, so
 // every output gets the same bits.  8 waves; wave w covers rows
-// (w / 2) * (ROWS / 4) + [0, ROWS / 4) and columns (w % 2) * 128 + [0, 128)
+// (w / 4) * (ROWS / 2) + [0, ROWS / 2) and columns (w % 4) * 64 + [0, 64)
 // as acc[i][j][q] = C[row0 + i*16 + 4*g + q][col0 + j*16 + li], i < ROWS /
-// 64.  With so little arithmetic per weight byte the tile is bound by the
+// 32, j < 4 (the 256-row tile's arrangement with fewer rows; fewer registers
+// than waves of 128 columns, the same time).  With so little arithmetic per weight byte the tile is bound by the
 // bytes it keeps in flight: ROWS = 128 runs five stages (96 KiB in flight,
 // one workgroup per CU); ROWS = 64 runs three stages of 20 KiB so that two
 // workgroups share a CU (594 vocabulary tiles then take two rounds of 512
@@ -372,7 +373,7 @@ __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict_
 template <int ROWS>
 struct NarrowCfg {
   static constexpr int kStages = ROWS == 128 ? 5 : 3;
-  static constexpr int kMI = ROWS / 64;
+  static constexpr int kMI = ROWS / 32;
 };
 
 template <int ROWS>
@@ -384,22 +385,26 @@ struct StagesNarrow {
 // acc += A[a_row0 + 0..ROWS-1, 0..K) * B[b_row0 + 0..255, 0..K)^T, K =
 // ksteps * 32 (ksteps even, >= 2); A row-major, B row-major or K32-blocked
 // (BBLK, ldb = distance between 16-row blocks); rows at or past a_rows /
-// b_rows are read from the last valid row (block).  All 512 threads must
+// b_rows are read from the last valid row (block).  NTB: B is read once per
+// launch (no other workgroup reads the same rows) and K32-blocked, so its
+// direct loads carry the non-temporal hint (measured: the decode-sized
+// forward with a prepared weight 0.250 -> 0.227 ms; on row-major B, whose
+// loads take half lines, the hint made it 43% slower).  All 512 threads must
 // call; on return every direct load has landed and the stages may be reused
 // after a barrier.
-template <int ROWS, bool BBLK = false>
+template <int ROWS, bool BBLK = false, bool NTB = false>
 __device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
                                                 const uint16_t* __restrict__ A, int64_t lda,
                                                 int64_t a_row0, int64_t a_rows,
                                                 const uint16_t* __restrict__ B, int64_t ldb,
                                                 int64_t b_row0, int64_t b_rows, int ksteps,
-                                                f32x4 (&acc)[NarrowCfg<ROWS>::kMI][8]) {
+                                                f32x4 (&acc)[NarrowCfg<ROWS>::kMI][4]) {
   constexpr int S = NarrowCfg<ROWS>::kStages;
   constexpr int MI = NarrowCfg<ROWS>::kMI;
   const int tid = threadIdx.x;
   const int lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / 4, wn = wave % 4;
   const int li = lane % 16, g = lane / 16;
   const int lrow = lane / 4;
   const int lk = ((lane % 4) ^ swz(lrow)) * 8;
@@ -408,14 +413,15 @@ __device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
   const uint16_t* b0 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, wave, lrow, lk);
   const uint16_t* b1 = lane_chunk<BBLK>(B, ldb, b_row0, b_rows, wave + 8, lrow, lk);
   constexpr int SB = BBLK ? 512 : kK;
-  const int aoff = (wm * (ROWS / 4) + li) * kK + ((g ^ swz(li)) * 8);
-  const int boff = (wn * 128 + li) * kK + ((g ^ swz(li)) * 8);
+  const int aoff = (wm * (ROWS / 2) + li) * kK + ((g ^ swz(li)) * 8);
+  const int boff = (wn * 64 + li) * kK + ((g ^ swz(li)) * 8);
   constexpr int kBlk = 16 * kK;
   auto issue_step = [&](int s, int step) {
     const int64_t k0 = static_cast<int64_t>(step) * kK, kb = static_cast<int64_t>(step) * SB;
     if (has_a) __builtin_amdgcn_global_load_lds(a0 + k0, sm.a[s] + wave * kBlk, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b0 + kb, sm.b[s] + wave * kBlk, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b1 + kb, sm.b[s] + (wave + 8) * kBlk, 16, 0, 0);
+    constexpr int kAux = NTB ? 2 : 0;  // cache policy: 2 = non-temporal
+    __builtin_amdgcn_global_load_lds(b0 + kb, sm.b[s] + wave * kBlk, 16, 0, kAux);
+    __builtin_amdgcn_global_load_lds(b1 + kb, sm.b[s] + (wave + 8) * kBlk, 16, 0, kAux);
   };
   // Iteration kt: MFMAs of step kt on fragments in registers, fragment reads
   // of step kt+1, direct loads of step kt+S (kt+2 .. kt+S-1 in flight).
@@ -428,9 +434,9 @@ __device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
   else
     wait_vm<(S - 1) * 2>();
   __builtin_amdgcn_s_barrier();
-  bf16x8 xa[MI], xb[8], ya[MI], yb[8];
+  bf16x8 xa[MI], xb[4], ya[MI], yb[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(sm.b[0] + boff + j * 16 * kK);
+  for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const bf16x8*>(sm.b[0] + boff + j * 16 * kK);
 #pragma unroll
   for (int i = 0; i < MI; ++i) xa[i] = *reinterpret_cast<const bf16x8*>(sm.a[0] + aoff + i * 16 * kK);
   int cur = 0;  // stage of step kt
@@ -443,13 +449,13 @@ __device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
     __builtin_amdgcn_s_barrier();                                                            \
     const int nxt = cur + 1 == S ? 0 : cur + 1;                                              \
     issue_step(cur, (KT) + S < ksteps ? (KT) + S : ksteps - 1);                              \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                            \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                            \
       NB[j] = *reinterpret_cast<const bf16x8*>(sm.b[nxt] + boff + j * 16 * kK);              \
     _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
       NA[i] = *reinterpret_cast<const bf16x8*>(sm.a[nxt] + aoff + i * 16 * kK);              \
     cur = nxt;                                                                               \
     _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
-      _Pragma("unroll") for (int j = 0; j < 8; ++j)                                          \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0); \
   }
   for (int kt = 0; kt < ksteps; kt += 2) {
