@@ -11,8 +11,9 @@ one JSON line.  `value` is rows/s over the timed steps; the roofline object
 prices the dominant kernel's algorithmic bytes against the MI355X HBM peak and
 against the read and copy rates measured in the same run.  After the headline
 timing the default run also times, on their own inputs: the N = 4096 forward
-workload and the fused LM head (forward with and without a prepared weight,
-backward) at N = H = 4096, V = 151936 ("secondary"); and the float64 CPU
+workload, the fused LM head (forward with and without a prepared weight,
+backward) at N = H = 4096, V = 151936 and its decode-sized forward (N = 1 and
+64) ("secondary"); and the float64 CPU
 oracle on the host's cores over the whole headline batch, a forward-only pass
 over the N = 4096 forward batch, and one core on 256 rows ("cpu_baseline").
 Every input buffer is fingerprinted with SHA-256 ("inputs_sha256").
@@ -631,7 +632,9 @@ def standalone_linear_bwd(args, torch, itl, synth, ctx, saved=False, prepared=Fa
 
 def default_secondary(args, torch, itl, synth, ctx):
     """Measurements after the headline's timed region: the N = 4096 forward
-    workload and the fused LM head at N = H = 4096, V = 151936."""
+    workload, the fused LM head at N = H = 4096, V = 151936 (forward, with a
+    prepared weight, backward with the default and a whole-vocabulary chunk)
+    and at decode sizes (N = 1 and 64)."""
     sec = {"fwd_qwen3_4096x151936": secondary_fwd(args, torch, itl, synth, ctx)}
     r, _ = linear_fwd_stats(args, torch, itl, synth, False, ctx)
     sec["linear_fwd_qwen3_4096x4096x151936"] = r
@@ -647,6 +650,9 @@ def default_secondary(args, torch, itl, synth, ctx):
     r, _ = linear_bwd_stats(args, torch, itl, synth, vocab_chunk=synth.QWEN3_VOCAB)
     sec["linear_bwd_one_chunk_qwen3_4096x4096x151936"] = r
     torch.cuda.empty_cache()
+    # decode-sized fused forward (the narrow tile): weight-stream GB/s
+    sec["linear_decode_qwen3_4096x151936"] = linear_decode(args, torch, itl, synth, False)
+    sec["linear_decode_prepared_qwen3_4096x151936"] = linear_decode(args, torch, itl, synth, True)
     return sec
 
 
