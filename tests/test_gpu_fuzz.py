@@ -162,3 +162,39 @@ def test_fuzz_linear_bwd(c):
     bh, bw = _bounds(hn, wn, tn, gn, lse64)
     assert (np.abs(to_np(dh) - dh64) <= bh).all(), what
     assert (np.abs(to_np(dw) - dw64) <= bw).all(), what
+
+
+@st.composite
+def linear_grid_cases(draw):
+    return dict(n=draw(st.integers(129, 1100)), h=draw(st.sampled_from([64, 128])),
+                v=draw(st.integers(20000, 70000)), ent=draw(st.booleans()),
+                n_ign=draw(st.integers(0, 40)), seed=draw(st.integers(0, 2 ** 30)))
+
+
+@_settings(12)
+@given(linear_grid_cases())
+def test_fuzz_linear_grids(c):
+    """The 256-row kernel on grids of several hundred to about 1400 tiles:
+    XCD ranges of unequal length, tiles handed out at run time, and (when the
+    final round would be at most a quarter full) the last vocabulary blocks
+    on the 64-row tile.  Sampled rows against the oracle; every row's bits
+    equal to the row alone, and to the prepared-weight call."""
+    n, h, v = c["n"], c["h"], c["v"]
+    hid = synth.normal_matrix(n, h, 1.0, torch.bfloat16, seed=c["seed"]).to(dev())
+    w = synth.normal_matrix(v, h, 0.05, torch.bfloat16, seed=c["seed"] + 1).to(dev())
+    ign = torch.randperm(n, generator=torch.Generator().manual_seed(c["seed"]))[:c["n_ign"]]
+    t = synth.uniform_targets(n, v, seed=c["seed"] + 2, ignore_rows=ign).to(dev())
+    what = str(c)
+    out = itl.linear_logp_fwd(hid, w, t, return_entropy=c["ent"])
+    rows = torch.tensor(sorted({0, n // 3, n // 2, n - 1}), device=dev())
+    ref = oracle.linear_logp_fwd(to_np(hid[rows]), to_np(w), t[rows].cpu().numpy())
+    assert_logp_parity(out[0][rows], out[1][rows], *ref, t[rows], what=what)
+    for r in (0, n - 1):
+        alone = itl.linear_logp_fwd(hid[r:r + 1].contiguous(), w, t[r:r + 1].contiguous(),
+                                    return_entropy=c["ent"])
+        for a, b in zip(out, alone):
+            assert torch.equal(bits(a)[r:r + 1], bits(b)), what
+    prep = itl.linear_logp_fwd(hid, w, t, return_entropy=c["ent"],
+                               prepared_weight=itl.prepare_weight(w))
+    for a, b in zip(out, prep):
+        assert torch.equal(bits(a), bits(b)), what
