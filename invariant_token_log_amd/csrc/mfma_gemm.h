@@ -242,12 +242,134 @@ __device__ __forceinline__ void issue_loads(Stages& sm, const LoaderSrc<ABLK>& s
 // on MFMAs the moment the barrier opens.  Every wave must call with its own
 // role (mainloop does that); acc, the arguments and the result are as for
 // mainloop.
+// Row-major B in pairs of K steps.  A row-major B's 16-row x 32-K block
+// spans half of sixteen 128-byte lines, so each direct load would fetch half
+// lines; here B is staged two K steps at a time instead: 256 rows x 64 K (a
+// "pair slot", row = 128 bytes, chunk c of row r in slot c ^ swzp(r), which
+// keeps the 16 rows of a fragment read on distinct banks), each direct load
+// filling 8 rows x 128 bytes, whole lines.  The 128 KiB of Stages hold A in
+// four K32 slots (elements [0, 32768)) and B in two pair slots ([32768,
+// 65536)).  Loader wave w issues A blocks w + 4u of every step (4 loads) and,
+// on odd steps, rows (w + 4u) * 8 + [0, 8), u < 8, of the B pair two steps
+// ahead (8 loads); the waits below count exactly those.  Same fragments, so
+// the same bits (measured on the bare product: 1.45 -> 1.49 PFLOP/s).
+__device__ __forceinline__ int swzp(int r) { return (r >> 1) & 7; }
+
+template <bool ABLK, bool LOADER>
+__device__ __forceinline__ void mainloop_pairs(Stages& sm, const uint16_t* __restrict__ A,
+                                               int64_t lda, int64_t a_row0, int64_t a_rows,
+                                               const uint16_t* __restrict__ B, int64_t ldb,
+                                               int64_t b_row0, int64_t b_rows, int ksteps,
+                                               f32x4 (&acc)[8][4]) {
+  constexpr int SA = ABLK ? 512 : kK;
+  constexpr int kPairElems = kTile * 2 * kK;   // one pair slot
+  constexpr int kBBase = kStages * kStageElems;  // first pair slot
+  uint16_t* const base = &sm.s[0][0][0];
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int wm = wave / 4, wn = wave % 4;
+  const int li = lane % 16, g = lane / 16;
+  const int lrow = lane / 4;
+  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
+  LoaderSrc<ABLK> sa;
+  const uint16_t* bp[8];
+  if constexpr (LOADER) {
+    sa.init(A, lda, a_row0, a_rows, wave, lrow, lk);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = (wave + 4 * u) * 8 + lane / 8;  // tile row this lane fills
+      bp[u] = B + min(b_row0 + r, b_rows - 1) * ldb + ((lane % 8) ^ swzp(r)) * 8;
+    }
+  }
+  constexpr int kBlk = 16 * kK;  // elements per 1 KiB direct load
+#define ITL_ISSUE_A(SLOT, STEP)                                                                 \
+  if constexpr (LOADER) {                                                                       \
+    const int64_t ka_ = static_cast<int64_t>(STEP) * SA;                                        \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) __builtin_amdgcn_global_load_lds(             \
+        sa.at(u, ka_), base + (SLOT) * kStageElems + (wave + 4 * u) * kBlk, 16, 0, 0);          \
+  }
+#define ITL_ISSUE_B(PSLOT, PAIR)                                                                \
+  if constexpr (LOADER) {                                                                       \
+    const int64_t kb_ = static_cast<int64_t>(PAIR) * 2 * kK;                                    \
+    _Pragma("unroll") for (int u = 0; u < 8; ++u) __builtin_amdgcn_global_load_lds(             \
+        bp[u] + kb_, base + kBBase + (PSLOT) * kPairElems + (wave + 4 * u) * kBlk, 16, 0, 0);   \
+  }
+  const int npairs = ksteps / 2;
+  const int aoff = (wm * 128 + li) * kK + ((g ^ swz(li)) * 8);
+  const int brow = wn * 64 + li;  // + 16 j; swzp(brow + 16 j) == swzp(li)
+  const int bsw = swzp(li);
+  constexpr int NA = LOADER ? 4 : 0, NB = LOADER ? 8 : 0;
+  // Prologue = iterations -4 .. -1: each issues A of step it + 4, the odd ones
+  // also the B pair (it + 3, it + 4).
+  ITL_ISSUE_A(0, 0);
+  ITL_ISSUE_A(1, 1 < ksteps ? 1 : ksteps - 1);
+  ITL_ISSUE_B(0, 0);
+  ITL_ISSUE_A(2, 2 < ksteps ? 2 : ksteps - 1);
+  ITL_ISSUE_A(3, 3 < ksteps ? 3 : ksteps - 1);
+  ITL_ISSUE_B(1, 1 < npairs ? 1 : npairs - 1);
+  wait_vm<2 * NA + NB>();
+  __builtin_amdgcn_s_barrier();
+  bf16x8 xa[8], xb[4], ya[8], yb[4];
+#define ITL_READ(FA, FB, STEP)                                                                  \
+  {                                                                                             \
+    const uint16_t* fa_ = base + ((STEP) % kStages) * kStageElems;                              \
+    const uint16_t* fb_ = base + kBBase + (((STEP) / 2) % 2) * kPairElems;                      \
+    const int ch_ = ((4 * ((STEP) % 2) + g) ^ bsw) * 8;                                         \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
+      FB[j] = *reinterpret_cast<const bf16x8*>(fb_ + (brow + 16 * j) * 2 * kK + ch_);           \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
+      FA[i] = *reinterpret_cast<const bf16x8*>(fa_ + aoff + i * 16 * kK);                       \
+  }
+  ITL_READ(xa, xb, 0)
+  // Even iteration KT: A(KT+1) and the B pair (KT, KT+1), issued at KT-3,
+  // have landed once at most A(KT-2), A(KT-1) and B(KT-1) are in flight; odd
+  // KT: the B pair (KT+1, KT+2), issued at KT-2, once at most A(KT-1) is.
+#define ITL_PSTEP(CA, CB, NXA, NXB, KT, ODD)                                                    \
+  {                                                                                             \
+    if constexpr (ODD)                                                                          \
+      wait_vm_lgkm0<NA>();                                                                      \
+    else                                                                                        \
+      wait_vm_lgkm0<2 * NA + NB>();                                                             \
+    __builtin_amdgcn_s_barrier();                                                               \
+    ITL_ISSUE_A((KT) % kStages, (KT) + kStages < ksteps ? (KT) + kStages : ksteps - 1);         \
+    if constexpr (ODD) {                                                                        \
+      const int p_ = ((KT) + 3) / 2;                                                            \
+      ITL_ISSUE_B(p_ % 2, p_ < npairs ? p_ : npairs - 1);                                       \
+    }                                                                                           \
+    ITL_READ(NXA, NXB, (KT) + 1)                                                                \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0);  \
+    if constexpr (LOADER) __builtin_amdgcn_sched_group_barrier(0x020, ODD ? NA + NB : NA, 0);   \
+    _Pragma("unroll") for (int u = 0; u < 12; ++u) {                                            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                        \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                        \
+    }                                                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                          \
+  }
+  for (int kt = 0; kt < ksteps; kt += 2) {
+    ITL_PSTEP(xa, xb, ya, yb, kt, false)
+    ITL_PSTEP(ya, yb, xa, xb, kt + 1, true)
+  }
+#undef ITL_PSTEP
+#undef ITL_READ
+#undef ITL_ISSUE_B
+#undef ITL_ISSUE_A
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <bool ABLK, bool BBLK, bool LOADER>
 __device__ __forceinline__ void mainloop_role(Stages& sm, const uint16_t* __restrict__ A,
                                               int64_t lda, int64_t a_row0, int64_t a_rows,
                                               const uint16_t* __restrict__ B, int64_t ldb,
                                               int64_t b_row0, int64_t b_rows, int ksteps,
                                               f32x4 (&acc)[8][4]) {
+  if constexpr (!BBLK) {
+    mainloop_pairs<ABLK, LOADER>(sm, A, lda, a_row0, a_rows, B, ldb, b_row0, b_rows, ksteps,
+                                 acc);
+    return;
+  }
   constexpr int SA = ABLK ? 512 : kK, SB = BBLK ? 512 : kK;
   constexpr int NL = LOADER ? kLoaderLoads : 0;  // this wave's loads per step
   const int tid = threadIdx.x;
