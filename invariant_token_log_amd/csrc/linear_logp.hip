@@ -32,6 +32,7 @@
 //     (few rows give little arithmetic per weight byte, so these tiles are
 //     bound by the bytes they keep in flight).
 #include <atomic>
+#include <type_traits>
 
 #include "launch.h"
 #include "logp_device.h"
@@ -430,9 +431,12 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
 // row-major [n, ld_h], mblocks = ceil(n / ROWS) row blocks; the grid covers
 // vocabulary blocks [vb0, vb0 + vtiles).
 // ---------------------------------------------------------------------------
-template <int ROWS>
+// WBLK: the stage ring of mainloop_narrow; row-major weight: the pair slots
+// of mainloop_narrow_pairs.
+template <int ROWS, bool WBLK>
 struct SmemNarrow {
-  gemm::StagesNarrow<ROWS> st;
+  typename std::conditional<WBLK, gemm::StagesNarrow<ROWS>, gemm::StagesNarrowPairs<ROWS>>::type
+      st;
   Reduce<ROWS> rd;
 };
 
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
   constexpr int MI = gemm::NarrowCfg<ROWS>::kMI;
   const Targets targets{tgt, tgt32};
-  __shared__ __align__(16) SmemNarrow<ROWS> sm;
+  __shared__ __align__(16) SmemNarrow<ROWS, WBLK> sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -465,9 +469,13 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int ksteps = static_cast<int>(hdim / BK);
-  gemm::mainloop_narrow<ROWS, WBLK, NTB && WBLK>(sm.st, hidden, ld_h, m0, n, weight,
-                                    WBLK ? static_cast<int64_t>(ksteps) * 512 : ld_w, v0,
-                                    WBLK ? static_cast<int64_t>(vblocks) * BN : v, ksteps, acc);
+  if constexpr (WBLK)
+    gemm::mainloop_narrow<ROWS, true, NTB>(sm.st, hidden, ld_h, m0, n, weight,
+                                           static_cast<int64_t>(ksteps) * 512, v0,
+                                           static_cast<int64_t>(vblocks) * BN, ksteps, acc);
+  else
+    gemm::mainloop_narrow_pairs<ROWS, NTB>(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
+                                           ksteps, acc);
   __syncthreads();
   stats_epilogue<MI, 4, ROWS, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * (ROWS / 2),
                                                           wn * 64, li, g, tid,
@@ -489,15 +497,17 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
   const uint16_t* wn = wblk ? wblk : weight;
   const int64_t ldn = wblk ? 0 : ld_w;
   // once: every weight row is read by one workgroup only (a single row
-  // block), so a prepared weight streams with non-temporal loads
+  // block), so the weight streams with non-temporal loads
   auto narrow = [&](int rows, int mb, int vb0, int vt, bool once) {
     auto kern = rows == 64
                     ? (wblk ? (once ? linear_stats_narrow<64, true, true>
                                     : linear_stats_narrow<64, true, false>)
-                            : linear_stats_narrow<64, false>)
+                            : (once ? linear_stats_narrow<64, false, true>
+                                    : linear_stats_narrow<64, false, false>))
                     : (wblk ? (once ? linear_stats_narrow<128, true, true>
                                     : linear_stats_narrow<128, true, false>)
-                            : linear_stats_narrow<128, false>);
+                            : (once ? linear_stats_narrow<128, false, true>
+                                    : linear_stats_narrow<128, false, false>));
     hipLaunchKernelGGL(kern, dim3(mb * vt), dim3(kDmaThreads), 0, s, hidden, ld_h, wn, ldn, n, h,
                        v, mb, vblocks, vb0, vt, targets.p, targets.is32, ignore, pm, ps, pt, ex);
   };

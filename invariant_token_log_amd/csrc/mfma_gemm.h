@@ -504,6 +504,114 @@ struct StagesNarrow {
   uint16_t b[NarrowCfg<ROWS>::kStages][kTile * kK];  // 16 KiB each
 };
 
+// The narrow tile with a row-major B staged in pairs of K steps, as
+// mainloop_pairs does for the 256-row tile: four A slots of ROWS x 32 and two
+// B pair slots of 256 x 64 (80 KiB for ROWS = 64, one workgroup per CU),
+// every B direct load 8 rows x 128 bytes.  Wave w issues, on odd steps, rows
+// (w + 8u) * 8 + [0, 8), u < 4, of the B pair two steps ahead and, for w <
+// ROWS / 16, A block w of every step.  NTB: the B loads carry the
+// non-temporal hint (B read by this workgroup only).
+template <int ROWS>
+struct StagesNarrowPairs {
+  uint16_t a[4][ROWS * kK];
+  uint16_t b[2][kTile * 2 * kK];  // 32 KiB each
+};
+
+template <int ROWS, bool NTB>
+__device__ __forceinline__ void mainloop_narrow_pairs(StagesNarrowPairs<ROWS>& sm,
+                                                      const uint16_t* __restrict__ A, int64_t lda,
+                                                      int64_t a_row0, int64_t a_rows,
+                                                      const uint16_t* __restrict__ B, int64_t ldb,
+                                                      int64_t b_row0, int64_t b_rows, int ksteps,
+                                                      f32x4 (&acc)[ROWS / 32][4]) {
+  constexpr int MI = ROWS / 32;
+  constexpr int kAux = NTB ? 2 : 0;  // cache policy: 2 = non-temporal
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int wm = wave / 4, wn = wave % 4;
+  const int li = lane % 16, g = lane / 16;
+  const int lrow = lane / 4;
+  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
+  const bool has_a = wave < ROWS / 16;  // uniform
+  const uint16_t* a0 = A + min(a_row0 + (has_a ? wave : 0) * 16 + lrow, a_rows - 1) * lda + lk;
+  const uint16_t* bp[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = (wave + 8 * u) * 8 + lane / 8;  // tile row this lane fills
+    bp[u] = B + min(b_row0 + r, b_rows - 1) * ldb + ((lane % 8) ^ swzp(r)) * 8;
+  }
+  constexpr int kBlk = 16 * kK;  // elements per 1 KiB direct load
+  auto issue_a = [&](int slot, int step) {
+    if (has_a)
+      __builtin_amdgcn_global_load_lds(a0 + static_cast<int64_t>(step) * kK,
+                                       sm.a[slot] + wave * kBlk, 16, 0, 0);
+  };
+  auto issue_b = [&](int pslot, int pair) {
+    const int64_t kb = static_cast<int64_t>(pair) * 2 * kK;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_global_load_lds(bp[u] + kb, sm.b[pslot] + (wave + 8 * u) * kBlk, 16, 0,
+                                       kAux);
+  };
+  const int npairs = ksteps / 2;
+  const int aoff = (wm * (ROWS / 2) + li) * kK + ((g ^ swz(li)) * 8);
+  const int brow = wn * 64 + li;
+  const int bsw = swzp(li);
+  // Prologue = iterations -4 .. -1 (A of step it + 4; odd: B pair it + 3, it + 4).
+  issue_a(0, 0);
+  issue_a(1, 1 < ksteps ? 1 : ksteps - 1);
+  issue_b(0, 0);
+  issue_a(2, 2 < ksteps ? 2 : ksteps - 1);
+  issue_a(3, 3 < ksteps ? 3 : ksteps - 1);
+  issue_b(1, 1 < npairs ? 1 : npairs - 1);
+  if (has_a)
+    wait_vm<2 + 4>();
+  else
+    wait_vm<4>();
+  __builtin_amdgcn_s_barrier();
+  bf16x8 xa[MI], xb[4], ya[MI], yb[4];
+  auto read_frags = [&](bf16x8 (&fa)[MI], bf16x8 (&fb)[4], int step) {
+    const uint16_t* fa_ = sm.a[step % 4];
+    const uint16_t* fb_ = sm.b[(step / 2) % 2];
+    const int ch = ((4 * (step % 2) + g) ^ bsw) * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8*>(fb_ + (brow + 16 * j) * 2 * kK + ch);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8*>(fa_ + aoff + i * 16 * kK);
+  };
+  read_frags(xa, xb, 0);
+  // Even KT: A(KT+1) and the pair (KT, KT+1), issued at KT-3, have landed
+  // once at most A(KT-2), A(KT-1), B(KT-1) are in flight; odd KT: the pair
+  // (KT+1, KT+2), issued at KT-2, once at most A(KT-1) is.
+#define ITL_NPSTEP(CA, CB, NXA, NXB, KT, ODD)                                                   \
+  {                                                                                             \
+    if (has_a) {                                                                                \
+      if constexpr (ODD) wait_vm_lgkm0<1>(); else wait_vm_lgkm0<2 + 4>();                       \
+    } else {                                                                                    \
+      if constexpr (ODD) wait_vm_lgkm0<0>(); else wait_vm_lgkm0<4>();                           \
+    }                                                                                           \
+    __builtin_amdgcn_s_barrier();                                                               \
+    issue_a((KT) % 4, (KT) + 4 < ksteps ? (KT) + 4 : ksteps - 1);                               \
+    if constexpr (ODD) {                                                                        \
+      const int p_ = ((KT) + 3) / 2;                                                            \
+      issue_b(p_ % 2, p_ < npairs ? p_ : npairs - 1);                                           \
+    }                                                                                           \
+    read_frags(NXA, NXB, (KT) + 1);                                                             \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                              \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0);  \
+  }
+  for (int kt = 0; kt < ksteps; kt += 2) {
+    ITL_NPSTEP(xa, xb, ya, yb, kt, false)
+    ITL_NPSTEP(ya, yb, xa, xb, kt + 1, true)
+  }
+#undef ITL_NPSTEP
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // acc += A[a_row0 + 0..ROWS-1, 0..K) * B[b_row0 + 0..255, 0..K)^T, K =
 // ksteps * 32 (ksteps even, >= 2); A row-major, B row-major or K32-blocked
 // (BBLK, ldb = distance between 16-row blocks); rows at or past a_rows /
