@@ -47,9 +47,6 @@ KERNEL_SOURCES = {
     "linear_dz_saved_kernel": ["invariant_token_log_amd/csrc/linear_bwd.hip",
                                "invariant_token_log_amd/csrc/mfma_gemm.h",
                                "invariant_token_log_amd/csrc/logp_device.h"],
-    "transpose_blocked": ["invariant_token_log_amd/csrc/linear_bwd.hip",
-                          "invariant_token_log_amd/csrc/mfma_gemm.h",
-                          "invariant_token_log_amd/csrc/logp_device.h"],
 }
 # The fused backward at N = H = 4096, V = 151936 with 204 rows ignored and the
 # default vocabulary chunk (32768 columns: 5 chunks over Vp = 152064).
@@ -761,15 +758,12 @@ def _algorithmic_bytes(workload, kernel):
         return v * h * 2 + n * h * 2 + n * 16
     if workload == "qwen3_4096x4096x151936_bwd_saved":
         # per launch, averaged over one backward's launches: the saved-logits
-        # dz kernel reads the active rows' fp32 logits and writes dz_c and
-        # dz_c^T (bf16, padded to Vp columns) once per chunk; the transpose
-        # reads W and writes W^T_c per chunk, then h -> h^T once
-        n, h, v, vp = 4096, 4096, 151936, 152064
+        # dz kernel reads the active rows' fp32 logits and writes dz_c (bf16,
+        # padded to Vp columns) once per chunk
+        n, v, vp = 4096, 151936, 152064
         act = n - int(0.05 * n)
         if kernel == "linear_dz_saved_kernel":
-            return (act * v * 4 + 2 * n * vp * 2) // LINEAR_BWD_CHUNKS
-        if kernel == "transpose_blocked":
-            return (v * h * 2 + vp * h * 2 + 2 * n * h * 2) // (LINEAR_BWD_CHUNKS + 1)
+            return (act * v * 4 + n * vp * 2) // LINEAR_BWD_CHUNKS
     raise ValueError((workload, kernel))
 
 
@@ -908,7 +902,7 @@ def main():
                   "fwd": ("qwen3_4096x151936", ["logp_fwd_fused_kernel"]),
                   "linear": ("qwen3_4096x4096x151936", ["linear_stats_dma"]),
                   "linear_bwd_saved": ("qwen3_4096x4096x151936_bwd_saved",
-                                       ["linear_dz_saved_kernel", "transpose_blocked"]),
+                                       ["linear_dz_saved_kernel"]),
                   }[args.workload]
         for p in summarize_traffic(*args.summarize_traffic, wl, ks, *args.pmc_commands):
             print(p)

@@ -311,13 +311,13 @@ enum logp_bwd_flags {
  * Workspace of linear_logp_bwd in bytes for a call with these options
  * (flags: logp_bwd_flags of the call) and vocabulary chunk (vocab_chunk: as
  * linear_logp_bwd's).  The backward walks the vocabulary in chunks, so the
- * workspace holds one chunk's dz and dz^T (bf16, [Np, C] and [C, Np]), the
- * chunk's W^T (bf16 [h, C], none with a prepared weight), a re-laid copy of
- * hidden ([Np, h], none with saved logits), hidden^T ([h, Np], only for
- * dweight) and, for bf16 dhidden over several chunks, the fp32 dhidden
- * between chunks ([n, h]); Np = n rounded up to 256, C = the chunk width.
- * About 0.87 GB at n = h = 4096, v = 151936 with the default chunk and both
- * outputs (0.60 GB with a prepared weight).  0 when n = 0 or for arguments
+ * workspace holds one chunk's dz (bf16 [Np, C]; both products read it), a
+ * re-laid copy of hidden ([Np, h], none with saved logits), hidden^T ([h,
+ * Np], only for dweight) and, for bf16 dhidden over several chunks, the fp32
+ * dhidden between chunks ([n, h]); Np = n rounded up to 256, C = the chunk
+ * width.  The weight is read where it is (or from the prepared buffer).
+ * About 0.34 GB at n = h = 4096, v = 151936 with the default chunk and both
+ * outputs, prepared weight or not.  0 when n = 0 or for arguments
  * linear_logp_bwd would reject.
  */
 size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t tile_width,
@@ -360,13 +360,13 @@ size_t linear_logp_bwd_workspace_bytes(int64_t n, int64_t h, int64_t v, int32_t 
  *               LOGP_ROUND_BF16 (where the bf16 logits are exactly z);
  *               otherwise LOGP_ERR_DTYPE.
  *   prepared, prepared_bytes
- *               NULL: the backward transposes weight into the workspace for
- *               dhidden.  Otherwise linear_logp_prepare_weight's buffer for
- *               this weight (short: LOGP_ERR_SHAPE; not 16-byte aligned:
- *               LOGP_ERR_ALIGN), read instead: the same values, so the same
- *               bits, without the transpose (the prepared weight is reused
- *               while the weight does not change, e.g. over the micro-batches
- *               of one optimiser step).
+ *               NULL: the backward reads weight as it is.  Otherwise
+ *               linear_logp_prepare_weight's buffer for this weight (short:
+ *               LOGP_ERR_SHAPE; not 16-byte aligned: LOGP_ERR_ALIGN), read
+ *               instead: the same values, so the same bits, in layouts that
+ *               load faster (the prepared weight is reused while the weight
+ *               does not change, e.g. over the micro-batches of one
+ *               optimiser step).
  *   lse         fp32 [n] from linear_logp_fwd.
  *   grad_logp   fp32 [n], the upstream gradient g.
  *   entropy, grad_entropy

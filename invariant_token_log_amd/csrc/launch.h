@@ -70,16 +70,17 @@ int xcd_cus();
 
 // Fused LM-head backward.  The vocabulary is walked in chunks of vc columns
 // (a multiple of 256; kDefaultChunk unless the caller asks for another), so
-// the workspace holds one chunk's dz_c [np, vc] and dz_c^T [vc, np], W^T_c
-// [h, vc] (no prepared weight), the blocked hidden rows [np, h] (logits
-// recomputed), h^T [h, np] (dW), and the fp32 dh [n, h] between chunks (bf16
-// dh over several chunks); only the regions the call uses (flags).  Byte
+// the workspace holds one chunk's dz_c [np, vc] and dz_c^T [vc, np], the
+// blocked hidden rows [np, h] (logits recomputed), h^T [h, np] (dW), and the
+// fp32 dh [n, h] between chunks (bf16 dh over several chunks); only the
+// regions the call uses (flags).  The weight needs no copy: dh reads it as
+// it is, as a K-outer operand (or the prepared transpose).  Byte
 // offsets, -1 for a region not used; np, vp = n, v rounded up to 256.
 constexpr int64_t kDefaultChunk = 32768;
 enum { kBwdDhidden = 1, kBwdDweight = 2, kBwdPrepared = 4, kBwdSaved = 8, kBwdBf16Out = 16 };
 struct LinearBwdLayout {
   int64_t np, vp, vc;
-  int64_t hb, ht, dz, dzt, wt, dh32, total;
+  int64_t hb, ht, dz, dh32, total;
 };
 int64_t linear_bwd_chunk(int64_t v, int64_t vocab_chunk);
 LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v, int32_t flags,

@@ -17,7 +17,7 @@
 //
 // The vocabulary is walked in chunks of whole 256-column tiles (the
 // caller's vocab_chunk, default kDefaultChunk columns); per chunk [c0, c1):
-//   dz_c, dz_c^T = the chunk's columns of dz (recomputed tiles, or the saved
+//   dz_c         = the chunk's columns of dz (recomputed tiles, or the saved
 //                  logits);
 //   dW[c0:c1]    = dz_c^T h        (K = all tokens, ascending: final rows);
 //   dh          += dz_c W[c0:c1]   (K = the chunk's vocabulary, ascending,
@@ -30,18 +30,20 @@
 // Kernels (the products on the 256 x 256 tile of mfma_gemm.h):
 //   block_rows_bf16   : h [N, H] -> the K32-blocked copy the recomputed
 //                       product reads;
-//   linear_dz_kernel  : h x W^T tile of one chunk -> dz in registers ->
-//                       transposed, then row-major LDS tile -> dz_c^T and dz_c;
-//   linear_dz_saved_kernel: the same dz_c and dz_c^T from saved logits, 32 x
-//                       256 tiles through LDS;
-//   transpose_blocked : W[c0:c1] -> W^T_c [H, c1 - c0], h -> h^T [H, Np]
-//                       (32 x 256 tiles through LDS);
+//   linear_dz_kernel  : h x W^T tile of one chunk -> dz in registers -> LDS
+//                       tile -> dz_c;
+//   linear_dz_saved_kernel: the same dz_c from saved logits, 32 x 256 tiles
+//                       through LDS;
+//   transpose_blocked : h -> h^T [H, Np] (32 x 256 tiles through LDS);
 //   gemm_out_kernel   : C = A B^T (+ stored C) with fp32 or RNE-bf16 output.
-// Every operand the backward writes for a product (dz_c, dz_c^T, W^T_c, h^T
-// and the blocked h) is in the K32-blocked layout of mfma_gemm.h: the same
-// values, read with whole-line loads.  Np, Vp are N and V rounded up to
-// multiples of 256; padded rows and columns hold zeros and add exact zeros to
-// the K walks.
+// The operands the backward writes for a product (dz_c, h^T and the blocked
+// h) are in the K32-blocked layout of mfma_gemm.h; the two operands whose K
+// index is the outer one are read as they are, through mfma_gemm.h's
+// K-outer staging (transposed LDS reads, same fragments, same bits): the
+// weight rows W[c0:c1] for dh, and dz_c along its token axis for dW.  Np, Vp
+// are N and V rounded up to multiples of 256; padded rows and columns hold
+// zeros and add exact zeros to the K walks (a K-outer operand's lines past
+// its data read a zero line).
 #include "launch.h"
 #include "logp_device.h"
 #include "mfma_gemm.h"
@@ -181,8 +183,8 @@ struct SmemDz {
 };
 
 // dz of the vocabulary chunk of vcb 256-column blocks starting at block vb0:
-// dz_c [Np, K = vcb * 256] and dz_c^T [vcb * 256, K = Np], both K32-blocked
-// with the chunk's own columns (either may be null: not stored).  hidden
+// dz_c [Np, K = vcb * 256], K32-blocked with the chunk's own columns (the
+// product over tokens reads it along its other axis).  hidden
 // K32-blocked (mblocks * 256 rows); weight row-major, or K32-blocked with
 // vblocks * 256 rows when WBLK (a prepared weight).  PLAIN: launched only
 // when no option is on (no rounding, T = 1, no entropy term), so the
@@ -194,8 +196,7 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
     int vcb, const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse,
     const float* __restrict__ grad, float inv_t, int32_t round_bf16,
-    const float* __restrict__ ent, const float* __restrict__ gent, uint16_t* __restrict__ dz,
-    uint16_t* __restrict__ dzt) {
+    const float* __restrict__ ent, const float* __restrict__ gent, uint16_t* __restrict__ dz) {
   const Targets targets{tgt, tgt32};
   __shared__ __align__(16) SmemDz sm;
   const int tid = threadIdx.x;
@@ -245,9 +246,8 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   __syncthreads();
 
   // dz of every element (dz_value; 0 on ignored / padded rows and columns),
-  // rounded to bf16.  Lane (li, g) holds rows 4g .. 4g+3 of each 16 x 16
-  // block, so its four values of a column pack into 8 contiguous bytes of the
-  // transposed tile.
+  // rounded to bf16; lane (li, g) holds rows 4g .. 4g+3 of column li of each
+  // 16 x 16 block, packed in pairs.
   const bool scaled = inv_t != 1.0f;
   const bool with_ent = ent != nullptr;
   uint32_t dv[8][4][2];
@@ -281,30 +281,8 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
       dv[i][j][1] = static_cast<uint32_t>(b[2]) | (static_cast<uint32_t>(b[3]) << 16);
     }
   }
-  // dz^T: tile[c][r] (column-major), then out in K32-blocked order: 128
-  // pieces of 16 rows x 32 tokens, one contiguous KiB each.
-  const int64_t np_steps = static_cast<int64_t>(mblocks) * (kT / gemm::kK);
   const int64_t vc_steps = static_cast<int64_t>(vcb) * (kT / gemm::kK);
-  if (dzt) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int lc = wn * 64 + j * 16 + li;
-        const int lr = wm * 128 + i * 16 + 4 * g;
-        *reinterpret_cast<uint2*>(&sm.u.tile[lc][lr]) = make_uint2(dv[i][j][0], dv[i][j][1]);
-      }
-    __syncthreads();
-    for (int idx = tid; idx < kT * 32; idx += gemm::kThreads) {
-      const int piece = idx >> 6, e = idx & 63;
-      const int c = (piece >> 3) * 16 + (e >> 2), r = (piece & 7) * 32 + (e & 3) * 8;
-      store_stream(dzt + gemm::kblocked_index(vl0 + c, m0 + r, np_steps),
-                   *reinterpret_cast<const uint4*>(&sm.u.tile[c][r]));
-    }
-    __syncthreads();
-  }
-  if (!dz) return;
-  // dz: tile[r][c] (row-major), then out in K32-blocked order.
+  // tile[r][c] (row-major), then out in K32-blocked order.
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -325,26 +303,22 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
   }
 }
 
-// dz_c and dz_c^T of the vocabulary chunk [c0, c0 + cols_p) from the
-// forward's saved unscaled logits (fp32, or bf16 with ZBF16; [n, ld_z],
-// 16-byte aligned rows) instead of the recomputed product: the same values
-// through the same dz_value, so the same bits.  Tiles of 32 rows x 256
-// chunk columns: the logits of a row segment come in as 16-byte non-temporal
-// loads of whole 512-byte (bf16) or 1 KiB (fp32) pieces, the bf16 dz goes
-// to an LDS tile, and leaves as 1 KiB K32-blocked pieces: along the rows for
-// dz_c [Np, K = cols_p], transposed for dz_c^T [cols_p, K = Np] (either may
-// be null: not stored).  Rows past n or ignored, and columns past v, get 0
-// without reading the logits.  Grid: x = row tiles, y = column tiles
-// (grid-stride beyond gridDim.y): neighbouring workgroups take neighbouring
-// 32-row tiles, so each one's dz_c^T pieces continue the previous one's in
-// memory.
+// dz_c of the vocabulary chunk [c0, c0 + cols_p) from the forward's saved
+// unscaled logits (fp32, or bf16 with ZBF16; [n, ld_z], 16-byte aligned
+// rows) instead of the recomputed product: the same values through the same
+// dz_value, so the same bits.  Tiles of 32 rows x 256 chunk columns: the
+// logits of a row segment come in as 16-byte non-temporal loads of whole
+// 512-byte (bf16) or 1 KiB (fp32) pieces, the bf16 dz goes to an LDS tile and
+// leaves as 1 KiB K32-blocked pieces of dz_c [Np, K = cols_p].  Rows past n
+// or ignored, and columns past v, get 0 without reading the logits.  Grid:
+// x = row tiles, y = column tiles (grid-stride beyond gridDim.y).
 template <bool ZBF16>
 __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
-    const void* __restrict__ zsaved, int64_t ld_z, int64_t n, int64_t v, int64_t np_rows,
+    const void* __restrict__ zsaved, int64_t ld_z, int64_t n, int64_t v,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse, const float* __restrict__ grad, float inv_t,
     int32_t round_bf16, const float* __restrict__ ent, const float* __restrict__ gent,
-    int64_t c0, int64_t cols_p, uint16_t* __restrict__ dz, uint16_t* __restrict__ dzt) {
+    int64_t c0, int64_t cols_p, uint16_t* __restrict__ dz) {
   const Targets targets{tgt, tgt32};
   __shared__ __align__(16) uint16_t tile[kTR][kTS];
   __shared__ float rowc[kTR][4];  // lse, g, entropy, -gH of each tile row
@@ -356,7 +330,7 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
   constexpr int E = ZBF16 ? 8 : 4;         // elements per 16-byte chunk
   constexpr int CPR = kTC / E;             // chunks per tile row
   constexpr int RPS = 256 / CPR;           // tile rows per step of the block
-  const int64_t vc_steps = cols_p / gemm::kK, np_steps = np_rows / gemm::kK;
+  const int64_t vc_steps = cols_p / gemm::kK;
   for (int64_t cl0 = static_cast<int64_t>(blockIdx.y) * kTC; cl0 < cols_p;
        cl0 += static_cast<int64_t>(gridDim.y) * kTC) {
     const int64_t col0 = c0 + cl0;  // vocabulary column of the tile
@@ -444,19 +418,16 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
       }
     }
     __syncthreads();
-    if (dz) {
-      // along the rows: pieces (16-row block rb, K step ks) of the tile
+    // pieces (16-row block rb, K step ks) of the tile
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int q = tid + 256 * u;
-        const int p = q >> 6, e = q & 63;
-        const int rb = p >> 3, ks = p & 7;
-        const int r = rb * 16 + (e >> 2), c = ks * 32 + (e & 3) * 8;
-        store_stream(dz + gemm::kblocked_index(r0 + r, cl0 + c, vc_steps),
-                     *reinterpret_cast<const uint4*>(&tile[r][c]));
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + 256 * u;
+      const int p = q >> 6, e = q & 63;
+      const int rb = p >> 3, ks = p & 7;
+      const int r = rb * 16 + (e >> 2), c = ks * 32 + (e & 3) * 8;
+      store_stream(dz + gemm::kblocked_index(r0 + r, cl0 + c, vc_steps),
+                   *reinterpret_cast<const uint4*>(&tile[r][c]));
     }
-    if (dzt) store_transposed(tile, dzt, cl0, kTC, r0, np_steps, tid);
     __syncthreads();
   }
 }
@@ -469,47 +440,54 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
 // One role's share of the tile (gemm::mainloop_role): each role runs its
 // own copy from the accumulator load to the store, so that no accumulator
 // crosses the branch between the two loop bodies.
-template <bool BF16OUT, bool LOADER>
+template <bool BF16OUT, bool LOADER, int AF, int BF>
 __device__ __forceinline__ void gemm_out_tile(gemm::Stages& st, const uint16_t* __restrict__ A,
-                                              int64_t lda, int64_t arows,
+                                              int64_t lda, int64_t arows, int a_kvalid,
                                               const uint16_t* __restrict__ B, int64_t ldb,
-                                              int64_t brows, int ksteps, int64_t m0, int64_t n0,
-                                              int64_t m_out, int64_t n_out, const float* Cin,
-                                              int64_t ldcin, void* C, int64_t ldc) {
+                                              int64_t brows, int b_kvalid, int ksteps, int64_t m0,
+                                              int64_t n0, int64_t m_out, int64_t n_out,
+                                              const float* Cin, int64_t ldcin, void* C,
+                                              int64_t ldc) {
+  constexpr int MI = 8, NJ = 4, WM = 128, WN = 64;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 4, wn = wave % 4;
   const int li = lane % 16, g = lane / 16;
-  f32x4 acc[8][4];
+  f32x4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (Cin) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + wm * 128 + i * 16 + 4 * g + q;
+        const int64_t row = m0 + wm * WM + i * 16 + 4 * g + q;
         if (row >= m_out) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t col = n0 + wn * 64 + j * 16 + li;
+        for (int j = 0; j < NJ; ++j) {
+          const int64_t col = n0 + wn * WN + j * 16 + li;
           if (col < n_out) acc[i][j][q] = Cin[row * ldcin + col];
         }
       }
   }
-  gemm::mainloop_role<true, true, LOADER>(st, A, lda, m0, arows, B, ldb, n0, brows, ksteps, acc);
+  if constexpr (AF != gemm::kKContig || BF != gemm::kKContig)
+    gemm::mainloop_ko<AF, BF, LOADER>(st, A, lda, m0, arows, a_kvalid, B, ldb, n0, brows,
+                                      b_kvalid, ksteps, acc);
+  else
+    gemm::mainloop_role<true, true, LOADER>(st, A, lda, m0, arows, B, ldb, n0, brows, ksteps,
+                                            acc);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t row = m0 + wm * 128 + i * 16 + 4 * g + q;
+      const int64_t row = m0 + wm * WM + i * 16 + 4 * g + q;
       if (row >= m_out) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = n0 + wn * 64 + j * 16 + li;
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t col = n0 + wn * WN + j * 16 + li;
         if (col < n_out) {
           if (BF16OUT)
             static_cast<uint16_t*>(C)[row * ldc + col] = bf16_bits(acc[i][j][q]);
@@ -520,22 +498,27 @@ __device__ __forceinline__ void gemm_out_tile(gemm::Stages& st, const uint16_t* 
     }
 }
 
-template <bool BF16OUT>
+// AF / BF: the operand's form (mfma_gemm.h: K32-blocked, or K-outer with
+// its ld and kvalid = the lines that hold data).
+template <bool BF16OUT, int AF, int BF>
 __global__ __launch_bounds__(gemm::kThreads) void gemm_out_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, int64_t arows, const uint16_t* __restrict__ B,
-    int64_t ldb, int64_t brows, int ksteps, int mblocks, int nblocks, int64_t m_out,
-    int64_t n_out, const float* Cin, int64_t ldcin, void* C, int64_t ldc) {
+    const uint16_t* __restrict__ A, int64_t lda, int64_t arows, int a_kvalid,
+    const uint16_t* __restrict__ B, int64_t ldb, int64_t brows, int b_kvalid, int ksteps,
+    int mblocks, int nblocks, int64_t m_out, int64_t n_out, const float* Cin, int64_t ldcin,
+    void* C, int64_t ldc) {
   __shared__ __align__(16) gemm::Stages st;
   int mb, nb;
   gemm::tile_coords(gemm::xcd_logical(blockIdx.x, mblocks * nblocks), mblocks, nblocks, mb, nb);
   const int64_t m0 = static_cast<int64_t>(mb) * kT;
   const int64_t n0 = static_cast<int64_t>(nb) * kT;
   if (gemm::loader_wave())
-    gemm_out_tile<BF16OUT, true>(st, A, lda, arows, B, ldb, brows, ksteps, m0, n0, m_out, n_out,
-                                 Cin, ldcin, C, ldc);
+    gemm_out_tile<BF16OUT, true, AF, BF>(st, A, lda, arows, a_kvalid, B, ldb, brows,
+                                             b_kvalid, ksteps, m0, n0, m_out, n_out, Cin, ldcin,
+                                             C, ldc);
   else
-    gemm_out_tile<BF16OUT, false>(st, A, lda, arows, B, ldb, brows, ksteps, m0, n0, m_out, n_out,
-                                  Cin, ldcin, C, ldc);
+    gemm_out_tile<BF16OUT, false, AF, BF>(st, A, lda, arows, a_kvalid, B, ldb, brows,
+                                              b_kvalid, ksteps, m0, n0, m_out, n_out, Cin, ldcin,
+                                              C, ldc);
 }
 
 // Zero rows x cols of C (a sum over no tokens).
@@ -570,22 +553,30 @@ void launch_transpose(const uint16_t* src, int64_t ld, int64_t rows, int64_t row
                      rows_p, cols, dst);
 }
 
-// C = A B^T (+ Cin), A [arows, k] and B [brows, k] K32-blocked with 16-row
-// block strides lda, ldb (elements).
-void launch_gemm(bool bf16, const uint16_t* A, int64_t lda, int64_t arows, const uint16_t* B,
-                 int64_t ldb, int64_t brows, int64_t k, int64_t m_out, int64_t n_out,
-                 const float* cin, int64_t ldcin, void* C, int64_t ldc, hipStream_t s) {
+// C = A B^T (+ Cin), A [arows, k] and B [brows, k] in the forms af / bf
+// (mfma_gemm.h): K32-blocked with 16-row block strides lda, ldb (elements),
+// or K-outer with their ld and a_kvalid / b_kvalid lines holding data.
+void launch_gemm(bool bf16, int af, const uint16_t* A, int64_t lda, int64_t arows, int64_t a_kvalid,
+                 int bf, const uint16_t* B, int64_t ldb, int64_t brows, int64_t b_kvalid,
+                 int64_t k, int64_t m_out, int64_t n_out, const float* cin, int64_t ldcin,
+                 void* C, int64_t ldc, hipStream_t s) {
   const int mblocks = static_cast<int>((m_out + kT - 1) / kT);
   const int nblocks = static_cast<int>((n_out + kT - 1) / kT);
   const int ksteps = static_cast<int>(k / gemm::kK);
-  if (bf16)
-    hipLaunchKernelGGL(gemm_out_kernel<true>, dim3(mblocks * nblocks), dim3(gemm::kThreads), 0, s,
-                       A, lda, arows, B, ldb, brows, ksteps, mblocks, nblocks, m_out, n_out, cin,
-                       ldcin, C, ldc);
-  else
-    hipLaunchKernelGGL(gemm_out_kernel<false>, dim3(mblocks * nblocks), dim3(gemm::kThreads), 0,
-                       s, A, lda, arows, B, ldb, brows, ksteps, mblocks, nblocks, m_out, n_out, cin,
-                       ldcin, C, ldc);
+  const int akv = static_cast<int>(a_kvalid), bkv = static_cast<int>(b_kvalid);
+#define ITL_GEMM(BF16, AF, BF)                                                                   \
+  hipLaunchKernelGGL((gemm_out_kernel<BF16, AF, BF>), dim3(mblocks * nblocks),                   \
+                     dim3(gemm::kThreads), 0, s, A, lda, arows, akv, B, ldb, brows, bkv, ksteps, \
+                     mblocks, nblocks, m_out, n_out, cin, ldcin, C, ldc)
+  constexpr int KC = gemm::kKContig, KO = gemm::kKOuter, KB = gemm::kKOuterBlocked;
+  if (af == KC && bf == KC) {
+    if (bf16) ITL_GEMM(true, KC, KC); else ITL_GEMM(false, KC, KC);
+  } else if (af == KC && bf == KO) {
+    if (bf16) ITL_GEMM(true, KC, KO); else ITL_GEMM(false, KC, KO);
+  } else {  // af == KB, bf == KC
+    if (bf16) ITL_GEMM(true, KB, KC); else ITL_GEMM(false, KB, KC);
+  }
+#undef ITL_GEMM
 }
 
 }  // namespace
@@ -599,7 +590,7 @@ int64_t linear_bwd_chunk(int64_t v, int64_t vocab_chunk) {
 LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v, int32_t flags,
                                   int64_t vocab_chunk) {
   const bool need_dh = flags & kBwdDhidden, need_dw = flags & kBwdDweight;
-  const bool prepared = flags & kBwdPrepared, saved = flags & kBwdSaved;
+  const bool saved = flags & kBwdSaved;
   LinearBwdLayout l;
   l.np = round_tile(n);
   l.vp = round_tile(v);
@@ -615,9 +606,7 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v, int32_t flags
   };
   l.hb = take(!saved, l.np * h * 2);                      // blocked h for the recompute
   l.ht = take(need_dw, h * l.np * 2);                     // h^T for dW
-  l.dz = take(need_dh, l.np * l.vc * 2);                  // dz_c for dh
-  l.dzt = take(need_dw, l.vc * l.np * 2);                 // dz_c^T for dW
-  l.wt = take(need_dh && !prepared, h * l.vc * 2);        // W^T_c for dh
+  l.dz = take(need_dh || need_dw, l.np * l.vc * 2);       // dz_c for dh and dW
   l.dh32 = take(need_dh && (flags & kBwdBf16Out) && nchunks > 1,
                 n * h * 4);                               // fp32 dh between chunks
   l.total = off;
@@ -651,8 +640,6 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
   uint16_t* hb = at(l.hb);
   uint16_t* ht = at(l.ht);
   uint16_t* dz = at(l.dz);
-  uint16_t* dzt = at(l.dzt);
-  uint16_t* wt = at(l.wt);
   float* dh32 = l.dh32 < 0 ? nullptr : reinterpret_cast<float*>(ws + l.dh32);
   const int mblocks = static_cast<int>(l.np / kT), vblocks = static_cast<int>(l.vp / kT);
   const int64_t hsteps = h / gemm::kK, npsteps = l.np / gemm::kK, vpsteps = l.vp / gemm::kK;
@@ -666,12 +653,12 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
     const int64_t cols = c1 - c0, csteps = cols / gemm::kK;
     const int vb0 = static_cast<int>(c0 / kT), vcb = static_cast<int>(cols / kT);
     const bool first = c0 == 0, last = c1 == l.vp;
-    // dz_c and dz_c^T of the chunk's columns
+    // dz_c of the chunk's columns
     if (!zsaved) {
 #define ITL_DZ(WB, PL)                                                                            \
   hipLaunchKernelGGL((linear_dz_kernel<WB, PL>), dim3(mblocks * vcb), dim3(gemm::kThreads), 0,   \
                      s, hb, ld_h, wop, ldw, n, h, v, mblocks, vblocks, vb0, vcb, targets.p,      \
-                     targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz, dzt)
+                     targets.is32, ignore, lse, grad, inv_t, round_bf16, ent, gent, dz)
       if (prepared) {
         if (plain) ITL_DZ(true, true); else ITL_DZ(true, false);
       } else {
@@ -683,18 +670,19 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
       const dim3 grid(static_cast<unsigned>(l.np / kTR), static_cast<unsigned>(ct < 65535 ? ct : 65535));
       if (z_bf16)
         hipLaunchKernelGGL(linear_dz_saved_kernel<true>, grid, dim3(256), 0, s, zsaved, ld_z, n, v,
-                           l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
-                           ent, gent, c0, cols, dz, dzt);
+                           targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16, ent,
+                           gent, c0, cols, dz);
       else
         hipLaunchKernelGGL(linear_dz_saved_kernel<false>, grid, dim3(256), 0, s, zsaved, ld_z, n,
-                           v, l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
-                           ent, gent, c0, cols, dz, dzt);
+                           v, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16, ent,
+                           gent, c0, cols, dz);
     }
-    // dW[c0, c1) = dz_c^T h: K = every token, ascending (final rows)
+    // dW[c0, c1) = dz_c^T h: K = every token, ascending (final rows); dz_c
+    // read along its token axis (K-outer)
     if (dw && c0 < v) {
       const int64_t rows = (c1 < v ? c1 : v) - c0;
-      launch_gemm(bf16_out, dzt, npsteps * 512, cols, ht, npsteps * 512, h, l.np, rows, h,
-                  nullptr, 0,
+      launch_gemm(bf16_out, gemm::kKOuterBlocked, dz, csteps, cols, l.np, gemm::kKContig, ht,
+                  npsteps * 512, h, -1, l.np, rows, h, nullptr, 0,
                   static_cast<char*>(dw) + c0 * ld_dw * (bf16_out ? 2 : 4), ld_dw, s);
     }
     // dh += dz_c W[c0, c1): K = the chunk's vocabulary, continuing the fp32
@@ -706,19 +694,18 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
       if (prepared) {  // the prepared W^T [h, Vp]: columns [c0, c1)
         wtc = prepared_blocked_wt(prepared, v, h) + (c0 / gemm::kK) * 512;
         ldwt = vpsteps * 512;
-      } else {  // W[c0, c1) transposed into the workspace
-        const int64_t rows = c0 < v ? (c1 < v ? c1 : v) - c0 : 0;
-        launch_transpose(weight + c0 * ld_w, ld_w, rows, cols, h, wt, s);
-        wtc = wt;
-        ldwt = csteps * 512;
+      } else {  // W[c0, c1) as it is: K-outer, its rows the lines
+        wtc = weight + c0 * ld_w;
+        ldwt = ld_w;
       }
       const float* cin = first ? nullptr : (dh32 ? dh32 : static_cast<const float*>(dh));
       const int64_t ldcin = dh32 ? h : ld_dh;
       const bool out_bf16 = bf16_out && last;
       void* cout = bf16_out && !last ? static_cast<void*>(dh32) : dh;
       const int64_t ldc = bf16_out && !last ? h : ld_dh;
-      launch_gemm(out_bf16, dz, csteps * 512, l.np, wtc, ldwt, h, cols, n, h, cin, ldcin, cout,
-                  ldc, s);
+      launch_gemm(out_bf16, gemm::kKContig, dz, csteps * 512, l.np, -1,
+                  prepared ? gemm::kKContig : gemm::kKOuter, wtc, ldwt, h,
+                  prepared ? -1 : (c1 < v ? c1 : v) - c0, cols, n, h, cin, ldcin, cout, ldc, s);
     }
   }
   (void)hsteps;

@@ -1,5 +1,6 @@
-// 256 x 256 bf16 MFMA tile of C = A * B^T (both operands K-contiguous), the
-// product engine of the fused LM head and of its backward.
+// 256 x 256 bf16 MFMA tile of C = A * B^T (operands K-contiguous, or read
+// K-outer through transposed LDS reads), the product engine of the fused LM
+// head and of its backward.
 //
 // Arithmetic (part of the fused-LM-head contract): every output is one fp32
 // accumulator fed by v_mfma_f32_16x16x32_bf16 over K in ascending steps of
@@ -472,11 +473,224 @@ __device__ __forceinline__ void mainloop(Stages& sm, const uint16_t* __restrict_
                                      acc);
 }
 
-// acc += A[a_row0 + 0..255, 0..K) * B[b_row0 + 0..255, 0..K)^T with K =
-// ksteps * 32 (ksteps even, >= 2); ABLK / BBLK: the operand is K32-blocked
-// and its lda / ldb is the distance between 16-row blocks in elements (512
-// times the operand's K steps).  All 512 threads must call; on return every
-// direct load has landed and the stages may be reused after a barrier.
+// ---------------------------------------------------------------------------
+// K-outer operands: the K index is the outer one.  Two forms:
+//   kKOuter: element (r, k) at X[k * ld + r], as the weight [V, H] is for a
+//     product over the vocabulary and the hidden rows [N, H] for a product
+//     over tokens;
+//   kKOuterBlocked: a K32-blocked matrix read along its other axis, element
+//     (r, k) at X[kblocked_index(k, r, ld)] (ld = that matrix's K steps), as
+//     dz_c [tokens, chunk columns] is for the product over tokens.
+// A K step takes 32 lines (K values) of 256 elements (the tile's rows).
+// Fragments come from ds_read_b64_tr_b16: within each group of 16 lanes that
+// instruction gives lane i element i % 4 of the 8-byte pieces read by lanes
+// i / 4 + 4s, s = 0..3.  Lane (li, g) of a 16-row fragment reads rows
+// 4 (li % 4) .. + 3 of line 8g + li / 4, then of line 8g + 4 + li / 4, so it
+// receives row li at K 8g .. 8g + 7: the fragment a K-contiguous read gives,
+// hence the same products and bits.
+//   kKOuter stage: the 32 lines in order, 512 B each, the 32-byte unit p
+//     (rows 16p .. 16p + 15) of line k at unit p ^ ksw(k), ksw(k) = (k & 3) |
+//     ((k >> 1) & 4), so the eight lines one half-wave of a read touches fall
+//     on different banks; one direct load fills two lines (lane L: line
+//     L / 32, 16-byte unit L % 32), eight whole 128-byte lines.  Lines at or
+//     past kvalid read a zero line (the zero rows of a padded K32-blocked
+//     operand), rows at or past rvalid read rows from rvalid - 8 on (they
+//     feed only outputs the caller masks; rvalid a multiple of 8, >= 8).
+//   kKOuterBlocked stage: the source's own 1 KiB pieces (16 lines x 32 rows,
+//     64 B per line), piece (line / 16) * 8 + row / 32, so one direct load
+//     copies one whole piece; inside a piece the two 32-byte halves of line k
+//     swap when bit 3 of k is set, which puts the eight lines of a half-wave
+//     read on different banks.  Every line and row must hold data (the source
+//     is padded with zeros to whole 256-row tiles and 32-line steps).
+// ---------------------------------------------------------------------------
+enum { kKContig = 0, kKOuter = 1, kKOuterBlocked = 2 };
+
+static __device__ uint16_t kZeroLine[kTile];  // never written: zero from load time
+
+__device__ __forceinline__ int ksw(int k) { return (k & 3) | ((k >> 1) & 4); }
+
+// A loader wave's sources for one K-outer operand: load u (< 4) of a K step
+// fills 1 KiB of the stage at (wave + 4u) KiB: lines 2 (wave + 4u) and
+// 2 (wave + 4u) + 1 (kKOuter), or piece wave + 4u (kKOuterBlocked).
+struct KOuterSrc {
+  const uint16_t* p[4];  // this lane's source of load u at K step 0
+  int line[4];           // its line within a K step
+  int zofs;              // its 16-byte piece of the zero line
+  int64_t sstride;       // elements between K steps
+  template <int FORM>
+  __device__ __forceinline__ void init(const uint16_t* X, int64_t ld, int64_t row0,
+                                       int64_t rvalid, int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = wave + 4 * u;
+      if constexpr (FORM == kKOuterBlocked) {
+        const int l = (piece >> 3) * 16 + lane / 4;
+        const int half = ((lane % 4) >> 1) ^ ((l >> 3) & 1);
+        p[u] = X + kblocked_index(l, row0 + (piece & 7) * 32 + half * 16 + (lane & 1) * 8, ld);
+        line[u] = l;
+      } else {
+        const int up = lane % 32;  // physical 16-byte unit of the line
+        const int l = 2 * piece + lane / 32;
+        const int64_t r = min(row0 + 16 * ((up / 2) ^ ksw(l)) + 8 * (up % 2), rvalid - 8);
+        p[u] = X + l * ld + r;
+        line[u] = l;
+      }
+    }
+    zofs = 8 * (lane % 32);
+    sstride = FORM == kKOuterBlocked ? 2 * ld * 512 : kK * ld;
+  }
+  __device__ __forceinline__ const uint16_t* at(int u, int step, int kvalid) const {
+    return step * kK + line[u] < kvalid ? p[u] + step * sstride : kZeroLine + zofs;
+  }
+};
+
+// A loader wave's 4 direct loads of one operand for K step `step` into the
+// 16 KiB at dst: K32-blocked (blocks wave + 4u) or K-outer (line pairs
+// wave + 4u).
+__device__ __forceinline__ void load_blocked(const LoaderSrc<true>& s, uint16_t* dst, int wave,
+                                             int step) {
+  const int64_t k = static_cast<int64_t>(step) * 512;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    __builtin_amdgcn_global_load_lds(s.at(u, k), dst + (wave + 4 * u) * 16 * kK, 16, 0, 0);
+}
+__device__ __forceinline__ void load_kouter(const KOuterSrc& s, int kvalid, uint16_t* dst,
+                                            int wave, int step) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    __builtin_amdgcn_global_load_lds(s.at(u, step, kvalid), dst + (wave + 4 * u) * 16 * kK, 16,
+                                     0, 0);
+}
+
+// The fragment of a K-outer stage whose first transposed read is at p and
+// second at p + SECOND (four lines on).
+template <int SECOND>
+__device__ __forceinline__ bf16x8 read_kouter_frag(const uint16_t* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + SECOND));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Element offset, inside a K-outer stage of form FORM, of lane (li, g)'s
+// first transposed read for the fragment of rows r0 .. r0 + 15 (r0 a
+// multiple of 16), and the second read's distance.
+template <int FORM>
+__device__ __forceinline__ int kouter_off(int r0, int li, int g) {
+  const int l = 8 * g + li / 4;
+  if constexpr (FORM == kKOuterBlocked)
+    return ((l >> 4) * 8 + (r0 >> 5)) * 512 + (l & 15) * 32 +
+           ((((r0 >> 4) & 1) ^ ((l >> 3) & 1)) * 16) + 4 * (li % 4);
+  else
+    return l * kTile + (((r0 >> 4) ^ ksw(l)) * 16) + 4 * (li % 4);
+}
+template <int FORM>
+constexpr int kouter_second() {
+  return FORM == kKOuterBlocked ? 4 * 32 : 4 * kTile;
+}
+
+// The 256 x 256 tile's main loop (mainloop_role's pipeline, barriers, wait
+// counts and loader waves) with each operand in one of the forms above (AF /
+// BF; kKContig = K32-blocked with ld between 16-row blocks; a K-outer operand
+// takes its ld and kvalid = its lines that hold data, counted from the
+// first).  Waves of 128 x 64 as in mainloop_role.  Per K step a wave reads 8
+// A and 4 B fragments, two transposed reads each for a K-outer operand,
+// spread over its first 24 MFMAs.  (Waves of 64 x 128, which halve a K-outer
+// A's transposed reads, measured slower.)
+template <int AF, int BF, bool LOADER>
+__device__ __forceinline__ void mainloop_ko(Stages& sm, const uint16_t* __restrict__ A,
+                                            int64_t lda, int64_t a_row0, int64_t a_rows,
+                                            int a_kvalid, const uint16_t* __restrict__ B,
+                                            int64_t ldb, int64_t b_row0, int64_t b_rows,
+                                            int b_kvalid, int ksteps, f32x4 (&acc)[8][4]) {
+  constexpr int MI = 8, NJ = 4, WM = 128, WN = 64;
+  constexpr bool AKO = AF != kKContig, BKO = BF != kKContig;
+  constexpr int NL = LOADER ? kLoaderLoads : 0;
+  constexpr int NR = MI * (AKO ? 2 : 1) + NJ * (BKO ? 2 : 1);  // LDS reads per K step
+  static_assert(NR >= 12 && NR <= 24, "read interleave assumes 12 to 24 reads per step");
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int wm = wave / 4, wn = wave % 4;
+  const int li = lane % 16, g = lane / 16;
+  const int lrow = lane / 4;
+  const int lk = ((lane % 4) ^ swz(lrow)) * 8;
+  LoaderSrc<true> ab, bb;
+  KOuterSrc ak, bk;
+  if constexpr (LOADER) {
+    if constexpr (AKO) ak.init<AF>(A, lda, a_row0, a_rows, wave, lane);
+    else ab.init(A, lda, a_row0, a_rows, wave, lrow, lk);
+    if constexpr (BKO) bk.init<BF>(B, ldb, b_row0, b_rows, wave, lane);
+    else bb.init(B, ldb, b_row0, b_rows, wave, lrow, lk);
+  }
+#define ITL_KO_ISSUE(S_, STEP_)                                                                 \
+  if constexpr (LOADER) {                                                                       \
+    if constexpr (AKO) load_kouter(ak, a_kvalid, sm.s[S_][0], wave, (STEP_));                   \
+    else load_blocked(ab, sm.s[S_][0], wave, (STEP_));                                          \
+    if constexpr (BKO) load_kouter(bk, b_kvalid, sm.s[S_][1], wave, (STEP_));                   \
+    else load_blocked(bb, sm.s[S_][1], wave, (STEP_));                                          \
+  }
+  // Fragment offsets (elements) inside a stage.  K-contiguous: row wm*WM +
+  // li (+16 i) of A, row wn*WN + li (+16 j) of B, chunk g.  K-outer: as
+  // kouter_off gives them.
+  const int aoff = (wm * WM + li) * kK + ((g ^ swz(li)) * 8);
+  const int boff = (wn * WN + li) * kK + ((g ^ swz(li)) * 8);
+#define ITL_KO_READ(FA, FB, ST)                                                                 \
+  {                                                                                             \
+    const uint16_t* fa = sm.s[ST][0];                                                           \
+    const uint16_t* fb = sm.s[ST][1];                                                           \
+    _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                            \
+      if constexpr (BKO)                                                                        \
+        FB[j] = read_kouter_frag<kouter_second<BF>()>(                                          \
+            fb + kouter_off<BF>(wn * WN + 16 * j, li, g));                                      \
+      else                                                                                      \
+        FB[j] = *reinterpret_cast<const bf16x8*>(fb + boff + j * 16 * kK);                      \
+    }                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                            \
+      if constexpr (AKO)                                                                        \
+        FA[i] = read_kouter_frag<kouter_second<AF>()>(                                          \
+            fa + kouter_off<AF>(wm * WM + 16 * i, li, g));                                      \
+      else                                                                                      \
+        FA[i] = *reinterpret_cast<const bf16x8*>(fa + aoff + i * 16 * kK);                      \
+    }                                                                                           \
+  }
+  for (int st = 0; st < kStages; ++st) ITL_KO_ISSUE(st, st < ksteps ? st : ksteps - 1);
+  wait_vm<(kStages - 1) * NL>();
+  __builtin_amdgcn_s_barrier();
+  bf16x8 xa[MI], xb[NJ], ya[MI], yb[NJ];
+  ITL_KO_READ(xa, xb, 0)
+#define ITL_KO_STEP(CA, CB, NA, NB, KT)                                                         \
+  {                                                                                             \
+    wait_vm_lgkm0<(kStages - 2) * NL>();                                                        \
+    __builtin_amdgcn_s_barrier();                                                               \
+    ITL_KO_ISSUE((KT) % kStages, (KT) + kStages < ksteps ? (KT) + kStages : ksteps - 1);        \
+    ITL_KO_READ(NA, NB, ((KT) + 1) % kStages)                                                   \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                              \
+      _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                            \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CA[i], CB[j], acc[i][j], 0, 0, 0);  \
+    if constexpr (LOADER) __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);                   \
+    _Pragma("unroll") for (int u = 0; u < 2 * NR - 24; ++u) {                                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                        \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                        \
+    }                                                                                           \
+    _Pragma("unroll") for (int u = 0; u < 24 - NR; ++u) {                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                        \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                        \
+    }                                                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                          \
+  }
+  for (int kt = 0; kt < ksteps; kt += 2) {
+    ITL_KO_STEP(xa, xb, ya, yb, kt)
+    ITL_KO_STEP(ya, yb, xa, xb, kt + 1)
+  }
+#undef ITL_KO_STEP
+#undef ITL_KO_READ
+#undef ITL_KO_ISSUE
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
 // Narrow tiles for few hidden rows: ROWS (64 or 128) A rows x 256 B rows,

@@ -367,4 +367,4 @@ def test_vocab_chunk_full_size_same_bits():
             assert torch.equal(_bits_any(a), _bits_any(b)), out_dtype
     big = itl.linear_logp_bwd_workspace_bytes(512, 4096, synth.QWEN3_VOCAB, vocab_chunk=vp)
     small = itl.linear_logp_bwd_workspace_bytes(512, 4096, synth.QWEN3_VOCAB)
-    assert small * 4 < big
+    assert small * 3 < big
