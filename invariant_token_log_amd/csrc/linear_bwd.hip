@@ -311,10 +311,12 @@ __global__ __launch_bounds__(gemm::kThreads) void linear_dz_kernel(
 // 512-byte (bf16) or 1 KiB (fp32) pieces, the bf16 dz goes to an LDS tile and
 // leaves as 1 KiB K32-blocked pieces of dz_c [Np, K = cols_p].  Rows past n
 // or ignored, and columns past v, get 0 without reading the logits.  Grid:
-// x = row tiles, y = column tiles (grid-stride beyond gridDim.y).
+// x = column tiles, y = row tiles of the np_rows (grid-stride beyond
+// gridDim.y): neighbouring workgroups read neighbouring KiB of the same rows
+// and write neighbouring pieces of dz_c.
 template <bool ZBF16>
 __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
-    const void* __restrict__ zsaved, int64_t ld_z, int64_t n, int64_t v,
+    const void* __restrict__ zsaved, int64_t ld_z, int64_t n, int64_t v, int64_t np_rows,
     const void* __restrict__ tgt, int32_t tgt32, int64_t ignore_index,
     const float* __restrict__ lse, const float* __restrict__ grad, float inv_t,
     int32_t round_bf16, const float* __restrict__ ent, const float* __restrict__ gent,
@@ -324,16 +326,16 @@ __global__ __launch_bounds__(256) void linear_dz_saved_kernel(
   __shared__ float rowc[kTR][4];  // lse, g, entropy, -gH of each tile row
   __shared__ int64_t rowt[kTR];   // target (ignore_index: no gradient)
   const int tid = threadIdx.x;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTR;
+  const int64_t cl0 = static_cast<int64_t>(blockIdx.x) * kTC;
+  const int64_t col0 = c0 + cl0;  // vocabulary column of the tile
   const bool scaled = inv_t != 1.0f;
   const bool with_ent = ent != nullptr;
   constexpr int E = ZBF16 ? 8 : 4;         // elements per 16-byte chunk
   constexpr int CPR = kTC / E;             // chunks per tile row
   constexpr int RPS = 256 / CPR;           // tile rows per step of the block
   const int64_t vc_steps = cols_p / gemm::kK;
-  for (int64_t cl0 = static_cast<int64_t>(blockIdx.y) * kTC; cl0 < cols_p;
-       cl0 += static_cast<int64_t>(gridDim.y) * kTC) {
-    const int64_t col0 = c0 + cl0;  // vocabulary column of the tile
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.y) * kTR; r0 < np_rows;
+       r0 += static_cast<int64_t>(gridDim.y) * kTR) {
     if (tid < kTR) {
       const int64_t row = r0 + tid;
       int64_t t = ignore_index;
@@ -666,16 +668,16 @@ void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* wei
       }
 #undef ITL_DZ
     } else {
-      const int64_t ct = cols / kTC;
-      const dim3 grid(static_cast<unsigned>(l.np / kTR), static_cast<unsigned>(ct < 65535 ? ct : 65535));
+      const int64_t rt = l.np / kTR;
+      const dim3 grid(static_cast<unsigned>(cols / kTC), static_cast<unsigned>(rt < 65535 ? rt : 65535));
       if (z_bf16)
         hipLaunchKernelGGL(linear_dz_saved_kernel<true>, grid, dim3(256), 0, s, zsaved, ld_z, n, v,
-                           targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16, ent,
+                           l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16, ent,
                            gent, c0, cols, dz);
       else
         hipLaunchKernelGGL(linear_dz_saved_kernel<false>, grid, dim3(256), 0, s, zsaved, ld_z, n,
-                           v, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16, ent,
-                           gent, c0, cols, dz);
+                           v, l.np, targets.p, targets.is32, ignore, lse, grad, inv_t, round_bf16,
+                           ent, gent, c0, cols, dz);
     }
     // dW[c0, c1) = dz_c^T h: K = every token, ascending (final rows); dz_c
     // read along its token axis (K-outer)
