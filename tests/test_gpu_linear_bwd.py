@@ -63,7 +63,10 @@ def _case(n, hd, v, seed, ignore_frac=0.05):
 
 
 @pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (200, 128, 1000), (1, 64, 256),
-                                    (129, 512, 529), (300, 512, 4096), (257, 64, 300)])
+                                    (129, 512, 529), (300, 512, 4096), (257, 64, 300),
+                                    # H past a whole 256-row tile: the weight rows read
+                                    # K-outer for dh end inside the last tile
+                                    (100, 320, 700), (70, 576, 1300)])
 def test_parity_small(n, hd, v):
     h, w, t, g = _case(n, hd, v, seed=n * 7 + v)
     _, lse = itl.linear_logp_fwd(h, w, t)
@@ -256,7 +259,7 @@ def _blocked(x, rows_p, k):
 
 
 @pytest.mark.parametrize("n,hd,v", [(64, 256, 4096), (257, 64, 300), (1, 128, 529),
-                                    (300, 128, 1000)])
+                                    (300, 128, 1000), (90, 320, 800)])
 def test_prepared_weight_same_bits(n, hd, v):
     """prepare_weight writes the weight [Vp, H] and its transpose [H, Vp]
     (zero vocabulary padding up to Vp = round_up(V, 256)) in the blocked
