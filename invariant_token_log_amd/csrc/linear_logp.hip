@@ -431,14 +431,19 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
 // row-major [n, ld_h], mblocks = ceil(n / ROWS) row blocks; the grid covers
 // vocabulary blocks [vb0, vb0 + vtiles).
 // ---------------------------------------------------------------------------
-// WBLK: the stage ring of mainloop_narrow; row-major weight: the pair slots
-// of mainloop_narrow_pairs.
-template <int ROWS, bool WBLK>
+// WBLK: the stage ring of mainloop_narrow; row-major weight: the NPS pair
+// slots of mainloop_narrow_pairs.
+template <int ROWS, bool WBLK, int NPS>
 struct SmemNarrow {
-  typename std::conditional<WBLK, gemm::StagesNarrow<ROWS>, gemm::StagesNarrowPairs<ROWS>>::type
-      st;
+  typename std::conditional<WBLK, gemm::StagesNarrow<ROWS>,
+                            gemm::StagesNarrowPairs<ROWS, NPS>>::type st;
   Reduce<ROWS> rd;
 };
+
+// Row-major weight pair slots of the narrow tiles: 4 for 64 rows (144 KiB,
+// the whole LDS of a CU: three pairs in flight), 2 for 128 rows.
+template <int ROWS>
+constexpr int kNarrowPairs = ROWS == 64 ? 4 : 2;
 
 template <int ROWS, bool WBLK, bool NTB = false>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
   constexpr int MI = gemm::NarrowCfg<ROWS>::kMI;
   const Targets targets{tgt, tgt32};
-  __shared__ __align__(16) SmemNarrow<ROWS, WBLK> sm;
+  __shared__ __align__(16) SmemNarrow<ROWS, WBLK, kNarrowPairs<ROWS>> sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -474,7 +479,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
                                            static_cast<int64_t>(ksteps) * 512, v0,
                                            static_cast<int64_t>(vblocks) * BN, ksteps, acc);
   else
-    gemm::mainloop_narrow_pairs<ROWS, NTB>(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
+    gemm::mainloop_narrow_pairs<ROWS, NTB, kNarrowPairs<ROWS>>(sm.st, hidden, ld_h, m0, n, weight, ld_w, v0, v,
                                            ksteps, acc);
   __syncthreads();
   stats_epilogue<MI, 4, ROWS, kDmaThreads, sizeof(sm.st)>(acc, sm.rd, &sm.st, wm * (ROWS / 2),

@@ -719,20 +719,21 @@ struct StagesNarrow {
 };
 
 // The narrow tile with a row-major B staged in pairs of K steps, as
-// mainloop_pairs does for the 256-row tile: four A slots of ROWS x 32 and two
-// B pair slots of 256 x 64 (80 KiB for ROWS = 64, one workgroup per CU),
-// every B direct load 8 rows x 128 bytes.  Wave w issues, on odd steps, rows
-// (w + 8u) * 8 + [0, 8), u < 4, of the B pair two steps ahead and, for w <
-// ROWS / 16, A block w of every step.  NTB: the B loads carry the
-// non-temporal hint (B read by this workgroup only).
-template <int ROWS>
+// mainloop_pairs does for the 256-row tile: four A slots of ROWS x 32 and NPS
+// B pair slots of 256 x 64 (NPS = 2: 80 KiB for ROWS = 64; NPS = 4: 144 KiB,
+// NPS - 1 pairs in flight; one workgroup per CU either way), every B direct
+// load 8 rows x 128 bytes.  Wave w issues, on odd steps, rows (w + 8u) * 8 +
+// [0, 8), u < 4, of the B pair 2 NPS - 2 steps ahead and, for w < ROWS / 16,
+// A block w of every step.  NTB: the B loads carry the non-temporal hint (B
+// read by this workgroup only).
+template <int ROWS, int NPS = 2>
 struct StagesNarrowPairs {
   uint16_t a[4][ROWS * kK];
-  uint16_t b[2][kTile * 2 * kK];  // 32 KiB each
+  uint16_t b[NPS][kTile * 2 * kK];  // 32 KiB each
 };
 
-template <int ROWS, bool NTB>
-__device__ __forceinline__ void mainloop_narrow_pairs(StagesNarrowPairs<ROWS>& sm,
+template <int ROWS, bool NTB, int NPS = 2>
+__device__ __forceinline__ void mainloop_narrow_pairs(StagesNarrowPairs<ROWS, NPS>& sm,
                                                       const uint16_t* __restrict__ A, int64_t lda,
                                                       int64_t a_row0, int64_t a_rows,
                                                       const uint16_t* __restrict__ B, int64_t ldb,
@@ -772,22 +773,33 @@ __device__ __forceinline__ void mainloop_narrow_pairs(StagesNarrowPairs<ROWS>& s
   const int aoff = (wm * (ROWS / 2) + li) * kK + ((g ^ swz(li)) * 8);
   const int brow = wn * 64 + li;
   const int bsw = swzp(li);
-  // Prologue = iterations -4 .. -1 (A of step it + 4; odd: B pair it + 3, it + 4).
-  issue_a(0, 0);
-  issue_a(1, 1 < ksteps ? 1 : ksteps - 1);
-  issue_b(0, 0);
-  issue_a(2, 2 < ksteps ? 2 : ksteps - 1);
-  issue_a(3, 3 < ksteps ? 3 : ksteps - 1);
-  issue_b(1, 1 < npairs ? 1 : npairs - 1);
-  if (has_a)
-    wait_vm<2 + 4>();
-  else
-    wait_vm<4>();
+  // Iteration it issues A of step it + 4 and, when it is odd, the B pair
+  // (it + 2 NPS - 1) / 2 (steps it + 2 NPS - 1, it + 2 NPS) into slot pair %
+  // NPS, whose previous pair was last read for step it.  Prologue =
+  // iterations -max(4, 2 NPS - 1) .. -1.
+  constexpr int P0 = 2 * NPS - 1 > 4 ? 2 * NPS - 1 : 4;
+#pragma unroll
+  for (int it = -P0; it < 0; ++it) {
+    if (it >= -4) issue_a(it + 4, it + 4 < ksteps ? it + 4 : ksteps - 1);
+    if (it & 1) {
+      const int p = (it + 2 * NPS - 1) / 2;
+      issue_b(p, p < npairs ? p : npairs - 1);
+    }
+  }
+  // Waits (NA = this wave's A loads per step, NB = its B loads per pair):
+  // before step 0, A(0) and pair 0 have landed once the loads issued after
+  // the later of the two are all that is in flight.
+  constexpr int NB = 4;
+  if (has_a) {
+    if constexpr (NPS == 2) wait_vm<2 + NB>(); else wait_vm<3 + 2 * NB>();
+  } else {
+    if constexpr (NPS == 2) wait_vm<NB>(); else wait_vm<2 * NB>();
+  }
   __builtin_amdgcn_s_barrier();
   bf16x8 xa[MI], xb[4], ya[MI], yb[4];
   auto read_frags = [&](bf16x8 (&fa)[MI], bf16x8 (&fb)[4], int step) {
     const uint16_t* fa_ = sm.a[step % 4];
-    const uint16_t* fb_ = sm.b[(step / 2) % 2];
+    const uint16_t* fb_ = sm.b[(step / 2) % NPS];
     const int ch = ((4 * (step % 2) + g) ^ bsw) * 8;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -797,21 +809,31 @@ __device__ __forceinline__ void mainloop_narrow_pairs(StagesNarrowPairs<ROWS>& s
       fa[i] = *reinterpret_cast<const bf16x8*>(fa_ + aoff + i * 16 * kK);
   };
   read_frags(xa, xb, 0);
-  // Even KT: A(KT+1) and the pair (KT, KT+1), issued at KT-3, have landed
-  // once at most A(KT-2), A(KT-1), B(KT-1) are in flight; odd KT: the pair
-  // (KT+1, KT+2), issued at KT-2, once at most A(KT-1) is.
+  // Before iteration KT, A(KT+1) (issued at KT-3) and the pair of step
+  // KT+1 must have landed: with NPS = 2 (that pair issued at KT-3 after the
+  // A load for even KT, at KT-2 for odd KT) 2 NA + NB loads may still be in
+  // flight for even KT and NA for odd KT; with NPS >= 3 (the pair older than
+  // A(KT+1)) 2 NA + 2 NB for even KT and 2 NA + NB for odd KT.
 #define ITL_NPSTEP(CA, CB, NXA, NXB, KT, ODD)                                                   \
   {                                                                                             \
     if (has_a) {                                                                                \
-      if constexpr (ODD) wait_vm_lgkm0<1>(); else wait_vm_lgkm0<2 + 4>();                       \
+      if constexpr (NPS == 2) {                                                                 \
+        if constexpr (ODD) wait_vm_lgkm0<1>(); else wait_vm_lgkm0<2 + NB>();                    \
+      } else {                                                                                  \
+        if constexpr (ODD) wait_vm_lgkm0<2 + NB>(); else wait_vm_lgkm0<2 + 2 * NB>();           \
+      }                                                                                         \
     } else {                                                                                    \
-      if constexpr (ODD) wait_vm_lgkm0<0>(); else wait_vm_lgkm0<4>();                           \
+      if constexpr (NPS == 2) {                                                                 \
+        if constexpr (ODD) wait_vm_lgkm0<0>(); else wait_vm_lgkm0<NB>();                        \
+      } else {                                                                                  \
+        if constexpr (ODD) wait_vm_lgkm0<NB>(); else wait_vm_lgkm0<2 * NB>();                   \
+      }                                                                                         \
     }                                                                                           \
     __builtin_amdgcn_s_barrier();                                                               \
     issue_a((KT) % 4, (KT) + 4 < ksteps ? (KT) + 4 : ksteps - 1);                               \
     if constexpr (ODD) {                                                                        \
-      const int p_ = ((KT) + 3) / 2;                                                            \
-      issue_b(p_ % 2, p_ < npairs ? p_ : npairs - 1);                                           \
+      const int p_ = ((KT) + 2 * NPS - 1) / 2;                                                  \
+      issue_b(p_ % NPS, p_ < npairs ? p_ : npairs - 1);                                         \
     }                                                                                           \
     read_frags(NXA, NXB, (KT) + 1);                                                             \
     _Pragma("unroll") for (int i = 0; i < MI; ++i)                                              \
