@@ -433,19 +433,24 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_dma(
 // ---------------------------------------------------------------------------
 // WBLK: the stage ring of mainloop_narrow; row-major weight: the NPS pair
 // slots of mainloop_narrow_pairs.
-template <int ROWS, bool WBLK, int NPS>
+template <int ROWS, bool WBLK, int NPS, int S>
 struct SmemNarrow {
-  typename std::conditional<WBLK, gemm::StagesNarrow<ROWS>,
+  typename std::conditional<WBLK, gemm::StagesNarrow<ROWS, S>,
                             gemm::StagesNarrowPairs<ROWS, NPS>>::type st;
   Reduce<ROWS> rd;
 };
 
 // Row-major weight pair slots of the narrow tiles: 4 for 64 rows (144 KiB,
-// the whole LDS of a CU: three pairs in flight), 2 for 128 rows.
+// the whole LDS of a CU: three pairs in flight), 2 for 128 rows.  A
+// prepared weight's ring: NarrowCfg's stages, or with DEEP (64 rows only,
+// for launches of at most one workgroup per CU) seven (140 KiB, six in
+// flight).
 template <int ROWS>
 constexpr int kNarrowPairs = ROWS == 64 ? 4 : 2;
+template <int ROWS, bool DEEP>
+constexpr int kNarrowStages = DEEP ? 7 : gemm::NarrowCfg<ROWS>::kStages;
 
-template <int ROWS, bool WBLK, bool NTB = false>
+template <int ROWS, bool WBLK, bool NTB = false, bool DEEP = false>
 __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     const uint16_t* __restrict__ hidden, int64_t ld_h, const uint16_t* __restrict__ weight,
     int64_t ld_w, int64_t n, int64_t hdim, int64_t v, int mblocks, int vblocks, int vb0,
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     float* __restrict__ ps, float* __restrict__ pt, LinearExtras ex) {
   constexpr int MI = gemm::NarrowCfg<ROWS>::kMI;
   const Targets targets{tgt, tgt32};
-  __shared__ __align__(16) SmemNarrow<ROWS, WBLK, kNarrowPairs<ROWS>> sm;
+  __shared__ __align__(16) SmemNarrow<ROWS, WBLK, kNarrowPairs<ROWS>, kNarrowStages<ROWS, DEEP>> sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -475,7 +480,7 @@ __global__ __launch_bounds__(kDmaThreads) void linear_stats_narrow(
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int ksteps = static_cast<int>(hdim / BK);
   if constexpr (WBLK)
-    gemm::mainloop_narrow<ROWS, true, NTB>(sm.st, hidden, ld_h, m0, n, weight,
+    gemm::mainloop_narrow<ROWS, true, NTB, kNarrowStages<ROWS, DEEP>>(sm.st, hidden, ld_h, m0, n, weight,
                                            static_cast<int64_t>(ksteps) * 512, v0,
                                            static_cast<int64_t>(vblocks) * BN, ksteps, acc);
   else
@@ -503,9 +508,10 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
   const int64_t ldn = wblk ? 0 : ld_w;
   // once: every weight row is read by one workgroup only (a single row
   // block), so the weight streams with non-temporal loads
-  auto narrow = [&](int rows, int mb, int vb0, int vt, bool once) {
+  auto narrow = [&](int rows, int mb, int vb0, int vt, bool once, bool deep) {
     auto kern = rows == 64
                     ? (wblk ? (once ? linear_stats_narrow<64, true, true>
+                               : deep ? linear_stats_narrow<64, true, false, true>
                                     : linear_stats_narrow<64, true, false>)
                             : (once ? linear_stats_narrow<64, false, true>
                                     : linear_stats_narrow<64, false, false>))
@@ -517,7 +523,7 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
                        v, mb, vblocks, vb0, vt, targets.p, targets.is32, ignore, pm, ps, pt, ex);
   };
   if (n <= 128) {
-    narrow(n <= 64 ? 64 : 128, 1, 0, vblocks, true);
+    narrow(n <= 64 ? 64 : 128, 1, 0, vblocks, true, false);
   } else {
     const int mblocks = static_cast<int>((n + 255) / 256);
     const int64_t np = static_cast<int64_t>(mblocks) * 256;
@@ -542,7 +548,9 @@ void launch_linear_partials(const uint16_t* hidden, int64_t ld_h, const uint16_t
       hipLaunchKernelGGL(linear_stats_dma<false>, grid, dim3(kDmaThreads), 0, s, hb, ld_h, weight,
                          ld_w, n, h, v, mblocks, vblocks, vmain, targets.p, targets.is32, ignore,
                          pm, ps, pt, ex, queue, qp.queued);
-    if (tail) narrow(64, static_cast<int>((n + 63) / 64), vmain, tail, false);
+    // a tail of at most one workgroup per CU takes the deep ring
+    const int tmb = static_cast<int>((n + 63) / 64);
+    if (tail) narrow(64, tmb, vmain, tail, false, static_cast<int64_t>(tmb) * tail <= cus);
   }
 }
 

@@ -712,10 +712,10 @@ struct NarrowCfg {
   static constexpr int kMI = ROWS / 32;
 };
 
-template <int ROWS>
+template <int ROWS, int S = NarrowCfg<ROWS>::kStages>
 struct StagesNarrow {
-  uint16_t a[NarrowCfg<ROWS>::kStages][ROWS * kK];
-  uint16_t b[NarrowCfg<ROWS>::kStages][kTile * kK];  // 16 KiB each
+  uint16_t a[S][ROWS * kK];
+  uint16_t b[S][kTile * kK];  // 16 KiB each
 };
 
 // The narrow tile with a row-major B staged in pairs of K steps, as
@@ -858,14 +858,13 @@ __device__ __forceinline__ void mainloop_narrow_pairs(StagesNarrowPairs<ROWS, NP
 // loads take half lines, the hint made it 43% slower).  All 512 threads must
 // call; on return every direct load has landed and the stages may be reused
 // after a barrier.
-template <int ROWS, bool BBLK = false, bool NTB = false>
-__device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS>& sm,
+template <int ROWS, bool BBLK = false, bool NTB = false, int S = NarrowCfg<ROWS>::kStages>
+__device__ __forceinline__ void mainloop_narrow(StagesNarrow<ROWS, S>& sm,
                                                 const uint16_t* __restrict__ A, int64_t lda,
                                                 int64_t a_row0, int64_t a_rows,
                                                 const uint16_t* __restrict__ B, int64_t ldb,
                                                 int64_t b_row0, int64_t b_rows, int ksteps,
                                                 f32x4 (&acc)[NarrowCfg<ROWS>::kMI][4]) {
-  constexpr int S = NarrowCfg<ROWS>::kStages;
   constexpr int MI = NarrowCfg<ROWS>::kMI;
   const int tid = threadIdx.x;
   const int lane = tid % 64;
