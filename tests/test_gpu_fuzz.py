@@ -101,9 +101,11 @@ def test_fuzz_streaming(c):
 
 @st.composite
 def linear_cases(draw):
-    return dict(n=draw(st.integers(1, 300)), h=draw(st.sampled_from([64, 128, 256, 512])),
+    return dict(n=draw(st.integers(1, 300)),
+                h=draw(st.sampled_from([64, 128, 256, 320, 448, 512])),
                 v=draw(st.integers(1, 3000)), temp=draw(st.sampled_from([1.0, 0.7, 2.0])),
                 ent=draw(st.booleans()), n_ign=draw(st.integers(0, 5)),
+                chunk=draw(st.sampled_from([256, 512, 768, 1024])),
                 seed=draw(st.integers(0, 2 ** 30)))
 
 
@@ -138,7 +140,7 @@ def test_fuzz_linear(c):
 @given(linear_cases())
 def test_fuzz_linear_bwd(c):
     """dh and dW against the float64 oracle by the fused backward's bound, and
-    the saved-logits and prepared-weight paths with the same bits."""
+    the saved-logits, prepared-weight and chunked paths with the same bits."""
     from test_gpu_linear_bwd import _bounds
 
     n, h, v = c["n"], c["h"], c["v"]
@@ -156,6 +158,10 @@ def test_fuzz_linear_bwd(c):
     assert torch.equal(dh, dh2) and torch.equal(dw, dw2), what
     dh3, dw3 = itl.linear_logp_bwd(hid, w, t, lse, g, prepared_weight=itl.prepare_weight(w))
     assert torch.equal(dh, dh3) and torch.equal(dw, dw3), what
+    # several vocabulary chunks (a partial last chunk, whose weight lines past
+    # v read zeros): the same bits
+    dh4, dw4 = itl.linear_logp_bwd(hid, w, t, lse, g, vocab_chunk=c["chunk"])
+    assert torch.equal(dh, dh4) and torch.equal(dw, dw4), what
     hn, wn, tn, gn = to_np(hid), to_np(w), t.cpu().numpy(), to_np(g)
     dh64, dw64 = oracle.linear_logp_bwd(hn, wn, tn, gn)
     _, lse64 = oracle.linear_logp_fwd(hn, wn, tn)
