@@ -545,8 +545,8 @@ struct KOuterSrc {
 };
 
 // A loader wave's 4 direct loads of one operand for K step `step` into the
-// 16 KiB at dst: K32-blocked (blocks wave + 4u) or K-outer (line pairs
-// wave + 4u).
+// 16 KiB at dst: K32-blocked (blocks wave + 4u) or K-outer (the line pairs
+// or pieces wave + 4u of KOuterSrc).
 __device__ __forceinline__ void load_blocked(const LoaderSrc<true>& s, uint16_t* dst, int wave,
                                              int step) {
   const int64_t k = static_cast<int64_t>(step) * 512;
