@@ -24,6 +24,7 @@ Every input buffer is fingerprinted with SHA-256 ("inputs_sha256").
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -53,11 +54,20 @@ KERNEL_SOURCES = {
 LINEAR_BWD_CHUNKS = 5
 
 
+def _code_only(text):
+    """Source text without comments, trailing blanks and empty lines, so that
+    a comment edit does not retire counters taken on the same code."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_hash(kernel):
+    """SHA-256 (first 16 hex digits) of the code of a kernel's sources."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
