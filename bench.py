@@ -918,7 +918,7 @@ def main():
             print(p)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(rows are independent, so data-parallel scaling needs no exchange); "
               f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)

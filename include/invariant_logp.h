@@ -405,10 +405,10 @@ int32_t linear_logp_bwd(const void* hidden, int64_t ld_h, const void* weight, in
 /* Short English text for a status code (static storage, host memory). */
 const char* logp_status_str(int32_t status);
 
-/* Identifier of the arithmetic contracts this build implements (static
+/* Identifier of the arithmetic contracts this library implements (static
  * storage, host memory): tile tree, merge order, exp/log primitives, MFMA
- * form and K walk.  Two builds that report the same string produce the same
- * bits. */
+ * form and K walk.  Two compiled libraries that report the same string
+ * produce the same bits. */
 const char* logp_contract_id(void);
 
 #ifdef __cplusplus
