@@ -17,7 +17,7 @@ import torch
 import invariant_token_log_amd as itl
 import oracle
 import synth
-from gpu_helpers import bits, dev
+from gpu_helpers import assert_logp_parity, bits, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -190,6 +190,42 @@ def test_full_size_sampled():
     ew = np.abs(_f64(dw)[vr] - dw64)
     assert (ew <= bw).all(), (np.argwhere(ew > bw)[:5], ew.max())
     assert torch.isfinite(dh).all() and torch.isfinite(dw).all()
+
+
+def test_large_n_sampled():
+    """N = 20000 rows on the Qwen3-8B head (79 row blocks: a long tile queue in
+    the forward, 10112 dz tiles per chunk and a 20224-token K walk for dW):
+    sampled forward rows and dh rows against the float64 oracle, and sampled
+    vocabulary rows of dW against the oracle given the forward's LSE (the
+    full-row LSE of 20000 rows is too much float64 work here; its fp32 error
+    is far inside the bf16 bound of dz)."""
+    n = 20000
+    h, w, t, g = _case(n, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB, seed=2024, ignore_frac=0.05)
+    logp, lse = itl.linear_logp_fwd(h, w, t)
+    dh, dw = itl.linear_logp_bwd(h, w, t, lse, g)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dh).all() and torch.isfinite(dw).all()
+    hn, wn, tn, gn = _f64(h), _f64(w), t.cpu().numpy(), _f64(g)
+    rows = np.array([0, 1, 4999, 10007, 15000, 19998, n - 1])
+    lp64, lse_rows = oracle.linear_logp_fwd(hn[rows], wn, tn[rows])
+    assert_logp_parity(logp[rows], lse[rows], lp64, lse_rows, t[rows], what="linear large n")
+    dh64, _ = oracle.linear_logp_bwd(hn[rows], wn, tn[rows], gn[rows], need_dweight=False)
+    bh, _ = _bounds(hn[rows], wn, tn[rows], gn[rows], lse_rows, need_dweight=False)
+    eh = np.abs(_f64(dh)[rows] - dh64)
+    assert (eh <= bh).all(), (np.argwhere(eh > bh)[:5], eh.max())
+    lse_gpu = _f64(lse)
+    active_targets = np.unique(tn[tn != -100])
+    vr = np.unique(np.concatenate([[0, 151935], active_targets[::997]]))
+    dw64 = oracle.linear_logp_bwd_weight_rows(hn, wn, tn, gn, vr, lse=lse_gpu)
+    act = tn != -100
+    pp = np.exp(hn @ wn[vr].T - lse_gpu[:, None])
+    hit = (tn[:, None] == vr[None, :]) & act[:, None]
+    dzz = gn[:, None] * (hit.astype(np.float64) - pp)
+    dzz[~act] = 0.0
+    tgt = np.where(hit, np.abs(gn)[:, None] * pp * EPS_Z, 0.0)
+    bw = REL * (np.abs(dzz).T @ np.abs(hn)) + tgt.T @ np.abs(hn) + ABS
+    ew = np.abs(_f64(dw)[vr] - dw64)
+    assert (ew <= bw).all(), (np.argwhere(ew > bw)[:5], ew.max())
 
 
 def test_int32_targets_same_bits():
