@@ -162,6 +162,12 @@ def test_fuzz_linear_bwd(c):
     # v read zeros): the same bits
     dh4, dw4 = itl.linear_logp_bwd(hid, w, t, lse, g, vocab_chunk=c["chunk"])
     assert torch.equal(dh, dh4) and torch.equal(dw, dw4), what
+    # bf16 outputs (dh carried in fp32 between chunks, rounded once)
+    b1 = itl.linear_logp_bwd(hid, w, t, lse, g, out_dtype=torch.bfloat16)
+    b2 = itl.linear_logp_bwd(hid, w, t, lse, g, out_dtype=torch.bfloat16, vocab_chunk=c["chunk"])
+    for x32, x1, x2 in zip((dh, dw), b1, b2):
+        assert torch.equal(bits(x1), bits(x2)), what
+        assert torch.equal(x1, x32.to(torch.bfloat16)), what
     hn, wn, tn, gn = to_np(hid), to_np(w), t.cpu().numpy(), to_np(g)
     dh64, dw64 = oracle.linear_logp_bwd(hn, wn, tn, gn)
     _, lse64 = oracle.linear_logp_fwd(hn, wn, tn)
