@@ -57,10 +57,12 @@ def assert_logp_parity(logp, lse, ref_logp, ref_lse, targets, ignore_index=-100,
 def rne_bf16(d):
     """Round float64 values to the nearest bf16 value, ties to even (one
     rounding, straight from float64).  bf16 keeps 8 significant bits: for
-    d = m * 2^e with 0.5 <= |m| < 1 the spacing is 2^(e-8)."""
+    d = m * 2^e with 0.5 <= |m| < 1 the spacing is 2^(e-8).  Below the
+    smallest normal, 2^-126 (e <= -126), bf16 values are subnormal and the
+    spacing stays at 2^-133."""
     d = np.asarray(d, dtype=np.float64)
     _, e = np.frexp(d)
-    ulp = np.ldexp(1.0, e - 8)
+    ulp = np.ldexp(1.0, np.maximum(e, -125) - 8)
     q = d / ulp  # exact: a power-of-two scaling
     lo = np.floor(q)
     frac = q - lo
