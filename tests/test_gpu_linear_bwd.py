@@ -393,7 +393,7 @@ def test_vocab_chunk_same_bits(n, hd, v, out_dtype):
 
 def test_vocab_chunk_full_size_same_bits():
     """The Qwen3-8B head (H = 4096, V = 151936) at N = 512: the default chunk
-    (the benchmarked launch sequence, 10 chunks) against one chunk over the
+    (the benchmarked launch sequence, 5 chunks) against one chunk over the
     whole vocabulary, fp32 and bf16 outputs; and the default workspace stays
     far below the one-chunk workspace."""
     h, w, t, g = _case(512, synth.QWEN3_HIDDEN, synth.QWEN3_VOCAB, seed=77)
