@@ -70,9 +70,9 @@ int xcd_cus();
 
 // Fused LM-head backward.  The vocabulary is walked in chunks of vc columns
 // (a multiple of 256; kDefaultChunk unless the caller asks for another), so
-// the workspace holds one chunk's dz_c [np, vc] and dz_c^T [vc, np], the
-// blocked hidden rows [np, h] (logits recomputed), h^T [h, np] (dW), and the
-// fp32 dh [n, h] between chunks (bf16 dh over several chunks); only the
+// the workspace holds one chunk's dz_c [np, vc], the blocked hidden rows
+// [np, h] (logits recomputed), h^T [h, np] (dW), and the fp32 dh [n, h]
+// between chunks (bf16 dh over several chunks); only the
 // regions the call uses (flags).  The weight needs no copy: dh reads it as
 // it is, as a K-outer operand (or the prepared transpose).  Byte
 // offsets, -1 for a region not used; np, vp = n, v rounded up to 256.
