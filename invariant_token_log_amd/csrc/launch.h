@@ -92,8 +92,9 @@ LinearBwdLayout linear_bwd_layout(int64_t n, int64_t h, int64_t v, int32_t flags
 // with z_bf16; [n, ld_z]) holds the forward's unscaled logits to read instead
 // of recomputing them, or is null.  prepared (or null) is the caller's
 // prepared weight (launch_prepare_weight): its blocked W feeds the recomputed
-// product and its W^T the dh product instead of transposing W into the
-// workspace.  vocab_chunk: columns per chunk (0 = kDefaultChunk), any value
+// product and its W^T the dh product as K-contiguous operands (without it,
+// the dh product reads W's rows in place as a K-outer operand, with the same
+// bits).  vocab_chunk: columns per chunk (0 = kDefaultChunk), any value
 // gives the same bits; ws: linear_bwd_layout(...).total bytes.
 void launch_linear_bwd(const uint16_t* hidden, int64_t ld_h, const uint16_t* weight, int64_t ld_w,
                        int64_t n, int64_t h, int64_t v, Targets targets, int64_t ignore,
