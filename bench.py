@@ -630,8 +630,8 @@ def standalone_linear_bwd(args, torch, itl, synth, ctx, saved=False, prepared=Fa
         "roofline": {"bound": "mfma", "achieved": r["tflops"],
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": r["mfma_frac"], "traffic": None,
-                     "kernel": "linear_logp_bwd (all launches: dz, the transposes, "
-                               "two products)"},
+                     "kernel": "linear_logp_bwd (all launches: the hidden rows' re-layout and "
+                               "transpose, dz, the two products)"},
         "extra_memory_bytes": extra, "workspace_bytes": r["workspace_bytes"],
         "vocab_chunk": r["vocab_chunk"],
     }
