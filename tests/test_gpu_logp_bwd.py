@@ -11,7 +11,7 @@ import torch
 import invariant_token_log_amd as itl
 import oracle
 import synth
-from gpu_helpers import assert_grad_parity, dev, to_np
+from gpu_helpers import assert_grad_parity, assert_logp_parity, bits, dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -124,6 +124,36 @@ def test_full_size_sampled():
     assert (d[ign].view(torch.int16) == 0).all()
     rs = d[~ign][:512].float().sum(dim=1).abs() / g[~ign][:512].abs()
     assert (rs < 0.05).all()
+
+
+def test_past_two_to_the_31_elements():
+    """14200 Qwen3-vocab rows hold 2.16e9 logits, more than 2^31: rows on both
+    sides of element 2^31 and the last rows get the oracle's logp, lse and
+    dlogits, the last rows computed alone give the same bits, and the 2-shard
+    forward agrees bit for bit, so no offset wraps at 32 bits."""
+    n = 14200
+    assert n * V > 2 ** 31
+    x = synth.normal_matrix(n, V, 3.0, torch.bfloat16, seed=81, device=dev())
+    t = synth.uniform_targets(n, V, seed=82, device=dev())
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=83, device=dev())[0]
+    logp, lse = itl.logp_fwd(x, t, -100, 4096)
+    d = itl.logp_bwd(x, t, lse, g, -100, 4096)
+    first_past = -(-(2 ** 31) // V)  # the first row that starts past element 2^31
+    rows = torch.tensor([0, first_past - 1, first_past, n - 2, n - 1], device=dev())
+    xn = x[rows].float().cpu().numpy().astype(np.float64)
+    tn = t[rows].cpu().numpy()
+    ref_logp, ref_lse = oracle.logp_fwd(xn, tn)
+    assert_logp_parity(logp[rows], lse[rows], ref_logp, ref_lse, t[rows], what="2^31 fwd")
+    d64 = oracle.logp_bwd(xn, tn, g[rows].cpu().numpy(), lse=ref_lse)
+    assert_grad_parity(d[rows], d64, xn, ref_lse, g[rows].cpu().numpy(), t[rows], what="2^31 bwd")
+    tail = slice(n - 8, n)
+    lp_a, lse_a = itl.logp_fwd(x[tail].contiguous(), t[tail].contiguous(), -100, 4096)
+    assert torch.equal(bits(lp_a), bits(logp[tail])) and torch.equal(bits(lse_a), bits(lse[tail]))
+    d_a = itl.logp_bwd(x[tail].contiguous(), t[tail].contiguous(), lse_a, g[tail].contiguous(),
+                       -100, 4096)
+    assert torch.equal(d_a.view(torch.int16), d[tail].view(torch.int16))
+    lp2, lse2 = itl.logp_fwd(x, t, -100, 4096, num_shards=2)
+    assert torch.equal(bits(lp2), bits(logp)) and torch.equal(bits(lse2), bits(lse))
 
 
 @pytest.mark.parametrize("v,w", [(300, 512), (V, 4096)])
