@@ -263,6 +263,28 @@ def test_saved_logits_same_bits(n, hd, v, out_dtype):
             itl.linear_logp_bwd(h, w, t, lse, g, saved_logits=z)
 
 
+def test_logits_past_two_to_the_31_elements():
+    """N = 14200 rows of the Qwen3-8B head: the forward's fp32 logits output
+    holds 2.16e9 values, past 2^31.  The last rows get the same logits, logp
+    and lse bits as when computed alone, and the backward that reads the saved
+    logits gives the recomputing backward's dh and dW bits, so no logits
+    offset wraps at 32 bits."""
+    n = 14200
+    c = synth.qwen3_linear(seed=95, n=n, device=dev(), ignore_frac=0.05)
+    h, w, t = c["hidden"], c["weight"], c["targets"]
+    assert n * w.shape[0] > 2 ** 31
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=96, device=dev())[0]
+    logp, lse, z = itl.linear_logp_fwd(h, w, t, return_logits=True, logits_dtype=torch.float32)
+    tail = slice(n - 16, n)
+    lp_a, lse_a, z_a = itl.linear_logp_fwd(h[tail].contiguous(), w, t[tail].contiguous(),
+                                           return_logits=True, logits_dtype=torch.float32)
+    assert torch.equal(bits(z_a), bits(z[tail]))
+    assert torch.equal(bits(lp_a), bits(logp[tail])) and torch.equal(bits(lse_a), bits(lse[tail]))
+    dh0, dw0 = itl.linear_logp_bwd(h, w, t, lse, g)
+    dh1, dw1 = itl.linear_logp_bwd(h, w, t, lse, g, saved_logits=z)
+    assert torch.equal(bits(dh0), bits(dh1)) and torch.equal(bits(dw0), bits(dw1))
+
+
 def test_saved_bf16_logits_rounded_variant():
     """In the bf16-rounded contract the bf16 logits output is exactly z, so
     reading it gives the recomputed gradient's bits; the autograd function
