@@ -59,6 +59,29 @@ def test_zero_weight_is_minus_log_v(v):
     assert torch.equal(bits(logp), bits(lz)) and torch.equal(bits(lse), bits(sz))
 
 
+def test_empty_and_all_ignored():
+    """N = 0: the fused forward and the streaming backward return empty
+    outputs.  Every row ignored: logp, lse and entropy are +0, and dh and dW
+    (sums of zero dz terms) are +0 too."""
+    hd, v = 64, 1000
+    w = synth.normal_matrix(v, hd, 0.02, torch.bfloat16, seed=5).to(dev())
+    h0 = torch.empty(0, hd, dtype=torch.bfloat16, device=dev())
+    t0 = torch.empty(0, dtype=torch.int64, device=dev())
+    logp, lse, ent = itl.linear_logp_fwd(h0, w, t0, return_entropy=True)
+    assert logp.numel() == 0 and lse.numel() == 0 and ent.numel() == 0
+    e0 = torch.empty(0, dtype=torch.float32, device=dev())
+    d = itl.logp_bwd(torch.empty(0, v, dtype=torch.bfloat16, device=dev()), t0, e0, e0, -100, 512)
+    assert d.shape == (0, v)
+    n = 300
+    h = synth.normal_matrix(n, hd, 1.0, torch.bfloat16, seed=6).to(dev())
+    t = torch.full((n,), -100, dtype=torch.int64, device=dev())
+    logp, lse, ent = itl.linear_logp_fwd(h, w, t, return_entropy=True)
+    for x in (logp, lse, ent):
+        assert (bits(x) == 0).all()
+    dh, dw = itl.linear_logp_bwd(h, w, t, lse, torch.ones(n, device=dev()))
+    assert (bits(dh) == 0).all() and (bits(dw) == 0).all()
+
+
 def test_row_invariance():
     """A row's z, statistics and logp do not depend on N, its position in the
     128-row block, or its neighbours."""
