@@ -169,7 +169,7 @@ def test_autograd_logp_and_entropy():
 
 # ----- fused LM head: temperature, entropy, logits -----------------------------
 
-@pytest.mark.parametrize("temp", [0.7, 1.0, 2.0, 1.3])
+@pytest.mark.parametrize("temp", [0.7, 1.0, 2.0, 1.3, 0.05, 25.0])
 def test_linear_temperature_entropy_parity(temp):
     c = synth.qwen3_linear(seed=21, n=200, h=256, v=3000, device=dev(), ignore_frac=0.05)
     h, w, t = c["hidden"], c["weight"], c["targets"]
@@ -222,7 +222,7 @@ def _linear_bwd_bounds(hn, wn, tn, gn, ghn, temp):
     return bh, bw
 
 
-@pytest.mark.parametrize("temp", [1.0, 0.8])
+@pytest.mark.parametrize("temp", [1.0, 0.8, 0.05, 25.0])
 def test_linear_bwd_temperature_entropy_parity(temp):
     c = synth.qwen3_linear(seed=23, n=130, h=256, v=1500, device=dev(), ignore_frac=0.05)
     h, w, t = c["hidden"], c["weight"], c["targets"]
