@@ -89,8 +89,10 @@ def assert_grad_parity(d_gpu, d_ref, x, lse_ref, g, targets, ignore_index=-100, 
     active = t != ignore_index
     p = np.exp(x - lse_ref[:, None])
     gg = np.abs(np.asarray(g, dtype=np.float64).reshape(-1))[:, None]
-    budget = (gg * p * (ATOL + RTOL * np.abs(x - lse_ref[:, None])) + 1e-6 * np.abs(d_ref)
-              + gg * FLT_MIN)
+    # a masked (-inf) logit has p = 0 and no error to carry (0 * inf would be NaN)
+    with np.errstate(invalid="ignore"):
+        carried = np.where(p > 0, p * (ATOL + RTOL * np.abs(x - lse_ref[:, None])), 0.0)
+    budget = gg * carried + 1e-6 * np.abs(d_ref) + gg * FLT_MIN
     if d_gpu.dtype == torch.bfloat16:
         ok = (d >= rne_bf16(d_ref - budget)) & (d <= rne_bf16(d_ref + budget))
     elif d_gpu.dtype == torch.float16:

@@ -12,7 +12,7 @@ import torch
 import invariant_token_log_amd as itl
 import oracle
 import synth
-from gpu_helpers import assert_logp_parity, bits, dev, to_np
+from gpu_helpers import assert_grad_parity, assert_logp_parity, bits, dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -269,6 +269,40 @@ def test_validate_invalid_targets_under_shards(shards):
     assert torch.equal(bits(logp)[ok], bits(ref_logp)[ok])
     # the LSE of a row does not depend on its target
     assert torch.equal(bits(lse)[[0, 1, 3, 4, 5]], bits(ref_lse)[[0, 1, 3, 4, 5]])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_masked_and_huge_logits(dtype):
+    """Masked vocabulary entries (-inf): half a row, whole leading tiles, every
+    other column, a row whose only finite logit is its target (logp exactly
+    +0); and logits of magnitude 1e37.  logp, lse and dlogits against the
+    oracle, and the 2-shard forward with the same bits."""
+    v, w, n = 5000, 512, 8
+    inf = float("inf")
+    x = synth.normal_matrix(n, v, 3.0, torch.float32, seed=91)
+    t = torch.tensor([10, 2600, 4999, 8, 100, 3000, 1, 4000])
+    x[0, 2500:] = -inf
+    x[1, :2560] = -inf
+    x[2, :] = -inf
+    x[2, 4999] = 1.5
+    x[3, 1::2] = -inf
+    x[4, 50], x[4, 60] = 1e37, -1e37
+    x[6, 1] = 1e37
+    x[7, :] = -1e37
+    x[7, 4000] = 0.0
+    x = x.to(dtype).to(dev())
+    t = t.to(dev())
+    logp, lse = itl.logp_fwd(x, t, -100, w)
+    x64, tn = to_np(x), t.cpu().numpy()
+    ref_logp, ref_lse = oracle.logp_fwd(x64, tn)
+    assert_logp_parity(logp, lse, ref_logp, ref_lse, t, what=f"masked {dtype}")
+    assert bits(logp)[2] == 0 and bits(logp)[7] == 0
+    lp2, lse2 = itl.logp_fwd(x, t, -100, w, num_shards=2)
+    assert torch.equal(bits(lp2), bits(logp)) and torch.equal(bits(lse2), bits(lse))
+    g = synth.normal_matrix(1, n, 1.0, torch.float32, seed=92)[0].to(dev())
+    d = itl.logp_bwd(x, t, lse, g, -100, w)
+    d64 = oracle.logp_bwd(x64, tn, to_np(g), lse=ref_lse)
+    assert_grad_parity(d, d64, x64, ref_lse, to_np(g), t, what=f"masked bwd {dtype}")
 
 
 def test_empty_batch():
