@@ -868,6 +868,14 @@ def run(args, ctx, pool, cores):
                                     prepared=wl == "linear_bwd_prepared")
     if pool is not None:
         out["cpu_baseline"] = cpu_baselines(pool, cores, ctx)
+        if wl == "fwd_bwd" and not args.no_secondary and out["cpu_baseline"]:
+            # the fused LM head's oracle (h W^T in float64, then logp) on a
+            # 64-row sample of the N = H = 4096 workload
+            _, h, v, hid, wt, t = _linear_case(torch, synth)
+            out["cpu_baseline"]["linear_fwd_qwen3_4096x4096x151936"] = cpu_baseline_linear(
+                hid, wt, t, 64)
+            del hid, wt, t
+            torch.cuda.empty_cache()
     elif wl == "linear" and not args.no_cpu_baseline:
         _, h, v, hid, wt, t = _linear_case(torch, synth)
         out["cpu_baseline"] = cpu_baseline_linear(hid, wt, t, args.cpu_rows or 512)
